@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked Gated Delta Product prefill forward on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input, all on the
+GPU through the C ABI of libgdp.so:
+    gdp_prefill_prepare  (split / GQA-expand / Householder-fold / gate)
+    gdp_recompute_w_u    (L2 norm, decays, transition block, inverse, w, u)
+    gdp_chunk_h          (state recurrence, corrected values)
+    gdp_chunk_o          (output)
+Workload: the long single-sequence prefill, B=1, T=32768 tokens, 16 heads
+(query/key groups = value heads = 16), K=V=128, M=2 Householder copies, chunk
+64, bf16 activations with fp32 gates, state and accumulation.  Inputs are
+drawn once (seeded, synthetic) and resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s over the timed steps, per-kernel times from
+HIP events recorded on the launch stream, the roofline of the dominant kernel
+(algorithmic bytes per launch / its average duration vs 8 TB/s HBM) and the
+oracle's throughput on the host cores as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDP prefill forward tokens/s (T=32k, H=16, K=V=128, M=2) + % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = dict(workload="long_prefill_32k", B=1, T=32768, H=16, HV=16, G=16, K=128, V=128, M=2, chunk=64,
+                dtype="bf16", path="prepare+recompute_w_u+chunk_h+chunk_o")
+KERNELS = ["gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o"]
+KERNEL_SRC = {
+    "gdp_prefill_prepare": ["prepare.hip"],
+    "gdp_recompute_w_u": ["wy.hip"],
+    "gdp_chunk_h": ["chunk_h.hip"],
+    "gdp_chunk_o": ["chunk_o.hip"],
+}
+KERNEL_SYMBOL = {  # device kernel names as rocprofv3 reports them
+    "gdp_prefill_prepare": "gdp_prepare_k",
+    "gdp_recompute_w_u": "gdp_wy_k",
+    "gdp_chunk_h": "gdp_chunk_h_k",
+    "gdp_chunk_o": "gdp_chunk_o_k",
+}
+
+
+def algorithmic_bytes(w):
+    """HBM bytes each stage must move at minimum (inputs read once, outputs
+    written once), per launch.  es = 2 (bf16); beta, g, k_rnorm are fp32."""
+    T, M, H, HV, G, K, V = w["T"] * w["B"], w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
+    P, N = V, K
+    es = 2
+    TM = T * M
+    nte = w["B"] * math.ceil(w["T"] * M / 64)
+    ntok_chunks = w["B"] * math.ceil(w["T"] / 64)
+    prep = T * (M * H * P + M * G * N + G * N) * es + T * (M * H + H) * es \
+        + T * H * N * es + TM * H * N * es + TM * H * P * es + TM * H * 4 + T * H * 4
+    wy = TM * H * K * es + TM * HV * V * es + TM * HV * 4 + T * HV * 4 \
+        + TM * HV * K * es + TM * HV * V * es + TM * H * 4
+    ch = TM * H * K * es + TM * H * 4 + TM * HV * K * es + TM * HV * V * es + T * HV * 4 \
+        + TM * HV * V * es + nte * HV * V * K * es
+    co = T * H * K * es + TM * H * K * es + TM * H * 4 + TM * HV * V * es + ntok_chunks * HV * V * K * es \
+        + T * HV * 4 + T * HV * V * es
+    return {"gdp_prefill_prepare": prep, "gdp_recompute_w_u": wy, "gdp_chunk_h": ch, "gdp_chunk_o": co}
+
+
+def src_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SRC[kernel] + ["gdp_common.h"]:
+        with open(os.path.join(ROOT, "gated_delta_product_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_long_prefill_32k.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    if not e or e.get("src_digest") != src_digest(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(d, w, threads):
+    """The oracle (numpy prepare + C recurrence and WY) on the same workload,
+    timed on the host cores."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from oracle import prepare as OP
+
+    T, M, H, K, V = w["T"], w["M"], w["H"], w["K"], w["V"]
+    Ts = int(os.environ.get("GDP_BENCH_CPU_TOKENS", T))
+    x = d["x"][:, :Ts].float().numpy()
+    ba = d["ba"][:, :Ts].float().numpy()
+    oracle.lib()
+    t0 = time.perf_counter()
+    q, k, v, beta, g = OP.prefill_prepare(x, ba, d["A_log"].numpy(), d["dt_bias"].numpy(), M, H, w["G"], V, K)
+
+    def head(hv):
+        qh = np.ascontiguousarray(q[0, :, hv])
+        kh = np.ascontiguousarray(k[0, :, hv])
+        vh = np.ascontiguousarray(v[0, :, hv])
+        bh = np.ascontiguousarray(beta[0, :, hv])
+        gh = np.ascontiguousarray(g[0, :, hv])
+        oracle.recurrence(qh, kh, vh, bh, gh, M, scale=1.0 / math.sqrt(K))
+        oracle.wy(kh, vh, bh, gh, M)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(head, range(w["HV"])))
+    dt = time.perf_counter() - t0
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d tokens x %d heads of the same workload (prepare, serial fp64 recurrence "
+                      "-> o, v_new, h, and per-chunk WY -> w, u); %.1f s wall" % (Ts, w["HV"], dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU hot path only; --gpus %d (WORLD_SIZE %d) is not supported: "
+              "this build has no multi-GPU path." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_product_amd import binding as G
+    from gated_delta_product_amd import synth
+
+    w = dict(WORKLOAD)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = synth.prepare_draws(1, w["T"], w["M"], w["H"], w["G"], w["V"], w["K"], "bf16", synth.seed_of(4) + 100)
+    x, ba = d["x"].to(dev), d["ba"].to(dev)
+    A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
+    M, H, Gq, P, N = w["M"], w["H"], w["G"], w["V"], w["K"]
+    prep_out = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N)
+    buf = G.ChunkBuffers(*prep_out)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
+        if ev:
+            ev[1].record(stream)
+        buf.recompute_w_u()
+        if ev:
+            ev[2].record(stream)
+        buf.chunk_h()
+        if ev:
+            ev[3].record(stream)
+        buf.chunk_o()
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ktimes = {k: 0.0 for k in KERNELS}
+    for e in evs:
+        for i, k in enumerate(KERNELS):
+            ktimes[k] += e[i].elapsed_time(e[i + 1]) / args.steps  # ms
+    tokens = w["B"] * w["T"]
+    value = tokens / (ms_per_step / 1e3)
+
+    ab = algorithmic_bytes(w)
+    kern = {}
+    for k in KERNELS:
+        us = ktimes[k] * 1e3
+        gbs = ab[k] / (ktimes[k] / 1e3) / 1e9
+        kern[k] = {"us": round(us, 2), "alg_bytes": ab[k], "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(KERNELS, key=lambda k: ktimes[k])
+    achieved = ab[dom] / (ktimes[dom] / 1e3) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(d, w, threads)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": w, "roofline": roof, "cpu_baseline": cpu, "kernels": kern,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

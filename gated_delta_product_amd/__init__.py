@@ -5,15 +5,12 @@ kernels); :mod:`gated_delta_product_amd.binding` is a thin ctypes binding that
 marshals torch tensors into it.  :mod:`gated_delta_product_amd.synth` draws
 seeded synthetic inputs.
 """
+import importlib
 
-__all__ = ["binding", "synth"]
+__all__ = ["binding", "synth", "build"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    if name == "synth":
-        from . import synth
-        return synth
+    if name in __all__:
+        return importlib.import_module(__name__ + "." + name)
     raise AttributeError(name)

@@ -1,0 +1,263 @@
+"""Thin ctypes binding of libgdp.so (include/gdp.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch provides device memory (outputs are allocated
+with torch.empty on the inputs' device) and the current stream.  If the
+library is not built this module raises; there is no fallback path.
+
+Names follow the Megatron-Core GDP op pages: prefill_prepare
+(core.ssm.ops.gdp.prepare), recompute_w_u (core.ssm.ops.gdp.wy_fast),
+chunk_h and chunk_o (core.ssm.ops.gdp.chunk_o) and chunk_fwd for the three
+chunk stages in order.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdp.so")
+
+GDP_OK, GDP_ERR_INVALID, GDP_ERR_UNSUPPORTED, GDP_ERR_HIP = 0, 1, 2, 3
+GDP_F32, GDP_BF16 = 0, 1
+CHUNK = 64
+
+_i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+
+
+class ChunkArgs(ctypes.Structure):
+    """Mirror of gdp_chunk_args (include/gdp.h)."""
+    _fields_ = [
+        ("B", _i64), ("T", _i64), ("H", _i32), ("HV", _i32), ("K", _i32), ("V", _i32),
+        ("M", _i32), ("chunk_size", _i32), ("scale", _f32), ("dtype", ctypes.c_int),
+        ("cu_seqlens", _vp), ("num_seqs", _i64), ("h_chunks", _i64),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("g", _vp), ("k_rnorm", _vp),
+        ("w", _vp), ("u", _vp), ("v_new", _vp), ("h", _vp), ("o", _vp),
+    ]
+
+
+class GdpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("gdp status %d: %s" % (status, msg))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdp.so is not built; run gated_delta_product_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdp_prefill_prepare.restype = ctypes.c_int
+        L.gdp_prefill_prepare.argtypes = [
+            _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp,
+            _i64, _i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+            _vp, _vp, _vp, _vp, _vp, _vp]
+        for name in ("gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o", "gdp_chunk_fwd"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
+        L.gdp_num_state_chunks.restype = _i64
+        L.gdp_num_state_chunks.argtypes = [ctypes.POINTER(_i32), _i64, _i64, _i64, _i32, _i32]
+        L.gdp_last_error.restype = ctypes.c_char_p
+        L.gdp_last_error.argtypes = []
+        L.gdp_version.restype = ctypes.c_char_p
+        L.gdp_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != GDP_OK:
+        raise GdpError(status, lib().gdp_last_error().decode())
+
+
+def _dtype_code(t):
+    if t == torch.bfloat16:
+        return GDP_BF16
+    if t == torch.float32:
+        return GDP_F32
+    raise TypeError("unsupported dtype %s (bf16 or f32)" % t)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices")
+    return dev
+
+
+def _contig(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+# ------------------------------------------------------------------ prepare
+
+def prefill_prepare(x, ba, A_log, dt_bias, num_householder, num_heads, num_groups, head_dim, state_dim,
+                    out=None):
+    """Split, GQA-expand, Householder-fold and gate a prefill step.
+
+    x [n, T, M*H*P + M*G*N + G*N] and ba [n, T, M*H + H] (bf16 or f32, last
+    dim contiguous, rows may be strided); A_log, dt_bias [H] float32.
+    Returns (q [n,T,H,N], k [n,T*M,H,N], v [n,T*M,H,P], beta [n,T*M,H] f32,
+    g [n,T,H] f32).  ``out`` may hold preallocated (q, k, v, beta, g).
+    """
+    M, H, G, P, N = num_householder, num_heads, num_groups, head_dim, state_dim
+    dev = _need_cuda(x, ba, A_log, dt_bias)
+    if x.dim() != 3 or ba.dim() != 3:
+        raise ValueError("x and ba must be 3-D [n, T, ...]")
+    if x.stride(-1) != 1 or ba.stride(-1) != 1:
+        raise ValueError("the last dimension of x and ba must be contiguous")
+    if ba.dtype != x.dtype:
+        raise ValueError("x and ba must share a dtype")
+    if A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise ValueError("A_log and dt_bias must be float32")
+    _contig(A_log, "A_log")
+    _contig(dt_bias, "dt_bias")
+    n, T = x.shape[0], x.shape[1]
+    shapes = [((n, T, H, N), x.dtype), ((n, T * M, H, N), x.dtype), ((n, T * M, H, P), x.dtype),
+              ((n, T * M, H), torch.float32), ((n, T, H), torch.float32)]
+    if out is None:
+        out = [torch.empty(s, dtype=d, device=dev) for s, d in shapes]
+    for t, (s, d) in zip(out, shapes):
+        if tuple(t.shape) != s or t.dtype != d or not t.is_contiguous() or t.device != dev:
+            raise ValueError("out tensor mismatch: want %s %s" % (s, d))
+    q, k, v, beta, g = out
+    if x.shape[2] != M * H * P + M * G * N + G * N:
+        raise ValueError("x last dim %d != M*H*P + M*G*N + G*N" % x.shape[2])
+    if tuple(ba.shape) != (n, T, M * H + H):
+        raise ValueError("ba must be [n, T, M*H + H]")
+    _check(lib().gdp_prefill_prepare(
+        _ptr(x), x.stride(0), x.stride(1), _ptr(ba), ba.stride(0), ba.stride(1),
+        _ptr(A_log), _ptr(dt_bias), n, T, M, H, G, P, N, _dtype_code(x.dtype),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _stream(dev)))
+    return q, k, v, beta, g
+
+
+# ------------------------------------------------------------------ chunk stages
+
+def num_state_chunks(T, M, B=1, cu_seqlens_host=None):
+    """Chunks h must hold (sum over sequences of ceil(len*M/64))."""
+    if cu_seqlens_host is None:
+        return B * math.ceil(T * M / CHUNK)
+    cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    n = cu.numel() - 1
+    arr = (_i32 * (n + 1))(*cu.tolist())
+    return int(lib().gdp_num_state_chunks(arr, n, 1, T, M, CHUNK))
+
+
+class ChunkBuffers:
+    """All tensors of one chunk forward (inputs, scratch and outputs)."""
+
+    def __init__(self, q, k, v, beta, g, cu_seqlens=None, scale=None, h_chunks=None,
+                 cu_seqlens_host=None, num_householder=None):
+        dev = _need_cuda(q, k, v, beta, g, cu_seqlens)
+        for t, nm in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (g, "g")):
+            _contig(t, nm)
+        if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+            raise ValueError("q, k, v must be 4-D")
+        B, T, H, K = q.shape
+        M = num_householder if num_householder is not None else k.shape[1] // max(T, 1)
+        HV, V = v.shape[2], v.shape[3]
+        if tuple(k.shape) != (B, T * M, H, K):
+            raise ValueError("k must be [B, T*M, H, K] = %s, got %s" % ((B, T * M, H, K), tuple(k.shape)))
+        if tuple(v.shape[:2]) != (B, T * M):
+            raise ValueError("v must be [B, T*M, HV, V]")
+        if tuple(beta.shape) != (B, T * M, HV) or beta.dtype != torch.float32:
+            raise ValueError("beta must be float32 [B, T*M, HV]")
+        if tuple(g.shape) != (B, T, HV) or g.dtype != torch.float32:
+            raise ValueError("g must be float32 [B, T, HV]")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("q, k, v must share a dtype")
+        nseq = B
+        if cu_seqlens is not None:
+            if cu_seqlens.dtype != torch.int32:
+                raise ValueError("cu_seqlens must be int32")
+            _contig(cu_seqlens, "cu_seqlens")
+            nseq = cu_seqlens.numel() - 1
+        if h_chunks is None:
+            if cu_seqlens is None:
+                h_chunks = num_state_chunks(T, M, B)
+            elif cu_seqlens_host is not None:
+                h_chunks = num_state_chunks(T, M, 1, cu_seqlens_host)
+            else:
+                h_chunks = math.ceil(T * M / CHUNK) + nseq
+        dt = q.dtype
+        self.dims = dict(B=B, T=T, H=H, HV=HV, K=K, V=V, M=M, nseq=nseq)
+        self.q, self.k, self.v, self.beta, self.g = q, k, v, beta, g
+        self.cu_seqlens = cu_seqlens
+        self.k_rnorm = torch.empty((B, T * M, H), dtype=torch.float32, device=dev)
+        self.w = torch.empty((B, T * M, HV, K), dtype=dt, device=dev)
+        self.u = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
+        self.v_new = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
+        self.h = torch.empty((h_chunks, HV, V, K), dtype=dt, device=dev)
+        self.o = torch.empty((B, T, HV, V), dtype=dt, device=dev)
+        self.device = dev
+        self.args = ChunkArgs(
+            B=B, T=T, H=H, HV=HV, K=K, V=V, M=M, chunk_size=CHUNK,
+            scale=float(scale) if scale is not None else 0.0, dtype=_dtype_code(dt),
+            cu_seqlens=None if cu_seqlens is None else cu_seqlens.data_ptr(),
+            num_seqs=nseq, h_chunks=h_chunks,
+            q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), beta=beta.data_ptr(), g=g.data_ptr(),
+            k_rnorm=self.k_rnorm.data_ptr(), w=self.w.data_ptr(), u=self.u.data_ptr(),
+            v_new=self.v_new.data_ptr(), h=self.h.data_ptr(), o=self.o.data_ptr())
+
+    def set(self, **tensors):
+        """Point a slot (e.g. h, v_new) at another tensor of the same shape."""
+        for name, t in tensors.items():
+            cur = getattr(self, name)
+            if tuple(t.shape) != tuple(cur.shape) or t.dtype != cur.dtype or not t.is_contiguous():
+                raise ValueError("%s: shape/dtype mismatch" % name)
+            setattr(self, name, t)
+            setattr(self.args, name, t.data_ptr())
+
+    def _call(self, fn, stream=None):
+        s = stream if stream is not None else _stream(self.device)
+        _check(fn(ctypes.byref(self.args), s))
+
+    def recompute_w_u(self, stream=None):
+        self._call(lib().gdp_recompute_w_u, stream)
+
+    def chunk_h(self, stream=None):
+        self._call(lib().gdp_chunk_h, stream)
+
+    def chunk_o(self, stream=None):
+        self._call(lib().gdp_chunk_o, stream)
+
+    def forward(self, stream=None):
+        self._call(lib().gdp_chunk_fwd, stream)
+        return self.o
+
+
+def chunk_fwd(q, k, v, beta, g, scale=None, cu_seqlens=None, cu_seqlens_host=None):
+    """Chunked GDP forward.  q [B,T,H,K]; k [B,T*M,H,K]; v [B,T*M,HV,V];
+    beta [B,T*M,HV] f32; g [B,T,HV] f32 natural-log decay per token.
+    Returns the ChunkBuffers holding o and the intermediates (w, u, v_new, h)."""
+    buf = ChunkBuffers(q, k, v, beta, g, cu_seqlens=cu_seqlens, scale=scale, cu_seqlens_host=cu_seqlens_host)
+    buf.forward()
+    return buf
+
+
+def version():
+    return lib().gdp_version().decode()

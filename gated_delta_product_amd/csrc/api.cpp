@@ -1,0 +1,190 @@
+// api.cpp -- the C ABI declared in include/gdp.h: argument validation,
+// error reporting and kernel launches on the caller's stream.  No allocation,
+// no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gdp_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+gdp_status fail(gdp_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+gdp_status ok() {
+    g_err.clear();
+    return GDP_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t dsize(gdp_dtype d) { return d == GDP_BF16 ? 2 : 4; }
+
+gdp_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(GDP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Stage masks for validation.
+enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u };
+
+gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParams *out) {
+    if (!a) return fail(GDP_ERR_INVALID, "args is NULL");
+    if (a->dtype != GDP_F32 && a->dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "unknown dtype %d", (int)a->dtype);
+    if (a->B < 0 || a->T < 0) return fail(GDP_ERR_INVALID, "B and T must be >= 0 (B=%lld T=%lld)",
+                                          (long long)a->B, (long long)a->T);
+    if (a->H < 1 || a->HV < 1) return fail(GDP_ERR_INVALID, "H and HV must be >= 1");
+    if (a->HV % a->H) return fail(GDP_ERR_INVALID, "HV (%d) must be a multiple of H (%d)", a->HV, a->H);
+    if (a->HV > 65535) return fail(GDP_ERR_UNSUPPORTED, "HV > 65535");
+    if (a->M < 1 || a->M > 4) return fail(GDP_ERR_UNSUPPORTED, "num_householder M=%d not in [1, 4]", a->M);
+    if (a->chunk_size != 64) return fail(GDP_ERR_UNSUPPORTED, "chunk_size %d: only 64 is built", a->chunk_size);
+    if (a->dtype == GDP_BF16) {
+        if (!(a->K == 64 || a->K == 128)) return fail(GDP_ERR_UNSUPPORTED, "K=%d: bf16 supports 64, 128", a->K);
+        if (!(a->V == 64 || a->V == 128 || a->V == 256))
+            return fail(GDP_ERR_UNSUPPORTED, "V=%d: bf16 supports 64, 128, 256", a->V);
+    } else {
+        if (a->K != 64 || !(a->V == 64 || a->V == 128))
+            return fail(GDP_ERR_UNSUPPORTED, "f32 supports K=64 with V in {64, 128} (K=%d V=%d)", a->K, a->V);
+    }
+    if (!std::isfinite(a->scale)) return fail(GDP_ERR_INVALID, "scale is not finite");
+    if (a->cu_seqlens) {
+        if (a->B != 1) return fail(GDP_ERR_INVALID, "cu_seqlens requires B == 1 (got %lld)", (long long)a->B);
+        if (a->num_seqs < 0) return fail(GDP_ERR_INVALID, "num_seqs < 0");
+    }
+    if (a->h_chunks < 0) return fail(GDP_ERR_INVALID, "h_chunks < 0");
+
+    const int64_t T = a->T;
+    const int64_t nseq = a->cu_seqlens ? a->num_seqs : a->B;
+    const int64_t per_seq = cdiv(T * a->M, 64);
+    const int64_t max_items = a->cu_seqlens ? (nseq > 0 ? per_seq + nseq : 0) : a->B * per_seq;
+    const int64_t max_tok = a->cu_seqlens ? (nseq > 0 ? cdiv(T, 64) + nseq : 0) : a->B * cdiv(T, 64);
+    if (max_items > 0x7fffffff || max_tok > 0x7fffffff || nseq * a->HV * 16 > 0x7fffffff)
+        return fail(GDP_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (!a->cu_seqlens && (stages & (ST_H | ST_O)) && a->h_chunks < a->B * per_seq)
+        return fail(GDP_ERR_INVALID, "h_chunks %lld < required %lld", (long long)a->h_chunks,
+                    (long long)(a->B * per_seq));
+
+    const bool empty = (T == 0 || nseq == 0);
+    struct Need {
+        unsigned stages;
+        const void *p;
+        const char *name;
+    } needs[] = {
+        {ST_O, a->q, "q"},           {ST_WY | ST_H | ST_O, a->k, "k"}, {ST_WY, a->v, "v"},
+        {ST_WY, a->beta, "beta"},    {ST_WY | ST_H | ST_O, a->g, "g"}, {ST_WY | ST_H | ST_O, a->k_rnorm, "k_rnorm"},
+        {ST_WY | ST_H, a->w, "w"},   {ST_WY | ST_H, a->u, "u"},        {ST_H | ST_O, a->v_new, "v_new"},
+        {ST_H | ST_O, a->h, "h"},    {ST_O, a->o, "o"},
+    };
+    if (!empty) {
+        for (const Need &n : needs) {
+            if (!(n.stages & stages)) continue;
+            if (!n.p) return fail(GDP_ERR_INVALID, "%s is NULL", n.name);
+            if (!aligned16(n.p)) return fail(GDP_ERR_INVALID, "%s is not 16-byte aligned", n.name);
+        }
+    }
+    out->a = *a;
+    if (!(out->a.scale > 0.f)) out->a.scale = 1.0f / std::sqrt((float)a->K);
+    out->nseq = empty ? 0 : nseq;
+    out->max_items = empty ? 0 : max_items;
+    out->max_tok_chunks = empty ? 0 : max_tok;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+gdp_status gdp_prefill_prepare(const void *x, int64_t x_n_stride, int64_t x_t_stride, const void *ba,
+                               int64_t ba_n_stride, int64_t ba_t_stride, const float *A_log,
+                               const float *dt_bias, int64_t n, int64_t T, int32_t M, int32_t H, int32_t G,
+                               int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k, void *v, float *beta,
+                               float *g, void *stream) {
+    if (dtype != GDP_F32 && dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "unknown dtype %d", (int)dtype);
+    if (n < 0 || T < 0) return fail(GDP_ERR_INVALID, "n and T must be >= 0");
+    if (M < 1 || H < 1 || G < 1 || P < 1 || N < 1) return fail(GDP_ERR_INVALID, "M, H, G, P, N must be >= 1");
+    if (H % G) return fail(GDP_ERR_INVALID, "num_heads H=%d must be a multiple of num_groups G=%d", H, G);
+    if (n > 65535 || T > 0x7fffffff) return fail(GDP_ERR_UNSUPPORTED, "n or T too large for one launch");
+    const int64_t width = (int64_t)M * H * P + (int64_t)M * G * N + (int64_t)G * N;
+    if (x_t_stride < 0 || x_n_stride < 0 || ba_t_stride < 0 || ba_n_stride < 0)
+        return fail(GDP_ERR_INVALID, "strides must be >= 0");
+    if (n == 0 || T == 0) return ok();
+    if (!x || !ba || !A_log || !dt_bias || !q || !k || !v || !beta || !g)
+        return fail(GDP_ERR_INVALID, "a tensor pointer is NULL");
+    if (T > 1 && x_t_stride < width) return fail(GDP_ERR_INVALID, "x rows overlap (t stride %lld < width %lld)",
+                                                 (long long)x_t_stride, (long long)width);
+    if (T > 1 && ba_t_stride < (int64_t)M * H + H) return fail(GDP_ERR_INVALID, "ba rows overlap");
+    const size_t es = dsize(dtype);
+    const bool vec16 = aligned16(x) && aligned16(q) && aligned16(k) && aligned16(v) &&
+                       ((x_t_stride * es) % 16 == 0) && ((x_n_stride * es) % 16 == 0) &&
+                       ((P * es) % 16 == 0) && ((N * es) % 16 == 0);
+    gdp::PrepareParams p{x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride, A_log, dt_bias, n, T,
+                         M, H, G, P, N, dtype, vec16, q, k, v, beta, g};
+    return hip_status(gdp::launch_prepare(p, (hipStream_t)stream), "gdp_prefill_prepare launch");
+}
+
+gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream) {
+    gdp::ChunkParams p;
+    gdp_status st = check_chunk(a, ST_WY, &p);
+    if (st != GDP_OK) return st;
+    return hip_status(gdp::launch_wy(p, (hipStream_t)stream), "gdp_recompute_w_u launch");
+}
+
+gdp_status gdp_chunk_h(const gdp_chunk_args *a, void *stream) {
+    gdp::ChunkParams p;
+    gdp_status st = check_chunk(a, ST_H, &p);
+    if (st != GDP_OK) return st;
+    return hip_status(gdp::launch_chunk_h(p, (hipStream_t)stream), "gdp_chunk_h launch");
+}
+
+gdp_status gdp_chunk_o(const gdp_chunk_args *a, void *stream) {
+    gdp::ChunkParams p;
+    gdp_status st = check_chunk(a, ST_O, &p);
+    if (st != GDP_OK) return st;
+    return hip_status(gdp::launch_chunk_o(p, (hipStream_t)stream), "gdp_chunk_o launch");
+}
+
+gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream) {
+    gdp::ChunkParams p;
+    gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
+    if (st != GDP_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = hip_status(gdp::launch_wy(p, s), "gdp_chunk_fwd: recompute_w_u launch")) != GDP_OK) return st;
+    if ((st = hip_status(gdp::launch_chunk_h(p, s), "gdp_chunk_fwd: chunk_h launch")) != GDP_OK) return st;
+    return hip_status(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd: chunk_o launch");
+}
+
+int64_t gdp_num_state_chunks(const int32_t *cu_seqlens_host, int64_t num_seqs, int64_t B, int64_t T, int32_t M,
+                             int32_t chunk_size) {
+    if (T < 0 || B < 0 || M < 1 || chunk_size < 1) return -1;
+    if (!cu_seqlens_host) return B * cdiv(T * M, chunk_size);
+    if (num_seqs < 0) return -1;
+    int64_t total = 0;
+    for (int64_t i = 0; i < num_seqs; ++i) {
+        int64_t a = cu_seqlens_host[i], b = cu_seqlens_host[i + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        b = b < a ? a : (b > T ? T : b);
+        total += cdiv((b - a) * M, chunk_size);
+    }
+    return total;
+}
+
+const char *gdp_last_error(void) { return g_err.c_str(); }
+
+const char *gdp_version(void) { return "gdp-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// gdp_internal.h -- launcher interface between the C ABI (api.cpp) and the
+// kernel translation units.  Host-only declarations; no device code.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdp.h"
+
+namespace gdp {
+
+struct PrepareParams {
+    const void *x;
+    int64_t x_n_stride, x_t_stride;
+    const void *ba;
+    int64_t ba_n_stride, ba_t_stride;
+    const float *A_log, *dt_bias;
+    int64_t n, T;
+    int M, H, G, P, N;
+    gdp_dtype dtype;
+    bool vec16;  // every row start and segment is 16-byte aligned
+    void *q, *k, *v;
+    float *beta, *g;
+};
+
+hipError_t launch_prepare(const PrepareParams &p, hipStream_t stream);
+
+// Validated chunk-stage arguments (scale resolved, nseq resolved).
+struct ChunkParams {
+    gdp_chunk_args a;
+    int64_t nseq;       // sequences: num_seqs with cu_seqlens, else B
+    int64_t max_items;  // upper bound on 64-row chunks over all sequences
+    int64_t max_tok_chunks;  // upper bound on 64-token chunks
+};
+
+hipError_t launch_wy(const ChunkParams &p, hipStream_t stream);
+hipError_t launch_chunk_h(const ChunkParams &p, hipStream_t stream);
+hipError_t launch_chunk_o(const ChunkParams &p, hipStream_t stream);
+
+}  // namespace gdp

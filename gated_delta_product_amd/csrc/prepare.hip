@@ -1,0 +1,121 @@
+// prepare.hip -- fused prefill prepare for the Gated Delta Product
+// (core.ssm.ops.gdp.prepare: module description and gdp_prefill_prepare).
+//
+// One block per (token, batch row).  The block writes every output of its
+// token: the value copies, the GQA-expanded key copies and query, beta for
+// each (copy, head) and g for each head.  Copies move in 16-byte vectors when
+// the rows allow it.  HBM-bound: each x row is read once (key/query groups are
+// re-read from cache once per head sharing them) and every output is written
+// once.
+#include "gdp_common.h"
+#include "gdp_internal.h"
+
+namespace gdp {
+
+// beta = 1 / (1 + exp(-b)) with float32 rounding after each operation;
+// exp is evaluated in double and rounded once.
+__device__ __forceinline__ float gate_beta(float b) {
+#pragma clang fp contract(off)
+    const float e = (float)exp(-(double)b);
+    const float d = 1.0f + e;
+    return 1.0f / d;
+}
+
+// g = -exp(A_log) * softplus(a + dt_bias); softplus(s) = s for s > 20,
+// else log1p(exp(s)) (core.ssm.ops.gdp.prepare, softplus).
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
+#pragma clang fp contract(off)
+    const float s = a + dt_bias;
+    float sp;
+    if (s > 20.0f) {
+        sp = s;
+    } else {
+        const float e = (float)exp((double)s);
+        sp = (float)log1p((double)e);
+    }
+    const float ea = (float)exp((double)A_log);
+    return -(ea * sp);
+}
+
+// Copy unit: a 16-byte vector when VEC16, else one element.
+template <typename T, bool VEC16>
+struct Unit {
+    typedef typename std::conditional<VEC16, uint4, T>::type type;
+    static constexpr int elems = VEC16 ? (int)(16 / sizeof(T)) : 1;
+};
+
+template <typename T, bool VEC16>
+__global__ void __launch_bounds__(256)
+gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
+              const T *__restrict__ ba, int64_t bns, int64_t bts,
+              const float *__restrict__ A_log, const float *__restrict__ dt_bias,
+              int64_t T_, int M, int H, int G, int P, int N,
+              T *__restrict__ q, T *__restrict__ k, T *__restrict__ v,
+              float *__restrict__ beta, float *__restrict__ g) {
+    typedef typename Unit<T, VEC16>::type U;
+    constexpr int E = Unit<T, VEC16>::elems;
+    const int64_t t = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int64_t tok = b * T_ + t;  // flattened token index
+    const T *xr = x + b * xns + t * xts;
+    const T *br = ba + b * bns + t * bts;
+    const int hpg = H / G;
+    const int HN = H * N;
+
+    const int64_t nv = (int64_t)M * H * P / E;  // value units
+    const int64_t nk = (int64_t)M * HN / E;     // key units (expanded)
+    const int64_t nq = (int64_t)HN / E;         // query units (expanded)
+    const int64_t kbase = (int64_t)M * H * P;   // key segment offset in x
+    const int64_t qbase = kbase + (int64_t)M * G * N;
+
+    U *vo = (U *)(v + tok * (int64_t)M * H * P);
+    U *ko = (U *)(k + tok * (int64_t)M * HN);
+    U *qo = (U *)(q + tok * (int64_t)HN);
+    const U *xv = (const U *)xr;
+
+    for (int64_t i = threadIdx.x; i < nv + nk + nq; i += blockDim.x) {
+        if (i < nv) {
+            // value copies are already in (copy, head, dim) order
+            vo[i] = xv[i];
+        } else if (i < nv + nk) {
+            const int64_t e = (i - nv) * E;  // element within the token's key copies
+            const int j = (int)(e / HN);
+            const int rem = (int)(e - (int64_t)j * HN);
+            const int h = rem / N, n = rem - (rem / N) * N;
+            ko[i - nv] = *(const U *)(xr + kbase + (int64_t)j * G * N + (h / hpg) * N + n);
+        } else {
+            const int e = (int)((i - nv - nk) * E);
+            const int h = e / N, n = e - (e / N) * N;
+            qo[i - nv - nk] = *(const U *)(xr + qbase + (h / hpg) * N + n);
+        }
+    }
+    // gates: beta for (copy, head) = M*H values, then g for H heads
+    for (int i = threadIdx.x; i < M * H + H; i += blockDim.x) {
+        if (i < M * H) {
+            beta[tok * (int64_t)M * H + i] = gate_beta(to_f32(br[i]));
+        } else {
+            const int h = i - M * H;
+            g[tok * (int64_t)H + h] = gate_g(to_f32(br[i]), A_log[h], dt_bias[h]);
+        }
+    }
+}
+
+template <typename T, bool VEC16>
+static hipError_t launch_prepare_t(const PrepareParams &p, hipStream_t stream) {
+    dim3 grid((unsigned)p.T, (unsigned)p.n);
+    hipLaunchKernelGGL((gdp_prepare_k<T, VEC16>), grid, dim3(256), 0, stream,
+                       (const T *)p.x, p.x_n_stride, p.x_t_stride,
+                       (const T *)p.ba, p.ba_n_stride, p.ba_t_stride,
+                       p.A_log, p.dt_bias, p.T, p.M, p.H, p.G, p.P, p.N,
+                       (T *)p.q, (T *)p.k, (T *)p.v, p.beta, p.g);
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare(const PrepareParams &p, hipStream_t stream) {
+    if (p.n == 0 || p.T == 0) return hipSuccess;
+    if (p.dtype == GDP_BF16)
+        return p.vec16 ? launch_prepare_t<bf16, true>(p, stream) : launch_prepare_t<bf16, false>(p, stream);
+    return p.vec16 ? launch_prepare_t<float, true>(p, stream) : launch_prepare_t<float, false>(p, stream);
+}
+
+}  // namespace gdp

@@ -1,0 +1,241 @@
+// wy.hip -- per-chunk WY factors of the Gated Delta Product
+// (core.ssm.ops.gdp.wy_fast: module description, recompute_w_u_fwd).
+//
+// One block (4 waves) per (64-row chunk of the expanded stream, value head).
+// Fused steps, all on chip:
+//   khat = k / sqrt(sum k^2 + 1e-6)           (L2 norm left to the chunk op,
+//                                               core.ssm.ops.gdp.prepare, Returns)
+//   gamma_e = within-chunk cumulative log decay; a token's decay sits on its
+//             first copy
+//   L[a][b] = beta_a exp(gamma_a - gamma_b) khat_a . khat_b   (b < a)
+//   A = (I + L)^-1                             (the solve_tril block)
+//   u = A diag(beta) V                         (effective values)
+//   w = A diag(beta exp(gamma)) Khat           (effective keys with decay)
+// The Gram matrix K K^T and the two products run on the matrix cores (bf16 in,
+// fp32 accumulate); the norms are applied as fp32 row scales so the raw bf16
+// inputs are the operands.  A is built in fp32: the four 16x16 diagonal
+// blocks by forward substitution (one lane per column), the off-diagonal
+// blocks level by level with fp32 MFMA:  A_ij = -A_ii sum_{j<=m<i} L_im A_mj.
+// u and w are computed transposed (u^T = V^T A1^T) so each lane ends up with
+// four consecutive columns of one output row, stored as one 8-byte write.
+#include "gdp_common.h"
+#include "gdp_internal.h"
+
+namespace gdp {
+
+namespace {
+
+constexpr int C = 64;      // chunk rows
+constexpr int LDA = C + 4;  // fp32 row stride of L and A in LDS
+
+template <typename T> struct Pad { static constexpr int value = 32 / (int)sizeof(T); };
+
+}  // namespace
+
+template <typename T, int KD, int VD>
+__global__ void __launch_bounds__(256)
+gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ beta,
+         const float *__restrict__ g, const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok,
+         int H, int HV, int M, float *__restrict__ k_rnorm, T *__restrict__ w, T *__restrict__ u) {
+    typedef typename Frag<T>::type FragT;
+    constexpr int LDK = KD + Pad<T>::value;
+    constexpr int LDV = VD + Pad<T>::value;
+    __shared__ __attribute__((aligned(16))) T Ks[C * LDK];
+    __shared__ __attribute__((aligned(16))) T Vs[C * LDV];
+    __shared__ __attribute__((aligned(16))) float Lm[C * LDA];
+    __shared__ __attribute__((aligned(16))) float Am[C * LDA];
+    __shared__ float s_beta[C], s_gam[C], s_rk[C], s_ws[C];
+
+    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, blockIdx.x);
+    if (loc.seq < 0) return;
+    const int hv = blockIdx.y;
+    const int hk = hv / (HV / H);
+    const int64_t r0 = loc.bos * M + C * loc.c;  // first expanded row (global)
+    const int64_t rend = loc.eos * M;
+    const int n = (int)((rend - r0) < C ? (rend - r0) : C);
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    const int lg = lane >> 4, lc = lane & 15;
+
+    // ---- stage K (with row norms) and V
+    stage_tile<T, C, KD, LDK, 256>(Ks, k + (r0 * H + hk) * (int64_t)KD, (int64_t)H * KD, n, s_rk);
+    stage_tile<T, C, VD, LDV, 256>(Vs, v + (r0 * HV + hv) * (int64_t)VD, (int64_t)HV * VD, n, nullptr);
+    if (wv == 0) {
+        const int64_t e = r0 + lane;
+        const bool in = lane < n;
+        const float b = in ? beta[e * HV + hv] : 0.f;
+        const float lg_decay = (in && (e % M) == 0) ? g[(e / M) * HV + hv] : 0.f;
+        const float gam = wave_inclusive_sum(lg_decay);
+        s_beta[lane] = b;
+        s_gam[lane] = gam;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const float rk = 1.0f / sqrtf(s_rk[lane] + 1e-6f);
+        s_rk[lane] = rk;
+        s_ws[lane] = s_beta[lane] * __expf(s_gam[lane]) * rk;
+        if (lane < n && (hv % (HV / H)) == 0) k_rnorm[(r0 + lane) * H + hk] = rk;
+    }
+    __syncthreads();
+
+    // ---- L = strictly lower beta_a exp(g_a - g_b) r_a r_b (K K^T)_ab, row block wv
+    {
+        const int ra = 16 * wv;
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 acc = zero4();
+            if (ct <= wv) {
+#pragma unroll
+                for (int ks = 0; ks < KD / 32; ++ks) {
+                    FragT a = lds_row8<T>(Ks + (ra + lc) * LDK + 32 * ks + 8 * lg);
+                    FragT b = lds_row8<T>(Ks + (16 * ct + lc) * LDK + 32 * ks + 8 * lg);
+                    acc = mma(a, b, acc);
+                }
+            }
+            const int col = 16 * ct + lc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = ra + 4 * lg + i;
+                float val = 0.f;
+                if (col < row)
+                    val = s_beta[row] * __expf(s_gam[row] - s_gam[col]) * s_rk[row] * s_rk[col] * acc[i];
+                Lm[row * LDA + col] = val;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- diagonal 16x16 blocks of A by forward substitution (lane = column)
+    {
+        const int d0 = 16 * wv;
+        if (lane < 16) {
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+                for (int b = 0; b < i; ++b) s -= Lm[(d0 + i) * LDA + d0 + b] * x[b];
+                x[i] = s;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Am[(d0 + i) * LDA + d0 + lane] = x[i];
+        }
+        // zero the strictly-upper blocks of this block row
+        for (int idx = lane; idx < 16 * (C - d0 - 16); idx += 64) {
+            const int r = idx / (C - d0 - 16), cc = idx % (C - d0 - 16);
+            Am[(d0 + r) * LDA + d0 + 16 + cc] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- off-diagonal blocks, level by level:
+    //   T_ij = sum_{j<=m<i} L_im A_mj ;  A_ij = -A_ii T_ij
+    // fp32 MFMA 16x16x4; T stays in registers and feeds the second product:
+    // slot s of lane (g,c) holds T[4g+s][c], so step s contracts over rows
+    // {4g+s} and reads A_ii[row][4g+s].
+    for (int lev = 1; lev < 4; ++lev) {
+        if (wv < 4 - lev) {
+            const int j = wv, i = wv + lev;
+            f32x4 t = zero4();
+            for (int m = j; m < i; ++m) {
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4) {
+                    const float a = Lm[(16 * i + lc) * LDA + 16 * m + k0 + lg];
+                    const float b = Am[(16 * m + k0 + lg) * LDA + 16 * j + lc];
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+                }
+            }
+            f32x4 r = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float a = Am[(16 * i + lc) * LDA + 16 * i + 4 * lg + s];
+                r = __builtin_amdgcn_mfma_f32_16x16x4f32(a, t[s], r, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Am[(16 * i + 4 * lg + q) * LDA + 16 * j + lc] = -r[q];
+        }
+        __syncthreads();
+    }
+
+    // ---- u^T = V^T (A diag(beta))^T and w^T = Khat^T (A diag(beta e^gamma r))^T
+    //      wave wv produces output rows a in [16 wv, 16 wv + 16)
+    {
+        const int a_row = 16 * wv + lc;  // output row this lane's B fragment covers
+        const int nks = (wv >= 2) ? 2 : 1;  // contraction tiles with any b <= a
+        FragT bu[2], bw[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks < nks) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int b = 32 * ks + 8 * lg + m;
+                    const float av = Am[a_row * LDA + b];
+                    bu[ks][m] = from_f32<T>(av * s_beta[b]);
+                    bw[ks][m] = from_f32<T>(av * s_ws[b]);
+                }
+            }
+        }
+        const bool row_ok = a_row < n;
+        const int64_t grow = r0 + a_row;
+#pragma unroll
+        for (int vt = 0; vt < VD / 16; ++vt) {
+            f32x4 acc = zero4();
+            for (int ks = 0; ks < nks; ++ks) {
+                FragT a = lds_col8<T>(Vs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * vt);
+                acc = mma(a, bu[ks], acc);
+            }
+            if (row_ok) {
+                T *dst = u + (grow * HV + hv) * (int64_t)VD + 16 * vt + 4 * lg;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = from_f32<T>(acc[q]);
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < KD / 16; ++kt) {
+            f32x4 acc = zero4();
+            for (int ks = 0; ks < nks; ++ks) {
+                FragT a = lds_col8<T>(Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * kt);
+                acc = mma(a, bw[ks], acc);
+            }
+            if (row_ok) {
+                T *dst = w + (grow * HV + hv) * (int64_t)KD + 16 * kt + 4 * lg;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[q] = from_f32<T>(acc[q]);
+            }
+        }
+    }
+}
+
+template <typename T, int KD, int VD>
+static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream) {
+    const gdp_chunk_args &a = p.a;
+    dim3 grid((unsigned)p.max_items, (unsigned)a.HV);
+    hipLaunchKernelGGL((gdp_wy_k<T, KD, VD>), grid, dim3(256), 0, stream,
+                       (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
+                       a.H, a.HV, a.M, a.k_rnorm, (T *)a.w, (T *)a.u);
+    return hipGetLastError();
+}
+
+// bf16: K in {64, 128} x V in {64, 128, 256}; f32 (small-case reference
+// precision): K = 64, V in {64, 128}.
+static hipError_t launch_wy_bf16(const ChunkParams &p, hipStream_t stream) {
+    const int K = p.a.K, V = p.a.V;
+    if (K == 64 && V == 64) return launch_wy_t<bf16, 64, 64>(p, stream);
+    if (K == 64 && V == 128) return launch_wy_t<bf16, 64, 128>(p, stream);
+    if (K == 64 && V == 256) return launch_wy_t<bf16, 64, 256>(p, stream);
+    if (K == 128 && V == 64) return launch_wy_t<bf16, 128, 64>(p, stream);
+    if (K == 128 && V == 128) return launch_wy_t<bf16, 128, 128>(p, stream);
+    if (K == 128 && V == 256) return launch_wy_t<bf16, 128, 256>(p, stream);
+    return hipErrorInvalidValue;
+}
+static hipError_t launch_wy_f32(const ChunkParams &p, hipStream_t stream) {
+    const int K = p.a.K, V = p.a.V;
+    if (K == 64 && V == 64) return launch_wy_t<float, 64, 64>(p, stream);
+    if (K == 64 && V == 128) return launch_wy_t<float, 64, 128>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_wy(const ChunkParams &p, hipStream_t stream) {
+    if (p.max_items == 0) return hipSuccess;
+    return p.a.dtype == GDP_BF16 ? launch_wy_bf16(p, stream) : launch_wy_f32(p, stream);
+}
+
+}  // namespace gdp

@@ -1,0 +1,184 @@
+/*
+ * gdp.h -- C ABI of the MI355X (gfx950) chunked Gated Delta Product forward.
+ *
+ * Operations (names follow the Megatron-Core GDP op pages):
+ *   gdp_prefill_prepare  split / GQA-expand / Householder-fold / gate a prefill
+ *                        step (core.ssm.ops.gdp.prepare, gdp_prefill_prepare)
+ *   gdp_recompute_w_u    per-chunk WY factors: L2 norm of k, within-chunk
+ *                        cumulative decay, the strictly-lower transition
+ *                        block, its unit-lower inverse, then w and u
+ *                        (core.ssm.ops.gdp.wy_fast, recompute_w_u_fwd)
+ *   gdp_chunk_h          inter-chunk state recurrence: state at every chunk
+ *                        boundary and the corrected values (the chunk_h stage
+ *                        named by core.ssm.ops.gdp.chunk_o)
+ *   gdp_chunk_o          output from the boundary state plus causal in-chunk
+ *                        attention summed over the Householder copies
+ *                        (core.ssm.ops.gdp.chunk_o,
+ *                        chunk_gated_delta_product_fwd_o)
+ *   gdp_chunk_fwd        the three chunk stages in order
+ *
+ * Conventions shared by every entry point
+ *   * All tensor pointers are device pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises; each call only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL is the null stream) and
+ *     returns.  Shapes are runtime values, so calls can be captured into a
+ *     HIP graph.
+ *   * Every call validates its arguments before launching anything.  A bad
+ *     argument returns GDP_ERR_INVALID or GDP_ERR_UNSUPPORTED with nothing
+ *     launched and nothing written; gdp_last_error() then describes it.  A
+ *     failed launch returns GDP_ERR_HIP.
+ *   * Results are deterministic: no atomics, every output element is owned
+ *     by exactly one thread, and the order of every reduction is fixed.
+ *   * Tensors are row-major and contiguous unless a stride is given.
+ *   * "Expanded stream": the Householder copies folded into the sequence
+ *     dimension; copy j of token t is row t*M + j.
+ */
+#ifndef GDP_H
+#define GDP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdp_status {
+    GDP_OK = 0,
+    GDP_ERR_INVALID = 1,      /* inconsistent or out-of-range argument */
+    GDP_ERR_UNSUPPORTED = 2,  /* valid but not built (head dims, M, chunk) */
+    GDP_ERR_HIP = 3           /* a HIP launch failed */
+} gdp_status;
+
+typedef enum gdp_dtype {
+    GDP_F32 = 0,
+    GDP_BF16 = 1
+} gdp_dtype;
+
+/*
+ * gdp_prefill_prepare -- one launch that turns the post-conv activations of a
+ * prefill step into the inputs of the chunk forward
+ * (core.ssm.ops.gdp.prepare: module description, gdp_prefill_prepare).
+ *
+ *   x     [n, T, M*H*P + M*G*N + G*N]  dtype; value (M,H,P) | key (M,G,N) |
+ *         query (G,N) along the last dimension.  Element (b, t, c) is at
+ *         x + b*x_n_stride + t*x_t_stride + c (strides in elements; the last
+ *         dimension must be contiguous).
+ *   ba    [n, T, M*H + H]              dtype; b (M,H) | a (H), strides as x.
+ *   A_log, dt_bias [H]                 float32.
+ *   Outputs (contiguous, caller-allocated):
+ *   q     [n, T,   H, N]   dtype   q[b,t,h]      = query group h/(H/G)
+ *   k     [n, T*M, H, N]   dtype   k[b,t*M+j,h]  = key copy j, group h/(H/G)
+ *   v     [n, T*M, H, P]   dtype   v[b,t*M+j,h]  = value copy j, head h
+ *   beta  [n, T*M, H]      float32 sigmoid(b[t, j, h])
+ *   g     [n, T,   H]      float32 -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ * softplus(s) is s for s > 20, else log1p(exp(s)).  Gate arithmetic is
+ * float32 per operation in the order written, with exp and log1p evaluated
+ * in float64 and rounded once.  The L2 norm of q and k is left to the chunk
+ * forward.  Requires H % G == 0 and n, T >= 0 (T == 0 launches nothing).
+ */
+gdp_status gdp_prefill_prepare(
+    const void *x, int64_t x_n_stride, int64_t x_t_stride,
+    const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
+    const float *A_log, const float *dt_bias,
+    int64_t n, int64_t T, int32_t M, int32_t H, int32_t G, int32_t P, int32_t N,
+    gdp_dtype dtype,
+    void *q, void *k, void *v, float *beta, float *g,
+    void *stream);
+
+/*
+ * Arguments of the chunk stages.  Sizes:
+ *   B           batch rows.  Without cu_seqlens every row is one sequence of
+ *               T tokens; with cu_seqlens B must be 1 and the T tokens are
+ *               packed requests (dynamic-batching prefill,
+ *               core.ssm.ops.gdp.prepare, gdp_prefill_prepare).
+ *   T           tokens per batch row (the packed total with cu_seqlens).
+ *   H, HV       query/key heads and value/output heads; HV % H == 0 and
+ *               value head hv reads key head hv / (HV/H)
+ *               (core.ssm.ops.gdp.wy_fast, recompute_w_u_fwd, Parameters).
+ *   K, V        key and value head dims; K in {64, 128}, V in {64, 128, 256}.
+ *   M           Householder copies, 1..4.
+ *   chunk_size  64 (rows of the expanded stream per chunk).
+ *   scale       output scale; <= 0 selects 1/sqrt(K).
+ *   cu_seqlens  device int32 [num_seqs + 1], token offsets of the requests
+ *               on the unexpanded stream, or NULL.  Offsets are clamped into
+ *               [0, T] on the device; a non-monotone array gives undefined
+ *               results but never an out-of-bounds access.
+ *   h_chunks    number of chunks h can hold (see gdp_num_state_chunks); h is
+ *               written only below it.
+ * Tensors (dtype unless noted; e = expanded row):
+ *   q      [B, T,   H,  K]  in
+ *   k      [B, T*M, H,  K]  in
+ *   v      [B, T*M, HV, V]  in
+ *   beta   [B, T*M, HV]     in, float32
+ *   g      [B, T,   HV]     in, float32 natural-log decay per token; it acts
+ *                           on copy 0 of its token
+ *   k_rnorm[B, T*M, H]      float32 1/sqrt(sum k^2 + 1e-6) per key row;
+ *                           written by gdp_recompute_w_u, read by gdp_chunk_h
+ *                           and gdp_chunk_o
+ *   w      [B, T*M, HV, K]  out of gdp_recompute_w_u (effective keys)
+ *   u      [B, T*M, HV, V]  out of gdp_recompute_w_u (effective values)
+ *   v_new  [B, T*M, HV, V]  out of gdp_chunk_h (corrected values)
+ *   h      [h_chunks, HV, V, K]  out of gdp_chunk_h: the V x K state S
+ *                           entering each chunk (S maps a normalised key to a
+ *                           value); chunk c of sequence i is at index
+ *                           (chunks of sequences < i) + c
+ *   o      [B, T,   HV, V]  out of gdp_chunk_o
+ */
+typedef struct gdp_chunk_args {
+    int64_t B;
+    int64_t T;
+    int32_t H;
+    int32_t HV;
+    int32_t K;
+    int32_t V;
+    int32_t M;
+    int32_t chunk_size;
+    float scale;
+    gdp_dtype dtype;
+    const int32_t *cu_seqlens;
+    int64_t num_seqs;
+    int64_t h_chunks;
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *beta;
+    const float *g;
+    float *k_rnorm;
+    void *w;
+    void *u;
+    void *v_new;
+    void *h;
+    void *o;
+} gdp_chunk_args;
+
+/* w, u and k_rnorm from q/k/v/beta/g (reads k, v, beta, g). */
+gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream);
+/* h and v_new from k, k_rnorm, w, u, g.  One serial pass per sequence and
+   value head over its chunks. */
+gdp_status gdp_chunk_h(const gdp_chunk_args *a, void *stream);
+/* o from q, k, k_rnorm, v_new, h, g. */
+gdp_status gdp_chunk_o(const gdp_chunk_args *a, void *stream);
+/* gdp_recompute_w_u, gdp_chunk_h, gdp_chunk_o in order on one stream. */
+gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
+
+/*
+ * Number of state chunks h must hold: sum over sequences of
+ * ceil(len * M / chunk_size).  With cu_seqlens_host == NULL it is
+ * B * ceil(T * M / chunk_size).  cu_seqlens_host is a host copy of the
+ * offsets.  Returns -1 on bad arguments.  ceil(T*M/chunk_size) + num_seqs is
+ * always enough and needs no copy of the offsets.
+ */
+int64_t gdp_num_state_chunks(const int32_t *cu_seqlens_host, int64_t num_seqs,
+                             int64_t B, int64_t T, int32_t M, int32_t chunk_size);
+
+/* Message describing the last non-OK status of this thread ("" if none). */
+const char *gdp_last_error(void);
+
+/* Library version string. */
+const char *gdp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDP_H */

@@ -1,0 +1,149 @@
+"""CPU checks of the C ABI: the header compiles as C99, libgdp.so exports
+every function the header declares, the ctypes mirror of gdp_chunk_args has
+the C layout, and argument validation rejects bad calls before any launch (so
+no GPU is touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_product_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdp.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdp_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_compiles_as_c99(tmp_path):
+    c = tmp_path / "t.c"
+    c.write_text('#include "gdp.h"\nint main(void){ gdp_chunk_args a; (void)a; return 0; }\n')
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                           "-I", os.path.join(ROOT, "include"), str(c)])
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o",
+            "gdp_chunk_fwd", "gdp_num_state_chunks", "gdp_last_error", "gdp_version"} <= set(names)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.check_output(["nm", "-D", "--defined-only", B.LIB_PATH], text=True)
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in B.ChunkArgs._fields_]
+    prog = '#include <stdio.h>\n#include <stddef.h>\n#include "gdp.h"\nint main(void){\n'
+    prog += 'printf("%zu\\n", sizeof(gdp_chunk_args));\n'
+    for f in fields:
+        prog += 'printf("%%zu\\n", offsetof(gdp_chunk_args, %s));\n' % f
+    prog += "return 0;}\n"
+    c = tmp_path / "layout.c"
+    c.write_text(prog)
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)])
+    vals = [int(x) for x in subprocess.check_output([str(exe)], text=True).split()]
+    assert vals[0] == ctypes.sizeof(B.ChunkArgs)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(B.ChunkArgs, f).offset == off, f
+
+
+def test_version_string():
+    assert "gfx950" in B.version()
+
+
+def _args(**kw):
+    base = dict(B=1, T=128, H=2, HV=2, K=64, V=64, M=1, chunk_size=64, scale=0.0, dtype=B.GDP_BF16,
+                cu_seqlens=None, num_seqs=0, h_chunks=2,
+                q=0x10000, k=0x20000, v=0x30000, beta=0x40000, g=0x50000, k_rnorm=0x60000,
+                w=0x70000, u=0x80000, v_new=0x90000, h=0xA0000, o=0xB0000)
+    base.update(kw)
+    return B.ChunkArgs(**base)
+
+
+# Every case fails validation, so nothing reaches the HIP runtime.
+BAD_CHUNK = [
+    ("M=5", dict(M=5), B.GDP_ERR_UNSUPPORTED),
+    ("M=0", dict(M=0), B.GDP_ERR_UNSUPPORTED),
+    ("chunk 32", dict(chunk_size=32), B.GDP_ERR_UNSUPPORTED),
+    ("K=96", dict(K=96), B.GDP_ERR_UNSUPPORTED),
+    ("V=512", dict(V=512), B.GDP_ERR_UNSUPPORTED),
+    ("f32 K=128", dict(dtype=B.GDP_F32, K=128), B.GDP_ERR_UNSUPPORTED),
+    ("HV % H", dict(H=2, HV=3), B.GDP_ERR_INVALID),
+    ("H=0", dict(H=0), B.GDP_ERR_INVALID),
+    ("dtype", dict(dtype=7), B.GDP_ERR_INVALID),
+    ("B<0", dict(B=-1), B.GDP_ERR_INVALID),
+    ("varlen B=2", dict(B=2, cu_seqlens=0x1000, num_seqs=2), B.GDP_ERR_INVALID),
+    ("h too small", dict(h_chunks=1), B.GDP_ERR_INVALID),
+    ("null k", dict(k=None), B.GDP_ERR_INVALID),
+    ("misaligned v", dict(v=0x30008), B.GDP_ERR_INVALID),
+    ("nan scale", dict(scale=float("nan")), B.GDP_ERR_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_CHUNK, ids=[c[0] for c in BAD_CHUNK])
+def test_chunk_fwd_rejects(name, kw, status):
+    a = _args(**kw)
+    st = B.lib().gdp_chunk_fwd(ctypes.byref(a), None)
+    assert st == status, (st, B.lib().gdp_last_error())
+    assert B.lib().gdp_last_error()
+
+
+def test_stage_specific_requirements():
+    # chunk_o needs q and o but not v/beta/w/u; recompute_w_u needs v and beta
+    L = B.lib()
+    assert L.gdp_chunk_o(ctypes.byref(_args(q=None)), None) == B.GDP_ERR_INVALID
+    assert L.gdp_recompute_w_u(ctypes.byref(_args(beta=None)), None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_h(ctypes.byref(_args(u=None)), None) == B.GDP_ERR_INVALID
+
+
+def test_null_args_rejected():
+    assert B.lib().gdp_chunk_fwd(None, None) == B.GDP_ERR_INVALID
+
+
+def test_empty_problem_launches_nothing():
+    # T == 0: valid, returns OK without touching the GPU
+    a = _args(T=0, q=None, k=None, v=None, beta=None, g=None, k_rnorm=None, w=None, u=None,
+              v_new=None, h=None, o=None, h_chunks=0)
+    assert B.lib().gdp_chunk_fwd(ctypes.byref(a), None) == B.GDP_OK
+
+
+def _prep(**kw):
+    base = dict(x=0x10000, xn=0, xt=5632, ba=0x20000, bn=0, bt=48, A_log=0x30000, dt_bias=0x40000,
+                n=1, T=16, M=2, H=16, G=4, P=128, N=128, dtype=B.GDP_BF16,
+                q=0x50000, k=0x60000, v=0x70000, beta=0x80000, g=0x90000)
+    base.update(kw)
+    b = base
+    return B.lib().gdp_prefill_prepare(b["x"], b["xn"], b["xt"], b["ba"], b["bn"], b["bt"], b["A_log"],
+                                       b["dt_bias"], b["n"], b["T"], b["M"], b["H"], b["G"], b["P"],
+                                       b["N"], b["dtype"], b["q"], b["k"], b["v"], b["beta"], b["g"], None)
+
+
+def test_prepare_rejects():
+    assert _prep(G=3) == B.GDP_ERR_INVALID          # H % G
+    assert _prep(M=0) == B.GDP_ERR_INVALID
+    assert _prep(dtype=5) == B.GDP_ERR_INVALID
+    assert _prep(q=None) == B.GDP_ERR_INVALID
+    assert _prep(xt=100) == B.GDP_ERR_INVALID       # rows would overlap
+    assert _prep(T=-1) == B.GDP_ERR_INVALID
+    assert _prep(T=0, x=None) == B.GDP_OK           # empty: nothing launched
+
+
+def test_num_state_chunks():
+    assert B.num_state_chunks(1000, 2, B=3) == 3 * 32
+    cu = [0, 1, 64, 64, 200]   # lengths 1, 63, 0, 136
+    M = 3
+    expect = sum(-(-(l * M) // 64) for l in (1, 63, 0, 136))
+    assert B.num_state_chunks(200, M, cu_seqlens_host=cu) == expect
+    # offsets are clamped into [0, T]
+    assert B.num_state_chunks(100, 1, cu_seqlens_host=[0, 500]) == 2
+    assert B.lib().gdp_num_state_chunks(None, 0, 1, -1, 1, 64) == -1

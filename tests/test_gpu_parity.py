@@ -1,0 +1,375 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Small workloads are compared on every (sequence, value head); the long and
+wide workloads on sampled heads that the oracle runs end to end.  Tolerances:
+prepare copies bit-exact and gates within 1 ulp; chunk outputs within relative
+L2 5e-3 and max-abs 2e-2 (bf16 inputs, fp32 accumulation) -- raw for o, and
+beyond each element's half-ulp bf16 storage quantum for the bf16 intermediates
+w, u, v_new and h, whose values reach ~10."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import prepare as OP
+from gated_delta_product_amd import binding as G
+from gated_delta_product_amd import synth
+from helpers import TOL, Acc, f32, gates, log, oracle_pair, run_pairs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _ulps(a, b):
+    ai = a.view(np.int32).astype(np.int64)
+    bi = b.view(np.int32).astype(np.int64)
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)
+
+
+# ---------------------------------------------------------------------- chunk
+
+def _seqs_equal(B, T, M):
+    nte = math.ceil(T * M / 64)
+    return [(b, 0, T, b * nte) for b in range(B)]
+
+
+def _seqs_varlen(cu, M):
+    out, base = [], 0
+    for i in range(len(cu) - 1):
+        t0, t1 = int(cu[i]), int(cu[i + 1])
+        out.append((0, t0, t1, base))
+        base += math.ceil((t1 - t0) * M / 64)
+    return out
+
+
+def check_chunk(q, k, v, beta, g, seqs, hv_list, M, scale=None, cu=None, cu_host=None, tag="",
+                want_wu=True, buf=None):
+    """Run the GPU forward (unless buf is given) and compare o, v_new, h, w, u
+    with the oracle on the listed (sequence, value head) pairs."""
+    dt = q.dtype
+    tol = TOL[dt]
+    H, HV, K = q.shape[2], v.shape[2], q.shape[3]
+    if buf is None:
+        buf = G.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), g.to(DEV), scale=scale,
+                          cu_seqlens=None if cu is None else torch.as_tensor(cu, dtype=torch.int32).to(DEV),
+                          cu_seqlens_host=cu_host)
+        torch.cuda.synchronize()
+    sc = scale if scale is not None else 1.0 / math.sqrt(K)
+    items = [(s, hv) for s in seqs for hv in hv_list if s[2] > s[1]]
+    log("%s: %d (seq, head) pairs" % (tag, len(items)))
+
+    def one(item):
+        (b, t0, t1, hbase), hv = item
+        hk = hv // (HV // H)
+        qn = f32(q[b, t0:t1, hk])
+        kn = f32(k[b, t0 * M:t1 * M, hk])
+        vn = f32(v[b, t0 * M:t1 * M, hv])
+        bn = f32(beta[b, t0 * M:t1 * M, hv])
+        gn = f32(g[b, t0:t1, hv])
+        return oracle_pair(qn, kn, vn, bn, gn, M, sc, want_wu)
+
+    refs = run_pairs(one, items)
+    accs = {n: Acc(n, raw_max_abs=(n == "o")) for n in (["o", "v_new", "h", "w", "u"] if want_wu
+                                                        else ["o", "v_new", "h"])}
+    bf = dt == torch.bfloat16
+    for ((b, t0, t1, hbase), hv), r in zip(items, refs):
+        nc = math.ceil((t1 - t0) * M / 64)
+        accs["o"].add(f32(buf.o[b, t0:t1, hv]), r["o"], bf)
+        accs["v_new"].add(f32(buf.v_new[b, t0 * M:t1 * M, hv]), r["v_new"], bf)
+        accs["h"].add(f32(buf.h[hbase:hbase + nc, hv]), r["h"], bf)
+        if want_wu:
+            accs["w"].add(f32(buf.w[b, t0 * M:t1 * M, hv]), r["w"], bf)
+            accs["u"].add(f32(buf.u[b, t0 * M:t1 * M, hv]), r["u"], bf)
+    for a in accs.values():
+        a.check(tol)
+    return buf
+
+
+def _cfg_inputs(cfg):
+    d = synth.config_chunk_draws(cfg)
+    beta, g = gates(d)
+    c = synth.CONFIGS[cfg]
+    beta = beta.reshape(c["B"], c["T"] * c["M"], c["HV"])
+    return d, beta, g
+
+
+def test_chunk_tiny_f32():
+    """B=1, T=128, H=HV=2, K=V=64, M=1, float32: every output, every head."""
+    c = synth.CONFIGS[1]
+    d, beta, g = _cfg_inputs(1)
+    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(c["B"], c["T"], c["M"]), range(c["HV"]),
+                c["M"], tag="tiny_f32")
+
+
+def test_chunk_householder_m2():
+    """B=2, T=1024, H=HV=8, K=V=128, M=2, bf16: every output, every head."""
+    c = synth.CONFIGS[2]
+    d, beta, g = _cfg_inputs(2)
+    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(c["B"], c["T"], c["M"]), range(c["HV"]),
+                c["M"], tag="householder_m2")
+
+
+def test_chunk_long_prefill_sampled():
+    """B=1, T=32768, H=HV=16, K=V=128, M=2 (the timed workload): the whole
+    sequence on sampled heads."""
+    c = synth.CONFIGS[4]
+    d, beta, g = _cfg_inputs(4)
+    log("long_prefill: inputs drawn")
+    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(c["B"], c["T"], c["M"]), [0, 9, 15],
+                c["M"], tag="long_prefill_32k")
+
+
+def test_chunk_wide_head_stress_sampled():
+    """B=4, T=8192, H=HV=32, K=128, V=256, M=3, extreme gates (planted on
+    batch 0 / head 0): sampled (batch row, head) pairs."""
+    c = synth.CONFIGS[5]
+    d, beta, g = _cfg_inputs(5)
+    log("wide_head: inputs drawn; g range [%.1f, %.1f]" % (float(g.min()), float(g.max())))
+    seqs = _seqs_equal(c["B"], c["T"], c["M"])
+    buf = None
+    for srow, hvs in ((0, [0]), (3, [31]), (1, [17])):
+        buf = check_chunk(d["q"], d["k"], d["v"], beta, g, [seqs[srow]], hvs, c["M"], tag="wide_head",
+                          buf=buf)
+
+
+def test_chunk_ragged_and_degenerate():
+    """Ragged tails (T*M not a multiple of 64), M=3 and M=4, T=1, and the
+    degenerate gates: beta=0 (no writes: v_new = 0, o = 0), g=0 (no decay),
+    long memory (|g| ~ 1e-3) so the state carries over many chunks."""
+    cases = [
+        dict(B=2, T=100, H=2, HV=4, K=64, V=128, M=3, seed=11),
+        dict(B=1, T=1, H=1, HV=1, K=128, V=64, M=2, seed=12),
+        dict(B=1, T=77, H=2, HV=2, K=128, V=256, M=4, seed=13),
+        dict(B=1, T=300, H=1, HV=2, K=64, V=64, M=1, seed=14),
+    ]
+    for cs in cases:
+        d = synth.chunk_draws(cs["B"], cs["T"], cs["H"], cs["HV"], cs["K"], cs["V"], cs["M"], "bf16",
+                              cs["seed"])
+        beta, g = gates(d)
+        check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(cs["B"], cs["T"], cs["M"]), range(cs["HV"]),
+                    cs["M"], tag="ragged %s" % cs)
+    # degenerate gates on one shape
+    B_, T, H, HV, K, V, M = 1, 200, 2, 2, 128, 128, 2
+    d = synth.chunk_draws(B_, T, H, HV, K, V, M, "bf16", 21)
+    beta, g = gates(d)
+    buf = G.chunk_fwd(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), torch.zeros_like(beta).to(DEV),
+                      g.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(buf.v_new).item() == 0 and torch.count_nonzero(buf.o).item() == 0
+    check_chunk(d["q"], d["k"], d["v"], beta, torch.zeros_like(g), _seqs_equal(B_, T, M), range(HV), M,
+                tag="no decay")
+    dl = synth.chunk_draws(B_, T, H, HV, K, V, M, "bf16", 22)
+    dl["dt_bias"] = torch.empty(HV).uniform_(-9, -7, generator=torch.Generator().manual_seed(5))
+    beta, g = gates(dl)
+    check_chunk(dl["q"], dl["k"], dl["v"], beta, g, _seqs_equal(B_, T, M), range(HV), M, tag="long memory")
+
+
+def test_chunk_determinism():
+    c = synth.CONFIGS[2]
+    d, beta, g = _cfg_inputs(2)
+    args = [t.to(DEV) for t in (d["q"], d["k"], d["v"], beta, g)]
+    b1 = G.chunk_fwd(*args)
+    b2 = G.chunk_fwd(*args)
+    torch.cuda.synchronize()
+    for n in ("o", "w", "u", "v_new", "h", "k_rnorm"):
+        assert torch.equal(getattr(b1, n), getattr(b2, n)), n
+
+
+def test_stages_match_fused_call():
+    """Calling recompute_w_u, chunk_h and chunk_o one by one gives the same
+    bytes as gdp_chunk_fwd."""
+    d = synth.chunk_draws(2, 200, 2, 4, 128, 128, 2, "bf16", 31)
+    beta, g = gates(d)
+    args = [t.to(DEV) for t in (d["q"], d["k"], d["v"], beta, g)]
+    b1 = G.chunk_fwd(*args)
+    b2 = G.ChunkBuffers(*args)
+    b2.recompute_w_u()
+    b2.chunk_h()
+    b2.chunk_o()
+    torch.cuda.synchronize()
+    for n in ("o", "w", "u", "v_new", "h"):
+        assert torch.equal(getattr(b1, n), getattr(b2, n)), n
+
+
+def test_chunk_o_alone_on_oracle_state():
+    """chunk_o fed with the oracle's own boundary states and corrected values
+    (rounded to bf16) reproduces the oracle output: isolates the output stage."""
+    B_, T, H, HV, K, V, M = 1, 256, 2, 2, 128, 128, 3
+    d = synth.chunk_draws(B_, T, H, HV, K, V, M, "bf16", 41)
+    beta, g = gates(d)
+    args = [t.to(DEV) for t in (d["q"], d["k"], d["v"], beta, g)]
+    buf = G.ChunkBuffers(*args)
+    buf.recompute_w_u()  # k_rnorm
+    sc = 1.0 / math.sqrt(K)
+    h_ref = torch.empty_like(buf.h, device="cpu")
+    vn_ref = torch.empty_like(buf.v_new, device="cpu")
+    refs = []
+    for hv in range(HV):
+        hk = hv // (HV // H)
+        r = oracle.recurrence(f32(d["q"][0, :, hk]), f32(d["k"][0, :, hk]), f32(d["v"][0, :, hv]),
+                              f32(beta[0, :, hv]), f32(g[0, :, hv]), M, scale=sc)
+        h_ref[:, hv] = torch.from_numpy(r["h"]).to(torch.bfloat16)
+        vn_ref[0, :, hv] = torch.from_numpy(r["v_new"]).to(torch.bfloat16)
+        refs.append(r)
+    buf.set(h=h_ref.to(DEV), v_new=vn_ref.to(DEV))
+    buf.chunk_o()
+    torch.cuda.synchronize()
+    acc = Acc("o", raw_max_abs=True)
+    for hv in range(HV):
+        acc.add(f32(buf.o[0, :, hv]), refs[hv]["o"])
+    acc.check(TOL[torch.bfloat16])
+
+
+# ---------------------------------------------------------------------- prepare
+
+def _prepare_check(x, ba, A_log, dt_bias, M, H, G_, P, N, tag):
+    q, k, v, beta, g = G.prefill_prepare(x.to(DEV) if not x.is_cuda else x, ba.to(DEV) if not ba.is_cuda else ba,
+                                         A_log.to(DEV), dt_bias.to(DEV), M, H, G_, P, N)
+    torch.cuda.synchronize()
+    rq, rk, rv, rb, rg = OP.prefill_prepare(f32(x), f32(ba), A_log.numpy(), dt_bias.numpy(), M, H, G_, P, N)
+    dt = q.dtype
+    assert torch.equal(q.cpu(), torch.from_numpy(rq).to(dt)), tag + " q"
+    assert torch.equal(k.cpu(), torch.from_numpy(rk).to(dt)), tag + " k"
+    assert torch.equal(v.cpu(), torch.from_numpy(rv).to(dt)), tag + " v"
+    ub = _ulps(beta.cpu().numpy(), rb)
+    ug = _ulps(g.cpu().numpy(), rg)
+    log("%s: beta max ulp %d (%d differ), g max ulp %d (%d differ)" % (
+        tag, ub.max(), (ub > 0).sum(), ug.max(), (ug > 0).sum()))
+    assert ub.max() <= 1 and ug.max() <= 1
+    return q, k, v, beta, g
+
+
+def test_prepare_varlen_prefill():
+    """The packed n == 1 prefill of 8 requests (H=16, G=4, P=N=128, M=2)."""
+    d = synth.varlen_prepare_draws(3)
+    p = synth.CONFIGS[3]["prep"]
+    log("varlen prepare: T=%d, cu_seqlens=%s" % (int(d["cu_seqlens"][-1]), list(d["cu_seqlens"])))
+    _prepare_check(d["x"], d["ba"], d["A_log"], d["dt_bias"], synth.CONFIGS[3]["M"], p["H"], p["G"], p["P"],
+                   p["N"], "varlen_prepare")
+
+
+def test_prepare_gate_edges_planted():
+    """a + dt_bias hits 20 (log1p side), nextafter(20) (identity side), 25,
+    88, -16, -30, -90, -104; b hits 0, 17, 100, -104 and large negatives."""
+    M, H, G_, P, N, T = 2, 2, 1, 8, 8, 8
+    width = M * H * P + M * G_ * N + G_ * N
+    for dtype in (torch.bfloat16, torch.float32):
+        x = torch.randn(1, T, width, generator=torch.Generator().manual_seed(1)).to(dtype)
+        ba = torch.zeros(1, T, M * H + H)
+        a_vals = torch.tensor([20.0, 20.0, 25.0, 88.0, -16.0, -30.0, -90.0, -104.0])
+        ba[0, :, M * H + 0] = a_vals            # head 0: dt_bias 0 -> s = a
+        ba[0, :, M * H + 1] = 20.0               # head 1: dt_bias 2^-19 -> s = nextafter(20)
+        b_vals = torch.tensor([0.0, 17.0, 100.0, -104.0, -20.0, 1.5, -0.75, 88.0])
+        for j in range(M * H):
+            ba[0, :, j] = b_vals
+        ba = ba.to(dtype)
+        A_log = torch.tensor([0.0, math.log(16.0)], dtype=torch.float32)
+        dt_bias = torch.tensor([0.0, 2.0 ** -19], dtype=torch.float32)
+        _, _, _, beta, g = _prepare_check(x, ba, A_log, dt_bias, M, H, G_, P, N, "edges %s" % dtype)
+        s1 = np.float32(20.0) + np.float32(2.0 ** -19)
+        assert s1 == np.nextafter(np.float32(20), np.float32(30))
+        assert g[0, 0, 0].item() == -20.0 and beta[0, 0, 0].item() == 0.5
+
+
+def test_prepare_strided_rows_and_scalar_path():
+    """x as a row-strided view (wider parent rows) and ba as a column slice of
+    a wider tensor give the same results; odd head dims take the element-wise
+    copy path."""
+    M, H, G_, P, N, T = 3, 4, 2, 16, 24, 37
+    width = M * H * P + M * G_ * N + G_ * N
+    gen = torch.Generator().manual_seed(3)
+    parent = torch.randn(2, T, width + 40, generator=gen).to(torch.bfloat16).to(DEV)
+    x = parent[:, :, 8:8 + width]
+    bparent = torch.randn(2, T, M * H + H + 5, generator=gen).to(torch.bfloat16).to(DEV)
+    ba = bparent[:, :, 2:2 + M * H + H]
+    A_log = torch.log(torch.rand(H, generator=gen) * 15 + 1)
+    dt_bias = torch.rand(H, generator=gen) * 2 - 1
+    _prepare_check(x, ba, A_log, dt_bias, M, H, G_, P, N, "strided")
+    P2, N2 = 12, 20  # not multiples of 8 elements: per-element path
+    width2 = M * H * P2 + M * G_ * N2 + G_ * N2
+    x2 = torch.randn(1, T, width2, generator=gen).to(torch.bfloat16)
+    ba2 = torch.randn(1, T, M * H + H, generator=gen).to(torch.bfloat16)
+    _prepare_check(x2, ba2, A_log, dt_bias, M, H, G_, P2, N2, "scalar path")
+
+
+# ---------------------------------------------------------------------- end to end
+
+def test_varlen_gva_end_to_end():
+    """Packed 8-request prefill: GPU prepare then GPU chunk forward with GVA
+    (H=4 query/key heads for HV=16 value heads) against the oracle on every
+    (request, head); the GVA run equals the run on head-expanded q/k, and the
+    packed run equals each request run on its own, bit for bit."""
+    c = synth.CONFIGS[3]
+    p = c["prep"]
+    M = c["M"]
+    d = synth.varlen_prepare_draws(3)
+    cu = d["cu_seqlens"]
+    q, k, v, beta, g = _prepare_check(d["x"], d["ba"], d["A_log"], d["dt_bias"], M, p["H"], p["G"], p["P"],
+                                      p["N"], "e2e prepare")
+    hpg = p["H"] // p["G"]
+    qg = q[:, :, ::hpg].contiguous()   # heads 0, 4, 8, 12 = the G groups
+    kg = k[:, :, ::hpg].contiguous()
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).to(DEV)
+    seqs = _seqs_varlen(cu, M)
+    buf = check_chunk(qg.cpu(), kg.cpu(), v.cpu(), beta.cpu(), g.cpu(), seqs, range(c["HV"]), M, cu=cu,
+                      cu_host=cu, tag="varlen_gva")
+    full = G.chunk_fwd(q, k, v, beta, g, cu_seqlens=cu_d, cu_seqlens_host=cu)
+    torch.cuda.synchronize()
+    for n in ("o", "w", "u", "v_new", "h"):
+        assert torch.equal(getattr(buf, n), getattr(full, n)), "GVA vs expanded: " + n
+    for i, (b, t0, t1, hbase) in enumerate(seqs):
+        one = G.chunk_fwd(qg[:, t0:t1].contiguous(), kg[:, t0 * M:t1 * M].contiguous(),
+                          v[:, t0 * M:t1 * M].contiguous(), beta[:, t0 * M:t1 * M].contiguous(),
+                          g[:, t0:t1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(one.o, buf.o[:, t0:t1]), "request %d o" % i
+        nc = one.h.shape[0]
+        assert torch.equal(one.h, buf.h[hbase:hbase + nc]), "request %d h" % i
+
+
+def test_varlen_empty_and_tiny_requests():
+    """Requests of length 0, 1, 63, 64, 65 packed together (ragged chunks at
+    every request boundary)."""
+    lens = [0, 1, 63, 0, 64, 65, 130]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    M, H, HV, K, V = 3, 2, 4, 64, 64
+    d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", 51)
+    beta, g = gates(d)
+    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_varlen(cu, M), range(HV), M, cu=cu, cu_host=cu,
+                tag="tiny requests")
+
+
+def test_long_prefill_path_with_prepare():
+    """The timed workload's launch configuration: prepare (H=G=16,
+    P=N=128, M=2) feeding the chunk forward at T=32768; the output of
+    sampled heads against the oracle run on the oracle's prepare output."""
+    c = synth.CONFIGS[4]
+    M, H, T = c["M"], c["HV"], c["T"]
+    d = synth.prepare_draws(1, T, M, H, H, c["V"], c["K"], "bf16", synth.seed_of(4) + 100)
+    log("long prepare: inputs drawn")
+    x = d["x"].to(DEV)
+    ba = d["ba"].to(DEV)
+    q, k, v, beta, g = G.prefill_prepare(x, ba, d["A_log"].to(DEV), d["dt_bias"].to(DEV), M, H, H, c["V"], c["K"])
+    buf = G.chunk_fwd(q, k, v, beta, g)
+    torch.cuda.synchronize()
+    # oracle prepare on the sampled heads' slices only
+    xs = f32(d["x"][0])
+    bas = f32(d["ba"][0])
+    P_, N_ = c["V"], c["K"]
+    heads = [0, 13]
+    for hv in heads:
+        vh = np.ascontiguousarray(xs[:, : M * H * P_].reshape(T, M, H, P_)[:, :, hv].reshape(T * M, P_))
+        kh = np.ascontiguousarray(xs[:, M * H * P_: M * H * P_ + M * H * N_].reshape(T, M, H, N_)[:, :, hv]
+                                  .reshape(T * M, N_))
+        qh = np.ascontiguousarray(xs[:, M * H * P_ + M * H * N_:].reshape(T, H, N_)[:, hv])
+        bh = OP.sigmoid_rn32(bas[:, : M * H].reshape(T, M, H)[:, :, hv].reshape(T * M))
+        gh = OP.decay_rn32(bas[:, M * H + hv], d["A_log"].numpy()[hv], d["dt_bias"].numpy()[hv])
+        r = oracle.recurrence(qh, kh, vh, bh, np.ascontiguousarray(gh), M, scale=1.0 / math.sqrt(N_))
+        a = Acc("o[%d]" % hv, raw_max_abs=True)
+        a.add(f32(buf.o[0, :, hv]), r["o"])
+        a.check(TOL[torch.bfloat16])
