@@ -29,7 +29,9 @@ template <> struct Frag<float> { typedef f32x8 type; typedef f32x4 half; };
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index inside the block, known to the compiler as wave-uniform (it
+// can then live in SGPRs and feed buffer descriptors).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------- MFMA
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -121,6 +123,11 @@ __device__ __forceinline__ void seq_bounds(const int32_t *cu, int64_t T, int64_t
 }
 
 __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Exact x / d for 0 <= x < 2^31 and d in [1, 4] (the Householder copy count)
+// with one multiply-high: magic = floor((2^32 - 1) / d) + 1, 0 meaning d = 1.
+__device__ __forceinline__ uint32_t small_div_magic(int d) { return d == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)d + 1u; }
+__device__ __forceinline__ uint32_t small_div(uint32_t x, uint32_t magic) { return magic ? __umulhi(x, magic) : x; }
 
 // Block-cooperative lookup of linear item `id` over sequences, where
 // sequence i owns ceil(len_i * rows_per_token / chunk) consecutive items.
@@ -241,6 +248,77 @@ __device__ __forceinline__ void stage_tile(T *dst, const T *src, int64_t rs, int
             if (cu == 0) ssq[row] = s;
         }
     }
+}
+
+// ---------------------------------------------------------------- buffer access
+// Raw buffer resources: the hardware range check returns zeros for loads
+// past `bytes` and drops stores past it, which handles ragged tails without
+// per-row branches.  Offsets are 32-bit byte offsets from `base`.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, untyped access
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return __builtin_bit_cast(uint4, v);
+}
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint2 v) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, uint4 v) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)off, 0, 0);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, then s_barrier.  Outstanding global loads stay in flight (a
+// plain __syncthreads also drains them).  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------- HBM -> LDS DMA
+// buffer_load ... lds: each lane's 16 (or 4) bytes land at LDS address
+// lds_base + 16*lane (4*lane).  Issued through inline assembly so the
+// compiler does not add its conservative wait-for-everything before later
+// LDS reads; the caller waits with wait_vmcnt<N>() where N counts only DMAs
+// issued after the ones it needs (other vector memory operations in between
+// can only make that wait stricter, never looser, as the counter retires in
+// order).  lds_base must be wave-uniform.  Lanes outside the buffer range do
+// not fetch memory and write zeros.  One wait state separates the M0 write
+// from the DMA that reads it.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voffset, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_base), "v"(voffset), "s"(r) : "memory");
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_base), "v"(voffset), "s"(r) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 32-bit LDS byte address of a __shared__ object.
+template <typename P>
+__device__ __forceinline__ uint32_t lds_addr(const P *p) {
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
 }
 
 }  // namespace gdp

@@ -6,7 +6,7 @@
 //   khat = k / sqrt(sum k^2 + 1e-6)           (L2 norm left to the chunk op,
 //                                               core.ssm.ops.gdp.prepare, Returns)
 //   gamma_e = within-chunk cumulative log decay; a token's decay sits on its
-//             first copy
+//             first copy (also written out in log2 units for chunk_h)
 //   L[a][b] = beta_a exp(gamma_a - gamma_b) khat_a . khat_b   (b < a)
 //   A = (I + L)^-1                             (the solve_tril block)
 //   u = A diag(beta) V                         (effective values)
@@ -36,7 +36,8 @@ template <typename T, int KD, int VD>
 __global__ void __launch_bounds__(256)
 gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ beta,
          const float *__restrict__ g, const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok,
-         int H, int HV, int M, float *__restrict__ k_rnorm, T *__restrict__ w, T *__restrict__ u) {
+         int H, int HV, int M, float *__restrict__ k_rnorm, float *__restrict__ gcum, T *__restrict__ w,
+         T *__restrict__ u) {
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
     constexpr int LDV = VD + Pad<T>::value;
@@ -67,6 +68,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         const float gam = wave_inclusive_sum(lg_decay);
         s_beta[lane] = b;
         s_gam[lane] = gam;
+        if (in) gcum[e * HV + hv] = gam * 1.4426950408889634f;  // log2 units for chunk_h
     }
     __syncthreads();
     if (wv == 0) {
@@ -118,10 +120,14 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 #pragma unroll
             for (int i = 0; i < 16; ++i) Am[(d0 + i) * LDA + d0 + lane] = x[i];
         }
-        // zero the strictly-upper blocks of this block row
-        for (int idx = lane; idx < 16 * (C - d0 - 16); idx += 64) {
-            const int r = idx / (C - d0 - 16), cc = idx % (C - d0 - 16);
-            Am[(d0 + r) * LDA + d0 + 16 + cc] = 0.f;
+        // zero the strictly-upper blocks of this block row (4 values per lane
+        // per 16x16 block)
+#pragma unroll
+        for (int cb = 1; cb < 4; ++cb) {
+            if (cb > wv) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Am[(d0 + 4 * lg + q) * LDA + 16 * cb + lc] = 0.f;
+            }
         }
     }
     __syncthreads();
@@ -178,9 +184,12 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 #pragma unroll
         for (int vt = 0; vt < VD / 16; ++vt) {
             f32x4 acc = zero4();
-            for (int ks = 0; ks < nks; ++ks) {
-                FragT a = lds_col8<T>(Vs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * vt);
-                acc = mma(a, bu[ks], acc);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks < nks) {
+                    FragT a = lds_col8<T>(Vs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * vt);
+                    acc = mma(a, bu[ks], acc);
+                }
             }
             if (row_ok) {
                 T *dst = u + (grow * HV + hv) * (int64_t)VD + 16 * vt + 4 * lg;
@@ -191,9 +200,12 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 #pragma unroll
         for (int kt = 0; kt < KD / 16; ++kt) {
             f32x4 acc = zero4();
-            for (int ks = 0; ks < nks; ++ks) {
-                FragT a = lds_col8<T>(Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * kt);
-                acc = mma(a, bw[ks], acc);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks < nks) {
+                    FragT a = lds_col8<T>(Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * kt);
+                    acc = mma(a, bw[ks], acc);
+                }
             }
             if (row_ok) {
                 T *dst = w + (grow * HV + hv) * (int64_t)KD + 16 * kt + 4 * lg;
@@ -210,7 +222,7 @@ static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream) {
     dim3 grid((unsigned)p.max_items, (unsigned)a.HV);
     hipLaunchKernelGGL((gdp_wy_k<T, KD, VD>), grid, dim3(256), 0, stream,
                        (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
-                       a.H, a.HV, a.M, a.k_rnorm, (T *)a.w, (T *)a.u);
+                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, (T *)a.w, (T *)a.u);
     return hipGetLastError();
 }
 

@@ -115,6 +115,11 @@ gdp_status gdp_prefill_prepare(
  *   k_rnorm[B, T*M, H]      float32 1/sqrt(sum k^2 + 1e-6) per key row;
  *                           written by gdp_recompute_w_u, read by gdp_chunk_h
  *                           and gdp_chunk_o
+ *   gcum   [B, T*M, HV]     float32 within-chunk cumulative decay in log2
+ *                           units per expanded row (the sum of g*log2(e) over
+ *                           the first-copy rows of the chunk up to and
+ *                           including the row); written by gdp_recompute_w_u,
+ *                           read by gdp_chunk_h
  *   w      [B, T*M, HV, K]  out of gdp_recompute_w_u (effective keys)
  *   u      [B, T*M, HV, V]  out of gdp_recompute_w_u (effective values)
  *   v_new  [B, T*M, HV, V]  out of gdp_chunk_h (corrected values)
@@ -144,6 +149,7 @@ typedef struct gdp_chunk_args {
     const float *beta;
     const float *g;
     float *k_rnorm;
+    float *gcum;
     void *w;
     void *u;
     void *v_new;
@@ -151,9 +157,9 @@ typedef struct gdp_chunk_args {
     void *o;
 } gdp_chunk_args;
 
-/* w, u and k_rnorm from q/k/v/beta/g (reads k, v, beta, g). */
+/* w, u, k_rnorm and gcum from k, v, beta, g. */
 gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream);
-/* h and v_new from k, k_rnorm, w, u, g.  One serial pass per sequence and
+/* h and v_new from k, k_rnorm, gcum, w, u.  One serial pass per sequence and
    value head over its chunks. */
 gdp_status gdp_chunk_h(const gdp_chunk_args *a, void *stream);
 /* o from q, k, k_rnorm, v_new, h, g. */
