@@ -17,10 +17,9 @@ HIP events recorded on the launch stream, the roofline of the dominant kernel
 (algorithmic bytes per launch / its average duration vs 8 TB/s HBM) and the
 oracle's throughput on the host cores as a reported baseline.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-mib N]
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -35,18 +34,6 @@ HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(workload="long_prefill_32k", B=1, T=32768, H=16, HV=16, G=16, K=128, V=128, M=2, chunk=64,
                 dtype="bf16", path="prepare+recompute_w_u+chunk_h+chunk_o")
 KERNELS = ["gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o"]
-KERNEL_SRC = {
-    "gdp_prefill_prepare": ["prepare.hip"],
-    "gdp_recompute_w_u": ["wy.hip"],
-    "gdp_chunk_h": ["chunk_h.hip"],
-    "gdp_chunk_o": ["chunk_o.hip"],
-}
-KERNEL_SYMBOL = {  # device kernel names as rocprofv3 reports them
-    "gdp_prefill_prepare": "gdp_prepare_k",
-    "gdp_recompute_w_u": "gdp_wy_k",
-    "gdp_chunk_h": "gdp_chunk_h_k",
-    "gdp_chunk_o": "gdp_chunk_o_k",
-}
 
 
 def algorithmic_bytes(w):
@@ -69,24 +56,17 @@ def algorithmic_bytes(w):
     return {"gdp_prefill_prepare": prep, "gdp_recompute_w_u": wy, "gdp_chunk_h": ch, "gdp_chunk_o": co}
 
 
-def src_digest(kernel):
-    h = hashlib.sha256()
-    for f in KERNEL_SRC[kernel] + ["gdp_common.h"]:
-        with open(os.path.join(ROOT, "gated_delta_product_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
+    from gated_delta_product_amd import profiling
     path = os.path.join(ROOT, "profiles", "traffic_long_prefill_32k.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     e = t.get(kernel)
-    if not e or e.get("src_digest") != src_digest(kernel):
+    if not e or e.get("src_digest") != profiling.src_digest(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -131,6 +111,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB (untimed), "
+                         "the known-size kernel that calibrates rocprofv3 byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -198,6 +181,14 @@ def main():
     achieved = ab[dom] / (ktimes[dom] / 1e3) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom)}
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * 1024 * 1024 // 2
+        src = torch.ones(n, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

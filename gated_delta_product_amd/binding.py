@@ -33,7 +33,7 @@ class ChunkArgs(ctypes.Structure):
         ("M", _i32), ("chunk_size", _i32), ("scale", _f32), ("dtype", ctypes.c_int),
         ("cu_seqlens", _vp), ("num_seqs", _i64), ("h_chunks", _i64),
         ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("g", _vp), ("k_rnorm", _vp),
-        ("gcum", _vp), ("w", _vp), ("u", _vp), ("v_new", _vp), ("h", _vp), ("o", _vp),
+        ("gcum", _vp), ("kdecay", _vp), ("w", _vp), ("u", _vp), ("v_new", _vp), ("h", _vp), ("o", _vp),
     ]
 
 
@@ -209,6 +209,7 @@ class ChunkBuffers:
         self.cu_seqlens = cu_seqlens
         self.k_rnorm = torch.empty((B, T * M, H), dtype=torch.float32, device=dev)
         self.gcum = torch.empty((B, T * M, HV), dtype=torch.float32, device=dev)
+        self.kdecay = torch.empty((B, T * M, HV), dtype=torch.float32, device=dev)
         self.w = torch.empty((B, T * M, HV, K), dtype=dt, device=dev)
         self.u = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
         self.v_new = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
@@ -221,7 +222,7 @@ class ChunkBuffers:
             cu_seqlens=None if cu_seqlens is None else cu_seqlens.data_ptr(),
             num_seqs=nseq, h_chunks=h_chunks,
             q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), beta=beta.data_ptr(), g=g.data_ptr(),
-            k_rnorm=self.k_rnorm.data_ptr(), gcum=self.gcum.data_ptr(), w=self.w.data_ptr(), u=self.u.data_ptr(),
+            k_rnorm=self.k_rnorm.data_ptr(), gcum=self.gcum.data_ptr(), kdecay=self.kdecay.data_ptr(), w=self.w.data_ptr(), u=self.u.data_ptr(),
             v_new=self.v_new.data_ptr(), h=self.h.data_ptr(), o=self.o.data_ptr())
 
     def set(self, **tensors):

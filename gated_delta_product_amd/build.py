@@ -22,9 +22,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
-    # packed fp32 VALU forms stay off (see the design notes)
+    # no packed-fp32 VALU forms (v_pk_{add,mul,fma}_f32): every fp32 op stays scalar
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INCLUDE, "-I" + CSRC,
+    # matrix-core accumulators in VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -86,8 +86,8 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
         const char *name;
     } needs[] = {
         {ST_O, a->q, "q"},           {ST_WY | ST_H | ST_O, a->k, "k"}, {ST_WY, a->v, "v"},
-        {ST_WY, a->beta, "beta"},    {ST_WY | ST_O, a->g, "g"},        {ST_WY | ST_H | ST_O, a->k_rnorm, "k_rnorm"},
-        {ST_WY | ST_H, a->gcum, "gcum"},
+        {ST_WY, a->beta, "beta"},    {ST_WY | ST_O, a->g, "g"},        {ST_WY | ST_O, a->k_rnorm, "k_rnorm"},
+        {ST_WY | ST_H, a->gcum, "gcum"},    {ST_WY | ST_H, a->kdecay, "kdecay"},
         {ST_WY | ST_H, a->w, "w"},   {ST_WY | ST_H, a->u, "u"},        {ST_H | ST_O, a->v_new, "v_new"},
         {ST_H | ST_O, a->h, "h"},    {ST_O, a->o, "o"},
     };

@@ -308,6 +308,16 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint32_t voffset, uint32_t lds_ba
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :: "s"(lds_base), "v"(voffset), "s"(r) : "memory");
 }
+// As dma16 / dma4 with the LDS destination at lds_base + off (off a
+// compile-time constant folded into the M0 write).
+__device__ __forceinline__ void dma16_at(rsrc_t r, uint32_t voffset, uint32_t lds_base, int off) {
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_base), "v"(voffset), "s"(r), "i"(off) : "memory", "scc");
+}
+__device__ __forceinline__ void dma4_at(rsrc_t r, uint32_t voffset, uint32_t lds_base, int off) {
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds_base), "v"(voffset), "s"(r), "i"(off) : "memory", "scc");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

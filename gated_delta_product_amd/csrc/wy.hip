@@ -6,7 +6,8 @@
 //   khat = k / sqrt(sum k^2 + 1e-6)           (L2 norm left to the chunk op,
 //                                               core.ssm.ops.gdp.prepare, Returns)
 //   gamma_e = within-chunk cumulative log decay; a token's decay sits on its
-//             first copy (also written out in log2 units for chunk_h)
+//             first copy (also written out in log2 units for chunk_h, with
+//             kdecay_e = rnorm_e exp(gamma_last - gamma_e))
 //   L[a][b] = beta_a exp(gamma_a - gamma_b) khat_a . khat_b   (b < a)
 //   A = (I + L)^-1                             (the solve_tril block)
 //   u = A diag(beta) V                         (effective values)
@@ -36,7 +37,8 @@ template <typename T, int KD, int VD>
 __global__ void __launch_bounds__(256)
 gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ beta,
          const float *__restrict__ g, const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok,
-         int H, int HV, int M, float *__restrict__ k_rnorm, float *__restrict__ gcum, T *__restrict__ w,
+         int H, int HV, int M, float *__restrict__ k_rnorm, float *__restrict__ gcum,
+         float *__restrict__ kdecay, T *__restrict__ w,
          T *__restrict__ u) {
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
@@ -76,6 +78,11 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         s_rk[lane] = rk;
         s_ws[lane] = s_beta[lane] * __expf(s_gam[lane]) * rk;
         if (lane < n && (hv % (HV / H)) == 0) k_rnorm[(r0 + lane) * H + hk] = rk;
+        if (lane < n) {  // decay of the row's key to the chunk end, times its norm
+            const float g2 = s_gam[lane] * 1.4426950408889634f;
+            const float gl2 = s_gam[n - 1] * 1.4426950408889634f;
+            kdecay[(r0 + lane) * HV + hv] = rk * exp2f(gl2 - g2);
+        }
     }
     __syncthreads();
 
@@ -222,7 +229,7 @@ static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream) {
     dim3 grid((unsigned)p.max_items, (unsigned)a.HV);
     hipLaunchKernelGGL((gdp_wy_k<T, KD, VD>), grid, dim3(256), 0, stream,
                        (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
-                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, (T *)a.w, (T *)a.u);
+                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u);
     return hipGetLastError();
 }
 

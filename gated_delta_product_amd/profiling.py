@@ -1,0 +1,135 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the
+benchmark: per-kernel launch statistics and measured HBM traffic per launch.
+
+    python -m gated_delta_product_amd.profiling stats  STATS_CSV OUT.md  --command "..."
+    python -m gated_delta_product_amd.profiling traffic FETCH_CSV WRITE_CSV OUT.json \
+        --copy-mib 512 --command "..."
+
+Traffic: FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB).  The same run
+contains one plain device copy of a known size, which fixes how many bytes
+one counted KiB stands for (the raw counts need not equal the bytes moved: on
+MI355X the fetch count of a copy reads half of the bytes it copies).  Each
+kernel's bytes per launch = mean over its dispatches of FETCH_SIZE * fetch_factor + WRITE_SIZE * write_factor, with
+fetch_factor = copy bytes / copy FETCH_SIZE and likewise for writes.  The
+JSON records the kernel-source digest it was taken on, so a reader can tell
+when the figure no longer describes the built kernel.
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_product_amd", "csrc")
+
+# host-visible operation -> (device symbol substring, sources that define it)
+KERNELS = {
+    "gdp_prefill_prepare": ("gdp_prepare_k", ["prepare.hip"]),
+    "gdp_recompute_w_u": ("gdp_wy_k", ["wy.hip"]),
+    "gdp_chunk_h": ("gdp_chunk_h_k", ["chunk_h.hip"]),
+    "gdp_chunk_o": ("gdp_chunk_o_k", ["chunk_o.hip"]),
+}
+COPY_SYMBOL = "copyBuffer"
+
+
+def src_digest(op):
+    """Digest of the sources a kernel is built from (its file + the shared header)."""
+    h = hashlib.sha256()
+    for f in KERNELS[op][1] + ["gdp_common.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _op_of(name):
+    for op, (sym, _) in KERNELS.items():
+        if sym in name:
+            return op
+    if COPY_SYMBOL in name:
+        return "copy"
+    return None
+
+
+def read_counter(path, counter):
+    """{op: [value per dispatch]} for one counter of a counter-collection CSV."""
+    out = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            op = _op_of(r["Kernel_Name"])
+            if op:
+                out[op].append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic(fetch_csv, write_csv, copy_mib):
+    fe = read_counter(fetch_csv, "FETCH_SIZE")
+    wr = read_counter(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * 1024 * 1024
+    # the calibration copy is the largest copy dispatch in the run
+    cf, cw = max(fe.get("copy", [0.0])), max(wr.get("copy", [0.0]))
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no calibration copy found in the counter CSVs")
+    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    res = {"_calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+                            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)}}
+    for op in KERNELS:
+        if not fe.get(op) or not wr.get(op):
+            continue
+        f_kib = sum(fe[op]) / len(fe[op])
+        w_kib = sum(wr[op]) / len(wr[op])
+        res[op] = {"fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
+                   "bytes_per_launch": int(round(f_kib * 1024 * ff + w_kib * 1024 * wf)),
+                   "dispatches": [len(fe[op]), len(wr[op])], "src_digest": src_digest(op)}
+    return res
+
+
+def stats_table(stats_csv):
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                         float(r["MaxNs"]), float(r["Percentage"])))
+    lines = ["| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, pct in rows:
+        op = _op_of(name) or name[:60]
+        lines.append("| %s | %d | %.1f | %.1f | %.1f | %.1f |" % (op, calls, avg / 1e3, mn / 1e3, mx / 1e3, pct))
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("stats_csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="Kernel launch statistics")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("out")
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        digests = ", ".join("%s %s" % (op, src_digest(op)) for op in KERNELS)
+        text = "# %s\n\nCommand (run from the repository root on one MI355X):\n\n    %s\n\n%s\n\n" \
+               "Kernel source digests: %s\n" % (a.title, a.command, stats_table(a.stats_csv), digests)
+        with open(a.out, "w") as f:
+            f.write(text)
+    else:
+        res = traffic(a.fetch_csv, a.write_csv, a.copy_mib)
+        res["_command"] = a.command
+        with open(a.out, "w") as f:
+            json.dump(res, f, indent=1, sort_keys=True)
+            f.write("\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -113,13 +113,17 @@ gdp_status gdp_prefill_prepare(
  *   g      [B, T,   HV]     in, float32 natural-log decay per token; it acts
  *                           on copy 0 of its token
  *   k_rnorm[B, T*M, H]      float32 1/sqrt(sum k^2 + 1e-6) per key row;
- *                           written by gdp_recompute_w_u, read by gdp_chunk_h
- *                           and gdp_chunk_o
+ *                           written by gdp_recompute_w_u, read by gdp_chunk_o
  *   gcum   [B, T*M, HV]     float32 within-chunk cumulative decay in log2
  *                           units per expanded row (the sum of g*log2(e) over
  *                           the first-copy rows of the chunk up to and
  *                           including the row); written by gdp_recompute_w_u,
  *                           read by gdp_chunk_h
+ *   kdecay [B, T*M, HV]     float32 per expanded row e of chunk c:
+ *                           k_rnorm[e] * 2^(gcum[last row of c] - gcum[e]),
+ *                           the factor with which the row's normalised key
+ *                           enters the state at the end of its chunk;
+ *                           written by gdp_recompute_w_u, read by gdp_chunk_h
  *   w      [B, T*M, HV, K]  out of gdp_recompute_w_u (effective keys)
  *   u      [B, T*M, HV, V]  out of gdp_recompute_w_u (effective values)
  *   v_new  [B, T*M, HV, V]  out of gdp_chunk_h (corrected values)
@@ -150,6 +154,7 @@ typedef struct gdp_chunk_args {
     const float *g;
     float *k_rnorm;
     float *gcum;
+    float *kdecay;
     void *w;
     void *u;
     void *v_new;
@@ -157,9 +162,9 @@ typedef struct gdp_chunk_args {
     void *o;
 } gdp_chunk_args;
 
-/* w, u, k_rnorm and gcum from k, v, beta, g. */
+/* w, u, k_rnorm, gcum and kdecay from k, v, beta, g. */
 gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream);
-/* h and v_new from k, k_rnorm, gcum, w, u.  One serial pass per sequence and
+/* h and v_new from k, kdecay, gcum, w, u.  One serial pass per sequence and
    value head over its chunks. */
 gdp_status gdp_chunk_h(const gdp_chunk_args *a, void *stream);
 /* o from q, k, k_rnorm, v_new, h, g. */

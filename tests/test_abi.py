@@ -65,7 +65,7 @@ def _args(**kw):
     base = dict(B=1, T=128, H=2, HV=2, K=64, V=64, M=1, chunk_size=64, scale=0.0, dtype=B.GDP_BF16,
                 cu_seqlens=None, num_seqs=0, h_chunks=2,
                 q=0x10000, k=0x20000, v=0x30000, beta=0x40000, g=0x50000, k_rnorm=0x60000,
-                gcum=0x68000, w=0x70000, u=0x80000, v_new=0x90000, h=0xA0000, o=0xB0000)
+                gcum=0x68000, kdecay=0x6C000, w=0x70000, u=0x80000, v_new=0x90000, h=0xA0000, o=0xB0000)
     base.update(kw)
     return B.ChunkArgs(**base)
 
@@ -104,6 +104,7 @@ def test_stage_specific_requirements():
     assert L.gdp_chunk_o(ctypes.byref(_args(q=None)), None) == B.GDP_ERR_INVALID
     assert L.gdp_recompute_w_u(ctypes.byref(_args(beta=None)), None) == B.GDP_ERR_INVALID
     assert L.gdp_chunk_h(ctypes.byref(_args(u=None)), None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_h(ctypes.byref(_args(kdecay=None)), None) == B.GDP_ERR_INVALID
 
 
 def test_null_args_rejected():
@@ -112,7 +113,7 @@ def test_null_args_rejected():
 
 def test_empty_problem_launches_nothing():
     # T == 0: valid, returns OK without touching the GPU
-    a = _args(T=0, q=None, k=None, v=None, beta=None, g=None, k_rnorm=None, gcum=None, w=None, u=None,
+    a = _args(T=0, q=None, k=None, v=None, beta=None, g=None, k_rnorm=None, gcum=None, kdecay=None, w=None, u=None,
               v_new=None, h=None, o=None, h_chunks=0)
     assert B.lib().gdp_chunk_fwd(ctypes.byref(a), None) == B.GDP_OK
 
