@@ -11,25 +11,29 @@
 // cumulative decay gcum on its last row) and kdecay = rnorm(k) exp2(gl - gcum)
 // per row, both precomputed by the WY stage.
 //
-// Work split: one block of two waves per (sequence, value head, 16 value
-// columns).  Wave k owns rows [k K/2, (k+1) K/2) of the fp32 state slice,
-// which stays in its registers for the whole sequence.  Per chunk each wave
-// forms its partial w h over its half of K; the halves are summed through
-// LDS (one barrier), both waves form v_new, and each wave updates its half
-// of h with its half of K.  Result tiles of the matrix cores feed the next
-// product directly: a result tile gives a lane four consecutive rows of one
-// column, a valid operand fragment once the other operand reads its
-// contraction index in the same order -- w is read with its K columns
-// permuted to match h, and K^T (transposed on the fly by ds_read_b64_tr_b16)
-// with its rows permuted to match v_new.
+// One block of four waves per (sequence, value head, 16 value columns), with
+// two roles:
 //
-// Memory: every wave streams its own w and K half tiles, the u slice,
-// kdecay and gcum straight from HBM into a three-stage LDS ring (buffer
-// loads with the LDS destination, two chunks ahead; no staging registers).
-// Tile rows are XOR-swizzled in 16-byte units so the fragment reads of both
-// products avoid bank conflicts.  The only cross-wave barrier is the
-// partial-sum exchange, and it waits on LDS only, so the stream stays in
-// flight across it.
+// * Compute waves 0 and 1 run the serial chain and issue no global memory
+//   instruction at all.  Wave k owns rows [k K/2, (k+1) K/2) of the fp32
+//   state slice, in registers for the whole sequence.  Per chunk each forms
+//   its partial w h over its half of K on the matrix cores; the halves meet
+//   in LDS behind the step's one barrier; both form v_new, and each updates
+//   its half of h.  Result tiles feed the next product directly: a result
+//   tile gives a lane four consecutive rows of one column, a valid operand
+//   fragment once the other operand reads its contraction index in the same
+//   order (w with its K columns permuted to match h; K^T, transposed on the
+//   fly by ds_read_b64_tr_b16, with its rows permuted to match v_new).  They
+//   leave v_new (transposed) and the next state snapshot in LDS.
+// * Memory waves 2 and 3 stream w, K, u, kdecay and gcum from HBM straight
+//   into a three-stage LDS ring (buffer loads with the LDS destination, two
+//   chunks ahead; the range check zero-fills rows past the end), and write
+//   v_new and the snapshots from LDS to HBM.  They wait on their own loads
+//   before each barrier, so the barrier also publishes the next stage.
+//
+// A compute wave's step is then bound by its own instruction stream, not by
+// the memory queue.  Tile rows are XOR-swizzled in 16-byte units so the
+// fragment reads of both products avoid bank conflicts.
 #include "gdp_common.h"
 #include "gdp_internal.h"
 
@@ -43,15 +47,15 @@ constexpr int C = 64;
 
 template <typename T, int KD>
 struct HStage {
-    T w[C * (KD / 2)];  // w half tile, swizzled rows
-    T k[C * (KD / 2)];  // K half tile, swizzled rows
-    T u[C * 16];        // u slice, plain rows of 16 elements
-    float kd[C];        // key decay factor per row (0 past the end)
-    float gc[C];        // cumulative log2 decay per row
+    T w[2][C * (KD / 2)];  // w half tiles [K half], swizzled rows
+    T k[2][C * (KD / 2)];  // K half tiles [K half], swizzled rows
+    T u[C * 16];           // u slice, plain rows of 16 elements
+    float kd[C];           // key decay factor per row (0 past the end)
+    float gc[C];           // cumulative log2 decay per row
 };
 
 template <typename T, int KD, int VD>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T *__restrict__ w,
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
@@ -59,26 +63,33 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     typedef typename Frag<T>::type FragT;
     typedef typename Frag<T>::half HalfT;
     constexpr int ES = (int)sizeof(T);
-    constexpr int KH = KD / 2;                 // state rows per wave
+    constexpr int KH = KD / 2;                 // state rows per compute wave
     constexpr int RB = KH * ES;                // bytes per half-tile row
     constexpr int UPR = RB / 16;               // 16-byte units per half-tile row
     constexpr int RPI = 64 / UPR;              // half-tile rows per DMA instruction
     constexpr int UUPR = 16 * ES / 16;         // 16-byte units per u row
     constexpr int NU = C * UUPR / 64;          // DMA instructions for the u slice
-    constexpr int NDMA = 2 * UPR + NU + 2;     // DMA instructions per wave per chunk
     constexpr int NS = 3;                      // ring stages (prefetch distance 2)
-    constexpr int NKT = KH / 16;               // 16-row state tiles per wave
+    constexpr int NKT = KH / 16;               // 16-row state tiles per compute wave
     constexpr int NKS = KH / 32;               // phase-1 contraction steps per wave
     constexpr int LDT = 64 + 32 / ES;          // row stride of the v_new transpose
+    constexpr int LDH = KD + 16 / ES;          // row stride of the snapshot staging
     constexpr int S = VD / 16;                 // column slices per head
     constexpr int SB = (int)sizeof(HStage<T, KD>);
-    static_assert(NKS >= 1 && (UPR & (UPR - 1)) == 0, "tile shape");
-    static_assert(2 * NDMA + 12 < 64, "in-flight DMA count must fit the vector memory counter");
+    // memory wave 0 loads the w halves and kdecay, wave 1 the K halves, u and gcum
+    constexpr int NDMA0 = 2 * UPR + 1, NDMA1 = 2 * UPR + NU + 1;
+    constexpr int HLPR = KD * ES / 16;         // lanes per snapshot row (16 B each)
+    constexpr int HRPI = 64 / HLPR;            // snapshot rows per store instruction
+    constexpr int NHS = 8 / HRPI > 0 ? 8 / HRPI : 1;  // snapshot stores per memory wave (8 rows)
+    constexpr int NVS = 2;                     // v_new stores per memory wave (32 rows)
+    static_assert(NKS >= 1 && (UPR & (UPR - 1)) == 0 && HRPI <= 8, "tile shape");
+    static_assert(NDMA1 + NHS + NVS < 64, "in-flight count must fit the vector memory counter");
     static_assert(SB % 16 == 0, "stage size");
 
-    __shared__ __attribute__((aligned(16))) HStage<T, KD> ring[2][NS];   // [wave][stage]
-    __shared__ __attribute__((aligned(16))) T Vt[2][16 * LDT];            // [wave] v_new transpose
-    __shared__ __attribute__((aligned(16))) f32x4 Xs[NS][2][4][64];       // [stage][wave][row tile][lane]
+    __shared__ __attribute__((aligned(16))) HStage<T, KD> ring[NS];
+    __shared__ __attribute__((aligned(16))) f32x4 Xs[NS][2][4][64];   // [stage][wave][row tile][lane]
+    __shared__ __attribute__((aligned(16))) T Vt[2][16 * LDT];        // [parity] v_new, column-major
+    __shared__ __attribute__((aligned(16))) T Hs[2][16 * LDH];        // [parity] snapshot rows (V x K)
 
     // ---- block -> (sequence, value head, slice); slices of one head share an XCD
     const int64_t P = nseq * HV;
@@ -97,127 +108,198 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     const int64_t cbase = items_before(cu, Ttok, M, C, seq);
     if (nch == 0) return;
 
-    const int lane = lane_id(), kw = wave_id();
+    const int lane = lane_id(), wave = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
     const int ldk = H * KD, ldw = HV * KD, ldv = HV * VD;  // global row strides (elements)
     const int64_t r0 = bos * M;  // first expanded row of the sequence
-    // chunks whose state snapshot fits below h_chunks
-    const int64_t hroom = h_chunks - cbase;
-    const int hlim = hroom < 0 ? 0 : (hroom > nch ? nch : (int)hroom);
 
+    auto clamp_rows = [](int r) { return r < 0 ? 0 : (r < C ? r : C); };
+    // bytes a buffer resource must cover for n rows of `width_b` bytes
+    auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
     // byte offset of element column `col` of half-tile row r (swizzled)
     auto swz = [&](int r, int col) {
         const int b = col * ES;
         return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
     };
-    // bytes a buffer resource must cover for n rows of `width` elements
-    auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
-    auto clamp_rows = [](int r) { return r < 0 ? 0 : (r < C ? r : C); };
 
-    // Per-lane DMA source offsets inside a chunk (fixed for the whole loop).
-    uint32_t ow[UPR], ok[UPR], ou[NU];
-#pragma unroll
-    for (int i = 0; i < UPR; ++i) {
-        const int r = i * RPI + lane / UPR;
-        const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
-        ow[i] = (uint32_t)((r * ldw) * ES + unit * 16);
-        ok[i] = (uint32_t)((r * ldk) * ES + unit * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < NU; ++i) ou[i] = (uint32_t)(((i * (64 / UUPR) + lane / UUPR) * ldv) * ES + (lane % UUPR) * 16);
-    const uint32_t okd = (uint32_t)(lane * HV * 4), ogc = okd;
-
-    // Streams advance by one chunk per issue.
-    const char *pw = (const char *)(w + (r0 * HV + hv) * KD + kw * KH);
-    const char *pk = (const char *)(k + (r0 * H + hk) * KD + kw * KH);
-    const char *pu = (const char *)(u + (r0 * HV + hv) * VD + 16 * sl);
-    const char *pd = (const char *)(kdecay + r0 * HV + hv);
-    const char *pg = (const char *)(gcum + r0 * HV + hv);
-    const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * ldv * ES,
-                  std_ = (int64_t)C * HV * 4;
-    int rem_issue = (int)rows;  // rows left from the next chunk to issue
-    const uint32_t ring_base = lds_addr(&ring[kw][0]);
-
-    // Stream the next chunk into stage st: exactly NDMA DMA instructions.
-    auto issue = [&](int st) {
-        const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
-        const uint32_t sb = ring_base + st * SB;
-        if (n < C) {  // tail or padding chunk: zero the stage first
-            HStage<T, KD> &Sg = ring[kw][st];
-            for (int i = lane; i < SB / 16; i += 64) ((uint4 *)&Sg)[i] = make_uint4(0, 0, 0, 0);
-            wait_lgkm0();
-        }
-        const rsrc_t rw = make_rsrc(pw, span(n, ldw * ES, RB));
-        const rsrc_t rk_ = make_rsrc(pk, span(n, ldk * ES, RB));
-        const rsrc_t ru = make_rsrc(pu, span(n, ldv * ES, 16 * ES));
-        const rsrc_t rd = make_rsrc(pd, span(n, HV * 4, 4));
-        const rsrc_t rg = make_rsrc(pg, span(n, HV * 4, 4));
+    if (wave >= 2) {
+        // ======================= memory waves =======================
+        const int mw = wave - 2;
+        const int64_t hroom = h_chunks - cbase;  // chunks whose snapshot fits below h_chunks
+        const int hlim = hroom < 0 ? 0 : (hroom > nch ? nch : (int)hroom);
+        const uint32_t ring_base = lds_addr(&ring[0]);
+        constexpr int OFW = (int)__builtin_offsetof(HStage<T, KD>, w);
+        constexpr int OFK = (int)__builtin_offsetof(HStage<T, KD>, k);
+        constexpr int OFU = (int)__builtin_offsetof(HStage<T, KD>, u);
+        constexpr int OFD = (int)__builtin_offsetof(HStage<T, KD>, kd);
+        constexpr int OFG = (int)__builtin_offsetof(HStage<T, KD>, gc);
+        constexpr int HALF = C * KH * ES;  // bytes of one half tile
+        // per-lane source offsets inside a chunk, less the DMA's offset in
+        // its 4 KiB M0 window; tile t (0: w, 1: K) half hh
+        uint32_t ot[2][UPR];
 #pragma unroll
         for (int i = 0; i < UPR; ++i) {
-            dma16_at(rw, ow[i], sb, (int)__builtin_offsetof(HStage<T, KD>, w) + i * 1024);
-            dma16_at(rk_, ok[i], sb, (int)__builtin_offsetof(HStage<T, KD>, k) + i * 1024);
+            const int r = i * RPI + lane / UPR;
+            const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
+            const int ld = mw == 0 ? ldw : ldk;
+            ot[0][i] = (uint32_t)((r * ld) * ES + unit * 16 - 1024 * (i % 4));
+            ot[1][i] = ot[0][i] + KH * ES;  // second K half of the same rows
         }
+        uint32_t ou[NU];
 #pragma unroll
-        for (int i = 0; i < NU; ++i) dma16_at(ru, ou[i], sb, (int)__builtin_offsetof(HStage<T, KD>, u) + i * 1024);
-        dma4_at(rd, okd, sb, (int)__builtin_offsetof(HStage<T, KD>, kd));
-        dma4_at(rg, ogc, sb, (int)__builtin_offsetof(HStage<T, KD>, gc));
-        pw += stw;
-        pk += stk;
-        pu += stu;
-        pd += std_;
-        pg += std_;
-        rem_issue -= C;
-    };
+        for (int i = 0; i < NU; ++i)
+            ou[i] = (uint32_t)(((i * (64 / UUPR) + lane / UUPR) * ldv) * ES + (lane % UUPR) * 16 - 1024 * (i % 4));
+        const uint32_t o4 = (uint32_t)(lane * HV * 4);
 
+        const char *pt = mw == 0 ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
+        const int ldt = mw == 0 ? ldw : ldk;
+        const int64_t stt = (int64_t)C * ldt * ES;
+        const char *pu = (const char *)(u + (r0 * HV + hv) * VD + 16 * sl);
+        const char *p4 = mw == 0 ? (const char *)(kdecay + r0 * HV + hv) : (const char *)(gcum + r0 * HV + hv);
+        const int64_t stu = (int64_t)C * ldv * ES, st4 = (int64_t)C * HV * 4;
+        const int tile_off = mw == 0 ? OFW : OFK;
+        const int off4 = mw == 0 ? OFD : OFG;
+        int rem_issue = (int)rows;
+
+        // stream the next chunk into stage st (NDMA0 or NDMA1 instructions)
+        auto issue = [&](int st) {
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
+            const uint32_t sb = ring_base + st * SB + tile_off;
+            const rsrc_t rt = make_rsrc(pt, span(n, ldt * ES, KD * ES));
+            static_for<0, 2>([&](auto hc) {
+                constexpr int hh = decltype(hc)::value;
+                static_for<0, UPR>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (i % 4 == 0) set_m0(sb + (hh * HALF + 1024 * i));
+                    dma16_m0<1024 * (i % 4)>(rt, ot[hh][i]);
+                });
+            });
+            if (mw == 1) {
+                const rsrc_t ru = make_rsrc(pu, span(n, ldv * ES, 16 * ES));
+                const uint32_t sbu = ring_base + st * SB + OFU;
+                static_for<0, NU>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
+                    dma16_m0<1024 * (i % 4)>(ru, ou[i]);
+                });
+            }
+            dma4(make_rsrc(p4, span(n, HV * 4, 4)), o4, ring_base + st * SB + off4);
+            pt += stt;
+            pu += stu;
+            p4 += st4;
+            rem_issue -= C;
+        };
+
+        // snapshot of the state entering chunk c: rows [8mw, 8mw + 8) of the
+        // V slice, from Hs[c & 1]
+        char *ph = (char *)(hout + (cbase * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl) * KD);
+        const int64_t sth = (int64_t)HV * VD * KD * ES;
+        auto store_h = [&](int c) {
+            const rsrc_t rh = make_rsrc(ph, c < hlim ? (uint32_t)(16 * KD * ES) : 0u);
+            const T *src = Hs[c & 1];
+#pragma unroll
+            for (int i = 0; i < NHS; ++i) {
+                const int r = 8 * mw + i * HRPI + lane / HLPR;
+                const int e = (lane % HLPR) * (16 / ES);
+                const uint4 val = *(const uint4 *)(src + r * LDH + e);
+                buf_store16(rh, (uint32_t)((r * KD + e) * ES), val);
+            }
+            ph += sth;
+        };
+        // v_new rows [32mw, 32mw + 32) of chunk c, from Vt[c & 1]
+        char *pv = (char *)(v_new + (r0 * HV + hv) * VD + 16 * sl);
+        int rem_v = (int)rows;
+        auto store_v = [&](int c) {
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_v));
+            const rsrc_t rv = make_rsrc(pv, span(n, ldv * ES, 16 * ES));
+#pragma unroll
+            for (int r2 = 0; r2 < NVS; ++r2) {
+                const HalfT o4v = lds_col4<T>(Vt[c & 1], LDT, 4 * lg, 32 * mw + 16 * r2);
+                const uint32_t off = (uint32_t)(((32 * mw + 16 * r2 + lc) * ldv + 4 * lg) * ES);
+                if constexpr (ES == 2)
+                    buf_store8(rv, off, __builtin_bit_cast(uint2, o4v));
+                else
+                    buf_store16(rv, off, __builtin_bit_cast(uint4, o4v));
+            }
+            pv += stu;
+            rem_v -= C;
+        };
+
+        auto loop = [&](auto ndc) {
+            constexpr int ND = decltype(ndc)::value;
+            issue(0);
+            issue(1);
+            wait_vmcnt<ND>();  // chunk 0 landed
+            lds_barrier();     // publishes stage 0 and the zero snapshot
+            for (int c = 0; c < nch; ++c) {
+                issue((c + 2) % NS);
+                // chunk c + 1 landed: count what was issued after its DMAs
+                if (c == 0)
+                    wait_vmcnt<ND>();
+                else if (c == 1)
+                    wait_vmcnt<ND + NHS>();
+                else
+                    wait_vmcnt<ND + NHS + NVS>();
+                lds_barrier();  // compute step c's exchange; publishes stage c + 1
+                store_h(c);
+                if (c >= 1) store_v(c - 1);
+            }
+            lds_barrier();  // v_new of the last chunk is in Vt
+            store_v(nch - 1);
+            wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
+        };
+        if (mw == 0)
+            loop(std::integral_constant<int, NDMA0>{});
+        else
+            loop(std::integral_constant<int, NDMA1>{});
+        return;
+    }
+
+    // ======================= compute waves =======================
+    // (instantiated per wave so every wave-dependent offset is a constant)
+    auto compute = [&](auto kwc) {
+    constexpr int kw = decltype(kwc)::value;
     // State slice of this wave, in a permuted K order: hs[kt][q] holds h at
     // K index kw*KH + kperm(kt, 4lg + q), column 16sl + lc, with
     //   kperm(kt, i) = 32(kt/2) + 8(i/4) + 4(kt%2) + i%4,
-    // so that hb[ks] (tiles 2ks, 2ks+1 as bf16) holds 8 consecutive K
-    // indices 32ks + 8lg .. +7: the phase-1 operand matches a plain 16-byte
-    // row read of w and the snapshot is one 16-byte store.  K^T is read with
-    // the same permutation.
+    // so that hb[ks] (tiles 2ks, 2ks+1 in storage precision) holds 8
+    // consecutive K indices 32ks + 8lg .. +7: the phase-1 operand matches a
+    // plain 16-byte row read of w and the snapshot is a 16-byte write.  K^T
+    // is read with the same permutation.
     f32x4 hs[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) hs[kt] = zero4();
     FragT hb[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) hb[ks] = FragT{};
-
-    char *ph = (char *)(hout + (cbase * HV + hv) * (int64_t)VD * KD);
-    char *pv = (char *)(v_new + (r0 * HV + hv) * VD + 16 * sl);
-    const int64_t sth = (int64_t)HV * VD * KD * ES;
+    auto put_snapshot = [&](T *dst) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            T *p = dst + lc * LDH + kw * KH + 32 * ks + 8 * lg;
+            if constexpr (ES == 2) {
+                *(FragT *)p = hb[ks];
+            } else {
+                HalfT lo, hi;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    lo[q] = hb[ks][q];
+                    hi[q] = hb[ks][4 + q];
+                }
+                *(HalfT *)p = lo;
+                *(HalfT *)(p + 4) = hi;
+            }
+        }
+    };
+    put_snapshot(Hs[0]);  // h[0] = 0
+    lds_barrier();        // stage 0 landed
     int rem = (int)rows;  // rows left from the current chunk
 
     // One chunk on ring stage ST (a compile-time constant, so every LDS
     // address below is a fixed offset from a per-lane base).
     auto step = [&](int c, auto stc) {
         constexpr int ST = decltype(stc)::value;
-        issue((ST + 2) % NS);
-        wait_vmcnt<2 * NDMA>();  // chunk c landed (issued two steps ago)
-        const HStage<T, KD> &Sg = ring[kw][ST];
+        const HStage<T, KD> &Sg = ring[ST];
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // uniform
-
-        // snapshot of the state entering chunk c (S = h^T, V x K); dropped
-        // past h_chunks
-        {
-            const rsrc_t rh = make_rsrc(ph, c < hlim ? (uint32_t)(VD * KD * ES) : 0u);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const uint32_t off = (uint32_t)(((16 * sl + lc) * KD + kw * KH + 32 * ks + 8 * lg) * ES);
-                if constexpr (ES == 2) {
-                    buf_store16(rh, off, __builtin_bit_cast(uint4, hb[ks]));
-                } else {
-                    HalfT lo, hi;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        lo[q] = hb[ks][q];
-                        hi[q] = hb[ks][4 + q];
-                    }
-                    buf_store16(rh, off, __builtin_bit_cast(uint4, lo));
-                    buf_store16(rh, off + 16, __builtin_bit_cast(uint4, hi));
-                }
-            }
-        }
 
         // phase 1: partial w h over this wave's half of K (w columns
         // 32ks + 8lg .. +7, the order of hb)
@@ -228,7 +310,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             const int r = 16 * rt + lc;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const char *wb = (const char *)Sg.w;
+                const char *wb = (const char *)Sg.w[kw];
                 FragT a;
                 if constexpr (ES == 2) {
                     a = *(const FragT *)(wb + swz(r, 32 * ks + 8 * lg));
@@ -240,7 +322,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             }
         }
 
-        // wave-private reads that need no barrier: u, key decays, K^T
+        // reads that need no barrier: u, key decays, the chunk decay, K^T
         HalfT uu[4];
         f32x4 kd4[4];
 #pragma unroll
@@ -255,7 +337,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 HalfT x0, x1;
-                const char *kb = (const char *)Sg.k;
+                const char *kb = (const char *)Sg.k[kw];
                 const int kbase = 32 * (kt >> 1) + 4 * (kt & 1);  // kperm(kt, 0)
                 if constexpr (ES == 2) {
                     // transposed read: source lane j of the 16-lane group
@@ -279,36 +361,46 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 }
                 ka[kt][s] = join<T>(x0, x1);
             }
+        // gl <= 0; rows past the end carry key decay 0
+        const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
+        f32x4 uf[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) uf[rt][q] = to_f32(uu[rt][q]);
 
-        // exchange partials (one buffer per ring stage: one barrier)
+        // exchange partials (one buffer per ring stage; the step's barrier)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) Xs[ST][kw][rt][lane] = acc[rt];
         lds_barrier();
-
-        // gl <= 0, and rows past the end carry decay factor 0
-        const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
-        FragT vb[2];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hs[kt][q] *= gl;
+
+        FragT vb[2];
+        T *vt = Vt[c & 1];
+        static_for<0, 4>([&](auto rtc) {
+            constexpr int rt = decltype(rtc)::value;
             const f32x4 other = Xs[ST][kw ^ 1][rt][lane];
             HalfT v4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float vn = to_f32(uu[rt][q]) - acc[rt][q] - other[q];
+                // own + other is the same sum in both waves (addition
+                // commutes), so both hold bit-identical v_new
+                const float vn = uf[rt][q] - (acc[rt][q] + other[q]);
                 v4[q] = from_f32<T>(vn);
                 vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(vn * kd4[rt][q]);
             }
-            *(HalfT *)(&Vt[kw][lc * LDT + 16 * rt + 4 * lg]) = v4;
-        }
+            // compute wave kw publishes rows [32kw, 32kw + 32)
+            if constexpr ((rt >> 1) == kw) *(HalfT *)(&vt[lc * LDT + 16 * rt + 4 * lg]) = v4;
+        });
 
         // phase 2: h = exp2(gl) h + K^T (kd * v_new), this wave's K half
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) hs[kt][q] *= gl;
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int s = 0; s < 2; ++s) hs[kt] = mma(ka[kt][s], vb[s], hs[kt]);
-        }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -316,32 +408,25 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 hb[ks][q] = from_f32<T>(hs[2 * ks][q]);
                 hb[ks][4 + q] = from_f32<T>(hs[2 * ks + 1][q]);
             }
-
-        // v_new rows [32kw, 32kw + 32) of this wave: 4 columns of a row per lane
-        const rsrc_t rv = make_rsrc(pv, span(n, ldv * ES, 16 * ES));
-#pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
-            const HalfT o4 = lds_col4<T>(Vt[kw], LDT, 4 * lg, 32 * kw + 16 * r2);
-            const uint32_t off = (uint32_t)(((32 * kw + 16 * r2 + lc) * ldv + 4 * lg) * ES);
-            if constexpr (ES == 2)
-                buf_store8(rv, off, __builtin_bit_cast(uint2, o4));
-            else
-                buf_store16(rv, off, __builtin_bit_cast(uint4, o4));
-        }
-        ph += sth;
-        pv += stu;
+        put_snapshot(Hs[(c + 1) & 1]);  // the state entering chunk c + 1
         rem -= C;
     };
 
-    issue(0);
-    issue(1);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     static_assert(NS == 3, "the loop below is unrolled over three ring stages");
     for (int c = 0; c < nch; c += 3) {
-        step(c, std::integral_constant<int, 0>{});
-        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>{});
-        if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>{});
+        step(c, I0{});
+        if (c + 1 < nch) step(c + 1, I1{});
+        if (c + 2 < nch) step(c + 2, I2{});
     }
-    wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
+    lds_barrier();  // publishes the last chunk's v_new
+    };
+    if (wave == 0)
+        compute(std::integral_constant<int, 0>{});
+    else
+        compute(std::integral_constant<int, 1>{});
 }
 
 template <typename T, int KD, int VD>
@@ -350,7 +435,7 @@ static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
     const int64_t P = p.nseq * a.HV;
     const int64_t S = VD / 16;
     const int64_t nblk = ((P + 7) / 8) * 8 * S;
-    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(128), 0, stream,
+    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(256), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
                        p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, (T *)a.v_new, (T *)a.h);
     return hipGetLastError();

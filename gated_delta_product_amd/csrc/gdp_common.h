@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gdp {
 
 typedef __bf16 bf16;
@@ -318,12 +320,33 @@ __device__ __forceinline__ void dma4_at(rsrc_t r, uint32_t voffset, uint32_t lds
     asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :: "s"(lds_base), "v"(voffset), "s"(r), "i"(off) : "memory", "scc");
 }
+// Windowed form: set_m0(base) once, then up to four dma16_m0<IMM> whose LDS
+// destination is base + IMM (+ 16*lane).  The 12-bit instruction offset is
+// added to both the LDS and the memory address and is part of the buffer
+// range check, so the caller passes voffset - IMM.
+__device__ __forceinline__ void set_m0(uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" :: "s"(lds_base) : "memory");
+}
+template <int IMM>
+__device__ __forceinline__ void dma16_m0(rsrc_t r, uint32_t voffset) {
+    static_assert(IMM >= 0 && IMM < 4096, "12-bit instruction offset");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" :: "v"(voffset), "s"(r), "n"(IMM) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // 32-bit LDS byte address of a __shared__ object.
 template <typename P>
