@@ -11,8 +11,8 @@
 // cumulative decay gcum on its last row) and kdecay = rnorm(k) exp2(gl - gcum)
 // per row, both precomputed by the WY stage.
 //
-// One block of four waves per (sequence, value head, 16 value columns), with
-// two roles:
+// One block of five waves per (sequence, value head, 16 value columns), with
+// three roles:
 //
 // * Compute waves 0 and 1 run the serial chain and issue no global memory
 //   instruction at all.  Wave k owns rows [k K/2, (k+1) K/2) of the fp32
@@ -25,6 +25,8 @@
 //   order (w with its K columns permuted to match h; K^T, transposed on the
 //   fly by ds_read_b64_tr_b16, with its rows permuted to match v_new).  They
 //   leave v_new (transposed) and the next state snapshot in LDS.
+// * Prefetch wave 4 pulls the lines of the chunk five ahead into L2 (each
+//   of a head's column blocks a share), so the memory waves hit L2.
 // * Memory waves 2 and 3 stream w, K, u, kdecay and gcum from HBM straight
 //   into a three-stage LDS ring (buffer loads with the LDS destination, two
 //   chunks ahead; the range check zero-fills rows past the end), and write
@@ -55,7 +57,7 @@ struct HStage {
 };
 
 template <typename T, int KD, int VD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(320)
 gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T *__restrict__ w,
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
@@ -90,6 +92,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     __shared__ __attribute__((aligned(16))) f32x4 Xs[NS][2][4][64];   // [stage][wave][row tile][lane]
     __shared__ __attribute__((aligned(16))) T Vt[2][16 * LDT];        // [parity] v_new, column-major
     __shared__ __attribute__((aligned(16))) T Hs[2][16 * LDH];        // [parity] snapshot rows (V x K)
+    __shared__ __attribute__((aligned(16))) char Pf[1024];            // landing area of L2 prefetches
 
     // ---- block -> (sequence, value head, slice); slices of one head share an XCD
     const int64_t P = nseq * HV;
@@ -121,6 +124,57 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         const int b = col * ES;
         return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
     };
+
+    if (wave == 4) {
+        // ======================= prefetch wave =======================
+        // Pulls the lines of chunk c + PF into L2 while the memory waves
+        // stream chunk c + 2 into LDS, so their loads hit L2 instead of
+        // waiting on HBM.  The S blocks of a head share an XCD (and its L2);
+        // block sl prefetches rows [RPB sl, RPB sl + RPB) of each chunk.  The
+        // data lands in a scratch LDS area that nothing reads.
+        constexpr int PF = 5;                    // prefetch distance in chunks
+        constexpr int RPB = C / S;               // rows per block per chunk
+        const uint32_t pf = lds_addr(&Pf[0]);
+        const int rbw = KD * ES, rbu = VD * ES;  // row bytes of w / k and of u
+        const char *pw = (const char *)(w + ((r0 + RPB * sl) * HV + hv) * KD);
+        const char *pk = (const char *)(k + ((r0 + RPB * sl) * H + hk) * KD);
+        const char *pu = (const char *)(u + ((r0 + RPB * sl) * HV + hv) * VD);
+        const char *pd = (const char *)(kdecay + r0 * HV + hv);
+        const char *pg = (const char *)(gcum + r0 * HV + hv);
+        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * ldv * ES,
+                      st4 = (int64_t)C * HV * 4;
+        // rows [0, nr) of a tile with `rb`-byte rows `ld` bytes apart: one
+        // 16-byte unit per lane, 1 KiB per instruction
+        auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb, int nrmax) {
+            const int lpr = rb / 16;
+            const rsrc_t r = make_rsrc(base, span(nr, ld, rb));
+            for (int i = 0; i < nrmax * lpr; i += 64) {
+                const int idx = i + lane;
+                dma16(r, (uint32_t)((idx / lpr) * ld + (idx % lpr) * 16), pf);
+            }
+        };
+        int rem_pf = (int)rows;
+        auto prefetch = [&](int c) {
+            const int nr = clamp_rows(rem_pf - C * c - RPB * sl);
+            const int n = clamp_rows(rem_pf - C * c);
+            const int64_t oc = c;
+            rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw, RPB);
+            rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw, RPB);
+            rows_to_l2(pu + oc * stu, nr < RPB ? nr : RPB, ldv * ES, rbu, RPB);
+            dma4(make_rsrc(pd + oc * st4, span(n, HV * 4, 4)), (uint32_t)(lane * HV * 4), pf);
+            dma4(make_rsrc(pg + oc * st4, span(n, HV * 4, 4)), (uint32_t)(lane * HV * 4), pf);
+        };
+        for (int c = 2; c < PF; ++c) prefetch(c);
+        lds_barrier();
+        for (int c = 0; c < nch; ++c) {
+            prefetch(c + PF);
+            wait_vmcnt<32>();  // bound the number of prefetches in flight
+            lds_barrier();
+        }
+        lds_barrier();
+        wait_vmcnt<0>();
+        return;
+    }
 
     if (wave >= 2) {
         // ======================= memory waves =======================
@@ -435,7 +489,7 @@ static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
     const int64_t P = p.nseq * a.HV;
     const int64_t S = VD / 16;
     const int64_t nblk = ((P + 7) / 8) * 8 * S;
-    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(256), 0, stream,
+    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(320), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
                        p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, (T *)a.v_new, (T *)a.h);
     return hipGetLastError();

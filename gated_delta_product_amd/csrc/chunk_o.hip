@@ -2,20 +2,29 @@
 // (core.ssm.ops.gdp.chunk_o: module description,
 // chunk_gated_delta_product_fwd_o).
 //
-// One block (4 waves) per (64-token chunk i of a sequence, value head).  The
-// queries are one per token; keys and corrected values live on the expanded
-// stream, copy j of token s at row s*M + j.  With G the within-chunk
-// cumulative log decay of the tokens and S the V x K state entering the
-// chunk (the chunk_h snapshot at expanded chunk i*M):
+// One block (4 waves) per (64-token chunk i of a sequence, value head, slab
+// of up to 128 value columns).  The queries are one per token; keys and
+// corrected values live on the expanded stream, copy j of token s at row
+// s*M + j.  With G the within-chunk cumulative log decay of the tokens and S
+// the V x K state entering the chunk (the chunk_h snapshot at expanded chunk
+// i*M):
 //   o_t = scale * [ exp(G_t) S qhat_t
 //                   + sum_j sum_{s <= t} exp(G_t - G_s) (qhat_t . khat_{sM+j}) v_new_{sM+j} ]
 // computed transposed, O^T = S Q^T + sum_j V_j^T P_j^T, so a result lane
-// holds four consecutive output columns of one token.  The score tile
-// S_j^T = K_j Q^T comes out of the matrix cores with each lane holding four
-// consecutive key rows of one query column -- exactly the B-operand layout the
-// P V product needs once V_j^T is read with the same row order (LDS transpose
-// reads).  Norms enter as fp32 scales on the scores and on the inter term.
-// Wave w owns tokens [16w, 16w + 16) and skips the key tiles past them.
+// holds four consecutive output columns of one token.  Wave w owns tokens
+// [16w, 16w + 16) and skips the key tiles past them, so its scores never
+// leave its registers: the score tile P_j^T = K_j Q^T comes out of the
+// matrix cores with each lane holding four consecutive key rows of one
+// query column, which is the operand layout of the P V product once V_j^T
+// is read with the same row order (LDS transpose reads).
+//
+// Only the operands that several waves share or that need a transpose go
+// through LDS: the state slab (copied in with buffer_load ... lds) and the
+// copy's V_j slab.  Q and K_j fragments are plain 16-byte row reads straight
+// into registers.  That keeps LDS near 50 KB so three blocks share a CU and
+// one block's loads overlap another's math.  Norms enter as fp32 scales on
+// the scores and on the inter term; rows past the end of a sequence read as
+// zeros through the buffer range checks.
 #include "gdp_common.h"
 #include "gdp_internal.h"
 
@@ -23,152 +32,259 @@ namespace gdp {
 
 namespace {
 constexpr int C = 64;
-template <typename T> struct PadO { static constexpr int value = 32 / (int)sizeof(T); };
 }  // namespace
 
-template <typename T, int KD, int VD>
+template <typename T, int KD, int VB>
 __global__ void __launch_bounds__(256)
 gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ k_rnorm,
               const T *__restrict__ v_new, const T *__restrict__ hst, const float *__restrict__ g,
-              const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok, int H, int HV, int M,
+              const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok, int H, int HV, int M, int VD,
               int64_t h_chunks, float scale, T *__restrict__ o) {
     typedef typename Frag<T>::type FragT;
-    constexpr int LDK = KD + PadO<T>::value;
-    constexpr int LDV = VD + PadO<T>::value;
-    constexpr int NVT = VD / 16;
-    constexpr int NKS = KD / 32;
-    __shared__ __attribute__((aligned(16))) T Qs[C * LDK];
-    __shared__ __attribute__((aligned(16))) T Ss[VD * LDK];
-    __shared__ __attribute__((aligned(16))) T Kj[C * LDK];
-    __shared__ __attribute__((aligned(16))) T Vj[C * LDV];
-    __shared__ float s_rq[C], s_G[C], s_rk[C];
+    typedef typename Frag<T>::half HalfT;
+    constexpr int ES = (int)sizeof(T);
+    constexpr int NKS = KD / 32;           // contraction steps over K
+    constexpr int NVT = VB / 16;           // 16-column output tiles
+    constexpr int SRB = KD * ES;           // bytes per state row
+    constexpr int SUPR = SRB / 16;         // 16-byte units per state row
+    constexpr int VRB = VB * ES;           // bytes per V slab row
+    constexpr int VUPR = VRB / 16;         // 16-byte units per V slab row
+    constexpr int NSD = VB * SRB / 1024;   // DMA instructions for the state slab
+    constexpr int NVD = C * VRB / 1024;    // DMA instructions for a V slab
+    static_assert(NSD % 4 == 0 && NVD % 4 == 0 && SUPR >= 8 && VUPR >= 8, "tile shape");
+    __shared__ __attribute__((aligned(16))) T Ss[VB * KD];   // state slab, swizzled rows
+    __shared__ __attribute__((aligned(16))) T Vs[C * VB];    // V_j slab, swizzled rows
+    __shared__ float sG[4][C], sRk[4][C];                    // per-wave scratch
 
     const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, blockIdx.x);
     if (loc.seq < 0) return;
     const int hv = blockIdx.y;
     const int hk = hv / (HV / H);
+    const int vb0 = VB * (int)blockIdx.z;
     const int64_t t0 = loc.bos + C * loc.c;  // first token (flattened)
     const int nt = (int)((loc.eos - t0) < C ? (loc.eos - t0) : C);
     const int64_t hidx = items_before(cu, Ttok, M, C, loc.seq) + loc.c * M;
-    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    const int lane = lane_id(), wv = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
+    const int tt = wv;               // token tile of this wave
+    const int t_loc = 16 * tt + lc;  // token whose column this lane holds
+    auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
+    // swizzled byte offsets: state rows XOR their 16-byte unit with the row;
+    // V rows XOR 32-byte unit pairs, so a transposed read of four
+    // consecutive rows touches four distinct bank groups
+    auto s_off = [](int r, int unit) { return r * SRB + ((unit ^ (r & (SUPR - 1))) << 4); };
+    auto v_off = [](int r, int unit) { return r * VRB + ((unit ^ ((r & (VUPR / 2 - 1)) << 1)) << 4); };
 
-    // ---- stage Q (with norms), the boundary state S, decays
-    stage_tile<T, C, KD, LDK, 256>(Qs, q + (t0 * H + hk) * (int64_t)KD, (int64_t)H * KD, nt, s_rq);
-    stage_tile<T, VD, KD, LDK, 256>(Ss, hst + (hidx * HV + hv) * (int64_t)VD * KD, (int64_t)KD,
-                                    hidx < h_chunks ? VD : 0, nullptr);
-    if (wv == 0) {
-        const float gt = lane < nt ? g[(t0 + lane) * HV + hv] : 0.f;
-        s_G[lane] = wave_inclusive_sum(gt);
+    // ---- state slab (rows vb0 .. vb0 + VB of S) -> LDS; the snapshot is
+    // zero-filled past h_chunks by the range check
+    {
+        const rsrc_t rs = make_rsrc(hst + ((hidx * HV + hv) * (int64_t)VD + vb0) * KD,
+                                    hidx < h_chunks ? (uint32_t)(VB * SRB) : 0u);
+        const uint32_t base = lds_addr(Ss);
+#pragma unroll
+        for (int i = 0; i < NSD / 4; ++i) {
+            const int blk = wv * (NSD / 4) + i;
+            const int r = blk * (1024 / SRB) + lane / SUPR, u = lane % SUPR;
+            dma16(rs, (uint32_t)(r * SRB + ((u ^ (r & (SUPR - 1))) << 4)), base + blk * 1024);
+        }
     }
-    __syncthreads();
-    if (wv == 0) s_rq[lane] = 1.0f / sqrtf(s_rq[lane] + 1e-6f);
-    __syncthreads();
+    const int64_t ldkv_k = (int64_t)M * H * KD, ldkv_v = (int64_t)M * HV * VD;  // row strides per token
+    auto stage_v = [&](int j) {
+        const rsrc_t rv = make_rsrc(v_new + ((t0 * M + j) * HV + hv) * (int64_t)VD + vb0,
+                                    span(nt, (int)(ldkv_v * ES), VRB));
+        const uint32_t base = lds_addr(Vs);
+#pragma unroll
+        for (int i = 0; i < NVD / 4; ++i) {
+            const int blk = wv * (NVD / 4) + i;
+            const int r = blk * (1024 / VRB) + lane / VUPR, u = lane % VUPR;
+            dma16(rv, (uint32_t)(r * ldkv_v * ES + ((u ^ ((r & (VUPR / 2 - 1)) << 1)) << 4)), base + blk * 1024);
+        }
+    };
+    stage_v(0);
 
-    const int tt = wv;                 // token tile of this wave
-    const int t_loc = 16 * tt + lc;    // token whose column this lane holds
-    const float Gt = s_G[t_loc];
+    // ---- register operands: this lane's query row (B operand of both
+    // products), its keys per copy, the decays and key norms
+    const rsrc_t rq = make_rsrc(q + (t0 * H + hk) * (int64_t)KD, span(nt, H * KD * ES, SRB));
+    FragT qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const uint32_t off = (uint32_t)((t_loc * H * KD + 32 * ks + 8 * lg) * ES);
+        if constexpr (ES == 2) {
+            qf[ks] = __builtin_bit_cast(FragT, buf_load16(rq, off));
+        } else {
+            qf[ks] = join<T>(__builtin_bit_cast(HalfT, buf_load16(rq, off)),
+                             __builtin_bit_cast(HalfT, buf_load16(rq, off + 16)));
+        }
+    }
+    const float gl = lane < nt ? g[(t0 + lane) * HV + hv] : 0.f;
+    FragT kf[4][NKS];
+    float rkl = 0.f;
+    auto load_k = [&](int j) {
+        const rsrc_t rk = make_rsrc(k + ((t0 * M + j) * H + hk) * (int64_t)KD, span(nt, (int)(ldkv_k * ES), SRB));
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (st <= tt) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const uint32_t off = (uint32_t)(((16 * st + lc) * ldkv_k + 32 * ks + 8 * lg) * ES);
+                    if constexpr (ES == 2) {
+                        kf[st][ks] = __builtin_bit_cast(FragT, buf_load16(rk, off));
+                    } else {
+                        kf[st][ks] = join<T>(__builtin_bit_cast(HalfT, buf_load16(rk, off)),
+                                             __builtin_bit_cast(HalfT, buf_load16(rk, off + 16)));
+                    }
+                }
+            }
+        }
+        rkl = lane < nt ? k_rnorm[((t0 + lane) * M + j) * H + hk] : 0.f;
+    };
+    load_k(0);
+
+    // ---- decays and the query norm (no LDS traffic beyond this wave's own)
+    const float Gl = wave_inclusive_sum(gl);
+    sG[wv][lane] = Gl;
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = to_f32(qf[ks][i]);
+            ss += x * x;
+        }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float fq = scale / sqrtf(ss + 1e-6f);  // scale * rnorm(q_t)
+    const float Gt = sG[wv][t_loc];
+
+    wait_vmcnt<0>();
+    __syncthreads();  // state slab and V_0 landed
 
     // ---- inter-chunk term: O^T[vt] = S[16vt.., :] Q^T[:, t]
     f32x4 acc[NVT];
     {
-        FragT qb[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qb[ks] = lds_row8<T>(Qs + t_loc * LDK + 32 * ks + 8 * lg);
-        const float f = scale * s_rq[t_loc] * __expf(Gt);
+        const float f = fq * __expf(Gt);
+        const char *sb = (const char *)Ss;
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) {
             f32x4 a4 = zero4();
+            const int r = 16 * vt + lc;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                a4 = mma(lds_row8<T>(Ss + (16 * vt + lc) * LDK + 32 * ks + 8 * lg), qb[ks], a4);
+            for (int ks = 0; ks < NKS; ++ks) {
+                FragT a;
+                if constexpr (ES == 2) {
+                    a = *(const FragT *)(sb + s_off(r, 4 * ks + lg));
+                } else {
+                    a = join<T>(*(const HalfT *)(sb + s_off(r, 8 * ks + 2 * lg)),
+                                *(const HalfT *)(sb + s_off(r, 8 * ks + 2 * lg + 1)));
+                }
+                a4 = mma(a, qf[ks], a4);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[vt][i] = a4[i] * f;
         }
     }
 
-    // ---- intra-chunk attention, one Householder copy at a time
-    const float fq = scale * s_rq[t_loc];
-    for (int j = 0; j < M; ++j) {
-        __syncthreads();  // previous copy's tiles are no longer read
-        const int64_t r0 = t0 * M + j;  // expanded row of copy j of token t0
-        stage_tile<T, C, KD, LDK, 256>(Kj, k + (r0 * H + hk) * (int64_t)KD, (int64_t)M * H * KD, nt, nullptr);
-        stage_tile<T, C, VD, LDV, 256>(Vj, v_new + (r0 * HV + hv) * (int64_t)VD, (int64_t)M * HV * VD, nt,
-                                       nullptr);
-        if (wv == 0) s_rk[lane] = lane < nt ? k_rnorm[(r0 + (int64_t)lane * M) * H + hk] : 0.f;
-        __syncthreads();
-
-        // scores P^T tiles for key tiles st <= tt: lane holds s = 16st + 4lg + i, t = t_loc
-        FragT qb[NKS];
+    // exp(G_t - G_s) of the key rows this lane holds (s = 16st + 4lg + i),
+    // masked to s <= t and s < nt; shared by all copies
+    f32x4 dec[4];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qb[ks] = lds_row8<T>(Qs + t_loc * LDK + 32 * ks + 8 * lg);
-        f32x4 p[4];
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sidx = 16 * st + 4 * lg + i;
+            dec[st][i] = (st <= tt && sidx <= t_loc && sidx < nt) ? fq * __expf(Gt - sG[wv][sidx]) : 0.f;
+        }
+
+    // ---- intra-chunk attention, one Householder copy at a time
+    for (int j = 0; j < M; ++j) {
+        sRk[wv][lane] = rkl;
+        // scores P^T tiles for key tiles st <= tt
+        FragT pb[2];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            p[st] = zero4();
+            f32x4 p = zero4();
             if (st <= tt) {
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    p[st] = mma(lds_row8<T>(Kj + (16 * st + lc) * LDK + 32 * ks + 8 * lg), qb[ks], p[st]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = 16 * st + 4 * lg + i;
-                    p[st][i] = (s <= t_loc && s < nt) ? p[st][i] * fq * s_rk[s] * __expf(Gt - s_G[s]) : 0.f;
-                }
+                for (int ks = 0; ks < NKS; ++ks) p = mma(kf[st][ks], qf[ks], p);
             }
+            const f32x4 rk4 = *(const f32x4 *)&sRk[wv][16 * st + 4 * lg];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pb[st >> 1][4 * (st & 1) + i] = from_f32<T>(p[i] * dec[st][i] * rk4[i]);
         }
+        if (j + 1 < M) load_k(j + 1);  // next copy's keys while this one's products run
         // O^T[vt] += V_j^T[vt, s] P^T[s, t]; contraction slot m <-> s = 32ks + 16(m/4) + 4lg + m%4
+        const char *vb = (const char *)Vs;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (2 * ks <= tt) {
-                FragT pb;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pb[i] = from_f32<T>(p[2 * ks][i]);
-                    pb[4 + i] = from_f32<T>(p[2 * ks + 1][i]);
-                }
 #pragma unroll
                 for (int vt = 0; vt < NVT; ++vt) {
-                    FragT a = lds_col8<T>(Vj, LDV, 32 * ks + 4 * lg, 32 * ks + 16 + 4 * lg, 16 * vt);
-                    acc[vt] = mma(a, pb, acc[vt]);
+                    HalfT x0, x1;
+                    if constexpr (ES == 2) {
+                        // transposed reads: source lane jj of the 16-lane group
+                        // points at row rowA + jj/4, columns 16vt + 4(jj%4) .. +3
+                        const int jj = lane & 15;
+                        const int ra = 32 * ks + 4 * lg + (jj >> 2), rb = ra + 16;
+                        const int col = 16 * vt + 4 * (jj & 3);
+                        const int unit = col * 2 / 16, inner = (col * 2) & 15;
+                        x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_off(ra, unit) + inner))));
+                        x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_off(rb, unit) + inner))));
+                    } else {
+                        const int col = 16 * vt + lc;
+                        const int unit = col * 4 / 16, inner = (col * 4) & 15;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            x0[i] = *(const float *)(vb + v_off(32 * ks + 4 * lg + i, unit) + inner);
+                            x1[i] = *(const float *)(vb + v_off(32 * ks + 16 + 4 * lg + i, unit) + inner);
+                        }
+                    }
+                    acc[vt] = mma(join<T>(x0, x1), pb[ks], acc[vt]);
                 }
             }
         }
+        if (j + 1 < M) {
+            __syncthreads();  // every wave is done with V_j
+            stage_v(j + 1);
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
     }
 
-    // ---- store: lane holds o[t_loc][16vt + 4lg + i]
-    if (t_loc < nt) {
-        T *dst = o + ((t0 + t_loc) * HV + hv) * (int64_t)VD + 4 * lg;
+    // ---- store: lane holds o[t_loc][vb0 + 16vt + 4lg + i]
+    const rsrc_t ro = make_rsrc(o + (t0 * HV + hv) * (int64_t)VD + vb0, span(nt, HV * VD * ES, VRB));
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-            typename Frag<T>::half o4;
+    for (int vt = 0; vt < NVT; ++vt) {
+        HalfT o4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[vt][i]);
-            *(typename Frag<T>::half *)(dst + 16 * vt) = o4;
-        }
+        for (int i = 0; i < 4; ++i) o4[i] = from_f32<T>(acc[vt][i]);
+        const uint32_t off = (uint32_t)((t_loc * HV * VD + 16 * vt + 4 * lg) * ES);
+        if constexpr (ES == 2)
+            buf_store8(ro, off, __builtin_bit_cast(uint2, o4));
+        else
+            buf_store16(ro, off, __builtin_bit_cast(uint4, o4));
     }
 }
 
-template <typename T, int KD, int VD>
+template <typename T, int KD, int VB>
 static hipError_t launch_chunk_o_t(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
-    dim3 grid((unsigned)p.max_tok_chunks, (unsigned)a.HV);
-    hipLaunchKernelGGL((gdp_chunk_o_k<T, KD, VD>), grid, dim3(256), 0, stream,
+    dim3 grid((unsigned)p.max_tok_chunks, (unsigned)a.HV, (unsigned)(a.V / VB));
+    hipLaunchKernelGGL((gdp_chunk_o_k<T, KD, VB>), grid, dim3(256), 0, stream,
                        (const T *)a.q, (const T *)a.k, a.k_rnorm, (const T *)a.v_new, (const T *)a.h, a.g,
-                       a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.scale, (T *)a.o);
+                       a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.V, a.h_chunks, a.scale, (T *)a.o);
     return hipGetLastError();
 }
 
-// bf16: K in {64, 128} x V in {64, 128, 256}; f32 (small-case reference
-// precision): K = 64, V in {64, 128}.
+// bf16: K in {64, 128} x V in {64, 128, 256} (V = 256 as two 128-column
+// slabs); f32 (small-case reference precision): K = 64, V in {64, 128}.
 static hipError_t launch_chunk_o_bf16(const ChunkParams &p, hipStream_t stream) {
     const int K = p.a.K, V = p.a.V;
     if (K == 64 && V == 64) return launch_chunk_o_t<bf16, 64, 64>(p, stream);
-    if (K == 64 && V == 128) return launch_chunk_o_t<bf16, 64, 128>(p, stream);
-    if (K == 64 && V == 256) return launch_chunk_o_t<bf16, 64, 256>(p, stream);
+    if (K == 64 && (V == 128 || V == 256)) return launch_chunk_o_t<bf16, 64, 128>(p, stream);
     if (K == 128 && V == 64) return launch_chunk_o_t<bf16, 128, 64>(p, stream);
-    if (K == 128 && V == 128) return launch_chunk_o_t<bf16, 128, 128>(p, stream);
-    if (K == 128 && V == 256) return launch_chunk_o_t<bf16, 128, 256>(p, stream);
+    if (K == 128 && (V == 128 || V == 256)) return launch_chunk_o_t<bf16, 128, 128>(p, stream);
     return hipErrorInvalidValue;
 }
 static hipError_t launch_chunk_o_f32(const ChunkParams &p, hipStream_t stream) {

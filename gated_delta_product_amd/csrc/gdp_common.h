@@ -131,9 +131,34 @@ __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a 
 __device__ __forceinline__ uint32_t small_div_magic(int d) { return d == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)d + 1u; }
 __device__ __forceinline__ uint32_t small_div(uint32_t x, uint32_t magic) { return magic ? __umulhi(x, magic) : x; }
 
+// A value the caller knows is the same in every lane, made visibly uniform
+// (scalar registers) for the compiler.
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Inclusive prefix sum of a 64-bit value over the 64 lanes of a wave.
+__device__ __forceinline__ int64_t wave_inclusive_sum_i64(int64_t x) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = __shfl_up(x, d, 64);
+        if (lane_id() >= d) x += y;
+    }
+    return x;
+}
+// Sum of a 64-bit value over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
 // Block-cooperative lookup of linear item `id` over sequences, where
 // sequence i owns ceil(len_i * rows_per_token / chunk) consecutive items.
-// Every thread of the block must call it (it uses barriers).  Returns the
+// Every thread of the block must call it (it uses barriers); wave 0 scans
+// the sequences 64 at a time, so any block size works.  Returns the
 // sequence (or -1 if id is past the last item), the item's index inside its
 // sequence, and the number of items of all earlier sequences.
 struct ChunkLoc {
@@ -152,52 +177,49 @@ __device__ __forceinline__ ChunkLoc find_chunk(const int32_t *cu, int64_t nseq, 
         seq_bounds(nullptr, T, r.seq < 0 ? 0 : r.seq, r.bos, r.eos);
         return r;
     }
-    __shared__ int64_t s_scan[256];
     __shared__ int64_t s_found[3];
-    const int tid = threadIdx.x, nt = blockDim.x;
-    if (tid == 0) { s_found[0] = -1; s_found[1] = 0; s_found[2] = 0; }
-    int64_t carry = 0;
-    for (int64_t i0 = 0; i0 < nseq; i0 += nt) {
-        __syncthreads();
-        const int64_t i = i0 + tid;
-        int64_t n = 0;
-        if (i < nseq) {
-            int64_t b, e;
-            seq_bounds(cu, T, i, b, e);
-            n = ceil_div64((e - b) * rows_per_token, chunk);
+    if (wave_id() == 0) {
+        const int lane = lane_id();
+        if (lane == 0) {
+            s_found[0] = -1;
+            s_found[1] = 0;
+            s_found[2] = 0;
         }
-        s_scan[tid] = n;
-        __syncthreads();
-        for (int d = 1; d < nt; d <<= 1) {
-            int64_t y = tid >= d ? s_scan[tid - d] : 0;
-            __syncthreads();
-            s_scan[tid] += y;
-            __syncthreads();
+        int64_t carry = 0;
+        for (int64_t i0 = 0; i0 < nseq; i0 += 64) {
+            const int64_t i = i0 + lane;
+            int64_t n = 0;
+            if (i < nseq) {
+                int64_t b, e;
+                seq_bounds(cu, T, i, b, e);
+                n = ceil_div64((e - b) * rows_per_token, chunk);
+            }
+            const int64_t incl = carry + wave_inclusive_sum_i64(n);
+            const int64_t excl = incl - n;
+            if (i < nseq && n > 0 && id >= excl && id < incl) {  // at most one lane
+                s_found[0] = i;
+                s_found[1] = id - excl;
+                s_found[2] = excl;
+            }
+            carry = __shfl(incl, 63, 64);
         }
-        const int64_t incl = carry + s_scan[tid];
-        const int64_t excl = incl - n;
-        if (i < nseq && n > 0 && id >= excl && id < incl) {
-            s_found[0] = i;
-            s_found[1] = id - excl;
-            s_found[2] = excl;
-        }
-        carry += s_scan[nt - 1];
     }
     __syncthreads();
-    r.seq = s_found[0];
-    r.c = s_found[1];
-    r.base = s_found[2];
+    r.seq = uniform_i64(s_found[0]);
+    r.c = uniform_i64(s_found[1]);
+    r.base = uniform_i64(s_found[2]);
     if (r.seq >= 0) seq_bounds(cu, T, r.seq, r.bos, r.eos);
     else { r.bos = 0; r.eos = 0; }
     __syncthreads();
     return r;
 }
 
-// Number of items of sequences [0, i) (block-cooperative, barriers inside).
+// Number of items of sequences [0, i) (block-cooperative, barriers inside;
+// any block size up to 1024 threads).
 __device__ __forceinline__ int64_t items_before(const int32_t *cu, int64_t T, int64_t rows_per_token,
                                                 int64_t chunk, int64_t i) {
     if (cu == nullptr) return i * ceil_div64(T * rows_per_token, chunk);
-    __shared__ int64_t s_red[256];
+    __shared__ int64_t s_part[16];
     const int tid = threadIdx.x, nt = blockDim.x;
     int64_t acc = 0;
     for (int64_t j = tid; j < i; j += nt) {
@@ -205,16 +227,14 @@ __device__ __forceinline__ int64_t items_before(const int32_t *cu, int64_t T, in
         seq_bounds(cu, T, j, b, e);
         acc += ceil_div64((e - b) * rows_per_token, chunk);
     }
+    acc = wave_sum_i64(acc);
     __syncthreads();
-    s_red[tid] = acc;
+    if (lane_id() == 0) s_part[tid >> 6] = acc;
     __syncthreads();
-    for (int d = nt / 2; d > 0; d >>= 1) {
-        if (tid < d) s_red[tid] += s_red[tid + d];
-        __syncthreads();
-    }
-    int64_t r = s_red[0];
+    int64_t r = 0;
+    for (int w = 0; w < (nt + 63) / 64; ++w) r += s_part[w];
     __syncthreads();
-    return r;
+    return uniform_i64(r);
 }
 
 // ---------------------------------------------------------------- tile staging
