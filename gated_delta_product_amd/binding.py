@@ -207,9 +207,9 @@ class ChunkBuffers:
         self.dims = dict(B=B, T=T, H=H, HV=HV, K=K, V=V, M=M, nseq=nseq)
         self.q, self.k, self.v, self.beta, self.g = q, k, v, beta, g
         self.cu_seqlens = cu_seqlens
-        self.k_rnorm = torch.empty((B, T * M, H), dtype=torch.float32, device=dev)
-        self.gcum = torch.empty((B, T * M, HV), dtype=torch.float32, device=dev)
-        self.kdecay = torch.empty((B, T * M, HV), dtype=torch.float32, device=dev)
+        self.k_rnorm = torch.empty((B, H, T * M), dtype=torch.float32, device=dev)
+        self.gcum = torch.empty((B, HV, T * M), dtype=torch.float32, device=dev)
+        self.kdecay = torch.empty((B, HV, T * M), dtype=torch.float32, device=dev)
         self.w = torch.empty((B, T * M, HV, K), dtype=dt, device=dev)
         self.u = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
         self.v_new = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)

@@ -115,6 +115,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     const int lg = lane >> 4, lc = lane & 15;
     const int ldk = H * KD, ldw = HV * KD, ldv = HV * VD;  // global row strides (elements)
     const int64_t r0 = bos * M;  // first expanded row of the sequence
+    const int64_t h0r = hm_index(cu ? 0 : seq, HV, hv, Ttok * M, r0);  // kdecay / gcum of row r0
 
     auto clamp_rows = [](int r) { return r < 0 ? 0 : (r < C ? r : C); };
     // bytes a buffer resource must cover for n rows of `width_b` bytes
@@ -139,10 +140,10 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         const char *pw = (const char *)(w + ((r0 + RPB * sl) * HV + hv) * KD);
         const char *pk = (const char *)(k + ((r0 + RPB * sl) * H + hk) * KD);
         const char *pu = (const char *)(u + ((r0 + RPB * sl) * HV + hv) * VD);
-        const char *pd = (const char *)(kdecay + r0 * HV + hv);
-        const char *pg = (const char *)(gcum + r0 * HV + hv);
+        const char *pd = (const char *)(kdecay + h0r);
+        const char *pg = (const char *)(gcum + h0r);
         const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * ldv * ES,
-                      st4 = (int64_t)C * HV * 4;
+                      st4 = (int64_t)C * 4;
         // rows [0, nr) of a tile with `rb`-byte rows `ld` bytes apart: one
         // 16-byte unit per lane, 1 KiB per instruction
         auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb, int nrmax) {
@@ -155,14 +156,16 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         };
         int rem_pf = (int)rows;
         auto prefetch = [&](int c) {
-            const int nr = clamp_rows(rem_pf - C * c - RPB * sl);
-            const int n = clamp_rows(rem_pf - C * c);
+            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c - RPB * sl));
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c));
             const int64_t oc = c;
             rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw, RPB);
             rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw, RPB);
             rows_to_l2(pu + oc * stu, nr < RPB ? nr : RPB, ldv * ES, rbu, RPB);
-            dma4(make_rsrc(pd + oc * st4, span(n, HV * 4, 4)), (uint32_t)(lane * HV * 4), pf);
-            dma4(make_rsrc(pg + oc * st4, span(n, HV * 4, 4)), (uint32_t)(lane * HV * 4), pf);
+            if (sl == 0) {  // 256 contiguous bytes each: one block of the head is enough
+                dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
+                dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
+            }
         };
         for (int c = 2; c < PF; ++c) prefetch(c);
         lds_barrier();
@@ -203,14 +206,14 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
         for (int i = 0; i < NU; ++i)
             ou[i] = (uint32_t)(((i * (64 / UUPR) + lane / UUPR) * ldv) * ES + (lane % UUPR) * 16 - 1024 * (i % 4));
-        const uint32_t o4 = (uint32_t)(lane * HV * 4);
+        const uint32_t o4 = (uint32_t)(lane * 4);
 
         const char *pt = mw == 0 ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
         const int ldt = mw == 0 ? ldw : ldk;
         const int64_t stt = (int64_t)C * ldt * ES;
         const char *pu = (const char *)(u + (r0 * HV + hv) * VD + 16 * sl);
-        const char *p4 = mw == 0 ? (const char *)(kdecay + r0 * HV + hv) : (const char *)(gcum + r0 * HV + hv);
-        const int64_t stu = (int64_t)C * ldv * ES, st4 = (int64_t)C * HV * 4;
+        const char *p4 = mw == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
+        const int64_t stu = (int64_t)C * ldv * ES, st4 = (int64_t)C * 4;
         const int tile_off = mw == 0 ? OFW : OFK;
         const int off4 = mw == 0 ? OFD : OFG;
         int rem_issue = (int)rows;
@@ -237,7 +240,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                     dma16_m0<1024 * (i % 4)>(ru, ou[i]);
                 });
             }
-            dma4(make_rsrc(p4, span(n, HV * 4, 4)), o4, ring_base + st * SB + off4);
+            dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
             pt += stt;
             pu += stu;
             p4 += st4;

@@ -136,7 +136,7 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
                 }
             }
         }
-        rkl = lane < nt ? k_rnorm[((t0 + lane) * M + j) * H + hk] : 0.f;
+        rkl = lane < nt ? k_rnorm[hm_index(cu ? 0 : loc.seq, H, hk, Ttok * M, (t0 + lane) * M + j)] : 0.f;
     };
     load_k(0);
 

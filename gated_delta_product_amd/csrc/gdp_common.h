@@ -237,6 +237,13 @@ __device__ __forceinline__ int64_t items_before(const int32_t *cu, int64_t T, in
     return uniform_i64(r);
 }
 
+// Index of (head hd, expanded row e) in a head-major per-row array
+// [B, NH, T*M]: e is the flattened expanded row over all batch rows, bi the
+// batch row it belongs to (0 for packed sequences) and TM = T*M.
+__device__ __forceinline__ int64_t hm_index(int64_t bi, int nh, int hd, int64_t TM, int64_t e) {
+    return (bi * nh + hd) * TM + (e - bi * TM);
+}
+
 // ---------------------------------------------------------------- tile staging
 // Copy ROWS rows of D elements (global row stride `rs` elements) into a
 // row-major LDS tile with row stride LD, using 16-byte units spread over the

@@ -37,10 +37,12 @@ __device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
     return -(ea * sp);
 }
 
-// Copy unit: a 16-byte vector when VEC16, else one element.
+// Copy unit: a 16-byte vector when VEC16, else one element.  (A native
+// vector type, so arrays of units stay in registers.)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 template <typename T, bool VEC16>
 struct Unit {
-    typedef typename std::conditional<VEC16, uint4, T>::type type;
+    typedef typename std::conditional<VEC16, u32x4_t, T>::type type;
     static constexpr int elems = VEC16 ? (int)(16 / sizeof(T)) : 1;
 };
 
@@ -62,31 +64,50 @@ gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
     const int hpg = H / G;
     const int HN = H * N;
 
-    const int64_t nv = (int64_t)M * H * P / E;  // value units
-    const int64_t nk = (int64_t)M * HN / E;     // key units (expanded)
-    const int64_t nq = (int64_t)HN / E;         // query units (expanded)
-    const int64_t kbase = (int64_t)M * H * P;   // key segment offset in x
-    const int64_t qbase = kbase + (int64_t)M * G * N;
+    const int nv = M * H * P / E;  // value units
+    const int nk = M * HN / E;     // key units (expanded)
+    const int nq = HN / E;         // query units (expanded)
+    const int ntot = nv + nk + nq;
+    const int kbase = M * H * P;   // key segment offset in x
+    const int qbase = kbase + M * G * N;
 
     U *vo = (U *)(v + tok * (int64_t)M * H * P);
     U *ko = (U *)(k + tok * (int64_t)M * HN);
     U *qo = (U *)(q + tok * (int64_t)HN);
     const U *xv = (const U *)xr;
 
-    for (int64_t i = threadIdx.x; i < nv + nk + nq; i += blockDim.x) {
-        if (i < nv) {
-            // value copies are already in (copy, head, dim) order
-            vo[i] = xv[i];
-        } else if (i < nv + nk) {
-            const int64_t e = (i - nv) * E;  // element within the token's key copies
-            const int j = (int)(e / HN);
-            const int rem = (int)(e - (int64_t)j * HN);
-            const int h = rem / N, n = rem - (rem / N) * N;
-            ko[i - nv] = *(const U *)(xr + kbase + (int64_t)j * G * N + (h / hpg) * N + n);
-        } else {
-            const int e = (int)((i - nv - nk) * E);
-            const int h = e / N, n = e - (e / N) * N;
-            qo[i - nv - nk] = *(const U *)(xr + qbase + (h / hpg) * N + n);
+    // Batches of UB units per thread: all loads of a batch are issued before
+    // its stores, so each thread keeps UB 16-byte reads in flight.
+    constexpr int UB = 8;
+    for (int base = 0; base < ntot; base += UB * 256) {
+        U val[UB];
+#pragma unroll
+        for (int it = 0; it < UB; ++it) {
+            const int i = base + (int)threadIdx.x + 256 * it;
+            if (i < nv) {
+                // value copies are already in (copy, head, dim) order
+                val[it] = xv[i];
+            } else if (i < nv + nk) {
+                const int e = (i - nv) * E;  // element within the token's key copies
+                const int j = e / HN;
+                const int rem = e - j * HN;
+                const int h = rem / N, n = rem - h * N;
+                val[it] = *(const U *)(xr + kbase + j * G * N + (h / hpg) * N + n);
+            } else if (i < ntot) {
+                const int e = (i - nv - nk) * E;
+                const int h = e / N, n = e - h * N;
+                val[it] = *(const U *)(xr + qbase + (h / hpg) * N + n);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < UB; ++it) {
+            const int i = base + (int)threadIdx.x + 256 * it;
+            if (i < nv)
+                vo[i] = val[it];
+            else if (i < nv + nk)
+                ko[i - nv] = val[it];
+            else if (i < ntot)
+                qo[i - nv - nk] = val[it];
         }
     }
     // gates: beta for (copy, head) = M*H values, then g for H heads

@@ -29,7 +29,9 @@ namespace {
 constexpr int C = 64;      // chunk rows
 constexpr int LDA = C + 4;  // fp32 row stride of L and A in LDS
 
-template <typename T> struct Pad { static constexpr int value = 32 / (int)sizeof(T); };
+// 16 bytes of padding per LDS row: row reads of 16 consecutive rows hit 16
+// distinct bank groups
+template <typename T> struct Pad { static constexpr int value = 16 / (int)sizeof(T); };
 
 }  // namespace
 
@@ -43,11 +45,16 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
     constexpr int LDV = VD + Pad<T>::value;
+    constexpr int LV_BYTES = (C * LDA * 4 > C * LDV * (int)sizeof(T)) ? C * LDA * 4 : C * LDV * (int)sizeof(T);
+    constexpr int VUPR = VD * (int)sizeof(T) / 16;   // 16-byte units per V row
+    constexpr int VPT = C * VUPR / 256;               // V units per thread
     __shared__ __attribute__((aligned(16))) T Ks[C * LDK];
-    __shared__ __attribute__((aligned(16))) T Vs[C * LDV];
-    __shared__ __attribute__((aligned(16))) float Lm[C * LDA];
+    // L while A is being built, then the V tile (V waits in registers)
+    __shared__ __attribute__((aligned(16))) char LV[LV_BYTES];
     __shared__ __attribute__((aligned(16))) float Am[C * LDA];
-    __shared__ float s_beta[C], s_gam[C], s_rk[C], s_ws[C];
+    __shared__ __attribute__((aligned(16))) float s_beta[C], s_gam[C], s_rk[C], s_ws[C];
+    float *Lm = (float *)LV;
+    T *Vs = (T *)LV;
 
     const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, blockIdx.x);
     if (loc.seq < 0) return;
@@ -58,10 +65,20 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     const int n = (int)((rend - r0) < C ? (rend - r0) : C);
     const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
+    const int64_t bi = cu ? 0 : loc.seq, TM = Ttok * M;  // head-major per-row outputs
 
-    // ---- stage K (with row norms) and V
+    // ---- V into registers now (it is needed last), K into LDS with row norms
+    uint4 vreg[VPT];
+    {
+        const T *vsrc = v + (r0 * HV + hv) * (int64_t)VD;
+#pragma unroll
+        for (int it = 0; it < VPT; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
+            vreg[it] = row < n ? *(const uint4 *)(vsrc + (int64_t)row * HV * VD + cu16 * (16 / (int)sizeof(T)))
+                               : make_uint4(0, 0, 0, 0);
+        }
+    }
     stage_tile<T, C, KD, LDK, 256>(Ks, k + (r0 * H + hk) * (int64_t)KD, (int64_t)H * KD, n, s_rk);
-    stage_tile<T, C, VD, LDV, 256>(Vs, v + (r0 * HV + hv) * (int64_t)VD, (int64_t)HV * VD, n, nullptr);
     if (wv == 0) {
         const int64_t e = r0 + lane;
         const bool in = lane < n;
@@ -70,18 +87,18 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         const float gam = wave_inclusive_sum(lg_decay);
         s_beta[lane] = b;
         s_gam[lane] = gam;
-        if (in) gcum[e * HV + hv] = gam * 1.4426950408889634f;  // log2 units for chunk_h
+        if (in) gcum[hm_index(bi, HV, hv, TM, e)] = gam * 1.4426950408889634f;  // log2 units for chunk_h
     }
     __syncthreads();
     if (wv == 0) {
         const float rk = 1.0f / sqrtf(s_rk[lane] + 1e-6f);
         s_rk[lane] = rk;
         s_ws[lane] = s_beta[lane] * __expf(s_gam[lane]) * rk;
-        if (lane < n && (hv % (HV / H)) == 0) k_rnorm[(r0 + lane) * H + hk] = rk;
+        if (lane < n && (hv % (HV / H)) == 0) k_rnorm[hm_index(bi, H, hk, TM, r0 + lane)] = rk;
         if (lane < n) {  // decay of the row's key to the chunk end, times its norm
             const float g2 = s_gam[lane] * 1.4426950408889634f;
             const float gl2 = s_gam[n - 1] * 1.4426950408889634f;
-            kdecay[(r0 + lane) * HV + hv] = rk * exp2f(gl2 - g2);
+            kdecay[hm_index(bi, HV, hv, TM, r0 + lane)] = rk * exp2f(gl2 - g2);
         }
     }
     __syncthreads();
@@ -89,6 +106,12 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // ---- L = strictly lower beta_a exp(g_a - g_b) r_a r_b (K K^T)_ab, row block wv
     {
         const int ra = 16 * wv;
+        // factors of this lane's four rows: beta * rnorm, and gamma
+        const f32x4 b4 = *(const f32x4 *)&s_beta[ra + 4 * lg], r4 = *(const f32x4 *)&s_rk[ra + 4 * lg];
+        const f32x4 gr = *(const f32x4 *)&s_gam[ra + 4 * lg];
+        f32x4 rowf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rowf[i] = b4[i] * r4[i];
         for (int ct = 0; ct < 4; ++ct) {
             f32x4 acc = zero4();
             if (ct <= wv) {
@@ -100,12 +123,11 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 }
             }
             const int col = 16 * ct + lc;
+            const float gc = s_gam[col], rc = s_rk[col];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = ra + 4 * lg + i;
-                float val = 0.f;
-                if (col < row)
-                    val = s_beta[row] * __expf(s_gam[row] - s_gam[col]) * s_rk[row] * s_rk[col] * acc[i];
+                const float val = col < row ? rowf[i] * rc * __expf(gr[i] - gc) * acc[i] : 0.f;
                 Lm[row * LDA + col] = val;
             }
         }
@@ -120,8 +142,12 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float s = (i == lane) ? 1.f : 0.f;
+                f32x4 lr[4];  // row i of the diagonal block (same address in every lane)
 #pragma unroll
-                for (int b = 0; b < i; ++b) s -= Lm[(d0 + i) * LDA + d0 + b] * x[b];
+                for (int q = 0; q < 4; ++q)
+                    if (4 * q < i) lr[q] = *(const f32x4 *)&Lm[(d0 + i) * LDA + d0 + 4 * q];
+#pragma unroll
+                for (int b = 0; b < i; ++b) s -= lr[b >> 2][b & 3] * x[b];
                 x[i] = s;
             }
 #pragma unroll
@@ -168,6 +194,14 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         __syncthreads();
     }
 
+    // ---- L is dead: the V tile moves from registers into its space
+#pragma unroll
+    for (int it = 0; it < VPT; ++it) {
+        const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
+        *(uint4 *)(Vs + row * LDV + cu16 * (16 / (int)sizeof(T))) = vreg[it];
+    }
+    __syncthreads();
+
     // ---- u^T = V^T (A diag(beta))^T and w^T = Khat^T (A diag(beta e^gamma r))^T
     //      wave wv produces output rows a in [16 wv, 16 wv + 16)
     {
@@ -177,12 +211,16 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks < nks) {
+                const int b0 = 32 * ks + 8 * lg;
+                const f32x4 a0 = *(const f32x4 *)&Am[a_row * LDA + b0], a1 = *(const f32x4 *)&Am[a_row * LDA + b0 + 4];
+                const f32x4 be0 = *(const f32x4 *)&s_beta[b0], be1 = *(const f32x4 *)&s_beta[b0 + 4];
+                const f32x4 ws0 = *(const f32x4 *)&s_ws[b0], ws1 = *(const f32x4 *)&s_ws[b0 + 4];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int b = 32 * ks + 8 * lg + m;
-                    const float av = Am[a_row * LDA + b];
-                    bu[ks][m] = from_f32<T>(av * s_beta[b]);
-                    bw[ks][m] = from_f32<T>(av * s_ws[b]);
+                for (int m = 0; m < 4; ++m) {
+                    bu[ks][m] = from_f32<T>(a0[m] * be0[m]);
+                    bw[ks][m] = from_f32<T>(a0[m] * ws0[m]);
+                    bu[ks][4 + m] = from_f32<T>(a1[m] * be1[m]);
+                    bw[ks][4 + m] = from_f32<T>(a1[m] * ws1[m]);
                 }
             }
         }

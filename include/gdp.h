@@ -112,14 +112,14 @@ gdp_status gdp_prefill_prepare(
  *   beta   [B, T*M, HV]     in, float32
  *   g      [B, T,   HV]     in, float32 natural-log decay per token; it acts
  *                           on copy 0 of its token
- *   k_rnorm[B, T*M, H]      float32 1/sqrt(sum k^2 + 1e-6) per key row;
+ *   k_rnorm[B, H, T*M]      float32 1/sqrt(sum k^2 + 1e-6) per key row (head-major);
  *                           written by gdp_recompute_w_u, read by gdp_chunk_o
- *   gcum   [B, T*M, HV]     float32 within-chunk cumulative decay in log2
+ *   gcum   [B, HV, T*M]     float32 (head-major) within-chunk cumulative decay in log2
  *                           units per expanded row (the sum of g*log2(e) over
  *                           the first-copy rows of the chunk up to and
  *                           including the row); written by gdp_recompute_w_u,
  *                           read by gdp_chunk_h
- *   kdecay [B, T*M, HV]     float32 per expanded row e of chunk c:
+ *   kdecay [B, HV, T*M]     float32 (head-major) per expanded row e of chunk c:
  *                           k_rnorm[e] * 2^(gcum[last row of c] - gcum[e]),
  *                           the factor with which the row's normalised key
  *                           enters the state at the end of its chunk;
