@@ -135,6 +135,8 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         // data lands in a scratch LDS area that nothing reads.
         constexpr int PF = 5;                    // prefetch distance in chunks
         constexpr int RPB = C / S;               // rows per block per chunk
+        static_assert(RPB * KD * ES / 128 <= 64 && RPB * VD * ES / 128 <= 64 && KD * ES >= 128 && VD * ES >= 128,
+                      "one 4-byte load per line must cover a block's rows");
         const uint32_t pf = lds_addr(&Pf[0]);
         const int rbw = KD * ES, rbu = VD * ES;  // row bytes of w / k and of u
         const char *pw = (const char *)(w + ((r0 + RPB * sl) * HV + hv) * KD);
@@ -145,23 +147,20 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * ldv * ES,
                       st4 = (int64_t)C * 4;
         // rows [0, nr) of a tile with `rb`-byte rows `ld` bytes apart: one
-        // 16-byte unit per lane, 1 KiB per instruction
-        auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb, int nrmax) {
-            const int lpr = rb / 16;
+        // 4-byte load per 128-byte line is enough to bring it into L2
+        auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb) {
+            const int lpr = rb / 128;  // lines per row
             const rsrc_t r = make_rsrc(base, span(nr, ld, rb));
-            for (int i = 0; i < nrmax * lpr; i += 64) {
-                const int idx = i + lane;
-                dma16(r, (uint32_t)((idx / lpr) * ld + (idx % lpr) * 16), pf);
-            }
+            dma4(r, (uint32_t)((lane / lpr) * ld + (lane % lpr) * 128), pf);  // rows >= nr: out of range
         };
         int rem_pf = (int)rows;
         auto prefetch = [&](int c) {
             const int nr = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c - RPB * sl));
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c));
             const int64_t oc = c;
-            rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw, RPB);
-            rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw, RPB);
-            rows_to_l2(pu + oc * stu, nr < RPB ? nr : RPB, ldv * ES, rbu, RPB);
+            rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw);
+            rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw);
+            rows_to_l2(pu + oc * stu, nr < RPB ? nr : RPB, ldv * ES, rbu);
             if (sl == 0) {  // 256 contiguous bytes each: one block of the head is enough
                 dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
                 dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
@@ -171,7 +170,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         lds_barrier();
         for (int c = 0; c < nch; ++c) {
             prefetch(c + PF);
-            wait_vmcnt<32>();  // bound the number of prefetches in flight
+            wait_vmcnt<24>();  // bound the number of prefetches in flight
             lds_barrier();
         }
         lds_barrier();
