@@ -34,6 +34,7 @@ class ChunkArgs(ctypes.Structure):
         ("cu_seqlens", _vp), ("num_seqs", _i64), ("h_chunks", _i64),
         ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("g", _vp), ("k_rnorm", _vp),
         ("gcum", _vp), ("kdecay", _vp), ("w", _vp), ("u", _vp), ("v_new", _vp), ("h", _vp), ("o", _vp),
+        ("h0", _vp), ("ht", _vp),
     ]
 
 
@@ -171,10 +172,11 @@ class ChunkBuffers:
     """All tensors of one chunk forward (inputs, scratch and outputs)."""
 
     def __init__(self, q, k, v, beta, g, cu_seqlens=None, scale=None, h_chunks=None,
-                 cu_seqlens_host=None, num_householder=None):
-        dev = _need_cuda(q, k, v, beta, g, cu_seqlens)
-        for t, nm in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (g, "g")):
-            _contig(t, nm)
+                 cu_seqlens_host=None, num_householder=None, initial_state=None, output_final_state=False):
+        dev = _need_cuda(q, k, v, beta, g, cu_seqlens, initial_state)
+        for t, nm in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (g, "g"), (initial_state, "initial_state")):
+            if t is not None:
+                _contig(t, nm)
         if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
             raise ValueError("q, k, v must be 4-D")
         B, T, H, K = q.shape
@@ -186,8 +188,8 @@ class ChunkBuffers:
             raise ValueError("v must be [B, T*M, HV, V]")
         if tuple(beta.shape) != (B, T * M, HV) or beta.dtype != torch.float32:
             raise ValueError("beta must be float32 [B, T*M, HV]")
-        if tuple(g.shape) != (B, T, HV) or g.dtype != torch.float32:
-            raise ValueError("g must be float32 [B, T, HV]")
+        if g is not None and (tuple(g.shape) != (B, T, HV) or g.dtype != torch.float32):
+            raise ValueError("g must be float32 [B, T, HV] (or None: ungated)")
         if k.dtype != q.dtype or v.dtype != q.dtype:
             raise ValueError("q, k, v must share a dtype")
         nseq = B
@@ -203,8 +205,13 @@ class ChunkBuffers:
                 h_chunks = num_state_chunks(T, M, 1, cu_seqlens_host)
             else:
                 h_chunks = math.ceil(T * M / CHUNK) + nseq
+        if initial_state is not None and (tuple(initial_state.shape) != (nseq, HV, V, K)
+                                          or initial_state.dtype != torch.float32):
+            raise ValueError("initial_state must be float32 [nseq, HV, V, K] = %s" % ((nseq, HV, V, K),))
         dt = q.dtype
         self.dims = dict(B=B, T=T, H=H, HV=HV, K=K, V=V, M=M, nseq=nseq)
+        self.h0 = initial_state
+        self.ht = torch.empty((nseq, HV, V, K), dtype=torch.float32, device=dev) if output_final_state else None
         self.q, self.k, self.v, self.beta, self.g = q, k, v, beta, g
         self.cu_seqlens = cu_seqlens
         self.k_rnorm = torch.empty((B, H, T * M), dtype=torch.float32, device=dev)
@@ -221,9 +228,12 @@ class ChunkBuffers:
             scale=float(scale) if scale is not None else 0.0, dtype=_dtype_code(dt),
             cu_seqlens=None if cu_seqlens is None else cu_seqlens.data_ptr(),
             num_seqs=nseq, h_chunks=h_chunks,
-            q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), beta=beta.data_ptr(), g=g.data_ptr(),
+            q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), beta=beta.data_ptr(),
+            g=None if g is None else g.data_ptr(),
             k_rnorm=self.k_rnorm.data_ptr(), gcum=self.gcum.data_ptr(), kdecay=self.kdecay.data_ptr(), w=self.w.data_ptr(), u=self.u.data_ptr(),
-            v_new=self.v_new.data_ptr(), h=self.h.data_ptr(), o=self.o.data_ptr())
+            v_new=self.v_new.data_ptr(), h=self.h.data_ptr(), o=self.o.data_ptr(),
+            h0=None if initial_state is None else initial_state.data_ptr(),
+            ht=None if self.ht is None else self.ht.data_ptr())
 
     def set(self, **tensors):
         """Point a slot (e.g. h, v_new) at another tensor of the same shape."""
@@ -252,11 +262,15 @@ class ChunkBuffers:
         return self.o
 
 
-def chunk_fwd(q, k, v, beta, g, scale=None, cu_seqlens=None, cu_seqlens_host=None):
+def chunk_fwd(q, k, v, beta, g, scale=None, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+              output_final_state=False):
     """Chunked GDP forward.  q [B,T,H,K]; k [B,T*M,H,K]; v [B,T*M,HV,V];
-    beta [B,T*M,HV] f32; g [B,T,HV] f32 natural-log decay per token.
-    Returns the ChunkBuffers holding o and the intermediates (w, u, v_new, h)."""
-    buf = ChunkBuffers(q, k, v, beta, g, cu_seqlens=cu_seqlens, scale=scale, cu_seqlens_host=cu_seqlens_host)
+    beta [B,T*M,HV] f32; g [B,T,HV] f32 natural-log decay per token, or None
+    (ungated); initial_state [nseq,HV,V,K] f32 or None.
+    Returns the ChunkBuffers holding o, the intermediates (w, u, v_new, h) and,
+    if output_final_state, ht [nseq,HV,V,K] f32."""
+    buf = ChunkBuffers(q, k, v, beta, g, cu_seqlens=cu_seqlens, scale=scale, cu_seqlens_host=cu_seqlens_host,
+                       initial_state=initial_state, output_final_state=output_final_state)
     buf.forward()
     return buf
 

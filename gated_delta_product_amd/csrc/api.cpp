@@ -86,7 +86,7 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
         const char *name;
     } needs[] = {
         {ST_O, a->q, "q"},           {ST_WY | ST_H | ST_O, a->k, "k"}, {ST_WY, a->v, "v"},
-        {ST_WY, a->beta, "beta"},    {ST_WY | ST_O, a->g, "g"},        {ST_WY | ST_O, a->k_rnorm, "k_rnorm"},
+        {ST_WY, a->beta, "beta"},    {ST_WY | ST_O, a->k_rnorm, "k_rnorm"},
         {ST_WY | ST_H, a->gcum, "gcum"},    {ST_WY | ST_H, a->kdecay, "kdecay"},
         {ST_WY | ST_H, a->w, "w"},   {ST_WY | ST_H, a->u, "u"},        {ST_H | ST_O, a->v_new, "v_new"},
         {ST_H | ST_O, a->h, "h"},    {ST_O, a->o, "o"},
@@ -98,6 +98,13 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
             if (!aligned16(n.p)) return fail(GDP_ERR_INVALID, "%s is not 16-byte aligned", n.name);
         }
     }
+    // optional tensors: g (NULL = ungated), h0, ht
+    const struct {
+        const void *p;
+        const char *name;
+    } opt[] = {{a->g, "g"}, {a->h0, "h0"}, {a->ht, "ht"}};
+    for (const auto &o : opt)
+        if (o.p && !aligned16(o.p)) return fail(GDP_ERR_INVALID, "%s is not 16-byte aligned", o.name);
     out->a = *a;
     if (!(out->a.scale > 0.f)) out->a.scale = 1.0f / std::sqrt((float)a->K);
     out->nseq = empty ? 0 : nseq;

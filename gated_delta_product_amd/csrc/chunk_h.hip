@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(320)
 gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T *__restrict__ w,
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
-              T *__restrict__ v_new, T *__restrict__ hout) {
+              const float *__restrict__ h0, float *__restrict__ ht, T *__restrict__ v_new,
+              T *__restrict__ hout) {
     typedef typename Frag<T>::type FragT;
     typedef typename Frag<T>::half HalfT;
     constexpr int ES = (int)sizeof(T);
@@ -109,10 +110,23 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     const int64_t rows = (eos - bos) * M;
     const int nch = (int)ceil_div64(rows, C);
     const int64_t cbase = items_before(cu, Ttok, M, C, seq);
-    if (nch == 0) return;
 
     const int lane = lane_id(), wave = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
+    // The fp32 state of compute wave kw in its permuted K order (see below):
+    // element (kt, q) is S[16sl + lc][kw*KH + 32(kt/2) + 8lg + 4(kt%2) + q],
+    // four consecutive K indices per (kt), i.e. one 16-byte unit of h0 / ht.
+    auto state_off = [&](int kw_, int kt) {
+        return ((seq * HV + hv) * (int64_t)VD + 16 * sl + lc) * KD + kw_ * KH + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1);
+    };
+    if (nch == 0) {  // empty sequence: the final state is the initial one
+        if (ht != nullptr && wave < 2) {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+                *(f32x4 *)(ht + state_off(wave, kt)) = h0 ? *(const f32x4 *)(h0 + state_off(wave, kt)) : zero4();
+        }
+        return;
+    }
     const int ldk = H * KD, ldw = HV * KD, ldv = HV * VD;  // global row strides (elements)
     const int64_t r0 = bos * M;  // first expanded row of the sequence
     const int64_t h0r = hm_index(cu ? 0 : seq, HV, hv, Ttok * M, r0);  // kdecay / gcum of row r0
@@ -324,10 +338,15 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     // is read with the same permutation.
     f32x4 hs[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) hs[kt] = zero4();
+    for (int kt = 0; kt < NKT; ++kt) hs[kt] = h0 ? *(const f32x4 *)(h0 + state_off(kw, kt)) : zero4();
     FragT hb[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) hb[ks] = FragT{};
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hb[ks][q] = from_f32<T>(hs[2 * ks][q]);
+            hb[ks][4 + q] = from_f32<T>(hs[2 * ks + 1][q]);
+        }
     auto put_snapshot = [&](T *dst) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
@@ -346,7 +365,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             }
         }
     };
-    put_snapshot(Hs[0]);  // h[0] = 0
+    put_snapshot(Hs[0]);  // h[0]: the initial state
     lds_barrier();        // stage 0 landed
     int rem = (int)rows;  // rows left from the current chunk
 
@@ -419,21 +438,28 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             }
         // gl <= 0; rows past the end carry key decay 0
         const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
-        f32x4 uf[4];
+        // everything that does not need the partner's partial, before the
+        // barrier: u - own partial, its key-decayed copy, the decayed state
+        f32x4 ua[4], uk[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) uf[rt][q] = to_f32(uu[rt][q]);
-
-        // exchange partials (one buffer per ring stage; the step's barrier)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) Xs[ST][kw][rt][lane] = acc[rt];
-        lds_barrier();
+            for (int q = 0; q < 4; ++q) {
+                ua[rt][q] = to_f32(uu[rt][q]) - acc[rt][q];
+                uk[rt][q] = ua[rt][q] * kd4[rt][q];
+            }
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) hs[kt][q] *= gl;
 
+        // exchange partials (one buffer per ring stage; the step's barrier)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) Xs[ST][kw][rt][lane] = acc[rt];
+        lds_barrier();
+
+        // v_new = (u - own) - other; the phase-2 operand kd * v_new as one
+        // fused multiply-add on the precomputed kd * (u - own)
         FragT vb[2];
         T *vt = Vt[c & 1];
         static_for<0, 4>([&](auto rtc) {
@@ -442,11 +468,8 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             HalfT v4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                // own + other is the same sum in both waves (addition
-                // commutes), so both hold bit-identical v_new
-                const float vn = uf[rt][q] - (acc[rt][q] + other[q]);
-                v4[q] = from_f32<T>(vn);
-                vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(vn * kd4[rt][q]);
+                v4[q] = from_f32<T>(ua[rt][q] - other[q]);
+                vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(__builtin_fmaf(-other[q], kd4[rt][q], uk[rt][q]));
             }
             // compute wave kw publishes rows [32kw, 32kw + 32)
             if constexpr ((rt >> 1) == kw) *(HalfT *)(&vt[lc * LDT + 16 * rt + 4 * lg]) = v4;
@@ -478,6 +501,10 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         if (c + 2 < nch) step(c + 2, I2{});
     }
     lds_barrier();  // publishes the last chunk's v_new
+    if (ht != nullptr) {
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) *(f32x4 *)(ht + state_off(kw, kt)) = hs[kt];
+    }
     };
     if (wave == 0)
         compute(std::integral_constant<int, 0>{});
@@ -493,7 +520,7 @@ static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
     const int64_t nblk = ((P + 7) / 8) * 8 * S;
     hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(320), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
-                       p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, (T *)a.v_new, (T *)a.h);
+                       p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h);
     return hipGetLastError();
 }
 

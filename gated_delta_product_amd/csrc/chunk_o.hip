@@ -116,7 +116,7 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
                              __builtin_bit_cast(HalfT, buf_load16(rq, off + 16)));
         }
     }
-    const float gl = lane < nt ? g[(t0 + lane) * HV + hv] : 0.f;
+    const float gl = (g != nullptr && lane < nt) ? g[(t0 + lane) * HV + hv] : 0.f;  // NULL: ungated
     FragT kf[4][NKS];
     float rkl = 0.f;
     auto load_k = [&](int j) {

@@ -84,7 +84,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         const int64_t e = r0 + lane;
         const bool in = lane < n;
         const float b = in ? beta[e * HV + hv] : 0.f;
-        const float lg_decay = (in && (e % M) == 0) ? g[(e / M) * HV + hv] : 0.f;
+        const float lg_decay = (g != nullptr && in && (e % M) == 0) ? g[(e / M) * HV + hv] : 0.f;  // NULL: ungated
         const float gam = wave_inclusive_sum(lg_decay);
         s_beta[lane] = b;
         s_gam[lane] = gam;

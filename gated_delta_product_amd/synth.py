@@ -92,6 +92,12 @@ def chunk_draws(B, T, H, HV, K, V, M, dtype, seed, a_sigma=1.0,
                 A_log=torch.from_numpy(A_log), dt_bias=torch.from_numpy(dt_bias))
 
 
+def initial_state_draws(nseq, HV, V, K, seed, sigma=0.1):
+    """A float32 initial state S [nseq, HV, V, K] ~ N(0, sigma^2)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return torch.from_numpy(_normal(rng, (nseq, HV, V, K), sigma))
+
+
 def varlen_lengths(n_req, lo, hi, seed):
     """Request lengths uniform in [lo, hi] (inclusive) and their cu_seqlens."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -111,7 +111,8 @@ gdp_status gdp_prefill_prepare(
  *   v      [B, T*M, HV, V]  in
  *   beta   [B, T*M, HV]     in, float32
  *   g      [B, T,   HV]     in, float32 natural-log decay per token; it acts
- *                           on copy 0 of its token
+ *                           on copy 0 of its token.  NULL selects the
+ *                           ungated rule (every decay is 0; the pages' g=None)
  *   k_rnorm[B, H, T*M]      float32 1/sqrt(sum k^2 + 1e-6) per key row (head-major);
  *                           written by gdp_recompute_w_u, read by gdp_chunk_o
  *   gcum   [B, HV, T*M]     float32 (head-major) within-chunk cumulative decay in log2
@@ -132,6 +133,15 @@ gdp_status gdp_prefill_prepare(
  *                           value); chunk c of sequence i is at index
  *                           (chunks of sequences < i) + c
  *   o      [B, T,   HV, V]  out of gdp_chunk_o
+ *   h0     [nseq, HV, V, K] in, float32, or NULL: the state S each sequence
+ *                           starts from (NULL: zero).  h[first chunk] is
+ *                           its storage-precision copy.  Read by gdp_chunk_h.
+ *   ht     [nseq, HV, V, K] out, float32, or NULL: the state S after each
+ *                           sequence's last row (h0, or zero, for an empty
+ *                           sequence).  Written by gdp_chunk_h.  Passing one
+ *                           call's ht as the next call's h0 continues the
+ *                           recurrence exactly (chunked prefill).
+ * nseq is num_seqs with cu_seqlens, else B.
  */
 typedef struct gdp_chunk_args {
     int64_t B;
@@ -160,11 +170,13 @@ typedef struct gdp_chunk_args {
     void *v_new;
     void *h;
     void *o;
+    const float *h0;
+    float *ht;
 } gdp_chunk_args;
 
 /* w, u, k_rnorm, gcum and kdecay from k, v, beta, g. */
 gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream);
-/* h and v_new from k, kdecay, gcum, w, u.  One serial pass per sequence and
+/* h, v_new and (if requested) ht from k, kdecay, gcum, w, u and h0.  One serial pass per sequence and
    value head over its chunks. */
 gdp_status gdp_chunk_h(const gdp_chunk_args *a, void *stream);
 /* o from q, k, k_rnorm, v_new, h, g. */

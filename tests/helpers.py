@@ -90,10 +90,11 @@ class Acc:
         assert self.rel() <= tol["rel_l2"], (self.name, self.rel())
 
 
-def oracle_pair(qn, kn, vn, bn, gn, M, scale, want_wu=True):
+def oracle_pair(qn, kn, vn, bn, gn, M, scale, want_wu=True, h0=None):
     """Run the oracle for one (sequence, value head) given float32 numpy
-    slices q [L,K], k [L*M,K], v [L*M,V], beta [L*M], g [L]."""
-    r = oracle.recurrence(qn, kn, vn, bn, gn, M, scale=scale, chunk=64)
+    slices q [L,K], k [L*M,K], v [L*M,V], beta [L*M], g [L] (or None: ungated)
+    and an optional initial state h0 [V,K]."""
+    r = oracle.recurrence(qn, kn, vn, bn, gn, M, scale=scale, chunk=64, h0=h0)
     if want_wu:
         w, u = oracle.wy(kn, vn, bn, gn, M, chunk=64)
         r["w"], r["u"] = w, u

@@ -87,6 +87,9 @@ BAD_CHUNK = [
     ("null k", dict(k=None), B.GDP_ERR_INVALID),
     ("misaligned v", dict(v=0x30008), B.GDP_ERR_INVALID),
     ("nan scale", dict(scale=float("nan")), B.GDP_ERR_INVALID),
+    ("misaligned g", dict(g=0x50008), B.GDP_ERR_INVALID),
+    ("misaligned h0", dict(h0=0xC0008), B.GDP_ERR_INVALID),
+    ("misaligned ht", dict(ht=0xD0004), B.GDP_ERR_INVALID),
 ]
 
 

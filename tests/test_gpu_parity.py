@@ -47,36 +47,42 @@ def _seqs_varlen(cu, M):
 
 
 def check_chunk(q, k, v, beta, g, seqs, hv_list, M, scale=None, cu=None, cu_host=None, tag="",
-                want_wu=True, buf=None):
+                want_wu=True, buf=None, h0=None):
     """Run the GPU forward (unless buf is given) and compare o, v_new, h, w, u
-    with the oracle on the listed (sequence, value head) pairs."""
+    (and the final state when an initial state h0 [nseq,HV,V,K] is given)
+    with the oracle on the listed (sequence, value head) pairs.  g may be
+    None (ungated)."""
     dt = q.dtype
     tol = TOL[dt]
     H, HV, K = q.shape[2], v.shape[2], q.shape[3]
     if buf is None:
-        buf = G.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), g.to(DEV), scale=scale,
+        buf = G.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), None if g is None else g.to(DEV),
+                          scale=scale,
                           cu_seqlens=None if cu is None else torch.as_tensor(cu, dtype=torch.int32).to(DEV),
-                          cu_seqlens_host=cu_host)
+                          cu_seqlens_host=cu_host, initial_state=None if h0 is None else h0.to(DEV),
+                          output_final_state=h0 is not None)
         torch.cuda.synchronize()
     sc = scale if scale is not None else 1.0 / math.sqrt(K)
-    items = [(s, hv) for s in seqs for hv in hv_list if s[2] > s[1]]
+    items = [(si, s, hv) for si, s in enumerate(seqs) for hv in hv_list if s[2] > s[1]]
     log("%s: %d (seq, head) pairs" % (tag, len(items)))
 
     def one(item):
-        (b, t0, t1, hbase), hv = item
+        si, (b, t0, t1, hbase), hv = item
         hk = hv // (HV // H)
         qn = f32(q[b, t0:t1, hk])
         kn = f32(k[b, t0 * M:t1 * M, hk])
         vn = f32(v[b, t0 * M:t1 * M, hv])
         bn = f32(beta[b, t0 * M:t1 * M, hv])
-        gn = f32(g[b, t0:t1, hv])
-        return oracle_pair(qn, kn, vn, bn, gn, M, sc, want_wu)
+        gn = None if g is None else f32(g[b, t0:t1, hv])
+        h0n = None if h0 is None else h0[si, hv].double().numpy()
+        return oracle_pair(qn, kn, vn, bn, gn, M, sc, want_wu, h0=h0n)
 
     refs = run_pairs(one, items)
-    accs = {n: Acc(n, raw_max_abs=(n == "o")) for n in (["o", "v_new", "h", "w", "u"] if want_wu
-                                                        else ["o", "v_new", "h"])}
+    names = ["o", "v_new", "h"] + (["w", "u"] if want_wu else []) + (["ht"] if h0 is not None else [])
+    # the final state is fp32 on both sides: judged raw
+    accs = {n: Acc(n, raw_max_abs=(n in ("o", "ht"))) for n in names}
     bf = dt == torch.bfloat16
-    for ((b, t0, t1, hbase), hv), r in zip(items, refs):
+    for (si, (b, t0, t1, hbase), hv), r in zip(items, refs):
         nc = math.ceil((t1 - t0) * M / 64)
         accs["o"].add(f32(buf.o[b, t0:t1, hv]), r["o"], bf)
         accs["v_new"].add(f32(buf.v_new[b, t0 * M:t1 * M, hv]), r["v_new"], bf)
@@ -84,6 +90,8 @@ def check_chunk(q, k, v, beta, g, seqs, hv_list, M, scale=None, cu=None, cu_host
         if want_wu:
             accs["w"].add(f32(buf.w[b, t0 * M:t1 * M, hv]), r["w"], bf)
             accs["u"].add(f32(buf.u[b, t0 * M:t1 * M, hv]), r["u"], bf)
+        if h0 is not None:
+            accs["ht"].add(f32(buf.ht[si, hv]), r["h_final"], False)
     for a in accs.values():
         a.check(tol)
     return buf
@@ -373,3 +381,61 @@ def test_long_prefill_path_with_prepare():
         a = Acc("o[%d]" % hv, raw_max_abs=True)
         a.add(f32(buf.o[0, :, hv]), r["o"])
         a.check(TOL[torch.bfloat16])
+
+
+# ------------------------------------------------- ungated rule, state chaining
+
+def test_ungated_matches_oracle_and_zero_decay():
+    """g = None (the pages' ungated call) against the oracle's ungated
+    recurrence, with GVA and a ragged tail; bit for bit the run with g = 0."""
+    B, T, H, HV, K, V, M = 2, 300, 2, 4, 128, 128, 2
+    d = synth.chunk_draws(B, T, H, HV, K, V, M, "bf16", synth.seed_of(2) + 7)
+    beta, _ = gates(d)
+    beta = beta.reshape(B, T * M, HV)
+    q, k, v = d["q"], d["k"], d["v"]
+    buf = check_chunk(q, k, v, beta, None, _seqs_equal(B, T, M), range(HV), M, tag="ungated")
+    zero = G.chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), torch.zeros(B, T, HV, device=DEV))
+    torch.cuda.synchronize()
+    for n in ("o", "w", "u", "v_new", "h"):
+        assert torch.equal(getattr(buf, n), getattr(zero, n)), n
+
+
+def test_initial_and_final_state_varlen():
+    """A given initial state per request and the final state, against the
+    oracle (which starts its recurrence from h0), on packed requests that
+    include an empty one (its final state is its initial state) and ragged
+    tails."""
+    M, H, HV, K, V = 2, 2, 4, 128, 128
+    cu = [0, 70, 70, 200, 457]
+    T = cu[-1]
+    d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", synth.seed_of(3) + 11)
+    beta, g = gates(d)
+    beta = beta.reshape(1, T * M, HV)
+    h0 = synth.initial_state_draws(len(cu) - 1, HV, V, K, synth.seed_of(3) + 12)
+    buf = check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_varlen(cu, M), range(HV), M, cu=cu, cu_host=cu,
+                      tag="h0/ht varlen", h0=h0)
+    assert torch.equal(buf.ht[1].cpu(), h0[1]), "empty request: ht must equal h0"
+
+
+def test_state_chaining_is_exact():
+    """Running a sequence in two calls -- the second starting from the first
+    call's final state -- reproduces the single call bit for bit (the split
+    is on a 64-token boundary, so every chunk is the same)."""
+    B, T, H, HV, K, V, M = 1, 512, 2, 2, 128, 128, 2
+    d = synth.chunk_draws(B, T, H, HV, K, V, M, "bf16", synth.seed_of(2) + 13)
+    beta, g = gates(d)
+    beta = beta.reshape(B, T * M, HV).to(DEV)
+    q, k, v, g = d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), g.to(DEV)
+    full = G.chunk_fwd(q, k, v, beta, g, output_final_state=True)
+    s = 192
+    a = G.chunk_fwd(q[:, :s].contiguous(), k[:, :s * M].contiguous(), v[:, :s * M].contiguous(),
+                    beta[:, :s * M].contiguous(), g[:, :s].contiguous(), output_final_state=True)
+    b = G.chunk_fwd(q[:, s:].contiguous(), k[:, s * M:].contiguous(), v[:, s * M:].contiguous(),
+                    beta[:, s * M:].contiguous(), g[:, s:].contiguous(), initial_state=a.ht,
+                    output_final_state=True)
+    torch.cuda.synchronize()
+    nc = s * M // 64
+    assert torch.equal(full.o, torch.cat([a.o, b.o], 1))
+    assert torch.equal(full.v_new, torch.cat([a.v_new, b.v_new], 1))
+    assert torch.equal(full.h, torch.cat([a.h, b.h], 0)) and a.h.shape[0] == nc
+    assert torch.equal(full.ht, b.ht)
