@@ -3,21 +3,25 @@
 
 One step = the whole hot path over one batch of synthetic input, all on the
 GPU through the C ABI of libgdp.so:
-    gdp_prefill_prepare  (split / GQA-expand / Householder-fold / gate)
-    gdp_recompute_w_u    (L2 norm, decays, transition block, inverse, w, u)
-    gdp_chunk_h          (state recurrence, corrected values)
-    gdp_chunk_o          (output)
+    gdp_prefill_prepare      (split / GQA-expand / Householder-fold / gate)
+    gdp_chunk_fwd_pipelined  (recompute_w_u -> chunk_h -> chunk_o over
+                              segments of the sequence: chunk_h runs the
+                              segments in order, handing its fp32 state on,
+                              while recompute_w_u of later segments and
+                              chunk_o of finished ones run on side streams)
 Workload: the long single-sequence prefill, B=1, T=32768 tokens, 16 heads
 (query/key groups = value heads = 16), K=V=128, M=2 Householder copies, chunk
 64, bf16 activations with fp32 gates, state and accumulation.  Inputs are
 drawn once (seeded, synthetic) and resident in HBM before timing starts.
 
-Prints one JSON line: tokens/s over the timed steps, per-kernel times from
-HIP events recorded on the launch stream, the roofline of the dominant kernel
-(algorithmic bytes per launch / its average duration vs 8 TB/s HBM) and the
-oracle's throughput on the host cores as a reported baseline.
+Prints one JSON line: tokens/s over the timed steps, the roofline of the
+dominant kernel (chunk_h: algorithmic bytes per launch / its average launch
+duration from HIP events recorded on its stream around every segment launch,
+vs 8 TB/s HBM) and the oracle's throughput on the host cores as a reported
+baseline.  --stages adds a sequential (not overlapped) pass that times each
+stage on its own.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-mib N]
+    python bench.py [--steps K] [--warmup W] [--segments S] [--stages] [--no-cpu-baseline] [--copy-mib N]
 """
 import argparse
 import json
@@ -32,19 +36,22 @@ sys.path.insert(0, ROOT)
 METRIC = "GDP prefill forward tokens/s (T=32k, H=16, K=V=128, M=2) + % MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(workload="long_prefill_32k", B=1, T=32768, H=16, HV=16, G=16, K=128, V=128, M=2, chunk=64,
-                dtype="bf16", path="prepare+recompute_w_u+chunk_h+chunk_o")
+                dtype="bf16", path="prepare+pipelined(recompute_w_u,chunk_h,chunk_o)")
+SEGMENTS = 4
 KERNELS = ["gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o"]
 
 
-def algorithmic_bytes(w):
+def algorithmic_bytes(w, T=None):
     """HBM bytes each stage must move at minimum (inputs read once, outputs
-    written once), per launch.  es = 2 (bf16); beta, g, k_rnorm are fp32."""
-    T, M, H, HV, G, K, V = w["T"] * w["B"], w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
+    written once), per launch over T tokens (default: the whole workload).
+    es = 2 (bf16); beta, g, k_rnorm are fp32."""
+    T = w["T"] * w["B"] if T is None else T
+    M, H, HV, G, K, V = w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
     P, N = V, K
     es = 2
     TM = T * M
-    nte = w["B"] * math.ceil(w["T"] * M / 64)
-    ntok_chunks = w["B"] * math.ceil(w["T"] / 64)
+    nte = math.ceil(T * M / 64)
+    ntok_chunks = math.ceil(T / 64)
     prep = T * (M * H * P + M * G * N + G * N) * es + T * (M * H + H) * es \
         + T * H * N * es + TM * H * N * es + TM * H * P * es + TM * H * 4 + T * H * 4
     wy = TM * H * K * es + TM * HV * V * es + TM * HV * 4 + T * HV * 4 \
@@ -110,6 +117,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--segments", type=int, default=SEGMENTS, help="pipeline segments of the chunk forward")
+    ap.add_argument("--stages", action="store_true", help="also time each stage sequentially (not overlapped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (untimed), "
@@ -136,6 +145,13 @@ def main():
     prep_out = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N)
     buf = G.ChunkBuffers(*prep_out)
     stream = torch.cuda.current_stream(dev)
+    nseg = G.pipeline_segments(w["T"], args.segments)
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)  # instantiate the handles
+        return evs
 
     def step(ev=None):
         if ev:
@@ -143,20 +159,12 @@ def main():
         G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
         if ev:
             ev[1].record(stream)
-        buf.recompute_w_u()
-        if ev:
-            ev[2].record(stream)
-        buf.chunk_h()
-        if ev:
-            ev[3].record(stream)
-        buf.chunk_o()
-        if ev:
-            ev[4].record(stream)
+        buf.forward_pipelined(nseg, chunk_h_events=ev[2:] if ev else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [new_events(2 + 2 * nseg) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -164,23 +172,47 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ktimes = {k: 0.0 for k in KERNELS}
-    for e in evs:
-        for i, k in enumerate(KERNELS):
-            ktimes[k] += e[i].elapsed_time(e[i + 1]) / args.steps  # ms
     tokens = w["B"] * w["T"]
     value = tokens / (ms_per_step / 1e3)
 
+    # chunk_h: every segment launch, bracketed on its own stream
+    seg_ms = [e[2 + 2 * j].elapsed_time(e[3 + 2 * j]) for e in evs for j in range(nseg)]
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    Ls = math.ceil(math.ceil(w["T"] / 64) / args.segments) * 64
+    seg_tokens = [min(Ls, w["T"] - j * Ls) for j in range(nseg)]
+    ch_bytes = sum(algorithmic_bytes(w, t)["gdp_chunk_h"] for t in seg_tokens) / nseg  # per launch
+    ch_ms = sum(seg_ms) / len(seg_ms)
     ab = algorithmic_bytes(w)
-    kern = {}
-    for k in KERNELS:
-        us = ktimes[k] * 1e3
-        gbs = ab[k] / (ktimes[k] / 1e3) / 1e9
-        kern[k] = {"us": round(us, 2), "alg_bytes": ab[k], "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    dom = max(KERNELS, key=lambda k: ktimes[k])
-    achieved = ab[dom] / (ktimes[dom] / 1e3) / 1e9
-    roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom)}
+    kern = {
+        "gdp_prefill_prepare": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1, "alg_bytes": ab["gdp_prefill_prepare"],
+                                "GB/s": round(ab["gdp_prefill_prepare"] / (prep_ms / 1e3) / 1e9, 1)},
+        "gdp_chunk_h": {"us_per_launch": round(ch_ms * 1e3, 2), "launches_per_step": nseg,
+                        "alg_bytes_per_launch": int(ch_bytes), "GB/s": round(ch_bytes / (ch_ms / 1e3) / 1e9, 1)},
+    }
+    achieved = ch_bytes / (ch_ms / 1e3) / 1e9
+    roof = {"kernel": "gdp_chunk_h", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gdp_chunk_h")}
+
+    stages = None
+    if args.stages:  # each stage alone, whole workload, for reference
+        torch.cuda.synchronize()
+        se = [new_events(5) for _ in range(3)]
+        for e in se:
+            e[0].record(stream)
+            G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
+            e[1].record(stream)
+            buf.recompute_w_u()
+            e[2].record(stream)
+            buf.chunk_h()
+            e[3].record(stream)
+            buf.chunk_o()
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        stages = {}
+        for i, k in enumerate(KERNELS):
+            ms = sum(e[i].elapsed_time(e[i + 1]) for e in se) / len(se)
+            stages[k] = {"us": round(ms * 1e3, 2), "GB/s": round(ab[k] / (ms / 1e3) / 1e9, 1),
+                         "hbm_frac": round(ab[k] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     if args.copy_mib > 0:
         n = args.copy_mib * 1024 * 1024 // 2
@@ -199,8 +231,10 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": w, "roofline": roof, "cpu_baseline": cpu, "kernels": kern,
+        "config": dict(w, segments=nseg), "roofline": roof, "cpu_baseline": cpu, "kernels": kern,
     }
+    if stages:
+        out["stages_sequential"] = stages
     print(json.dumps(out), flush=True)
 
 

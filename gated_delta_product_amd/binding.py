@@ -63,6 +63,10 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
+        L.gdp_chunk_fwd_pipelined.restype = ctypes.c_int
+        L.gdp_chunk_fwd_pipelined.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _vp, _vp]
+        L.gdp_pipeline_segments.restype = _i32
+        L.gdp_pipeline_segments.argtypes = [_i64, _i32]
         L.gdp_num_state_chunks.restype = _i64
         L.gdp_num_state_chunks.argtypes = [ctypes.POINTER(_i32), _i64, _i64, _i64, _i32, _i32]
         L.gdp_last_error.restype = ctypes.c_char_p
@@ -157,6 +161,11 @@ def prefill_prepare(x, ba, A_log, dt_bias, num_householder, num_heads, num_group
 
 
 # ------------------------------------------------------------------ chunk stages
+
+def pipeline_segments(T, num_segments):
+    """Segments gdp_chunk_fwd_pipelined runs for T tokens."""
+    return int(lib().gdp_pipeline_segments(int(T), int(num_segments)))
+
 
 def num_state_chunks(T, M, B=1, cu_seqlens_host=None):
     """Chunks h must hold (sum over sequences of ceil(len*M/64))."""
@@ -259,6 +268,26 @@ class ChunkBuffers:
 
     def forward(self, stream=None):
         self._call(lib().gdp_chunk_fwd, stream)
+        return self.o
+
+    def forward_pipelined(self, num_segments, stream=None, chunk_h_events=None):
+        """gdp_chunk_fwd_pipelined: the same results for B == 1 without
+        cu_seqlens, with the parallel stages of neighbouring segments
+        overlapping the serial one.  chunk_h_events: optional list of
+        2 * pipeline_segments(T, num_segments) torch.cuda.Event (timing
+        enabled, recorded at least once) marking each segment's chunk_h."""
+        d = self.dims
+        if getattr(self, "_ws", None) is None:
+            self._ws = torch.empty((2, d["HV"], d["V"], d["K"]), dtype=torch.float32, device=self.device)
+        ev = None
+        if chunk_h_events is not None:
+            n = pipeline_segments(d["T"], num_segments)
+            if len(chunk_h_events) != 2 * n:
+                raise ValueError("need %d events" % (2 * n))
+            ev = (_vp * (2 * n))(*[e.cuda_event for e in chunk_h_events])
+        s = stream if stream is not None else _stream(self.device)
+        _check(lib().gdp_chunk_fwd_pipelined(ctypes.byref(self.args), int(num_segments), self._ws.data_ptr(),
+                                             ev, s))
         return self.o
 
 

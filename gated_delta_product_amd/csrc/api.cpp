@@ -1,12 +1,15 @@
 // api.cpp -- the C ABI declared in include/gdp.h: argument validation,
-// error reporting and kernel launches on the caller's stream.  No allocation,
-// no synchronisation.
+// error reporting and kernel launches on the caller's stream.  No device
+// memory allocation and no synchronisation with the host; the pipelined
+// forward creates two side streams and its events once per device.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "gdp_internal.h"
 
@@ -115,6 +118,36 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
 
 }  // namespace
 
+namespace gdp {
+
+// Side streams and events of the pipelined forward, created once per device
+// and kept for the life of the process.
+struct PipeCtx {
+    hipStream_t side[2] = {nullptr, nullptr};  // [0]: recompute_w_u, [1]: chunk_o
+    std::vector<hipEvent_t> ev;
+};
+static std::mutex g_pipe_mu;
+static PipeCtx g_pipe[64];
+
+static hipError_t pipe_ctx(int dev, size_t nev, PipeCtx *&out) {
+    PipeCtx &c = g_pipe[dev];
+    for (int i = 0; i < 2; ++i)
+        if (!c.side[i]) {
+            hipError_t e = hipStreamCreateWithFlags(&c.side[i], hipStreamNonBlocking);
+            if (e != hipSuccess) return e;
+        }
+    while (c.ev.size() < nev) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+        c.ev.push_back(ev);
+    }
+    out = &c;
+    return hipSuccess;
+}
+
+}  // namespace gdp
+
 extern "C" {
 
 gdp_status gdp_prefill_prepare(const void *x, int64_t x_n_stride, int64_t x_t_stride, const void *ba,
@@ -174,6 +207,91 @@ gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream) {
     if ((st = hip_status(gdp::launch_wy(p, s), "gdp_chunk_fwd: recompute_w_u launch")) != GDP_OK) return st;
     if ((st = hip_status(gdp::launch_chunk_h(p, s), "gdp_chunk_fwd: chunk_h launch")) != GDP_OK) return st;
     return hip_status(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd: chunk_o launch");
+}
+
+int32_t gdp_pipeline_segments(int64_t T, int32_t num_segments) {
+    if (T < 0 || num_segments < 1) return -1;
+    if (T == 0) return 0;
+    const int64_t Ls = cdiv(cdiv(T, 64), num_segments) * 64;
+    return (int32_t)cdiv(T, Ls);
+}
+
+gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,
+                                   void *const *chunk_h_events, void *stream) {
+    gdp::ChunkParams p;
+    gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
+    if (st != GDP_OK) return st;
+    if (a->cu_seqlens) return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_pipelined: cu_seqlens must be NULL");
+    if (a->B != 1) return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_pipelined: B must be 1 (got %lld)", (long long)a->B);
+    if (num_segments < 1) return fail(GDP_ERR_INVALID, "num_segments must be >= 1");
+    if (a->T == 0) return ok();
+    if (!state_workspace || !aligned16(state_workspace))
+        return fail(GDP_ERR_INVALID, "state_workspace must be a 16-byte aligned device pointer");
+    const int64_t tok_chunks = cdiv(a->T, 64);
+    const int64_t seg_chunks = cdiv(tok_chunks, num_segments);
+    const int64_t Ls = seg_chunks * 64;  // tokens per segment (the last may be shorter)
+    const int64_t nseg = cdiv(a->T, Ls);
+    const size_t es = dsize(a->dtype);
+    const int64_t state_elems = (int64_t)a->HV * a->V * a->K;
+    hipStream_t s0 = (hipStream_t)stream;
+
+    std::lock_guard<std::mutex> lock(gdp::g_pipe_mu);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(GDP_ERR_UNSUPPORTED, "device index %d", dev);
+    gdp::PipeCtx *ctx = nullptr;
+    if ((e = gdp::pipe_ctx(dev, (size_t)(2 * nseg + 2), ctx)) != hipSuccess)
+        return hip_status(e, "gdp_chunk_fwd_pipelined: stream/event creation");
+    hipStream_t sw = ctx->side[0], so = ctx->side[1];
+    hipEvent_t ev_start = ctx->ev[0], ev_end = ctx->ev[1];
+#define GDP_TRY(call, what)                                      \
+    do {                                                         \
+        hipError_t e_ = (call);                                  \
+        if (e_ != hipSuccess) return hip_status(e_, what);       \
+    } while (0)
+    GDP_TRY(hipEventRecord(ev_start, s0), "hipEventRecord");
+    GDP_TRY(hipStreamWaitEvent(sw, ev_start, 0), "hipStreamWaitEvent");
+    GDP_TRY(hipStreamWaitEvent(so, ev_start, 0), "hipStreamWaitEvent");
+    for (int64_t sidx = 0; sidx < nseg; ++sidx) {
+        const int64_t t0 = sidx * Ls, Tn = (a->T - t0) < Ls ? (a->T - t0) : Ls;
+        const int64_t r0 = t0 * a->M;      // first expanded row
+        const int64_t c0 = r0 / 64;        // first state chunk (t0 is a multiple of 64)
+        gdp_chunk_args sa = *a;
+        sa.T = Tn;
+        sa.h_chunks = a->h_chunks - c0;
+        sa.q = (const char *)a->q + t0 * a->H * a->K * es;
+        sa.k = (const char *)a->k + r0 * a->H * a->K * es;
+        sa.v = (const char *)a->v + r0 * a->HV * a->V * es;
+        sa.beta = a->beta + r0 * a->HV;
+        sa.g = a->g ? a->g + t0 * a->HV : nullptr;
+        sa.k_rnorm = a->k_rnorm + r0 * a->H;
+        sa.gcum = a->gcum + r0 * a->HV;
+        sa.kdecay = a->kdecay + r0 * a->HV;
+        sa.w = (char *)a->w + r0 * a->HV * a->K * es;
+        sa.u = (char *)a->u + r0 * a->HV * a->V * es;
+        sa.v_new = (char *)a->v_new + r0 * a->HV * a->V * es;
+        sa.h = (char *)a->h + c0 * state_elems * es;
+        sa.o = (char *)a->o + t0 * a->HV * a->V * es;
+        sa.h0 = sidx == 0 ? a->h0 : state_workspace + ((sidx - 1) & 1) * state_elems;
+        sa.ht = sidx == nseg - 1 ? a->ht : state_workspace + (sidx & 1) * state_elems;
+        gdp::ChunkParams sp;
+        if ((st = check_chunk(&sa, ST_WY | ST_H | ST_O, &sp)) != GDP_OK) return st;
+        hipEvent_t ev_w = ctx->ev[2 + 2 * sidx], ev_h = ctx->ev[3 + 2 * sidx];
+        GDP_TRY(gdp::launch_wy(sp, sw), "gdp_chunk_fwd_pipelined: recompute_w_u launch");
+        GDP_TRY(hipEventRecord(ev_w, sw), "hipEventRecord");
+        GDP_TRY(hipStreamWaitEvent(s0, ev_w, 0), "hipStreamWaitEvent");
+        if (chunk_h_events) GDP_TRY(hipEventRecord((hipEvent_t)chunk_h_events[2 * sidx], s0), "hipEventRecord");
+        GDP_TRY(gdp::launch_chunk_h(sp, s0), "gdp_chunk_fwd_pipelined: chunk_h launch");
+        if (chunk_h_events) GDP_TRY(hipEventRecord((hipEvent_t)chunk_h_events[2 * sidx + 1], s0), "hipEventRecord");
+        GDP_TRY(hipEventRecord(ev_h, s0), "hipEventRecord");
+        GDP_TRY(hipStreamWaitEvent(so, ev_h, 0), "hipStreamWaitEvent");
+        GDP_TRY(gdp::launch_chunk_o(sp, so), "gdp_chunk_fwd_pipelined: chunk_o launch");
+    }
+    GDP_TRY(hipEventRecord(ev_end, so), "hipEventRecord");
+    GDP_TRY(hipStreamWaitEvent(s0, ev_end, 0), "hipStreamWaitEvent");
+#undef GDP_TRY
+    return ok();
 }
 
 int64_t gdp_num_state_chunks(const int32_t *cu_seqlens_host, int64_t num_seqs, int64_t B, int64_t T, int32_t M,

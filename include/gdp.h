@@ -185,6 +185,38 @@ gdp_status gdp_chunk_o(const gdp_chunk_args *a, void *stream);
 gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
 
 /*
+ * gdp_chunk_fwd_pipelined -- the same results as gdp_chunk_fwd for one long
+ * sequence (B == 1, cu_seqlens == NULL), computed in num_segments pieces of
+ * whole 64-token chunks so that the parallel stages overlap the serial one:
+ * chunk_h runs the segments in order on `stream`, handing the fp32 state
+ * from one segment to the next (as h0 / ht), while gdp_recompute_w_u of the
+ * next segments and gdp_chunk_o of the finished ones run on two streams of
+ * the library's own (created once per device, default priority) that join
+ * `stream` through events.  On return all work is ordered before later work
+ * on `stream`; nothing is synchronised with the host, and the calls can be
+ * captured into a HIP graph.
+ *   state_workspace  float32 [2, HV, V, K], device, caller-owned: the state
+ *                    handed between segments.
+ *   chunk_h_events   NULL, or 2 * gdp_pipeline_segments(T, num_segments)
+ *                    hipEvent_t handles (as void *), which are recorded on
+ *                    `stream` right before and right after each segment's
+ *                    chunk_h launch (for timing that stage).
+ *   The per-row intermediates k_rnorm, gcum and kdecay are laid out per
+ *   segment (segment s, starting at token t_s, holds its head-major block of
+ *   H or HV rows of (its tokens * M) values at offset t_s * M * (H or HV)).
+ *   Every other tensor is as for gdp_chunk_fwd, and o, w, u, v_new, h and ht
+ *   are bit-identical to it.
+ * Concurrent calls on one device are serialised while they enqueue.
+ */
+gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,
+                                   void *const *chunk_h_events, void *stream);
+
+/* Segments gdp_chunk_fwd_pipelined actually runs for T tokens (whole
+   64-token chunks, at most num_segments); 0 for T == 0, -1 on bad
+   arguments. */
+int32_t gdp_pipeline_segments(int64_t T, int32_t num_segments);
+
+/*
  * Number of state chunks h must hold: sum over sequences of
  * ceil(len * M / chunk_size).  With cu_seqlens_host == NULL it is
  * B * ceil(T * M / chunk_size).  cu_seqlens_host is a host copy of the

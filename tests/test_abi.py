@@ -110,6 +110,23 @@ def test_stage_specific_requirements():
     assert L.gdp_chunk_h(ctypes.byref(_args(kdecay=None)), None) == B.GDP_ERR_INVALID
 
 
+def test_pipelined_rejects_and_segments():
+    L = B.lib()
+    ws = ctypes.c_void_p(0x100000)
+    assert L.gdp_chunk_fwd_pipelined(ctypes.byref(_args(B=2, h_chunks=4)), 4, ws, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_pipelined(ctypes.byref(_args(cu_seqlens=0x1000, num_seqs=1)), 4, ws, None,
+                                     None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_pipelined(ctypes.byref(_args()), 0, ws, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_pipelined(ctypes.byref(_args()), 2, None, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_pipelined(ctypes.byref(_args(q=None)), 2, ws, None, None) == B.GDP_ERR_INVALID
+    # segments of whole 64-token chunks, at most the number asked for
+    assert B.pipeline_segments(32768, 8) == 8
+    assert B.pipeline_segments(1000, 3) == 3      # 16 chunks -> 6, 6, 4
+    assert B.pipeline_segments(100, 8) == 2       # 2 chunks
+    assert B.pipeline_segments(0, 8) == 0
+    assert L.gdp_pipeline_segments(10, 0) == -1
+
+
 def test_null_args_rejected():
     assert B.lib().gdp_chunk_fwd(None, None) == B.GDP_ERR_INVALID
 

@@ -439,3 +439,30 @@ def test_state_chaining_is_exact():
     assert torch.equal(full.v_new, torch.cat([a.v_new, b.v_new], 1))
     assert torch.equal(full.h, torch.cat([a.h, b.h], 0)) and a.h.shape[0] == nc
     assert torch.equal(full.ht, b.ht)
+
+
+def test_pipelined_forward_is_bit_identical():
+    """gdp_chunk_fwd_pipelined (segments chained through the fp32 state, with
+    the parallel stages on side streams) gives exactly the outputs of
+    gdp_chunk_fwd, for several segment counts, with an initial state, a
+    ragged last chunk and the ungated rule."""
+    B, T, H, HV, K, V, M = 1, 1000, 2, 4, 128, 128, 2
+    d = synth.chunk_draws(B, T, H, HV, K, V, M, "bf16", synth.seed_of(2) + 17)
+    beta, g = gates(d)
+    beta = beta.reshape(B, T * M, HV).to(DEV)
+    q, k, v, g = d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), g.to(DEV)
+    h0 = synth.initial_state_draws(1, HV, V, K, synth.seed_of(2) + 18).to(DEV)
+    for gg in (g, None):
+        ref = G.ChunkBuffers(q, k, v, beta, gg, initial_state=h0, output_final_state=True)
+        ref.forward()
+        for nseg in (1, 3, 7, 64):
+            pip = G.ChunkBuffers(q, k, v, beta, gg, initial_state=h0, output_final_state=True)
+            n = G.pipeline_segments(T, nseg)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            for e in evs:
+                e.record()
+            pip.forward_pipelined(nseg, chunk_h_events=evs)
+            torch.cuda.synchronize()
+            for nm in ("o", "w", "u", "v_new", "h", "ht"):
+                assert torch.equal(getattr(ref, nm), getattr(pip, nm)), (nseg, gg is None, nm)
+            assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0 for i in range(n))
