@@ -38,6 +38,15 @@ class ChunkArgs(ctypes.Structure):
     ]
 
 
+class DecodeArgs(ctypes.Structure):
+    """Mirror of gdp_decode_args (include/gdp.h)."""
+    _fields_ = [
+        ("n", _i64), ("S", _i64), ("H", _i32), ("HV", _i32), ("K", _i32), ("V", _i32), ("M", _i32),
+        ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("pool", _i64),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("g", _vp), ("state", _vp), ("slots", _vp), ("o", _vp),
+    ]
+
+
 class GdpError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__("gdp status %d: %s" % (status, msg))
@@ -63,6 +72,10 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
+        L.gdp_decode_prepare.restype = ctypes.c_int
+        L.gdp_decode_prepare.argtypes = L.gdp_prefill_prepare.argtypes
+        L.gdp_decode_update.restype = ctypes.c_int
+        L.gdp_decode_update.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.gdp_chunk_fwd_pipelined.restype = ctypes.c_int
         L.gdp_chunk_fwd_pipelined.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _vp, _vp]
         L.gdp_pipeline_segments.restype = _i32
@@ -306,3 +319,61 @@ def chunk_fwd(q, k, v, beta, g, scale=None, cu_seqlens=None, cu_seqlens_host=Non
 
 def version():
     return lib().gdp_version().decode()
+
+
+# ------------------------------------------------------------------ decode
+
+def decode_prepare(x, ba, A_log, dt_bias, M, H, G, P, N, out=None):
+    """gdp_decode_prepare: x [n, S, M*H*P + M*G*N + G*N], ba [n, S, M*H + H]
+    (last dimensions contiguous).  Returns (q [n,S*M,H,N] with the query on
+    each token's last copy, k [n,S*M,H,N], v [n,S*M,H,P], beta [n,S*M,H]
+    f32, g [n,S*M,H] f32 with the decay on each token's first copy)."""
+    dev = _need_cuda(x, ba, A_log, dt_bias)
+    n, S, width = x.shape
+    if width != M * H * P + M * G * N + G * N or x.stride(2) != 1:
+        raise ValueError("x must be [n, S, M*H*P + M*G*N + G*N] with a contiguous last dimension")
+    if tuple(ba.shape) != (n, S, M * H + H) or ba.stride(2) != 1:
+        raise ValueError("ba must be [n, S, M*H + H]")
+    if out is None:
+        dt = x.dtype
+        out = (torch.empty((n, S * M, H, N), dtype=dt, device=dev), torch.empty((n, S * M, H, N), dtype=dt, device=dev),
+               torch.empty((n, S * M, H, P), dtype=dt, device=dev),
+               torch.empty((n, S * M, H), dtype=torch.float32, device=dev),
+               torch.empty((n, S * M, H), dtype=torch.float32, device=dev))
+    q, k, v, beta, g = out
+    _check(lib().gdp_decode_prepare(
+        _ptr(x), x.stride(0), x.stride(1), _ptr(ba), ba.stride(0), ba.stride(1),
+        _ptr(A_log), _ptr(dt_bias), n, S, M, H, G, P, N, _dtype_code(x.dtype),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _stream(dev)))
+    return out
+
+
+def decode_update(q, k, v, beta, g, state, M, slots=None, scale=None, o=None):
+    """gdp_decode_update: one decode step over rows from decode_prepare.
+    q, k [n, S*M, H, K]; v [n, S*M, HV, V]; beta, g [n, S*M, HV] f32 (g may
+    be None); state [pool, HV, V, K] f32 updated in place; slots int32 [n]
+    or None.  Returns o [n, S*M, HV, V]."""
+    dev = _need_cuda(q, k, v, beta, g, state, slots)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (g, "g"), (state, "state"), (slots, "slots")):
+        if t is not None:
+            _contig(t, nm)
+    n, L, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if L % M:
+        raise ValueError("rows per request must be a multiple of M")
+    if tuple(k.shape) != (n, L, H, K) or tuple(v.shape[:2]) != (n, L) or tuple(beta.shape) != (n, L, HV):
+        raise ValueError("q, k, v, beta shapes disagree")
+    if g is not None and tuple(g.shape) != (n, L, HV):
+        raise ValueError("g must be [n, S*M, HV]")
+    if state.dtype != torch.float32 or tuple(state.shape[1:]) != (HV, V, K):
+        raise ValueError("state must be float32 [pool, HV, V, K]")
+    if slots is not None and (slots.dtype != torch.int32 or tuple(slots.shape) != (n,)):
+        raise ValueError("slots must be int32 [n]")
+    if o is None:
+        o = torch.empty((n, L, HV, V), dtype=q.dtype, device=dev)
+    a = DecodeArgs(n=n, S=L // M, H=H, HV=HV, K=K, V=V, M=M, scale=float(scale) if scale is not None else 0.0,
+                   dtype=_dtype_code(q.dtype), pool=state.shape[0], q=_ptr(q), k=_ptr(k), v=_ptr(v),
+                   beta=_ptr(beta), g=None if g is None else _ptr(g), state=_ptr(state),
+                   slots=None if slots is None else _ptr(slots), o=_ptr(o))
+    _check(lib().gdp_decode_update(ctypes.byref(a), _stream(dev)))
+    return o

@@ -150,32 +150,78 @@ static hipError_t pipe_ctx(int dev, size_t nev, PipeCtx *&out) {
 
 extern "C" {
 
-gdp_status gdp_prefill_prepare(const void *x, int64_t x_n_stride, int64_t x_t_stride, const void *ba,
-                               int64_t ba_n_stride, int64_t ba_t_stride, const float *A_log,
-                               const float *dt_bias, int64_t n, int64_t T, int32_t M, int32_t H, int32_t G,
-                               int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k, void *v, float *beta,
-                               float *g, void *stream) {
-    if (dtype != GDP_F32 && dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "unknown dtype %d", (int)dtype);
-    if (n < 0 || T < 0) return fail(GDP_ERR_INVALID, "n and T must be >= 0");
-    if (M < 1 || H < 1 || G < 1 || P < 1 || N < 1) return fail(GDP_ERR_INVALID, "M, H, G, P, N must be >= 1");
-    if (H % G) return fail(GDP_ERR_INVALID, "num_heads H=%d must be a multiple of num_groups G=%d", H, G);
-    if (n > 65535 || T > 0x7fffffff) return fail(GDP_ERR_UNSUPPORTED, "n or T too large for one launch");
+static gdp_status prepare_common(const char *name, bool decode, const void *x, int64_t x_n_stride,
+                                 int64_t x_t_stride, const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
+                                 const float *A_log, const float *dt_bias, int64_t n, int64_t T, int32_t M,
+                                 int32_t H, int32_t G, int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k,
+                                 void *v, float *beta, float *g, void *stream) {
+    if (dtype != GDP_F32 && dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "%s: unknown dtype %d", name, (int)dtype);
+    if (n < 0 || T < 0) return fail(GDP_ERR_INVALID, "%s: n and T must be >= 0", name);
+    if (M < 1 || H < 1 || G < 1 || P < 1 || N < 1) return fail(GDP_ERR_INVALID, "%s: M, H, G, P, N must be >= 1", name);
+    if (H % G) return fail(GDP_ERR_INVALID, "%s: num_heads H=%d must be a multiple of num_groups G=%d", name, H, G);
+    if (n > 65535 || T > 0x7fffffff) return fail(GDP_ERR_UNSUPPORTED, "%s: n or T too large for one launch", name);
     const int64_t width = (int64_t)M * H * P + (int64_t)M * G * N + (int64_t)G * N;
+    if (width * M > 0x7fffffff) return fail(GDP_ERR_UNSUPPORTED, "%s: rows too wide", name);
     if (x_t_stride < 0 || x_n_stride < 0 || ba_t_stride < 0 || ba_n_stride < 0)
-        return fail(GDP_ERR_INVALID, "strides must be >= 0");
+        return fail(GDP_ERR_INVALID, "%s: strides must be >= 0", name);
     if (n == 0 || T == 0) return ok();
     if (!x || !ba || !A_log || !dt_bias || !q || !k || !v || !beta || !g)
-        return fail(GDP_ERR_INVALID, "a tensor pointer is NULL");
-    if (T > 1 && x_t_stride < width) return fail(GDP_ERR_INVALID, "x rows overlap (t stride %lld < width %lld)",
-                                                 (long long)x_t_stride, (long long)width);
-    if (T > 1 && ba_t_stride < (int64_t)M * H + H) return fail(GDP_ERR_INVALID, "ba rows overlap");
+        return fail(GDP_ERR_INVALID, "%s: a tensor pointer is NULL", name);
+    if (T > 1 && x_t_stride < width) return fail(GDP_ERR_INVALID, "%s: x rows overlap (t stride %lld < width %lld)",
+                                                 name, (long long)x_t_stride, (long long)width);
+    if (T > 1 && ba_t_stride < (int64_t)M * H + H) return fail(GDP_ERR_INVALID, "%s: ba rows overlap", name);
     const size_t es = dsize(dtype);
     const bool vec16 = aligned16(x) && aligned16(q) && aligned16(k) && aligned16(v) &&
                        ((x_t_stride * es) % 16 == 0) && ((x_n_stride * es) % 16 == 0) &&
                        ((P * es) % 16 == 0) && ((N * es) % 16 == 0);
     gdp::PrepareParams p{x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride, A_log, dt_bias, n, T,
-                         M, H, G, P, N, dtype, vec16, q, k, v, beta, g};
-    return hip_status(gdp::launch_prepare(p, (hipStream_t)stream), "gdp_prefill_prepare launch");
+                         M, H, G, P, N, dtype, decode, vec16, q, k, v, beta, g};
+    return hip_status(gdp::launch_prepare(p, (hipStream_t)stream), name);
+}
+
+gdp_status gdp_prefill_prepare(const void *x, int64_t x_n_stride, int64_t x_t_stride, const void *ba,
+                               int64_t ba_n_stride, int64_t ba_t_stride, const float *A_log,
+                               const float *dt_bias, int64_t n, int64_t T, int32_t M, int32_t H, int32_t G,
+                               int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k, void *v, float *beta,
+                               float *g, void *stream) {
+    return prepare_common("gdp_prefill_prepare", false, x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride,
+                          A_log, dt_bias, n, T, M, H, G, P, N, dtype, q, k, v, beta, g, stream);
+}
+
+gdp_status gdp_decode_prepare(const void *x, int64_t x_n_stride, int64_t x_t_stride, const void *ba,
+                              int64_t ba_n_stride, int64_t ba_t_stride, const float *A_log,
+                              const float *dt_bias, int64_t n, int64_t S, int32_t M, int32_t H, int32_t G,
+                              int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k, void *v, float *beta,
+                              float *g, void *stream) {
+    return prepare_common("gdp_decode_prepare", true, x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride,
+                          A_log, dt_bias, n, S, M, H, G, P, N, dtype, q, k, v, beta, g, stream);
+}
+
+gdp_status gdp_decode_update(const gdp_decode_args *a, void *stream) {
+    if (!a) return fail(GDP_ERR_INVALID, "args is NULL");
+    if (a->dtype != GDP_F32 && a->dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "unknown dtype %d", (int)a->dtype);
+    if (a->n < 0 || a->S < 0) return fail(GDP_ERR_INVALID, "n and S must be >= 0");
+    if (a->H < 1 || a->HV < 1 || a->HV % a->H) return fail(GDP_ERR_INVALID, "HV must be a positive multiple of H");
+    if (a->M < 1 || a->M > 4) return fail(GDP_ERR_UNSUPPORTED, "num_householder M=%d not in [1, 4]", a->M);
+    if (!(a->K == 64 || a->K == 128) || !(a->V == 64 || a->V == 128 || a->V == 256))
+        return fail(GDP_ERR_UNSUPPORTED, "head dims K=%d, V=%d not built (K in {64, 128}, V in {64, 128, 256})",
+                    a->K, a->V);
+    if (!std::isfinite(a->scale)) return fail(GDP_ERR_INVALID, "scale is not finite");
+    if (a->n > 0x7fffffff || a->HV > 65535 || a->S * a->M > 4096)
+        return fail(GDP_ERR_UNSUPPORTED, "decode step too large (n, HV or S*M)");
+    if (a->pool < 0 || (!a->slots && a->pool < a->n)) return fail(GDP_ERR_INVALID, "state pool too small");
+    if (a->n == 0 || a->S == 0) return ok();
+    const struct {
+        const void *p;
+        const char *name;
+    } need[] = {{a->q, "q"}, {a->k, "k"}, {a->v, "v"}, {a->beta, "beta"}, {a->state, "state"}, {a->o, "o"}};
+    for (const auto &t : need) {
+        if (!t.p) return fail(GDP_ERR_INVALID, "%s is NULL", t.name);
+        if (!aligned16(t.p)) return fail(GDP_ERR_INVALID, "%s is not 16-byte aligned", t.name);
+    }
+    gdp_decode_args d = *a;
+    if (!(d.scale > 0.f)) d.scale = 1.0f / std::sqrt((float)a->K);
+    return hip_status(gdp::launch_decode(d, (hipStream_t)stream), "gdp_decode_update launch");
 }
 
 gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream) {

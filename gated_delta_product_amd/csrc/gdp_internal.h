@@ -17,12 +17,14 @@ struct PrepareParams {
     int64_t n, T;
     int M, H, G, P, N;
     gdp_dtype dtype;
+    bool decode;  // query and g interleaved onto the copies
     bool vec16;  // every row start and segment is 16-byte aligned
     void *q, *k, *v;
     float *beta, *g;
 };
 
 hipError_t launch_prepare(const PrepareParams &p, hipStream_t stream);
+hipError_t launch_decode(const gdp_decode_args &a, hipStream_t stream);
 
 // Validated chunk-stage arguments (scale resolved, nseq resolved).
 struct ChunkParams {

@@ -1,5 +1,6 @@
-// prepare.hip -- fused prefill prepare for the Gated Delta Product
-// (core.ssm.ops.gdp.prepare: module description and gdp_prefill_prepare).
+// prepare.hip -- fused prefill and decode prepare for the Gated Delta Product
+// (core.ssm.ops.gdp.prepare: module description, gdp_prefill_prepare and
+// gdp_decode_prepare).
 //
 // One block per (token, batch row).  The block writes every output of its
 // token: the value copies, the GQA-expanded key copies and query, beta for
@@ -46,7 +47,10 @@ struct Unit {
     static constexpr int elems = VEC16 ? (int)(16 / sizeof(T)) : 1;
 };
 
-template <typename T, bool VEC16>
+// DECODE: the query goes to the last copy of its token and g to the first,
+// zeros elsewhere (q [n, T*M, H, N], g [n, T*M, H]); otherwise both stay
+// one per token.
+template <typename T, bool VEC16, bool DECODE>
 __global__ void __launch_bounds__(256)
 gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
               const T *__restrict__ ba, int64_t bns, int64_t bts,
@@ -66,14 +70,14 @@ gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
 
     const int nv = M * H * P / E;  // value units
     const int nk = M * HN / E;     // key units (expanded)
-    const int nq = HN / E;         // query units (expanded)
+    const int nq = (DECODE ? M : 1) * HN / E;  // query units (expanded; all copies in decode)
     const int ntot = nv + nk + nq;
     const int kbase = M * H * P;   // key segment offset in x
     const int qbase = kbase + M * G * N;
 
     U *vo = (U *)(v + tok * (int64_t)M * H * P);
     U *ko = (U *)(k + tok * (int64_t)M * HN);
-    U *qo = (U *)(q + tok * (int64_t)HN);
+    U *qo = (U *)(q + tok * (int64_t)(DECODE ? M : 1) * HN);
     const U *xv = (const U *)xr;
 
     // Batches of UB units per thread: all loads of a batch are issued before
@@ -94,9 +98,18 @@ gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
                 const int h = rem / N, n = rem - h * N;
                 val[it] = *(const U *)(xr + kbase + j * G * N + (h / hpg) * N + n);
             } else if (i < ntot) {
-                const int e = (i - nv - nk) * E;
+                int e = (i - nv - nk) * E;
+                bool copy_q = true;
+                if constexpr (DECODE) {  // element within the token's M query rows
+                    const int j = e / HN;
+                    copy_q = j == M - 1;
+                    e -= j * HN;
+                }
                 const int h = e / N, n = e - h * N;
-                val[it] = *(const U *)(xr + qbase + (h / hpg) * N + n);
+                if (copy_q)
+                    val[it] = *(const U *)(xr + qbase + (h / hpg) * N + n);
+                else
+                    val[it] = U{};
             }
         }
 #pragma unroll
@@ -110,21 +123,23 @@ gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
                 qo[i - nv - nk] = val[it];
         }
     }
-    // gates: beta for (copy, head) = M*H values, then g for H heads
-    for (int i = threadIdx.x; i < M * H + H; i += blockDim.x) {
+    // gates: beta for (copy, head) = M*H values, then g for H heads (for
+    // every copy in decode, zero past the first)
+    const int ng = (DECODE ? M : 1) * H;
+    for (int i = threadIdx.x; i < M * H + ng; i += blockDim.x) {
         if (i < M * H) {
             beta[tok * (int64_t)M * H + i] = gate_beta(to_f32(br[i]));
         } else {
-            const int h = i - M * H;
-            g[tok * (int64_t)H + h] = gate_g(to_f32(br[i]), A_log[h], dt_bias[h]);
+            const int c = i - M * H, h = c % H;
+            g[tok * (int64_t)ng + c] = c < H ? gate_g(to_f32(br[M * H + h]), A_log[h], dt_bias[h]) : 0.0f;
         }
     }
 }
 
-template <typename T, bool VEC16>
+template <typename T, bool VEC16, bool DECODE>
 static hipError_t launch_prepare_t(const PrepareParams &p, hipStream_t stream) {
     dim3 grid((unsigned)p.T, (unsigned)p.n);
-    hipLaunchKernelGGL((gdp_prepare_k<T, VEC16>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((gdp_prepare_k<T, VEC16, DECODE>), grid, dim3(256), 0, stream,
                        (const T *)p.x, p.x_n_stride, p.x_t_stride,
                        (const T *)p.ba, p.ba_n_stride, p.ba_t_stride,
                        p.A_log, p.dt_bias, p.T, p.M, p.H, p.G, p.P, p.N,
@@ -132,11 +147,16 @@ static hipError_t launch_prepare_t(const PrepareParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <bool DECODE>
+static hipError_t launch_prepare_d(const PrepareParams &p, hipStream_t stream) {
+    if (p.dtype == GDP_BF16)
+        return p.vec16 ? launch_prepare_t<bf16, true, DECODE>(p, stream) : launch_prepare_t<bf16, false, DECODE>(p, stream);
+    return p.vec16 ? launch_prepare_t<float, true, DECODE>(p, stream) : launch_prepare_t<float, false, DECODE>(p, stream);
+}
+
 hipError_t launch_prepare(const PrepareParams &p, hipStream_t stream) {
     if (p.n == 0 || p.T == 0) return hipSuccess;
-    if (p.dtype == GDP_BF16)
-        return p.vec16 ? launch_prepare_t<bf16, true>(p, stream) : launch_prepare_t<bf16, false>(p, stream);
-    return p.vec16 ? launch_prepare_t<float, true>(p, stream) : launch_prepare_t<float, false>(p, stream);
+    return p.decode ? launch_prepare_d<true>(p, stream) : launch_prepare_d<false>(p, stream);
 }
 
 }  // namespace gdp

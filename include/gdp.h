@@ -16,6 +16,15 @@
  *                        (core.ssm.ops.gdp.chunk_o,
  *                        chunk_gated_delta_product_fwd_o)
  *   gdp_chunk_fwd        the three chunk stages in order
+ *   gdp_chunk_fwd_pipelined  the same for one long sequence, in segments
+ *                        whose parallel stages overlap the serial one
+ *   gdp_decode_prepare   the prepare of a decode step: query and decay
+ *                        interleaved onto the Householder copies
+ *                        (core.ssm.ops.gdp.prepare, gdp_decode_prepare)
+ *   gdp_decode_update    the recurrence over a decode step's S*M rows, the
+ *                        state read from and written back to a state pool
+ *                        (the fused recurrent update the prepare page names
+ *                        as the decode consumer)
  *
  * Conventions shared by every entry point
  *   * All tensor pointers are device pointers owned by the caller.  The
@@ -84,6 +93,75 @@ gdp_status gdp_prefill_prepare(
     gdp_dtype dtype,
     void *q, void *k, void *v, float *beta, float *g,
     void *stream);
+
+/*
+ * gdp_decode_prepare -- the decode-step form of gdp_prefill_prepare
+ * (core.ssm.ops.gdp.prepare: module description, the decode bullet, and
+ * gdp_decode_prepare).  The S tokens of each request (1 plus the draft
+ * length) walk the copies as one sequence of S*M rows: row t*M + j is copy j
+ * of token t.  Same arguments and validation as gdp_prefill_prepare with T =
+ * S; the outputs differ only in where query and g go:
+ *   q     [n, S*M, H, N]   query of token t on row t*M + M - 1, zeros on the
+ *                          other copies
+ *   k     [n, S*M, H, N]   as prefill
+ *   v     [n, S*M, H, P]   as prefill
+ *   beta  [n, S*M, H]      float32, as prefill
+ *   g     [n, S*M, H]      float32, g of token t on row t*M, zeros elsewhere
+ */
+gdp_status gdp_decode_prepare(
+    const void *x, int64_t x_n_stride, int64_t x_t_stride,
+    const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
+    const float *A_log, const float *dt_bias,
+    int64_t n, int64_t S, int32_t M, int32_t H, int32_t G, int32_t P, int32_t N,
+    gdp_dtype dtype,
+    void *q, void *k, void *v, float *beta, float *g,
+    void *stream);
+
+/*
+ * Arguments of gdp_decode_update: one decode step of n requests, each a
+ * sequence of L = S*M rows (the outputs of gdp_decode_prepare), gated delta
+ * rule per row with the row's own decay and query:
+ *   delta = beta (v - exp(g) S khat),  S <- exp(g) S + delta khat^T,
+ *   o     = scale * S qhat             (zero on rows whose query is zero)
+ * with khat, qhat L2-normalised as in the chunk forward.  Over rows from
+ * gdp_decode_prepare this is the Gated Delta Product recurrence of the S
+ * tokens (the decode interleave of the prepare page).
+ *   q, k   [n, L, H, K]  dtype;  v [n, L, HV, V] dtype
+ *   beta   [n, L, HV] float32;  g [n, L, HV] float32 natural-log decay per
+ *          row, or NULL (ungated)
+ *   state  [pool, HV, V, K] float32, the state S of each slot; read and
+ *          written in place
+ *   slots  int32 [n] device: the state slot of each request, or NULL (slot
+ *          i for request i).  A slot outside [0, pool) -- e.g. -1 for a
+ *          padding entry -- skips the request: no state is touched and its
+ *          o rows are zero.  Slots of one call must be distinct.
+ *   o      [n, L, HV, V] dtype, every row
+ *   scale  <= 0 selects 1/sqrt(K).
+ * Sizes: K in {64, 128}, V in {64, 128, 256}, HV % H == 0, 1 <= M <= 4,
+ * S*M <= 4096, n < 2^31, HV <= 65535.
+ */
+typedef struct gdp_decode_args {
+    int64_t n;
+    int64_t S;
+    int32_t H;
+    int32_t HV;
+    int32_t K;
+    int32_t V;
+    int32_t M;
+    float scale;
+    gdp_dtype dtype;
+    int64_t pool;
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *beta;
+    const float *g;
+    float *state;
+    const int32_t *slots;
+    void *o;
+} gdp_decode_args;
+
+gdp_status gdp_decode_update(const gdp_decode_args *a, void *stream);
 
 /*
  * Arguments of the chunk stages.  Sizes:

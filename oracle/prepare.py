@@ -99,3 +99,22 @@ def prefill_prepare(x, ba, A_log, dt_bias, M, H, G, P, N):
     g = decay_rn32(a, A_log, dt_bias)
     return (np.ascontiguousarray(q), np.ascontiguousarray(k),
             np.ascontiguousarray(v), beta, g)
+
+
+def decode_prepare(x, ba, A_log, dt_bias, M, H, G, P, N):
+    """Split, expand and gate a decode step whose S tokens walk the
+    Householder copies as one sequence of S*M rows (core.ssm.ops.gdp.prepare,
+    module description, the decode bullet; gdp_decode_prepare, Returns): the
+    query sits on the last copy of each token and the decay on the first,
+    zeros elsewhere.  Key, value and beta are as in prefill.
+
+    Returns (q [n,S*M,H,N], k [n,S*M,H,N], v [n,S*M,H,P], beta [n,S*M,H],
+    g [n,S*M,H]) as float32 arrays.
+    """
+    q, k, v, beta, g = prefill_prepare(x, ba, A_log, dt_bias, M, H, G, P, N)
+    n, S = q.shape[0], q.shape[1]
+    qi = np.zeros((n, S, M, H, N), dtype=_F32)
+    qi[:, :, M - 1] = q
+    gi = np.zeros((n, S, M, H), dtype=_F32)
+    gi[:, :, 0] = g
+    return qi.reshape(n, S * M, H, N), k, v, beta, gi.reshape(n, S * M, H)

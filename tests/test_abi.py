@@ -30,8 +30,9 @@ def test_header_compiles_as_c99(tmp_path):
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert {"gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o",
-            "gdp_chunk_fwd", "gdp_num_state_chunks", "gdp_last_error", "gdp_version"} <= set(names)
+    assert {"gdp_prefill_prepare", "gdp_decode_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o",
+            "gdp_chunk_fwd", "gdp_chunk_fwd_pipelined", "gdp_pipeline_segments", "gdp_decode_update",
+            "gdp_num_state_chunks", "gdp_last_error", "gdp_version"} <= set(names)
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -40,21 +41,22 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
-def test_struct_layout_matches_c(tmp_path):
-    fields = [f for f, _ in B.ChunkArgs._fields_]
+@pytest.mark.parametrize("cls,cname", [(B.ChunkArgs, "gdp_chunk_args"), (B.DecodeArgs, "gdp_decode_args")])
+def test_struct_layout_matches_c(tmp_path, cls, cname):
+    fields = [f for f, _ in cls._fields_]
     prog = '#include <stdio.h>\n#include <stddef.h>\n#include "gdp.h"\nint main(void){\n'
-    prog += 'printf("%zu\\n", sizeof(gdp_chunk_args));\n'
+    prog += 'printf("%%zu\\n", sizeof(%s));\n' % cname
     for f in fields:
-        prog += 'printf("%%zu\\n", offsetof(gdp_chunk_args, %s));\n' % f
+        prog += 'printf("%%zu\\n", offsetof(%s, %s));\n' % (cname, f)
     prog += "return 0;}\n"
     c = tmp_path / "layout.c"
     c.write_text(prog)
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)])
     vals = [int(x) for x in subprocess.check_output([str(exe)], text=True).split()]
-    assert vals[0] == ctypes.sizeof(B.ChunkArgs)
+    assert vals[0] == ctypes.sizeof(cls)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(B.ChunkArgs, f).offset == off, f
+        assert getattr(cls, f).offset == off, f
 
 
 def test_version_string():
@@ -138,18 +140,27 @@ def test_empty_problem_launches_nothing():
     assert B.lib().gdp_chunk_fwd(ctypes.byref(a), None) == B.GDP_OK
 
 
-def _prep(**kw):
+def _prep_call(fn, **kw):
     base = dict(x=0x10000, xn=0, xt=5632, ba=0x20000, bn=0, bt=48, A_log=0x30000, dt_bias=0x40000,
                 n=1, T=16, M=2, H=16, G=4, P=128, N=128, dtype=B.GDP_BF16,
                 q=0x50000, k=0x60000, v=0x70000, beta=0x80000, g=0x90000)
     base.update(kw)
     b = base
-    return B.lib().gdp_prefill_prepare(b["x"], b["xn"], b["xt"], b["ba"], b["bn"], b["bt"], b["A_log"],
-                                       b["dt_bias"], b["n"], b["T"], b["M"], b["H"], b["G"], b["P"],
-                                       b["N"], b["dtype"], b["q"], b["k"], b["v"], b["beta"], b["g"], None)
+    return fn(b["x"], b["xn"], b["xt"], b["ba"], b["bn"], b["bt"], b["A_log"], b["dt_bias"], b["n"], b["T"],
+              b["M"], b["H"], b["G"], b["P"], b["N"], b["dtype"], b["q"], b["k"], b["v"], b["beta"], b["g"], None)
 
 
-def test_prepare_rejects():
+def _prep_prefill(**kw):
+    return _prep_call(B.lib().gdp_prefill_prepare, **kw)
+
+
+def _prep_decode(**kw):
+    return _prep_call(B.lib().gdp_decode_prepare, **kw)
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_prepare_rejects(decode):
+    _prep = _prep_decode if decode else _prep_prefill
     assert _prep(G=3) == B.GDP_ERR_INVALID          # H % G
     assert _prep(M=0) == B.GDP_ERR_INVALID
     assert _prep(dtype=5) == B.GDP_ERR_INVALID
@@ -168,3 +179,43 @@ def test_num_state_chunks():
     # offsets are clamped into [0, T]
     assert B.num_state_chunks(100, 1, cu_seqlens_host=[0, 500]) == 2
     assert B.lib().gdp_num_state_chunks(None, 0, 1, -1, 1, 64) == -1
+
+
+def _dec(**kw):
+    base = dict(n=4, S=1, H=2, HV=4, K=128, V=128, M=2, scale=0.0, dtype=B.GDP_BF16, pool=8,
+                q=0x10000, k=0x20000, v=0x30000, beta=0x40000, g=0x50000, state=0x60000, slots=None, o=0x70000)
+    base.update(kw)
+    return B.lib().gdp_decode_update(ctypes.byref(B.DecodeArgs(**base)), None)
+
+
+BAD_DECODE = [
+    ("K=96", dict(K=96), B.GDP_ERR_UNSUPPORTED),
+    ("V=32", dict(V=32), B.GDP_ERR_UNSUPPORTED),
+    ("M=5", dict(M=5), B.GDP_ERR_UNSUPPORTED),
+    ("S*M too long", dict(S=2049), B.GDP_ERR_UNSUPPORTED),
+    ("HV % H", dict(HV=3), B.GDP_ERR_INVALID),
+    ("dtype", dict(dtype=4), B.GDP_ERR_INVALID),
+    ("n<0", dict(n=-1), B.GDP_ERR_INVALID),
+    ("pool < n without slots", dict(pool=3), B.GDP_ERR_INVALID),
+    ("null state", dict(state=None), B.GDP_ERR_INVALID),
+    ("null beta", dict(beta=None), B.GDP_ERR_INVALID),
+    ("misaligned k", dict(k=0x20008), B.GDP_ERR_INVALID),
+    ("misaligned state", dict(state=0x60004), B.GDP_ERR_INVALID),
+    ("inf scale", dict(scale=float("inf")), B.GDP_ERR_INVALID),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_DECODE, ids=[c[0] for c in BAD_DECODE])
+def test_decode_update_rejects(name, kw, status):
+    st = _dec(**kw)
+    assert st == status, (st, B.lib().gdp_last_error())
+    assert B.lib().gdp_last_error()
+
+
+def test_decode_update_empty_and_null():
+    assert B.lib().gdp_decode_update(None, None) == B.GDP_ERR_INVALID
+    # nothing to do: valid without buffers, nothing launched
+    assert _dec(n=0, q=None, k=None, v=None, beta=None, g=None, state=None, o=None) == B.GDP_OK
+    assert _dec(S=0, q=None, k=None, v=None, beta=None, g=None, state=None, o=None) == B.GDP_OK
+    # with slots the pool may be smaller than n (slots name the rows used)
+    assert _dec(n=0, pool=0, slots=0x80000, q=None, k=None, v=None, beta=None, state=None, o=None) == B.GDP_OK

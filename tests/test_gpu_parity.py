@@ -16,7 +16,7 @@ import oracle
 from oracle import prepare as OP
 from gated_delta_product_amd import binding as G
 from gated_delta_product_amd import synth
-from helpers import TOL, Acc, f32, gates, log, oracle_pair, run_pairs
+from helpers import TOL, Acc, f32, gates, log, metrics, oracle_pair, run_pairs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -466,3 +466,124 @@ def test_pipelined_forward_is_bit_identical():
             for nm in ("o", "w", "u", "v_new", "h", "ht"):
                 assert torch.equal(getattr(ref, nm), getattr(pip, nm)), (nseg, gg is None, nm)
             assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0 for i in range(n))
+
+
+# ---------------------------------------------------------------------- decode
+
+def test_decode_prepare_matches_oracle():
+    """gdp_decode_prepare: key, value and the query copies bit-exact, the
+    query only on each token's last copy and the decay only on its first
+    (exact zeros elsewhere), gates within 1 ulp; bf16 and f32, M = 2 and 3."""
+    cases = (("bf16", 5, 3, 2, 16, 4, 128, 128), ("f32", 3, 2, 3, 4, 2, 64, 64), ("bf16", 64, 1, 4, 16, 16, 128, 128))
+    for i, (dt, n, S, M, H, G_, P, N) in enumerate(cases):
+        d = synth.prepare_draws(n, S, M, H, G_, P, N, dt, synth.seed_of(3) + 50 + i)
+        log("decode prepare case %d: %s n=%d S=%d M=%d H=%d G=%d P=%d N=%d" % (i, dt, n, S, M, H, G_, P, N))
+        q, k, v, beta, g = G.decode_prepare(d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV),
+                                            d["dt_bias"].to(DEV), M, H, G_, P, N)
+        torch.cuda.synchronize()
+        rq, rk, rv, rb, rg = OP.decode_prepare(f32(d["x"]), f32(d["ba"]), d["A_log"].numpy(), d["dt_bias"].numpy(),
+                                               M, H, G_, P, N)
+        t = q.dtype
+        assert torch.equal(q.cpu(), torch.from_numpy(rq).to(t)), "q"
+        assert torch.equal(k.cpu(), torch.from_numpy(rk).to(t)), "k"
+        assert torch.equal(v.cpu(), torch.from_numpy(rv).to(t)), "v"
+        gc = g.cpu().numpy()
+        assert np.all(gc[:, [e for e in range(S * M) if e % M]] == 0.0)
+        assert _ulps(beta.cpu().numpy(), rb).max() <= 1 and _ulps(gc, rg).max() <= 1
+
+
+def _decode_oracle(q, k, v, beta, g, state, slots, scale=None):
+    """The per-row gated delta rule of each request from its slot's state,
+    by oracle.recurrence with one copy per row.  Returns (o [n,L,HV,V],
+    state after the step [pool,HV,V,K]) in float64."""
+    n, L, H, _ = q.shape
+    HV = v.shape[2]
+    o = np.zeros((n, L, HV, v.shape[3]))
+    st = state.astype(np.float64).copy()
+    for i in range(n):
+        s = int(slots[i])
+        if s < 0 or s >= state.shape[0]:
+            continue
+        for hv in range(HV):
+            hk = hv // (HV // H)
+            r = oracle.recurrence(q[i, :, hk], k[i, :, hk], v[i, :, hv], beta[i, :, hv],
+                                  None if g is None else g[i, :, hv], 1, scale=scale, h0=state[s, hv],
+                                  want_vnew=False, want_h=False)
+            o[i, :, hv] = r["o"]
+            st[s, hv] = r["h_final"]
+    return o, st
+
+
+DECODE_CASES = [
+    # dtype, n, S, M, H, HV, K, V, pool, slots (None = request i -> slot i), gated
+    ("bf16", 5, 3, 2, 2, 4, 128, 128, 7, [6, -1, 0, 3, 7], True),
+    ("f32", 3, 2, 3, 1, 2, 64, 256, 3, None, True),
+    ("bf16", 4, 5, 1, 2, 2, 64, 64, 4, [2, 3, 1, 0], False),
+    ("bf16", 2, 1, 4, 1, 2, 128, 256, 2, None, True),
+    ("f32", 2, 7, 2, 2, 2, 128, 64, 9, [8, 4], True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=["%s-K%dV%d-M%d" % (c[0], c[6], c[7], c[3]) for c in DECODE_CASES])
+def test_decode_update_matches_oracle(case):
+    """gdp_decode_update against the oracle's serial recurrence: every row has
+    its own query, key, beta and decay; states come from a pool through
+    slots (negative and out-of-pool slots skip their request: o rows zero,
+    no state touched); unnamed slots keep their bits."""
+    dt, n, S, M, H, HV, K, V, pool, slots, gated = case
+    L = S * M
+    log("decode update: %s n=%d S=%d M=%d H=%d HV=%d K=%d V=%d pool=%d slots=%s gated=%s" % case)
+    d = synth.chunk_draws(n, L, H, HV, K, V, 1, dt, synth.seed_of(2) + 60 + K + V + M)
+    beta, g = gates(d)
+    beta = beta.reshape(n, L, HV)
+    g = g if gated else None
+    st0 = synth.initial_state_draws(pool, HV, V, K, synth.seed_of(2) + 61, sigma=0.2)
+    state = st0.to(DEV)
+    sl = None if slots is None else torch.tensor(slots, dtype=torch.int32, device=DEV)
+    o = G.decode_update(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), beta.to(DEV),
+                        None if g is None else g.to(DEV), state, M, slots=sl)
+    torch.cuda.synchronize()
+    slots_h = list(range(n)) if slots is None else slots
+    ro, rst = _decode_oracle(f32(d["q"]), f32(d["k"]), f32(d["v"]), beta.numpy(), None if g is None else g.numpy(),
+                             st0.numpy(), slots_h)
+    tol = TOL[d["q"].dtype]
+    mo, ro_l2, fin = metrics(f32(o), ro)
+    ms, rs_l2, fin_s = metrics(state.cpu().numpy(), rst)
+    log("  o: max_abs %.3g rel_l2 %.3g; state: max_abs %.3g rel_l2 %.3g" % (mo, ro_l2, ms, rs_l2))
+    assert fin and fin_s
+    assert mo <= tol["max_abs"] and ro_l2 <= tol["rel_l2"]
+    assert ms <= TOL[torch.float32]["max_abs"] and rs_l2 <= TOL[torch.float32]["rel_l2"]
+    used = {s for s in slots_h if 0 <= s < pool}
+    for s in range(pool):
+        if s not in used:
+            assert torch.equal(state[s].cpu(), st0[s]), "slot %d touched" % s
+    for i, s in enumerate(slots_h):
+        if not 0 <= s < pool:
+            assert torch.count_nonzero(o[i]) == 0, "skipped request %d wrote o" % i
+
+
+def test_decode_continues_chunked_prefill():
+    """A prompt run through gdp_prefill_prepare + gdp_chunk_fwd, then S tokens
+    through gdp_decode_prepare + gdp_decode_update from its final state, gives
+    the outputs (read on each token's last copy) and final state of the
+    chunked forward over prompt plus the S tokens; and S one-token decode
+    calls equal one S-token call bit for bit."""
+    n, T0, S, M, H, G_, P, N = 3, 200, 3, 2, 4, 2, 128, 128
+    d = synth.prepare_draws(n, T0 + S, M, H, G_, P, N, "bf16", synth.seed_of(3) + 70)
+    x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
+    full = G.chunk_fwd(*G.prefill_prepare(x, ba, A_log, dt_bias, M, H, G_, P, N), output_final_state=True)
+    pre = G.chunk_fwd(*G.prefill_prepare(x[:, :T0], ba[:, :T0], A_log, dt_bias, M, H, G_, P, N),
+                      output_final_state=True)
+    state = pre.ht.clone()
+    o = G.decode_update(*G.decode_prepare(x[:, T0:], ba[:, T0:], A_log, dt_bias, M, H, G_, P, N), state, M)
+    state1 = pre.ht.clone()
+    o1 = [G.decode_update(*G.decode_prepare(x[:, T0 + t:T0 + t + 1], ba[:, T0 + t:T0 + t + 1], A_log, dt_bias,
+                                            M, H, G_, P, N), state1, M) for t in range(S)]
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(o1, 1), o) and torch.equal(state1, state)
+    tol = TOL[torch.bfloat16]
+    mo, ro, fin = metrics(f32(o[:, M - 1::M]), f32(full.o[:, T0:]))
+    ms, rs, fin_s = metrics(state.cpu().numpy(), full.ht.cpu().numpy())
+    log("decode after prefill: o max_abs %.3g rel_l2 %.3g; state max_abs %.3g rel_l2 %.3g" % (mo, ro, ms, rs))
+    assert fin and fin_s and mo <= tol["max_abs"] and ro <= tol["rel_l2"] and rs <= tol["rel_l2"]
+    assert torch.count_nonzero(o.reshape(n, S, M, -1)[:, :, :M - 1]) == 0

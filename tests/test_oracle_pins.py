@@ -395,3 +395,17 @@ def test_prepare_index_maps_by_construction():
                     assert np.array_equal(v[b, t * M + j, h], vv[b, t, j, h])
                     assert np.array_equal(k[b, t * M + j, h], kg[b, t, j, h // (H // G)])
                     assert beta[b, t * M + j, h] == P.sigmoid_rn32(ba[b, t, j * H + h])
+    # decode form: the same inputs walk the copies as one sequence of T*M
+    # rows, the query on each token's last copy and the decay on its first
+    dq, dk, dv, dbeta, dg = P.decode_prepare(x, ba, A_log, dt, M, H, G, Pd, N)
+    assert dq.shape == (n, T * M, H, N) and dg.shape == (n, T * M, H)
+    assert np.array_equal(dk, k) and np.array_equal(dv, v) and np.array_equal(dbeta, beta)
+    for b in range(n):
+        for t in range(T):
+            for h in range(H):
+                for j in range(M):
+                    e = t * M + j
+                    want_q = qg[b, t, h // (H // G)] if j == M - 1 else np.zeros(N, np.float32)
+                    assert np.array_equal(dq[b, e, h], want_q)
+                    want_g = P.decay_rn32(ba[b, t, M * H + h], A_log[h], dt[h]) if j == 0 else 0.0
+                    assert dg[b, e, h] == want_g
