@@ -38,6 +38,9 @@ HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(workload="long_prefill_32k", B=1, T=32768, H=16, HV=16, G=16, K=128, V=128, M=2, chunk=64,
                 dtype="bf16", path="prepare+pipelined(recompute_w_u,chunk_h,chunk_o)")
 SEGMENTS = 4
+# A serving decode step of the same layer: 256 requests, one token each
+# (no draft tokens), the fp32 state of every request read and written once.
+DECODE = dict(workload="decode_step", n=256, S=1, H=16, HV=16, G=16, K=128, V=128, M=2, dtype="bf16")
 KERNELS = ["gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o"]
 
 
@@ -61,6 +64,14 @@ def algorithmic_bytes(w, T=None):
     co = T * H * K * es + TM * H * K * es + TM * H * 4 + TM * HV * V * es + ntok_chunks * HV * V * K * es \
         + T * HV * 4 + T * HV * V * es
     return {"gdp_prefill_prepare": prep, "gdp_recompute_w_u": wy, "gdp_chunk_h": ch, "gdp_chunk_o": co}
+
+
+def decode_bytes(c):
+    """Minimum HBM bytes of gdp_decode_update: the fp32 state read and
+    written once, the q, k, v rows and fp32 beta, g read, o written."""
+    n, L, es = c["n"], c["S"] * c["M"], 2
+    return (2 * n * c["HV"] * c["V"] * c["K"] * 4 + n * L * (2 * c["H"] * c["K"] + c["HV"] * c["V"]) * es
+            + n * L * c["HV"] * 8 + n * L * c["HV"] * c["V"] * es)
 
 
 def measured_traffic(kernel):
@@ -112,6 +123,40 @@ def cpu_baseline(d, w, threads):
                       "-> o, v_new, h, and per-chunk WY -> w, u); %.1f s wall" % (Ts, w["HV"], dt)}
 
 
+def decode_step(G, torch, dev, stream, steps):
+    """Time gdp_decode_prepare + gdp_decode_update on the DECODE workload
+    (inputs resident; the state pool advanced in place every step)."""
+    from gated_delta_product_amd import synth
+    c = DECODE
+    n, S, M, H, Gq, P, N = c["n"], c["S"], c["M"], c["H"], c["G"], c["V"], c["K"]
+    d = synth.prepare_draws(n, S, M, H, Gq, P, N, "bf16", synth.seed_of(4) + 200)
+    x, ba = d["x"].to(dev), d["ba"].to(dev)
+    A_log, dt_bias = d["A_log"].to(dev), d["dt_bias"].to(dev)
+    gen = torch.Generator(device=dev).manual_seed(synth.seed_of(4) + 201)
+    state = torch.randn((n, c["HV"], c["V"], c["K"]), generator=gen, device=dev) * 0.1
+    rows = G.decode_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N)
+    o = torch.empty((n, S * M, c["HV"], c["V"]), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        G.decode_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=rows)
+        G.decode_update(*rows, state, M, o=o)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        G.decode_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=rows)
+        e[1].record(stream)
+        G.decode_update(*rows, state, M, o=o)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    prep_us = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e3
+    upd_us = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e3
+    ub = decode_bytes(c)
+    return {"config": dict(c), "tokens_per_s": round(n * S / ((prep_us + upd_us) / 1e6), 1),
+            "gdp_decode_prepare_us": round(prep_us, 2),
+            "gdp_decode_update": {"us": round(upd_us, 2), "alg_bytes": ub, "GB/s": round(ub / upd_us / 1e3, 1),
+                                  "hbm_frac": round(ub / upd_us / 1e3 / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +165,7 @@ def main():
     ap.add_argument("--segments", type=int, default=SEGMENTS, help="pipeline segments of the chunk forward")
     ap.add_argument("--stages", action="store_true", help="also time each stage sequentially (not overlapped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (untimed), "
                          "the known-size kernel that calibrates rocprofv3 byte counters")
@@ -214,6 +260,10 @@ def main():
             stages[k] = {"us": round(ms * 1e3, 2), "GB/s": round(ab[k] / (ms / 1e3) / 1e9, 1),
                          "hbm_frac": round(ab[k] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    dec = None
+    if not args.no_decode:
+        dec = decode_step(G, torch, dev, stream, max(args.steps, 20))
+
     if args.copy_mib > 0:
         n = args.copy_mib * 1024 * 1024 // 2
         src = torch.ones(n, dtype=torch.int16, device=dev)
@@ -235,6 +285,8 @@ def main():
     }
     if stages:
         out["stages_sequential"] = stages
+    if dec:
+        out["decode"] = dec
     print(json.dumps(out), flush=True)
 
 

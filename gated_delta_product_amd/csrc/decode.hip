@@ -8,17 +8,26 @@
 //             o = scale * S qhat,
 // the corrected-value form of S <- exp(g) S (I - beta khat khat^T) + beta v khat^T.
 //
-// One block of NT threads per (request, value head), NT sized so that each
-// thread holds at most 32 state entries.  The V x K fp32 state is split into
-// runs of EPT consecutive K entries of one row: thread t holds row t / TPR,
-// entries (t % TPR) * EPT .. +EPT.  The two matrix-vector
-// products of a row reduce over the TPR consecutive lanes of a row with
-// cross-lane adds; the rank-1 update is local.  The step is bound by moving
-// the state (read and written once per step).
+// One block of NT threads per (request, value head).  Each state row (K fp32
+// entries) is spread over TPR = K/4 consecutive lanes, 4 entries per lane,
+// so one wave-wide 16-byte load or store covers whole contiguous rows; the
+// block covers NT/TPR rows per pass and each thread holds RPT rows spaced by
+// that stride.  The row dot products reduce over the TPR lanes of a row
+// (DPP within 16 lanes, one swizzle beyond); the rank-1 update is local.
+// The step is bound by moving the state (read and written once per step).
 #include "gdp_common.h"
 #include "gdp_internal.h"
 
 namespace gdp {
+
+template <typename T> __device__ __forceinline__ f32x4 load4(const T *p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float *p) { return *(const f32x4 *)p; }
+template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
+    const uint2 u = *(const uint2 *)p;
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
 
 template <typename T, int KD, int VD, int NT>
 __global__ void __launch_bounds__(NT)
@@ -26,79 +35,49 @@ gdp_decode_k(const T *__restrict__ q, const T *__restrict__ k, const T *__restri
              const float *__restrict__ beta, const float *__restrict__ g, float *__restrict__ state,
              const int32_t *__restrict__ slots, int64_t pool, int L, int H, int HV, float scale,
              T *__restrict__ o) {
-    constexpr int EPT = KD * VD / NT;   // state entries per thread
-    constexpr int TPR = KD / EPT;       // threads per state row
-    constexpr int E = 16 / (int)sizeof(T);
-    static_assert(EPT % 4 == 0 && EPT % E == 0 && TPR >= 1 && TPR <= 64 && (TPR & (TPR - 1)) == 0,
-                  "state split");
+    constexpr int TPR = KD / 4;      // lanes per state row
+    constexpr int RSTEP = NT / TPR;  // rows covered per pass of the block
+    constexpr int RPT = VD / RSTEP;  // rows per thread
+    static_assert(64 % TPR == 0 && VD % RSTEP == 0 && RPT >= 1, "state split");
     const int64_t req = blockIdx.x;
     const int hv = blockIdx.y, hk = hv / (HV / H);
-    const int tid = threadIdx.x;
-    const int vr = tid / TPR, k0 = (tid % TPR) * EPT;
-    const bool writer = (tid % TPR) == 0;
+    const int tid = threadIdx.x, p = tid % TPR, r0 = tid / TPR;
     const int64_t slot = slots ? (int64_t)slots[req] : req;
 
     if (slot < 0 || slot >= pool) {  // skipped request: its rows are zero
-        for (int e = 0; e < L; ++e)
-            if (writer) o[((req * L + e) * HV + hv) * (int64_t)VD + vr] = from_f32<T>(0.f);
+        for (int i = tid; i < L * VD; i += NT)
+            o[((req * L + i / VD) * HV + hv) * (int64_t)VD + i % VD] = from_f32<T>(0.f);
         return;
     }
-    float *st = state + ((slot * HV + hv) * (int64_t)VD + vr) * KD + k0;
-    float s[EPT];
+    float *st = state + (slot * HV + hv) * (int64_t)VD * KD + 4 * p;
+    f32x4 s[RPT];
 #pragma unroll
-    for (int i = 0; i < EPT; i += 4) {
-        const f32x4 x = *(const f32x4 *)(st + i);
-        s[i] = x[0], s[i + 1] = x[1], s[i + 2] = x[2], s[i + 3] = x[3];
-    }
-    // sum over the TPR lanes of one state row
-    auto row_sum = [](float x) {
-#pragma unroll
-        for (int d = 1; d < TPR; d <<= 1) x += __shfl_xor(x, d, 64);
-        return x;
-    };
+    for (int j = 0; j < RPT; ++j) s[j] = *(const f32x4 *)(st + (int64_t)(r0 + j * RSTEP) * KD);
 
     for (int e = 0; e < L; ++e) {
         const int64_t row = req * L + e;
-        float kr[EPT], qr[EPT];
-        const T *kp = k + (row * H + hk) * (int64_t)KD + k0;
-        const T *qp = q + (row * H + hk) * (int64_t)KD + k0;
+        const f32x4 kr = load4<T>(k + (row * H + hk) * (int64_t)KD + 4 * p);
+        const f32x4 qr = load4<T>(q + (row * H + hk) * (int64_t)KD + 4 * p);
+        const T *vp = v + (row * HV + hv) * (int64_t)VD + r0;
+        float vv[RPT];
 #pragma unroll
-        for (int i = 0; i < EPT; i += E) {
-            const uint4 ku = *(const uint4 *)(kp + i), qu = *(const uint4 *)(qp + i);
-            const T *ke = (const T *)&ku, *qe = (const T *)&qu;
-#pragma unroll
-            for (int j = 0; j < E; ++j) {
-                kr[i + j] = to_f32(ke[j]);
-                qr[i + j] = to_f32(qe[j]);
-            }
-        }
-        const float vv = to_f32(v[(row * HV + hv) * (int64_t)VD + vr]);
+        for (int j = 0; j < RPT; ++j) vv[j] = to_f32(vp[j * RSTEP]);
         const float b = beta[row * HV + hv];
         const float alpha = g ? __expf(g[row * HV + hv]) : 1.0f;
-        float ssk = 0.f, ssq = 0.f, sk = 0.f;
+        const float rk = 1.0f / sqrtf(group_sum<TPR>(dot4(kr, kr)) + 1e-6f);
+        const float rq = 1.0f / sqrtf(group_sum<TPR>(dot4(qr, qr)) + 1e-6f);
+        T *op = o + (row * HV + hv) * (int64_t)VD + r0;
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            ssk += kr[i] * kr[i];
-            ssq += qr[i] * qr[i];
-            sk += s[i] * kr[i];
+        for (int j = 0; j < RPT; ++j) {
+            const float sk = group_sum<TPR>(dot4(s[j], kr));
+            const float dk = b * (vv[j] - alpha * (sk * rk)) * rk;
+            s[j] = alpha * s[j] + dk * kr;
+            const float so = group_sum<TPR>(dot4(s[j], qr));
+            if (p == 0) op[j * RSTEP] = from_f32<T>(scale * rq * so);
         }
-        ssk = row_sum(ssk);
-        ssq = row_sum(ssq);
-        sk = row_sum(sk);
-        const float rk = 1.0f / sqrtf(ssk + 1e-6f), rq = 1.0f / sqrtf(ssq + 1e-6f);
-        const float delta = b * (vv - alpha * (sk * rk));
-        const float dk = delta * rk;
-        float so = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            s[i] = alpha * s[i] + dk * kr[i];
-            so += s[i] * qr[i];
-        }
-        so = row_sum(so);
-        if (writer) o[(row * HV + hv) * (int64_t)VD + vr] = from_f32<T>(scale * rq * so);
     }
 #pragma unroll
-    for (int i = 0; i < EPT; i += 4) *(f32x4 *)(st + i) = f32x4{s[i], s[i + 1], s[i + 2], s[i + 3]};
+    for (int j = 0; j < RPT; ++j) *(f32x4 *)(st + (int64_t)(r0 + j * RSTEP) * KD) = s[j];
 }
 
 template <typename T, int KD, int VD>

@@ -155,6 +155,28 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
     return x;
 }
 
+// x moved across lanes by a DPP pattern (every source lane is in range for
+// the patterns used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over each aligned group of N consecutive lanes (N a power of two up to
+// 64); every lane of the group gets the same bits.  Within 16 lanes the
+// partners come from DPP: swap neighbours, swap pairs, mirror the half row,
+// mirror the row -- after each step all lanes of the growing group agree.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+    if constexpr (N >= 2) x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x += dpp_move<0x141>(x);  // row_half_mirror
+    if constexpr (N >= 16) x += dpp_move<0x140>(x); // row_mirror
+    if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 // Block-cooperative lookup of linear item `id` over sequences, where
 // sequence i owns ceil(len_i * rows_per_token / chunk) consecutive items.
 // Every thread of the block must call it (it uses barriers); wave 0 scans

@@ -271,8 +271,11 @@ gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
  * next segments and gdp_chunk_o of the finished ones run on two streams of
  * the library's own (created once per device, default priority) that join
  * `stream` through events.  On return all work is ordered before later work
- * on `stream`; nothing is synchronised with the host, and the calls can be
- * captured into a HIP graph.
+ * on `stream`; nothing is synchronised with the host.  The first call on a
+ * device, and a call with more segments than any before it, create the
+ * streams and events it needs: make such a call outside graph capture.
+ * Later calls create nothing and can be captured into a HIP graph (the
+ * side streams join the capture through the events).
  *   state_workspace  float32 [2, HV, V, K], device, caller-owned: the state
  *                    handed between segments.
  *   chunk_h_events   NULL, or 2 * gdp_pipeline_segments(T, num_segments)

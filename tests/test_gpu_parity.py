@@ -587,3 +587,50 @@ def test_decode_continues_chunked_prefill():
     log("decode after prefill: o max_abs %.3g rel_l2 %.3g; state max_abs %.3g rel_l2 %.3g" % (mo, ro, ms, rs))
     assert fin and fin_s and mo <= tol["max_abs"] and ro <= tol["rel_l2"] and rs <= tol["rel_l2"]
     assert torch.count_nonzero(o.reshape(n, S, M, -1)[:, :, :M - 1]) == 0
+
+
+# ---------------------------------------------------------------------- graphs
+
+def test_hip_graph_capture_replays():
+    """Prefill prepare, the chunk forward (one stream, and pipelined over the
+    library's side streams) and a decode step from the prefill's final state,
+    captured into one HIP graph over static buffers.  Before each replay the
+    inputs are rewritten in place by eager work; every replay equals the
+    eager calls on the same inputs bit for bit."""
+    T, S, M, H, G_, P, N = 700, 2, 2, 4, 2, 128, 128
+    draws = [synth.prepare_draws(1, T + S, M, H, G_, P, N, "bf16", synth.seed_of(4) + 80 + i) for i in range(3)]
+    A_log, dt_bias = draws[0]["A_log"].to(DEV), draws[0]["dt_bias"].to(DEV)
+    x, ba = draws[0]["x"].to(DEV), draws[0]["ba"].to(DEV)
+    xp, bap, xd, bad = x[:, :T], ba[:, :T], x[:, T:], ba[:, T:]
+    pre = G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N)
+    seq = G.ChunkBuffers(*pre, output_final_state=True)
+    pip = G.ChunkBuffers(*pre, output_final_state=True)
+    dec = G.decode_prepare(xd, bad, A_log, dt_bias, M, H, G_, P, N)
+    dec_o = torch.empty((1, S * M, H, P), dtype=torch.bfloat16, device=DEV)
+    # warm-up outside capture: the pipelined call creates its streams and events here
+    seq.forward()
+    pip.forward_pipelined(3)
+    G.decode_update(*dec, seq.ht, M, o=dec_o)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N, out=pre)
+        seq.forward()
+        pip.forward_pipelined(3)
+        G.decode_prepare(xd, bad, A_log, dt_bias, M, H, G_, P, N, out=dec)
+        G.decode_update(*dec, seq.ht, M, o=dec_o)   # continues from the prefill state, in place
+    for i in (1, 2, 0, 1):
+        log("graph replay on draw %d" % i)
+        x.copy_(draws[i]["x"].to(DEV))
+        ba.copy_(draws[i]["ba"].to(DEV))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = G.chunk_fwd(*G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N), output_final_state=True)
+        ref_ht = ref.ht.clone()
+        ref_o = G.decode_update(*G.decode_prepare(xd, bad, A_log, dt_bias, M, H, G_, P, N), ref.ht, M)
+        torch.cuda.synchronize()
+        for nm in ("o", "w", "u", "v_new", "h"):
+            assert torch.equal(getattr(seq, nm), getattr(ref, nm)), "sequential " + nm
+            assert torch.equal(getattr(pip, nm), getattr(ref, nm)), "pipelined " + nm
+        assert torch.equal(pip.ht, ref_ht), "pipelined ht"
+        assert torch.equal(dec_o, ref_o) and torch.equal(seq.ht, ref.ht), "decode"
