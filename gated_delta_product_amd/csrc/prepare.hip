@@ -51,13 +51,13 @@ struct Unit {
 // zeros elsewhere (q [n, T*M, H, N], g [n, T*M, H]); otherwise both stay
 // one per token.
 template <typename T, bool VEC16, bool DECODE>
-__global__ void __launch_bounds__(256)
-gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
-              const T *__restrict__ ba, int64_t bns, int64_t bts,
-              const float *__restrict__ A_log, const float *__restrict__ dt_bias,
-              int64_t T_, int M, int H, int G, int P, int N,
-              T *__restrict__ q, T *__restrict__ k, T *__restrict__ v,
-              float *__restrict__ beta, float *__restrict__ g) {
+__device__ __forceinline__ void
+prepare_body(const T *__restrict__ x, int64_t xns, int64_t xts,
+             const T *__restrict__ ba, int64_t bns, int64_t bts,
+             const float *__restrict__ A_log, const float *__restrict__ dt_bias,
+             int64_t T_, int M, int H, int G, int P, int N,
+             T *__restrict__ q, T *__restrict__ k, T *__restrict__ v,
+             float *__restrict__ beta, float *__restrict__ g) {
     typedef typename Unit<T, VEC16>::type U;
     constexpr int E = Unit<T, VEC16>::elems;
     const int64_t t = blockIdx.x;
@@ -136,10 +136,27 @@ gdp_prepare_k(const T *__restrict__ x, int64_t xns, int64_t xts,
     }
 }
 
+// The prefill and decode forms are separate kernels so that profiles tell
+// them apart.
+#define GDP_PREPARE_PARAMS                                                                          \
+    const T *__restrict__ x, int64_t xns, int64_t xts, const T *__restrict__ ba, int64_t bns,       \
+        int64_t bts, const float *__restrict__ A_log, const float *__restrict__ dt_bias, int64_t T_, \
+        int M, int H, int G, int P, int N, T *__restrict__ q, T *__restrict__ k, T *__restrict__ v,  \
+        float *__restrict__ beta, float *__restrict__ g
+template <typename T, bool VEC16>
+__global__ void __launch_bounds__(256) gdp_prepare_k(GDP_PREPARE_PARAMS) {
+    prepare_body<T, VEC16, false>(x, xns, xts, ba, bns, bts, A_log, dt_bias, T_, M, H, G, P, N, q, k, v, beta, g);
+}
+template <typename T, bool VEC16>
+__global__ void __launch_bounds__(256) gdp_decode_prepare_k(GDP_PREPARE_PARAMS) {
+    prepare_body<T, VEC16, true>(x, xns, xts, ba, bns, bts, A_log, dt_bias, T_, M, H, G, P, N, q, k, v, beta, g);
+}
+#undef GDP_PREPARE_PARAMS
+
 template <typename T, bool VEC16, bool DECODE>
 static hipError_t launch_prepare_t(const PrepareParams &p, hipStream_t stream) {
     dim3 grid((unsigned)p.T, (unsigned)p.n);
-    hipLaunchKernelGGL((gdp_prepare_k<T, VEC16, DECODE>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((DECODE ? gdp_decode_prepare_k<T, VEC16> : gdp_prepare_k<T, VEC16>), grid, dim3(256), 0, stream,
                        (const T *)p.x, p.x_n_stride, p.x_t_stride,
                        (const T *)p.ba, p.ba_n_stride, p.ba_t_stride,
                        p.A_log, p.dt_bias, p.T, p.M, p.H, p.G, p.P, p.N,

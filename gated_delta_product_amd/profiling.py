@@ -27,6 +27,8 @@ CSRC = os.path.join(ROOT, "gated_delta_product_amd", "csrc")
 
 # host-visible operation -> (device symbol substring, sources that define it)
 KERNELS = {
+    "gdp_decode_prepare": ("gdp_decode_prepare_k", ["prepare.hip"]),
+    "gdp_decode_update": ("gdp_decode_k", ["decode.hip"]),
     "gdp_prefill_prepare": ("gdp_prepare_k", ["prepare.hip"]),
     "gdp_recompute_w_u": ("gdp_wy_k", ["wy.hip"]),
     "gdp_chunk_h": ("gdp_chunk_h_k", ["chunk_h.hip"]),
