@@ -47,7 +47,11 @@ KERNELS = ["gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk
 def algorithmic_bytes(w, T=None):
     """HBM bytes each stage must move at minimum (inputs read once, outputs
     written once), per launch over T tokens (default: the whole workload).
-    es = 2 (bf16); beta, g, k_rnorm are fp32."""
+    es = 2 (bf16); beta, g, k_rnorm, gcum and kdecay are fp32.
+      prepare  x, ba -> q, k, v, beta, g
+      WY       k, v, beta, g -> w, u, k_rnorm, gcum, kdecay
+      chunk_h  k, kdecay, gcum, w, u -> v_new, h (one state per 64-row chunk)
+      chunk_o  q, k, k_rnorm, v_new, h (one per 64-token chunk), g -> o"""
     T = w["T"] * w["B"] if T is None else T
     M, H, HV, G, K, V = w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
     P, N = V, K
@@ -58,8 +62,8 @@ def algorithmic_bytes(w, T=None):
     prep = T * (M * H * P + M * G * N + G * N) * es + T * (M * H + H) * es \
         + T * H * N * es + TM * H * N * es + TM * H * P * es + TM * H * 4 + T * H * 4
     wy = TM * H * K * es + TM * HV * V * es + TM * HV * 4 + T * HV * 4 \
-        + TM * HV * K * es + TM * HV * V * es + TM * H * 4
-    ch = TM * H * K * es + TM * H * 4 + TM * HV * K * es + TM * HV * V * es + T * HV * 4 \
+        + TM * HV * K * es + TM * HV * V * es + TM * H * 4 + TM * HV * 8
+    ch = TM * H * K * es + TM * HV * 8 + TM * HV * K * es + TM * HV * V * es \
         + TM * HV * V * es + nte * HV * V * K * es
     co = T * H * K * es + TM * H * K * es + TM * H * 4 + TM * HV * V * es + ntok_chunks * HV * V * K * es \
         + T * HV * 4 + T * HV * V * es
