@@ -240,8 +240,10 @@ class ChunkBuffers:
         self.gcum = torch.empty((B, HV, T * M), dtype=torch.float32, device=dev)
         self.kdecay = torch.empty((B, HV, T * M), dtype=torch.float32, device=dev)
         self.w = torch.empty((B, T * M, HV, K), dtype=dt, device=dev)
-        self.u = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
-        self.v_new = torch.empty((B, T * M, HV, V), dtype=dt, device=dev)
+        # u and v_new are stored as 16-column slices [B, HV, V/16, T*M, 16]
+        # (slices_to_rows gives the [B, T*M, HV, V] view)
+        self.u = torch.empty((B, HV, V // 16, T * M, 16), dtype=dt, device=dev)
+        self.v_new = torch.empty((B, HV, V // 16, T * M, 16), dtype=dt, device=dev)
         self.h = torch.empty((h_chunks, HV, V, K), dtype=dt, device=dev)
         self.o = torch.empty((B, T, HV, V), dtype=dt, device=dev)
         self.device = dev
@@ -302,6 +304,18 @@ class ChunkBuffers:
         _check(lib().gdp_chunk_fwd_pipelined(ctypes.byref(self.args), int(num_segments), self._ws.data_ptr(),
                                              ev, s))
         return self.o
+
+
+def slices_to_rows(t):
+    """A slice-major u / v_new [B, HV, V/16, T*M, 16] as [B, T*M, HV, V] (a copy)."""
+    B, HV, S, TM, _ = t.shape
+    return t.permute(0, 3, 1, 2, 4).reshape(B, TM, HV, S * 16)
+
+
+def rows_to_slices(t):
+    """[B, T*M, HV, V] -> the slice-major [B, HV, V/16, T*M, 16] layout of u / v_new."""
+    B, TM, HV, V = t.shape
+    return t.reshape(B, TM, HV, V // 16, 16).permute(0, 2, 3, 1, 4).contiguous()
 
 
 def chunk_fwd(q, k, v, beta, g, scale=None, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,

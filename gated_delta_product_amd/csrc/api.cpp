@@ -113,6 +113,7 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
     out->nseq = empty ? 0 : nseq;
     out->max_items = empty ? 0 : max_items;
     out->max_tok_chunks = empty ? 0 : max_tok;
+    out->uv_ss = T * a->M * 16;
     return ok();
 }
 
@@ -315,14 +316,15 @@ gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments
         sa.gcum = a->gcum + r0 * a->HV;
         sa.kdecay = a->kdecay + r0 * a->HV;
         sa.w = (char *)a->w + r0 * a->HV * a->K * es;
-        sa.u = (char *)a->u + r0 * a->HV * a->V * es;
-        sa.v_new = (char *)a->v_new + r0 * a->HV * a->V * es;
+        sa.u = (char *)a->u + r0 * 16 * es;          // row r0 of every 16-column slice
+        sa.v_new = (char *)a->v_new + r0 * 16 * es;
         sa.h = (char *)a->h + c0 * state_elems * es;
         sa.o = (char *)a->o + t0 * a->HV * a->V * es;
         sa.h0 = sidx == 0 ? a->h0 : state_workspace + ((sidx - 1) & 1) * state_elems;
         sa.ht = sidx == nseg - 1 ? a->ht : state_workspace + (sidx & 1) * state_elems;
         gdp::ChunkParams sp;
         if ((st = check_chunk(&sa, ST_WY | ST_H | ST_O, &sp)) != GDP_OK) return st;
+        sp.uv_ss = a->T * a->M * 16;  // slices keep the whole sequence's stride
         hipEvent_t ev_w = ctx->ev[2 + 2 * sidx], ev_h = ctx->ev[3 + 2 * sidx];
         GDP_TRY(gdp::launch_wy(sp, sw), "gdp_chunk_fwd_pipelined: recompute_w_u launch");
         GDP_TRY(hipEventRecord(ev_w, sw), "hipEventRecord");

@@ -62,7 +62,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
               const float *__restrict__ h0, float *__restrict__ ht, T *__restrict__ v_new,
-              T *__restrict__ hout) {
+              T *__restrict__ hout, int64_t uv_ss) {
     typedef typename Frag<T>::type FragT;
     typedef typename Frag<T>::half HalfT;
     constexpr int ES = (int)sizeof(T);
@@ -127,7 +127,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         }
         return;
     }
-    const int ldk = H * KD, ldw = HV * KD, ldv = HV * VD;  // global row strides (elements)
+    const int ldk = H * KD, ldw = HV * KD;  // global row strides (elements)
     const int64_t r0 = bos * M;  // first expanded row of the sequence
     const int64_t h0r = hm_index(cu ? 0 : seq, HV, hv, Ttok * M, r0);  // kdecay / gcum of row r0
 
@@ -149,16 +149,16 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         // data lands in a scratch LDS area that nothing reads.
         constexpr int PF = 5;                    // prefetch distance in chunks
         constexpr int RPB = C / S;               // rows per block per chunk
-        static_assert(RPB * KD * ES / 128 <= 64 && RPB * VD * ES / 128 <= 64 && KD * ES >= 128 && VD * ES >= 128,
+        static_assert(RPB * KD * ES / 128 <= 64 && C * 16 * ES / 128 <= 64 && KD * ES >= 128,
                       "one 4-byte load per line must cover a block's rows");
         const uint32_t pf = lds_addr(&Pf[0]);
-        const int rbw = KD * ES, rbu = VD * ES;  // row bytes of w / k and of u
+        const int rbw = KD * ES;  // row bytes of w / k
         const char *pw = (const char *)(w + ((r0 + RPB * sl) * HV + hv) * KD);
         const char *pk = (const char *)(k + ((r0 + RPB * sl) * H + hk) * KD);
-        const char *pu = (const char *)(u + ((r0 + RPB * sl) * HV + hv) * VD);
+        const char *pu = (const char *)(u + uv_index(cu ? 0 : seq, r0 - (cu ? 0 : seq) * Ttok * M, hv, 16 * sl, HV, VD, uv_ss));
         const char *pd = (const char *)(kdecay + h0r);
         const char *pg = (const char *)(gcum + h0r);
-        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * ldv * ES,
+        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * 16 * ES,
                       st4 = (int64_t)C * 4;
         // rows [0, nr) of a tile with `rb`-byte rows `ld` bytes apart: one
         // 4-byte load per 128-byte line is enough to bring it into L2
@@ -174,7 +174,8 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             const int64_t oc = c;
             rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw);
             rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw);
-            rows_to_l2(pu + oc * stu, nr < RPB ? nr : RPB, ldv * ES, rbu);
+            // this block's u slice: n rows of 16 elements, contiguous
+            dma4(make_rsrc(pu + oc * stu, (uint32_t)(n * 16 * ES)), (uint32_t)(lane * 128), pf);
             if (sl == 0) {  // 256 contiguous bytes each: one block of the head is enough
                 dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
                 dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
@@ -218,15 +219,16 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         uint32_t ou[NU];
 #pragma unroll
         for (int i = 0; i < NU; ++i)
-            ou[i] = (uint32_t)(((i * (64 / UUPR) + lane / UUPR) * ldv) * ES + (lane % UUPR) * 16 - 1024 * (i % 4));
+            ou[i] = (uint32_t)((i * 64 + lane) * 16 - 1024 * (i % 4));  // the slice's rows are contiguous
         const uint32_t o4 = (uint32_t)(lane * 4);
 
         const char *pt = mw == 0 ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
         const int ldt = mw == 0 ? ldw : ldk;
         const int64_t stt = (int64_t)C * ldt * ES;
-        const char *pu = (const char *)(u + (r0 * HV + hv) * VD + 16 * sl);
+        const int64_t bseq = cu ? 0 : seq;  // batch row of the sequence
+        const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * Ttok * M, hv, 16 * sl, HV, VD, uv_ss));
         const char *p4 = mw == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
-        const int64_t stu = (int64_t)C * ldv * ES, st4 = (int64_t)C * 4;
+        const int64_t stu = (int64_t)C * 16 * ES, st4 = (int64_t)C * 4;  // slice bytes per chunk
         const int tile_off = mw == 0 ? OFW : OFK;
         const int off4 = mw == 0 ? OFD : OFG;
         int rem_issue = (int)rows;
@@ -245,7 +247,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 });
             });
             if (mw == 1) {
-                const rsrc_t ru = make_rsrc(pu, span(n, ldv * ES, 16 * ES));
+                const rsrc_t ru = make_rsrc(pu, (uint32_t)(n * 16 * ES));
                 const uint32_t sbu = ring_base + st * SB + OFU;
                 static_for<0, NU>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
@@ -277,15 +279,15 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             ph += sth;
         };
         // v_new rows [32mw, 32mw + 32) of chunk c, from Vt[c & 1]
-        char *pv = (char *)(v_new + (r0 * HV + hv) * VD + 16 * sl);
+        char *pv = (char *)(v_new + uv_index(bseq, r0 - bseq * Ttok * M, hv, 16 * sl, HV, VD, uv_ss));
         int rem_v = (int)rows;
         auto store_v = [&](int c) {
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_v));
-            const rsrc_t rv = make_rsrc(pv, span(n, ldv * ES, 16 * ES));
+            const rsrc_t rv = make_rsrc(pv, (uint32_t)(n * 16 * ES));
 #pragma unroll
             for (int r2 = 0; r2 < NVS; ++r2) {
                 const HalfT o4v = lds_col4<T>(Vt[c & 1], LDT, 4 * lg, 32 * mw + 16 * r2);
-                const uint32_t off = (uint32_t)(((32 * mw + 16 * r2 + lc) * ldv + 4 * lg) * ES);
+                const uint32_t off = (uint32_t)(((32 * mw + 16 * r2 + lc) * 16 + 4 * lg) * ES);
                 if constexpr (ES == 2)
                     buf_store8(rv, off, __builtin_bit_cast(uint2, o4v));
                 else
@@ -520,7 +522,7 @@ static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
     const int64_t nblk = ((P + 7) / 8) * 8 * S;
     hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(320), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
-                       p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h);
+                       p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h, p.uv_ss);
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ __global__ void __launch_bounds__(256)
 gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ k_rnorm,
               const T *__restrict__ v_new, const T *__restrict__ hst, const float *__restrict__ g,
               const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok, int H, int HV, int M, int VD,
-              int64_t h_chunks, float scale, T *__restrict__ o) {
+              int64_t h_chunks, float scale, T *__restrict__ o, int64_t uv_ss) {
     typedef typename Frag<T>::type FragT;
     typedef typename Frag<T>::half HalfT;
     constexpr int ES = (int)sizeof(T);
@@ -47,13 +47,13 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     constexpr int NVT = VB / 16;           // 16-column output tiles
     constexpr int SRB = KD * ES;           // bytes per state row
     constexpr int SUPR = SRB / 16;         // 16-byte units per state row
-    constexpr int VRB = VB * ES;           // bytes per V slab row
-    constexpr int VUPR = VRB / 16;         // 16-byte units per V slab row
+    constexpr int VRB = VB * ES;           // bytes per V slab row (as o stores it)
+    constexpr int VSB = C * 16 * ES;       // bytes per 16-column slice of the V slab
     constexpr int NSD = VB * SRB / 1024;   // DMA instructions for the state slab
     constexpr int NVD = C * VRB / 1024;    // DMA instructions for a V slab
-    static_assert(NSD % 4 == 0 && NVD % 4 == 0 && SUPR >= 8 && VUPR >= 8, "tile shape");
+    static_assert(NSD % 4 == 0 && NVD % 4 == 0 && SUPR >= 8 && VSB % 1024 == 0, "tile shape");
     __shared__ __attribute__((aligned(16))) T Ss[VB * KD];   // state slab, swizzled rows
-    __shared__ __attribute__((aligned(16))) T Vs[C * VB];    // V_j slab, swizzled rows
+    __shared__ __attribute__((aligned(16))) T Vs[C * VB];    // V_j slab: VB/16 slices of 64 rows x 16
     __shared__ float sG[4][C], sRk[4][C];                    // per-wave scratch
 
     const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, blockIdx.x);
@@ -69,11 +69,12 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     const int tt = wv;               // token tile of this wave
     const int t_loc = 16 * tt + lc;  // token whose column this lane holds
     auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
-    // swizzled byte offsets: state rows XOR their 16-byte unit with the row;
-    // V rows XOR 32-byte unit pairs, so a transposed read of four
-    // consecutive rows touches four distinct bank groups
+    // swizzled byte offsets of the state slab: rows XOR their 16-byte unit
+    // with the row.  The V slab is slice-major like v_new (row r of slice vt
+    // at vt * VSB + r * 16 * ES): a transposed read of four consecutive rows
+    // of one slice is 16 * 4 * ES contiguous bytes, free of bank conflicts.
     auto s_off = [](int r, int unit) { return r * SRB + ((unit ^ (r & (SUPR - 1))) << 4); };
-    auto v_off = [](int r, int unit) { return r * VRB + ((unit ^ ((r & (VUPR / 2 - 1)) << 1)) << 4); };
+    auto v_at = [](int vt, int r) { return vt * VSB + r * 16 * ES; };
 
     // ---- state slab (rows vb0 .. vb0 + VB of S) -> LDS; the snapshot is
     // zero-filled past h_chunks by the range check
@@ -88,16 +89,23 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
             dma16(rs, (uint32_t)(r * SRB + ((u ^ (r & (SUPR - 1))) << 4)), base + blk * 1024);
         }
     }
-    const int64_t ldkv_k = (int64_t)M * H * KD, ldkv_v = (int64_t)M * HV * VD;  // row strides per token
+    const int64_t ldkv_k = (int64_t)M * H * KD;  // key row stride per token
+    // V_j slab: rows (t0 + r) M + j of the VB/16 slices of v_new from column
+    // vb0; one DMA instruction fills RPI rows of one slice, whose rows sit
+    // M * 16 elements apart; rows past the chunk are zero-filled
+    const int64_t bseq = cu ? 0 : loc.seq;  // batch row of the sequence
     auto stage_v = [&](int j) {
-        const rsrc_t rv = make_rsrc(v_new + ((t0 * M + j) * HV + hv) * (int64_t)VD + vb0,
-                                    span(nt, (int)(ldkv_v * ES), VRB));
+        constexpr int IPS = VSB / 1024;        // DMA instructions per slice
+        constexpr int RPI = 1024 / (16 * ES);  // rows per instruction
+        constexpr int UPRV = 16 * ES / 16;     // 16-byte units per slice row
+        const T *vbase = v_new + uv_index(bseq, (t0 - bseq * Ttok) * M + j, hv, vb0, HV, VD, uv_ss);
         const uint32_t base = lds_addr(Vs);
 #pragma unroll
         for (int i = 0; i < NVD / 4; ++i) {
             const int blk = wv * (NVD / 4) + i;
-            const int r = blk * (1024 / VRB) + lane / VUPR, u = lane % VUPR;
-            dma16(rv, (uint32_t)(r * ldkv_v * ES + ((u ^ ((r & (VUPR / 2 - 1)) << 1)) << 4)), base + blk * 1024);
+            const int slc = blk / IPS, r = (blk % IPS) * RPI + lane / UPRV, u = lane % UPRV;
+            const rsrc_t rv = make_rsrc(vbase + slc * uv_ss, span(nt, M * 16 * ES, 16 * ES));
+            dma16(rv, (uint32_t)(r * M * 16 * ES + u * 16), base + blk * 1024);
         }
     };
     stage_v(0);
@@ -225,19 +233,16 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
                         // points at row rowA + jj/4, columns 16vt + 4(jj%4) .. +3
                         const int jj = lane & 15;
                         const int ra = 32 * ks + 4 * lg + (jj >> 2), rb = ra + 16;
-                        const int col = 16 * vt + 4 * (jj & 3);
-                        const int unit = col * 2 / 16, inner = (col * 2) & 15;
+                        const int cb = 4 * (jj & 3) * ES;  // byte of the column inside the slice row
                         x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_off(ra, unit) + inner))));
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_at(vt, ra) + cb))));
                         x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_off(rb, unit) + inner))));
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_at(vt, rb) + cb))));
                     } else {
-                        const int col = 16 * vt + lc;
-                        const int unit = col * 4 / 16, inner = (col * 4) & 15;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            x0[i] = *(const float *)(vb + v_off(32 * ks + 4 * lg + i, unit) + inner);
-                            x1[i] = *(const float *)(vb + v_off(32 * ks + 16 + 4 * lg + i, unit) + inner);
+                            x0[i] = *(const float *)(vb + v_at(vt, 32 * ks + 4 * lg + i) + lc * ES);
+                            x1[i] = *(const float *)(vb + v_at(vt, 32 * ks + 16 + 4 * lg + i) + lc * ES);
                         }
                     }
                     acc[vt] = mma(join<T>(x0, x1), pb[ks], acc[vt]);
@@ -273,7 +278,7 @@ static hipError_t launch_chunk_o_t(const ChunkParams &p, hipStream_t stream) {
     dim3 grid((unsigned)p.max_tok_chunks, (unsigned)a.HV, (unsigned)(a.V / VB));
     hipLaunchKernelGGL((gdp_chunk_o_k<T, KD, VB>), grid, dim3(256), 0, stream,
                        (const T *)a.q, (const T *)a.k, a.k_rnorm, (const T *)a.v_new, (const T *)a.h, a.g,
-                       a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.V, a.h_chunks, a.scale, (T *)a.o);
+                       a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.V, a.h_chunks, a.scale, (T *)a.o, p.uv_ss);
     return hipGetLastError();
 }
 

@@ -32,7 +32,17 @@ struct ChunkParams {
     int64_t nseq;       // sequences: num_seqs with cu_seqlens, else B
     int64_t max_items;  // upper bound on 64-row chunks over all sequences
     int64_t max_tok_chunks;  // upper bound on 64-token chunks
+    // u and v_new are stored as 16-column slices [B, HV, V/16, T*M, 16]:
+    // elements between consecutive slices (T*M*16 for a plain call; the
+    // whole sequence's for one segment of the pipelined forward)
+    int64_t uv_ss;
 };
+
+// Element offset of (batch row b, expanded row e relative to the batch row,
+// value head hv, column col) in a slice-major u / v_new tensor.
+__host__ __device__ inline int64_t uv_index(int64_t b, int64_t e, int hv, int col, int HV, int VD, int64_t ss) {
+    return (b * HV * (VD / 16) + (int64_t)hv * (VD / 16) + col / 16) * ss + e * 16 + col % 16;
+}
 
 hipError_t launch_wy(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_chunk_h(const ChunkParams &p, hipStream_t stream);

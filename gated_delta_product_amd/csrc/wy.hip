@@ -41,7 +41,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
          const float *__restrict__ g, const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok,
          int H, int HV, int M, float *__restrict__ k_rnorm, float *__restrict__ gcum,
          float *__restrict__ kdecay, T *__restrict__ w,
-         T *__restrict__ u) {
+         T *__restrict__ u, int64_t uv_ss) {
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
     constexpr int LDV = VD + Pad<T>::value;
@@ -273,10 +273,11 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                     acc = mma(a, bu[ks], acc);
                 }
             }
-            if (row_ok) {
-                T *dst = u + (grow * HV + hv) * (int64_t)VD + 16 * vt + 4 * lg;
+            if (row_ok) {  // u is slice-major: 4 consecutive columns of the row
+                typename Frag<T>::half o4;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[q] = from_f32<T>(acc[q]);
+                for (int q = 0; q < 4; ++q) o4[q] = from_f32<T>(acc[q]);
+                *(typename Frag<T>::half *)(u + uv_index(bi, grow - bi * TM, hv, 16 * vt + 4 * lg, HV, VD, uv_ss)) = o4;
             }
         }
 #pragma unroll
@@ -305,7 +306,7 @@ static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream) {
     dim3 grid((unsigned)p.max_items, (unsigned)a.HV);
     hipLaunchKernelGGL((gdp_wy_k<T, KD, VD>), grid, dim3(256), 0, stream,
                        (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
-                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u);
+                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u, p.uv_ss);
     return hipGetLastError();
 }
 

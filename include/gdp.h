@@ -204,8 +204,12 @@ gdp_status gdp_decode_update(const gdp_decode_args *a, void *stream);
  *                           enters the state at the end of its chunk;
  *                           written by gdp_recompute_w_u, read by gdp_chunk_h
  *   w      [B, T*M, HV, K]  out of gdp_recompute_w_u (effective keys)
- *   u      [B, T*M, HV, V]  out of gdp_recompute_w_u (effective values)
- *   v_new  [B, T*M, HV, V]  out of gdp_chunk_h (corrected values)
+ *   u      [B, HV, V/16, T*M, 16]  out of gdp_recompute_w_u (effective
+ *                           values), in 16-column slices: element (b, e, hv,
+ *                           c) at ((b*HV + hv)*(V/16) + c/16)*T*M*16 + e*16 +
+ *                           c%16, so the rows of one slice are contiguous
+ *   v_new  [B, HV, V/16, T*M, 16]  out of gdp_chunk_h (corrected values),
+ *                           sliced like u
  *   h      [h_chunks, HV, V, K]  out of gdp_chunk_h: the V x K state S
  *                           entering each chunk (S maps a normalised key to a
  *                           value); chunk c of sequence i is at index

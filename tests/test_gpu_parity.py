@@ -82,14 +82,16 @@ def check_chunk(q, k, v, beta, g, seqs, hv_list, M, scale=None, cu=None, cu_host
     # the final state is fp32 on both sides: judged raw
     accs = {n: Acc(n, raw_max_abs=(n in ("o", "ht"))) for n in names}
     bf = dt == torch.bfloat16
+    vn_rows = G.slices_to_rows(buf.v_new)
+    u_rows = G.slices_to_rows(buf.u) if want_wu else None
     for (si, (b, t0, t1, hbase), hv), r in zip(items, refs):
         nc = math.ceil((t1 - t0) * M / 64)
         accs["o"].add(f32(buf.o[b, t0:t1, hv]), r["o"], bf)
-        accs["v_new"].add(f32(buf.v_new[b, t0 * M:t1 * M, hv]), r["v_new"], bf)
+        accs["v_new"].add(f32(vn_rows[b, t0 * M:t1 * M, hv]), r["v_new"], bf)
         accs["h"].add(f32(buf.h[hbase:hbase + nc, hv]), r["h"], bf)
         if want_wu:
             accs["w"].add(f32(buf.w[b, t0 * M:t1 * M, hv]), r["w"], bf)
-            accs["u"].add(f32(buf.u[b, t0 * M:t1 * M, hv]), r["u"], bf)
+            accs["u"].add(f32(u_rows[b, t0 * M:t1 * M, hv]), r["u"], bf)
         if h0 is not None:
             accs["ht"].add(f32(buf.ht[si, hv]), r["h_final"], False)
     for a in accs.values():
@@ -214,7 +216,7 @@ def test_chunk_o_alone_on_oracle_state():
     buf.recompute_w_u()  # k_rnorm
     sc = 1.0 / math.sqrt(K)
     h_ref = torch.empty_like(buf.h, device="cpu")
-    vn_ref = torch.empty_like(buf.v_new, device="cpu")
+    vn_ref = torch.empty((B_, T * M, HV, V), dtype=torch.bfloat16)
     refs = []
     for hv in range(HV):
         hk = hv // (HV // H)
@@ -223,7 +225,7 @@ def test_chunk_o_alone_on_oracle_state():
         h_ref[:, hv] = torch.from_numpy(r["h"]).to(torch.bfloat16)
         vn_ref[0, :, hv] = torch.from_numpy(r["v_new"]).to(torch.bfloat16)
         refs.append(r)
-    buf.set(h=h_ref.to(DEV), v_new=vn_ref.to(DEV))
+    buf.set(h=h_ref.to(DEV), v_new=G.rows_to_slices(vn_ref).to(DEV))
     buf.chunk_o()
     torch.cuda.synchronize()
     acc = Acc("o", raw_max_abs=True)
@@ -436,7 +438,7 @@ def test_state_chaining_is_exact():
     torch.cuda.synchronize()
     nc = s * M // 64
     assert torch.equal(full.o, torch.cat([a.o, b.o], 1))
-    assert torch.equal(full.v_new, torch.cat([a.v_new, b.v_new], 1))
+    assert torch.equal(full.v_new, torch.cat([a.v_new, b.v_new], 3))  # slice-major: rows are dim 3
     assert torch.equal(full.h, torch.cat([a.h, b.h], 0)) and a.h.shape[0] == nc
     assert torch.equal(full.ht, b.ht)
 
