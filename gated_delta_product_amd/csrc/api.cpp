@@ -139,7 +139,9 @@ static hipError_t pipe_ctx(int dev, size_t nev, PipeCtx *&out) {
         }
     while (c.ev.size() < nev) {
         hipEvent_t ev;
-        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        // every consumer is on this device: a device-scope release suffices,
+        // and skips the system-scope cache writeback of a default event
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventReleaseToDevice);
         if (e != hipSuccess) return e;
         c.ev.push_back(ev);
     }
