@@ -47,6 +47,14 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class PrepareArgs(ctypes.Structure):
+    """Mirror of gdp_prepare_args (include/gdp.h)."""
+    _fields_ = [
+        ("x", _vp), ("x_n_stride", _i64), ("x_t_stride", _i64), ("ba", _vp), ("ba_n_stride", _i64),
+        ("ba_t_stride", _i64), ("A_log", _vp), ("dt_bias", _vp), ("G", _i32),
+    ]
+
+
 class GdpError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__("gdp status %d: %s" % (status, msg))
@@ -78,6 +86,9 @@ def lib():
         L.gdp_decode_update.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
         L.gdp_chunk_fwd_pipelined.restype = ctypes.c_int
         L.gdp_chunk_fwd_pipelined.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _vp, _vp]
+        L.gdp_prefill_fwd_pipelined.restype = ctypes.c_int
+        L.gdp_prefill_fwd_pipelined.argtypes = [ctypes.POINTER(PrepareArgs), ctypes.POINTER(ChunkArgs), _i32, _vp,
+                                                _vp, _vp]
         L.gdp_pipeline_segments.restype = _i32
         L.gdp_pipeline_segments.argtypes = [_i64, _i32]
         L.gdp_num_state_chunks.restype = _i64
@@ -285,12 +296,34 @@ class ChunkBuffers:
         self._call(lib().gdp_chunk_fwd, stream)
         return self.o
 
+    def prefill_pipelined(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, chunk_h_events=None):
+        """gdp_prefill_fwd_pipelined: prepare x / ba into this buffer's q, k,
+        v, beta, g (allocated with the prepare shapes) and run the pipelined
+        chunk forward, each segment's prepare overlapped with the serial
+        stage.  Arguments as prefill_prepare and forward_pipelined."""
+        _need_cuda(x, ba, A_log, dt_bias)
+        d = self.dims
+        if x.dim() != 3 or x.stride(2) != 1 or ba.dim() != 3 or ba.stride(2) != 1:
+            raise ValueError("x and ba must be 3-D with a contiguous last dimension")
+        if x.shape[:2] != (d["B"], d["T"]) or ba.shape[:2] != (d["B"], d["T"]) or x.dtype != self.q.dtype:
+            raise ValueError("x / ba do not match the buffers")
+        pa = PrepareArgs(x=x.data_ptr(), x_n_stride=x.stride(0), x_t_stride=x.stride(1), ba=ba.data_ptr(),
+                         ba_n_stride=ba.stride(0), ba_t_stride=ba.stride(1), A_log=A_log.data_ptr(),
+                         dt_bias=dt_bias.data_ptr(), G=int(num_groups))
+        return self._pipelined(lambda ws, ev, s: lib().gdp_prefill_fwd_pipelined(
+            ctypes.byref(pa), ctypes.byref(self.args), int(num_segments), ws, ev, s), num_segments, stream,
+            chunk_h_events)
+
     def forward_pipelined(self, num_segments, stream=None, chunk_h_events=None):
         """gdp_chunk_fwd_pipelined: the same results for B == 1 without
         cu_seqlens, with the parallel stages of neighbouring segments
         overlapping the serial one.  chunk_h_events: optional list of
         2 * pipeline_segments(T, num_segments) torch.cuda.Event (timing
         enabled, recorded at least once) marking each segment's chunk_h."""
+        return self._pipelined(lambda ws, ev, s: lib().gdp_chunk_fwd_pipelined(
+            ctypes.byref(self.args), int(num_segments), ws, ev, s), num_segments, stream, chunk_h_events)
+
+    def _pipelined(self, call, num_segments, stream, chunk_h_events):
         d = self.dims
         if getattr(self, "_ws", None) is None:
             self._ws = torch.empty((2, d["HV"], d["V"], d["K"]), dtype=torch.float32, device=self.device)
@@ -301,8 +334,7 @@ class ChunkBuffers:
                 raise ValueError("need %d events" % (2 * n))
             ev = (_vp * (2 * n))(*[e.cuda_event for e in chunk_h_events])
         s = stream if stream is not None else _stream(self.device)
-        _check(lib().gdp_chunk_fwd_pipelined(ctypes.byref(self.args), int(num_segments), self._ws.data_ptr(),
-                                             ev, s))
+        _check(call(self._ws.data_ptr(), ev, s))
         return self.o
 
 

@@ -153,11 +153,14 @@ static hipError_t pipe_ctx(int dev, size_t nev, PipeCtx *&out) {
 
 extern "C" {
 
-static gdp_status prepare_common(const char *name, bool decode, const void *x, int64_t x_n_stride,
-                                 int64_t x_t_stride, const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
-                                 const float *A_log, const float *dt_bias, int64_t n, int64_t T, int32_t M,
-                                 int32_t H, int32_t G, int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k,
-                                 void *v, float *beta, float *g, void *stream) {
+// Validates the arguments of a prepare call; on GDP_OK, *out holds the launch
+// parameters (out->n == 0 or out->T == 0: nothing to launch).
+static gdp_status prepare_check(const char *name, bool decode, const void *x, int64_t x_n_stride,
+                                int64_t x_t_stride, const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
+                                const float *A_log, const float *dt_bias, int64_t n, int64_t T, int32_t M,
+                                int32_t H, int32_t G, int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k,
+                                void *v, float *beta, float *g, gdp::PrepareParams *out) {
+    *out = gdp::PrepareParams{};
     if (dtype != GDP_F32 && dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "%s: unknown dtype %d", name, (int)dtype);
     if (n < 0 || T < 0) return fail(GDP_ERR_INVALID, "%s: n and T must be >= 0", name);
     if (M < 1 || H < 1 || G < 1 || P < 1 || N < 1) return fail(GDP_ERR_INVALID, "%s: M, H, G, P, N must be >= 1", name);
@@ -167,7 +170,7 @@ static gdp_status prepare_common(const char *name, bool decode, const void *x, i
     if (width * M > 0x7fffffff) return fail(GDP_ERR_UNSUPPORTED, "%s: rows too wide", name);
     if (x_t_stride < 0 || x_n_stride < 0 || ba_t_stride < 0 || ba_n_stride < 0)
         return fail(GDP_ERR_INVALID, "%s: strides must be >= 0", name);
-    if (n == 0 || T == 0) return ok();
+    if (n == 0 || T == 0) return ok();  // *out stays empty
     if (!x || !ba || !A_log || !dt_bias || !q || !k || !v || !beta || !g)
         return fail(GDP_ERR_INVALID, "%s: a tensor pointer is NULL", name);
     if (T > 1 && x_t_stride < width) return fail(GDP_ERR_INVALID, "%s: x rows overlap (t stride %lld < width %lld)",
@@ -177,8 +180,20 @@ static gdp_status prepare_common(const char *name, bool decode, const void *x, i
     const bool vec16 = aligned16(x) && aligned16(q) && aligned16(k) && aligned16(v) &&
                        ((x_t_stride * es) % 16 == 0) && ((x_n_stride * es) % 16 == 0) &&
                        ((P * es) % 16 == 0) && ((N * es) % 16 == 0);
-    gdp::PrepareParams p{x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride, A_log, dt_bias, n, T,
-                         M, H, G, P, N, dtype, decode, vec16, q, k, v, beta, g};
+    *out = gdp::PrepareParams{x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride, A_log, dt_bias, n, T,
+                              M, H, G, P, N, dtype, decode, vec16, q, k, v, beta, g};
+    return ok();
+}
+
+static gdp_status prepare_common(const char *name, bool decode, const void *x, int64_t x_n_stride,
+                                 int64_t x_t_stride, const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
+                                 const float *A_log, const float *dt_bias, int64_t n, int64_t T, int32_t M,
+                                 int32_t H, int32_t G, int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k,
+                                 void *v, float *beta, float *g, void *stream) {
+    gdp::PrepareParams p;
+    const gdp_status st = prepare_check(name, decode, x, x_n_stride, x_t_stride, ba, ba_n_stride, ba_t_stride,
+                                        A_log, dt_bias, n, T, M, H, G, P, N, dtype, q, k, v, beta, g, &p);
+    if (st != GDP_OK || p.n == 0 || p.T == 0) return st;
     return hip_status(gdp::launch_prepare(p, (hipStream_t)stream), name);
 }
 
@@ -265,8 +280,10 @@ int32_t gdp_pipeline_segments(int64_t T, int32_t num_segments) {
     return (int32_t)cdiv(T, Ls);
 }
 
-gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,
-                                   void *const *chunk_h_events, void *stream) {
+// The pipelined chunk forward; with prep, each segment's prepare runs on the
+// WY side stream right before that segment's WY.
+static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PrepareParams *prep, int32_t num_segments,
+                                 float *state_workspace, void *const *chunk_h_events, void *stream) {
     gdp::ChunkParams p;
     gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
     if (st != GDP_OK) return st;
@@ -328,6 +345,19 @@ gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments
         if ((st = check_chunk(&sa, ST_WY | ST_H | ST_O, &sp)) != GDP_OK) return st;
         sp.uv_ss = a->T * a->M * 16;  // slices keep the whole sequence's stride
         hipEvent_t ev_w = ctx->ev[2 + 2 * sidx], ev_h = ctx->ev[3 + 2 * sidx];
+        if (prep) {  // tokens [t0, t0 + Tn) of the one sequence
+            gdp::PrepareParams pp = *prep;
+            const int64_t pes = (int64_t)dsize(prep->dtype);
+            pp.x = (const char *)prep->x + t0 * prep->x_t_stride * pes;
+            pp.ba = (const char *)prep->ba + t0 * prep->ba_t_stride * pes;
+            pp.T = Tn;
+            pp.q = (char *)prep->q + t0 * prep->H * prep->N * pes;
+            pp.k = (char *)prep->k + t0 * prep->M * prep->H * prep->N * pes;
+            pp.v = (char *)prep->v + t0 * prep->M * prep->H * prep->P * pes;
+            pp.beta = prep->beta + t0 * prep->M * prep->H;
+            pp.g = prep->g + t0 * prep->H;
+            GDP_TRY(gdp::launch_prepare(pp, sw), "gdp_prefill_fwd_pipelined: prepare launch");
+        }
         GDP_TRY(gdp::launch_wy(sp, sw), "gdp_chunk_fwd_pipelined: recompute_w_u launch");
         GDP_TRY(hipEventRecord(ev_w, sw), "hipEventRecord");
         GDP_TRY(hipStreamWaitEvent(s0, ev_w, 0), "hipStreamWaitEvent");
@@ -342,6 +372,27 @@ gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments
     GDP_TRY(hipStreamWaitEvent(s0, ev_end, 0), "hipStreamWaitEvent");
 #undef GDP_TRY
     return ok();
+}
+
+gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,
+                                   void *const *chunk_h_events, void *stream) {
+    return pipelined_impl(a, nullptr, num_segments, state_workspace, chunk_h_events, stream);
+}
+
+gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *pa, const gdp_chunk_args *a, int32_t num_segments,
+                                     float *state_workspace, void *const *chunk_h_events, void *stream) {
+    if (!pa || !a) return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_pipelined: args is NULL");
+    if (a->HV != a->H)
+        return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_pipelined: prepare makes H value heads (HV=%d, H=%d)", a->HV,
+                    a->H);
+    if (!a->g && a->T > 0) return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_pipelined: g is NULL (prepare writes it)");
+    gdp::PrepareParams pp;
+    const gdp_status st = prepare_check("gdp_prefill_fwd_pipelined", false, pa->x, pa->x_n_stride, pa->x_t_stride,
+                                        pa->ba, pa->ba_n_stride, pa->ba_t_stride, pa->A_log, pa->dt_bias, a->B,
+                                        a->T, a->M, a->H, pa->G, a->V, a->K, a->dtype, (void *)a->q, (void *)a->k,
+                                        (void *)a->v, (float *)a->beta, (float *)a->g, &pp);
+    if (st != GDP_OK) return st;
+    return pipelined_impl(a, pp.T > 0 ? &pp : nullptr, num_segments, state_workspace, chunk_h_events, stream);
 }
 
 int64_t gdp_num_state_chunks(const int32_t *cu_seqlens_host, int64_t num_seqs, int64_t B, int64_t T, int32_t M,

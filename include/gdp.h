@@ -18,6 +18,8 @@
  *   gdp_chunk_fwd        the three chunk stages in order
  *   gdp_chunk_fwd_pipelined  the same for one long sequence, in segments
  *                        whose parallel stages overlap the serial one
+ *   gdp_prefill_fwd_pipelined  prepare plus the pipelined chunk forward,
+ *                        with each segment's prepare overlapped too
  *   gdp_decode_prepare   the prepare of a decode step: query and decay
  *                        interleaved onto the Householder copies
  *                        (core.ssm.ops.gdp.prepare, gdp_decode_prepare)
@@ -295,6 +297,38 @@ gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
  */
 gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,
                                    void *const *chunk_h_events, void *stream);
+
+/*
+ * Arguments of gdp_prefill_prepare that gdp_prefill_fwd_pipelined needs
+ * besides the chunk arguments (whose B = n, T, M, H, V = P, K = N and dtype
+ * it shares).
+ */
+typedef struct gdp_prepare_args {
+    const void *x;
+    int64_t x_n_stride;
+    int64_t x_t_stride;
+    const void *ba;
+    int64_t ba_n_stride;
+    int64_t ba_t_stride;
+    const float *A_log;
+    const float *dt_bias;
+    int32_t G;
+} gdp_prepare_args;
+
+/*
+ * gdp_prefill_fwd_pipelined -- gdp_prefill_prepare followed by
+ * gdp_chunk_fwd_pipelined, with the prepare of each segment run on the WY
+ * side stream just before that segment's WY, so that only the first
+ * segment's prepare precedes the serial stage.  Prepare writes the chunk
+ * arguments' q, k, v, beta and g (which must therefore be writable, g not
+ * NULL, and HV == H: prepare makes H value heads).  Results are
+ * bit-identical to the two calls in sequence; the requirements and the
+ * per-segment layout of k_rnorm, gcum and kdecay are those of
+ * gdp_chunk_fwd_pipelined, the prepare arguments are checked as by
+ * gdp_prefill_prepare.
+ */
+gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_args *a, int32_t num_segments,
+                                     float *state_workspace, void *const *chunk_h_events, void *stream);
 
 /* Segments gdp_chunk_fwd_pipelined actually runs for T tokens (whole
    64-token chunks, at most num_segments); 0 for T == 0, -1 on bad

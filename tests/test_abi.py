@@ -41,7 +41,16 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
-@pytest.mark.parametrize("cls,cname", [(B.ChunkArgs, "gdp_chunk_args"), (B.DecodeArgs, "gdp_decode_args")])
+def test_every_entry_point_has_ctypes_signature():
+    """Each declared function has argtypes in the binding, so no pointer or
+    64-bit argument is passed as a default 32-bit int."""
+    L = B.lib()
+    for n in _declared():
+        assert getattr(L, n).argtypes is not None, n
+
+
+@pytest.mark.parametrize("cls,cname", [(B.ChunkArgs, "gdp_chunk_args"), (B.DecodeArgs, "gdp_decode_args"),
+                                      (B.PrepareArgs, "gdp_prepare_args")])
 def test_struct_layout_matches_c(tmp_path, cls, cname):
     fields = [f for f, _ in cls._fields_]
     prog = '#include <stdio.h>\n#include <stddef.h>\n#include "gdp.h"\nint main(void){\n'
@@ -127,6 +136,26 @@ def test_pipelined_rejects_and_segments():
     assert B.pipeline_segments(100, 8) == 2       # 2 chunks
     assert B.pipeline_segments(0, 8) == 0
     assert L.gdp_pipeline_segments(10, 0) == -1
+
+
+def test_prefill_pipelined_rejects():
+    L = B.lib()
+    ws = ctypes.c_void_p(0x100000)
+    pa = B.PrepareArgs(x=0x200000, x_n_stride=0, x_t_stride=2 * 64 * 2 + 2 * 1 * 64 + 1 * 64, ba=0x300000,
+                       ba_n_stride=0, ba_t_stride=3 * 2, A_log=0x400000, dt_bias=0x500000, G=1)
+    # prepare makes H value heads: HV != H is refused before anything runs
+    assert L.gdp_prefill_fwd_pipelined(ctypes.byref(pa), ctypes.byref(_args(H=2, HV=4)), 2, ws, None,
+                                       None) == B.GDP_ERR_INVALID
+    # g is written by prepare, so it must be given
+    assert L.gdp_prefill_fwd_pipelined(ctypes.byref(pa), ctypes.byref(_args(g=None)), 2, ws, None,
+                                       None) == B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_pipelined(None, ctypes.byref(_args()), 2, ws, None, None) == B.GDP_ERR_INVALID
+    # prepare's own checks: H % G
+    bad = B.PrepareArgs(x=0x200000, x_n_stride=0, x_t_stride=4096, ba=0x300000, ba_n_stride=0, ba_t_stride=64,
+                        A_log=0x400000, dt_bias=0x500000, G=3)
+    assert L.gdp_prefill_fwd_pipelined(ctypes.byref(bad), ctypes.byref(_args()), 2, ws, None,
+                                       None) == B.GDP_ERR_INVALID
+    assert b"G=3" in L.gdp_last_error()
 
 
 def test_null_args_rejected():

@@ -470,6 +470,30 @@ def test_pipelined_forward_is_bit_identical():
             assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0 for i in range(n))
 
 
+def test_prefill_pipelined_is_bit_identical():
+    """gdp_prefill_fwd_pipelined (each segment's prepare on the WY side stream)
+    gives exactly the outputs of gdp_prefill_prepare then gdp_chunk_fwd, for
+    several segment counts and a ragged last chunk."""
+    T, M, H, G_, P, N = 1000, 2, 4, 2, 128, 128
+    d = synth.prepare_draws(1, T, M, H, G_, P, N, "bf16", synth.seed_of(4) + 90)
+    x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
+    pre = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, G_, P, N)
+    h0 = synth.initial_state_draws(1, H, P, N, synth.seed_of(4) + 91).to(DEV)
+    ref = G.ChunkBuffers(*pre, initial_state=h0, output_final_state=True)
+    ref.forward()
+    torch.cuda.synchronize()
+    for nseg in (1, 3, 5):
+        log("prefill pipelined, %d segments" % nseg)
+        outs = [torch.full_like(t, 7) for t in pre]  # prepare must overwrite all of them
+        pip = G.ChunkBuffers(*outs, initial_state=h0, output_final_state=True)
+        pip.prefill_pipelined(x, ba, A_log, dt_bias, G_, nseg)
+        torch.cuda.synchronize()
+        for a, b, nm in zip(outs, pre, ("q", "k", "v", "beta", "g")):
+            assert torch.equal(a, b), nm
+        for nm in ("o", "w", "u", "v_new", "h", "ht"):
+            assert torch.equal(getattr(pip, nm), getattr(ref, nm)), nm
+
+
 # ---------------------------------------------------------------------- decode
 
 def test_decode_prepare_matches_oracle():
