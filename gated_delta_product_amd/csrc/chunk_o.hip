@@ -48,12 +48,16 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     constexpr int SRB = KD * ES;           // bytes per state row
     constexpr int SUPR = SRB / 16;         // 16-byte units per state row
     constexpr int VRB = VB * ES;           // bytes per V slab row (as o stores it)
-    constexpr int VSB = C * 16 * ES;       // bytes per 16-column slice of the V slab
+    constexpr int CSB = C * 16 * ES;       // bytes of one copy in a 16-column slice of the V slab
     constexpr int NSD = VB * SRB / 1024;   // DMA instructions for the state slab
-    constexpr int NVD = C * VRB / 1024;    // DMA instructions for a V slab
-    static_assert(NSD % 4 == 0 && NVD % 4 == 0 && SUPR >= 8 && VSB % 1024 == 0, "tile shape");
+    constexpr int NVD = C * VRB / 1024;    // DMA instructions per copy of the V slab
+    static_assert(NSD % 4 == 0 && NVD % 4 == 0 && SUPR >= 8 && CSB % 1024 == 0, "tile shape");
     __shared__ __attribute__((aligned(16))) T Ss[VB * KD];   // state slab, swizzled rows
-    __shared__ __attribute__((aligned(16))) T Vs[C * VB];    // V_j slab: VB/16 slices of 64 rows x 16
+    // the V slab of all M copies: VB/16 slices of 64 M rows x 16, rows in
+    // v_new's order (token r, copy j at row r M + j); M * C * VB elements of
+    // dynamic LDS
+    extern __shared__ __attribute__((aligned(16))) char v_dyn[];
+    T *Vs = (T *)v_dyn;
     __shared__ float sG[4][C], sRk[4][C];                    // per-wave scratch
 
     const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, blockIdx.x);
@@ -71,10 +75,12 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
     // swizzled byte offsets of the state slab: rows XOR their 16-byte unit
     // with the row.  The V slab is slice-major like v_new (row r of slice vt
-    // at vt * VSB + r * 16 * ES): a transposed read of four consecutive rows
-    // of one slice is 16 * 4 * ES contiguous bytes, free of bank conflicts.
+    // at vt * M * CSB + (r M + j) * 16 * ES for token r, copy j): the four
+    // rows of a transposed read sit M * 16 * ES bytes apart, in distinct
+    // bank groups.
     auto s_off = [](int r, int unit) { return r * SRB + ((unit ^ (r & (SUPR - 1))) << 4); };
-    auto v_at = [](int vt, int r) { return vt * VSB + r * 16 * ES; };
+    const int vsb = M * CSB;  // bytes per slice of the slab
+    auto v_at = [&](int vt, int r, int j) { return vt * vsb + (r * M + j) * 16 * ES; };
 
     // ---- state slab (rows vb0 .. vb0 + VB of S) -> LDS; the snapshot is
     // zero-filled past h_chunks by the range check
@@ -90,25 +96,24 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
         }
     }
     const int64_t ldkv_k = (int64_t)M * H * KD;  // key row stride per token
-    // V_j slab: rows (t0 + r) M + j of the VB/16 slices of v_new from column
-    // vb0; one DMA instruction fills RPI rows of one slice, whose rows sit
-    // M * 16 elements apart; rows past the chunk are zero-filled
+    // V slab: rows t0 M .. (t0 + nt) M of the VB/16 slices of v_new from
+    // column vb0, all copies at once, so every 128-byte line is read whole;
+    // one DMA instruction fills RPI consecutive rows of one slice; rows past
+    // the chunk are zero-filled
     const int64_t bseq = cu ? 0 : loc.seq;  // batch row of the sequence
-    auto stage_v = [&](int j) {
-        constexpr int IPS = VSB / 1024;        // DMA instructions per slice
+    {
         constexpr int RPI = 1024 / (16 * ES);  // rows per instruction
         constexpr int UPRV = 16 * ES / 16;     // 16-byte units per slice row
-        const T *vbase = v_new + uv_index(bseq, (t0 - bseq * Ttok) * M + j, hv, vb0, HV, VD, uv_ss);
+        const int ips = M * (CSB / 1024);      // DMA instructions per slice
+        const T *vbase = v_new + uv_index(bseq, (t0 - bseq * Ttok) * M, hv, vb0, HV, VD, uv_ss);
         const uint32_t base = lds_addr(Vs);
-#pragma unroll
-        for (int i = 0; i < NVD / 4; ++i) {
-            const int blk = wv * (NVD / 4) + i;
-            const int slc = blk / IPS, r = (blk % IPS) * RPI + lane / UPRV, u = lane % UPRV;
-            const rsrc_t rv = make_rsrc(vbase + slc * uv_ss, span(nt, M * 16 * ES, 16 * ES));
-            dma16(rv, (uint32_t)(r * M * 16 * ES + u * 16), base + blk * 1024);
+        for (int i = 0; i < M * (NVD / 4); ++i) {
+            const int blk = wv * M * (NVD / 4) + i;
+            const int slc = blk / ips, r = (blk % ips) * RPI + lane / UPRV, u = lane % UPRV;
+            const rsrc_t rv = make_rsrc(vbase + slc * uv_ss, (uint32_t)(nt * M * 16 * ES));
+            dma16(rv, (uint32_t)(r * 16 * ES + u * 16), base + blk * 1024);
         }
-    };
-    stage_v(0);
+    }
 
     // ---- register operands: this lane's query row (B operand of both
     // products), its keys per copy, the decays and key norms
@@ -165,7 +170,7 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     const float Gt = sG[wv][t_loc];
 
     wait_vmcnt<0>();
-    __syncthreads();  // state slab and V_0 landed
+    __syncthreads();  // state slab and V slab landed
 
     // ---- inter-chunk term: O^T[vt] = S[16vt.., :] Q^T[:, t]
     f32x4 acc[NVT];
@@ -235,26 +240,21 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
                         const int ra = 32 * ks + 4 * lg + (jj >> 2), rb = ra + 16;
                         const int cb = 4 * (jj & 3) * ES;  // byte of the column inside the slice row
                         x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_at(vt, ra) + cb))));
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_at(vt, ra, j) + cb))));
                         x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_at(vt, rb) + cb))));
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(vb + v_at(vt, rb, j) + cb))));
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            x0[i] = *(const float *)(vb + v_at(vt, 32 * ks + 4 * lg + i) + lc * ES);
-                            x1[i] = *(const float *)(vb + v_at(vt, 32 * ks + 16 + 4 * lg + i) + lc * ES);
+                            x0[i] = *(const float *)(vb + v_at(vt, 32 * ks + 4 * lg + i, j) + lc * ES);
+                            x1[i] = *(const float *)(vb + v_at(vt, 32 * ks + 16 + 4 * lg + i, j) + lc * ES);
                         }
                     }
                     acc[vt] = mma(join<T>(x0, x1), pb[ks], acc[vt]);
                 }
             }
         }
-        if (j + 1 < M) {
-            __syncthreads();  // every wave is done with V_j
-            stage_v(j + 1);
-            wait_vmcnt<0>();
-            __syncthreads();
-        }
+
     }
 
     // ---- store: lane holds o[t_loc][vb0 + 16vt + 4lg + i]
@@ -276,7 +276,8 @@ template <typename T, int KD, int VB>
 static hipError_t launch_chunk_o_t(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
     dim3 grid((unsigned)p.max_tok_chunks, (unsigned)a.HV, (unsigned)(a.V / VB));
-    hipLaunchKernelGGL((gdp_chunk_o_k<T, KD, VB>), grid, dim3(256), 0, stream,
+    const size_t vdyn = (size_t)a.M * 64 * VB * sizeof(T);  // the V slab of all copies (<= 64 KiB)
+    hipLaunchKernelGGL((gdp_chunk_o_k<T, KD, VB>), grid, dim3(256), vdyn, stream,
                        (const T *)a.q, (const T *)a.k, a.k_rnorm, (const T *)a.v_new, (const T *)a.h, a.g,
                        a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.V, a.h_chunks, a.scale, (T *)a.o, p.uv_ss);
     return hipGetLastError();
@@ -295,7 +296,9 @@ static hipError_t launch_chunk_o_bf16(const ChunkParams &p, hipStream_t stream) 
 static hipError_t launch_chunk_o_f32(const ChunkParams &p, hipStream_t stream) {
     const int K = p.a.K, V = p.a.V;
     if (K == 64 && V == 64) return launch_chunk_o_t<float, 64, 64>(p, stream);
-    if (K == 64 && V == 128) return launch_chunk_o_t<float, 64, 128>(p, stream);
+    // the V slab of all M copies stays within 64 KiB of dynamic LDS
+    if (K == 64 && V == 128) return p.a.M <= 2 ? launch_chunk_o_t<float, 64, 128>(p, stream)
+                                               : launch_chunk_o_t<float, 64, 64>(p, stream);
     return hipErrorInvalidValue;
 }
 

@@ -115,6 +115,18 @@ def test_chunk_tiny_f32():
                 c["M"], tag="tiny_f32")
 
 
+@pytest.mark.parametrize("M", [2, 4])
+def test_chunk_f32_wide_value_many_copies(M):
+    """float32, K=64, V=128 with M = 2 (one 128-column output slab) and M = 4
+    (two 64-column slabs, so the V slab of all copies fits the output stage's
+    LDS), ragged T: every output, every head."""
+    B_, T, H, HV, K, V = 1, 100, 2, 2, 64, 128
+    d = synth.chunk_draws(B_, T, H, HV, K, V, M, "f32", synth.seed_of(1) + M)
+    beta, g = gates(d)
+    beta = beta.reshape(B_, T * M, HV)
+    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(B_, T, M), range(HV), M, tag="f32 V=128 M=%d" % M)
+
+
 def test_chunk_householder_m2():
     """B=2, T=1024, H=HV=8, K=V=128, M=2, bf16: every output, every head."""
     c = synth.CONFIGS[2]
