@@ -68,7 +68,16 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     const int lg = lane >> 4, lc = lane & 15;
     const int64_t bi = cu ? 0 : loc.seq, TM = Ttok * M;  // head-major per-row outputs
 
-    // ---- V into registers now (it is needed last), K into LDS with row norms
+    // ---- every global load of the block goes out first: the gates (wave
+    // 0), V into registers (it is needed last), then K into LDS with row
+    // norms, so their latencies overlap
+    const int64_t e_row = r0 + lane;
+    const bool e_in = lane < n;
+    float b_in = 0.f, gd_in = 0.f;
+    if (wv == 0) {
+        b_in = e_in ? beta[e_row * HV + hv] : 0.f;
+        gd_in = (g != nullptr && e_in && (e_row % M) == 0) ? g[(e_row / M) * HV + hv] : 0.f;  // NULL: ungated
+    }
     uint4 vreg[VPT];
     {
         const T *vsrc = v + (r0 * HV + hv) * (int64_t)VD;
@@ -81,14 +90,10 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
     stage_tile<T, C, KD, LDK, 256>(Ks, k + (r0 * H + hk) * (int64_t)KD, (int64_t)H * KD, n, s_rk);
     if (wv == 0) {
-        const int64_t e = r0 + lane;
-        const bool in = lane < n;
-        const float b = in ? beta[e * HV + hv] : 0.f;
-        const float lg_decay = (g != nullptr && in && (e % M) == 0) ? g[(e / M) * HV + hv] : 0.f;  // NULL: ungated
-        const float gam = wave_inclusive_sum(lg_decay);
-        s_beta[lane] = b;
+        const float gam = wave_inclusive_sum(gd_in);
+        s_beta[lane] = b_in;
         s_gam[lane] = gam;
-        if (in) gcum[hm_index(bi, HV, hv, TM, e)] = gam * 1.4426950408889634f;  // log2 units for chunk_h
+        if (e_in) gcum[hm_index(bi, HV, hv, TM, e_row)] = gam * 1.4426950408889634f;  // log2 units for chunk_h
     }
     __syncthreads();
 
