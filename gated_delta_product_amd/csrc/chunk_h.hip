@@ -25,8 +25,9 @@
 //   order (w with its K columns permuted to match h; K^T, transposed on the
 //   fly by ds_read_b64_tr_b16, with its rows permuted to match v_new).  They
 //   leave v_new (transposed) and the next state snapshot in LDS.
-// * Prefetch wave 4 pulls the lines of the chunk five ahead into L2 (each
-//   of a head's column blocks a share), so the memory waves hit L2.
+// * Prefetch wave 4 pulls the w and K lines of the chunk five ahead into L2
+//   (each of a head's column blocks a share), so the memory waves hit L2.
+//   The small contiguous u slice is left to the memory waves' own lead.
 // * Memory waves 2 and 3 stream w, K, u, kdecay and gcum from HBM straight
 //   into a three-stage LDS ring (buffer loads with the LDS destination, two
 //   chunks ahead; the range check zero-fills rows past the end), and write
@@ -149,17 +150,15 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         // data lands in a scratch LDS area that nothing reads.
         constexpr int PF = 5;                    // prefetch distance in chunks
         constexpr int RPB = C / S;               // rows per block per chunk
-        static_assert(RPB * KD * ES / 128 <= 64 && C * 16 * ES / 128 <= 64 && KD * ES >= 128,
+        static_assert(RPB * KD * ES / 128 <= 64 && KD * ES >= 128,
                       "one 4-byte load per line must cover a block's rows");
         const uint32_t pf = lds_addr(&Pf[0]);
         const int rbw = KD * ES;  // row bytes of w / k
         const char *pw = (const char *)(w + ((r0 + RPB * sl) * HV + hv) * KD);
         const char *pk = (const char *)(k + ((r0 + RPB * sl) * H + hk) * KD);
-        const char *pu = (const char *)(u + uv_index(cu ? 0 : seq, r0 - (cu ? 0 : seq) * Ttok * M, hv, 16 * sl, HV, VD, uv_ss));
         const char *pd = (const char *)(kdecay + h0r);
         const char *pg = (const char *)(gcum + h0r);
-        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, stu = (int64_t)C * 16 * ES,
-                      st4 = (int64_t)C * 4;
+        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, st4 = (int64_t)C * 4;
         // rows [0, nr) of a tile with `rb`-byte rows `ld` bytes apart: one
         // 4-byte load per 128-byte line is enough to bring it into L2
         auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb) {
@@ -174,8 +173,6 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             const int64_t oc = c;
             rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw);
             rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw);
-            // this block's u slice: n rows of 16 elements, contiguous
-            dma4(make_rsrc(pu + oc * stu, (uint32_t)(n * 16 * ES)), (uint32_t)(lane * 128), pf);
             if (sl == 0) {  // 256 contiguous bytes each: one block of the head is enough
                 dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
                 dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
