@@ -559,6 +559,7 @@ DECODE_CASES = [
     ("bf16", 4, 5, 1, 2, 2, 64, 64, 4, [2, 3, 1, 0], False),
     ("bf16", 2, 1, 4, 1, 2, 128, 256, 2, None, True),
     ("f32", 2, 7, 2, 2, 2, 128, 64, 9, [8, 4], True),
+    ("bf16", 1, 1024, 4, 1, 1, 64, 64, 1, None, True),   # the longest step: S*M = 4096 rows
 ]
 
 
