@@ -228,8 +228,8 @@ def main():
     # chunk_h: every segment launch, bracketed on its own stream
     seg_ms = [e[2 + 2 * j].elapsed_time(e[3 + 2 * j]) for e in evs for j in range(nseg)]
     prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    Ls = math.ceil(math.ceil(w["T"] / 64) / args.segments) * 64
-    seg_tokens = [min(Ls, w["T"] - j * Ls) for j in range(nseg)]
+    starts = G.pipeline_plan(w["T"], args.segments)
+    seg_tokens = [starts[j + 1] - starts[j] for j in range(nseg)]
     ch_bytes = sum(algorithmic_bytes(w, t)["gdp_chunk_h"] for t in seg_tokens) / nseg  # per launch
     ch_ms = sum(seg_ms) / len(seg_ms)
     ab = algorithmic_bytes(w)

@@ -91,6 +91,8 @@ def lib():
                                                 _vp, _vp]
         L.gdp_pipeline_segments.restype = _i32
         L.gdp_pipeline_segments.argtypes = [_i64, _i32]
+        L.gdp_pipeline_plan.restype = _i32
+        L.gdp_pipeline_plan.argtypes = [_i64, _i32, ctypes.POINTER(_i64)]
         L.gdp_num_state_chunks.restype = _i64
         L.gdp_num_state_chunks.argtypes = [ctypes.POINTER(_i32), _i64, _i64, _i64, _i32, _i32]
         L.gdp_last_error.restype = ctypes.c_char_p
@@ -189,6 +191,15 @@ def prefill_prepare(x, ba, A_log, dt_bias, num_householder, num_heads, num_group
 def pipeline_segments(T, num_segments):
     """Segments gdp_chunk_fwd_pipelined runs for T tokens."""
     return int(lib().gdp_pipeline_segments(int(T), int(num_segments)))
+
+
+def pipeline_plan(T, num_segments):
+    """Token offsets where those segments start, then T (a list of n + 1)."""
+    buf = (_i64 * (max(int(num_segments), 0) + 1))()
+    n = lib().gdp_pipeline_plan(int(T), int(num_segments), buf)
+    if n < 0:
+        raise GdpError(GDP_ERR_INVALID, "bad arguments to gdp_pipeline_plan")
+    return [int(buf[i]) for i in range(n + 1)]
 
 
 def num_state_chunks(T, M, B=1, cu_seqlens_host=None):

@@ -273,11 +273,35 @@ gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream) {
     return hip_status(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd: chunk_o launch");
 }
 
+// Segment plan of the pipelined forward: num_segments equal shares of the
+// 64-token chunks, each boundary rounded to a whole chunk, empty segments
+// dropped.  (Shorter first and last segments, whose recompute_w_u and chunk_o
+// overlap nothing, measured no faster: the step is bound by the memory
+// traffic of all stages together.)  Fills starts[0..n] (token offsets,
+// starts[n] = T) when starts is not NULL and returns n, the segment count.
+static int32_t segment_plan(int64_t T, int32_t num_segments, int64_t *starts) {
+    const int64_t nch = cdiv(T, 64);
+    int32_t n = 0;
+    int64_t prev = 0;
+    if (starts) starts[0] = 0;
+    for (int64_t i = 1; i <= num_segments; ++i) {
+        const int64_t end = (nch * i + num_segments / 2) / num_segments;  // in chunks, rounded
+        if (end <= prev) continue;
+        prev = end;
+        ++n;
+        if (starts) starts[n] = end * 64 < T ? end * 64 : T;
+    }
+    return n;
+}
+
 int32_t gdp_pipeline_segments(int64_t T, int32_t num_segments) {
     if (T < 0 || num_segments < 1) return -1;
-    if (T == 0) return 0;
-    const int64_t Ls = cdiv(cdiv(T, 64), num_segments) * 64;
-    return (int32_t)cdiv(T, Ls);
+    return segment_plan(T, num_segments, nullptr);
+}
+
+int32_t gdp_pipeline_plan(int64_t T, int32_t num_segments, int64_t *starts) {
+    if (T < 0 || num_segments < 1 || !starts) return -1;
+    return segment_plan(T, num_segments, starts);
 }
 
 // The pipelined chunk forward; with prep, each segment's prepare runs on the
@@ -293,10 +317,8 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
     if (a->T == 0) return ok();
     if (!state_workspace || !aligned16(state_workspace))
         return fail(GDP_ERR_INVALID, "state_workspace must be a 16-byte aligned device pointer");
-    const int64_t tok_chunks = cdiv(a->T, 64);
-    const int64_t seg_chunks = cdiv(tok_chunks, num_segments);
-    const int64_t Ls = seg_chunks * 64;  // tokens per segment (the last may be shorter)
-    const int64_t nseg = cdiv(a->T, Ls);
+    std::vector<int64_t> starts((size_t)num_segments + 1);
+    const int64_t nseg = segment_plan(a->T, num_segments, starts.data());
     const size_t es = dsize(a->dtype);
     const int64_t state_elems = (int64_t)a->HV * a->V * a->K;
     hipStream_t s0 = (hipStream_t)stream;
@@ -320,7 +342,7 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
     GDP_TRY(hipStreamWaitEvent(sw, ev_start, 0), "hipStreamWaitEvent");
     GDP_TRY(hipStreamWaitEvent(so, ev_start, 0), "hipStreamWaitEvent");
     for (int64_t sidx = 0; sidx < nseg; ++sidx) {
-        const int64_t t0 = sidx * Ls, Tn = (a->T - t0) < Ls ? (a->T - t0) : Ls;
+        const int64_t t0 = starts[sidx], Tn = starts[sidx + 1] - t0;
         const int64_t r0 = t0 * a->M;      // first expanded row
         const int64_t c0 = r0 / 64;        // first state chunk (t0 is a multiple of 64)
         gdp_chunk_args sa = *a;

@@ -17,6 +17,11 @@
 // inputs are the operands.  A is built in fp32: the four 16x16 diagonal
 // blocks by forward substitution (one lane per column), the off-diagonal
 // blocks level by level with fp32 MFMA:  A_ij = -A_ii sum_{j<=m<i} L_im A_mj.
+// L and A share one LDS array: A's diagonal blocks replace L's (dead once
+// solved) and its lower blocks are stored transposed in the upper triangle,
+// which L leaves unused; the lower blocks of L stay intact until the last
+// level.  With that array, the K tile and the gates the block takes about
+// 35 KB of LDS at K = V = 128 bf16, so four blocks share a CU.
 // u and w are computed transposed (u^T = V^T A1^T) so each lane ends up with
 // four consecutive columns of one output row, stored as one 8-byte write.
 #include "gdp_common.h"
@@ -45,17 +50,22 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
     constexpr int LDV = VD + Pad<T>::value;
-    constexpr int LV_BYTES = (C * LDA * 4 > C * LDV * (int)sizeof(T)) ? C * LDA * 4 : C * LDV * (int)sizeof(T);
+    constexpr int LA_BYTES = (C * LDA * 4 > C * LDV * (int)sizeof(T)) ? C * LDA * 4 : C * LDV * (int)sizeof(T);
     constexpr int VUPR = VD * (int)sizeof(T) / 16;   // 16-byte units per V row
     constexpr int VPT = C * VUPR / 256;               // V units per thread
     __shared__ __attribute__((aligned(16))) T Ks[C * LDK];
-    // L while A is being built, then the V tile (V waits in registers)
-    __shared__ __attribute__((aligned(16))) char LV[LV_BYTES];
-    __shared__ __attribute__((aligned(16))) float Am[C * LDA];
+    // L and A (fp32, row stride LDA) while A is being built, then the V
+    // tile (V waits in registers until then)
+    __shared__ __attribute__((aligned(16))) char LA[LA_BYTES];
     __shared__ __attribute__((aligned(16))) float s_beta[C], s_gam[C], s_rk[C], s_ws[C];
     __shared__ __attribute__((aligned(16))) float s_pf[64];  // landing area of L2 pulls
-    float *Lm = (float *)LV;
-    T *Vs = (T *)LV;
+    float *Lm = (float *)LA;
+    T *Vs = (T *)LA;
+    // A[r][c] for r, c in the same 16-row block or r > c: the diagonal
+    // blocks in place, the lower blocks transposed
+    auto a_at = [&](int r, int c) -> float & {
+        return (r >> 4) == (c >> 4) ? Lm[r * LDA + c] : Lm[c * LDA + r];
+    };
 
     const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, blockIdx.x);
     if (loc.seq < 0) return;
@@ -103,7 +113,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // landing in a scratch word array nothing reads.  Issued after this
     // block's own loads were consumed, so no wait here covers them.
     {
-        constexpr int64_t PFD = 256;
+        constexpr int64_t PFD = 512;
         const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x + PFD;
         if (lin < (int64_t)gridDim.x * gridDim.y) {
             const ChunkLoc pl = find_chunk(cu, nseq, Ttok, M, C, lin % gridDim.x);
@@ -154,9 +164,9 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         f32x4 rowf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) rowf[i] = b4[i] * r4[i];
-        for (int ct = 0; ct < 4; ++ct) {
+        for (int ct = 0; ct <= wv; ++ct) {  // upper blocks: A's transposed lower blocks go there
             f32x4 acc = zero4();
-            if (ct <= wv) {
+            {
 #pragma unroll
                 for (int ks = 0; ks < KD / 32; ++ks) {
                     FragT a = lds_row8<T>(Ks + (ra + lc) * LDK + 32 * ks + 8 * lg);
@@ -176,7 +186,8 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
     __syncthreads();
 
-    // ---- diagonal 16x16 blocks of A by forward substitution (lane = column)
+    // ---- diagonal 16x16 blocks of A by forward substitution (lane = column),
+    // in place of L's: every row of the block is read before any is written
     {
         const int d0 = 16 * wv;
         if (lane < 16) {
@@ -193,16 +204,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 x[i] = s;
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Am[(d0 + i) * LDA + d0 + lane] = x[i];
-        }
-        // zero the strictly-upper blocks of this block row (4 values per lane
-        // per 16x16 block)
-#pragma unroll
-        for (int cb = 1; cb < 4; ++cb) {
-            if (cb > wv) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) Am[(d0 + 4 * lg + q) * LDA + 16 * cb + lc] = 0.f;
-            }
+            for (int i = 0; i < 16; ++i) Lm[(d0 + i) * LDA + d0 + lane] = x[i];
         }
     }
     __syncthreads();
@@ -219,33 +221,27 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             for (int m = j; m < i; ++m) {
 #pragma unroll
                 for (int k0 = 0; k0 < 16; k0 += 4) {
-                    const float a = Lm[(16 * i + lc) * LDA + 16 * m + k0 + lg];
-                    const float b = Am[(16 * m + k0 + lg) * LDA + 16 * j + lc];
+                    const float a = Lm[(16 * i + lc) * LDA + 16 * m + k0 + lg];  // L_im, m < i
+                    const float b = a_at(16 * m + k0 + lg, 16 * j + lc);        // A_mj, m >= j
                     t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
                 }
             }
             f32x4 r = zero4();
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const float a = Am[(16 * i + lc) * LDA + 16 * i + 4 * lg + s];
+                const float a = Lm[(16 * i + lc) * LDA + 16 * i + 4 * lg + s];  // A_ii
                 r = __builtin_amdgcn_mfma_f32_16x16x4f32(a, t[s], r, 0, 0, 0);
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) Am[(16 * i + 4 * lg + q) * LDA + 16 * j + lc] = -r[q];
+            // A_ij, transposed: rows 16i + 4lg .. +3 of column 16j + lc
+            *(f32x4 *)&Lm[(16 * j + lc) * LDA + 16 * i + 4 * lg] = -r;
         }
         __syncthreads();
     }
 
-    // ---- L is dead: the V tile moves from registers into its space
-#pragma unroll
-    for (int it = 0; it < VPT; ++it) {
-        const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
-        *(uint4 *)(Vs + row * LDV + cu16 * (16 / (int)sizeof(T))) = vreg[it];
-    }
-    __syncthreads();
-
     // ---- u^T = V^T (A diag(beta))^T and w^T = Khat^T (A diag(beta e^gamma r))^T
-    //      wave wv produces output rows a in [16 wv, 16 wv + 16)
+    //      wave wv produces output rows a in [16 wv, 16 wv + 16).  The lane's
+    //      row of A goes to registers first (blocks past the diagonal are 0),
+    //      then the V tile takes the array's space.
     {
         const int a_row = 16 * wv + lc;  // output row this lane's B fragment covers
         const int nks = (wv >= 2) ? 2 : 1;  // contraction tiles with any b <= a
@@ -253,19 +249,31 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks < nks) {
-                const int b0 = 32 * ks + 8 * lg;
-                const f32x4 a0 = *(const f32x4 *)&Am[a_row * LDA + b0], a1 = *(const f32x4 *)&Am[a_row * LDA + b0 + 4];
+                const int b0 = 32 * ks + 8 * lg, bb = b0 >> 4;  // A[a_row][b0 .. b0 + 7], block bb
                 const f32x4 be0 = *(const f32x4 *)&s_beta[b0], be1 = *(const f32x4 *)&s_beta[b0 + 4];
                 const f32x4 ws0 = *(const f32x4 *)&s_ws[b0], ws1 = *(const f32x4 *)&s_ws[b0 + 4];
+                float av[8];
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const int addr = bb == wv ? a_row * LDA + b0 + m : (b0 + m) * LDA + a_row;
+                    av[m] = bb <= wv ? Lm[addr] : 0.f;
+                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    bu[ks][m] = from_f32<T>(a0[m] * be0[m]);
-                    bw[ks][m] = from_f32<T>(a0[m] * ws0[m]);
-                    bu[ks][4 + m] = from_f32<T>(a1[m] * be1[m]);
-                    bw[ks][4 + m] = from_f32<T>(a1[m] * ws1[m]);
+                    bu[ks][m] = from_f32<T>(av[m] * be0[m]);
+                    bw[ks][m] = from_f32<T>(av[m] * ws0[m]);
+                    bu[ks][4 + m] = from_f32<T>(av[4 + m] * be1[m]);
+                    bw[ks][4 + m] = from_f32<T>(av[4 + m] * ws1[m]);
                 }
             }
         }
+        __syncthreads();  // every row of A is in registers
+#pragma unroll
+        for (int it = 0; it < VPT; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
+            *(uint4 *)(Vs + row * LDV + cu16 * (16 / (int)sizeof(T))) = vreg[it];
+        }
+        __syncthreads();
         const bool row_ok = a_row < n;
         const int64_t grow = r0 + a_row;
 #pragma unroll
@@ -285,6 +293,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 *(typename Frag<T>::half *)(u + uv_index(bi, grow - bi * TM, hv, 16 * vt + 4 * lg, HV, VD, uv_ss)) = o4;
             }
         }
+        typename Frag<T>::half wq[KD / 16];  // w[a_row][16kt + 4lg .. +3]
 #pragma unroll
         for (int kt = 0; kt < KD / 16; ++kt) {
             f32x4 acc = zero4();
@@ -295,11 +304,23 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                     acc = mma(a, bw[ks], acc);
                 }
             }
-            if (row_ok) {
-                T *dst = w + (grow * HV + hv) * (int64_t)KD + 16 * kt + 4 * lg;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[q] = from_f32<T>(acc[q]);
-            }
+            for (int q = 0; q < 4; ++q) wq[kt][q] = from_f32<T>(acc[q]);
+        }
+        // w leaves through the K tile's space so that every store writes
+        // whole 128-byte lines (a lane's four columns are only 8 bytes)
+        __syncthreads();  // every wave is done reading K
+#pragma unroll
+        for (int kt = 0; kt < KD / 16; ++kt) *(typename Frag<T>::half *)(Ks + a_row * LDK + 16 * kt + 4 * lg) = wq[kt];
+        __syncthreads();
+        constexpr int WU = KD * (int)sizeof(T) / 16;  // 16-byte units per w row
+        T *wdst = w + (r0 * HV + hv) * (int64_t)KD;
+#pragma unroll
+        for (int it = 0; it < C * WU / 256; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / WU, c16 = uidx % WU;
+            if (row < n)
+                *(uint4 *)(wdst + (int64_t)row * HV * KD + c16 * (16 / (int)sizeof(T))) =
+                    *(const uint4 *)(Ks + row * LDK + c16 * (16 / (int)sizeof(T)));
         }
     }
     wait_vmcnt<0>();  // no load may still target LDS when the block retires

@@ -271,7 +271,8 @@ gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
 /*
  * gdp_chunk_fwd_pipelined -- the same results as gdp_chunk_fwd for one long
  * sequence (B == 1, cu_seqlens == NULL), computed in num_segments pieces of
- * whole 64-token chunks so that the parallel stages overlap the serial one:
+ * whole 64-token chunks (gdp_pipeline_plan gives where each starts) so that
+ * the parallel stages overlap the serial one:
  * chunk_h runs the segments in order on `stream`, handing the fp32 state
  * from one segment to the next (as h0 / ht), while gdp_recompute_w_u of the
  * next segments and gdp_chunk_o of the finished ones run on two streams of
@@ -334,6 +335,15 @@ gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_
    64-token chunks, at most num_segments); 0 for T == 0, -1 on bad
    arguments. */
 int32_t gdp_pipeline_segments(int64_t T, int32_t num_segments);
+
+/* Where those segments start: writes n + 1 token offsets to starts (host
+   memory, room for num_segments + 1), starts[0] = 0 and starts[n] = T, and
+   returns n = gdp_pipeline_segments(T, num_segments); -1 on bad arguments
+   (starts NULL included).  Segments hold equal shares of the 64-token
+   chunks (boundaries rounded to whole chunks, so every boundary is a
+   multiple of 64 tokens).  The per-segment blocks of k_rnorm, gcum and
+   kdecay start at these offsets. */
+int32_t gdp_pipeline_plan(int64_t T, int32_t num_segments, int64_t *starts);
 
 /*
  * Number of state chunks h must hold: sum over sequences of

@@ -31,7 +31,7 @@ def test_header_compiles_as_c99(tmp_path):
 def test_library_exports_every_declared_symbol():
     names = _declared()
     assert {"gdp_prefill_prepare", "gdp_decode_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o",
-            "gdp_chunk_fwd", "gdp_chunk_fwd_pipelined", "gdp_pipeline_segments", "gdp_decode_update",
+            "gdp_chunk_fwd", "gdp_chunk_fwd_pipelined", "gdp_pipeline_segments", "gdp_pipeline_plan", "gdp_decode_update",
             "gdp_num_state_chunks", "gdp_last_error", "gdp_version"} <= set(names)
     L = B.lib()
     for n in names:
@@ -132,10 +132,24 @@ def test_pipelined_rejects_and_segments():
     assert L.gdp_chunk_fwd_pipelined(ctypes.byref(_args(q=None)), 2, ws, None, None) == B.GDP_ERR_INVALID
     # segments of whole 64-token chunks, at most the number asked for
     assert B.pipeline_segments(32768, 8) == 8
-    assert B.pipeline_segments(1000, 3) == 3      # 16 chunks -> 6, 6, 4
+    assert B.pipeline_segments(1000, 3) == 3      # 16 chunks -> 5, 6, 5
     assert B.pipeline_segments(100, 8) == 2       # 2 chunks
     assert B.pipeline_segments(0, 8) == 0
     assert L.gdp_pipeline_segments(10, 0) == -1
+    assert L.gdp_pipeline_plan(10, 2, None) == -1
+    # the plan: equal shares of whole chunks, T covered once
+    assert B.pipeline_plan(32768, 3) == [0, 10944, 21824, 32768]  # 512 chunks: 171, 170, 171
+    assert B.pipeline_plan(1000, 3) == [0, 320, 704, 1000]        # 16 chunks: 5, 6, 5
+    assert B.pipeline_plan(0, 4) == [0]
+    for T in list(range(1, 700, 7)) + [4096, 32767, 32768, 100000]:
+        for ns in range(1, 10):
+            st = B.pipeline_plan(T, ns)
+            assert len(st) - 1 == B.pipeline_segments(T, ns) == min(ns, (T + 63) // 64)
+            assert st[0] == 0 and st[-1] == T
+            assert all(b > a for a, b in zip(st, st[1:]))
+            assert all(x % 64 == 0 for x in st[:-1])
+            n_ch = [(b - a + 63) // 64 for a, b in zip(st, st[1:])]
+            assert max(n_ch) - min(n_ch) <= 1, (T, ns, n_ch)
 
 
 def test_prefill_pipelined_rejects():
