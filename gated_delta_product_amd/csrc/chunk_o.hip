@@ -60,11 +60,16 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     T *Vs = (T *)v_dyn;
     __shared__ float sG[4][C], sRk[4][C];                    // per-wave scratch
 
-    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, blockIdx.x);
+    // block -> (token chunk, value head, value slab), slabs then heads
+    // fastest: the blocks in flight together cover whole rows of q, k and
+    // o (all heads of a few chunks), so HBM sees long contiguous runs
+    const int nslab = VD / VB;
+    const int64_t lin = blockIdx.x;
+    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, lin / ((int64_t)HV * nslab));
     if (loc.seq < 0) return;
-    const int hv = blockIdx.y;
+    const int hv = (int)((lin / nslab) % HV);
     const int hk = hv / (HV / H);
-    const int vb0 = VB * (int)blockIdx.z;
+    const int vb0 = VB * (int)(lin % nslab);
     const int64_t t0 = loc.bos + C * loc.c;  // first token (flattened)
     const int nt = (int)((loc.eos - t0) < C ? (loc.eos - t0) : C);
     const int64_t hidx = items_before(cu, Ttok, M, C, loc.seq) + loc.c * M;
@@ -275,7 +280,9 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
 template <typename T, int KD, int VB>
 static hipError_t launch_chunk_o_t(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
-    dim3 grid((unsigned)p.max_tok_chunks, (unsigned)a.HV, (unsigned)(a.V / VB));
+    const int64_t nblk = p.max_tok_chunks * a.HV * (a.V / VB);
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)nblk);
     const size_t vdyn = (size_t)a.M * 64 * VB * sizeof(T);  // the V slab of all copies (<= 64 KiB)
     hipLaunchKernelGGL((gdp_chunk_o_k<T, KD, VB>), grid, dim3(256), vdyn, stream,
                        (const T *)a.q, (const T *)a.k, a.k_rnorm, (const T *)a.v_new, (const T *)a.h, a.g,

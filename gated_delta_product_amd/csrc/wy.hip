@@ -1,7 +1,8 @@
 // wy.hip -- per-chunk WY factors of the Gated Delta Product
 // (core.ssm.ops.gdp.wy_fast: module description, recompute_w_u_fwd).
 //
-// One block (4 waves) per (64-row chunk of the expanded stream, value head).
+// One block (4 waves) per (64-row chunk of the expanded stream, value head),
+// heads fastest in the launch order.
 // Fused steps, all on chip:
 //   khat = k / sqrt(sum k^2 + 1e-6)           (L2 norm left to the chunk op,
 //                                               core.ssm.ops.gdp.prepare, Returns)
@@ -67,9 +68,13 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         return (r >> 4) == (c >> 4) ? Lm[r * LDA + c] : Lm[c * LDA + r];
     };
 
-    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, blockIdx.x);
+    // block -> (chunk, value head), heads fastest: the blocks in flight
+    // together cover whole rows of k, v and w (all heads of a few chunks),
+    // so HBM sees long contiguous runs
+    const int64_t lin = blockIdx.x;
+    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, lin / HV);
     if (loc.seq < 0) return;
-    const int hv = blockIdx.y;
+    const int hv = (int)(lin % HV);
     const int hk = hv / (HV / H);
     const int64_t r0 = loc.bos * M + C * loc.c;  // first expanded row (global)
     const int64_t rend = loc.eos * M;
@@ -114,12 +119,12 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // block's own loads were consumed, so no wait here covers them.
     {
         constexpr int64_t PFD = 512;
-        const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x + PFD;
-        if (lin < (int64_t)gridDim.x * gridDim.y) {
-            const ChunkLoc pl = find_chunk(cu, nseq, Ttok, M, C, lin % gridDim.x);
+        const int64_t plin = lin + PFD;
+        if (plin < (int64_t)gridDim.x) {
+            const ChunkLoc pl = find_chunk(cu, nseq, Ttok, M, C, plin / HV);
             if (pl.seq >= 0) {
                 constexpr int ES = (int)sizeof(T);
-                const int phv = (int)(lin / gridDim.x), phk = phv / (HV / H);
+                const int phv = (int)(plin % HV), phk = phv / (HV / H);
                 const int64_t pr0 = pl.bos * M + C * pl.c, prend = pl.eos * M;
                 const int pn = (int)((prend - pr0) < C ? (prend - pr0) : C);
                 const uint32_t pf = lds_addr(s_pf);
@@ -329,7 +334,8 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
 template <typename T, int KD, int VD>
 static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
-    dim3 grid((unsigned)p.max_items, (unsigned)a.HV);
+    if (p.max_items * a.HV > 0x7fffffff) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)(p.max_items * a.HV));
     hipLaunchKernelGGL((gdp_wy_k<T, KD, VD>), grid, dim3(256), 0, stream,
                        (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
                        a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u, p.uv_ss);
