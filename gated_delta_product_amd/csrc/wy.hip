@@ -59,7 +59,6 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // tile (V waits in registers until then)
     __shared__ __attribute__((aligned(16))) char LA[LA_BYTES];
     __shared__ __attribute__((aligned(16))) float s_beta[C], s_gam[C], s_rk[C], s_ws[C];
-    __shared__ __attribute__((aligned(16))) float s_pf[64];  // landing area of L2 pulls
     float *Lm = (float *)LA;
     T *Vs = (T *)LA;
     // A[r][c] for r, c in the same 16-row block or r > c: the diagonal
@@ -112,41 +111,6 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
     __syncthreads();
 
-    // ---- pull the K and V lines of the block dispatched PFD blocks later
-    // into L2 (blocks go out in order, round-robin over the XCDs, so that
-    // block shares this XCD's L2): one 4-byte load per 128-byte line,
-    // landing in a scratch word array nothing reads.  Issued after this
-    // block's own loads were consumed, so no wait here covers them.
-    {
-        constexpr int64_t PFD = 512;
-        const int64_t plin = lin + PFD;
-        if (plin < (int64_t)gridDim.x) {
-            const ChunkLoc pl = find_chunk(cu, nseq, Ttok, M, C, plin / HV);
-            if (pl.seq >= 0) {
-                constexpr int ES = (int)sizeof(T);
-                const int phv = (int)(plin % HV), phk = phv / (HV / H);
-                const int64_t pr0 = pl.bos * M + C * pl.c, prend = pl.eos * M;
-                const int pn = (int)((prend - pr0) < C ? (prend - pr0) : C);
-                const uint32_t pf = lds_addr(s_pf);
-                const rsrc_t rk = make_rsrc(k + (pr0 * H + phk) * (int64_t)KD,
-                                            pn > 0 ? (uint32_t)(((pn - 1) * H * KD + KD) * ES) : 0u);
-                const rsrc_t rv = make_rsrc(v + (pr0 * HV + phv) * (int64_t)VD,
-                                            pn > 0 ? (uint32_t)(((pn - 1) * HV * VD + VD) * ES) : 0u);
-                constexpr int KL = KD * ES / 128, VL = VD * ES / 128;  // 128-byte lines per row
-                // wave wv covers rows [16 wv, 16 wv + 16) of both tiles
-#pragma unroll
-                for (int i = 0; i < (16 * KL + 63) / 64; ++i) {
-                    const int l = 64 * i + lane, row = 16 * wv + l / KL;
-                    dma4(rk, (uint32_t)(row * H * KD * ES + (l % KL) * 128), pf);
-                }
-#pragma unroll
-                for (int i = 0; i < (16 * VL + 63) / 64; ++i) {
-                    const int l = 64 * i + lane, row = 16 * wv + l / VL;
-                    dma4(rv, (uint32_t)(row * HV * VD * ES + (l % VL) * 128), pf);
-                }
-            }
-        }
-    }
     if (wv == 0) {
         const float rk = 1.0f / sqrtf(s_rk[lane] + 1e-6f);
         s_rk[lane] = rk;
@@ -328,7 +292,6 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                     *(const uint4 *)(Ks + row * LDK + c16 * (16 / (int)sizeof(T)));
         }
     }
-    wait_vmcnt<0>();  // no load may still target LDS when the block retires
 }
 
 template <typename T, int KD, int VD>
