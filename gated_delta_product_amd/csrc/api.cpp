@@ -304,8 +304,8 @@ int32_t gdp_pipeline_plan(int64_t T, int32_t num_segments, int64_t *starts) {
     return segment_plan(T, num_segments, starts);
 }
 
-// The pipelined chunk forward; with prep, each segment's prepare runs on the
-// WY side stream right before that segment's WY.
+// The pipelined chunk forward; with prep, each segment's prepare runs right
+// before that segment's WY, on the same stream.
 static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PrepareParams *prep, int32_t num_segments,
                                  float *state_workspace, void *const *chunk_h_events, void *stream) {
     gdp::ChunkParams p;
@@ -328,19 +328,9 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_status(e, "hipGetDevice");
     if (dev < 0 || dev >= 64) return fail(GDP_ERR_UNSUPPORTED, "device index %d", dev);
-    gdp::PipeCtx *ctx = nullptr;
-    if ((e = gdp::pipe_ctx(dev, (size_t)(2 * nseg + 2), ctx)) != hipSuccess)
-        return hip_status(e, "gdp_chunk_fwd_pipelined: stream/event creation");
-    hipStream_t sw = ctx->side[0], so = ctx->side[1];
-    hipEvent_t ev_start = ctx->ev[0], ev_end = ctx->ev[1];
-#define GDP_TRY(call, what)                                      \
-    do {                                                         \
-        hipError_t e_ = (call);                                  \
-        if (e_ != hipSuccess) return hip_status(e_, what);       \
-    } while (0)
-    GDP_TRY(hipEventRecord(ev_start, s0), "hipEventRecord");
-    GDP_TRY(hipStreamWaitEvent(sw, ev_start, 0), "hipStreamWaitEvent");
-    GDP_TRY(hipStreamWaitEvent(so, ev_start, 0), "hipStreamWaitEvent");
+    // every segment's arguments are checked before anything is enqueued
+    std::vector<gdp::ChunkParams> sps((size_t)nseg);
+    std::vector<gdp::PrepareParams> pps(prep ? (size_t)nseg : 0);
     for (int64_t sidx = 0; sidx < nseg; ++sidx) {
         const int64_t t0 = starts[sidx], Tn = starts[sidx + 1] - t0;
         const int64_t r0 = t0 * a->M;      // first expanded row
@@ -363,12 +353,11 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
         sa.o = (char *)a->o + t0 * a->HV * a->V * es;
         sa.h0 = sidx == 0 ? a->h0 : state_workspace + ((sidx - 1) & 1) * state_elems;
         sa.ht = sidx == nseg - 1 ? a->ht : state_workspace + (sidx & 1) * state_elems;
-        gdp::ChunkParams sp;
-        if ((st = check_chunk(&sa, ST_WY | ST_H | ST_O, &sp)) != GDP_OK) return st;
-        sp.uv_ss = a->T * a->M * 16;  // slices keep the whole sequence's stride
-        hipEvent_t ev_w = ctx->ev[2 + 2 * sidx], ev_h = ctx->ev[3 + 2 * sidx];
+        if ((st = check_chunk(&sa, ST_WY | ST_H | ST_O, &sps[sidx])) != GDP_OK) return st;
+        sps[sidx].uv_ss = a->T * a->M * 16;  // slices keep the whole sequence's stride
         if (prep) {  // tokens [t0, t0 + Tn) of the one sequence
-            gdp::PrepareParams pp = *prep;
+            gdp::PrepareParams &pp = pps[sidx];
+            pp = *prep;
             const int64_t pes = (int64_t)dsize(prep->dtype);
             pp.x = (const char *)prep->x + t0 * prep->x_t_stride * pes;
             pp.ba = (const char *)prep->ba + t0 * prep->ba_t_stride * pes;
@@ -378,20 +367,61 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
             pp.v = (char *)prep->v + t0 * prep->M * prep->H * prep->P * pes;
             pp.beta = prep->beta + t0 * prep->M * prep->H;
             pp.g = prep->g + t0 * prep->H;
-            GDP_TRY(gdp::launch_prepare(pp, sw), "gdp_prefill_fwd_pipelined: prepare launch");
         }
-        GDP_TRY(gdp::launch_wy(sp, sw), "gdp_chunk_fwd_pipelined: recompute_w_u launch");
-        GDP_TRY(hipEventRecord(ev_w, sw), "hipEventRecord");
-        GDP_TRY(hipStreamWaitEvent(s0, ev_w, 0), "hipStreamWaitEvent");
-        if (chunk_h_events) GDP_TRY(hipEventRecord((hipEvent_t)chunk_h_events[2 * sidx], s0), "hipEventRecord");
-        GDP_TRY(gdp::launch_chunk_h(sp, s0), "gdp_chunk_fwd_pipelined: chunk_h launch");
-        if (chunk_h_events) GDP_TRY(hipEventRecord((hipEvent_t)chunk_h_events[2 * sidx + 1], s0), "hipEventRecord");
-        GDP_TRY(hipEventRecord(ev_h, s0), "hipEventRecord");
-        GDP_TRY(hipStreamWaitEvent(so, ev_h, 0), "hipStreamWaitEvent");
-        GDP_TRY(gdp::launch_chunk_o(sp, so), "gdp_chunk_fwd_pipelined: chunk_o launch");
     }
-    GDP_TRY(hipEventRecord(ev_end, so), "hipEventRecord");
-    GDP_TRY(hipStreamWaitEvent(s0, ev_end, 0), "hipStreamWaitEvent");
+
+    gdp::PipeCtx *ctx = nullptr;
+    if ((e = gdp::pipe_ctx(dev, (size_t)(2 * nseg + 2), ctx)) != hipSuccess)
+        return hip_status(e, "gdp_chunk_fwd_pipelined: stream/event creation");
+    hipStream_t sw = ctx->side[0], so = ctx->side[1];
+    hipEvent_t ev_end = ctx->ev[1];
+    auto ev_w = [&](int64_t sidx) { return ctx->ev[2 + 2 * sidx]; };  // segment's WY done
+    auto ev_h = [&](int64_t sidx) { return ctx->ev[3 + 2 * sidx]; };  // segment's chunk_h done
+#define GDP_TRY(call, what)                                      \
+    do {                                                         \
+        hipError_t e_ = (call);                                  \
+        if (e_ != hipSuccess) return hip_status(e_, what);       \
+    } while (0)
+    // Order of work.  Every cross-stream wait costs the serial chain about
+    // 10-15 us, so the chain on `stream` holds only the waits it needs:
+    //   stream: [prepare 0] WY 0, chunk_h 0, (wait WY 1) chunk_h 1, ...,
+    //           chunk_h n-1, chunk_o n-1, (wait the last side chunk_o)
+    //   side 0: [prepare s] WY s for s >= 1, back to back once WY 0 is done
+    //           (they all overlap the first chunk_h or two: spreading them
+    //           one per chunk_h measured slower, as each chunk_h then
+    //           shares the memory system with a WY and a chunk_o)
+    //   side 1: chunk_o s after chunk_h s, for s < n-1
+    // A side stream's first operation waits on an event of `stream`, and
+    // its last is waited on by `stream`, so a capture takes both in.
+    if (prep) GDP_TRY(gdp::launch_prepare(pps[0], s0), "gdp_prefill_fwd_pipelined: prepare launch");
+    GDP_TRY(gdp::launch_wy(sps[0], s0), "gdp_chunk_fwd_pipelined: recompute_w_u launch");
+    if (nseg > 1) {
+        GDP_TRY(hipEventRecord(ev_w(0), s0), "hipEventRecord");
+        GDP_TRY(hipStreamWaitEvent(sw, ev_w(0), 0), "hipStreamWaitEvent");
+    }
+    for (int64_t sidx = 0; sidx < nseg; ++sidx) {
+        const bool last = sidx == nseg - 1;
+        if (!last) {  // the next segment's WY
+            if (prep) GDP_TRY(gdp::launch_prepare(pps[sidx + 1], sw), "gdp_prefill_fwd_pipelined: prepare launch");
+            GDP_TRY(gdp::launch_wy(sps[sidx + 1], sw), "gdp_chunk_fwd_pipelined: recompute_w_u launch");
+            GDP_TRY(hipEventRecord(ev_w(sidx + 1), sw), "hipEventRecord");
+        }
+        if (sidx >= 1) GDP_TRY(hipStreamWaitEvent(s0, ev_w(sidx), 0), "hipStreamWaitEvent");
+        if (chunk_h_events) GDP_TRY(hipEventRecord((hipEvent_t)chunk_h_events[2 * sidx], s0), "hipEventRecord");
+        GDP_TRY(gdp::launch_chunk_h(sps[sidx], s0), "gdp_chunk_fwd_pipelined: chunk_h launch");
+        if (chunk_h_events) GDP_TRY(hipEventRecord((hipEvent_t)chunk_h_events[2 * sidx + 1], s0), "hipEventRecord");
+        if (!last) {
+            GDP_TRY(hipEventRecord(ev_h(sidx), s0), "hipEventRecord");
+            GDP_TRY(hipStreamWaitEvent(so, ev_h(sidx), 0), "hipStreamWaitEvent");
+            GDP_TRY(gdp::launch_chunk_o(sps[sidx], so), "gdp_chunk_fwd_pipelined: chunk_o launch");
+        } else {
+            GDP_TRY(gdp::launch_chunk_o(sps[sidx], s0), "gdp_chunk_fwd_pipelined: chunk_o launch");
+        }
+    }
+    if (nseg > 1) {
+        GDP_TRY(hipEventRecord(ev_end, so), "hipEventRecord");
+        GDP_TRY(hipStreamWaitEvent(s0, ev_end, 0), "hipStreamWaitEvent");
+    }
 #undef GDP_TRY
     return ok();
 }

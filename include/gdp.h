@@ -274,10 +274,13 @@ gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
  * whole 64-token chunks (gdp_pipeline_plan gives where each starts) so that
  * the parallel stages overlap the serial one:
  * chunk_h runs the segments in order on `stream`, handing the fp32 state
- * from one segment to the next (as h0 / ht), while gdp_recompute_w_u of the
- * next segments and gdp_chunk_o of the finished ones run on two streams of
- * the library's own (created once per device, default priority) that join
- * `stream` through events.  On return all work is ordered before later work
+ * from one segment to the next (as h0 / ht).  The first segment's
+ * gdp_recompute_w_u and the last one's gdp_chunk_o also run on `stream`;
+ * the other segments' gdp_recompute_w_u (back to back, from the end of the
+ * first one) and gdp_chunk_o (each after its own chunk_h) run on two
+ * streams of the library's own (created once per device, default
+ * priority) that join `stream` through events.  With one segment every
+ * stage runs on `stream`.  On return all work is ordered before later work
  * on `stream`; nothing is synchronised with the host.  The first call on a
  * device, and a call with more segments than any before it, create the
  * streams and events it needs: make such a call outside graph capture.
@@ -318,8 +321,8 @@ typedef struct gdp_prepare_args {
 
 /*
  * gdp_prefill_fwd_pipelined -- gdp_prefill_prepare followed by
- * gdp_chunk_fwd_pipelined, with the prepare of each segment run on the WY
- * side stream just before that segment's WY, so that only the first
+ * gdp_chunk_fwd_pipelined, with the prepare of each segment run just
+ * before that segment's WY, on the same stream, so that only the first
  * segment's prepare precedes the serial stage.  Prepare writes the chunk
  * arguments' q, k, v, beta and g (which must therefore be writable, g not
  * NULL, and HV == H: prepare makes H value heads).  Results are
