@@ -17,13 +17,15 @@ drawn once (seeded, synthetic) and resident in HBM before timing starts.
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (chunk_h: algorithmic bytes per launch / its average launch
 duration from HIP events recorded on its stream around every segment launch,
-vs 8 TB/s HBM) and the oracle's throughput on the host cores as a reported
+vs 8 TB/s HBM; the events record without a system-scope fence, so they do
+not slow the step they time) and the oracle's throughput on the host cores as a reported
 baseline.  --stages adds a sequential (not overlapped) pass that times each
 stage on its own.
 
     python bench.py [--steps K] [--warmup W] [--segments S] [--stages] [--no-cpu-baseline] [--copy-mib N]
 """
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -37,11 +39,57 @@ METRIC = "GDP prefill forward tokens/s (T=32k, H=16, K=V=128, M=2) + % MFMA/HBM 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(workload="long_prefill_32k", B=1, T=32768, H=16, HV=16, G=16, K=128, V=128, M=2, chunk=64,
                 dtype="bf16", path="prepare+pipelined(recompute_w_u,chunk_h,chunk_o)")
-SEGMENTS = 4
+SEGMENTS = 3
 # A serving decode step of the same layer: 256 requests, one token each
 # (no draft tokens), the fp32 state of every request read and written once.
 DECODE = dict(workload="decode_step", n=256, S=1, H=16, HV=16, G=16, K=128, V=128, M=2, dtype="bf16")
 KERNELS = ["gdp_prefill_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o"]
+
+
+class TimingEvent:
+    """A HIP timing event that records without a system-scope fence
+    (hipEventDisableSystemFence).  A default event writes back and
+    invalidates the caches when it records, which slows the work around it:
+    with one such event before and after each kernel the step took about
+    40 us longer.  Read elapsed_time only after the device is synchronised.
+    The interface is the part of torch.cuda.Event the benchmark uses
+    (record, elapsed_time, and cuda_event, the raw handle)."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has loaded
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+        self.cuda_event = h.value
+
+    def record(self, stream):
+        rc = self._runtime().hipEventRecord(self.cuda_event, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        rc = self._runtime().hipEventElapsedTime(ctypes.byref(ms), self.cuda_event, end.cuda_event)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.cuda_event:
+            self._hip.hipEventDestroy(self.cuda_event)
 
 
 def algorithmic_bytes(w, T=None):
@@ -143,7 +191,7 @@ def decode_step(G, torch, dev, stream, steps):
     for _ in range(3):
         G.decode_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=rows)
         G.decode_update(*rows, state, M, o=o)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for e in ev:
         e[0].record(stream)
@@ -198,7 +246,7 @@ def main():
     nseg = G.pipeline_segments(w["T"], args.segments)
 
     def new_events(n):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        evs = [TimingEvent() for _ in range(n)]
         for e in evs:
             e.record(stream)  # instantiate the handles
         return evs
