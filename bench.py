@@ -126,9 +126,10 @@ def decode_bytes(c):
             + n * L * c["HV"] * 8 + n * L * c["HV"] * c["V"] * es)
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, segments):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    it was taken on the current kernel source with the same pipeline
+    segments (the launch sizes); else None."""
     from gated_delta_product_amd import profiling
     path = os.path.join(ROOT, "profiles", "traffic_long_prefill_32k.json")
     if not os.path.exists(path):
@@ -136,7 +137,7 @@ def measured_traffic(kernel):
     with open(path) as f:
         t = json.load(f)
     e = t.get(kernel)
-    if not e or e.get("src_digest") != profiling.src_digest(kernel):
+    if not e or e.get("src_digest") != profiling.src_digest(kernel) or t.get("_segments") != segments:
         return None
     return e.get("bytes_per_launch")
 
@@ -289,7 +290,7 @@ def main():
     }
     achieved = ch_bytes / (ch_ms / 1e3) / 1e9
     roof = {"kernel": "gdp_chunk_h", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gdp_chunk_h")}
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gdp_chunk_h", nseg)}
 
     stages = None
     if args.stages:  # each stage alone, whole workload, for reference

@@ -117,6 +117,9 @@ def main(argv=None):
     t.add_argument("out")
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--command", required=True)
+    t.add_argument("--segments", type=int, default=None,
+                   help="pipeline segments of the profiled run: the per-launch bytes of the chunk "
+                        "stages hold for that split only")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         digests = ", ".join("%s %s" % (op, src_digest(op)) for op in KERNELS)
@@ -127,6 +130,8 @@ def main(argv=None):
     else:
         res = traffic(a.fetch_csv, a.write_csv, a.copy_mib)
         res["_command"] = a.command
+        if a.segments is not None:
+            res["_segments"] = a.segments
         with open(a.out, "w") as f:
             json.dump(res, f, indent=1, sort_keys=True)
             f.write("\n")
