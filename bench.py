@@ -40,6 +40,7 @@ HBM_PEAK_GBS = 8000.0
 WORKLOAD = dict(workload="long_prefill_32k", B=1, T=32768, H=16, HV=16, G=16, K=128, V=128, M=2, chunk=64,
                 dtype="bf16", path="prepare+pipelined(recompute_w_u,chunk_h,chunk_o)")
 SEGMENTS = 3
+SCAN_SEGMENTS = 16
 # A serving decode step of the same layer: 256 requests, one token each
 # (no draft tokens), the fp32 state of every request read and written once.
 DECODE = dict(workload="decode_step", n=256, S=1, H=16, HV=16, G=16, K=128, V=128, M=2, dtype="bf16")
@@ -215,7 +216,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--segments", type=int, default=SEGMENTS, help="pipeline segments of the chunk forward")
+    ap.add_argument("--path", choices=["pipelined", "scan"], default="pipelined",
+                    help="chunk forward: gdp_chunk_fwd_pipelined or gdp_chunk_fwd_scan")
+    ap.add_argument("--segments", type=int, default=None,
+                    help="segments of the chunk forward (default %d pipelined, %d scan)" % (SEGMENTS, SCAN_SEGMENTS))
     ap.add_argument("--stages", action="store_true", help="also time each stage sequentially (not overlapped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
@@ -235,6 +239,11 @@ def main():
     from gated_delta_product_amd import synth
 
     w = dict(WORKLOAD)
+    scan = args.path == "scan"
+    if args.segments is None:
+        args.segments = SCAN_SEGMENTS if scan else SEGMENTS
+    if scan:
+        w["path"] = "prepare+scan(recompute_w_u,seg_map,seg_scan,chunk_h,chunk_o)"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = synth.prepare_draws(1, w["T"], w["M"], w["H"], w["G"], w["V"], w["K"], "bf16", synth.seed_of(4) + 100)
@@ -244,7 +253,8 @@ def main():
     prep_out = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N)
     buf = G.ChunkBuffers(*prep_out)
     stream = torch.cuda.current_stream(dev)
-    nseg = G.pipeline_segments(w["T"], args.segments)
+    nseg = G.scan_segments(w["T"], args.segments) if scan else G.pipeline_segments(w["T"], args.segments)
+    nev = 2 + (3 if scan else 2 * nseg)
 
     def new_events(n):
         evs = [TimingEvent() for _ in range(n)]
@@ -258,12 +268,15 @@ def main():
         G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
         if ev:
             ev[1].record(stream)
-        buf.forward_pipelined(nseg, chunk_h_events=ev[2:] if ev else None)
+        if scan:
+            buf.forward_scan(args.segments, stage_events=ev[2:] if ev else None)
+        else:
+            buf.forward_pipelined(nseg, chunk_h_events=ev[2:] if ev else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [new_events(2 + 2 * nseg) for _ in range(args.steps)]
+    evs = [new_events(nev) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -274,23 +287,40 @@ def main():
     tokens = w["B"] * w["T"]
     value = tokens / (ms_per_step / 1e3)
 
-    # chunk_h: every segment launch, bracketed on its own stream
-    seg_ms = [e[2 + 2 * j].elapsed_time(e[3 + 2 * j]) for e in evs for j in range(nseg)]
     prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    starts = G.pipeline_plan(w["T"], args.segments)
-    seg_tokens = [starts[j + 1] - starts[j] for j in range(nseg)]
-    ch_bytes = sum(algorithmic_bytes(w, t)["gdp_chunk_h"] for t in seg_tokens) / nseg  # per launch
-    ch_ms = sum(seg_ms) / len(seg_ms)
     ab = algorithmic_bytes(w)
+    if scan:
+        # chunk_h: one launch over every segment at once, bracketed on its stream
+        seg_ms = [e[3].elapsed_time(e[4]) for e in evs]
+        ch_bytes = ab["gdp_chunk_h"]
+        map_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    else:
+        # chunk_h: every segment launch, bracketed on its own stream
+        seg_ms = [e[2 + 2 * j].elapsed_time(e[3 + 2 * j]) for e in evs for j in range(nseg)]
+        starts = G.pipeline_plan(w["T"], args.segments)
+        seg_tokens = [starts[j + 1] - starts[j] for j in range(nseg)]
+        ch_bytes = sum(algorithmic_bytes(w, t)["gdp_chunk_h"] for t in seg_tokens) / nseg  # per launch
+    ch_ms = sum(seg_ms) / len(seg_ms)
     kern = {
         "gdp_prefill_prepare": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1, "alg_bytes": ab["gdp_prefill_prepare"],
                                 "GB/s": round(ab["gdp_prefill_prepare"] / (prep_ms / 1e3) / 1e9, 1)},
-        "gdp_chunk_h": {"us_per_launch": round(ch_ms * 1e3, 2), "launches_per_step": nseg,
+        "gdp_chunk_h": {"us_per_launch": round(ch_ms * 1e3, 2), "launches_per_step": 1 if scan else nseg,
                         "alg_bytes_per_launch": int(ch_bytes), "GB/s": round(ch_bytes / (ch_ms / 1e3) / 1e9, 1)},
     }
+    if scan:
+        # the segment maps read k, kdecay, gcum, w and u of every segment but
+        # the last once, and write each segment's fp32 map; the scan reads
+        # the maps and writes one fp32 state per segment
+        seg_tok = math.ceil(math.ceil(w["T"] / 64) / args.segments) * 64
+        TM = (nseg - 1) * seg_tok * w["M"]
+        mb = TM * w["H"] * w["K"] * 2 + TM * w["HV"] * 8 + TM * w["HV"] * (w["K"] + w["V"]) * 2 \
+            + (nseg - 1) * w["HV"] * w["K"] * (w["K"] + w["V"]) * 4
+        kern["gdp_seg_map+gdp_seg_scan"] = {"us": round(map_ms * 1e3, 2), "segments": nseg, "map_alg_bytes": mb,
+                                            "GB/s": round(mb / (map_ms / 1e3) / 1e9, 1)}
     achieved = ch_bytes / (ch_ms / 1e3) / 1e9
     roof = {"kernel": "gdp_chunk_h", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gdp_chunk_h", nseg)}
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if scan else measured_traffic("gdp_chunk_h", nseg)}
 
     stages = None
     if args.stages:  # each stage alone, whole workload, for reference

@@ -89,6 +89,12 @@ def lib():
         L.gdp_prefill_fwd_pipelined.restype = ctypes.c_int
         L.gdp_prefill_fwd_pipelined.argtypes = [ctypes.POINTER(PrepareArgs), ctypes.POINTER(ChunkArgs), _i32, _vp,
                                                 _vp, _vp]
+        L.gdp_chunk_fwd_scan.restype = ctypes.c_int
+        L.gdp_chunk_fwd_scan.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _i64, _vp, _vp]
+        L.gdp_scan_segments.restype = _i32
+        L.gdp_scan_segments.argtypes = [_i64, _i32]
+        L.gdp_scan_workspace_bytes.restype = _i64
+        L.gdp_scan_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
         L.gdp_pipeline_segments.restype = _i32
         L.gdp_pipeline_segments.argtypes = [_i64, _i32]
         L.gdp_pipeline_plan.restype = _i32
@@ -200,6 +206,14 @@ def pipeline_plan(T, num_segments):
     if n < 0:
         raise GdpError(GDP_ERR_INVALID, "bad arguments to gdp_pipeline_plan")
     return [int(buf[i]) for i in range(n + 1)]
+
+
+def scan_segments(T, num_segments):
+    """Segments gdp_chunk_fwd_scan runs for T tokens."""
+    n = lib().gdp_scan_segments(int(T), int(num_segments))
+    if n < 0:
+        raise ValueError("bad arguments")
+    return n
 
 
 def num_state_chunks(T, M, B=1, cu_seqlens_host=None):
@@ -333,6 +347,32 @@ class ChunkBuffers:
         enabled, recorded at least once) marking each segment's chunk_h."""
         return self._pipelined(lambda ws, ev, s: lib().gdp_chunk_fwd_pipelined(
             ctypes.byref(self.args), int(num_segments), ws, ev, s), num_segments, stream, chunk_h_events)
+
+    def forward_scan(self, num_segments, stream=None, stage_events=None):
+        """gdp_chunk_fwd_scan: the results of forward() for B == 1 without
+        cu_seqlens (to rounding past the first segment), with the serial
+        chunk_h chain cut into num_segments segments run in parallel from
+        the states a scan over the segments' composed maps gives.
+        stage_events: optional 3 torch.cuda.Event (timing enabled, recorded
+        at least once) recorded before the segment maps, before chunk_h and
+        after it."""
+        d = self.dims
+        need = lib().gdp_scan_workspace_bytes(d["T"], d["HV"], d["K"], d["V"], int(num_segments))
+        if need < 0:
+            raise ValueError("num_segments %r out of range" % (num_segments,))
+        ws = getattr(self, "_scan_ws", None)
+        if ws is None or ws.numel() < need:
+            # torch's caching allocator returns 512-byte aligned blocks
+            self._scan_ws = ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        ev = None
+        if stage_events is not None:
+            if len(stage_events) != 3:
+                raise ValueError("need 3 events")
+            ev = (_vp * 3)(*[e.cuda_event for e in stage_events])
+        s = stream if stream is not None else _stream(self.device)
+        _check(lib().gdp_chunk_fwd_scan(ctypes.byref(self.args), int(num_segments), ws.data_ptr(), ws.numel(),
+                                        ev, s))
+        return self.o
 
     def _pipelined(self, call, num_segments, stream, chunk_h_events):
         d = self.dims

@@ -426,6 +426,98 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
     return ok();
 }
 
+// Plan of the segment-parallel forward: segments of seg_tok tokens (equal
+// shares of the 64-token chunks, rounded up), the last one possibly shorter.
+static int32_t scan_plan(int64_t T, int32_t num_segments, int64_t *seg_tok) {
+    const int64_t nch = cdiv(T, 64);
+    const int64_t per = cdiv(nch, num_segments) * 64;
+    *seg_tok = per;
+    return T > 0 ? (int32_t)cdiv(T, per) : 0;
+}
+
+// Byte offsets of the regions of the scan workspace (each 256-byte aligned).
+struct ScanLayout {
+    int64_t maps, hstart, cu, total;
+};
+static ScanLayout scan_layout(int64_t nseg, int64_t HV, int64_t K, int64_t V) {
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    ScanLayout L;
+    L.maps = 0;
+    L.hstart = up((nseg > 1 ? nseg - 1 : 0) * HV * K * (K + V) * 4);
+    L.cu = L.hstart + up(nseg * HV * V * K * 4);
+    L.total = L.cu + up((nseg + 1) * 4);
+    return L;
+}
+
+int32_t gdp_scan_segments(int64_t T, int32_t num_segments) {
+    if (T < 0 || num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS) return -1;
+    int64_t st;
+    return scan_plan(T, num_segments, &st);
+}
+
+int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, int32_t num_segments) {
+    if (T < 0 || HV < 1 || K < 1 || V < 1 || num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS) return -1;
+    int64_t st;
+    const int64_t nseg = scan_plan(T, num_segments, &st);
+    return scan_layout(nseg, HV, K, V).total;
+}
+
+gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
+                              int64_t workspace_bytes, void *const *stage_events, void *stream) {
+    gdp::ChunkParams p;
+    gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
+    if (st != GDP_OK) return st;
+    if (a->cu_seqlens) return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: cu_seqlens must be NULL");
+    if (a->B != 1) return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: B must be 1 (got %lld)", (long long)a->B);
+    if (num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS)
+        return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: num_segments %d not in [1, %d]", num_segments,
+                    GDP_SCAN_MAX_SEGMENTS);
+    if (a->dtype != GDP_BF16 || !((a->K == 64 || a->K == 128) && (a->V == 64 || a->V == 128)))
+        return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd_scan: bf16 with K, V in {64, 128} only (K=%d V=%d)", a->K,
+                    a->V);
+    if (a->T == 0) return ok();
+    int64_t seg_tok = 0;
+    const int64_t nseg = scan_plan(a->T, num_segments, &seg_tok);
+    const ScanLayout L = scan_layout(nseg, a->HV, a->K, a->V);
+    if (!workspace || ((uintptr_t)workspace & 255u))
+        return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: workspace must be a 256-byte aligned device pointer");
+    if (workspace_bytes < L.total)
+        return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: workspace of %lld bytes, %lld needed",
+                    (long long)workspace_bytes, (long long)L.total);
+    char *ws = (char *)workspace;
+    gdp::ScanParams sp{p, nseg, seg_tok, (float *)(ws + L.maps), (float *)(ws + L.hstart),
+                       (int32_t *)(ws + L.cu)};
+    // the chunk_h pass: the segments as packed sequences, each from its
+    // entering state, whose final states replace it in place
+    gdp_chunk_args ha = *a;
+    ha.cu_seqlens = sp.cu;
+    ha.num_seqs = nseg;
+    ha.h0 = sp.hstart;
+    ha.ht = sp.hstart;
+    gdp::ChunkParams hp;
+    if ((st = check_chunk(&ha, ST_H, &hp)) != GDP_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = hip_status(gdp::launch_wy(p, s), "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK) return st;
+    auto mark = [&](int i) {
+        return stage_events ? hip_status(hipEventRecord((hipEvent_t)stage_events[i], s), "hipEventRecord") : ok();
+    };
+    if ((st = mark(0)) != GDP_OK) return st;
+    if ((st = hip_status(gdp::launch_seg_scan(sp, s), "gdp_chunk_fwd_scan: segment scan launch")) != GDP_OK)
+        return st;
+    if ((st = mark(1)) != GDP_OK) return st;
+    if ((st = hip_status(gdp::launch_chunk_h(hp, s), "gdp_chunk_fwd_scan: chunk_h launch")) != GDP_OK) return st;
+    if ((st = mark(2)) != GDP_OK) return st;
+    if ((st = hip_status(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd_scan: chunk_o launch")) != GDP_OK) return st;
+    if (a->ht) {
+        const size_t bytes = (size_t)a->HV * a->V * a->K * sizeof(float);
+        if ((st = hip_status(hipMemcpyAsync(a->ht, sp.hstart + (nseg - 1) * a->HV * a->V * a->K, bytes,
+                                            hipMemcpyDeviceToDevice, s),
+                             "gdp_chunk_fwd_scan: final state copy")) != GDP_OK)
+            return st;
+    }
+    return ok();
+}
+
 gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,
                                    void *const *chunk_h_events, void *stream) {
     return pipelined_impl(a, nullptr, num_segments, state_workspace, chunk_h_events, stream);

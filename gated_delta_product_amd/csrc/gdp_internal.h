@@ -44,6 +44,22 @@ __host__ __device__ inline int64_t uv_index(int64_t b, int64_t e, int hv, int co
     return (b * HV * (VD / 16) + (int64_t)hv * (VD / 16) + col / 16) * ss + e * 16 + col % 16;
 }
 
+// Segment-parallel state recurrence of one long sequence (B == 1, no
+// cu_seqlens): nseg segments of seg_tok tokens (the last one may be
+// shorter), the maps of segments [0, nseg - 1) in `maps`
+// ([nseg - 1, HV, K, V + K] fp32), the state entering every segment in
+// `hstart` ([nseg, HV, V, K] fp32) and the segment offsets in `cu`
+// ([nseg + 1] int32), all in caller-owned device memory.
+struct ScanParams {
+    ChunkParams p;
+    int64_t nseg, seg_tok;
+    float *maps, *hstart;
+    int32_t *cu;
+};
+
+// Enqueues the segment maps and the scan over segments (not the chunk_h pass).
+hipError_t launch_seg_scan(const ScanParams &sp, hipStream_t stream);
+
 hipError_t launch_wy(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_chunk_h(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_chunk_o(const ChunkParams &p, hipStream_t stream);

@@ -1,0 +1,424 @@
+// scan.hip -- segment-parallel form of the inter-chunk state recurrence.
+//
+// Over one chunk c the state update of the chunk_h stage is affine in the
+// state entering it (h is the K x V transpose of the state S):
+//   h <- exp2(gl) h + K^T diag(kdecay) (u - w h)
+//      = D_c h + E_c,  D_c = exp2(gl) I - K^T diag(kdecay) w,
+//                      E_c = K^T diag(kdecay) u
+// (the chunk transition of the WY representation of a product of
+// generalised Householder factors).  Composing the maps of the chunks of a
+// segment gives the segment's map h_end = D h_start + E, so the long serial
+// chain splits into three stages:
+//   1. gdp_seg_map_k: every segment (in parallel) runs the recurrence on the
+//      augmented state X = [E | D] (K x (V + K)), started from [0 | I] and
+//      fed [u | 0].  Both halves follow the update above, so at the
+//      segment's end X holds its E and D.
+//   2. gdp_seg_scan_k: per value head, a short serial pass over the
+//      segments: h_start[s+1] = D_s h_start[s] + E_s, from the caller's
+//      initial state.
+//   3. the chunk_h stage, all segments at once, each from its h_start (the
+//      segments are handed to it as packed sequences with initial states).
+// Only the last stage writes h and v_new.
+#include "gdp_common.h"
+#include "gdp_internal.h"
+
+#include <type_traits>
+
+namespace gdp {
+
+namespace {
+constexpr int C = 64;
+}  // namespace
+
+// K index held by slot i (= 4 lg + q) of the map kernel's state tile kt.
+__device__ __forceinline__ int kperm(int kt, int i) { return 32 * (kt >> 1) + 8 * (i >> 2) + 4 * (kt & 1) + (i & 3); }
+
+// LDS ring of the map kernel, NS stages of one chunk each, grouped by tile
+// so that every fragment read is one per-lane offset register plus a
+// compile-time offset below 64 KiB: the w and K tiles (rows of KD
+// elements, 16-byte units XOR-swizzled by row), the u tile in 16-column
+// slices as in HBM, and the per-row key decays and cumulative decays.
+template <int KD, int VD, int NS>
+struct MapRing {
+    bf16 w[NS][64 * KD];
+    bf16 k[NS][64 * KD];
+    bf16 u[NS][VD / 16][64 * 16];
+    float kd[NS][64];
+    float gc[NS][64];
+};
+
+// One block of (KD + VD) / 32 waves per (segment, value head); wave wv owns
+// columns [32 wv, 32 wv + 32) of X for the whole segment, as fp32 result
+// tiles in a permuted K order: xs[kt][ct][q] holds X[kperm(kt, 4 lg + q)]
+// [32 wv + 16 ct + lc] with kperm(kt, i) = 32(kt/2) + 8(i/4) + 4(kt%2) +
+// i%4, so that the bf16 copy of tiles 2ks and 2ks+1 holds 8 consecutive K
+// indices per lane and the w operand of phase 1 is one 16-byte row read.
+// Columns below VD are E (fed by u), the others D.  Each chunk streams from
+// HBM straight into the three-stage LDS ring (buffer loads with the LDS as
+// destination, issued two chunks ahead and shared out over all waves), so a
+// chunk's loads have two steps to land and hold no registers.
+template <int KD, int VD>
+__global__ void __launch_bounds__((KD + VD) * 2)
+gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
+              const bf16 *__restrict__ u, const float *__restrict__ gcum, int64_t Ttok, int64_t seg_tok,
+              int nmap, int H, int HV, int M, int64_t uv_ss, float *__restrict__ maps) {
+    constexpr int XW = KD + VD;            // columns of X
+    constexpr int NW = XW / 32;            // waves
+    constexpr int NKT = KD / 16;           // 16-row tiles of X
+    constexpr int NKS = KD / 32;           // phase-1 contraction steps
+    constexpr int RB = KD * 2;             // bytes per tile row
+    constexpr int UPR = RB / 16;           // 16-byte units per tile row
+    constexpr int TS = 64 * RB;            // bytes per w or K tile
+    constexpr int US = 64 * VD * 2;        // bytes per u tile
+    constexpr int NIT = TS / 1024;         // 1 KiB DMA instructions per w or K tile
+    constexpr int NIU = US / 1024;         // per u tile
+    constexpr int NI = 2 * NIT + NIU;      // per chunk, shared out over the waves
+    constexpr int NIW = NI / NW;           // issued by every wave (some issue one more)
+    constexpr int NJ = (NI + NW - 1) / NW; // instruction slots per wave
+    constexpr int NS = 3;                  // ring stages: loads run two chunks ahead
+    typedef MapRing<KD, VD, NS> Ring;
+    constexpr int OW = (int)__builtin_offsetof(Ring, w), OK = (int)__builtin_offsetof(Ring, k);
+    constexpr int OU = (int)__builtin_offsetof(Ring, u), OD = (int)__builtin_offsetof(Ring, kd);
+    constexpr int OG = (int)__builtin_offsetof(Ring, gc);
+    static_assert(XW % 32 == 0 && NKS >= 1 && NIW >= 1, "shape");
+    static_assert(2 * TS + 16 * RB * 3 < 65536 && 2 * US + US < 65536, "fragment offsets fit 16 bits");
+
+    __shared__ __attribute__((aligned(16))) Ring ring;
+
+    const int s = (int)(blockIdx.x / HV);
+    const int hv = (int)(blockIdx.x % HV);
+    if (s >= nmap) return;
+    const int hk = hv / (HV / H);
+    const int64_t TM = Ttok * M;
+    const int64_t r0 = (int64_t)s * seg_tok * M;  // first expanded row of the segment
+    const int nch = (int)(seg_tok * M / 64);      // s < nmap: a whole segment, whole chunks
+
+    const int lane = lane_id(), wv = wave_id();
+    const int lg = lane >> 4, lc = lane & 15, j = lane & 15;
+    const bool is_e = 32 * wv < VD;               // wave-uniform
+    const uint32_t ring0 = lds_addr(&ring);
+    const char *lds = (const char *)&ring;
+
+    // ---- per-lane fragment offsets (bytes from the ring), fixed for the kernel
+    // phase 1, w[16rt + lc][32ks + 8lg .. +7] (one unit): o1[ks] + st TS + rt 16 RB
+    uint32_t o1[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) o1[ks] = (uint32_t)(OW + lc * RB + ((((4 * ks + lg) ^ lc) & (UPR - 1)) << 4));
+    // phase 2, K read transposed: source lane j of group lg points at row
+    // 4lg + j/4 (+ 32s + 16h), columns kperm(kt, 0) + 8(j%4) .. +3 (half a
+    // unit), so output lane i receives column kperm(kt, i):
+    // o2[kt] + st TS + (32s + 16h) RB
+    uint32_t o2[NKT];
+    const int ra0 = 4 * lg + (j >> 2);
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+        o2[kt] = (uint32_t)(OK + ra0 * RB + ((((4 * (kt >> 1) + (j & 3)) ^ ra0) & (UPR - 1)) << 4) + 8 * (kt & 1));
+    // u slice 2wv + ct, rows 16rt + 4lg + j/4, columns 4(j%4): ou + st US + ct 2048 + rt 512
+    const uint32_t ou = (uint32_t)(OU + (is_e ? 2 * wv : 0) * 2048 + (4 * lg + (j >> 2)) * 32 + 8 * (j & 3));
+    const uint32_t okd = (uint32_t)(OD + 16 * lg);
+
+    // ---- DMA slots of this wave: instruction i = wv + NW jj of a chunk.
+    // Instruction ii of a w or K tile fills LDS bytes [1024 ii, 1024 ii + 1024)
+    // of the tile: lane L's 16 bytes at 1024 ii + 16 L hold unit (L mod UPR)
+    // of row (1024 ii + 16 L) / RB after the swizzle, so the lane fetches the
+    // source unit that the swizzle puts there.
+    const int64_t ldw_b = (int64_t)HV * KD * 2, ldk_b = (int64_t)H * KD * 2;  // row strides (bytes)
+    uint32_t goff[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+        const int i = wv + NW * jj;
+        if (i < 2 * NIT) {
+            const int t = i / NIT, ii = i % NIT;
+            const int byte = 1024 * ii + 16 * lane;
+            const int r = byte / RB, us = (byte % RB) / 16;
+            goff[jj] = (uint32_t)(r * (t ? ldk_b : ldw_b) + 16 * ((us ^ r) & (UPR - 1)));
+        } else {
+            goff[jj] = (uint32_t)(1024 * ((i - 2 * NIT) % 2) + 16 * lane);
+        }
+    }
+    auto issue = [&](int c, auto stc) {
+        constexpr int st = decltype(stc)::value;
+        const int64_t e0 = r0 + 64LL * c;
+        const rsrc_t rw = make_rsrc(w + (e0 * HV + hv) * KD, (uint32_t)(63 * ldw_b + RB));
+        const rsrc_t rk = make_rsrc(k + (e0 * H + hk) * KD, (uint32_t)(63 * ldk_b + RB));
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            const int i = wv + NW * jj;  // wave-uniform
+            if (i >= NI) break;
+            if (i < 2 * NIT) {
+                const int t = i / NIT, ii = i % NIT;
+                dma16(t ? rk : rw, goff[jj], ring0 + (uint32_t)((t ? OK : OW) + st * TS + 1024 * ii));
+            } else {
+                const int iu = i - 2 * NIT, sl = iu / 2;  // slice sl, rows 32 (iu % 2) ..
+                const rsrc_t ru = make_rsrc(u + ((int64_t)hv * (VD / 16) + sl) * uv_ss + e0 * 16, 64 * 32);
+                dma16(ru, goff[jj], ring0 + (uint32_t)(OU + st * US + 2048 * sl + 1024 * (iu % 2)));
+            }
+        }
+        if (wv == 0)
+            dma4(make_rsrc(kdecay + (int64_t)hv * TM + e0, 256), (uint32_t)(4 * lane), ring0 + OD + st * 256);
+        if (wv == NW - 1)
+            dma4(make_rsrc(gcum + (int64_t)hv * TM + e0, 256), (uint32_t)(4 * lane), ring0 + OG + st * 256);
+    };
+
+    // X = [0 | I]
+    f32x4 xs[NKT][2];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = kperm(kt, 4 * lg + q), col = 32 * wv + 16 * ct + lc;
+                xs[kt][ct][q] = (col - VD == row) ? 1.f : 0.f;
+            }
+    // phase-1 operand: xb[ks][ct] holds X rows 32ks + 8lg + i (slot i) of
+    // column 32wv + 16ct + lc
+    bf16x8 xb[NKS][2];
+    auto pack = [&]() {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    xb[ks][ct][q] = (bf16)xs[2 * ks][ct][q];
+                    xb[ks][ct][4 + q] = (bf16)xs[2 * ks + 1][ct][q];
+                }
+    };
+    pack();
+
+    // one chunk on ring stage ST (compile-time, so every LDS offset is an
+    // immediate on top of the per-lane registers above)
+    auto step = [&](int c, auto stc) {
+        constexpr int ST = decltype(stc)::value;
+        const bool more = c + 2 < nch;  // uniform
+        if (more) issue(c + 2, std::integral_constant<int, (ST + 2) % NS>{});
+
+        // phase 1: P = w X (64 x 32), contraction order of xb
+        f32x4 acc[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 a = *(const bf16x8 *)(lds + o1[ks] + (ST * TS + rt * 16 * RB));
+                if (ks == 0) {
+                    acc[rt][0] = mma(a, xb[0][0], zero4());
+                    acc[rt][1] = mma(a, xb[0][1], zero4());
+                } else {
+                    acc[rt][0] = mma(a, xb[ks][0], acc[rt][0]);
+                    acc[rt][1] = mma(a, xb[ks][1], acc[rt][1]);
+                }
+            }
+        }
+        // (u | 0) - P, scaled per row by the key decay, as the phase-2 operand:
+        // vb[s][ct] holds rows 32s + 4lg + q (slots 0-3), 32s + 16 + 4lg + q (4-7)
+        bf16x8 vb[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 kd4 = *(const f32x4 *)(lds + okd + (ST * 256 + rt * 64));
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                bf16x4 uu = bf16x4{};
+                if (is_e)
+                    uu = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(lds + ou) +
+                                      (ST * US + ct * 2048 + rt * 512))));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    vb[rt >> 1][ct][4 * (rt & 1) + q] = (bf16)(((float)uu[q] - acc[rt][ct][q]) * kd4[q]);
+            }
+        }
+        const float gl = __builtin_amdgcn_exp2f(ring.gc[ST][63]);  // the chunk's decay (<= 1)
+        // phase 2: X = exp2(gl) X + K^T (kd (u - P))
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xs[kt][ct][q] *= gl;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                typedef __attribute__((address_space(3))) const char *lp;
+                const lp pk = (lp)(lds + o2[kt]);
+                const bf16x4 x0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(pk + (ST * TS + 32 * s2 * RB))));
+                const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(pk + (ST * TS + (32 * s2 + 16) * RB))));
+                const bf16x8 a = join<bf16>(x0, x1);
+                xs[kt][0] = mma(a, vb[s2][0], xs[kt][0]);
+                xs[kt][1] = mma(a, vb[s2][1], xs[kt][1]);
+            }
+        }
+        pack();
+        // chunk c + 1 landed: wait for all but this step's own DMAs
+        if (more)
+            wait_vmcnt<NIW>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();  // orders LDS only: the DMAs of chunk c + 2 stay in flight
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    issue(0, I0{});
+    if (nch > 1) issue(1, I1{});
+    wait_vmcnt<0>();
+    lds_barrier();
+    for (int c = 0; c < nch; c += 3) {
+        step(c, I0{});
+        if (c + 1 < nch) step(c + 1, I1{});
+        if (c + 2 < nch) step(c + 2, I2{});
+    }
+
+    // the segment's map, rows of X: [E (VD) | D (KD)]
+    float *dst = maps + ((int64_t)s * HV + hv) * KD * XW;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dst[(int64_t)kperm(kt, 4 * lg + q) * XW + 32 * wv + 16 * ct + lc] = xs[kt][ct][q];
+}
+
+// One block of KD / 32 waves per (value head, 16 value columns): the state
+// slice h[k][j0 .. j0+16) in LDS, carried over the segments in fp32:
+// hstart[s] is the state S entering segment s ([nseg, HV, VD, KD], the
+// layout of initial states), hstart[s+1] = D_s hstart[s] + E_s.  The product
+// runs on fp32 matrix-core tiles (16x16x4): wave w owns rows
+// [32 w, 32 w + 32) of the result.  D_s is staged in LDS by coalesced loads;
+// the maps travel through two register sets, each loaded two segments ahead
+// of its use.  Block 0 also writes the segment offsets cu[0..nseg] (tokens).
+template <int KD, int VD>
+__global__ void __launch_bounds__(KD * 2)
+gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int nseg, int HV, int64_t seg_tok,
+               int64_t Ttok, float *__restrict__ hstart, int32_t *__restrict__ cu) {
+    constexpr int XW = KD + VD;
+    constexpr int NT = KD * 2;       // threads
+    constexpr int CB = 16;           // value columns per block
+    constexpr int DU = KD * KD / 4;  // float4 units of D
+    constexpr int NDU = DU / NT;     // per thread
+    constexpr int LDD = KD + 4;      // LDS row stride of D (floats)
+    constexpr int SL = VD / CB;      // slices per head
+    __shared__ __attribute__((aligned(16))) float Ds[KD * LDD];
+    __shared__ __attribute__((aligned(16))) float Hs[KD * CB];
+
+    // block -> (value head, slice): the slices of one head share an XCD
+    // (blocks i and i + 8 do), so each D_s comes from HBM once per head and
+    // from that XCD's L2 for the other slices
+    const int slot = (int)(blockIdx.x / 8), xcd = (int)(blockIdx.x % 8);
+    const int hv = (slot / SL) * 8 + xcd;
+    const int j0 = (slot % SL) * CB;
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid <= nseg) {
+        const int64_t t = (int64_t)tid * seg_tok;
+        cu[tid] = (int32_t)(t < Ttok ? t : Ttok);
+    }
+    if (hv >= HV) return;
+    const int lane = lane_id(), wv = wave_id();
+    const int lg = lane >> 4, lc = lane & 15;
+
+    // the map of segment s in flight in registers: this thread's share of D_s
+    // (coalesced) and its result tiles' entries of E_s
+    struct MapRegs {
+        f32x4 d[NDU];
+        f32x4 e[2];
+    };
+    auto load_map = [&](MapRegs &R, int s) {
+        const float *m = maps + ((int64_t)s * HV + hv) * KD * XW;
+#pragma unroll
+        for (int i = 0; i < NDU; ++i) {
+            const int id = tid + NT * i, r = id / (KD / 4), c4 = id % (KD / 4);
+            R.d[i] = *(const f32x4 *)(m + (int64_t)r * XW + VD + 4 * c4);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) R.e[t][q] = m[(int64_t)(32 * wv + 16 * t + 4 * lg + q) * XW + j0 + lc];
+    };
+    // state rows are written out by (row, 8 columns) per thread: coalesced over rows
+    auto write_state = [&](int s) {
+        float *out = hstart + ((int64_t)s * HV + hv) * VD * KD;
+        const int k = tid % KD, c0 = (tid / KD) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[(int64_t)(j0 + c0 + i) * KD + k] = Hs[k * CB + c0 + i];
+    };
+    // initial state (S = h^T, V x K)
+    {
+        const int k = tid % KD, c0 = (tid / KD) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Hs[k * CB + c0 + i] = h0 ? h0[((int64_t)hv * VD + j0 + c0 + i) * KD + k] : 0.f;
+    }
+    const int nm = nseg - 1;  // maps to apply
+    MapRegs R0, R1;
+    if (nm > 0) load_map(R0, 0);
+    if (nm > 1) load_map(R1, 1);
+    // state entering segment s -> hstart[s], then apply map s (from R).  The
+    // next loads into R are issued before this step's stores, so the wait
+    // before storing a set into LDS leaves the other set in flight; the
+    // barriers order LDS only.
+    auto step = [&](int s, MapRegs &R) {
+        lds_barrier();  // Hs holds the state entering segment s; Ds is free
+#pragma unroll
+        for (int i = 0; i < NDU; ++i) {
+            const int id = tid + NT * i, r = id / (KD / 4), c4 = id % (KD / 4);
+            *(f32x4 *)(&Ds[r * LDD + 4 * c4]) = R.d[i];
+        }
+        f32x4 acc[2] = {R.e[0], R.e[1]};
+        if (s + 2 < nm) load_map(R, s + 2);  // in flight for two segments
+        write_state(s);
+        lds_barrier();  // Ds holds D_s
+        // acc[t] += D[32wv + 16t + .., 4ks + ..] h[4ks + .., ..]: lane holds
+        // A[lc][lg] = D[row][4ks + lg] and B[lg][lc] = h[4ks + lg][lc]
+#pragma unroll 8
+        for (int ks = 0; ks < KD / 4; ++ks) {
+            const float b = Hs[(4 * ks + lg) * CB + lc];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float a = Ds[(32 * wv + 16 * t + lc) * LDD + 4 * ks + lg];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
+            }
+        }
+        lds_barrier();  // every wave has read Hs and Ds
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Hs[(32 * wv + 16 * t + 4 * lg + q) * CB + lc] = acc[t][q];
+    };
+    int s = 0;
+    for (; s + 1 < nm; s += 2) {
+        step(s, R0);
+        step(s + 1, R1);
+    }
+    if (s < nm) step(s, R0);
+    lds_barrier();
+    write_state(nm);  // the state entering the last segment
+}
+
+template <int KD, int VD>
+static hipError_t launch_scan_t(const ScanParams &sp, hipStream_t stream) {
+    const gdp_chunk_args &a = sp.p.a;
+    if (sp.nseg > 1) {
+        hipLaunchKernelGGL((gdp_seg_map_k<KD, VD>), dim3((unsigned)((sp.nseg - 1) * a.HV)), dim3((KD + VD) * 2), 0,
+                           stream, (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.T,
+                           sp.seg_tok, sp.nseg - 1, a.H, a.HV, a.M, sp.p.uv_ss, sp.maps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((gdp_seg_scan_k<KD, VD>), dim3((unsigned)((a.HV + 7) / 8 * 8 * (VD / 16))), dim3(KD * 2), 0,
+                       stream, sp.maps,
+                       a.h0, sp.nseg, a.HV, sp.seg_tok, a.T, sp.hstart, sp.cu);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_scan(const ScanParams &sp, hipStream_t stream) {
+    const gdp_chunk_args &a = sp.p.a;
+    if (a.K == 128 && a.V == 128) return launch_scan_t<128, 128>(sp, stream);
+    if (a.K == 128 && a.V == 64) return launch_scan_t<128, 64>(sp, stream);
+    if (a.K == 64 && a.V == 128) return launch_scan_t<64, 128>(sp, stream);
+    if (a.K == 64 && a.V == 64) return launch_scan_t<64, 64>(sp, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdp

@@ -334,6 +334,52 @@ typedef struct gdp_prepare_args {
 gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_args *a, int32_t num_segments,
                                      float *state_workspace, void *const *chunk_h_events, void *stream);
 
+/*
+ * gdp_chunk_fwd_scan -- the same results as gdp_chunk_fwd for one long
+ * sequence (B == 1, cu_seqlens == NULL), within rounding, with the serial
+ * chunk_h chain cut into segments that run in parallel.  Over one chunk the
+ * state update is affine in the entering state (the chunk transition of the
+ * WY representation of the product of the chunk's generalised Householder
+ * factors, core.ssm.ops.gdp.wy_fast and the chunk_h stage of
+ * core.ssm.ops.gdp.chunk_o), so each segment's map h -> D h + E is
+ * composed first, all segments at once; a short serial pass over the
+ * segments then gives the state entering each of them, and one chunk_h pass
+ * runs every segment from its own entering state.  All work is enqueued on
+ * `stream`, in this order: gdp_recompute_w_u; the segment maps (kernel
+ * gdp_seg_map_k); the scan over segments (gdp_seg_scan_k); chunk_h;
+ * gdp_chunk_o; and, if ht is given, a device copy of the final state.
+ *   num_segments    1..GDP_SCAN_MAX_SEGMENTS requested; the sequence is cut
+ *                   into segments of ceil(ceil(T/64) / num_segments) * 64
+ *                   tokens (gdp_scan_segments gives how many result).
+ *   workspace       device memory of at least gdp_scan_workspace_bytes(...)
+ *                   bytes, 256-byte aligned, caller-owned; its contents on
+ *                   entry do not matter and on return are unspecified.
+ *   stage_events    NULL, or 3 hipEvent_t handles (as void *) recorded on
+ *                   `stream` right before the segment maps, right before
+ *                   the chunk_h launch (after the scan) and right after it
+ *                   (for timing those stages).
+ * Every tensor of `a` is as for gdp_chunk_fwd.  w, u, k_rnorm, gcum and
+ * kdecay are bit-identical to gdp_chunk_fwd, and so are h, v_new and o over
+ * the first segment; the states entering later segments come out of the
+ * composed maps, so h, v_new, o and ht there agree with gdp_chunk_fwd to
+ * rounding (the
+ * composition runs on bf16 matrix-core operands with fp32 accumulation,
+ * like the chunk recurrence itself).  Supported: dtype bf16 with K, V in
+ * {64, 128}; other shapes return GDP_ERR_UNSUPPORTED.
+ */
+#define GDP_SCAN_MAX_SEGMENTS 64
+gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
+                              int64_t workspace_bytes, void *const *stage_events, void *stream);
+
+/* Segments gdp_chunk_fwd_scan runs for T tokens and num_segments requested
+   (0 for T == 0), or -1 on bad arguments. */
+int32_t gdp_scan_segments(int64_t T, int32_t num_segments);
+
+/* Workspace bytes gdp_chunk_fwd_scan needs: per value head, a K x (V + K)
+   fp32 map for every segment but the last and a V x K fp32 state for every
+   segment, plus the segment offsets; -1 on bad arguments. */
+int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, int32_t num_segments);
+
 /* Segments gdp_chunk_fwd_pipelined actually runs for T tokens (whole
    64-token chunks, at most num_segments); 0 for T == 0, -1 on bad
    arguments. */

@@ -32,6 +32,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert {"gdp_prefill_prepare", "gdp_decode_prepare", "gdp_recompute_w_u", "gdp_chunk_h", "gdp_chunk_o",
             "gdp_chunk_fwd", "gdp_chunk_fwd_pipelined", "gdp_pipeline_segments", "gdp_pipeline_plan", "gdp_decode_update",
+            "gdp_chunk_fwd_scan", "gdp_scan_segments", "gdp_scan_workspace_bytes",
             "gdp_num_state_chunks", "gdp_last_error", "gdp_version"} <= set(names)
     L = B.lib()
     for n in names:
@@ -262,3 +263,38 @@ def test_decode_update_empty_and_null():
     assert _dec(S=0, q=None, k=None, v=None, beta=None, g=None, state=None, o=None) == B.GDP_OK
     # with slots the pool may be smaller than n (slots name the rows used)
     assert _dec(n=0, pool=0, slots=0x80000, q=None, k=None, v=None, beta=None, state=None, o=None) == B.GDP_OK
+
+
+def test_scan_rejects_and_plan():
+    """gdp_chunk_fwd_scan refuses what it does not run before launching
+    anything; the segment plan and workspace size follow the header."""
+    L = B.lib()
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 40
+    a = lambda **kw: ctypes.byref(_args(**dict(dict(K=128, V=128), **kw)))
+    assert L.gdp_chunk_fwd_scan(a(B=2, h_chunks=4), 4, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(cu_seqlens=0x1000, num_seqs=1), 4, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(), 0, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(), 65, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(), 2, None, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(), 2, ctypes.c_void_p(0x100010), big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(), 2, ws, 1024, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(q=None), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(dtype=B.GDP_F32, K=64, V=64), 2, ws, big, None, None) == B.GDP_ERR_UNSUPPORTED
+    assert L.gdp_chunk_fwd_scan(ctypes.byref(_args(K=128, V=256)), 2, ws, big, None, None) == B.GDP_ERR_UNSUPPORTED
+    assert B.lib().gdp_last_error()
+    # T == 0 launches nothing and needs no workspace
+    assert L.gdp_chunk_fwd_scan(a(T=0), 2, None, 0, None, None) == B.GDP_OK
+    # segments of ceil(ceil(T/64) / n) chunks; the last may be shorter
+    assert B.scan_segments(32768, 16) == 16
+    assert B.scan_segments(1000, 3) == 3     # 16 chunks -> 6, 6, 4
+    assert B.scan_segments(1000, 7) == 6     # 16 chunks -> 3 each, 6 segments
+    assert B.scan_segments(100, 64) == 2
+    assert B.scan_segments(0, 4) == 0
+    assert L.gdp_scan_segments(10, 0) == -1 and L.gdp_scan_segments(10, 65) == -1
+    # maps of all segments but the last, one state per segment, the offsets
+    up = lambda x: (x + 255) // 256 * 256
+    HV, K, V = 16, 128, 128
+    want = up(15 * HV * K * (K + V) * 4) + up(16 * HV * V * K * 4) + up(17 * 4)
+    assert L.gdp_scan_workspace_bytes(32768, HV, K, V, 16) == want
+    assert L.gdp_scan_workspace_bytes(32768, HV, K, V, 0) == -1
