@@ -4,8 +4,13 @@
 One step = the whole hot path over one batch of synthetic input, all on the
 GPU through the C ABI of libgdp.so:
     gdp_prefill_prepare      (split / GQA-expand / Householder-fold / gate)
-    gdp_chunk_fwd_pipelined  (recompute_w_u -> chunk_h -> chunk_o over
-                              segments of the sequence: chunk_h runs the
+    gdp_chunk_fwd_scan       (default, --path scan: recompute_w_u; the affine
+                              state map of each of 16 segments, composed in
+                              parallel; a scan over the segments for the
+                              state entering each; chunk_h over all segments
+                              at once; chunk_o)
+ or gdp_chunk_fwd_pipelined  (--path pipelined: recompute_w_u -> chunk_h ->
+                              chunk_o over 3 segments: chunk_h runs the
                               segments in order, handing its fp32 state on,
                               while recompute_w_u of later segments and
                               chunk_o of finished ones run on side streams)
@@ -16,13 +21,14 @@ drawn once (seeded, synthetic) and resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
 dominant kernel (chunk_h: algorithmic bytes per launch / its average launch
-duration from HIP events recorded on its stream around every segment launch,
-vs 8 TB/s HBM; the events record without a system-scope fence, so they do
-not slow the step they time) and the oracle's throughput on the host cores as a reported
-baseline.  --stages adds a sequential (not overlapped) pass that times each
-stage on its own.
+duration from HIP events recorded on its stream around every launch, vs
+8 TB/s HBM; the events record without a system-scope fence, so they do not
+slow the step they time) and the oracle's throughput on the host cores as a
+reported baseline.  --stages adds a sequential (not overlapped) pass that
+times each stage on its own.
 
-    python bench.py [--steps K] [--warmup W] [--segments S] [--stages] [--no-cpu-baseline] [--copy-mib N]
+    python bench.py [--steps K] [--warmup W] [--path scan|pipelined] [--segments S] [--stages]
+                    [--no-cpu-baseline] [--copy-mib N]
 """
 import argparse
 import ctypes
@@ -127,15 +133,16 @@ def decode_bytes(c):
             + n * L * c["HV"] * 8 + n * L * c["HV"] * c["V"] * es)
 
 
-def measured_traffic(kernel, segments):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source with the same pipeline
-    segments (the launch sizes); else None."""
+def measured_traffic(kernel, segments, path):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    the same chunk-forward path, if it was taken on the current kernel source
+    with the same segments (the launch sizes); else None."""
     from gated_delta_product_amd import profiling
-    path = os.path.join(ROOT, "profiles", "traffic_long_prefill_32k.json")
-    if not os.path.exists(path):
+    name = "traffic_long_prefill_32k_scan.json" if path == "scan" else "traffic_long_prefill_32k.json"
+    fn = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(fn):
         return None
-    with open(path) as f:
+    with open(fn) as f:
         t = json.load(f)
     e = t.get(kernel)
     if not e or e.get("src_digest") != profiling.src_digest(kernel) or t.get("_segments") != segments:
@@ -216,7 +223,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--path", choices=["pipelined", "scan"], default="pipelined",
+    ap.add_argument("--path", choices=["pipelined", "scan"], default="scan",
                     help="chunk forward: gdp_chunk_fwd_pipelined or gdp_chunk_fwd_scan")
     ap.add_argument("--segments", type=int, default=None,
                     help="segments of the chunk forward (default %d pipelined, %d scan)" % (SEGMENTS, SCAN_SEGMENTS))
@@ -320,7 +327,7 @@ def main():
     achieved = ch_bytes / (ch_ms / 1e3) / 1e9
     roof = {"kernel": "gdp_chunk_h", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if scan else measured_traffic("gdp_chunk_h", nseg)}
+            "traffic": measured_traffic("gdp_chunk_h", nseg, args.path)}
 
     stages = None
     if args.stages:  # each stage alone, whole workload, for reference

@@ -33,6 +33,8 @@ KERNELS = {
     "gdp_recompute_w_u": ("gdp_wy_k", ["wy.hip"]),
     "gdp_chunk_h": ("gdp_chunk_h_k", ["chunk_h.hip"]),
     "gdp_chunk_o": ("gdp_chunk_o_k", ["chunk_o.hip"]),
+    "gdp_seg_map": ("gdp_seg_map_k", ["scan.hip"]),
+    "gdp_seg_scan": ("gdp_seg_scan_k", ["scan.hip"]),
 }
 COPY_SYMBOL = "copyBuffer"
 
@@ -118,8 +120,9 @@ def main(argv=None):
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--segments", type=int, default=None,
-                   help="pipeline segments of the profiled run: the per-launch bytes of the chunk "
+                   help="segments of the profiled run: the per-launch bytes of the chunk "
                         "stages hold for that split only")
+    t.add_argument("--path", default=None, help="chunk forward of the profiled run (pipelined or scan)")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         digests = ", ".join("%s %s" % (op, src_digest(op)) for op in KERNELS)
@@ -132,6 +135,8 @@ def main(argv=None):
         res["_command"] = a.command
         if a.segments is not None:
             res["_segments"] = a.segments
+        if a.path is not None:
+            res["_path"] = a.path
         with open(a.out, "w") as f:
             json.dump(res, f, indent=1, sort_keys=True)
             f.write("\n")
