@@ -48,17 +48,17 @@ namespace {
 constexpr int C = 64;
 }  // namespace
 
-template <typename T, int KD>
+template <typename T, int KD, int NP>
 struct HStage {
     T w[2][C * (KD / 2)];  // w half tiles [K half], swizzled rows
     T k[2][C * (KD / 2)];  // K half tiles [K half], swizzled rows
-    T u[C * 16];           // u slice, plain rows of 16 elements
+    T u[NP][C * 16];       // u slices, plain rows of 16 elements
     float kd[C];           // key decay factor per row (0 past the end)
     float gc[C];           // cumulative log2 decay per row
 };
 
-template <typename T, int KD, int VD>
-__global__ void __launch_bounds__(320)
+template <typename T, int KD, int VD, int NP>
+__global__ void __launch_bounds__((2 * NP + 3) * 64)
 gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T *__restrict__ w,
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
@@ -74,34 +74,45 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     constexpr int UUPR = 16 * ES / 16;         // 16-byte units per u row
     constexpr int NU = C * UUPR / 64;          // DMA instructions for the u slice
     constexpr int NS = 3;                      // ring stages (prefetch distance 2)
+    // With one column pair the memory waves store the state snapshots from
+    // an LDS staging area; with two, the compute waves store their own (a
+    // 16-byte store per state tile pair), which keeps the block within LDS.
+    constexpr bool SNAP_LDS = NP == 1;
+    constexpr int NX = NP == 1 ? NS : 2;       // exchange buffers (by stage, or by step parity)
     constexpr int NKT = KH / 16;               // 16-row state tiles per compute wave
     constexpr int NKS = KH / 32;               // phase-1 contraction steps per wave
     constexpr int LDT = 64 + 32 / ES;          // row stride of the v_new transpose
     constexpr int LDH = KD + 16 / ES;          // row stride of the snapshot staging
     constexpr int S = VD / 16;                 // column slices per head
-    constexpr int SB = (int)sizeof(HStage<T, KD>);
+    constexpr int SG = S / NP;                 // blocks per head (NP slices each)
+    constexpr int SB = (int)sizeof(HStage<T, KD, NP>);
     // memory wave 0 loads the w halves and kdecay, wave 1 the K halves, u and gcum
-    constexpr int NDMA0 = 2 * UPR + 1, NDMA1 = 2 * UPR + NU + 1;
+    constexpr int NDMA0 = 2 * UPR + 1, NDMA1 = 2 * UPR + NU * NP + 1;
     constexpr int HLPR = KD * ES / 16;         // lanes per snapshot row (16 B each)
     constexpr int HRPI = 64 / HLPR;            // snapshot rows per store instruction
     constexpr int NHS = 8 / HRPI > 0 ? 8 / HRPI : 1;  // snapshot stores per memory wave (8 rows)
     constexpr int NVS = 2;                     // v_new stores per memory wave (32 rows)
     static_assert(NKS >= 1 && (UPR & (UPR - 1)) == 0 && HRPI <= 8, "tile shape");
-    static_assert(NDMA1 + NHS + NVS < 64, "in-flight count must fit the vector memory counter");
+    constexpr int NHS_M = SNAP_LDS ? NHS : 0;  // snapshot stores per memory wave and slice
+    static_assert(NDMA1 + (NHS_M + NVS) * NP < 64, "in-flight count must fit the vector memory counter");
+    static_assert(S % NP == 0, "column pairs per block");
     static_assert(SB % 16 == 0, "stage size");
 
-    __shared__ __attribute__((aligned(16))) HStage<T, KD> ring[NS];
-    __shared__ __attribute__((aligned(16))) f32x4 Xs[NS][2][4][64];   // [stage][wave][row tile][lane]
-    __shared__ __attribute__((aligned(16))) T Vt[2][16 * LDT];        // [parity] v_new, column-major
-    __shared__ __attribute__((aligned(16))) T Hs[2][16 * LDH];        // [parity] snapshot rows (V x K)
+    __shared__ __attribute__((aligned(16))) HStage<T, KD, NP> ring[NS];
+    __shared__ __attribute__((aligned(16))) f32x4 Xs[NX][NP][2][4][64];  // [buffer][pair][wave][row tile][lane]
+    __shared__ __attribute__((aligned(16))) T Vt[2][NP][16 * LDT];       // [parity][pair] v_new, column-major
+    __shared__ __attribute__((aligned(16))) T Hs[SNAP_LDS ? 2 : 1][NP][SNAP_LDS ? 16 * LDH : 8];  // [parity][pair] snapshot rows (V x K)
     __shared__ __attribute__((aligned(16))) char Pf[1024];            // landing area of L2 prefetches
 
-    // ---- block -> (sequence, value head, slice); slices of one head share an XCD
+    // ---- block -> (sequence, value head, slice group); the groups of one
+    // head share an XCD.  Group slg holds the NP slices [NP slg, NP slg + NP):
+    // compute waves 2p and 2p + 1 run slice NP slg + p.
     const int64_t P = nseq * HV;
     const int64_t id = blockIdx.x;
     const int64_t slot = id / 8, xcd = id % 8;
-    const int64_t pair = (slot / S) * 8 + xcd;
-    const int sl = (int)(slot % S);
+    const int64_t pair = (slot / SG) * 8 + xcd;
+    const int slg = (int)(slot % SG);
+    const int sl0 = NP * slg;
     if (pair >= P) return;
     const int64_t seq = pair / HV;
     const int hv = (int)(pair % HV);
@@ -114,6 +125,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 
     const int lane = lane_id(), wave = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
+    const int sl = sl0 + (wave < 2 * NP ? wave >> 1 : 0);  // a compute wave's slice
     // The fp32 state of compute wave kw in its permuted K order (see below):
     // element (kt, q) is S[16sl + lc][kw*KH + 32(kt/2) + 8lg + 4(kt%2) + q],
     // four consecutive K indices per (kt), i.e. one 16-byte unit of h0 / ht.
@@ -121,10 +133,11 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         return ((seq * HV + hv) * (int64_t)VD + 16 * sl + lc) * KD + kw_ * KH + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1);
     };
     if (nch == 0) {  // empty sequence: the final state is the initial one
-        if (ht != nullptr && wave < 2) {
+        if (ht != nullptr && wave < 2 * NP) {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
-                *(f32x4 *)(ht + state_off(wave, kt)) = h0 ? *(const f32x4 *)(h0 + state_off(wave, kt)) : zero4();
+                *(f32x4 *)(ht + state_off(wave & 1, kt)) =
+                    h0 ? *(const f32x4 *)(h0 + state_off(wave & 1, kt)) : zero4();
         }
         return;
     }
@@ -141,21 +154,21 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
     };
 
-    if (wave == 4) {
+    if (wave == 2 * NP + 2) {
         // ======================= prefetch wave =======================
         // Pulls the lines of chunk c + PF into L2 while the memory waves
         // stream chunk c + 2 into LDS, so their loads hit L2 instead of
-        // waiting on HBM.  The S blocks of a head share an XCD (and its L2);
-        // block sl prefetches rows [RPB sl, RPB sl + RPB) of each chunk.  The
-        // data lands in a scratch LDS area that nothing reads.
+        // waiting on HBM.  The SG blocks of a head share an XCD (and its L2);
+        // block slg prefetches rows [RPB slg, RPB slg + RPB) of each chunk.
+        // The data lands in a scratch LDS area that nothing reads.
         constexpr int PF = 5;                    // prefetch distance in chunks
-        constexpr int RPB = C / S;               // rows per block per chunk
+        constexpr int RPB = C / SG;              // rows per block per chunk
         static_assert(RPB * KD * ES / 128 <= 64 && KD * ES >= 128,
                       "one 4-byte load per line must cover a block's rows");
         const uint32_t pf = lds_addr(&Pf[0]);
         const int rbw = KD * ES;  // row bytes of w / k
-        const char *pw = (const char *)(w + ((r0 + RPB * sl) * HV + hv) * KD);
-        const char *pk = (const char *)(k + ((r0 + RPB * sl) * H + hk) * KD);
+        const char *pw = (const char *)(w + ((r0 + RPB * slg) * HV + hv) * KD);
+        const char *pk = (const char *)(k + ((r0 + RPB * slg) * H + hk) * KD);
         const char *pd = (const char *)(kdecay + h0r);
         const char *pg = (const char *)(gcum + h0r);
         const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, st4 = (int64_t)C * 4;
@@ -168,12 +181,12 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         };
         int rem_pf = (int)rows;
         auto prefetch = [&](int c) {
-            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c - RPB * sl));
+            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c - RPB * slg));
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_pf - C * c));
             const int64_t oc = c;
             rows_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, rbw);
             rows_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, rbw);
-            if (sl == 0) {  // 256 contiguous bytes each: one block of the head is enough
+            if (slg == 0) {  // 256 contiguous bytes each: one block of the head is enough
                 dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
                 dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
             }
@@ -190,17 +203,18 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         return;
     }
 
-    if (wave >= 2) {
+    if (wave >= 2 * NP) {
         // ======================= memory waves =======================
-        const int mw = wave - 2;
+        const int mw = wave - 2 * NP;
         const int64_t hroom = h_chunks - cbase;  // chunks whose snapshot fits below h_chunks
         const int hlim = hroom < 0 ? 0 : (hroom > nch ? nch : (int)hroom);
         const uint32_t ring_base = lds_addr(&ring[0]);
-        constexpr int OFW = (int)__builtin_offsetof(HStage<T, KD>, w);
-        constexpr int OFK = (int)__builtin_offsetof(HStage<T, KD>, k);
-        constexpr int OFU = (int)__builtin_offsetof(HStage<T, KD>, u);
-        constexpr int OFD = (int)__builtin_offsetof(HStage<T, KD>, kd);
-        constexpr int OFG = (int)__builtin_offsetof(HStage<T, KD>, gc);
+        typedef HStage<T, KD, NP> Stage;
+        constexpr int OFW = (int)__builtin_offsetof(Stage, w);
+        constexpr int OFK = (int)__builtin_offsetof(Stage, k);
+        constexpr int OFU = (int)__builtin_offsetof(Stage, u);
+        constexpr int OFD = (int)__builtin_offsetof(Stage, kd);
+        constexpr int OFG = (int)__builtin_offsetof(Stage, gc);
         constexpr int HALF = C * KH * ES;  // bytes of one half tile
         // per-lane source offsets inside a chunk, less the DMA's offset in
         // its 4 KiB M0 window; tile t (0: w, 1: K) half hh
@@ -223,7 +237,8 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         const int ldt = mw == 0 ? ldw : ldk;
         const int64_t stt = (int64_t)C * ldt * ES;
         const int64_t bseq = cu ? 0 : seq;  // batch row of the sequence
-        const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * Ttok * M, hv, 16 * sl, HV, VD, uv_ss));
+        const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * Ttok * M, hv, 16 * sl0, HV, VD, uv_ss));
+        const int64_t ssb = uv_ss * ES;  // bytes between consecutive slices of u / v_new
         const char *p4 = mw == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
         const int64_t stu = (int64_t)C * 16 * ES, st4 = (int64_t)C * 4;  // slice bytes per chunk
         const int tile_off = mw == 0 ? OFW : OFK;
@@ -244,12 +259,15 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 });
             });
             if (mw == 1) {
-                const rsrc_t ru = make_rsrc(pu, (uint32_t)(n * 16 * ES));
-                const uint32_t sbu = ring_base + st * SB + OFU;
-                static_for<0, NU>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
-                    dma16_m0<1024 * (i % 4)>(ru, ou[i]);
+                static_for<0, NP>([&](auto pc) {
+                    constexpr int pp = decltype(pc)::value;
+                    const rsrc_t ru = make_rsrc(pu + pp * ssb, (uint32_t)(n * 16 * ES));
+                    const uint32_t sbu = ring_base + st * SB + OFU + pp * (C * 16 * ES);
+                    static_for<0, NU>([&](auto ic) {
+                        constexpr int i = decltype(ic)::value;
+                        if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
+                        dma16_m0<1024 * (i % 4)>(ru, ou[i]);
+                    });
                 });
             }
             dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
@@ -259,36 +277,42 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             rem_issue -= C;
         };
 
-        // snapshot of the state entering chunk c: rows [8mw, 8mw + 8) of the
-        // V slice, from Hs[c & 1]
-        char *ph = (char *)(hout + (cbase * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl) * KD);
+        // snapshot of the state entering chunk c: rows [8mw, 8mw + 8) of each
+        // of the block's V slices, from Hs[c & 1]
+        char *ph = (char *)(hout + (cbase * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl0) * KD);
         const int64_t sth = (int64_t)HV * VD * KD * ES;
         auto store_h = [&](int c) {
-            const rsrc_t rh = make_rsrc(ph, c < hlim ? (uint32_t)(16 * KD * ES) : 0u);
-            const T *src = Hs[c & 1];
+            const rsrc_t rh = make_rsrc(ph, c < hlim ? (uint32_t)(NP * 16 * KD * ES) : 0u);
 #pragma unroll
-            for (int i = 0; i < NHS; ++i) {
-                const int r = 8 * mw + i * HRPI + lane / HLPR;
-                const int e = (lane % HLPR) * (16 / ES);
-                const uint4 val = *(const uint4 *)(src + r * LDH + e);
-                buf_store16(rh, (uint32_t)((r * KD + e) * ES), val);
+            for (int pp = 0; pp < NP; ++pp) {
+                const T *src = Hs[SNAP_LDS ? (c & 1) : 0][pp];
+#pragma unroll
+                for (int i = 0; i < NHS; ++i) {
+                    const int r = 8 * mw + i * HRPI + lane / HLPR;
+                    const int e = (lane % HLPR) * (16 / ES);
+                    const uint4 val = *(const uint4 *)(src + r * LDH + e);
+                    buf_store16(rh, (uint32_t)(((pp * 16 + r) * KD + e) * ES), val);
+                }
             }
             ph += sth;
         };
         // v_new rows [32mw, 32mw + 32) of chunk c, from Vt[c & 1]
-        char *pv = (char *)(v_new + uv_index(bseq, r0 - bseq * Ttok * M, hv, 16 * sl, HV, VD, uv_ss));
+        char *pv = (char *)(v_new + uv_index(bseq, r0 - bseq * Ttok * M, hv, 16 * sl0, HV, VD, uv_ss));
         int rem_v = (int)rows;
         auto store_v = [&](int c) {
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_v));
-            const rsrc_t rv = make_rsrc(pv, (uint32_t)(n * 16 * ES));
 #pragma unroll
-            for (int r2 = 0; r2 < NVS; ++r2) {
-                const HalfT o4v = lds_col4<T>(Vt[c & 1], LDT, 4 * lg, 32 * mw + 16 * r2);
-                const uint32_t off = (uint32_t)(((32 * mw + 16 * r2 + lc) * 16 + 4 * lg) * ES);
-                if constexpr (ES == 2)
-                    buf_store8(rv, off, __builtin_bit_cast(uint2, o4v));
-                else
-                    buf_store16(rv, off, __builtin_bit_cast(uint4, o4v));
+            for (int pp = 0; pp < NP; ++pp) {
+                const rsrc_t rv = make_rsrc(pv + pp * ssb, (uint32_t)(n * 16 * ES));
+#pragma unroll
+                for (int r2 = 0; r2 < NVS; ++r2) {
+                    const HalfT o4v = lds_col4<T>(Vt[c & 1][pp], LDT, 4 * lg, 32 * mw + 16 * r2);
+                    const uint32_t off = (uint32_t)(((32 * mw + 16 * r2 + lc) * 16 + 4 * lg) * ES);
+                    if constexpr (ES == 2)
+                        buf_store8(rv, off, __builtin_bit_cast(uint2, o4v));
+                    else
+                        buf_store16(rv, off, __builtin_bit_cast(uint4, o4v));
+                }
             }
             pv += stu;
             rem_v -= C;
@@ -301,16 +325,18 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             wait_vmcnt<ND>();  // chunk 0 landed
             lds_barrier();     // publishes stage 0 and the zero snapshot
             for (int c = 0; c < nch; ++c) {
+                // chunk c + 2 into the stage that chunk c - 1 left (its tiles
+                // went to registers before the last barrier)
                 issue((c + 2) % NS);
                 // chunk c + 1 landed: count what was issued after its DMAs
                 if (c == 0)
                     wait_vmcnt<ND>();
                 else if (c == 1)
-                    wait_vmcnt<ND + NHS>();
+                    wait_vmcnt<ND + NHS_M * NP>();
                 else
-                    wait_vmcnt<ND + NHS + NVS>();
+                    wait_vmcnt<ND + (NHS_M + NVS) * NP>();
                 lds_barrier();  // compute step c's exchange; publishes stage c + 1
-                store_h(c);
+                if constexpr (SNAP_LDS) store_h(c);
                 if (c >= 1) store_v(c - 1);
             }
             lds_barrier();  // v_new of the last chunk is in Vt
@@ -326,8 +352,9 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 
     // ======================= compute waves =======================
     // (instantiated per wave so every wave-dependent offset is a constant)
-    auto compute = [&](auto kwc) {
-    constexpr int kw = decltype(kwc)::value;
+    auto compute = [&](auto wc) {
+    constexpr int kw = decltype(wc)::value & 1;   // K half of the slice
+    constexpr int pp = decltype(wc)::value >> 1;  // column pair of the block
     // State slice of this wave, in a permuted K order: hs[kt][q] holds h at
     // K index kw*KH + kperm(kt, 4lg + q), column 16sl + lc, with
     //   kperm(kt, i) = 32(kt/2) + 8(i/4) + 4(kt%2) + i%4,
@@ -346,7 +373,22 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             hb[ks][q] = from_f32<T>(hs[2 * ks][q]);
             hb[ks][4 + q] = from_f32<T>(hs[2 * ks + 1][q]);
         }
-    auto put_snapshot = [&](T *dst) {
+    // the state entering chunk cc: staged in LDS for the memory waves, or
+    // stored straight to h (16 bytes per lane and tile pair; none at or past
+    // h_chunks)
+    const int64_t hroom_c = h_chunks - cbase;
+    const int hlim_c = hroom_c < 0 ? 0 : (hroom_c > nch ? nch : (int)hroom_c);
+    auto put_snapshot = [&](int cc) {
+        if constexpr (!SNAP_LDS) {
+            const T *base = hout + ((cbase + cc) * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl) * KD;
+            const rsrc_t rh = make_rsrc(base, cc < hlim_c ? (uint32_t)(16 * KD * ES) : 0u);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                buf_store16(rh, (uint32_t)((lc * KD + kw * KH + 32 * ks + 8 * lg) * ES),
+                            __builtin_bit_cast(uint4, hb[ks]));
+            return;
+        }
+        T *dst = Hs[SNAP_LDS ? (cc & 1) : 0][pp];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             T *p = dst + lc * LDH + kw * KH + 32 * ks + 8 * lg;
@@ -364,7 +406,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             }
         }
     };
-    put_snapshot(Hs[0]);  // h[0]: the initial state
+    put_snapshot(0);  // h[0]: the initial state
     lds_barrier();        // stage 0 landed
     int rem = (int)rows;  // rows left from the current chunk
 
@@ -372,7 +414,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     // address below is a fixed offset from a per-lane base).
     auto step = [&](int c, auto stc) {
         constexpr int ST = decltype(stc)::value;
-        const HStage<T, KD> &Sg = ring[ST];
+        const HStage<T, KD, NP> &Sg = ring[ST];
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // uniform
 
         // phase 1: partial w h over this wave's half of K (w columns
@@ -401,7 +443,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         f32x4 kd4[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            uu[rt] = lds_col4<T>(Sg.u, 16, 16 * rt + 4 * lg, 0);
+            uu[rt] = lds_col4<T>(Sg.u[pp], 16, 16 * rt + 4 * lg, 0);
             kd4[rt] = *(const f32x4 *)(&Sg.kd[16 * rt + 4 * lg]);
         }
         const float glast = Sg.gc[n > 0 ? n - 1 : 0];
@@ -452,18 +494,21 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
             for (int q = 0; q < 4; ++q) hs[kt][q] *= gl;
 
-        // exchange partials (one buffer per ring stage; the step's barrier)
+        // exchange partials (one buffer per ring stage, or by step parity
+        // with two column pairs: the partner reads a buffer before the next
+        // barrier, and it is written again two barriers later)
+        const int xb = NP == 1 ? ST : (c & 1);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) Xs[ST][kw][rt][lane] = acc[rt];
+        for (int rt = 0; rt < 4; ++rt) Xs[xb][pp][kw][rt][lane] = acc[rt];
         lds_barrier();
 
         // v_new = (u - own) - other; the phase-2 operand kd * v_new as one
         // fused multiply-add on the precomputed kd * (u - own)
         FragT vb[2];
-        T *vt = Vt[c & 1];
+        T *vt = Vt[c & 1][pp];
         static_for<0, 4>([&](auto rtc) {
             constexpr int rt = decltype(rtc)::value;
-            const f32x4 other = Xs[ST][kw ^ 1][rt][lane];
+            const f32x4 other = Xs[xb][pp][kw ^ 1][rt][lane];
             HalfT v4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -486,7 +531,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 hb[ks][q] = from_f32<T>(hs[2 * ks][q]);
                 hb[ks][4 + q] = from_f32<T>(hs[2 * ks + 1][q]);
             }
-        put_snapshot(Hs[(c + 1) & 1]);  // the state entering chunk c + 1
+        if (SNAP_LDS || c + 1 < nch) put_snapshot(c + 1);  // the state entering chunk c + 1
         rem -= C;
     };
 
@@ -507,20 +552,39 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     };
     if (wave == 0)
         compute(std::integral_constant<int, 0>{});
-    else
+    else if (wave == 1 || NP == 1)
         compute(std::integral_constant<int, 1>{});
+    else if constexpr (NP == 2) {
+        if (wave == 2)
+            compute(std::integral_constant<int, 2>{});
+        else
+            compute(std::integral_constant<int, 3>{});
+    }
 }
 
-template <typename T, int KD, int VD>
-static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
+template <typename T, int KD, int VD, int NP>
+static hipError_t launch_chunk_h_np(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
     const int64_t P = p.nseq * a.HV;
-    const int64_t S = VD / 16;
-    const int64_t nblk = ((P + 7) / 8) * 8 * S;
-    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD>), dim3((unsigned)nblk), dim3(320), 0, stream,
+    const int64_t SG = VD / 16 / NP;
+    const int64_t nblk = ((P + 7) / 8) * 8 * SG;
+    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD, NP>), dim3((unsigned)nblk), dim3((2 * NP + 3) * 64), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
                        p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h, p.uv_ss);
     return hipGetLastError();
+}
+
+// One column pair (16 value columns) per block gives the most chains; two
+// pairs per block halve the w and K tiles each CU streams per column, which
+// pays once there are chains enough for every CU several times over (many
+// sequences, or the segments of the segment-parallel forward).  Both give
+// the same bits: every slice runs the same arithmetic.
+template <typename T, int KD, int VD>
+static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
+    if constexpr (std::is_same<T, bf16>::value && VD >= 32) {
+        if (p.nseq * p.a.HV * (VD / 32) >= 512) return launch_chunk_h_np<T, KD, VD, 2>(p, stream);
+    }
+    return launch_chunk_h_np<T, KD, VD, 1>(p, stream);
 }
 
 // bf16: K in {64, 128} x V in {64, 128, 256}; f32 (small-case reference

@@ -789,3 +789,39 @@ def test_scan_long_prefill_sampled():
     buf = _scan_buf(d["q"], d["k"], d["v"], beta, g, 16)
     check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(c["B"], c["T"], c["M"]), [0, 9, 15], c["M"],
                 tag="long_prefill_32k scan", buf=buf)
+
+
+@pytest.mark.parametrize("K,V,M", [(128, 128, 2), (64, 256, 3), (128, 64, 1)])
+def test_chunk_h_two_pairs_per_block(K, V, M):
+    """With many chains (here 64 packed requests x 16 value heads) chunk_h
+    runs two 16-column slices per block.  Its outputs are bit-identical to
+    the same requests run one call each (one slice per block), and match the
+    oracle on every (request, head); the requests include empty and one-token
+    ones and ragged tails."""
+    H, HV, n = 4, 16, 64
+    rng = np.random.default_rng(900 + K + V + M)
+    lens = rng.integers(1, 90, size=n)
+    lens[[3, 17]] = 0
+    lens[5] = 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", synth.seed_of(3) + K + V + M)
+    beta, g = gates(d)
+    beta = beta.reshape(1, T * M, HV)
+    buf = check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_varlen(cu, M), range(HV), M, cu=cu, cu_host=cu,
+                      tag="two pairs K%d V%d M%d" % (K, V, M))
+    vn_rows = G.slices_to_rows(buf.v_new)
+    hbase = 0
+    for i in range(n):
+        t0, t1 = int(cu[i]), int(cu[i + 1])
+        if t1 == t0:
+            continue
+        one = G.chunk_fwd(d["q"][:, t0:t1].contiguous().to(DEV), d["k"][:, t0 * M:t1 * M].contiguous().to(DEV),
+                          d["v"][:, t0 * M:t1 * M].contiguous().to(DEV),
+                          beta[:, t0 * M:t1 * M].contiguous().to(DEV), g[:, t0:t1].contiguous().to(DEV))
+        torch.cuda.synchronize()
+        nc = math.ceil((t1 - t0) * M / 64)
+        assert torch.equal(one.o[0], buf.o[0, t0:t1]), i
+        assert torch.equal(G.slices_to_rows(one.v_new)[0], vn_rows[0, t0 * M:t1 * M]), i
+        assert torch.equal(one.h, buf.h[hbase:hbase + nc]), i
+        hbase += nc
