@@ -161,7 +161,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         // waiting on HBM.  The SG blocks of a head share an XCD (and its L2);
         // block slg prefetches rows [RPB slg, RPB slg + RPB) of each chunk.
         // The data lands in a scratch LDS area that nothing reads.
-        constexpr int PF = 5;                    // prefetch distance in chunks
+        constexpr int PF = NP == 1 ? 5 : 3;      // prefetch distance in chunks
         constexpr int RPB = C / SG;              // rows per block per chunk
         static_assert(RPB * KD * ES / 128 <= 64 && KD * ES >= 128,
                       "one 4-byte load per line must cover a block's rows");

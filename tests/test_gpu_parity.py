@@ -796,8 +796,9 @@ def test_chunk_h_two_pairs_per_block(K, V, M):
     """With many chains (here 64 packed requests x 16 value heads) chunk_h
     runs two 16-column slices per block.  Its outputs are bit-identical to
     the same requests run one call each (one slice per block), and match the
-    oracle on every (request, head); the requests include empty and one-token
-    ones and ragged tails."""
+    oracle on every (request, head), final states included; every request
+    starts from a given state; the requests include empty and one-token ones
+    and ragged tails."""
     H, HV, n = 4, 16, 64
     rng = np.random.default_rng(900 + K + V + M)
     lens = rng.integers(1, 90, size=n)
@@ -808,8 +809,9 @@ def test_chunk_h_two_pairs_per_block(K, V, M):
     d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", synth.seed_of(3) + K + V + M)
     beta, g = gates(d)
     beta = beta.reshape(1, T * M, HV)
+    h0 = synth.initial_state_draws(n, HV, V, K, synth.seed_of(3) + K + V + M + 1)
     buf = check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_varlen(cu, M), range(HV), M, cu=cu, cu_host=cu,
-                      tag="two pairs K%d V%d M%d" % (K, V, M))
+                      tag="two pairs K%d V%d M%d" % (K, V, M), h0=h0)
     vn_rows = G.slices_to_rows(buf.v_new)
     hbase = 0
     for i in range(n):
@@ -818,9 +820,11 @@ def test_chunk_h_two_pairs_per_block(K, V, M):
             continue
         one = G.chunk_fwd(d["q"][:, t0:t1].contiguous().to(DEV), d["k"][:, t0 * M:t1 * M].contiguous().to(DEV),
                           d["v"][:, t0 * M:t1 * M].contiguous().to(DEV),
-                          beta[:, t0 * M:t1 * M].contiguous().to(DEV), g[:, t0:t1].contiguous().to(DEV))
+                          beta[:, t0 * M:t1 * M].contiguous().to(DEV), g[:, t0:t1].contiguous().to(DEV),
+                          initial_state=h0[i:i + 1].contiguous().to(DEV), output_final_state=True)
         torch.cuda.synchronize()
         nc = math.ceil((t1 - t0) * M / 64)
+        assert torch.equal(one.ht[0], buf.ht[i]), i
         assert torch.equal(one.o[0], buf.o[0, t0:t1]), i
         assert torch.equal(G.slices_to_rows(one.v_new)[0], vn_rows[0, t0 * M:t1 * M]), i
         assert torch.equal(one.h, buf.h[hbase:hbase + nc]), i
