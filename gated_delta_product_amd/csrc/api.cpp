@@ -476,6 +476,8 @@ gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, voi
         return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd_scan: bf16 with K, V in {64, 128} only (K=%d V=%d)", a->K,
                     a->V);
     if (a->T == 0) return ok();
+    if (a->T * a->M * a->V * 2 >= ((int64_t)1 << 31))
+        return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd_scan: T*M*V*2 must stay below 2^31 (T=%lld)", (long long)a->T);
     int64_t seg_tok = 0;
     const int64_t nseg = scan_plan(a->T, num_segments, &seg_tok);
     const ScanLayout L = scan_layout(nseg, a->HV, a->K, a->V);

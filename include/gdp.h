@@ -365,7 +365,7 @@ gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_
  * rounding (the
  * composition runs on bf16 matrix-core operands with fp32 accumulation,
  * like the chunk recurrence itself).  Supported: dtype bf16 with K, V in
- * {64, 128}; other shapes return GDP_ERR_UNSUPPORTED.
+ * {64, 128} and T*M*V*2 < 2^31; other shapes return GDP_ERR_UNSUPPORTED.
  */
 #define GDP_SCAN_MAX_SEGMENTS 64
 gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
