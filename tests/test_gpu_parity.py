@@ -631,9 +631,9 @@ def test_decode_continues_chunked_prefill():
 # ---------------------------------------------------------------------- graphs
 
 def test_hip_graph_capture_replays():
-    """Prefill prepare, the chunk forward (one stream, and pipelined over the
-    library's side streams) and a decode step from the prefill's final state,
-    captured into one HIP graph over static buffers.  Before each replay the
+    """Prefill prepare, the chunk forward (one stream, pipelined over the
+    library's side streams, and segment-parallel) and a decode step from the
+    prefill's final state, captured into one HIP graph over static buffers.  Before each replay the
     inputs are rewritten in place by eager work; every replay equals the
     eager calls on the same inputs bit for bit."""
     T, S, M, H, G_, P, N = 700, 2, 2, 4, 2, 128, 128
@@ -644,11 +644,13 @@ def test_hip_graph_capture_replays():
     pre = G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N)
     seq = G.ChunkBuffers(*pre, output_final_state=True)
     pip = G.ChunkBuffers(*pre, output_final_state=True)
+    scn = G.ChunkBuffers(*pre, output_final_state=True)
     dec = G.decode_prepare(xd, bad, A_log, dt_bias, M, H, G_, P, N)
     dec_o = torch.empty((1, S * M, H, P), dtype=torch.bfloat16, device=DEV)
     # warm-up outside capture: the pipelined call creates its streams and events here
     seq.forward()
     pip.forward_pipelined(3)
+    scn.forward_scan(4)  # and the scan workspace is allocated here
     G.decode_update(*dec, seq.ht, M, o=dec_o)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -656,6 +658,7 @@ def test_hip_graph_capture_replays():
         G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N, out=pre)
         seq.forward()
         pip.forward_pipelined(3)
+        scn.forward_scan(4)
         G.decode_prepare(xd, bad, A_log, dt_bias, M, H, G_, P, N, out=dec)
         G.decode_update(*dec, seq.ht, M, o=dec_o)   # continues from the prefill state, in place
     for i in (1, 2, 0, 1):
@@ -664,14 +667,19 @@ def test_hip_graph_capture_replays():
         ba.copy_(draws[i]["ba"].to(DEV))
         graph.replay()
         torch.cuda.synchronize()
-        ref = G.chunk_fwd(*G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N), output_final_state=True)
+        pre_ref = G.prefill_prepare(xp, bap, A_log, dt_bias, M, H, G_, P, N)
+        ref_scn = G.ChunkBuffers(*pre_ref, output_final_state=True)
+        ref_scn.forward_scan(4)
+        ref = G.chunk_fwd(*pre_ref, output_final_state=True)
         ref_ht = ref.ht.clone()
         ref_o = G.decode_update(*G.decode_prepare(xd, bad, A_log, dt_bias, M, H, G_, P, N), ref.ht, M)
         torch.cuda.synchronize()
         for nm in ("o", "w", "u", "v_new", "h"):
             assert torch.equal(getattr(seq, nm), getattr(ref, nm)), "sequential " + nm
             assert torch.equal(getattr(pip, nm), getattr(ref, nm)), "pipelined " + nm
+            assert torch.equal(getattr(scn, nm), getattr(ref_scn, nm)), "scan " + nm
         assert torch.equal(pip.ht, ref_ht), "pipelined ht"
+        assert torch.equal(scn.ht, ref_scn.ht), "scan ht"
         assert torch.equal(dec_o, ref_o) and torch.equal(seq.ht, ref.ht), "decode"
 
 
