@@ -1,4 +1,6 @@
-// scan.hip -- segment-parallel form of the inter-chunk state recurrence.
+// scan.hip -- segment-parallel form of the inter-chunk state recurrence (the
+// chunk_h stage whose outputs core.ssm.ops.gdp.chunk_o consumes, over the w
+// and u of core.ssm.ops.gdp.wy_fast, recompute_w_u_fwd).
 //
 // Over one chunk c the state update of the chunk_h stage is affine in the
 // state entering it (h is the K x V transpose of the state S):
