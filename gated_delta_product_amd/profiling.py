@@ -4,6 +4,7 @@ benchmark: per-kernel launch statistics and measured HBM traffic per launch.
     python -m gated_delta_product_amd.profiling stats  STATS_CSV OUT.md  --command "..."
     python -m gated_delta_product_amd.profiling traffic FETCH_CSV WRITE_CSV OUT.json \
         --copy-mib 512 --command "..."
+    python -m gated_delta_product_amd.profiling mfma PMC_CSV OUT.md --command "..."
 
 Traffic: FETCH_SIZE and WRITE_SIZE are read per dispatch (KiB).  The same run
 contains one plain device copy of a known size, which fixes how many bytes
@@ -92,6 +93,39 @@ def traffic(fetch_csv, write_csv, copy_mib):
     return res
 
 
+MFMA_PEAK = {"MfmaFlopsBF16": 2.5e15, "MfmaFlopsF32": 157.3e12}  # MI355X dense peaks (flop/s)
+
+
+def mfma_table(pmc_csv):
+    """Per kernel: matrix-core flops per launch (rocprofv3's MfmaFlopsBF16 /
+    MfmaFlopsF32, i.e. MOPS x 512), the MfmaUtil busy percentage, and the
+    rate over the profiled launch duration against the dense peak."""
+    acc = defaultdict(lambda: defaultdict(list))
+    dur = defaultdict(list)
+    with open(pmc_csv) as f:
+        for r in csv.DictReader(f):
+            op = _op_of(r["Kernel_Name"])
+            if not op or op == "copy":
+                continue
+            acc[op][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "MfmaUtil":
+                dur[op].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    lines = ["| kernel | launches | bf16 MFMA GFLOP | f32 MFMA GFLOP | profiled us | MFMA TFLOP/s | fraction of dense peak | MfmaUtil % |",
+             "|---|---|---|---|---|---|---|---|"]
+    for op in KERNELS:
+        if op not in acc:
+            continue
+        d = acc[op]
+        mean = lambda k: sum(d.get(k, [0.0])) / max(1, len(d.get(k, [0.0])))
+        bf, f32, util = mean("MfmaFlopsBF16"), mean("MfmaFlopsF32"), mean("MfmaUtil")
+        t = sum(dur[op]) / max(1, len(dur[op]))
+        rate = (bf + f32) / t if t > 0 else 0.0
+        frac = (bf / t / MFMA_PEAK["MfmaFlopsBF16"] + f32 / t / MFMA_PEAK["MfmaFlopsF32"]) if t > 0 else 0.0
+        lines.append("| %s | %d | %.2f | %.2f | %.1f | %.1f | %.3f | %.1f |" % (
+            op, len(d.get("MfmaUtil", [])), bf / 1e9, f32 / 1e9, t * 1e6, rate / 1e12, frac, util))
+    return "\n".join(lines)
+
+
 def stats_table(stats_csv):
     rows = []
     with open(stats_csv) as f:
@@ -123,8 +157,22 @@ def main(argv=None):
                    help="segments of the profiled run: the per-launch bytes of the chunk "
                         "stages hold for that split only")
     t.add_argument("--path", default=None, help="chunk forward of the profiled run (pipelined or scan)")
+    m = sub.add_parser("mfma")
+    m.add_argument("pmc_csv")
+    m.add_argument("out")
+    m.add_argument("--command", required=True)
+    m.add_argument("--title", default="Matrix-core work per kernel")
     a = ap.parse_args(argv)
-    if a.cmd == "stats":
+    if a.cmd == "mfma":
+        digests = ", ".join("%s %s" % (op, src_digest(op)) for op in KERNELS)
+        text = ("# %s\n\nCommand (run from the repository root on one MI355X):\n\n    %s\n\n%s\n\n"
+                "MFMA flops are rocprofv3's MfmaFlopsBF16 / MfmaFlopsF32 (matrix-core operations x 512, "
+                "dense tiles as issued); the fraction sums each dtype's rate over its dense peak "
+                "(bf16 2.5 PFLOP/s, f32 157.3 TFLOP/s); durations are the profiled launches.\n\n"
+                "Kernel source digests: %s\n" % (a.title, a.command, mfma_table(a.pmc_csv), digests))
+        with open(a.out, "w") as f:
+            f.write(text)
+    elif a.cmd == "stats":
         digests = ", ".join("%s %s" % (op, src_digest(op)) for op in KERNELS)
         text = "# %s\n\nCommand (run from the repository root on one MI355X):\n\n    %s\n\n%s\n\n" \
                "Kernel source digests: %s\n" % (a.title, a.command, stats_table(a.stats_csv), digests)
