@@ -12,7 +12,7 @@
 // per row, both precomputed by the WY stage.
 //
 // One block of five waves per (sequence, value head, 16 value columns), with
-// three roles:
+// three roles (the two-slice form is described below):
 //
 // * Compute waves 0 and 1 run the serial chain and issue no global memory
 //   instruction at all.  Wave k owns rows [k K/2, (k+1) K/2) of the fp32
@@ -37,6 +37,13 @@
 // A compute wave's step is then bound by its own instruction stream, not by
 // the memory queue.  Tile rows are XOR-swizzled in 16-byte units so the
 // fragment reads of both products avoid bank conflicts.
+//
+// With chains to spare (many sequences, or the segments of the
+// segment-parallel forward) a block runs NP = 2 column slices: compute waves
+// 2p and 2p + 1 run slice p, waves 4 and 5 stream the shared w and K tiles
+// and both slices' u, and wave 6 prefetches.  The tiles then cross a CU once
+// per 32 columns.  To fit LDS, the compute waves store their own snapshots
+// and the partial sums are exchanged through two buffers by step parity.
 #include "gdp_common.h"
 #include "gdp_internal.h"
 
