@@ -3,31 +3,35 @@
 
 One step = the whole hot path over one batch of synthetic input, all on the
 GPU through the C ABI of libgdp.so:
-    gdp_prefill_prepare      (split / GQA-expand / Householder-fold / gate)
-    gdp_chunk_fwd_scan       (default, --path scan: recompute_w_u; the affine
-                              state map of each of 16 segments, composed in
-                              parallel; a scan over the segments for the
-                              state entering each; chunk_h over all segments
-                              at once; chunk_o)
- or gdp_chunk_fwd_pipelined  (--path pipelined: recompute_w_u -> chunk_h ->
-                              chunk_o over 3 segments: chunk_h runs the
-                              segments in order, handing its fp32 state on,
-                              while recompute_w_u of later segments and
-                              chunk_o of finished ones run on side streams)
+    gdp_prefill_fwd_scan     (default, --path prefill-scan: recompute_w_u
+                              with the prefill prepare (split /
+                              GQA-expand / Householder-fold / gate) done
+                              inside it; the affine state map of each of 16
+                              segments, composed in parallel; a scan over
+                              the segments for the state entering each;
+                              chunk_h over all segments at once; chunk_o)
+ or gdp_prefill_prepare then gdp_chunk_fwd_scan (--path scan: the same with
+                              prepare as its own launch)
+ or gdp_prefill_prepare then gdp_chunk_fwd_pipelined (--path pipelined:
+                              recompute_w_u -> chunk_h -> chunk_o over 3
+                              segments: chunk_h runs the segments in order,
+                              handing its fp32 state on, while recompute_w_u
+                              of later segments and chunk_o of finished ones
+                              run on side streams)
 Workload: the long single-sequence prefill, B=1, T=32768 tokens, 16 heads
 (query/key groups = value heads = 16), K=V=128, M=2 Householder copies, chunk
 64, bf16 activations with fp32 gates, state and accumulation.  Inputs are
 drawn once (seeded, synthetic) and resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s over the timed steps, the roofline of the
-dominant kernel (chunk_h: algorithmic bytes per launch / its average launch
-duration from HIP events recorded on its stream around every launch, vs
-8 TB/s HBM; the events record without a system-scope fence, so they do not
-slow the step they time) and the oracle's throughput on the host cores as a
-reported baseline.  --stages adds a sequential (not overlapped) pass that
+dominant kernel (the one with the longest launch: algorithmic bytes per
+launch / its average launch duration from HIP events recorded on its stream
+around every launch, vs 8 TB/s HBM; the events record without a
+system-scope fence, so they do not slow the step they time) and the
+oracle's throughput on the host cores as a reported baseline.  --stages adds a sequential (not overlapped) pass that
 times each stage on its own.
 
-    python bench.py [--steps K] [--warmup W] [--path scan|pipelined] [--segments S] [--stages]
+    python bench.py [--steps K] [--warmup W] [--path prefill-scan|scan|pipelined] [--segments S] [--stages]
                     [--no-cpu-baseline] [--copy-mib N]
 """
 import argparse
@@ -138,7 +142,8 @@ def measured_traffic(kernel, segments, path):
     the same chunk-forward path, if it was taken on the current kernel source
     with the same segments (the launch sizes); else None."""
     from gated_delta_product_amd import profiling
-    name = "traffic_long_prefill_32k_scan.json" if path == "scan" else "traffic_long_prefill_32k.json"
+    name = {"scan": "traffic_long_prefill_32k_scan.json", "prefill-scan": "traffic_long_prefill_32k_prefill_scan.json"}.get(
+        path, "traffic_long_prefill_32k.json")
     fn = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(fn):
         return None
@@ -223,8 +228,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--path", choices=["pipelined", "scan"], default="scan",
-                    help="chunk forward: gdp_chunk_fwd_pipelined or gdp_chunk_fwd_scan")
+    ap.add_argument("--path", choices=["pipelined", "scan", "prefill-scan"], default="prefill-scan",
+                    help="gdp_chunk_fwd_pipelined or gdp_chunk_fwd_scan after gdp_prefill_prepare, or "
+                         "gdp_prefill_fwd_scan (prepare inside the WY stage)")
     ap.add_argument("--segments", type=int, default=None,
                     help="segments of the chunk forward (default %d pipelined, %d scan)" % (SEGMENTS, SCAN_SEGMENTS))
     ap.add_argument("--stages", action="store_true", help="also time each stage sequentially (not overlapped)")
@@ -246,10 +252,13 @@ def main():
     from gated_delta_product_amd import synth
 
     w = dict(WORKLOAD)
-    scan = args.path == "scan"
+    fused = args.path == "prefill-scan"
+    scan = args.path == "scan" or fused
     if args.segments is None:
         args.segments = SCAN_SEGMENTS if scan else SEGMENTS
-    if scan:
+    if fused:
+        w["path"] = "prefill_scan(recompute_w_u with prepare,seg_map,seg_scan,chunk_h,chunk_o)"
+    elif scan:
         w["path"] = "prepare+scan(recompute_w_u,seg_map,seg_scan,chunk_h,chunk_o)"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -272,6 +281,11 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
+        if fused:
+            if ev:
+                ev[1].record(stream)
+            buf.prefill_scan(x, ba, A_log, dt_bias, Gq, args.segments, stage_events=ev[2:] if ev else None)
+            return
         G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
         if ev:
             ev[1].record(stream)
@@ -308,12 +322,21 @@ def main():
         seg_tokens = [starts[j + 1] - starts[j] for j in range(nseg)]
         ch_bytes = sum(algorithmic_bytes(w, t)["gdp_chunk_h"] for t in seg_tokens) / nseg  # per launch
     ch_ms = sum(seg_ms) / len(seg_ms)
-    kern = {
-        "gdp_prefill_prepare": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1, "alg_bytes": ab["gdp_prefill_prepare"],
-                                "GB/s": round(ab["gdp_prefill_prepare"] / (prep_ms / 1e3) / 1e9, 1)},
-        "gdp_chunk_h": {"us_per_launch": round(ch_ms * 1e3, 2), "launches_per_step": 1 if scan else nseg,
-                        "alg_bytes_per_launch": int(ch_bytes), "GB/s": round(ch_bytes / (ch_ms / 1e3) / 1e9, 1)},
-    }
+    if fused:  # prepare runs inside the WY stage: time that stage as one
+        prep_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        pw = ab["gdp_prefill_prepare"] + ab["gdp_recompute_w_u"] - (
+            w["T"] * w["M"] * w["HV"] * (w["K"] + w["V"]) * 2 + w["T"] * w["M"] * w["HV"] * 4 + w["T"] * w["HV"] * 4)
+    if fused:
+        # prepare's bytes plus WY's, less WY's reads of the key and value
+        # copies, beta and g (they stay on chip)
+        kern = {"gdp_recompute_w_u(prepare fused)": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1,
+                                                     "alg_bytes": pw, "GB/s": round(pw / (prep_ms / 1e3) / 1e9, 1)}}
+    else:
+        kern = {"gdp_prefill_prepare": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1,
+                                        "alg_bytes": ab["gdp_prefill_prepare"],
+                                        "GB/s": round(ab["gdp_prefill_prepare"] / (prep_ms / 1e3) / 1e9, 1)}}
+    kern["gdp_chunk_h"] = {"us_per_launch": round(ch_ms * 1e3, 2), "launches_per_step": 1 if scan else nseg,
+                           "alg_bytes_per_launch": int(ch_bytes), "GB/s": round(ch_bytes / (ch_ms / 1e3) / 1e9, 1)}
     if scan:
         # the segment maps read k, kdecay, gcum, w and u of every segment but
         # the last once, and write each segment's fp32 map; the scan reads
@@ -324,10 +347,17 @@ def main():
             + (nseg - 1) * w["HV"] * w["K"] * (w["K"] + w["V"]) * 4
         kern["gdp_seg_map+gdp_seg_scan"] = {"us": round(map_ms * 1e3, 2), "segments": nseg, "map_alg_bytes": mb,
                                             "GB/s": round(mb / (map_ms / 1e3) / 1e9, 1)}
-    achieved = ch_bytes / (ch_ms / 1e3) / 1e9
-    roof = {"kernel": "gdp_chunk_h", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("gdp_chunk_h", nseg, args.path)}
+    # the roofline is reported for the kernel that takes the longest per launch
+    cands = {"gdp_chunk_h": (ch_ms, ch_bytes)}
+    if fused:
+        cands["gdp_recompute_w_u"] = (prep_ms, pw)
+    else:
+        cands["gdp_prefill_prepare"] = (prep_ms, ab["gdp_prefill_prepare"])
+    dom = max(cands, key=lambda kk: cands[kk][0])
+    achieved = cands[dom][1] / (cands[dom][0] / 1e3) / 1e9
+    roof = {"kernel": dom + (" (prepare fused)" if dom == "gdp_recompute_w_u" else ""), "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, nseg, args.path)}
 
     stages = None
     if args.stages:  # each stage alone, whole workload, for reference

@@ -91,6 +91,9 @@ def lib():
                                                 _vp, _vp]
         L.gdp_chunk_fwd_scan.restype = ctypes.c_int
         L.gdp_chunk_fwd_scan.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _i64, _vp, _vp]
+        L.gdp_prefill_fwd_scan.restype = ctypes.c_int
+        L.gdp_prefill_fwd_scan.argtypes = [ctypes.POINTER(PrepareArgs), ctypes.POINTER(ChunkArgs), _i32, _vp, _i64,
+                                           _vp, _vp]
         L.gdp_scan_segments.restype = _i32
         L.gdp_scan_segments.argtypes = [_i64, _i32]
         L.gdp_scan_workspace_bytes.restype = _i64
@@ -348,6 +351,24 @@ class ChunkBuffers:
         return self._pipelined(lambda ws, ev, s: lib().gdp_chunk_fwd_pipelined(
             ctypes.byref(self.args), int(num_segments), ws, ev, s), num_segments, stream, chunk_h_events)
 
+    def prefill_scan(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, stage_events=None):
+        """gdp_prefill_fwd_scan: prepare x / ba into this buffer's q, k, v,
+        beta, g (allocated with the prepare shapes) inside the WY stage of the
+        segment-parallel forward.  Arguments as prefill_prepare and
+        forward_scan."""
+        _need_cuda(x, ba, A_log, dt_bias)
+        d = self.dims
+        if x.dim() != 3 or x.stride(2) != 1 or ba.dim() != 3 or ba.stride(2) != 1:
+            raise ValueError("x and ba must be 3-D with a contiguous last dimension")
+        if x.shape[:2] != (d["B"], d["T"]) or ba.shape[:2] != (d["B"], d["T"]) or x.dtype != self.q.dtype:
+            raise ValueError("x / ba do not match the buffers")
+        pa = PrepareArgs(x=x.data_ptr(), x_n_stride=x.stride(0), x_t_stride=x.stride(1), ba=ba.data_ptr(),
+                         ba_n_stride=ba.stride(0), ba_t_stride=ba.stride(1), A_log=A_log.data_ptr(),
+                         dt_bias=dt_bias.data_ptr(), G=int(num_groups))
+        return self._scan(lambda ws, nb, ev, s: lib().gdp_prefill_fwd_scan(
+            ctypes.byref(pa), ctypes.byref(self.args), int(num_segments), ws, nb, ev, s), num_segments, stream,
+            stage_events)
+
     def forward_scan(self, num_segments, stream=None, stage_events=None):
         """gdp_chunk_fwd_scan: the results of forward() for B == 1 without
         cu_seqlens (to rounding past the first segment), with the serial
@@ -356,6 +377,10 @@ class ChunkBuffers:
         stage_events: optional 3 torch.cuda.Event (timing enabled, recorded
         at least once) recorded before the segment maps, before chunk_h and
         after it."""
+        return self._scan(lambda ws, nb, ev, s: lib().gdp_chunk_fwd_scan(
+            ctypes.byref(self.args), int(num_segments), ws, nb, ev, s), num_segments, stream, stage_events)
+
+    def _scan(self, call, num_segments, stream, stage_events):
         d = self.dims
         need = lib().gdp_scan_workspace_bytes(d["T"], d["HV"], d["K"], d["V"], int(num_segments))
         if need < 0:
@@ -370,8 +395,7 @@ class ChunkBuffers:
                 raise ValueError("need 3 events")
             ev = (_vp * 3)(*[e.cuda_event for e in stage_events])
         s = stream if stream is not None else _stream(self.device)
-        _check(lib().gdp_chunk_fwd_scan(ctypes.byref(self.args), int(num_segments), ws.data_ptr(), ws.numel(),
-                                        ev, s))
+        _check(call(ws.data_ptr(), ws.numel(), ev, s))
         return self.o
 
     def _pipelined(self, call, num_segments, stream, chunk_h_events):

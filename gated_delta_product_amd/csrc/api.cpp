@@ -462,29 +462,32 @@ int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, in
     return scan_layout(nseg, HV, K, V).total;
 }
 
-gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
-                              int64_t workspace_bytes, void *const *stage_events, void *stream) {
+// The segment-parallel forward; with prep, WY also does the prepare of its
+// rows (launch_wy_prepare).
+static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp::PrepareParams *prep,
+                            int32_t num_segments, void *workspace, int64_t workspace_bytes,
+                            void *const *stage_events, void *stream) {
     gdp::ChunkParams p;
     gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
     if (st != GDP_OK) return st;
-    if (a->cu_seqlens) return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: cu_seqlens must be NULL");
-    if (a->B != 1) return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: B must be 1 (got %lld)", (long long)a->B);
+    if (a->cu_seqlens) return fail(GDP_ERR_INVALID, "%s: cu_seqlens must be NULL", name);
+    if (a->B != 1) return fail(GDP_ERR_INVALID, "%s: B must be 1 (got %lld)", name, (long long)a->B);
     if (num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS)
-        return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: num_segments %d not in [1, %d]", num_segments,
+        return fail(GDP_ERR_INVALID, "%s: num_segments %d not in [1, %d]", name, num_segments,
                     GDP_SCAN_MAX_SEGMENTS);
     if (a->dtype != GDP_BF16 || !((a->K == 64 || a->K == 128) && (a->V == 64 || a->V == 128)))
-        return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd_scan: bf16 with K, V in {64, 128} only (K=%d V=%d)", a->K,
+        return fail(GDP_ERR_UNSUPPORTED, "%s: bf16 with K, V in {64, 128} only (K=%d V=%d)", name, a->K,
                     a->V);
     if (a->T == 0) return ok();
     if (a->T * a->M * a->V * 2 >= ((int64_t)1 << 31))
-        return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd_scan: T*M*V*2 must stay below 2^31 (T=%lld)", (long long)a->T);
+        return fail(GDP_ERR_UNSUPPORTED, "%s: T*M*V*2 must stay below 2^31 (T=%lld)", name, (long long)a->T);
     int64_t seg_tok = 0;
     const int64_t nseg = scan_plan(a->T, num_segments, &seg_tok);
     const ScanLayout L = scan_layout(nseg, a->HV, a->K, a->V);
     if (!workspace || ((uintptr_t)workspace & 255u))
-        return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: workspace must be a 256-byte aligned device pointer");
+        return fail(GDP_ERR_INVALID, "%s: workspace must be a 256-byte aligned device pointer", name);
     if (workspace_bytes < L.total)
-        return fail(GDP_ERR_INVALID, "gdp_chunk_fwd_scan: workspace of %lld bytes, %lld needed",
+        return fail(GDP_ERR_INVALID, "%s: workspace of %lld bytes, %lld needed", name,
                     (long long)workspace_bytes, (long long)L.total);
     char *ws = (char *)workspace;
     gdp::ScanParams sp{p, nseg, seg_tok, (float *)(ws + L.maps), (float *)(ws + L.hstart),
@@ -499,7 +502,9 @@ gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, voi
     gdp::ChunkParams hp;
     if ((st = check_chunk(&ha, ST_H, &hp)) != GDP_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    if ((st = hip_status(gdp::launch_wy(p, s), "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK) return st;
+    if ((st = hip_status(prep ? gdp::launch_wy_prepare(p, *prep, s) : gdp::launch_wy(p, s),
+                         "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK)
+        return st;
     auto mark = [&](int i) {
         return stage_events ? hip_status(hipEventRecord((hipEvent_t)stage_events[i], s), "hipEventRecord") : ok();
     };
@@ -518,6 +523,30 @@ gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, voi
             return st;
     }
     return ok();
+}
+
+gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
+                              int64_t workspace_bytes, void *const *stage_events, void *stream) {
+    return scan_impl("gdp_chunk_fwd_scan", a, nullptr, num_segments, workspace, workspace_bytes, stage_events,
+                     stream);
+}
+
+gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *pa, const gdp_chunk_args *a, int32_t num_segments,
+                                void *workspace, int64_t workspace_bytes, void *const *stage_events, void *stream) {
+    if (!pa || !a) return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_scan: args is NULL");
+    if (a->HV != a->H)
+        return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_scan: prepare makes H value heads (HV=%d, H=%d)", a->HV, a->H);
+    if (!a->g && a->T > 0) return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_scan: g is NULL (prepare writes it)");
+    gdp::PrepareParams pp;
+    const gdp_status st = prepare_check("gdp_prefill_fwd_scan", false, pa->x, pa->x_n_stride, pa->x_t_stride, pa->ba,
+                                        pa->ba_n_stride, pa->ba_t_stride, pa->A_log, pa->dt_bias, a->B, a->T, a->M,
+                                        a->H, pa->G, a->V, a->K, a->dtype, (void *)a->q, (void *)a->k,
+                                        (void *)a->v, (float *)a->beta, (float *)a->g, &pp);
+    if (st != GDP_OK) return st;
+    if (pp.T > 0 && !pp.vec16)
+        return fail(GDP_ERR_UNSUPPORTED, "gdp_prefill_fwd_scan: x rows and outputs must be 16-byte aligned");
+    return scan_impl("gdp_prefill_fwd_scan", a, pp.T > 0 ? &pp : nullptr, num_segments, workspace,
+                     workspace_bytes, stage_events, stream);
 }
 
 gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,

@@ -108,6 +108,34 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
     return x;
 }
 
+// ---------------------------------------------------------------- gates
+// (core.ssm.ops.gdp.prepare: the gates of gdp_prefill_prepare; shared by the
+// prepare kernels and the WY stage that fuses prepare in)
+// beta = 1 / (1 + exp(-b)) with float32 rounding after each operation;
+// exp is evaluated in double and rounded once.
+__device__ __forceinline__ float gate_beta(float b) {
+#pragma clang fp contract(off)
+    const float e = (float)exp(-(double)b);
+    const float d = 1.0f + e;
+    return 1.0f / d;
+}
+
+// g = -exp(A_log) * softplus(a + dt_bias); softplus(s) = s for s > 20,
+// else log1p(exp(s)) (core.ssm.ops.gdp.prepare, softplus).
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
+#pragma clang fp contract(off)
+    const float s = a + dt_bias;
+    float sp;
+    if (s > 20.0f) {
+        sp = s;
+    } else {
+        const float e = (float)exp((double)s);
+        sp = (float)log1p((double)e);
+    }
+    const float ea = (float)exp((double)A_log);
+    return -(ea * sp);
+}
+
 // ---------------------------------------------------------------- sequences
 // Token range [bos, eos) of sequence i in the flattened [B*T] token stream.
 __device__ __forceinline__ void seq_bounds(const int32_t *cu, int64_t T, int64_t i,

@@ -61,6 +61,10 @@ struct ScanParams {
 hipError_t launch_seg_scan(const ScanParams &sp, hipStream_t stream);
 
 hipError_t launch_wy(const ChunkParams &p, hipStream_t stream);
+// launch_wy with the prefill prepare of its rows fused in (one sequence,
+// HV == H, bf16, K and V in {64, 128}): reads pp.x / pp.ba, writes pp's
+// outputs and uses them as the chunk inputs
+hipError_t launch_wy_prepare(const ChunkParams &p, const PrepareParams &pp, hipStream_t stream);
 hipError_t launch_chunk_h(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_chunk_o(const ChunkParams &p, hipStream_t stream);
 

@@ -13,31 +13,6 @@
 
 namespace gdp {
 
-// beta = 1 / (1 + exp(-b)) with float32 rounding after each operation;
-// exp is evaluated in double and rounded once.
-__device__ __forceinline__ float gate_beta(float b) {
-#pragma clang fp contract(off)
-    const float e = (float)exp(-(double)b);
-    const float d = 1.0f + e;
-    return 1.0f / d;
-}
-
-// g = -exp(A_log) * softplus(a + dt_bias); softplus(s) = s for s > 20,
-// else log1p(exp(s)) (core.ssm.ops.gdp.prepare, softplus).
-__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
-#pragma clang fp contract(off)
-    const float s = a + dt_bias;
-    float sp;
-    if (s > 20.0f) {
-        sp = s;
-    } else {
-        const float e = (float)exp((double)s);
-        sp = (float)log1p((double)e);
-    }
-    const float ea = (float)exp((double)A_log);
-    return -(ea * sp);
-}
-
 // Copy unit: a 16-byte vector when VEC16, else one element.  (A native
 // vector type, so arrays of units stay in registers.)
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));

@@ -41,13 +41,31 @@ template <typename T> struct Pad { static constexpr int value = 16 / (int)sizeof
 
 }  // namespace
 
-template <typename T, int KD, int VD>
+// With FUSE the block also does the prefill prepare of its rows (one
+// sequence, HV == H): it reads its key and value copies, query and gate
+// inputs straight from the post-conv activations x and ba (layouts of
+// core.ssm.ops.gdp.prepare, gdp_prefill_prepare), writes prepare's outputs
+// for them (q, k, v, beta, g, exactly as the prepare kernel does; q and g of
+// a token by the block holding its copy 0) and uses the same values.
+template <typename T>
+struct WyFuse {
+    const T *x;
+    int64_t xts;  // x row stride (elements)
+    const T *ba;
+    int64_t bts;  // ba row stride (elements)
+    const float *A_log, *dt_bias;
+    int G;
+    T *q, *k, *v;
+    float *beta, *g;
+};
+
+template <typename T, int KD, int VD, bool FUSE>
 __global__ void __launch_bounds__(256)
 gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ beta,
          const float *__restrict__ g, const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok,
          int H, int HV, int M, float *__restrict__ k_rnorm, float *__restrict__ gcum,
          float *__restrict__ kdecay, T *__restrict__ w,
-         T *__restrict__ u, int64_t uv_ss) {
+         T *__restrict__ u, int64_t uv_ss, WyFuse<T> fz) {
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
     constexpr int LDV = VD + Pad<T>::value;
@@ -88,12 +106,67 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     const int64_t e_row = r0 + lane;
     const bool e_in = lane < n;
     float b_in = 0.f, gd_in = 0.f;
-    if (wv == 0) {
+    if constexpr (FUSE) {
+        if (wv == 0 && e_in) {
+            const int64_t t = e_row / M;
+            const int j = (int)(e_row - t * M);
+            b_in = gate_beta(to_f32(fz.ba[t * fz.bts + j * H + hv]));
+            fz.beta[e_row * H + hv] = b_in;
+            if (j == 0) {
+                gd_in = gate_g(to_f32(fz.ba[t * fz.bts + M * H + hv]), fz.A_log[hv], fz.dt_bias[hv]);
+                fz.g[t * H + hv] = gd_in;
+            }
+        }
+    } else if (wv == 0) {
         b_in = e_in ? beta[e_row * HV + hv] : 0.f;
         gd_in = (g != nullptr && e_in && (e_row % M) == 0) ? g[(e_row / M) * HV + hv] : 0.f;  // NULL: ungated
     }
     uint4 vreg[VPT];
-    {
+    if constexpr (FUSE) {
+        // value copy j of token t: x[t, (j H + h) P ..]; key copy j: x[t,
+        // M H P + (j G + h / (H/G)) N ..]; query: x[t, M H P + M G N +
+        // (h / (H/G)) N ..] (value head h == key head)
+        constexpr int E = 16 / (int)sizeof(T);
+        const int grp = hv / (H / fz.G);
+        const int64_t kb = (int64_t)M * H * VD, qb = kb + (int64_t)M * fz.G * KD;
+#pragma unroll
+        for (int it = 0; it < VPT; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
+            vreg[it] = make_uint4(0, 0, 0, 0);
+            if (row < n) {
+                const int64_t e = r0 + row, t = e / M;
+                const int j = (int)(e - t * M);
+                vreg[it] = *(const uint4 *)(fz.x + t * fz.xts + ((int64_t)j * H + hv) * VD + cu16 * E);
+                *(uint4 *)(fz.v + (e * H + hv) * (int64_t)VD + cu16 * E) = vreg[it];
+            }
+        }
+        constexpr int KUPR = KD / E;  // units per key row (one wave holds whole rows)
+#pragma unroll
+        for (int it = 0; it < (C * KUPR) / 256; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / KUPR, cu16 = uidx % KUPR;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            const int64_t e = r0 + row, t = e / M;
+            const int j = (int)(e - t * M);
+            if (row < n) {
+                val = *(const uint4 *)(fz.x + t * fz.xts + kb + ((int64_t)j * fz.G + grp) * KD + cu16 * E);
+                *(uint4 *)(fz.k + (e * H + hv) * (int64_t)KD + cu16 * E) = val;
+                if (j == 0)  // the token's query, once
+                    *(uint4 *)(fz.q + (t * H + hv) * (int64_t)KD + cu16 * E) =
+                        *(const uint4 *)(fz.x + t * fz.xts + qb + (int64_t)grp * KD + cu16 * E);
+            }
+            *(uint4 *)(Ks + row * LDK + cu16 * E) = val;
+            const T *el = (const T *)&val;
+            float sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const float f = to_f32(el[i]);
+                sq += f * f;
+            }
+#pragma unroll
+            for (int d = 1; d < KUPR; d <<= 1) sq += __shfl_xor(sq, d, 64);
+            if (cu16 == 0) s_rk[row] = sq;
+        }
+    } else {
         const T *vsrc = v + (r0 * HV + hv) * (int64_t)VD;
 #pragma unroll
         for (int it = 0; it < VPT; ++it) {
@@ -101,8 +174,8 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             vreg[it] = row < n ? *(const uint4 *)(vsrc + (int64_t)row * HV * VD + cu16 * (16 / (int)sizeof(T)))
                                : make_uint4(0, 0, 0, 0);
         }
+        stage_tile<T, C, KD, LDK, 256>(Ks, k + (r0 * H + hk) * (int64_t)KD, (int64_t)H * KD, n, s_rk);
     }
-    stage_tile<T, C, KD, LDK, 256>(Ks, k + (r0 * H + hk) * (int64_t)KD, (int64_t)H * KD, n, s_rk);
     if (wv == 0) {
         const float gam = wave_inclusive_sum(gd_in);
         s_beta[lane] = b_in;
@@ -294,14 +367,14 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
 }
 
-template <typename T, int KD, int VD>
-static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream) {
+template <typename T, int KD, int VD, bool FUSE = false>
+static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream, const WyFuse<T> &fz = WyFuse<T>{}) {
     const gdp_chunk_args &a = p.a;
     if (p.max_items * a.HV > 0x7fffffff) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)(p.max_items * a.HV));
-    hipLaunchKernelGGL((gdp_wy_k<T, KD, VD>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((gdp_wy_k<T, KD, VD, FUSE>), grid, dim3(256), 0, stream,
                        (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
-                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u, p.uv_ss);
+                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u, p.uv_ss, fz);
     return hipGetLastError();
 }
 
@@ -327,6 +400,20 @@ static hipError_t launch_wy_f32(const ChunkParams &p, hipStream_t stream) {
 hipError_t launch_wy(const ChunkParams &p, hipStream_t stream) {
     if (p.max_items == 0) return hipSuccess;
     return p.a.dtype == GDP_BF16 ? launch_wy_bf16(p, stream) : launch_wy_f32(p, stream);
+}
+
+// WY with the prefill prepare fused in (bf16, K and V in {64, 128}); the
+// caller has checked both argument sets.
+hipError_t launch_wy_prepare(const ChunkParams &p, const PrepareParams &pp, hipStream_t stream) {
+    if (p.max_items == 0) return hipSuccess;
+    const WyFuse<bf16> fz{(const bf16 *)pp.x, pp.x_t_stride, (const bf16 *)pp.ba, pp.ba_t_stride, pp.A_log,
+                          pp.dt_bias, pp.G, (bf16 *)pp.q, (bf16 *)pp.k, (bf16 *)pp.v, pp.beta, pp.g};
+    const int K = p.a.K, V = p.a.V;
+    if (K == 64 && V == 64) return launch_wy_t<bf16, 64, 64, true>(p, stream, fz);
+    if (K == 64 && V == 128) return launch_wy_t<bf16, 64, 128, true>(p, stream, fz);
+    if (K == 128 && V == 64) return launch_wy_t<bf16, 128, 64, true>(p, stream, fz);
+    if (K == 128 && V == 128) return launch_wy_t<bf16, 128, 128, true>(p, stream, fz);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace gdp

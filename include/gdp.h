@@ -20,6 +20,9 @@
  *                        whose parallel stages overlap the serial one
  *   gdp_prefill_fwd_pipelined  prepare plus the pipelined chunk forward,
  *                        with each segment's prepare overlapped too
+ *   gdp_chunk_fwd_scan   the same for one long sequence, with the serial
+ *                        state chain cut into segments run in parallel
+ *   gdp_prefill_fwd_scan prepare fused into the WY stage of that form
  *   gdp_decode_prepare   the prepare of a decode step: query and decay
  *                        interleaved onto the Householder copies
  *                        (core.ssm.ops.gdp.prepare, gdp_decode_prepare)
@@ -370,6 +373,24 @@ gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_
 #define GDP_SCAN_MAX_SEGMENTS 64
 gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
                               int64_t workspace_bytes, void *const *stage_events, void *stream);
+
+/*
+ * gdp_prefill_fwd_scan -- gdp_prefill_prepare followed by gdp_chunk_fwd_scan
+ * for one sequence, with the prepare done inside the WY stage: each
+ * gdp_recompute_w_u block reads its key and value copies, query and gate
+ * inputs straight from x and ba (the layouts of gdp_prefill_prepare), writes
+ * prepare's outputs for its rows (q and g of a token by the block holding
+ * the token's copy 0) and uses them, so the key and value copies are not
+ * read back from HBM.  Prepare writes the chunk arguments' q, k, v, beta and
+ * g (which must therefore be writable, g not NULL, and HV == H: prepare
+ * makes H value heads).  Every output is bit-identical to the two calls in
+ * sequence.  The requirements are those of gdp_chunk_fwd_scan (B == n == 1)
+ * and of gdp_prefill_prepare, plus 16-byte aligned rows of x and of the
+ * outputs; stage_events as for gdp_chunk_fwd_scan (the first one is
+ * recorded after the WY-with-prepare stage).
+ */
+gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *p, const gdp_chunk_args *a, int32_t num_segments,
+                                void *workspace, int64_t workspace_bytes, void *const *stage_events, void *stream);
 
 /* Segments gdp_chunk_fwd_scan runs for T tokens and num_segments requested
    (0 for T == 0), or -1 on bad arguments. */

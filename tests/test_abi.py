@@ -298,3 +298,25 @@ def test_scan_rejects_and_plan():
     want = up(15 * HV * K * (K + V) * 4) + up(16 * HV * V * K * 4) + up(17 * 4)
     assert L.gdp_scan_workspace_bytes(32768, HV, K, V, 16) == want
     assert L.gdp_scan_workspace_bytes(32768, HV, K, V, 0) == -1
+
+
+def test_prefill_scan_rejects():
+    """gdp_prefill_fwd_scan refuses before launching anything: value heads
+    other than prepare's, a missing g, bad prepare arguments, and whatever
+    gdp_chunk_fwd_scan refuses."""
+    L = B.lib()
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 40
+    pa = B.PrepareArgs(x=0x200000, x_n_stride=0, x_t_stride=2 * 2 * 128 + 2 * 1 * 128 + 1 * 128, ba=0x300000,
+                       ba_n_stride=0, ba_t_stride=2 * 2 + 2, A_log=0x400000, dt_bias=0x500000, G=1)
+    a = lambda **kw: ctypes.byref(_args(**dict(dict(K=128, V=128, M=2, H=2, HV=2, h_chunks=8), **kw)))
+    assert L.gdp_prefill_fwd_scan(None, a(), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(HV=4), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(g=None), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    bad = B.PrepareArgs(**dict((f, getattr(pa, f)) for f, _ in B.PrepareArgs._fields_))
+    bad.G = 3  # H % G != 0
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(bad), a(), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(B=2, h_chunks=16), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(), 0, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(), 2, ws, 64, None, None) == B.GDP_ERR_INVALID
+    assert B.lib().gdp_last_error()

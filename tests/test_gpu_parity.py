@@ -837,3 +837,31 @@ def test_chunk_h_two_pairs_per_block(K, V, M):
         assert torch.equal(G.slices_to_rows(one.v_new)[0], vn_rows[0, t0 * M:t1 * M]), i
         assert torch.equal(one.h, buf.h[hbase:hbase + nc]), i
         hbase += nc
+
+
+@pytest.mark.parametrize("case", [(1000, 2, 4, 2, 128, 128, 5), (700, 3, 2, 1, 64, 64, 4), (513, 1, 4, 4, 128, 64, 3),
+                                  (32768, 2, 16, 16, 128, 128, 16)],
+                         ids=lambda c: "T%d-M%d-H%d-G%d-P%d-N%d-s%d" % c)
+def test_prefill_scan_is_bit_identical(case):
+    """gdp_prefill_fwd_scan (prepare done inside the WY stage) gives exactly
+    the outputs of gdp_prefill_prepare then gdp_chunk_fwd_scan: q, k, v, beta,
+    g and every chunk output, with an initial state, ragged tails, M = 1..3,
+    GQA groups, and the timed workload (T = 32768, 16 heads, 16 segments)."""
+    T, M, H, G_, P, N, nseg = case
+    d = synth.prepare_draws(1, T, M, H, G_, P, N, "bf16", synth.seed_of(4) + 300 + T % 97)
+    x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
+    pre = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, G_, P, N)
+    h0 = synth.initial_state_draws(1, H, P, N, synth.seed_of(4) + 301).to(DEV)
+    ref = G.ChunkBuffers(*pre, initial_state=h0, output_final_state=True)
+    ref.forward_scan(nseg)
+    outs = [torch.full_like(t, 7) for t in pre]  # the fused prepare must overwrite all of them
+    fz = G.ChunkBuffers(*outs, initial_state=h0, output_final_state=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in evs:
+        e.record()
+    fz.prefill_scan(x, ba, A_log, dt_bias, G_, nseg, stage_events=evs)
+    torch.cuda.synchronize()
+    for a_, b_, nm in zip(outs, pre, ("q", "k", "v", "beta", "g")):
+        assert torch.equal(a_, b_), nm
+    for nm in ("o", "w", "u", "v_new", "h", "ht", "k_rnorm", "gcum", "kdecay"):
+        assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
