@@ -107,16 +107,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     const bool e_in = lane < n;
     float b_in = 0.f, gd_in = 0.f;
     if constexpr (FUSE) {
-        if (wv == 0 && e_in) {
-            const int64_t t = e_row / M;
-            const int j = (int)(e_row - t * M);
-            b_in = gate_beta(to_f32(fz.ba[t * fz.bts + j * H + hv]));
-            fz.beta[e_row * H + hv] = b_in;
-            if (j == 0) {
-                gd_in = gate_g(to_f32(fz.ba[t * fz.bts + M * H + hv]), fz.A_log[hv], fz.dt_bias[hv]);
-                fz.g[t * H + hv] = gd_in;
-            }
-        }
+        // (the gates are computed below, once the tile loads are out)
     } else if (wv == 0) {
         b_in = e_in ? beta[e_row * HV + hv] : 0.f;
         gd_in = (g != nullptr && e_in && (e_row % M) == 0) ? g[(e_row / M) * HV + hv] : 0.f;  // NULL: ungated
@@ -127,8 +118,13 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         // M H P + (j G + h / (H/G)) N ..]; query: x[t, M H P + M G N +
         // (h / (H/G)) N ..] (value head h == key head)
         constexpr int E = 16 / (int)sizeof(T);
+        constexpr int KUPR = KD / E;          // units per key row (one wave holds whole rows)
+        constexpr int KPT = (C * KUPR) / 256;  // key units per thread
         const int grp = hv / (H / fz.G);
         const int64_t kb = (int64_t)M * H * VD, qb = kb + (int64_t)M * fz.G * KD;
+        // every load first (values, keys, the queries of copy-0 rows), then
+        // the stores, so the loads' latencies overlap
+        uint4 kreg[KPT], qreg[KPT];
 #pragma unroll
         for (int it = 0; it < VPT; ++it) {
             const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
@@ -137,25 +133,48 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 const int64_t e = r0 + row, t = e / M;
                 const int j = (int)(e - t * M);
                 vreg[it] = *(const uint4 *)(fz.x + t * fz.xts + ((int64_t)j * H + hv) * VD + cu16 * E);
-                *(uint4 *)(fz.v + (e * H + hv) * (int64_t)VD + cu16 * E) = vreg[it];
             }
         }
-        constexpr int KUPR = KD / E;  // units per key row (one wave holds whole rows)
 #pragma unroll
-        for (int it = 0; it < (C * KUPR) / 256; ++it) {
+        for (int it = 0; it < KPT; ++it) {
             const int uidx = tid + 256 * it, row = uidx / KUPR, cu16 = uidx % KUPR;
-            uint4 val = make_uint4(0, 0, 0, 0);
+            kreg[it] = make_uint4(0, 0, 0, 0);
+            qreg[it] = make_uint4(0, 0, 0, 0);
+            if (row < n) {
+                const int64_t e = r0 + row, t = e / M;
+                const int j = (int)(e - t * M);
+                kreg[it] = *(const uint4 *)(fz.x + t * fz.xts + kb + ((int64_t)j * fz.G + grp) * KD + cu16 * E);
+                if (j == 0) qreg[it] = *(const uint4 *)(fz.x + t * fz.xts + qb + (int64_t)grp * KD + cu16 * E);
+            }
+        }
+        // the gates of the block's rows: beta per row, g per token (on its copy 0)
+        if (wv == 0 && e_in) {
+            const int64_t t = e_row / M;
+            const int j = (int)(e_row - t * M);
+            b_in = gate_beta(to_f32(fz.ba[t * fz.bts + j * H + hv]));
+            if (j == 0) gd_in = gate_g(to_f32(fz.ba[t * fz.bts + M * H + hv]), fz.A_log[hv], fz.dt_bias[hv]);
+        }
+#pragma unroll
+        for (int it = 0; it < VPT; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
+            if (row < n) *(uint4 *)(fz.v + ((r0 + row) * H + hv) * (int64_t)VD + cu16 * E) = vreg[it];
+        }
+        if (wv == 0 && e_in) {
+            const int64_t t = e_row / M;
+            fz.beta[e_row * H + hv] = b_in;
+            if (e_row - t * M == 0) fz.g[t * H + hv] = gd_in;
+        }
+#pragma unroll
+        for (int it = 0; it < KPT; ++it) {
+            const int uidx = tid + 256 * it, row = uidx / KUPR, cu16 = uidx % KUPR;
             const int64_t e = r0 + row, t = e / M;
             const int j = (int)(e - t * M);
             if (row < n) {
-                val = *(const uint4 *)(fz.x + t * fz.xts + kb + ((int64_t)j * fz.G + grp) * KD + cu16 * E);
-                *(uint4 *)(fz.k + (e * H + hv) * (int64_t)KD + cu16 * E) = val;
-                if (j == 0)  // the token's query, once
-                    *(uint4 *)(fz.q + (t * H + hv) * (int64_t)KD + cu16 * E) =
-                        *(const uint4 *)(fz.x + t * fz.xts + qb + (int64_t)grp * KD + cu16 * E);
+                *(uint4 *)(fz.k + (e * H + hv) * (int64_t)KD + cu16 * E) = kreg[it];
+                if (j == 0) *(uint4 *)(fz.q + (t * H + hv) * (int64_t)KD + cu16 * E) = qreg[it];  // once per token
             }
-            *(uint4 *)(Ks + row * LDK + cu16 * E) = val;
-            const T *el = (const T *)&val;
+            *(uint4 *)(Ks + row * LDK + cu16 * E) = kreg[it];
+            const T *el = (const T *)&kreg[it];
             float sq = 0.f;
 #pragma unroll
             for (int i = 0; i < E; ++i) {
