@@ -9,7 +9,9 @@ GPU through the C ABI of libgdp.so:
                               inside it; the affine state map of each of 16
                               segments, composed in parallel; a scan over
                               the segments for the state entering each;
-                              chunk_h over all segments at once; chunk_o)
+                              chunk_h over all segments at once; chunk_o.
+                              The value copies and beta, which no stage after
+                              WY reads, are not stored unless --store-v-beta)
  or gdp_prefill_prepare then gdp_chunk_fwd_scan (--path scan: the same with
                               prepare as its own launch)
  or gdp_prefill_prepare then gdp_chunk_fwd_pipelined (--path pipelined:
@@ -32,7 +34,7 @@ oracle's throughput on the host cores as a reported baseline.  --stages adds a s
 times each stage on its own.
 
     python bench.py [--steps K] [--warmup W] [--path prefill-scan|scan|pipelined] [--segments S] [--stages]
-                    [--no-cpu-baseline] [--copy-mib N]
+                    [--no-cpu-baseline] [--copy-mib N] [--store-v-beta]
 """
 import argparse
 import ctypes
@@ -109,7 +111,8 @@ def algorithmic_bytes(w, T=None):
     es = 2 (bf16); beta, g, k_rnorm, gcum and kdecay are fp32.
       prepare  x, ba -> q, k, v, beta, g
       WY       k, v, beta, g -> w, u, k_rnorm, gcum, kdecay
-      chunk_h  k, kdecay, gcum, w, u -> v_new, h (one state per 64-row chunk)
+      chunk_h  k, kdecay, gcum, w, u -> v_new, h (one state per 64-row chunk;
+               the segment-parallel forms write one per 64-token chunk)
       chunk_o  q, k, k_rnorm, v_new, h (one per 64-token chunk), g -> o"""
     T = w["T"] * w["B"] if T is None else T
     M, H, HV, G, K, V = w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
@@ -235,6 +238,8 @@ def main():
                     help="segments of the chunk forward (default %d pipelined, %d scan)" % (SEGMENTS, SCAN_SEGMENTS))
     ap.add_argument("--stages", action="store_true", help="also time each stage sequentially (not overlapped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--store-v-beta", action="store_true",
+                    help="prefill-scan: also store the value copies and beta (no later stage reads them)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (untimed), "
@@ -257,7 +262,8 @@ def main():
     if args.segments is None:
         args.segments = SCAN_SEGMENTS if scan else SEGMENTS
     if fused:
-        w["path"] = "prefill_scan(recompute_w_u with prepare,seg_map,seg_scan,chunk_h,chunk_o)"
+        w["path"] = "prefill_scan(recompute_w_u with prepare,seg_map,seg_scan,chunk_h,chunk_o)" + (
+            "" if args.store_v_beta else "; v, beta not stored")
     elif scan:
         w["path"] = "prepare+scan(recompute_w_u,seg_map,seg_scan,chunk_h,chunk_o)"
     dev = torch.device("cuda:0")
@@ -284,7 +290,8 @@ def main():
         if fused:
             if ev:
                 ev[1].record(stream)
-            buf.prefill_scan(x, ba, A_log, dt_bias, Gq, args.segments, stage_events=ev[2:] if ev else None)
+            buf.prefill_scan(x, ba, A_log, dt_bias, Gq, args.segments, stage_events=ev[2:] if ev else None,
+                             store_v_beta=args.store_v_beta)
             return
         G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
         if ev:
@@ -313,7 +320,10 @@ def main():
     if scan:
         # chunk_h: one launch over every segment at once, bracketed on its stream
         seg_ms = [e[3].elapsed_time(e[4]) for e in evs]
-        ch_bytes = ab["gdp_chunk_h"]
+        # this form writes only the states entering each 64-token chunk
+        # (the ones chunk_o reads), not one per 64-row chunk
+        ch_bytes = ab["gdp_chunk_h"] - (math.ceil(w["T"] * w["M"] / 64) - math.ceil(w["T"] / 64)) * w["B"] \
+            * w["HV"] * w["V"] * w["K"] * 2
         map_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     else:
         # chunk_h: every segment launch, bracketed on its own stream
@@ -326,6 +336,8 @@ def main():
         prep_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
         pw = ab["gdp_prefill_prepare"] + ab["gdp_recompute_w_u"] - (
             w["T"] * w["M"] * w["HV"] * (w["K"] + w["V"]) * 2 + w["T"] * w["M"] * w["HV"] * 4 + w["T"] * w["HV"] * 4)
+        if not args.store_v_beta:  # nor prepare's writes of the value copies and beta
+            pw -= w["T"] * w["M"] * w["HV"] * (w["V"] * 2 + 4)
     if fused:
         # prepare's bytes plus WY's, less WY's reads of the key and value
         # copies, beta and g (they stay on chip)

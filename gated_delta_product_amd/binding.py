@@ -351,11 +351,13 @@ class ChunkBuffers:
         return self._pipelined(lambda ws, ev, s: lib().gdp_chunk_fwd_pipelined(
             ctypes.byref(self.args), int(num_segments), ws, ev, s), num_segments, stream, chunk_h_events)
 
-    def prefill_scan(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, stage_events=None):
+    def prefill_scan(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, stage_events=None,
+                     store_v_beta=True):
         """gdp_prefill_fwd_scan: prepare x / ba into this buffer's q, k, v,
         beta, g (allocated with the prepare shapes) inside the WY stage of the
         segment-parallel forward.  Arguments as prefill_prepare and
-        forward_scan."""
+        forward_scan.  store_v_beta=False passes v and beta as NULL: nothing
+        after the WY stage reads them, and they are left untouched."""
         _need_cuda(x, ba, A_log, dt_bias)
         d = self.dims
         if x.dim() != 3 or x.stride(2) != 1 or ba.dim() != 3 or ba.stride(2) != 1:
@@ -365,15 +367,21 @@ class ChunkBuffers:
         pa = PrepareArgs(x=x.data_ptr(), x_n_stride=x.stride(0), x_t_stride=x.stride(1), ba=ba.data_ptr(),
                          ba_n_stride=ba.stride(0), ba_t_stride=ba.stride(1), A_log=A_log.data_ptr(),
                          dt_bias=dt_bias.data_ptr(), G=int(num_groups))
+        args = self.args
+        if not store_v_beta:
+            args = type(self.args).from_buffer_copy(self.args)
+            args.v, args.beta = None, None
         return self._scan(lambda ws, nb, ev, s: lib().gdp_prefill_fwd_scan(
-            ctypes.byref(pa), ctypes.byref(self.args), int(num_segments), ws, nb, ev, s), num_segments, stream,
+            ctypes.byref(pa), ctypes.byref(args), int(num_segments), ws, nb, ev, s), num_segments, stream,
             stage_events)
 
     def forward_scan(self, num_segments, stream=None, stage_events=None):
         """gdp_chunk_fwd_scan: the results of forward() for B == 1 without
         cu_seqlens (to rounding past the first segment), with the serial
         chunk_h chain cut into num_segments segments run in parallel from
-        the states a scan over the segments' composed maps gives.
+        the states a scan over the segments' composed maps gives.  Of h only
+        the states entering chunks i*M (the ones chunk_o reads) are written;
+        the other slots keep what they held.
         stage_events: optional 3 torch.cuda.Event (timing enabled, recorded
         at least once) recorded before the segment maps, before chunk_h and
         after it."""

@@ -44,7 +44,9 @@ gdp_status hip_status(hipError_t e, const char *what) {
 }
 
 // Stage masks for validation.
-enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u };
+// stages of a call; ST_WYP is WY with the prepare fused in, which takes its
+// values and beta from the activations, so it needs neither tensor
+enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u, ST_WYP = 8u };
 
 gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParams *out) {
     if (!a) return fail(GDP_ERR_INVALID, "args is NULL");
@@ -88,10 +90,11 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
         const void *p;
         const char *name;
     } needs[] = {
-        {ST_O, a->q, "q"},           {ST_WY | ST_H | ST_O, a->k, "k"}, {ST_WY, a->v, "v"},
-        {ST_WY, a->beta, "beta"},    {ST_WY | ST_O, a->k_rnorm, "k_rnorm"},
-        {ST_WY | ST_H, a->gcum, "gcum"},    {ST_WY | ST_H, a->kdecay, "kdecay"},
-        {ST_WY | ST_H, a->w, "w"},   {ST_WY | ST_H, a->u, "u"},        {ST_H | ST_O, a->v_new, "v_new"},
+        {ST_O, a->q, "q"},           {ST_WY | ST_WYP | ST_H | ST_O, a->k, "k"}, {ST_WY, a->v, "v"},
+        {ST_WY, a->beta, "beta"},    {ST_WY | ST_WYP | ST_O, a->k_rnorm, "k_rnorm"},
+        {ST_WY | ST_WYP | ST_H, a->gcum, "gcum"},    {ST_WY | ST_WYP | ST_H, a->kdecay, "kdecay"},
+        {ST_WY | ST_WYP | ST_H, a->w, "w"},   {ST_WY | ST_WYP | ST_H, a->u, "u"},
+        {ST_H | ST_O, a->v_new, "v_new"},
         {ST_H | ST_O, a->h, "h"},    {ST_O, a->o, "o"},
     };
     if (!empty) {
@@ -159,7 +162,8 @@ static gdp_status prepare_check(const char *name, bool decode, const void *x, in
                                 int64_t x_t_stride, const void *ba, int64_t ba_n_stride, int64_t ba_t_stride,
                                 const float *A_log, const float *dt_bias, int64_t n, int64_t T, int32_t M,
                                 int32_t H, int32_t G, int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k,
-                                void *v, float *beta, float *g, gdp::PrepareParams *out) {
+                                void *v, float *beta, float *g, gdp::PrepareParams *out,
+                                bool vb_optional = false) {
     *out = gdp::PrepareParams{};
     if (dtype != GDP_F32 && dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "%s: unknown dtype %d", name, (int)dtype);
     if (n < 0 || T < 0) return fail(GDP_ERR_INVALID, "%s: n and T must be >= 0", name);
@@ -171,7 +175,7 @@ static gdp_status prepare_check(const char *name, bool decode, const void *x, in
     if (x_t_stride < 0 || x_n_stride < 0 || ba_t_stride < 0 || ba_n_stride < 0)
         return fail(GDP_ERR_INVALID, "%s: strides must be >= 0", name);
     if (n == 0 || T == 0) return ok();  // *out stays empty
-    if (!x || !ba || !A_log || !dt_bias || !q || !k || !v || !beta || !g)
+    if (!x || !ba || !A_log || !dt_bias || !q || !k || (!v && !vb_optional) || (!beta && !vb_optional) || !g)
         return fail(GDP_ERR_INVALID, "%s: a tensor pointer is NULL", name);
     if (T > 1 && x_t_stride < width) return fail(GDP_ERR_INVALID, "%s: x rows overlap (t stride %lld < width %lld)",
                                                  name, (long long)x_t_stride, (long long)width);
@@ -468,7 +472,7 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
                             int32_t num_segments, void *workspace, int64_t workspace_bytes,
                             void *const *stage_events, void *stream) {
     gdp::ChunkParams p;
-    gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
+    gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | ST_H | ST_O, &p);
     if (st != GDP_OK) return st;
     if (a->cu_seqlens) return fail(GDP_ERR_INVALID, "%s: cu_seqlens must be NULL", name);
     if (a->B != 1) return fail(GDP_ERR_INVALID, "%s: B must be 1 (got %lld)", name, (long long)a->B);
@@ -501,6 +505,10 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
     ha.ht = sp.hstart;
     gdp::ChunkParams hp;
     if ((st = check_chunk(&ha, ST_H, &hp)) != GDP_OK) return st;
+    // only the states chunk_o reads: the one entering each 64-token chunk.
+    // Every segment starts on a 64-token boundary, so counting chunks per
+    // segment keeps the whole sequence's c % M.
+    hp.hstep = a->M;
     hipStream_t s = (hipStream_t)stream;
     if ((st = hip_status(prep ? gdp::launch_wy_prepare(p, *prep, s) : gdp::launch_wy(p, s),
                          "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK)
@@ -541,7 +549,7 @@ gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *pa, const gdp_chunk_args
     const gdp_status st = prepare_check("gdp_prefill_fwd_scan", false, pa->x, pa->x_n_stride, pa->x_t_stride, pa->ba,
                                         pa->ba_n_stride, pa->ba_t_stride, pa->A_log, pa->dt_bias, a->B, a->T, a->M,
                                         a->H, pa->G, a->V, a->K, a->dtype, (void *)a->q, (void *)a->k,
-                                        (void *)a->v, (float *)a->beta, (float *)a->g, &pp);
+                                        (void *)a->v, (float *)a->beta, (float *)a->g, &pp, true);
     if (st != GDP_OK) return st;
     if (pp.T > 0 && !pp.vec16)
         return fail(GDP_ERR_UNSUPPORTED, "gdp_prefill_fwd_scan: x rows and outputs must be 16-byte aligned");

@@ -11,6 +11,13 @@
 // cumulative decay gcum on its last row) and kdecay = rnorm(k) exp2(gl - gcum)
 // per row, both precomputed by the WY stage.
 //
+// hstep > 1 writes only the snapshots of chunks c with c % hstep == 0 (c
+// counted from the sequence's first chunk).  With hstep = M these are the
+// states the output stage reads (it takes the state entering each 64-token
+// chunk, which is expanded chunk c = i*M); the other slots of h are left as
+// they were.  A skipped store keeps its instruction but gets an empty buffer
+// range, so the hardware drops it and nothing else in the schedule changes.
+//
 // One block of five waves per (sequence, value head, 16 value columns), with
 // three roles (the two-slice form is described below):
 //
@@ -70,7 +77,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
               const float *__restrict__ h0, float *__restrict__ ht, T *__restrict__ v_new,
-              T *__restrict__ hout, int64_t uv_ss) {
+              T *__restrict__ hout, int64_t uv_ss, int hstep) {
     typedef typename Frag<T>::type FragT;
     typedef typename Frag<T>::half HalfT;
     constexpr int ES = (int)sizeof(T);
@@ -289,7 +296,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         char *ph = (char *)(hout + (cbase * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl0) * KD);
         const int64_t sth = (int64_t)HV * VD * KD * ES;
         auto store_h = [&](int c) {
-            const rsrc_t rh = make_rsrc(ph, c < hlim ? (uint32_t)(NP * 16 * KD * ES) : 0u);
+            const rsrc_t rh = make_rsrc(ph, c < hlim && c % hstep == 0 ? (uint32_t)(NP * 16 * KD * ES) : 0u);
 #pragma unroll
             for (int pp = 0; pp < NP; ++pp) {
                 const T *src = Hs[SNAP_LDS ? (c & 1) : 0][pp];
@@ -382,13 +389,13 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         }
     // the state entering chunk cc: staged in LDS for the memory waves, or
     // stored straight to h (16 bytes per lane and tile pair; none at or past
-    // h_chunks)
+    // h_chunks, nor where cc % hstep != 0)
     const int64_t hroom_c = h_chunks - cbase;
     const int hlim_c = hroom_c < 0 ? 0 : (hroom_c > nch ? nch : (int)hroom_c);
     auto put_snapshot = [&](int cc) {
         if constexpr (!SNAP_LDS) {
             const T *base = hout + ((cbase + cc) * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl) * KD;
-            const rsrc_t rh = make_rsrc(base, cc < hlim_c ? (uint32_t)(16 * KD * ES) : 0u);
+            const rsrc_t rh = make_rsrc(base, cc < hlim_c && cc % hstep == 0 ? (uint32_t)(16 * KD * ES) : 0u);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 buf_store16(rh, (uint32_t)((lc * KD + kw * KH + 32 * ks + 8 * lg) * ES),
@@ -577,7 +584,8 @@ static hipError_t launch_chunk_h_np(const ChunkParams &p, hipStream_t stream) {
     const int64_t nblk = ((P + 7) / 8) * 8 * SG;
     hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD, NP>), dim3((unsigned)nblk), dim3((2 * NP + 3) * 64), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
-                       p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h, p.uv_ss);
+                       p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h, p.uv_ss,
+                       p.hstep);
     return hipGetLastError();
 }
 

@@ -36,6 +36,9 @@ struct ChunkParams {
     // elements between consecutive slices (T*M*16 for a plain call; the
     // whole sequence's for one segment of the pipelined forward)
     int64_t uv_ss;
+    // chunk_h writes the state snapshot of chunk c (counted per sequence)
+    // only when c % hstep == 0; 1 writes them all
+    int hstep = 1;
 };
 
 // Element offset of (batch row b, expanded row e relative to the batch row,

@@ -46,7 +46,9 @@ template <typename T> struct Pad { static constexpr int value = 16 / (int)sizeof
 // inputs straight from the post-conv activations x and ba (layouts of
 // core.ssm.ops.gdp.prepare, gdp_prefill_prepare), writes prepare's outputs
 // for them (q, k, v, beta, g, exactly as the prepare kernel does; q and g of
-// a token by the block holding its copy 0) and uses the same values.
+// a token by the block holding its copy 0) and uses the same values.  v and
+// beta may be NULL: no later stage reads them (the values enter u here), so
+// they are then not stored.
 template <typename T>
 struct WyFuse {
     const T *x;
@@ -154,14 +156,16 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             b_in = gate_beta(to_f32(fz.ba[t * fz.bts + j * H + hv]));
             if (j == 0) gd_in = gate_g(to_f32(fz.ba[t * fz.bts + M * H + hv]), fz.A_log[hv], fz.dt_bias[hv]);
         }
+        if (fz.v != nullptr) {
 #pragma unroll
-        for (int it = 0; it < VPT; ++it) {
-            const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
-            if (row < n) *(uint4 *)(fz.v + ((r0 + row) * H + hv) * (int64_t)VD + cu16 * E) = vreg[it];
+            for (int it = 0; it < VPT; ++it) {
+                const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
+                if (row < n) *(uint4 *)(fz.v + ((r0 + row) * H + hv) * (int64_t)VD + cu16 * E) = vreg[it];
+            }
         }
         if (wv == 0 && e_in) {
             const int64_t t = e_row / M;
-            fz.beta[e_row * H + hv] = b_in;
+            if (fz.beta != nullptr) fz.beta[e_row * H + hv] = b_in;
             if (e_row - t * M == 0) fz.g[t * H + hv] = gd_in;
         }
 #pragma unroll

@@ -361,13 +361,15 @@ gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_
  *                   `stream` right before the segment maps, right before
  *                   the chunk_h launch (after the scan) and right after it
  *                   (for timing those stages).
- * Every tensor of `a` is as for gdp_chunk_fwd.  w, u, k_rnorm, gcum and
- * kdecay are bit-identical to gdp_chunk_fwd, and so are h, v_new and o over
- * the first segment; the states entering later segments come out of the
- * composed maps, so h, v_new, o and ht there agree with gdp_chunk_fwd to
- * rounding (the
- * composition runs on bf16 matrix-core operands with fp32 accumulation,
- * like the chunk recurrence itself).  Supported: dtype bf16 with K, V in
+ * Every tensor of `a` is as for gdp_chunk_fwd, except h: only the states
+ * entering chunks c = i*M (those entering each 64-token chunk, the ones
+ * gdp_chunk_o reads) are written; the other slots of h are left untouched.
+ * w, u, k_rnorm, gcum and kdecay are bit-identical to gdp_chunk_fwd, and so
+ * are the written h, v_new and o over the first segment; the states entering
+ * later segments come out of the composed maps, so h, v_new, o and ht there
+ * agree with gdp_chunk_fwd to rounding (the composition runs on bf16
+ * matrix-core operands with fp32 accumulation, like the chunk recurrence
+ * itself).  Supported: dtype bf16 with K, V in
  * {64, 128} and T*M*V*2 < 2^31; other shapes return GDP_ERR_UNSUPPORTED.
  */
 #define GDP_SCAN_MAX_SEGMENTS 64
@@ -383,8 +385,10 @@ gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, voi
  * the token's copy 0) and uses them, so the key and value copies are not
  * read back from HBM.  Prepare writes the chunk arguments' q, k, v, beta and
  * g (which must therefore be writable, g not NULL, and HV == H: prepare
- * makes H value heads).  Every output is bit-identical to the two calls in
- * sequence.  The requirements are those of gdp_chunk_fwd_scan (B == n == 1)
+ * makes H value heads).  v and beta may be NULL: no stage after WY reads
+ * them (the values enter u inside it), so they are then not stored, which
+ * saves their HBM writes; every other output is unchanged.  Every output is
+ * bit-identical to the two calls in sequence.  The requirements are those of gdp_chunk_fwd_scan (B == n == 1)
  * and of gdp_prefill_prepare, plus 16-byte aligned rows of x and of the
  * outputs; stage_events as for gdp_chunk_fwd_scan (the first one is
  * recorded after the WY-with-prepare stage).

@@ -320,3 +320,11 @@ def test_prefill_scan_rejects():
     assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(), 0, ws, big, None, None) == B.GDP_ERR_INVALID
     assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(), 2, ws, 64, None, None) == B.GDP_ERR_INVALID
     assert B.lib().gdp_last_error()
+    # v and beta may be NULL here (not stored): the call gets as far as the
+    # workspace check; the plain scan form still needs them
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(v=None, beta=None), 2, ws, 64, None, None) == B.GDP_ERR_INVALID
+    assert b"workspace" in B.lib().gdp_last_error()
+    assert L.gdp_chunk_fwd_scan(a(v=None), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert b"v is NULL" in B.lib().gdp_last_error()
+    assert L.gdp_chunk_fwd_scan(a(beta=None), 2, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert b"beta is NULL" in B.lib().gdp_last_error()

@@ -47,11 +47,12 @@ def _seqs_varlen(cu, M):
 
 
 def check_chunk(q, k, v, beta, g, seqs, hv_list, M, scale=None, cu=None, cu_host=None, tag="",
-                want_wu=True, buf=None, h0=None):
+                want_wu=True, buf=None, h0=None, hstep=1):
     """Run the GPU forward (unless buf is given) and compare o, v_new, h, w, u
     (and the final state when an initial state h0 [nseq,HV,V,K] is given)
     with the oracle on the listed (sequence, value head) pairs.  g may be
-    None (ungated)."""
+    None (ungated).  hstep > 1 compares only the states entering chunks
+    c % hstep == 0 (the ones the segment-parallel forward writes)."""
     dt = q.dtype
     tol = TOL[dt]
     H, HV, K = q.shape[2], v.shape[2], q.shape[3]
@@ -88,7 +89,7 @@ def check_chunk(q, k, v, beta, g, seqs, hv_list, M, scale=None, cu=None, cu_host
         nc = math.ceil((t1 - t0) * M / 64)
         accs["o"].add(f32(buf.o[b, t0:t1, hv]), r["o"], bf)
         accs["v_new"].add(f32(vn_rows[b, t0 * M:t1 * M, hv]), r["v_new"], bf)
-        accs["h"].add(f32(buf.h[hbase:hbase + nc, hv]), r["h"], bf)
+        accs["h"].add(f32(buf.h[hbase:hbase + nc:hstep, hv]), r["h"][::hstep], bf)
         if want_wu:
             accs["w"].add(f32(buf.w[b, t0 * M:t1 * M, hv]), r["w"], bf)
             accs["u"].add(f32(u_rows[b, t0 * M:t1 * M, hv]), r["u"], bf)
@@ -677,7 +678,10 @@ def test_hip_graph_capture_replays():
         for nm in ("o", "w", "u", "v_new", "h"):
             assert torch.equal(getattr(seq, nm), getattr(ref, nm)), "sequential " + nm
             assert torch.equal(getattr(pip, nm), getattr(ref, nm)), "pipelined " + nm
-            assert torch.equal(getattr(scn, nm), getattr(ref_scn, nm)), "scan " + nm
+            got, want = getattr(scn, nm), getattr(ref_scn, nm)
+            if nm == "h":  # the scan form writes only the states entering chunks c % M == 0
+                got, want = got[::M], want[::M]
+            assert torch.equal(got, want), "scan " + nm
         assert torch.equal(pip.ht, ref_ht), "pipelined ht"
         assert torch.equal(scn.ht, ref_scn.ht), "scan ht"
         assert torch.equal(dec_o, ref_o) and torch.equal(seq.ht, ref.ht), "decode"
@@ -685,15 +689,31 @@ def test_hip_graph_capture_replays():
 
 # --------------------------------------------- segment-parallel state recurrence
 
+H_MARK = 7.0  # a bf16 value no snapshot of these draws takes in every element
+
+
+def _check_unwritten_h(buf, M):
+    """The segment-parallel forward writes only the states entering chunks
+    c % M == 0; every other slot must still hold the mark put there before."""
+    if M > 1:
+        keep = torch.ones(buf.h.shape[0], dtype=torch.bool, device=buf.h.device)
+        keep[::M] = False
+        rest = buf.h[keep]
+        assert bool((rest == H_MARK).all()), "a skipped state slot was written"
+        assert not bool((buf.h[::M] == H_MARK).all()), "the written state slots were not written"
+
+
 def _scan_buf(q, k, v, beta, g, nseg, h0=None):
     buf = G.ChunkBuffers(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), None if g is None else g.to(DEV),
                          initial_state=None if h0 is None else h0.to(DEV), output_final_state=h0 is not None)
+    buf.h.fill_(H_MARK)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     for e in evs:
         e.record()  # creates the HIP event
     buf.forward_scan(nseg, stage_events=evs)
     torch.cuda.synchronize()
     assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
+    _check_unwritten_h(buf, buf.dims["M"])
     return buf
 
 
@@ -732,7 +752,8 @@ def test_scan_forward_matches_oracle(case):
     n = G.scan_segments(T, nseg)
     log("scan %s: %d segments" % (case, n))
     buf = _scan_buf(d["q"], d["k"], d["v"], beta, g, nseg, h0)
-    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(B_, T, M), range(HV), M, tag="scan", buf=buf, h0=h0)
+    check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(B_, T, M), range(HV), M, tag="scan", buf=buf, h0=h0,
+                hstep=M)
     ref = G.chunk_fwd(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), beta.to(DEV),
                       None if g is None else g.to(DEV), initial_state=None if h0 is None else h0.to(DEV),
                       output_final_state=h0 is not None)
@@ -743,7 +764,7 @@ def test_scan_forward_matches_oracle(case):
     t1 = min(T, seg_tok)
     c1 = (t1 * M + 63) // 64
     assert torch.equal(ref.o[:, :t1], buf.o[:, :t1])
-    assert torch.equal(ref.h[:c1], buf.h[:c1])
+    assert torch.equal(ref.h[:c1:M], buf.h[:c1:M])
     assert torch.equal(ref.v_new[..., :t1 * M, :], buf.v_new[..., :t1 * M, :])
 
 
@@ -775,11 +796,11 @@ def test_scan_adds_no_error_long_memory(case):
         r = oracle_pair(f32(d["q"][0, :, hk]), f32(d["k"][0, :, hk]), f32(d["v"][0, :, hv]), f32(beta[0, :, hv]),
                         f32(g[0, :, hv]), M, 1.0 / math.sqrt(K), False)
         for nm in ("o", "h", "v_new"):
-            r2[nm] = r2.get(nm, 0.0) + float((r[nm] ** 2).sum())
+            r2[nm] = r2.get(nm, 0.0) + float(((r[nm][::M] if nm == "h" else r[nm]) ** 2).sum())
         for tag, b in (("seq", seq), ("scan", sc)):
-            got = {"o": f32(b.o[0, :, hv]), "h": f32(b.h[:nc, hv]), "v_new": f32(G.slices_to_rows(b.v_new)[0, :, hv])}
+            got = {"o": f32(b.o[0, :, hv]), "h": f32(b.h[:nc:M, hv]), "v_new": f32(G.slices_to_rows(b.v_new)[0, :, hv])}
             for nm, x in got.items():
-                e = x.astype(np.float64) - r[nm]
+                e = x.astype(np.float64) - (r[nm][::M] if nm == "h" else r[nm])
                 err[tag][nm] = err[tag].get(nm, 0.0) + float((e * e).sum())
     for nm in ("o", "h", "v_new"):
         es, ec = math.sqrt(err["seq"][nm] / r2[nm]), math.sqrt(err["scan"][nm] / r2[nm])
@@ -796,7 +817,7 @@ def test_scan_long_prefill_sampled():
     log("long_prefill scan: inputs drawn")
     buf = _scan_buf(d["q"], d["k"], d["v"], beta, g, 16)
     check_chunk(d["q"], d["k"], d["v"], beta, g, _seqs_equal(c["B"], c["T"], c["M"]), [0, 9, 15], c["M"],
-                tag="long_prefill_32k scan", buf=buf)
+                tag="long_prefill_32k scan", buf=buf, hstep=c["M"])
 
 
 @pytest.mark.parametrize("K,V,M", [(128, 128, 2), (64, 256, 3), (128, 64, 1)])
@@ -846,16 +867,20 @@ def test_prefill_scan_is_bit_identical(case):
     """gdp_prefill_fwd_scan (prepare done inside the WY stage) gives exactly
     the outputs of gdp_prefill_prepare then gdp_chunk_fwd_scan: q, k, v, beta,
     g and every chunk output, with an initial state, ragged tails, M = 1..3,
-    GQA groups, and the timed workload (T = 32768, 16 heads, 16 segments)."""
+    GQA groups, and the timed workload (T = 32768, 16 heads, 16 segments).
+    With v and beta passed as NULL they stay untouched and nothing else
+    changes."""
     T, M, H, G_, P, N, nseg = case
     d = synth.prepare_draws(1, T, M, H, G_, P, N, "bf16", synth.seed_of(4) + 300 + T % 97)
     x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
     pre = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, G_, P, N)
     h0 = synth.initial_state_draws(1, H, P, N, synth.seed_of(4) + 301).to(DEV)
     ref = G.ChunkBuffers(*pre, initial_state=h0, output_final_state=True)
+    ref.h.fill_(H_MARK)
     ref.forward_scan(nseg)
     outs = [torch.full_like(t, 7) for t in pre]  # the fused prepare must overwrite all of them
     fz = G.ChunkBuffers(*outs, initial_state=h0, output_final_state=True)
+    fz.h.fill_(H_MARK)  # the slots neither call writes then match as well
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     for e in evs:
         e.record()
@@ -865,3 +890,17 @@ def test_prefill_scan_is_bit_identical(case):
         assert torch.equal(a_, b_), nm
     for nm in ("o", "w", "u", "v_new", "h", "ht", "k_rnorm", "gcum", "kdecay"):
         assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
+    _check_unwritten_h(fz, M)
+    # v and beta passed as NULL: not stored, every other output unchanged
+    outs2 = [torch.full_like(t, 7) for t in pre]
+    nv = G.ChunkBuffers(*outs2, initial_state=h0, output_final_state=True)
+    nv.h.fill_(H_MARK)
+    nv.prefill_scan(x, ba, A_log, dt_bias, G_, nseg, store_v_beta=False)
+    torch.cuda.synchronize()
+    for a_, b_, nm in zip(outs2, pre, ("q", "k", "v", "beta", "g")):
+        if nm in ("v", "beta"):
+            assert bool((a_ == 7).all()), nm + " was written"
+        else:
+            assert torch.equal(a_, b_), nm
+    for nm in ("o", "w", "u", "v_new", "h", "ht", "k_rnorm", "gcum", "kdecay"):
+        assert torch.equal(getattr(nv, nm), getattr(ref, nm)), "without v, beta: " + nm
