@@ -726,6 +726,10 @@ SCAN_CASES = [
     (1, 513, 2, 2, 128, 64, 1, 3, 35, True, True, True),
     (1, 300, 2, 2, 64, 64, 2, 64, 36, True, True, False),
     (1, 64, 1, 1, 128, 128, 4, 8, 37, True, False, True),
+    # shorter than a chunk, one token past one, and a 1-token last segment
+    (1, 1, 1, 1, 64, 64, 2, 4, 38, True, False, True),
+    (1, 65, 2, 2, 128, 128, 2, 4, 39, True, True, True),
+    (1, 129, 1, 2, 64, 128, 3, 3, 40, True, False, False),
 ]
 
 
@@ -861,6 +865,7 @@ def test_chunk_h_two_pairs_per_block(K, V, M):
 
 
 @pytest.mark.parametrize("case", [(1000, 2, 4, 2, 128, 128, 5), (700, 3, 2, 1, 64, 64, 4), (513, 1, 4, 4, 128, 64, 3),
+                                  (1, 2, 2, 1, 64, 64, 4), (65, 4, 2, 2, 128, 128, 2),
                                   (32768, 2, 16, 16, 128, 128, 16)],
                          ids=lambda c: "T%d-M%d-H%d-G%d-P%d-N%d-s%d" % c)
 def test_prefill_scan_is_bit_identical(case):
