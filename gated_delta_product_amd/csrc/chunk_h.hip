@@ -71,8 +71,8 @@ struct HStage {
     float gc[C];           // cumulative log2 decay per row
 };
 
-template <typename T, int KD, int VD, int NP>
-__global__ void __launch_bounds__((2 * NP + 3) * 64)
+template <typename T, int KD, int VD, int NP, bool FK>
+__global__ void __launch_bounds__(((FK ? NP : 2 * NP) + 3) * 64)
 gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T *__restrict__ w,
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
@@ -92,6 +92,11 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     // an LDS staging area; with two, the compute waves store their own (a
     // 16-byte store per state tile pair), which keeps the block within LDS.
     constexpr bool SNAP_LDS = NP == 1;
+    // FK: one compute wave per slice holds both K halves of its state (no
+    // exchange of partial products); otherwise two waves per slice, one per
+    // K half, swap their phase-1 partials through LDS
+    constexpr int NC = FK ? NP : 2 * NP;       // compute waves
+    static_assert(!FK || (NP > 1 && !SNAP_LDS), "the whole-K form stores its own snapshots");
     constexpr int NX = NP == 1 ? NS : 2;       // exchange buffers (by stage, or by step parity)
     constexpr int NKT = KH / 16;               // 16-row state tiles per compute wave
     constexpr int NKS = KH / 32;               // phase-1 contraction steps per wave
@@ -113,7 +118,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     static_assert(SB % 16 == 0, "stage size");
 
     __shared__ __attribute__((aligned(16))) HStage<T, KD, NP> ring[NS];
-    __shared__ __attribute__((aligned(16))) f32x4 Xs[NX][NP][2][4][64];  // [buffer][pair][wave][row tile][lane]
+    __shared__ __attribute__((aligned(16))) f32x4 Xs[FK ? 1 : NX][FK ? 1 : NP][FK ? 1 : 2][FK ? 1 : 4][64];  // [buffer][pair][wave][row tile][lane]
     __shared__ __attribute__((aligned(16))) T Vt[2][NP][16 * LDT];       // [parity][pair] v_new, column-major
     __shared__ __attribute__((aligned(16))) T Hs[SNAP_LDS ? 2 : 1][NP][SNAP_LDS ? 16 * LDH : 8];  // [parity][pair] snapshot rows (V x K)
     __shared__ __attribute__((aligned(16))) char Pf[1024];            // landing area of L2 prefetches
@@ -139,7 +144,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 
     const int lane = lane_id(), wave = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
-    const int sl = sl0 + (wave < 2 * NP ? wave >> 1 : 0);  // a compute wave's slice
+    const int sl = sl0 + (wave < NC ? (FK ? wave : wave >> 1) : 0);  // a compute wave's slice
     // The fp32 state of compute wave kw in its permuted K order (see below):
     // element (kt, q) is S[16sl + lc][kw*KH + 32(kt/2) + 8lg + 4(kt%2) + q],
     // four consecutive K indices per (kt), i.e. one 16-byte unit of h0 / ht.
@@ -147,11 +152,14 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         return ((seq * HV + hv) * (int64_t)VD + 16 * sl + lc) * KD + kw_ * KH + 32 * (kt >> 1) + 8 * lg + 4 * (kt & 1);
     };
     if (nch == 0) {  // empty sequence: the final state is the initial one
-        if (ht != nullptr && wave < 2 * NP) {
+        if (ht != nullptr && wave < NC) {
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt)
-                *(f32x4 *)(ht + state_off(wave & 1, kt)) =
-                    h0 ? *(const f32x4 *)(h0 + state_off(wave & 1, kt)) : zero4();
+            for (int h2 = 0; h2 < (FK ? 2 : 1); ++h2) {
+                const int kwe = FK ? h2 : (wave & 1);
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    *(f32x4 *)(ht + state_off(kwe, kt)) = h0 ? *(const f32x4 *)(h0 + state_off(kwe, kt)) : zero4();
+            }
         }
         return;
     }
@@ -168,7 +176,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
     };
 
-    if (wave == 2 * NP + 2) {
+    if (wave == NC + 2) {
         // ======================= prefetch wave =======================
         // Pulls the lines of chunk c + PF into L2 while the memory waves
         // stream chunk c + 2 into LDS, so their loads hit L2 instead of
@@ -217,9 +225,9 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         return;
     }
 
-    if (wave >= 2 * NP) {
+    if (wave >= NC) {
         // ======================= memory waves =======================
-        const int mw = wave - 2 * NP;
+        const int mw = wave - NC;
         const int64_t hroom = h_chunks - cbase;  // chunks whose snapshot fits below h_chunks
         const int hlim = hroom < 0 ? 0 : (hroom > nch ? nch : (int)hroom);
         const uint32_t ring_base = lds_addr(&ring[0]);
@@ -564,25 +572,177 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         for (int kt = 0; kt < NKT; ++kt) *(f32x4 *)(ht + state_off(kw, kt)) = hs[kt];
     }
     };
-    if (wave == 0)
-        compute(std::integral_constant<int, 0>{});
-    else if (wave == 1 || NP == 1)
-        compute(std::integral_constant<int, 1>{});
-    else if constexpr (NP == 2) {
-        if (wave == 2)
-            compute(std::integral_constant<int, 2>{});
-        else
-            compute(std::integral_constant<int, 3>{});
+
+    if constexpr (FK) {
+    // ============ compute waves, whole-K form (one wave per slice) ============
+    // The same arithmetic as the split form above, in the same order, so the
+    // bits match: the two K halves' phase-1 partials P0, P1 stay apart; v_new
+    // rows [32kw, 32kw + 32) are (u - P_kw) - P_other, and half kw's phase-2
+    // operand is fma(-P_other, kd, (u - P_kw) kd).  No exchange buffer and no
+    // partner: the one barrier per chunk stays where the split form has it.
+    auto compute_fk = [&](auto wc) {
+    constexpr int pp = decltype(wc)::value;  // slice of the block
+    f32x4 hs[2][NKT];
+#pragma unroll
+    for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = h0 ? *(const f32x4 *)(h0 + state_off(kw, kt)) : zero4();
+    FragT hb[2][NKS];
+    auto pack = [&]() {
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    hb[kw][ks][q] = from_f32<T>(hs[kw][2 * ks][q]);
+                    hb[kw][ks][4 + q] = from_f32<T>(hs[kw][2 * ks + 1][q]);
+                }
+    };
+    pack();
+    const int64_t hroom_c = h_chunks - cbase;
+    const int hlim_c = hroom_c < 0 ? 0 : (hroom_c > nch ? nch : (int)hroom_c);
+    auto put_snapshot = [&](int cc) {
+        const T *base = hout + ((cbase + cc) * HV + hv) * (int64_t)VD * KD + (int64_t)(16 * sl) * KD;
+        const rsrc_t rh = make_rsrc(base, cc < hlim_c && cc % hstep == 0 ? (uint32_t)(16 * KD * ES) : 0u);
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                buf_store16(rh, (uint32_t)((lc * KD + kw * KH + 32 * ks + 8 * lg) * ES),
+                            __builtin_bit_cast(uint4, hb[kw][ks]));
+    };
+    put_snapshot(0);      // h[0]: the initial state
+    lds_barrier();        // stage 0 landed
+    int rem = (int)rows;  // rows left from the current chunk
+
+    auto step = [&](int c, auto stc) {
+        constexpr int ST = decltype(stc)::value;
+        const HStage<T, KD, NP> &Sg = ring[ST];
+        const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // uniform
+
+        // phase 1: the partial products of the two K halves
+        f32x4 acc[2][4];
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                acc[kw][rt] = zero4();
+                const int r = 16 * rt + lc;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const FragT a = *(const FragT *)((const char *)Sg.w[kw] + swz(r, 32 * ks + 8 * lg));
+                    acc[kw][rt] = mma(a, hb[kw][ks], acc[kw][rt]);
+                }
+            }
+        // every other read of the stage, before the barrier that frees it
+        HalfT uu[4];
+        f32x4 kd4[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            uu[rt] = lds_col4<T>(Sg.u[pp], 16, 16 * rt + 4 * lg, 0);
+            kd4[rt] = *(const f32x4 *)(&Sg.kd[16 * rt + 4 * lg]);
+        }
+        const float glast = Sg.gc[n > 0 ? n - 1 : 0];
+        FragT ka[2][NKT][2];
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const char *kb = (const char *)Sg.k[kw];
+                    const int kbase = 32 * (kt >> 1) + 4 * (kt & 1);  // kperm(kt, 0)
+                    const int j = lane & 15;
+                    const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
+                    const int col = kbase + 8 * (j & 3);
+                    const HalfT x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
+                    const HalfT x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
+                    ka[kw][kt][s] = join<T>(x0, x1);
+                }
+        const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hs[kw][kt][q] *= gl;
+        lds_barrier();  // publishes the next stage; Vt[c & 1] is free again
+
+        FragT vb[2][2];
+        T *vt = Vt[c & 1][pp];
+        static_for<0, 4>([&](auto rtc) {
+            constexpr int rt = decltype(rtc)::value;
+            constexpr int ho = rt >> 1;  // the half whose rows these are
+            HalfT v4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float u = to_f32(uu[rt][q]);
+                const float ua0 = u - acc[0][rt][q], ua1 = u - acc[1][rt][q];
+                const float uk0 = ua0 * kd4[rt][q], uk1 = ua1 * kd4[rt][q];
+                v4[q] = from_f32<T>(ho == 0 ? ua0 - acc[1][rt][q] : ua1 - acc[0][rt][q]);
+                vb[0][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(__builtin_fmaf(-acc[1][rt][q], kd4[rt][q], uk0));
+                vb[1][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(__builtin_fmaf(-acc[0][rt][q], kd4[rt][q], uk1));
+            }
+            *(HalfT *)(&vt[lc * LDT + 16 * rt + 4 * lg]) = v4;
+        });
+
+        // phase 2, both halves: h = exp2(gl) h + K^T (kd * v_new)
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) hs[kw][kt] = mma(ka[kw][kt][s], vb[kw][s], hs[kw][kt]);
+        pack();
+        if (c + 1 < nch) put_snapshot(c + 1);  // the state entering chunk c + 1
+        rem -= C;
+    };
+
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    for (int c = 0; c < nch; c += 3) {
+        step(c, J0{});
+        if (c + 1 < nch) step(c + 1, J1{});
+        if (c + 2 < nch) step(c + 2, J2{});
+    }
+    lds_barrier();  // publishes the last chunk's v_new
+    if (ht != nullptr) {
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) *(f32x4 *)(ht + state_off(kw, kt)) = hs[kw][kt];
+    }
+    };
+
+        static_for<0, NP>([&](auto wc) {
+            if (wave == decltype(wc)::value) compute_fk(wc);
+        });
+    } else {
+        if (wave == 0)
+            compute(std::integral_constant<int, 0>{});
+        else if (wave == 1 || NP == 1)
+            compute(std::integral_constant<int, 1>{});
+        else if constexpr (NP == 2) {
+            if (wave == 2)
+                compute(std::integral_constant<int, 2>{});
+            else
+                compute(std::integral_constant<int, 3>{});
+        }
     }
 }
 
-template <typename T, int KD, int VD, int NP>
+template <typename T, int KD, int VD, int NP, bool FK = false>
 static hipError_t launch_chunk_h_np(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
     const int64_t P = p.nseq * a.HV;
     const int64_t SG = VD / 16 / NP;
     const int64_t nblk = ((P + 7) / 8) * 8 * SG;
-    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD, NP>), dim3((unsigned)nblk), dim3((2 * NP + 3) * 64), 0, stream,
+    constexpr int NC = FK ? NP : 2 * NP;
+    hipLaunchKernelGGL((gdp_chunk_h_k<T, KD, VD, NP, FK>), dim3((unsigned)nblk), dim3((NC + 3) * 64), 0, stream,
                        (const T *)a.k, a.kdecay, (const T *)a.w, (const T *)a.u, a.gcum, a.cu_seqlens,
                        p.nseq, a.T, a.H, a.HV, a.M, a.h_chunks, a.h0, a.ht, (T *)a.v_new, (T *)a.h, p.uv_ss,
                        p.hstep);
@@ -596,6 +756,9 @@ static hipError_t launch_chunk_h_np(const ChunkParams &p, hipStream_t stream) {
 // the same bits: every slice runs the same arithmetic.
 template <typename T, int KD, int VD>
 static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
+    if constexpr (std::is_same<T, bf16>::value && VD >= 128) {
+        if (p.nseq * p.a.HV * (VD / 64) >= 512) return launch_chunk_h_np<T, KD, VD, 4, true>(p, stream);
+    }
     if constexpr (std::is_same<T, bf16>::value && VD >= 32) {
         if (p.nseq * p.a.HV * (VD / 32) >= 512) return launch_chunk_h_np<T, KD, VD, 2>(p, stream);
     }

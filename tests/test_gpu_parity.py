@@ -824,18 +824,20 @@ def test_scan_long_prefill_sampled():
                 tag="long_prefill_32k scan", buf=buf, hstep=c["M"])
 
 
-@pytest.mark.parametrize("K,V,M", [(128, 128, 2), (64, 256, 3), (128, 64, 1)])
-def test_chunk_h_two_pairs_per_block(K, V, M):
-    """With many chains (here 64 packed requests x 16 value heads) chunk_h
-    runs two 16-column slices per block.  Its outputs are bit-identical to
-    the same requests run one call each (one slice per block), and match the
-    oracle on every (request, head), final states included; every request
-    starts from a given state; the requests include empty and one-token ones
-    and ragged tails."""
-    H, HV, n = 4, 16, 64
+@pytest.mark.parametrize("K,V,M,n", [(128, 128, 2, 64), (64, 256, 3, 64), (128, 64, 1, 64), (128, 128, 2, 12)])
+def test_chunk_h_two_pairs_per_block(K, V, M, n):
+    """With many chains (packed requests x 16 value heads) chunk_h runs
+    several 16-column slices per block: two (two waves per slice, one per K
+    half) for V = 64 and for 12 requests at V = 128, four (one wave per
+    slice holding the whole K) for 64 requests at V >= 128.  Its outputs are
+    bit-identical to the same requests run one call each (one slice per
+    block), and match the oracle on every (request, head), final states
+    included; every request starts from a given state; the requests include
+    empty and one-token ones and ragged tails."""
+    H, HV = 4, 16
     rng = np.random.default_rng(900 + K + V + M)
     lens = rng.integers(1, 90, size=n)
-    lens[[3, 17]] = 0
+    lens[[3, 17 if n > 17 else n - 2]] = 0
     lens[5] = 1
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     T = int(cu[-1])
