@@ -183,7 +183,10 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         // waiting on HBM.  The SG blocks of a head share an XCD (and its L2);
         // block slg prefetches rows [RPB slg, RPB slg + RPB) of each chunk.
         // The data lands in a scratch LDS area that nothing reads.
-        constexpr int PF = NP == 1 ? 5 : 3;      // prefetch distance in chunks
+        // prefetch distance in chunks; the whole-K form's two blocks per head
+        // need their lines within a step of each other (3 ahead: 1.34x the
+        // algorithmic bytes; 2 ahead is faster)
+        constexpr int PF = NP == 1 ? 5 : (FK ? 2 : 3);
         constexpr int RPB = C / SG;              // rows per block per chunk
         static_assert(RPB * KD * ES / 128 <= 64 && KD * ES >= 128,
                       "one 4-byte load per line must cover a block's rows");
