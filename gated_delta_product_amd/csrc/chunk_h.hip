@@ -71,12 +71,16 @@ struct HStage {
     float gc[C];           // cumulative log2 decay per row
 };
 
+// h0 and ht may be the same buffer (the segment-parallel forward hands each
+// segment its entering state and takes its final state in place): every
+// lane reads its own 16-byte units of h0 before the chain starts and writes
+// the same units of ht after it ends, so neither is declared __restrict__.
 template <typename T, int KD, int VD, int NP, bool FK>
 __global__ void __launch_bounds__(((FK ? NP : 2 * NP) + 3) * 64)
 gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T *__restrict__ w,
               const T *__restrict__ u, const float *__restrict__ gcum, const int32_t *__restrict__ cu,
               int64_t nseq, int64_t Ttok, int H, int HV, int M, int64_t h_chunks,
-              const float *__restrict__ h0, float *__restrict__ ht, T *__restrict__ v_new,
+              const float *h0, float *ht, T *__restrict__ v_new,
               T *__restrict__ hout, int64_t uv_ss, int hstep) {
     typedef typename Frag<T>::type FragT;
     typedef typename Frag<T>::half HalfT;
@@ -528,8 +532,9 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         lds_barrier();
 
         // v_new = (u - own) - other; the phase-2 operand kd * v_new as one
-        // fused multiply-add on the precomputed kd * (u - own)
-        FragT vb[2];
+        // fused multiply-add on the precomputed kd * (u - own), in bf16 as
+        // a high and a low part (split_lo), one product each
+        FragT vb[2], vbl[2];
         T *vt = Vt[c & 1][pp];
         static_for<0, 4>([&](auto rtc) {
             constexpr int rt = decltype(rtc)::value;
@@ -538,7 +543,9 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 v4[q] = from_f32<T>(ua[rt][q] - other[q]);
-                vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(__builtin_fmaf(-other[q], kd4[rt][q], uk[rt][q]));
+                const float x = __builtin_fmaf(-other[q], kd4[rt][q], uk[rt][q]);
+                vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x);
+                if constexpr (Split<T>::on) vbl[rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x, vb[rt >> 1][4 * (rt & 1) + q]);
             }
             // compute wave kw publishes rows [32kw, 32kw + 32)
             if constexpr ((rt >> 1) == kw) *(HalfT *)(&vt[lc * LDT + 16 * rt + 4 * lg]) = v4;
@@ -548,7 +555,10 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) hs[kt] = mma(ka[kt][s], vb[s], hs[kt]);
+            for (int s = 0; s < 2; ++s) {
+                hs[kt] = mma(ka[kt][s], vb[s], hs[kt]);
+                if constexpr (Split<T>::on) hs[kt] = mma(ka[kt][s], vbl[s], hs[kt]);
+            }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -674,7 +684,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 for (int q = 0; q < 4; ++q) hs[kw][kt][q] *= gl;
         lds_barrier();  // publishes the next stage; Vt[c & 1] is free again
 
-        FragT vb[2][2];
+        FragT vb[2][2], vbl[2][2];  // phase-2 operands: high and low bf16 parts
         T *vt = Vt[c & 1][pp];
         static_for<0, 4>([&](auto rtc) {
             constexpr int rt = decltype(rtc)::value;
@@ -686,8 +696,14 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 const float ua0 = u - acc[0][rt][q], ua1 = u - acc[1][rt][q];
                 const float uk0 = ua0 * kd4[rt][q], uk1 = ua1 * kd4[rt][q];
                 v4[q] = from_f32<T>(ho == 0 ? ua0 - acc[1][rt][q] : ua1 - acc[0][rt][q]);
-                vb[0][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(__builtin_fmaf(-acc[1][rt][q], kd4[rt][q], uk0));
-                vb[1][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(__builtin_fmaf(-acc[0][rt][q], kd4[rt][q], uk1));
+                const float x0 = __builtin_fmaf(-acc[1][rt][q], kd4[rt][q], uk0);
+                const float x1 = __builtin_fmaf(-acc[0][rt][q], kd4[rt][q], uk1);
+                vb[0][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x0);
+                vb[1][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x1);
+                if constexpr (Split<T>::on) {
+                    vbl[0][rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x0, vb[0][rt >> 1][4 * (rt & 1) + q]);
+                    vbl[1][rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x1, vb[1][rt >> 1][4 * (rt & 1) + q]);
+                }
             }
             *(HalfT *)(&vt[lc * LDT + 16 * rt + 4 * lg]) = v4;
         });
@@ -698,7 +714,10 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) hs[kw][kt] = mma(ka[kw][kt][s], vb[kw][s], hs[kw][kt]);
+                for (int s = 0; s < 2; ++s) {
+                    hs[kw][kt] = mma(ka[kw][kt][s], vb[kw][s], hs[kw][kt]);
+                    if constexpr (Split<T>::on) hs[kw][kt] = mma(ka[kw][kt][s], vbl[kw][s], hs[kw][kt]);
+                }
         pack();
         if (c + 1 < nch) put_snapshot(c + 1);  // the state entering chunk c + 1
         rem -= C;

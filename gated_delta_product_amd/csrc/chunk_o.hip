@@ -22,7 +22,8 @@
 // through LDS: the state slab (copied in with buffer_load ... lds) and the
 // copy's V_j slab.  Q and K_j fragments are plain 16-byte row reads straight
 // into registers.  That keeps LDS near 50 KB so three blocks share a CU and
-// one block's loads overlap another's math.  Norms enter as fp32 scales on
+// one block's loads overlap another's math.  In bf16 the fp32 scores enter
+// the P V product as a high and a low bf16 part (two products).  Norms enter as fp32 scales on
 // the scores and on the inter term; rows past the end of a sequence read as
 // zeros through the buffer range checks.
 #include "gdp_common.h"
@@ -216,8 +217,10 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     // ---- intra-chunk attention, one Householder copy at a time
     for (int j = 0; j < M; ++j) {
         sRk[wv][lane] = rkl;
-        // scores P^T tiles for key tiles st <= tt
-        FragT pb[2];
+        // scores P^T tiles for key tiles st <= tt, as a high and a low bf16
+        // part (the P V product runs once per part): one rounded bf16 score
+        // per entry was one of the larger errors of the bf16 path
+        FragT pb[2], pbl[2];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             f32x4 p = zero4();
@@ -227,7 +230,11 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
             }
             const f32x4 rk4 = *(const f32x4 *)&sRk[wv][16 * st + 4 * lg];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pb[st >> 1][4 * (st & 1) + i] = from_f32<T>(p[i] * dec[st][i] * rk4[i]);
+            for (int i = 0; i < 4; ++i) {
+                const float x = p[i] * dec[st][i] * rk4[i];
+                pb[st >> 1][4 * (st & 1) + i] = from_f32<T>(x);
+                if constexpr (Split<T>::on) pbl[st >> 1][4 * (st & 1) + i] = split_lo<T>(x, pb[st >> 1][4 * (st & 1) + i]);
+            }
         }
         if (j + 1 < M) load_k(j + 1);  // next copy's keys while this one's products run
         // O^T[vt] += V_j^T[vt, s] P^T[s, t]; contraction slot m <-> s = 32ks + 16(m/4) + 4lg + m%4
@@ -255,7 +262,9 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
                             x1[i] = *(const float *)(vb + v_at(vt, 32 * ks + 16 + 4 * lg + i, j) + lc * ES);
                         }
                     }
-                    acc[vt] = mma(join<T>(x0, x1), pb[ks], acc[vt]);
+                    const FragT vf = join<T>(x0, x1);
+                    acc[vt] = mma(vf, pb[ks], acc[vt]);
+                    if constexpr (Split<T>::on) acc[vt] = mma(vf, pbl[ks], acc[vt]);
                 }
             }
         }

@@ -54,6 +54,20 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
+// A float operand of a bf16 matrix-core product as a sum of two bf16 values:
+// hi = from_f32(x), x rounded to bf16, and lo = split_lo(x, hi), the rounded
+// remainder (x - hi is exact in float), so hi + lo carries about 16
+// significant bits instead of 8.  Two products, one per part, then replace
+// one product on the rounded operand.  For float storage nothing is split
+// (Split<float>::on is false and lo is never used).
+template <typename T> struct Split { static constexpr bool on = false; };
+template <> struct Split<bf16> { static constexpr bool on = true; };
+template <typename T>
+__device__ __forceinline__ T split_lo(float x, T hi) {
+    if constexpr (Split<T>::on) return from_f32<T>(x - to_f32(hi));
+    else return T(0);
+}
+
 // ---------------------------------------------------------------- LDS fragments
 // 8 consecutive elements of one row of a row-major LDS tile (16-byte aligned).
 template <typename T>

@@ -109,12 +109,13 @@ gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, cons
     // phase 2, K read transposed: source lane j of group lg points at row
     // 4lg + j/4 (+ 32s + 16h), columns kperm(kt, 0) + 8(j%4) .. +3 (half a
     // unit), so output lane i receives column kperm(kt, i):
-    // o2[kt] + st TS + (32s + 16h) RB
-    uint32_t o2[NKT];
+    // o2[kt / 2] + 8 (kt % 2) + st TS + (32s + 16h) RB (tiles 2i and 2i + 1
+    // read the two halves of the same 16-byte unit)
+    uint32_t o2[NKT / 2];
     const int ra0 = 4 * lg + (j >> 2);
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-        o2[kt] = (uint32_t)(OK + ra0 * RB + ((((4 * (kt >> 1) + (j & 3)) ^ ra0) & (UPR - 1)) << 4) + 8 * (kt & 1));
+    for (int kp = 0; kp < NKT / 2; ++kp)
+        o2[kp] = (uint32_t)(OK + ra0 * RB + ((((4 * kp + (j & 3)) ^ ra0) & (UPR - 1)) << 4));
     // u slice 2wv + ct, rows 16rt + 4lg + j/4, columns 4(j%4): ou + st US + ct 2048 + rt 512
     const uint32_t ou = (uint32_t)(OU + (is_e ? 2 * wv : 0) * 2048 + (4 * lg + (j >> 2)) * 32 + 8 * (j & 3));
     const uint32_t okd = (uint32_t)(OD + 16 * lg);
@@ -212,43 +213,55 @@ gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, cons
                 }
             }
         }
-        // (u | 0) - P, scaled per row by the key decay, as the phase-2 operand:
-        // vb[s][ct] holds rows 32s + 4lg + q (slots 0-3), 32s + 16 + 4lg + q (4-7)
-        bf16x8 vb[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const f32x4 kd4 = *(const f32x4 *)(lds + okd + (ST * 256 + rt * 64));
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                bf16x4 uu = bf16x4{};
-                if (is_e)
-                    uu = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(lds + ou) +
-                                      (ST * US + ct * 2048 + rt * 512))));
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    vb[rt >> 1][ct][4 * (rt & 1) + q] = (bf16)(((float)uu[q] - acc[rt][ct][q]) * kd4[q]);
-            }
-        }
+        // phase 2: X = exp2(gl) X + K^T (kd ((u | 0) - P)), one half of the
+        // contraction (rows 32 s2 .. 32 s2 + 31 of the chunk) at a time.  The
+        // operand kd ((u | 0) - P) goes in as a high and a low bf16 part
+        // (split_lo), one product each, as in the chunk_h stage; vb[ct] holds
+        // rows 32s2 + 4lg + q (slots 0-3) and 32s2 + 16 + 4lg + q (4-7).
+        // Forming each half's operand just before its products keeps fewer
+        // registers live than forming both first.
         const float gl = __builtin_amdgcn_exp2f(ring.gc[ST][63]);  // the chunk's decay (<= 1)
-        // phase 2: X = exp2(gl) X + K^T (kd (u - P))
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) xs[kt][ct][q] *= gl;
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
+        for (int s2 = 0; s2 < 2; ++s2) {
+            bf16x8 vb[2], vbl[2];
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int rt = 2 * s2 + r2;
+                const f32x4 kd4 = *(const f32x4 *)(lds + okd + (ST * 256 + rt * 64));
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    bf16x4 uu = bf16x4{};
+                    if (is_e)
+                        uu = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(lds + ou) +
+                                          (ST * US + ct * 2048 + rt * 512))));
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float x = ((float)uu[q] - acc[rt][ct][q]) * kd4[q];
+                        vb[ct][4 * r2 + q] = (bf16)x;
+                        vbl[ct][4 * r2 + q] = split_lo<bf16>(x, vb[ct][4 * r2 + q]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
                 typedef __attribute__((address_space(3))) const char *lp;
-                const lp pk = (lp)(lds + o2[kt]);
+                const lp pk = (lp)(lds + o2[kt >> 1] + 8 * (kt & 1));
                 const bf16x4 x0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4 *)(pk + (ST * TS + 32 * s2 * RB))));
                 const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4 *)(pk + (ST * TS + (32 * s2 + 16) * RB))));
                 const bf16x8 a = join<bf16>(x0, x1);
-                xs[kt][0] = mma(a, vb[s2][0], xs[kt][0]);
-                xs[kt][1] = mma(a, vb[s2][1], xs[kt][1]);
+                xs[kt][0] = mma(a, vb[0], xs[kt][0]);
+                xs[kt][0] = mma(a, vbl[0], xs[kt][0]);
+                xs[kt][1] = mma(a, vb[1], xs[kt][1]);
+                xs[kt][1] = mma(a, vbl[1], xs[kt][1]);
             }
         }
         pack();

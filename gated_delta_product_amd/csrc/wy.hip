@@ -15,9 +15,12 @@
 //   w = A diag(beta exp(gamma)) Khat           (effective keys with decay)
 // The Gram matrix K K^T and the two products run on the matrix cores (bf16 in,
 // fp32 accumulate); the norms are applied as fp32 row scales so the raw bf16
-// inputs are the operands.  A is built in fp32: the four 16x16 diagonal
-// blocks by forward substitution (one lane per column), the off-diagonal
-// blocks level by level with fp32 MFMA:  A_ij = -A_ii sum_{j<=m<i} L_im A_mj.
+// inputs are the operands.  The fp32 factors A diag(beta) and
+// A diag(beta e^gamma r) enter the two products as a high and a low bf16
+// part (two products each), so A is not cut to 8 significant bits.  A is
+// built in fp32: the four 16x16 diagonal blocks by forward substitution (one
+// lane per column), the off-diagonal blocks level by level with fp32 MFMA:
+// A_ij = -A_ii sum_{j<=m<i} L_im A_mj.
 // L and A share one LDS array: A's diagonal blocks replace L's (dead once
 // solved) and its lower blocks are stored transposed in the upper triangle,
 // which L leaves unused; the lower blocks of L stay intact until the last
@@ -310,7 +313,11 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     {
         const int a_row = 16 * wv + lc;  // output row this lane's B fragment covers
         const int nks = (wv >= 2) ? 2 : 1;  // contraction tiles with any b <= a
-        FragT bu[2], bw[2];
+        // A diag(beta) and A diag(beta e^gamma r) as bf16 operands split into
+        // high and low parts (split_lo): rounding them to one bf16 each was
+        // the largest single error of the bf16 path in the long-memory regime
+        constexpr bool SPL = Split<T>::on;
+        FragT bu[2], bw[2], bul[2], bwl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks < nks) {
@@ -325,10 +332,18 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    bu[ks][m] = from_f32<T>(av[m] * be0[m]);
-                    bw[ks][m] = from_f32<T>(av[m] * ws0[m]);
-                    bu[ks][4 + m] = from_f32<T>(av[4 + m] * be1[m]);
-                    bw[ks][4 + m] = from_f32<T>(av[4 + m] * ws1[m]);
+                    const float xu0 = av[m] * be0[m], xw0 = av[m] * ws0[m];
+                    const float xu1 = av[4 + m] * be1[m], xw1 = av[4 + m] * ws1[m];
+                    bu[ks][m] = from_f32<T>(xu0);
+                    bw[ks][m] = from_f32<T>(xw0);
+                    bu[ks][4 + m] = from_f32<T>(xu1);
+                    bw[ks][4 + m] = from_f32<T>(xw1);
+                    if constexpr (SPL) {
+                        bul[ks][m] = split_lo<T>(xu0, bu[ks][m]);
+                        bwl[ks][m] = split_lo<T>(xw0, bw[ks][m]);
+                        bul[ks][4 + m] = split_lo<T>(xu1, bu[ks][4 + m]);
+                        bwl[ks][4 + m] = split_lo<T>(xw1, bw[ks][4 + m]);
+                    }
                 }
             }
         }
@@ -349,6 +364,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 if (ks < nks) {
                     FragT a = lds_col8<T>(Vs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * vt);
                     acc = mma(a, bu[ks], acc);
+                    if constexpr (SPL) acc = mma(a, bul[ks], acc);
                 }
             }
             if (row_ok) {  // u is slice-major: 4 consecutive columns of the row
@@ -367,6 +383,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 if (ks < nks) {
                     FragT a = lds_col8<T>(Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * kt);
                     acc = mma(a, bw[ks], acc);
+                    if constexpr (SPL) acc = mma(a, bwl[ks], acc);
                 }
             }
 #pragma unroll

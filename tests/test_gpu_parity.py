@@ -777,13 +777,12 @@ def test_scan_forward_matches_oracle(case):
                          ids=lambda c: "T%d-K%dV%d-M%d-s%d" % (c[0], c[3], c[4], c[5], c[6]))
 def test_scan_adds_no_error_long_memory(case):
     """Long memory (|g| ~ 1e-3): each segment's entering state comes from the
-    composed maps of every earlier segment.  Against the oracle, the error of
-    o, h and v_new through gdp_chunk_fwd_scan stays within 2% (plus 1e-5) of
-    the error of gdp_chunk_fwd on the same inputs: composing the maps adds
-    nothing measurable to the bf16 path's own error.  (In this regime that
-    own error reaches the 5e-3 bar itself for some draws, e.g. o at 5.01e-3
-    with K=64, V=128, M=3, seed 34, for both paths; the 2% margin is the
-    scan's budget.)"""
+    composed maps of every earlier segment.  Against the oracle, o, h and
+    v_new of both gdp_chunk_fwd and gdp_chunk_fwd_scan meet the tolerance
+    (rel-L2 <= 5e-3, o max-abs <= 2e-2) and o's rel-L2 stays at or below
+    4.2e-3, and the scan's error stays within 2% (plus 1e-5) of the
+    sequential path's: composing the maps adds nothing measurable to the
+    bf16 path's own error."""
     T, H, HV, K, V, M, nseg, seed = case
     d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", seed)
     d["dt_bias"] = torch.empty(HV).uniform_(-9, -7, generator=torch.Generator().manual_seed(seed))
@@ -794,6 +793,7 @@ def test_scan_adds_no_error_long_memory(case):
     sc = _scan_buf(d["q"], d["k"], d["v"], beta, g, nseg)
     err = {"seq": {}, "scan": {}}
     r2 = {}
+    o_max = {"seq": 0.0, "scan": 0.0}
     nc = math.ceil(T * M / 64)
     for hv in range(HV):
         hk = hv // (HV // H)
@@ -806,10 +806,17 @@ def test_scan_adds_no_error_long_memory(case):
             for nm, x in got.items():
                 e = x.astype(np.float64) - (r[nm][::M] if nm == "h" else r[nm])
                 err[tag][nm] = err[tag].get(nm, 0.0) + float((e * e).sum())
+                if nm == "o":
+                    o_max[tag] = max(o_max[tag], float(np.abs(e).max()))
     for nm in ("o", "h", "v_new"):
         es, ec = math.sqrt(err["seq"][nm] / r2[nm]), math.sqrt(err["scan"][nm] / r2[nm])
         log("  %-6s rel_l2 sequential %.4e scan %.4e" % (nm, es, ec))
+        assert es <= TOL[torch.bfloat16]["rel_l2"] and ec <= TOL[torch.bfloat16]["rel_l2"], (nm, es, ec)
         assert ec <= 1.02 * es + 1e-5, (nm, ec, es)
+        if nm == "o":
+            assert es <= 4.2e-3 and ec <= 4.2e-3, ("o margin", es, ec)
+    log("  o max_abs sequential %.3e scan %.3e" % (o_max["seq"], o_max["scan"]))
+    assert o_max["seq"] <= TOL[torch.bfloat16]["max_abs"] and o_max["scan"] <= TOL[torch.bfloat16]["max_abs"]
 
 
 def test_scan_long_prefill_sampled():
