@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(HERE, "libgdp.so")
 GDP_OK, GDP_ERR_INVALID, GDP_ERR_UNSUPPORTED, GDP_ERR_HIP = 0, 1, 2, 3
 GDP_F32, GDP_BF16 = 0, 1
 CHUNK = 64
+# size of the library's own scratch array used by gdp_chunk_fwd_scan_noalloc (GDP_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _i64, _i32, _f32, _vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -91,6 +93,8 @@ def lib():
                                                 _vp, _vp]
         L.gdp_chunk_fwd_scan.restype = ctypes.c_int
         L.gdp_chunk_fwd_scan.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _i64, _vp, _vp]
+        L.gdp_chunk_fwd_scan_noalloc.restype = ctypes.c_int
+        L.gdp_chunk_fwd_scan_noalloc.argtypes = [ctypes.POINTER(ChunkArgs), _i32, _vp, _vp]
         L.gdp_prefill_fwd_scan.restype = ctypes.c_int
         L.gdp_prefill_fwd_scan.argtypes = [ctypes.POINTER(PrepareArgs), ctypes.POINTER(ChunkArgs), _i32, _vp, _i64,
                                            _vp, _vp]
@@ -387,6 +391,20 @@ class ChunkBuffers:
         after it."""
         return self._scan(lambda ws, nb, ev, s: lib().gdp_chunk_fwd_scan(
             ctypes.byref(self.args), int(num_segments), ws, nb, ev, s), num_segments, stream, stage_events)
+
+    def forward_scan_noalloc(self, num_segments, stream=None, stage_events=None):
+        """gdp_chunk_fwd_scan_noalloc: forward_scan with the workspace taken
+        from the library's own device scratch array (GDP_NOALLOC_SCRATCH_BYTES)
+        instead of a tensor; nothing is allocated by the call.  Calls that
+        overlap on one GPU share that array."""
+        ev = None
+        if stage_events is not None:
+            if len(stage_events) != 3:
+                raise ValueError("need 3 events")
+            ev = (_vp * 3)(*[e.cuda_event for e in stage_events])
+        s = stream if stream is not None else _stream(self.device)
+        _check(lib().gdp_chunk_fwd_scan_noalloc(ctypes.byref(self.args), int(num_segments), ev, s))
+        return self.o
 
     def _scan(self, call, num_segments, stream, stage_events):
         d = self.dims

@@ -468,9 +468,13 @@ int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, in
 
 // The segment-parallel forward; with prep, WY also does the prepare of its
 // rows (launch_wy_prepare).
+// With scratch_base set, `workspace` is not the caller's: it is the
+// library's scratch array (gdp_chunk_fwd_scan_noalloc), looked up by
+// scratch_base() only once every argument, the plan and its size have been
+// checked, so a rejected call makes no HIP call at all.
 static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp::PrepareParams *prep,
                             int32_t num_segments, void *workspace, int64_t workspace_bytes,
-                            void *const *stage_events, void *stream) {
+                            void *const *stage_events, void *stream, gdp_status (*scratch_base)(void **) = nullptr) {
     gdp::ChunkParams p;
     gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | ST_H | ST_O, &p);
     if (st != GDP_OK) return st;
@@ -488,6 +492,15 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
     int64_t seg_tok = 0;
     const int64_t nseg = scan_plan(a->T, num_segments, &seg_tok);
     const ScanLayout L = scan_layout(nseg, a->HV, a->K, a->V);
+    if (scratch_base) {
+        if (L.total > workspace_bytes)
+            return fail(GDP_ERR_UNSUPPORTED,
+                        "%s: this call needs %lld bytes of scratch, more than the %lld bytes of the library's own "
+                        "(GDP_NOALLOC_SCRATCH_BYTES); use gdp_chunk_fwd_scan with a workspace, or fewer segments",
+                        name, (long long)L.total, (long long)workspace_bytes);
+        gdp_status st2 = scratch_base(&workspace);
+        if (st2 != GDP_OK) return st2;
+    }
     if (!workspace || ((uintptr_t)workspace & 255u))
         return fail(GDP_ERR_INVALID, "%s: workspace must be a 256-byte aligned device pointer", name);
     if (workspace_bytes < L.total)
@@ -555,6 +568,51 @@ gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *pa, const gdp_chunk_args
         return fail(GDP_ERR_UNSUPPORTED, "gdp_prefill_fwd_scan: x rows and outputs must be 16-byte aligned");
     return scan_impl("gdp_prefill_fwd_scan", a, pp.T > 0 ? &pp : nullptr, num_segments, workspace,
                      workspace_bytes, stage_events, stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free form of gdp_chunk_fwd_scan
+// The workspace of the segment-parallel forward (segment maps, entering
+// states, segment offsets) as a device array of the library's own, so the
+// caller allocates nothing.  In host code `scratch` names a host-side
+// stand-in, not device memory: every use below goes through the per-device
+// address hipGetSymbolAddress gives (each GPU holds its own copy of the
+// array, for the life of the process).  Nothing in it needs to start at
+// zero: each call writes every byte it reads first.
+static __device__ __align__(256) char scratch[GDP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[64];  // the array's device address, per device (null until first use)
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+gdp_status scratch_base(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "gdp_chunk_fwd_scan_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd_scan_noalloc: device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "gdp_chunk_fwd_scan_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p || ((uintptr_t)p & 255u))
+            return fail(GDP_ERR_HIP, "gdp_chunk_fwd_scan_noalloc: scratch address %p is not 256-byte aligned", p);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return ok();
+}
+}  // namespace
+
+extern "C" {
+
+gdp_status gdp_chunk_fwd_scan_noalloc(const gdp_chunk_args *a, int32_t num_segments, void *const *stage_events,
+                                      void *stream) {
+    return scan_impl("gdp_chunk_fwd_scan_noalloc", a, nullptr, num_segments, nullptr, GDP_NOALLOC_SCRATCH_BYTES,
+                     stage_events, stream, scratch_base);
 }
 
 gdp_status gdp_chunk_fwd_pipelined(const gdp_chunk_args *a, int32_t num_segments, float *state_workspace,

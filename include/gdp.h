@@ -377,6 +377,35 @@ gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, voi
                               int64_t workspace_bytes, void *const *stage_events, void *stream);
 
 /*
+ * gdp_chunk_fwd_scan_noalloc -- gdp_chunk_fwd_scan for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, results bit-identical
+ * to gdp_chunk_fwd_scan, with the workspace taken from a device array of the
+ * library's own instead of from the caller.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the caller still passes
+ * every input and output in `a`.
+ *   Limit: the workspace gdp_scan_workspace_bytes(T, HV, K, V,
+ *   num_segments) reports must fit GDP_NOALLOC_SCRATCH_BYTES (64 MiB; the
+ *   32768-token, 16-head, K = V = 128 sequence with 16 segments needs 47.5
+ *   MiB); a larger call returns GDP_ERR_UNSUPPORTED, launches nothing and
+ *   makes no HIP call.  Every other argument is checked, and refused, as by
+ *   gdp_chunk_fwd_scan.
+ *   The array: each GPU the library runs on holds one copy of
+ *   GDP_NOALLOC_SCRATCH_BYTES until the process ends.  Every call on a GPU
+ *   shares that GPU's copy and leaves its last contents there (nothing in it
+ *   needs to start at zero): calls on one GPU that overlap in time -- on
+ *   different streams, or from several threads without ordering -- race and
+ *   give undefined results; calls on one stream are ordered and safe.  The
+ *   first call on each device looks the array's device address up
+ *   (hipGetSymbolAddress) and keeps it; make that first call outside graph
+ *   capture.  Later calls can be captured.
+ *   stage_events as for gdp_chunk_fwd_scan.
+ */
+#define GDP_NOALLOC_SCRATCH_BYTES (64LL * 1024 * 1024)
+gdp_status gdp_chunk_fwd_scan_noalloc(const gdp_chunk_args *a, int32_t num_segments, void *const *stage_events,
+                                      void *stream);
+
+/*
  * gdp_prefill_fwd_scan -- gdp_prefill_prepare followed by gdp_chunk_fwd_scan
  * for one sequence, with the prepare done inside the WY stage: each
  * gdp_recompute_w_u block reads its key and value copies, query and gate

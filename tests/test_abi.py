@@ -328,3 +328,29 @@ def test_prefill_scan_rejects():
     assert b"v is NULL" in B.lib().gdp_last_error()
     assert L.gdp_chunk_fwd_scan(a(beta=None), 2, ws, big, None, None) == B.GDP_ERR_INVALID
     assert b"beta is NULL" in B.lib().gdp_last_error()
+
+
+def test_scan_noalloc_rejects_before_any_hip_call():
+    """gdp_chunk_fwd_scan_noalloc refuses, with no HIP call (this runs without
+    a GPU), a call whose workspace would pass its scratch array, with a
+    message naming the limit, and everything gdp_chunk_fwd_scan refuses."""
+    L = B.lib()
+    T, HV, K, V, nseg = 32768, 32, 128, 128, 16
+    need = L.gdp_scan_workspace_bytes(T, HV, K, V, nseg)
+    m = re.search(r"#define GDP_NOALLOC_SCRATCH_BYTES \((\d+)LL \* 1024 \* 1024\)", open(HEADER).read())
+    assert m and int(m.group(1)) << 20 == B.NOALLOC_SCRATCH_BYTES
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    a = lambda **kw: ctypes.byref(_args(**dict(dict(K=K, V=V, T=T, H=HV, HV=HV, M=2, h_chunks=1024), **kw)))
+    assert L.gdp_chunk_fwd_scan_noalloc(a(), nseg, None, None) == B.GDP_ERR_UNSUPPORTED
+    msg = L.gdp_last_error()
+    assert b"scratch" in msg and str(need).encode() in msg and b"GDP_NOALLOC_SCRATCH_BYTES" in msg
+    # the 32768-token, 16-head workload of the benchmark fits
+    assert L.gdp_scan_workspace_bytes(T, 16, K, V, nseg) <= B.NOALLOC_SCRATCH_BYTES
+    # the checks of gdp_chunk_fwd_scan come first
+    assert L.gdp_chunk_fwd_scan_noalloc(None, 4, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan_noalloc(a(B=2, h_chunks=2048), 4, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan_noalloc(a(), 0, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan_noalloc(a(q=None), 4, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan_noalloc(a(dtype=B.GDP_F32, K=64, V=64), 4, None, None) == B.GDP_ERR_UNSUPPORTED
+    # nothing to do: no scratch, no HIP call
+    assert L.gdp_chunk_fwd_scan_noalloc(a(T=0), 4, None, None) == B.GDP_OK
