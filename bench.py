@@ -132,6 +132,30 @@ def algorithmic_bytes(w, T=None):
     return {"gdp_prefill_prepare": prep, "gdp_recompute_w_u": wy, "gdp_chunk_h": ch, "gdp_chunk_o": co}
 
 
+def scan_bytes(w, segments, nseg):
+    """Algorithmic bytes per launch of the segment-parallel stages over the
+    whole workload (one sequence, es = 2).
+      wy_fused  the prepare's reads (x, ba) and writes (q, k, g; v and beta
+                are not stored) plus WY's writes (w, u, k_rnorm, gcum,
+                kdecay): the key and value copies, beta and g stay on chip
+      map       k, kdecay, gcum, w, u of every segment but the last, read
+                once; one fp32 K x (K + V) map per segment and head written
+      scan      the maps read, one fp32 state per segment and head written
+      chunk_h   as algorithmic_bytes, with one state per 64-token chunk"""
+    T, M, H, HV, G, K, V = w["T"] * w["B"], w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
+    ab = algorithmic_bytes(w)
+    TM = T * M
+    wy_fused = ab["gdp_prefill_prepare"] + ab["gdp_recompute_w_u"] - (TM * HV * (K + V) * 2 + TM * HV * 4 + T * HV * 4) \
+        - TM * HV * (V * 2 + 4)
+    seg_tok = math.ceil(math.ceil(T / 64) / segments) * 64
+    TMm = (nseg - 1) * seg_tok * M
+    maps = (nseg - 1) * HV * K * (K + V) * 4
+    mapb = TMm * H * K * 2 + TMm * HV * 8 + TMm * HV * (K + V) * 2 + maps
+    scanb = maps + nseg * HV * V * K * 4
+    ch = ab["gdp_chunk_h"] - (math.ceil(T * M / 64) - math.ceil(T / 64)) * HV * V * K * 2
+    return {"wy_fused": wy_fused, "map": mapb, "scan": scanb, "chunk_h": ch}
+
+
 def decode_bytes(c):
     """Minimum HBM bytes of gdp_decode_update: the fp32 state read and
     written once, the q, k, v rows and fp32 beta, g read, o written."""
@@ -187,7 +211,14 @@ def cpu_baseline(d, w, threads):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(head, range(w["HV"])))
     dt = time.perf_counter() - t0
-    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads, "host_cores": os.cpu_count(),
+            "cpu_model": model, "kind": "oracle",
             "sample": "%d tokens x %d heads of the same workload (prepare, serial fp64 recurrence "
                       "-> o, v_new, h, and per-chunk WY -> w, u); %.1f s wall" % (Ts, w["HV"], dt)}
 
@@ -276,7 +307,10 @@ def main():
     buf = G.ChunkBuffers(*prep_out)
     stream = torch.cuda.current_stream(dev)
     nseg = G.scan_segments(w["T"], args.segments) if scan else G.pipeline_segments(w["T"], args.segments)
-    nev = 2 + (3 if scan else 2 * nseg)
+    # events: [0] step start, [1] after prepare (its own launch), then the
+    # scan forms' five stage events (after WY, the maps, the scan, chunk_h,
+    # chunk_o) or a pair around each pipelined chunk_h launch
+    nev = 2 + (5 if scan else 2 * nseg)
 
     def new_events(n):
         evs = [TimingEvent() for _ in range(n)]
@@ -315,61 +349,45 @@ def main():
     tokens = w["B"] * w["T"]
     value = tokens / (ms_per_step / 1e3)
 
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    def span_us(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in evs) / args.steps * 1e3
+
     ab = algorithmic_bytes(w)
+    kern = {}
+
+    def add(name, us, alg, launches=1, note=None):
+        kern[name] = {"us": round(us, 2), "launches_per_step": launches, "alg_bytes": int(alg),
+                      "GB/s": round(alg / us / 1e3, 1), "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)}
+        if note:
+            kern[name]["note"] = note
+
     if scan:
-        # chunk_h: one launch over every segment at once, bracketed on its stream
-        seg_ms = [e[3].elapsed_time(e[4]) for e in evs]
-        # this form writes only the states entering each 64-token chunk
-        # (the ones chunk_o reads), not one per 64-row chunk
-        ch_bytes = ab["gdp_chunk_h"] - (math.ceil(w["T"] * w["M"] / 64) - math.ceil(w["T"] / 64)) * w["B"] \
-            * w["HV"] * w["V"] * w["K"] * 2
-        map_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+        sb = scan_bytes(w, args.segments, nseg)
+        if fused:
+            add("gdp_recompute_w_u (prepare fused)", span_us(1, 2), sb["wy_fused"] if not args.store_v_beta
+                else sb["wy_fused"] + w["T"] * w["M"] * w["HV"] * (w["V"] * 2 + 4))
+        else:
+            add("gdp_prefill_prepare", span_us(0, 1), ab["gdp_prefill_prepare"])
+            add("gdp_recompute_w_u", span_us(1, 2), ab["gdp_recompute_w_u"])
+        add("gdp_seg_map", span_us(2, 3), sb["map"])
+        add("gdp_seg_scan", span_us(3, 4), sb["scan"])
+        add("gdp_chunk_h", span_us(4, 5), sb["chunk_h"], note="all %d segments in one launch" % nseg)
+        add("gdp_chunk_o", span_us(5, 6), ab["gdp_chunk_o"])
     else:
+        add("gdp_prefill_prepare", span_us(0, 1), ab["gdp_prefill_prepare"])
         # chunk_h: every segment launch, bracketed on its own stream
         seg_ms = [e[2 + 2 * j].elapsed_time(e[3 + 2 * j]) for e in evs for j in range(nseg)]
         starts = G.pipeline_plan(w["T"], args.segments)
         seg_tokens = [starts[j + 1] - starts[j] for j in range(nseg)]
         ch_bytes = sum(algorithmic_bytes(w, t)["gdp_chunk_h"] for t in seg_tokens) / nseg  # per launch
-    ch_ms = sum(seg_ms) / len(seg_ms)
-    if fused:  # prepare runs inside the WY stage: time that stage as one
-        prep_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        pw = ab["gdp_prefill_prepare"] + ab["gdp_recompute_w_u"] - (
-            w["T"] * w["M"] * w["HV"] * (w["K"] + w["V"]) * 2 + w["T"] * w["M"] * w["HV"] * 4 + w["T"] * w["HV"] * 4)
-        if not args.store_v_beta:  # nor prepare's writes of the value copies and beta
-            pw -= w["T"] * w["M"] * w["HV"] * (w["V"] * 2 + 4)
-    if fused:
-        # prepare's bytes plus WY's, less WY's reads of the key and value
-        # copies, beta and g (they stay on chip)
-        kern = {"gdp_recompute_w_u(prepare fused)": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1,
-                                                     "alg_bytes": pw, "GB/s": round(pw / (prep_ms / 1e3) / 1e9, 1)}}
-    else:
-        kern = {"gdp_prefill_prepare": {"us": round(prep_ms * 1e3, 2), "launches_per_step": 1,
-                                        "alg_bytes": ab["gdp_prefill_prepare"],
-                                        "GB/s": round(ab["gdp_prefill_prepare"] / (prep_ms / 1e3) / 1e9, 1)}}
-    kern["gdp_chunk_h"] = {"us_per_launch": round(ch_ms * 1e3, 2), "launches_per_step": 1 if scan else nseg,
-                           "alg_bytes_per_launch": int(ch_bytes), "GB/s": round(ch_bytes / (ch_ms / 1e3) / 1e9, 1)}
-    if scan:
-        # the segment maps read k, kdecay, gcum, w and u of every segment but
-        # the last once, and write each segment's fp32 map; the scan reads
-        # the maps and writes one fp32 state per segment
-        seg_tok = math.ceil(math.ceil(w["T"] / 64) / args.segments) * 64
-        TM = (nseg - 1) * seg_tok * w["M"]
-        mb = TM * w["H"] * w["K"] * 2 + TM * w["HV"] * 8 + TM * w["HV"] * (w["K"] + w["V"]) * 2 \
-            + (nseg - 1) * w["HV"] * w["K"] * (w["K"] + w["V"]) * 4
-        kern["gdp_seg_map+gdp_seg_scan"] = {"us": round(map_ms * 1e3, 2), "segments": nseg, "map_alg_bytes": mb,
-                                            "GB/s": round(mb / (map_ms / 1e3) / 1e9, 1)}
+        add("gdp_chunk_h", sum(seg_ms) / len(seg_ms) * 1e3, ch_bytes, launches=nseg,
+            note="per segment launch, overlapped with the side streams' WY and chunk_o")
     # the roofline is reported for the kernel that takes the longest per launch
-    cands = {"gdp_chunk_h": (ch_ms, ch_bytes)}
-    if fused:
-        cands["gdp_recompute_w_u"] = (prep_ms, pw)
-    else:
-        cands["gdp_prefill_prepare"] = (prep_ms, ab["gdp_prefill_prepare"])
-    dom = max(cands, key=lambda kk: cands[kk][0])
-    achieved = cands[dom][1] / (cands[dom][0] / 1e3) / 1e9
-    roof = {"kernel": dom + (" (prepare fused)" if dom == "gdp_recompute_w_u" else ""), "bound": "hbm",
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, nseg, args.path)}
+    dom = max(kern, key=lambda kk: kern[kk]["us"])
+    kd = kern[dom]
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(dom.split(" ")[0], nseg, args.path)}
 
     stages = None
     if args.stages:  # each stage alone, whole workload, for reference
@@ -414,6 +432,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": dict(w, segments=nseg), "roofline": roof, "cpu_baseline": cpu, "kernels": kern,
+        "kernels_sum_us": round(sum(k["us"] * (1 if k["launches_per_step"] == 1 or scan else 0) for k in kern.values()), 1),
     }
     if stages:
         out["stages_sequential"] = stages

@@ -102,6 +102,8 @@ def lib():
         L.gdp_scan_segments.argtypes = [_i64, _i32]
         L.gdp_scan_workspace_bytes.restype = _i64
         L.gdp_scan_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
+        L.gdp_scan_workspace_bytes_varlen.restype = _i64
+        L.gdp_scan_workspace_bytes_varlen.argtypes = [_i64, _i64, _i32, _i32, _i32, _i32]
         L.gdp_pipeline_segments.restype = _i32
         L.gdp_pipeline_segments.argtypes = [_i64, _i32]
         L.gdp_pipeline_plan.restype = _i32
@@ -380,15 +382,16 @@ class ChunkBuffers:
             stage_events)
 
     def forward_scan(self, num_segments, stream=None, stage_events=None):
-        """gdp_chunk_fwd_scan: the results of forward() for B == 1 without
-        cu_seqlens (to rounding past the first segment), with the serial
-        chunk_h chain cut into num_segments segments run in parallel from
-        the states a scan over the segments' composed maps gives.  Of h only
-        the states entering chunks i*M (the ones chunk_o reads) are written;
-        the other slots keep what they held.
-        stage_events: optional 3 torch.cuda.Event (timing enabled, recorded
-        at least once) recorded before the segment maps, before chunk_h and
-        after it."""
+        """gdp_chunk_fwd_scan: the results of forward() for B == 1, one
+        sequence or packed requests (cu_seqlens), to rounding past the first
+        segment of each sequence, with every long serial chunk_h chain cut
+        into segments run in parallel from the states a scan over the
+        segments' composed maps gives.  Of h only the states entering chunks
+        i*M (the ones chunk_o reads) are written; the other slots keep what
+        they held.
+        stage_events: optional 5 events with a cuda_event handle (timing
+        enabled, recorded at least once), recorded after the WY stage, the
+        segment maps, the scan, chunk_h and chunk_o."""
         return self._scan(lambda ws, nb, ev, s: lib().gdp_chunk_fwd_scan(
             ctypes.byref(self.args), int(num_segments), ws, nb, ev, s), num_segments, stream, stage_events)
 
@@ -397,29 +400,28 @@ class ChunkBuffers:
         from the library's own device scratch array (GDP_NOALLOC_SCRATCH_BYTES)
         instead of a tensor; nothing is allocated by the call.  Calls that
         overlap on one GPU share that array."""
-        ev = None
-        if stage_events is not None:
-            if len(stage_events) != 3:
-                raise ValueError("need 3 events")
-            ev = (_vp * 3)(*[e.cuda_event for e in stage_events])
+        ev = _stage_events(stage_events)
         s = stream if stream is not None else _stream(self.device)
         _check(lib().gdp_chunk_fwd_scan_noalloc(ctypes.byref(self.args), int(num_segments), ev, s))
         return self.o
 
-    def _scan(self, call, num_segments, stream, stage_events):
+    def scan_workspace_bytes(self, num_segments):
+        """Workspace bytes gdp_chunk_fwd_scan needs for these buffers."""
         d = self.dims
-        need = lib().gdp_scan_workspace_bytes(d["T"], d["HV"], d["K"], d["V"], int(num_segments))
+        if self.cu_seqlens is not None:
+            return lib().gdp_scan_workspace_bytes_varlen(d["T"], d["nseq"], d["HV"], d["K"], d["V"],
+                                                         int(num_segments))
+        return lib().gdp_scan_workspace_bytes(d["T"], d["HV"], d["K"], d["V"], int(num_segments))
+
+    def _scan(self, call, num_segments, stream, stage_events):
+        need = self.scan_workspace_bytes(num_segments)
         if need < 0:
             raise ValueError("num_segments %r out of range" % (num_segments,))
         ws = getattr(self, "_scan_ws", None)
         if ws is None or ws.numel() < need:
             # torch's caching allocator returns 512-byte aligned blocks
             self._scan_ws = ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
-        ev = None
-        if stage_events is not None:
-            if len(stage_events) != 3:
-                raise ValueError("need 3 events")
-            ev = (_vp * 3)(*[e.cuda_event for e in stage_events])
+        ev = _stage_events(stage_events)
         s = stream if stream is not None else _stream(self.device)
         _check(call(ws.data_ptr(), ws.numel(), ev, s))
         return self.o
@@ -437,6 +439,15 @@ class ChunkBuffers:
         s = stream if stream is not None else _stream(self.device)
         _check(call(self._ws.data_ptr(), ev, s))
         return self.o
+
+
+def _stage_events(events):
+    """The 5 stage events of the segment-parallel forward as a C array."""
+    if events is None:
+        return None
+    if len(events) != 5:
+        raise ValueError("need 5 events")
+    return (_vp * 5)(*[e.cuda_event for e in events])
 
 
 def slices_to_rows(t):

@@ -432,66 +432,90 @@ static gdp_status pipelined_impl(const gdp_chunk_args *a, const gdp::PreparePara
 
 // Plan of the segment-parallel forward: segments of seg_tok tokens (equal
 // shares of the 64-token chunks, rounded up), the last one possibly shorter.
-static int32_t scan_plan(int64_t T, int32_t num_segments, int64_t *seg_tok) {
+// For packed requests seg_tok comes from the packed total T the same way and
+// every request is cut at multiples of it on the device (launch_seg_plan);
+// the return value is then the number of plan slots, an upper bound on the
+// segments: ceil(T / seg_tok) + num_seqs.
+static int64_t scan_plan(int64_t T, int32_t num_segments, int64_t num_seqs, bool packed, int64_t *seg_tok) {
     const int64_t nch = cdiv(T, 64);
     const int64_t per = cdiv(nch, num_segments) * 64;
     *seg_tok = per;
-    return T > 0 ? (int32_t)cdiv(T, per) : 0;
+    if (T <= 0) return 0;
+    return packed ? cdiv(T, per) + num_seqs : cdiv(T, per);
 }
 
-// Byte offsets of the regions of the scan workspace (each 256-byte aligned).
+// Byte offsets of the regions of the scan workspace (each 256-byte aligned):
+// maps, entering states, segment offsets, and for packed requests the plan's
+// per-slot last flags and per-request first slot and count.
 struct ScanLayout {
-    int64_t maps, hstart, cu, total;
+    int64_t maps, hstart, cu, seg_last, req_first, req_nseg, total;
 };
-static ScanLayout scan_layout(int64_t nseg, int64_t HV, int64_t K, int64_t V) {
+static ScanLayout scan_layout(int64_t nslot, bool packed, int64_t num_seqs, int64_t HV, int64_t K, int64_t V) {
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t nmaps = packed ? nslot : (nslot > 1 ? nslot - 1 : 0);
     ScanLayout L;
     L.maps = 0;
-    L.hstart = up((nseg > 1 ? nseg - 1 : 0) * HV * K * (K + V) * 4);
-    L.cu = L.hstart + up(nseg * HV * V * K * 4);
-    L.total = L.cu + up((nseg + 1) * 4);
+    L.hstart = up(nmaps * HV * K * (K + V) * 4);
+    L.cu = L.hstart + up(nslot * HV * V * K * 4);
+    L.seg_last = L.cu + up((nslot + 1) * 4);
+    L.req_first = L.seg_last + (packed ? up(nslot * 4) : 0);
+    L.req_nseg = L.req_first + (packed ? up(num_seqs * 4) : 0);
+    L.total = L.req_nseg + (packed ? up(num_seqs * 4) : 0);
     return L;
 }
 
 int32_t gdp_scan_segments(int64_t T, int32_t num_segments) {
     if (T < 0 || num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS) return -1;
     int64_t st;
-    return scan_plan(T, num_segments, &st);
+    return (int32_t)scan_plan(T, num_segments, 0, false, &st);
 }
 
 int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, int32_t num_segments) {
     if (T < 0 || HV < 1 || K < 1 || V < 1 || num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS) return -1;
     int64_t st;
-    const int64_t nseg = scan_plan(T, num_segments, &st);
-    return scan_layout(nseg, HV, K, V).total;
+    const int64_t nseg = scan_plan(T, num_segments, 0, false, &st);
+    return scan_layout(nseg, false, 0, HV, K, V).total;
+}
+
+int64_t gdp_scan_workspace_bytes_varlen(int64_t T, int64_t num_seqs, int32_t HV, int32_t K, int32_t V,
+                                        int32_t num_segments) {
+    if (T < 0 || num_seqs < 0 || HV < 1 || K < 1 || V < 1 || num_segments < 1 ||
+        num_segments > GDP_SCAN_MAX_SEGMENTS)
+        return -1;
+    int64_t st;
+    const int64_t nslot = scan_plan(T, num_segments, num_seqs, true, &st);
+    return scan_layout(nslot, true, num_seqs, HV, K, V).total;
 }
 
 // The segment-parallel forward; with prep, WY also does the prepare of its
-// rows (launch_wy_prepare).
-// With scratch_base set, `workspace` is not the caller's: it is the
-// library's scratch array (gdp_chunk_fwd_scan_noalloc), looked up by
-// scratch_base() only once every argument, the plan and its size have been
-// checked, so a rejected call makes no HIP call at all.
+// rows (launch_wy_prepare).  With scratch_base set, `workspace` is not the
+// caller's: it is the library's scratch array (gdp_chunk_fwd_scan_noalloc),
+// looked up by scratch_base() only once every argument, the plan and its
+// size have been checked, so a rejected call makes no HIP call at all.
 static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp::PrepareParams *prep,
                             int32_t num_segments, void *workspace, int64_t workspace_bytes,
                             void *const *stage_events, void *stream, gdp_status (*scratch_base)(void **) = nullptr) {
     gdp::ChunkParams p;
     gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | ST_H | ST_O, &p);
     if (st != GDP_OK) return st;
-    if (a->cu_seqlens) return fail(GDP_ERR_INVALID, "%s: cu_seqlens must be NULL", name);
-    if (a->B != 1) return fail(GDP_ERR_INVALID, "%s: B must be 1 (got %lld)", name, (long long)a->B);
+    const bool packed = a->cu_seqlens != nullptr;
+    if (a->B != 1)
+        return fail(GDP_ERR_INVALID, "%s: B must be 1 (got %lld; packed requests go through cu_seqlens)", name,
+                    (long long)a->B);
     if (num_segments < 1 || num_segments > GDP_SCAN_MAX_SEGMENTS)
         return fail(GDP_ERR_INVALID, "%s: num_segments %d not in [1, %d]", name, num_segments,
                     GDP_SCAN_MAX_SEGMENTS);
     if (a->dtype != GDP_BF16 || !((a->K == 64 || a->K == 128) && (a->V == 64 || a->V == 128)))
         return fail(GDP_ERR_UNSUPPORTED, "%s: bf16 with K, V in {64, 128} only (K=%d V=%d)", name, a->K,
                     a->V);
-    if (a->T == 0) return ok();
+    if (p.nseq == 0) return ok();  // T == 0 or no requests: nothing to launch
     if (a->T * a->M * a->V * 2 >= ((int64_t)1 << 31))
         return fail(GDP_ERR_UNSUPPORTED, "%s: T*M*V*2 must stay below 2^31 (T=%lld)", name, (long long)a->T);
     int64_t seg_tok = 0;
-    const int64_t nseg = scan_plan(a->T, num_segments, &seg_tok);
-    const ScanLayout L = scan_layout(nseg, a->HV, a->K, a->V);
+    const int64_t nslot = scan_plan(a->T, num_segments, p.nseq, packed, &seg_tok);
+    if (nslot * a->HV > 0x7fffffff || nslot >= 0x7fffffff / 8)
+        return fail(GDP_ERR_UNSUPPORTED, "%s: too many segments for one launch", name);
+    const ScanLayout L = scan_layout(nslot, packed, p.nseq, a->HV, a->K, a->V);
     if (scratch_base) {
         if (L.total > workspace_bytes)
             return fail(GDP_ERR_UNSUPPORTED,
@@ -507,41 +531,58 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
         return fail(GDP_ERR_INVALID, "%s: workspace of %lld bytes, %lld needed", name,
                     (long long)workspace_bytes, (long long)L.total);
     char *ws = (char *)workspace;
-    gdp::ScanParams sp{p, nseg, seg_tok, (float *)(ws + L.maps), (float *)(ws + L.hstart),
-                       (int32_t *)(ws + L.cu)};
+    gdp::ScanParams sp{p,
+                       nslot,
+                       seg_tok,
+                       (float *)(ws + L.maps),
+                       (float *)(ws + L.hstart),
+                       (int32_t *)(ws + L.cu),
+                       packed ? (int32_t *)(ws + L.seg_last) : nullptr,
+                       packed ? (int32_t *)(ws + L.req_first) : nullptr,
+                       packed ? (int32_t *)(ws + L.req_nseg) : nullptr};
     // the chunk_h pass: the segments as packed sequences, each from its
     // entering state, whose final states replace it in place
     gdp_chunk_args ha = *a;
     ha.cu_seqlens = sp.cu;
-    ha.num_seqs = nseg;
+    ha.num_seqs = nslot;
     ha.h0 = sp.hstart;
     ha.ht = sp.hstart;
     gdp::ChunkParams hp;
     if ((st = check_chunk(&ha, ST_H, &hp)) != GDP_OK) return st;
     // only the states chunk_o reads: the one entering each 64-token chunk.
-    // Every segment starts on a 64-token boundary, so counting chunks per
-    // segment keeps the whole sequence's c % M.
+    // Every segment starts on a 64-token boundary of its sequence, so
+    // counting chunks per segment keeps the sequence's own c % M.
     hp.hstep = a->M;
     hipStream_t s = (hipStream_t)stream;
-    if ((st = hip_status(prep ? gdp::launch_wy_prepare(p, *prep, s) : gdp::launch_wy(p, s),
-                         "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK)
-        return st;
     auto mark = [&](int i) {
         return stage_events ? hip_status(hipEventRecord((hipEvent_t)stage_events[i], s), "hipEventRecord") : ok();
     };
-    if ((st = mark(0)) != GDP_OK) return st;
-    if ((st = hip_status(gdp::launch_seg_scan(sp, s), "gdp_chunk_fwd_scan: segment scan launch")) != GDP_OK)
+    auto run = [&](hipError_t e, const char *what) { return hip_status(e, what); };
+    if ((st = run(prep ? gdp::launch_wy_prepare(p, *prep, s) : gdp::launch_wy(p, s),
+                  "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK)
         return st;
+    if (packed && (st = run(gdp::launch_seg_plan(sp, s), "gdp_chunk_fwd_scan: segment plan launch")) != GDP_OK)
+        return st;
+    if ((st = mark(0)) != GDP_OK) return st;
+    if ((st = run(gdp::launch_seg_map(sp, s), "gdp_chunk_fwd_scan: segment map launch")) != GDP_OK) return st;
     if ((st = mark(1)) != GDP_OK) return st;
-    if ((st = hip_status(gdp::launch_chunk_h(hp, s), "gdp_chunk_fwd_scan: chunk_h launch")) != GDP_OK) return st;
+    if ((st = run(gdp::launch_seg_scan(sp, s), "gdp_chunk_fwd_scan: segment scan launch")) != GDP_OK) return st;
     if ((st = mark(2)) != GDP_OK) return st;
-    if ((st = hip_status(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd_scan: chunk_o launch")) != GDP_OK) return st;
+    if ((st = run(gdp::launch_chunk_h(hp, s), "gdp_chunk_fwd_scan: chunk_h launch")) != GDP_OK) return st;
+    if ((st = mark(3)) != GDP_OK) return st;
+    if ((st = run(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd_scan: chunk_o launch")) != GDP_OK) return st;
+    if ((st = mark(4)) != GDP_OK) return st;
     if (a->ht) {
-        const size_t bytes = (size_t)a->HV * a->V * a->K * sizeof(float);
-        if ((st = hip_status(hipMemcpyAsync(a->ht, sp.hstart + (nseg - 1) * a->HV * a->V * a->K, bytes,
-                                            hipMemcpyDeviceToDevice, s),
-                             "gdp_chunk_fwd_scan: final state copy")) != GDP_OK)
-            return st;
+        if (packed) {
+            if ((st = run(gdp::launch_seg_final(sp, s), "gdp_chunk_fwd_scan: final state launch")) != GDP_OK)
+                return st;
+        } else {
+            const size_t bytes = (size_t)a->HV * a->V * a->K * sizeof(float);
+            if ((st = run(hipMemcpyAsync(a->ht, sp.hstart + (nslot - 1) * a->HV * a->V * a->K, bytes,
+                                         hipMemcpyDeviceToDevice, s),
+                          "gdp_chunk_fwd_scan: final state copy")) != GDP_OK)
+                return st;
+        }
     }
     return ok();
 }

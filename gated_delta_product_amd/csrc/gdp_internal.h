@@ -47,26 +47,38 @@ __host__ __device__ inline int64_t uv_index(int64_t b, int64_t e, int hv, int co
     return (b * HV * (VD / 16) + (int64_t)hv * (VD / 16) + col / 16) * ss + e * 16 + col % 16;
 }
 
-// Segment-parallel state recurrence of one long sequence (B == 1, no
+// Segment-parallel state recurrence.  One long sequence (B == 1, no
 // cu_seqlens): nseg segments of seg_tok tokens (the last one may be
 // shorter), the maps of segments [0, nseg - 1) in `maps`
 // ([nseg - 1, HV, K, V + K] fp32), the state entering every segment in
 // `hstart` ([nseg, HV, V, K] fp32) and the segment offsets in `cu`
-// ([nseg + 1] int32), all in caller-owned device memory.
+// ([nseg + 1] int32), all in caller-owned device memory.  Packed requests
+// (cu_seqlens, B == 1): nseg is the number of plan slots, ceil(T / seg_tok)
+// + num_seqs, each request cut into segments of seg_tok tokens by
+// launch_seg_plan on the device; maps and hstart hold one entry per slot,
+// seg_last[slot] marks segments that need no map, and req_first / req_nseg
+// give each request's slots.
 struct ScanParams {
     ChunkParams p;
     int64_t nseg, seg_tok;
     float *maps, *hstart;
     int32_t *cu;
+    int32_t *seg_last, *req_first, *req_nseg;  // packed requests only
 };
 
-// Enqueues the segment maps and the scan over segments (not the chunk_h pass).
+// Packed requests: the segment plan (one block), before launch_seg_scan.
+hipError_t launch_seg_plan(const ScanParams &sp, hipStream_t stream);
+// Packed requests: each request's final state into ht, after chunk_h.
+hipError_t launch_seg_final(const ScanParams &sp, hipStream_t stream);
+// The segment maps (every segment that needs one), then the scan over the
+// segments (not the chunk_h pass).
+hipError_t launch_seg_map(const ScanParams &sp, hipStream_t stream);
 hipError_t launch_seg_scan(const ScanParams &sp, hipStream_t stream);
 
 hipError_t launch_wy(const ChunkParams &p, hipStream_t stream);
-// launch_wy with the prefill prepare of its rows fused in (one sequence,
-// HV == H, bf16, K and V in {64, 128}): reads pp.x / pp.ba, writes pp's
-// outputs and uses them as the chunk inputs
+// launch_wy with the prefill prepare of its rows fused in (B == n == 1, one
+// sequence or packed requests, HV == H, bf16, K and V in {64, 128}): reads
+// pp.x / pp.ba, writes pp's outputs and uses them as the chunk inputs
 hipError_t launch_wy_prepare(const ChunkParams &p, const PrepareParams &pp, hipStream_t stream);
 hipError_t launch_chunk_h(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_chunk_o(const ChunkParams &p, hipStream_t stream);

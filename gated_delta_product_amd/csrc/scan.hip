@@ -63,7 +63,8 @@ template <int KD, int VD>
 __global__ void __launch_bounds__((KD + VD) * 2)
 gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
               const bf16 *__restrict__ u, const float *__restrict__ gcum, int64_t Ttok, int64_t seg_tok,
-              int nmap, int H, int HV, int M, int64_t uv_ss, float *__restrict__ maps) {
+              int nmap, int H, int HV, int M, int64_t uv_ss, float *__restrict__ maps,
+              const int32_t *__restrict__ seg_cu, const int32_t *__restrict__ seg_last) {
     constexpr int XW = KD + VD;            // columns of X
     constexpr int NW = XW / 32;            // waves
     constexpr int NKT = KD / 16;           // 16-row tiles of X
@@ -90,9 +91,14 @@ gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, cons
     const int s = (int)(blockIdx.x / HV);
     const int hv = (int)(blockIdx.x % HV);
     if (s >= nmap) return;
+    // packed requests: slot s is a segment of the plan; the last segment of
+    // each request (and every unused slot) needs no map
+    if (seg_cu != nullptr && seg_last[s] != 0) return;
     const int hk = hv / (HV / H);
     const int64_t TM = Ttok * M;
-    const int64_t r0 = (int64_t)s * seg_tok * M;  // first expanded row of the segment
+    // first expanded row of the segment: one sequence is cut at multiples of
+    // seg_tok; packed requests start where the plan says
+    const int64_t r0 = (seg_cu != nullptr ? (int64_t)seg_cu[s] : (int64_t)s * seg_tok) * M;
     const int nch = (int)(seg_tok * M / 64);      // s < nmap: a whole segment, whole chunks
 
     const int lane = lane_id(), wv = wave_id();
@@ -305,10 +311,15 @@ gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, cons
 // [32 w, 32 w + 32) of the result.  D_s is staged in LDS by coalesced loads;
 // the maps travel through two register sets, each loaded two segments ahead
 // of its use.  Block 0 also writes the segment offsets cu[0..nseg] (tokens).
+// With packed requests (req_first set) the grid holds per_req blocks per
+// request r, each running the same pass over r's segments req_first[r] ..
+// + req_nseg[r] - 1 of the plan, from r's initial state; the plan kernel
+// has written the offsets.
 template <int KD, int VD>
 __global__ void __launch_bounds__(KD * 2)
 gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int nseg, int HV, int64_t seg_tok,
-               int64_t Ttok, float *__restrict__ hstart, int32_t *__restrict__ cu) {
+               int64_t Ttok, float *__restrict__ hstart, int32_t *__restrict__ cu,
+               const int32_t *__restrict__ req_first, const int32_t *__restrict__ req_nseg, int per_req) {
     constexpr int XW = KD + VD;
     constexpr int NT = KD * 2;       // threads
     constexpr int CB = 16;           // value columns per block
@@ -322,15 +333,24 @@ gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int
     // block -> (value head, slice): the slices of one head share an XCD
     // (blocks i and i + 8 do), so each D_s comes from HBM once per head and
     // from that XCD's L2 for the other slices
-    const int slot = (int)(blockIdx.x / 8), xcd = (int)(blockIdx.x % 8);
-    const int hv = (slot / SL) * 8 + xcd;
-    const int j0 = (slot % SL) * CB;
+    int64_t blk = blockIdx.x;
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid <= nseg) {
+    if (req_first != nullptr) {  // request r: its segments are consecutive slots of the plan
+        const int64_t r = blk / per_req;
+        blk %= per_req;
+        const int64_t s0 = req_first[r];
+        nseg = req_nseg[r];
+        maps += s0 * HV * KD * XW;
+        hstart += s0 * HV * VD * KD;
+        if (h0) h0 += r * HV * VD * KD;
+    } else if (blk == 0 && tid <= nseg) {
         const int64_t t = (int64_t)tid * seg_tok;
         cu[tid] = (int32_t)(t < Ttok ? t : Ttok);
     }
-    if (hv >= HV) return;
+    const int slot = (int)(blk / 8), xcd = (int)(blk % 8);
+    const int hv = (slot / SL) * 8 + xcd;
+    const int j0 = (slot % SL) * CB;
+    if (hv >= HV || nseg <= 0) return;
     const int lane = lane_id(), wv = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
 
@@ -411,20 +431,131 @@ gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int
     write_state(nm);  // the state entering the last segment
 }
 
+// Segment plan of packed requests (one block): request r of length L_r is
+// cut into n_r = ceil(L_r / seg_tok) segments of seg_tok tokens, the last
+// one possibly shorter, numbered consecutively over the requests (first
+// segment req_first[r]).  Slot s of the plan gets its start seg_cu[s], and
+// seg_last[s] = 1 when it is the last segment of its request or unused (no
+// map needed).  Unused slots up to nslot are empty segments at the end of
+// the packed stream; slots past nslot are dropped (only a non-monotone
+// cu_seqlens, whose results are undefined, can ask for more).  Every
+// non-last segment holds seg_tok tokens, so its rows are whole chunks and
+// its chunk count is a multiple of M.
+__global__ void __launch_bounds__(256)
+gdp_seg_plan_k(const int32_t *__restrict__ cu_req, int64_t nreq, int64_t Ttok, int64_t seg_tok, int nslot,
+               int32_t *__restrict__ seg_cu, int32_t *__restrict__ seg_last, int32_t *__restrict__ req_first,
+               int32_t *__restrict__ req_nseg) {
+    __shared__ int64_t s_part[4];
+    __shared__ int64_t s_carry;
+    const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < nreq; base += 256) {
+        const int64_t i = base + tid;
+        int64_t bos = 0, eos = 0, n = 0;
+        if (i < nreq) {
+            seq_bounds(cu_req, Ttok, i, bos, eos);
+            n = ceil_div64(eos - bos, seg_tok);
+        }
+        // block-wide inclusive prefix sum of n
+        const int64_t incl_w = wave_inclusive_sum_i64(n);
+        if (lane == 63) s_part[wv] = incl_w;
+        __syncthreads();
+        int64_t before = s_carry;
+        for (int w = 0; w < wv; ++w) before += s_part[w];
+        const int64_t first = before + incl_w - n;
+        if (i < nreq) {
+            req_first[i] = (int32_t)(first < nslot ? first : nslot);
+            req_nseg[i] = (int32_t)(first + n <= nslot ? n : (first < nslot ? nslot - first : 0));
+            for (int64_t j = 0; j < n && first + j < nslot; ++j) {
+                seg_cu[first + j] = (int32_t)(bos + j * seg_tok);
+                seg_last[first + j] = j + 1 == n ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        if (tid == 255) s_carry = first + n;  // inclusive total of this group
+        __syncthreads();
+    }
+    // the end of the last segment, and the unused slots as empty segments there
+    int64_t end = 0;
+    if (nreq > 0) {
+        int64_t b0, e0;
+        seq_bounds(cu_req, Ttok, nreq - 1, b0, e0);
+        end = e0;
+    }
+    const int64_t used = s_carry < nslot ? s_carry : nslot;
+    for (int64_t s = used + tid; s <= nslot; s += 256) {
+        seg_cu[s] = (int32_t)end;
+        if (s < nslot) seg_last[s] = 1;
+    }
+}
+
+// Final state of each packed request (grid: request x value head): the
+// state after the last segment, which the chunk_h pass left in place of
+// that segment's entering state; the initial state (or zero) for an empty
+// request.
+__global__ void __launch_bounds__(256)
+gdp_seg_final_k(const float *__restrict__ hstart, const float *__restrict__ h0, const int32_t *__restrict__ req_first,
+                const int32_t *__restrict__ req_nseg, int HV, int64_t state_elems, float *__restrict__ ht) {
+    const int64_t r = blockIdx.x / HV;
+    const int hv = (int)(blockIdx.x % HV);
+    const int n = req_nseg[r];
+    const float *src = n > 0 ? hstart + ((int64_t)(req_first[r] + n - 1) * HV + hv) * state_elems
+                             : (h0 ? h0 + (r * HV + hv) * state_elems : nullptr);
+    float *dst = ht + (r * HV + hv) * state_elems;
+    for (int64_t i = threadIdx.x * 4; i < state_elems; i += 256 * 4)
+        *(f32x4 *)(dst + i) = src ? *(const f32x4 *)(src + i) : zero4();
+}
+
+template <int KD, int VD>
+static hipError_t launch_map_t(const ScanParams &sp, hipStream_t stream) {
+    const gdp_chunk_args &a = sp.p.a;
+    const bool packed = a.cu_seqlens != nullptr;
+    // maps of every segment but the last (of each request): one sequence has
+    // nseg - 1; packed requests launch every plan slot and skip the others
+    const int64_t nmap = packed ? sp.nseg : sp.nseg - 1;
+    if (nmap <= 0) return hipSuccess;
+    hipLaunchKernelGGL((gdp_seg_map_k<KD, VD>), dim3((unsigned)(nmap * a.HV)), dim3((KD + VD) * 2), 0, stream,
+                       (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.T, sp.seg_tok,
+                       (int)nmap, a.H, a.HV, a.M, sp.p.uv_ss, sp.maps, packed ? sp.cu : nullptr, sp.seg_last);
+    return hipGetLastError();
+}
+
 template <int KD, int VD>
 static hipError_t launch_scan_t(const ScanParams &sp, hipStream_t stream) {
     const gdp_chunk_args &a = sp.p.a;
-    if (sp.nseg > 1) {
-        hipLaunchKernelGGL((gdp_seg_map_k<KD, VD>), dim3((unsigned)((sp.nseg - 1) * a.HV)), dim3((KD + VD) * 2), 0,
-                           stream, (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.T,
-                           sp.seg_tok, sp.nseg - 1, a.H, a.HV, a.M, sp.p.uv_ss, sp.maps);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((gdp_seg_scan_k<KD, VD>), dim3((unsigned)((a.HV + 7) / 8 * 8 * (VD / 16))), dim3(KD * 2), 0,
-                       stream, sp.maps,
-                       a.h0, sp.nseg, a.HV, sp.seg_tok, a.T, sp.hstart, sp.cu);
+    const bool packed = a.cu_seqlens != nullptr;
+    const int per_req = (a.HV + 7) / 8 * 8 * (VD / 16);
+    const int64_t nblk = packed ? sp.p.nseq * per_req : per_req;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((gdp_seg_scan_k<KD, VD>), dim3((unsigned)nblk), dim3(KD * 2), 0, stream, sp.maps, a.h0,
+                       (int)sp.nseg, a.HV, sp.seg_tok, a.T, sp.hstart, sp.cu, packed ? sp.req_first : nullptr,
+                       sp.req_nseg, per_req);
     return hipGetLastError();
+}
+
+hipError_t launch_seg_plan(const ScanParams &sp, hipStream_t stream) {
+    const gdp_chunk_args &a = sp.p.a;
+    hipLaunchKernelGGL(gdp_seg_plan_k, dim3(1), dim3(256), 0, stream, a.cu_seqlens, sp.p.nseq, a.T, sp.seg_tok,
+                       (int)sp.nseg, sp.cu, sp.seg_last, sp.req_first, sp.req_nseg);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_final(const ScanParams &sp, hipStream_t stream) {
+    const gdp_chunk_args &a = sp.p.a;
+    if (sp.p.nseq == 0) return hipSuccess;
+    hipLaunchKernelGGL(gdp_seg_final_k, dim3((unsigned)(sp.p.nseq * a.HV)), dim3(256), 0, stream, sp.hstart, a.h0,
+                       sp.req_first, sp.req_nseg, a.HV, (int64_t)a.V * a.K, a.ht);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_map(const ScanParams &sp, hipStream_t stream) {
+    const gdp_chunk_args &a = sp.p.a;
+    if (a.K == 128 && a.V == 128) return launch_map_t<128, 128>(sp, stream);
+    if (a.K == 128 && a.V == 64) return launch_map_t<128, 64>(sp, stream);
+    if (a.K == 64 && a.V == 128) return launch_map_t<64, 128>(sp, stream);
+    if (a.K == 64 && a.V == 64) return launch_map_t<64, 64>(sp, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_seg_scan(const ScanParams &sp, hipStream_t stream) {

@@ -20,8 +20,12 @@
  *                        whose parallel stages overlap the serial one
  *   gdp_prefill_fwd_pipelined  prepare plus the pipelined chunk forward,
  *                        with each segment's prepare overlapped too
- *   gdp_chunk_fwd_scan   the same for one long sequence, with the serial
- *                        state chain cut into segments run in parallel
+ *   gdp_chunk_fwd_scan   the same for one long sequence or packed requests,
+ *                        with each long serial state chain cut into segments
+ *                        run in parallel
+ *   gdp_chunk_fwd_scan_noalloc  that form with its workspace in a device
+ *                        array of the library's own (callers that cannot
+ *                        allocate)
  *   gdp_prefill_fwd_scan prepare fused into the WY stage of that form
  *   gdp_decode_prepare   the prepare of a decode step: query and decay
  *                        interleaved onto the Householder copies
@@ -32,11 +36,15 @@
  *                        as the decode consumer)
  *
  * Conventions shared by every entry point
- *   * All tensor pointers are device pointers owned by the caller.  The
- *     library never allocates, frees or synchronises; each call only enqueues
- *     kernels on `stream` (a hipStream_t; NULL is the null stream) and
- *     returns.  Shapes are runtime values, so calls can be captured into a
- *     HIP graph.
+ *   * All tensor pointers are device pointers owned by the caller.  No call
+ *     allocates or frees device memory or synchronises with the host; each
+ *     only enqueues kernels on `stream` (a hipStream_t; NULL is the null
+ *     stream) and returns.  Shapes are runtime values, so calls can be
+ *     captured into a HIP graph.  Two entry points hold resources of their
+ *     own: the pipelined forwards create two side streams and their events
+ *     once per device, and gdp_chunk_fwd_scan_noalloc looks up its static
+ *     device array once per device; make the first such call on a device
+ *     outside graph capture.
  *   * Every call validates its arguments before launching anything.  A bad
  *     argument returns GDP_ERR_INVALID or GDP_ERR_UNSUPPORTED with nothing
  *     launched and nothing written; gdp_last_error() then describes it.  A
@@ -338,39 +346,50 @@ gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_
                                      float *state_workspace, void *const *chunk_h_events, void *stream);
 
 /*
- * gdp_chunk_fwd_scan -- the same results as gdp_chunk_fwd for one long
- * sequence (B == 1, cu_seqlens == NULL), within rounding, with the serial
- * chunk_h chain cut into segments that run in parallel.  Over one chunk the
- * state update is affine in the entering state (the chunk transition of the
- * WY representation of the product of the chunk's generalised Householder
+ * gdp_chunk_fwd_scan -- the same results as gdp_chunk_fwd, within rounding,
+ * for one long sequence (B == 1, cu_seqlens == NULL) or for packed requests
+ * (B == 1 with cu_seqlens: the dynamic-batching prefill of
+ * core.ssm.ops.gdp.prepare), with the serial chunk_h chain of every long
+ * sequence cut into segments that run in parallel.  Over one chunk the state
+ * update is affine in the entering state (the chunk transition of the WY
+ * representation of the product of the chunk's generalised Householder
  * factors, core.ssm.ops.gdp.wy_fast and the chunk_h stage of
  * core.ssm.ops.gdp.chunk_o), so each segment's map h -> D h + E is
- * composed first, all segments at once; a short serial pass over the
- * segments then gives the state entering each of them, and one chunk_h pass
- * runs every segment from its own entering state.  All work is enqueued on
- * `stream`, in this order: gdp_recompute_w_u; the segment maps (kernel
- * gdp_seg_map_k); the scan over segments (gdp_seg_scan_k); chunk_h;
- * gdp_chunk_o; and, if ht is given, a device copy of the final state.
- *   num_segments    1..GDP_SCAN_MAX_SEGMENTS requested; the sequence is cut
- *                   into segments of ceil(ceil(T/64) / num_segments) * 64
- *                   tokens (gdp_scan_segments gives how many result).
+ * composed first, all segments at once; a short serial pass over each
+ * sequence's segments then gives the state entering each of them, and one
+ * chunk_h pass runs every segment from its own entering state.  All work is
+ * enqueued on `stream`, in this order: gdp_recompute_w_u; for packed
+ * requests the segment plan (gdp_seg_plan_k, on the device from
+ * cu_seqlens); the segment maps (gdp_seg_map_k); the scan over segments
+ * (gdp_seg_scan_k); chunk_h; gdp_chunk_o; and, if ht is given, the final
+ * states (a device copy, or gdp_seg_final_k for packed requests).
+ *   num_segments    1..GDP_SCAN_MAX_SEGMENTS requested; segments are
+ *                   seg_tok = ceil(ceil(T/64) / num_segments) * 64 tokens
+ *                   long, T the sequence length or the packed total.  One
+ *                   sequence is cut into ceil(T / seg_tok) of them
+ *                   (gdp_scan_segments); each packed request of length L
+ *                   into ceil(L / seg_tok), so requests shorter than seg_tok
+ *                   stay whole and need no map.
  *   workspace       device memory of at least gdp_scan_workspace_bytes(...)
- *                   bytes, 256-byte aligned, caller-owned; its contents on
- *                   entry do not matter and on return are unspecified.
- *   stage_events    NULL, or 3 hipEvent_t handles (as void *) recorded on
- *                   `stream` right before the segment maps, right before
- *                   the chunk_h launch (after the scan) and right after it
- *                   (for timing those stages).
+ *                   (one sequence) or gdp_scan_workspace_bytes_varlen(...)
+ *                   (packed requests) bytes, 256-byte aligned,
+ *                   caller-owned; its contents on entry do not matter and on
+ *                   return are unspecified.
+ *   stage_events    NULL, or 5 hipEvent_t handles (as void *) recorded on
+ *                   `stream` right after the WY stage (and the plan), after
+ *                   the segment maps, after the scan, after chunk_h and after
+ *                   chunk_o (for timing each stage).
  * Every tensor of `a` is as for gdp_chunk_fwd, except h: only the states
- * entering chunks c = i*M (those entering each 64-token chunk, the ones
- * gdp_chunk_o reads) are written; the other slots of h are left untouched.
- * w, u, k_rnorm, gcum and kdecay are bit-identical to gdp_chunk_fwd, and so
- * are the written h, v_new and o over the first segment; the states entering
- * later segments come out of the composed maps, so h, v_new, o and ht there
- * agree with gdp_chunk_fwd to rounding (the composition runs on bf16
- * matrix-core operands with fp32 accumulation, like the chunk recurrence
- * itself).  Supported: dtype bf16 with K, V in
- * {64, 128} and T*M*V*2 < 2^31; other shapes return GDP_ERR_UNSUPPORTED.
+ * entering chunks c = i*M of each sequence (those entering each 64-token
+ * chunk, the ones gdp_chunk_o reads) are written; the other slots of h are
+ * left untouched.  w, u, k_rnorm, gcum and kdecay are bit-identical to
+ * gdp_chunk_fwd, and so are h, v_new and o over the first segment of each
+ * sequence; the states entering later segments come out of the composed
+ * maps, so h, v_new, o and ht there agree with gdp_chunk_fwd to rounding
+ * (the composition runs on the same bf16 matrix-core operands with fp32
+ * accumulation as the chunk recurrence itself).  Supported: dtype bf16 with
+ * K, V in {64, 128} and T*M*V*2 < 2^31; other shapes return
+ * GDP_ERR_UNSUPPORTED.  B > 1 without cu_seqlens returns GDP_ERR_INVALID.
  */
 #define GDP_SCAN_MAX_SEGMENTS 64
 gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, void *workspace,
@@ -385,7 +404,8 @@ gdp_status gdp_chunk_fwd_scan(const gdp_chunk_args *a, int32_t num_segments, voi
  * hipMalloc, hipFree or allocating library routine); the caller still passes
  * every input and output in `a`.
  *   Limit: the workspace gdp_scan_workspace_bytes(T, HV, K, V,
- *   num_segments) reports must fit GDP_NOALLOC_SCRATCH_BYTES (64 MiB; the
+ *   num_segments) reports (gdp_scan_workspace_bytes_varlen with
+ *   cu_seqlens) must fit GDP_NOALLOC_SCRATCH_BYTES (64 MiB; the
  *   32768-token, 16-head, K = V = 128 sequence with 16 segments needs 47.5
  *   MiB); a larger call returns GDP_ERR_UNSUPPORTED, launches nothing and
  *   makes no HIP call.  Every other argument is checked, and refused, as by
@@ -407,7 +427,8 @@ gdp_status gdp_chunk_fwd_scan_noalloc(const gdp_chunk_args *a, int32_t num_segme
 
 /*
  * gdp_prefill_fwd_scan -- gdp_prefill_prepare followed by gdp_chunk_fwd_scan
- * for one sequence, with the prepare done inside the WY stage: each
+ * for one sequence or packed requests (n == B == 1, with or without
+ * cu_seqlens), with the prepare done inside the WY stage: each
  * gdp_recompute_w_u block reads its key and value copies, query and gate
  * inputs straight from x and ba (the layouts of gdp_prefill_prepare), writes
  * prepare's outputs for its rows (q and g of a token by the block holding
@@ -417,10 +438,13 @@ gdp_status gdp_chunk_fwd_scan_noalloc(const gdp_chunk_args *a, int32_t num_segme
  * makes H value heads).  v and beta may be NULL: no stage after WY reads
  * them (the values enter u inside it), so they are then not stored, which
  * saves their HBM writes; every other output is unchanged.  Every output is
- * bit-identical to the two calls in sequence.  The requirements are those of gdp_chunk_fwd_scan (B == n == 1)
- * and of gdp_prefill_prepare, plus 16-byte aligned rows of x and of the
- * outputs; stage_events as for gdp_chunk_fwd_scan (the first one is
- * recorded after the WY-with-prepare stage).
+ * bit-identical to the two calls in sequence, except that with cu_seqlens
+ * the prepare outputs of tokens outside every request (none when the
+ * offsets run from 0 to T) are not written.  The requirements are those of
+ * gdp_chunk_fwd_scan (B == n == 1) and of gdp_prefill_prepare, plus 16-byte
+ * aligned rows of x and of the outputs; stage_events as for
+ * gdp_chunk_fwd_scan (the first one is recorded after the WY-with-prepare
+ * stage).
  */
 gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *p, const gdp_chunk_args *a, int32_t num_segments,
                                 void *workspace, int64_t workspace_bytes, void *const *stage_events, void *stream);
@@ -429,10 +453,19 @@ gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *p, const gdp_chunk_args 
    (0 for T == 0), or -1 on bad arguments. */
 int32_t gdp_scan_segments(int64_t T, int32_t num_segments);
 
-/* Workspace bytes gdp_chunk_fwd_scan needs: per value head, a K x (V + K)
-   fp32 map for every segment but the last and a V x K fp32 state for every
-   segment, plus the segment offsets; -1 on bad arguments. */
+/* Workspace bytes gdp_chunk_fwd_scan needs for one sequence: per value
+   head, a K x (V + K) fp32 map for every segment but the last and a V x K
+   fp32 state for every segment, plus the segment offsets; -1 on bad
+   arguments. */
 int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, int32_t num_segments);
+
+/* Workspace bytes gdp_chunk_fwd_scan needs for num_seqs packed requests of T
+   tokens in all: a map and a state per value head for each of the
+   ceil(T / seg_tok) + num_seqs slots that can hold a segment, plus the plan
+   (offsets and flags per slot, first slot and count per request); -1 on bad
+   arguments.  It depends on T and num_seqs only, not on the lengths. */
+int64_t gdp_scan_workspace_bytes_varlen(int64_t T, int64_t num_seqs, int32_t HV, int32_t K, int32_t V,
+                                        int32_t num_segments);
 
 /* Segments gdp_chunk_fwd_pipelined actually runs for T tokens (whole
    64-token chunks, at most num_segments); 0 for T == 0, -1 on bad

@@ -273,7 +273,9 @@ def test_scan_rejects_and_plan():
     big = 1 << 40
     a = lambda **kw: ctypes.byref(_args(**dict(dict(K=128, V=128), **kw)))
     assert L.gdp_chunk_fwd_scan(a(B=2, h_chunks=4), 4, ws, big, None, None) == B.GDP_ERR_INVALID
-    assert L.gdp_chunk_fwd_scan(a(cu_seqlens=0x1000, num_seqs=1), 4, ws, big, None, None) == B.GDP_ERR_INVALID
+    # packed requests go through cu_seqlens with B == 1
+    assert L.gdp_chunk_fwd_scan(a(B=2, cu_seqlens=0x1000, num_seqs=1), 4, ws, big, None, None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd_scan(a(cu_seqlens=0x1000, num_seqs=-1), 4, ws, big, None, None) == B.GDP_ERR_INVALID
     assert L.gdp_chunk_fwd_scan(a(), 0, ws, big, None, None) == B.GDP_ERR_INVALID
     assert L.gdp_chunk_fwd_scan(a(), 65, ws, big, None, None) == B.GDP_ERR_INVALID
     assert L.gdp_chunk_fwd_scan(a(), 2, None, big, None, None) == B.GDP_ERR_INVALID
@@ -298,6 +300,19 @@ def test_scan_rejects_and_plan():
     want = up(15 * HV * K * (K + V) * 4) + up(16 * HV * V * K * 4) + up(17 * 4)
     assert L.gdp_scan_workspace_bytes(32768, HV, K, V, 16) == want
     assert L.gdp_scan_workspace_bytes(32768, HV, K, V, 0) == -1
+    # packed requests: a map and a state for each of ceil(T / seg_tok) + N
+    # slots, the offsets and last flags per slot, first slot and count per
+    # request (seg_tok = 17 chunks for 16600 tokens in 16 segments)
+    T, N = 16600, 8
+    slots = -(-T // (17 * 64)) + N
+    want = up(slots * HV * K * (K + V) * 4) + up(slots * HV * V * K * 4) + up((slots + 1) * 4) + up(slots * 4) \
+        + 2 * up(N * 4)
+    assert L.gdp_scan_workspace_bytes_varlen(T, N, HV, K, V, 16) == want
+    assert L.gdp_scan_workspace_bytes_varlen(T, -1, HV, K, V, 16) == -1
+    # a packed call checks its workspace against the varlen size
+    assert L.gdp_chunk_fwd_scan(a(T=T, H=HV, HV=HV, cu_seqlens=0x1000, num_seqs=N, h_chunks=600), 16, ws,
+                                want - 256, None, None) == B.GDP_ERR_INVALID
+    assert b"workspace" in L.gdp_last_error()
 
 
 def test_prefill_scan_rejects():

@@ -692,28 +692,47 @@ def test_hip_graph_capture_replays():
 H_MARK = 7.0  # a bf16 value no snapshot of these draws takes in every element
 
 
-def _check_unwritten_h(buf, M):
+def _check_unwritten_h(buf, M, seqs=None):
     """The segment-parallel forward writes only the states entering chunks
-    c % M == 0; every other slot must still hold the mark put there before."""
-    if M > 1:
-        keep = torch.ones(buf.h.shape[0], dtype=torch.bool, device=buf.h.device)
+    c % M == 0 of each sequence (c counted from the sequence's first chunk);
+    every other slot must still hold the mark put there before.  seqs: the
+    (batch, t0, t1, first chunk) list of packed requests (default: one
+    sequence)."""
+    if M == 1:
+        return
+    keep = torch.ones(buf.h.shape[0], dtype=torch.bool, device=buf.h.device)
+    if seqs is None:
         keep[::M] = False
-        rest = buf.h[keep]
-        assert bool((rest == H_MARK).all()), "a skipped state slot was written"
-        assert not bool((buf.h[::M] == H_MARK).all()), "the written state slots were not written"
+    else:
+        for (_, t0, t1, hbase) in seqs:
+            nc = math.ceil((t1 - t0) * M / 64)
+            keep[hbase:hbase + nc:M] = False
+    rest = buf.h[keep]
+    assert bool((rest == H_MARK).all()), "a skipped state slot was written"
+    written = buf.h[~keep]
+    assert written.numel() == 0 or not bool((written == H_MARK).all()), "the written state slots were not written"
 
 
-def _scan_buf(q, k, v, beta, g, nseg, h0=None):
-    buf = G.ChunkBuffers(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), None if g is None else g.to(DEV),
-                         initial_state=None if h0 is None else h0.to(DEV), output_final_state=h0 is not None)
-    buf.h.fill_(H_MARK)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+def _stage_events():
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     for e in evs:
         e.record()  # creates the HIP event
+    return evs
+
+
+def _scan_buf(q, k, v, beta, g, nseg, h0=None, cu=None, seqs=None):
+    buf = G.ChunkBuffers(q.to(DEV), k.to(DEV), v.to(DEV), beta.to(DEV), None if g is None else g.to(DEV),
+                         cu_seqlens=None if cu is None else torch.as_tensor(cu, dtype=torch.int32).to(DEV),
+                         cu_seqlens_host=cu,
+                         initial_state=None if h0 is None else h0.to(DEV), output_final_state=h0 is not None)
+    buf.h.fill_(H_MARK)
+    evs = _stage_events()
     buf.forward_scan(nseg, stage_events=evs)
     torch.cuda.synchronize()
-    assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
-    _check_unwritten_h(buf, buf.dims["M"])
+    # the stages in order (a map stage with no map to compose may take ~0)
+    assert all(evs[i].elapsed_time(evs[i + 1]) >= 0 for i in range(4))
+    assert evs[2].elapsed_time(evs[3]) > 0 and evs[3].elapsed_time(evs[4]) > 0
+    _check_unwritten_h(buf, buf.dims["M"], seqs)
     return buf
 
 
@@ -831,6 +850,96 @@ def test_scan_long_prefill_sampled():
                 tag="long_prefill_32k scan", buf=buf, hstep=c["M"])
 
 
+VARLEN_SCAN_CASES = [
+    # lengths, H, HV, K, V, M, segments, seed, long memory, h0
+    ([1000, 0, 1, 64, 65, 2500, 130, 700], 2, 4, 128, 128, 2, 8, 61, False, True),
+    ([3000, 17, 1500], 1, 2, 64, 128, 3, 6, 62, True, False),
+    ([200, 300, 129], 2, 2, 128, 64, 1, 4, 63, False, True),
+    ([50, 60, 70], 1, 1, 64, 64, 2, 2, 64, False, True),  # every request shorter than a segment: no map
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_SCAN_CASES, ids=lambda c: "n%d-K%dV%d-M%d-s%d%s" % (
+    len(c[0]), c[3], c[4], c[5], c[6], "-long" if c[8] else ""))
+def test_scan_varlen_matches_oracle(case):
+    """gdp_chunk_fwd_scan on packed requests (cu_seqlens): each long request
+    cut into segments on the device, short, 1-token and empty requests kept
+    whole, GVA, M = 1..3, long memory, per-request initial and final states.
+    Every output of every (request, head) against the oracle; w, u and the
+    per-row intermediates bit-identical to gdp_chunk_fwd, and so are o and
+    v_new over the first segment of each request."""
+    lens, H, HV, K, V, M, nseg, seed, longmem, with_h0 = case
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", seed)
+    if longmem:
+        d["dt_bias"] = torch.empty(HV).uniform_(-9, -7, generator=torch.Generator().manual_seed(seed))
+    beta, g = gates(d)
+    beta = beta.reshape(1, T * M, HV)
+    h0 = synth.initial_state_draws(len(lens), HV, V, K, seed + 100) if with_h0 else None
+    seqs = _seqs_varlen(cu, M)
+    seg_tok = ((T + 63) // 64 + nseg - 1) // nseg * 64 if T else 64
+    log("varlen scan %s: T=%d, seg_tok %d, segments %s" % (lens, T, seg_tok, [-(-n // seg_tok) for n in lens]))
+    buf = _scan_buf(d["q"], d["k"], d["v"], beta, g, nseg, h0, cu=cu, seqs=seqs)
+    check_chunk(d["q"], d["k"], d["v"], beta, g, seqs, range(HV), M, cu=cu, cu_host=cu, tag="varlen scan",
+                buf=buf, h0=h0, hstep=M)
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).to(DEV)
+    ref = G.chunk_fwd(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), beta.to(DEV), g.to(DEV), cu_seqlens=cu_d,
+                      cu_seqlens_host=cu, initial_state=None if h0 is None else h0.to(DEV),
+                      output_final_state=h0 is not None)
+    torch.cuda.synchronize()
+    for nm in ("w", "u", "k_rnorm", "gcum", "kdecay"):
+        assert torch.equal(ref.__dict__[nm], buf.__dict__[nm]), nm
+    vn_ref, vn = G.slices_to_rows(ref.v_new), G.slices_to_rows(buf.v_new)
+    for (_, t0, t1, _) in seqs:
+        t1s = min(t1, t0 + seg_tok)
+        assert torch.equal(ref.o[:, t0:t1s], buf.o[:, t0:t1s]), ("first segment o", t0)
+        assert torch.equal(vn_ref[:, t0 * M:t1s * M], vn[:, t0 * M:t1s * M]), ("first segment v_new", t0)
+
+
+def test_prefill_scan_varlen_workload():
+    """The GVA varlen prefill workload (8 packed requests, lengths in [64,
+    4096], prepare with 16 heads from 4 groups, M = 2) through
+    gdp_prefill_fwd_scan: prepare's outputs and every chunk output
+    bit-identical to gdp_prefill_prepare then gdp_chunk_fwd_scan on the same
+    cu_seqlens, o against the oracle on sampled heads of every request, and
+    the GVA form (H = 4 key heads, the pre-expansion groups) of
+    gdp_chunk_fwd_scan equal to the expanded run."""
+    c = synth.CONFIGS[3]
+    p = c["prep"]
+    M, nseg = c["M"], 16
+    d = synth.varlen_prepare_draws(3)
+    cu = d["cu_seqlens"]
+    T = int(cu[-1])
+    x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).to(DEV)
+    pre = G.prefill_prepare(x, ba, A_log, dt_bias, M, p["H"], p["G"], p["P"], p["N"])
+    ref = G.ChunkBuffers(*pre, cu_seqlens=cu_d, cu_seqlens_host=cu)
+    ref.h.fill_(H_MARK)
+    ref.forward_scan(nseg)
+    outs = [torch.full_like(t, 7) for t in pre]
+    fz = G.ChunkBuffers(*outs, cu_seqlens=cu_d, cu_seqlens_host=cu)
+    fz.h.fill_(H_MARK)
+    fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], nseg, stage_events=_stage_events())
+    torch.cuda.synchronize()
+    for a_, b_, nm in zip(outs, pre, ("q", "k", "v", "beta", "g")):
+        assert torch.equal(a_, b_), nm
+    for nm in ("o", "w", "u", "v_new", "h", "k_rnorm", "gcum", "kdecay"):
+        assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
+    seqs = _seqs_varlen(cu, M)
+    _check_unwritten_h(fz, M, seqs)
+    hpg = p["H"] // p["G"]
+    q, k, v, beta, g = pre
+    gva = G.ChunkBuffers(q[:, :, ::hpg].contiguous(), k[:, :, ::hpg].contiguous(), v, beta, g, cu_seqlens=cu_d,
+                         cu_seqlens_host=cu)
+    gva.forward_scan(nseg)
+    torch.cuda.synchronize()
+    for nm in ("o", "w", "u", "v_new"):
+        assert torch.equal(getattr(gva, nm), getattr(ref, nm)), "GVA vs expanded: " + nm
+    check_chunk(q.cpu(), k.cpu(), v.cpu(), beta.cpu(), g.cpu(), seqs, [0, 7, 15], M, cu=cu, cu_host=cu,
+                tag="varlen prefill scan", buf=fz, hstep=M, want_wu=False)
+
+
 @pytest.mark.parametrize("K,V,M,n", [(128, 128, 2, 64), (64, 256, 3, 64), (128, 64, 1, 64), (128, 128, 2, 12)])
 def test_chunk_h_two_pairs_per_block(K, V, M, n):
     """With many chains (packed requests x 16 value heads) chunk_h runs
@@ -895,10 +1004,7 @@ def test_prefill_scan_is_bit_identical(case):
     outs = [torch.full_like(t, 7) for t in pre]  # the fused prepare must overwrite all of them
     fz = G.ChunkBuffers(*outs, initial_state=h0, output_final_state=True)
     fz.h.fill_(H_MARK)  # the slots neither call writes then match as well
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    for e in evs:
-        e.record()
-    fz.prefill_scan(x, ba, A_log, dt_bias, G_, nseg, stage_events=evs)
+    fz.prefill_scan(x, ba, A_log, dt_bias, G_, nseg, stage_events=_stage_events())
     torch.cuda.synchronize()
     for a_, b_, nm in zip(outs, pre, ("q", "k", "v", "beta", "g")):
         assert torch.equal(a_, b_), nm
