@@ -105,7 +105,7 @@ class TimingEvent:
             self._hip.hipEventDestroy(self.cuda_event)
 
 
-def algorithmic_bytes(w, T=None):
+def algorithmic_bytes(w, T=None, es=2):
     """HBM bytes each stage must move at minimum (inputs read once, outputs
     written once), per launch over T tokens (default: the whole workload).
     es = 2 (bf16); beta, g, k_rnorm, gcum and kdecay are fp32.
@@ -117,7 +117,6 @@ def algorithmic_bytes(w, T=None):
     T = w["T"] * w["B"] if T is None else T
     M, H, HV, G, K, V = w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
     P, N = V, K
-    es = 2
     TM = T * M
     nte = math.ceil(T * M / 64)
     ntok_chunks = math.ceil(T / 64)
@@ -132,7 +131,7 @@ def algorithmic_bytes(w, T=None):
     return {"gdp_prefill_prepare": prep, "gdp_recompute_w_u": wy, "gdp_chunk_h": ch, "gdp_chunk_o": co}
 
 
-def scan_bytes(w, segments, nseg):
+def scan_bytes(w, segments, nseg, mapped_tokens=None, nstates=None):
     """Algorithmic bytes per launch of the segment-parallel stages over the
     whole workload (one sequence, es = 2).
       wy_fused  the prepare's reads (x, ba) and writes (q, k, g; v and beta
@@ -141,17 +140,21 @@ def scan_bytes(w, segments, nseg):
       map       k, kdecay, gcum, w, u of every segment but the last, read
                 once; one fp32 K x (K + V) map per segment and head written
       scan      the maps read, one fp32 state per segment and head written
-      chunk_h   as algorithmic_bytes, with one state per 64-token chunk"""
+      chunk_h   as algorithmic_bytes, with one state per 64-token chunk
+    Packed requests give mapped_tokens (the tokens of every segment but the
+    last of each request) and nstates (the segments) instead of nseg."""
     T, M, H, HV, G, K, V = w["T"] * w["B"], w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
     ab = algorithmic_bytes(w)
     TM = T * M
     wy_fused = ab["gdp_prefill_prepare"] + ab["gdp_recompute_w_u"] - (TM * HV * (K + V) * 2 + TM * HV * 4 + T * HV * 4) \
         - TM * HV * (V * 2 + 4)
     seg_tok = math.ceil(math.ceil(T / 64) / segments) * 64
-    TMm = (nseg - 1) * seg_tok * M
-    maps = (nseg - 1) * HV * K * (K + V) * 4
+    if mapped_tokens is None:
+        mapped_tokens, nstates = (nseg - 1) * seg_tok, nseg
+    TMm = mapped_tokens * M
+    maps = mapped_tokens // seg_tok * HV * K * (K + V) * 4
     mapb = TMm * H * K * 2 + TMm * HV * 8 + TMm * HV * (K + V) * 2 + maps
-    scanb = maps + nseg * HV * V * K * 4
+    scanb = maps + nstates * HV * V * K * 4
     ch = ab["gdp_chunk_h"] - (math.ceil(T * M / 64) - math.ceil(T / 64)) * HV * V * K * 2
     return {"wy_fused": wy_fused, "map": mapb, "scan": scanb, "chunk_h": ch}
 
@@ -257,6 +260,202 @@ def decode_step(G, torch, dev, stream, steps):
                                   "hbm_frac": round(ub / upd_us / 1e3 / HBM_PEAK_GBS, 4)}}
 
 
+def varlen_segments(cu, segments):
+    """Segments the packed scan form cuts each request into (host copy of
+    the device plan): seg_tok from the packed total, ceil(len / seg_tok) per
+    request."""
+    T = int(cu[-1])
+    seg_tok = math.ceil(math.ceil(T / 64) / segments) * 64
+    return seg_tok, [math.ceil((int(cu[i + 1]) - int(cu[i])) / seg_tok) for i in range(len(cu) - 1)]
+
+
+def stage_record(torch, stream, n):
+    evs = [TimingEvent() for _ in range(n)]
+    for e in evs:
+        e.record(stream)
+    torch.cuda.synchronize()
+    return evs
+
+
+def time_stages(torch, stream, fn, n_ev, reps=10, warmup=3):
+    """Mean time (us) between consecutive events of fn(events) over reps
+    calls; fn records events[0] first and fills the rest."""
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    evs = [stage_record(torch, stream, n_ev) for _ in range(reps)]
+    for e in evs:
+        fn(e)
+    torch.cuda.synchronize()
+    return [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e3 for i in range(n_ev - 1)]
+
+
+def roofline_of(kern):
+    dom = max(kern, key=lambda kk: kern[kk]["us"])
+    return {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": kern[dom]["hbm_frac"]}
+
+
+def kernel_entry(us, alg):
+    return {"us": round(us, 2), "alg_bytes": int(alg), "GB/s": round(alg / us / 1e3, 1),
+            "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def chunk_fwd_line(G, torch, dev, stream, cfg_id, reps):
+    """gdp_chunk_fwd (its three stages in order, each bracketed by events) on
+    one of the equal-length workloads, inputs drawn on the device: q, k on the
+    unit sphere, v, b, a ~ N(0, 1) (a scaled by the workload's sigma), A_log =
+    log U[1, 16], dt_bias ~ U[-1, 1]; beta and g from them by the gate
+    formulas, outside the timed region."""
+    from gated_delta_product_amd import synth
+    c = synth.CONFIGS[cfg_id]
+    B, T, H, HV, K, V, M = c["B"], c["T"], c["H"], c["HV"], c["K"], c["V"], c["M"]
+    dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    gen = torch.Generator(device=dev).manual_seed(synth.seed_of(cfg_id) + 500)
+
+    def sphere(shape):
+        x = torch.randn(shape, generator=gen, device=dev)
+        return (x / x.norm(dim=-1, keepdim=True)).to(dt)
+
+    q, k = sphere((B, T, H, K)), sphere((B, T * M, H, K))
+    v = torch.randn((B, T * M, HV, V), generator=gen, device=dev).to(dt)
+    b = torch.randn((B, T * M, HV), generator=gen, device=dev)
+    a = torch.randn((B, T, HV), generator=gen, device=dev) * c.get("a_sigma", 1.0)
+    A_log = torch.log(torch.rand(HV, generator=gen, device=dev) * 15 + 1)
+    dt_bias = torch.rand(HV, generator=gen, device=dev) * 2 - 1
+    beta = torch.sigmoid(b)
+    g = -torch.exp(A_log) * torch.nn.functional.softplus(a + dt_bias)
+    buf = G.ChunkBuffers(q, k, v, beta, g)
+
+    def run(ev):
+        if ev:
+            ev[0].record(stream)
+        buf.recompute_w_u()
+        if ev:
+            ev[1].record(stream)
+        buf.chunk_h()
+        if ev:
+            ev[2].record(stream)
+        buf.chunk_o()
+        if ev:
+            ev[3].record(stream)
+
+    us = time_stages(torch, stream, run, 4, reps)
+    w = dict(B=B, T=T, H=H, HV=HV, G=H, K=K, V=V, M=M)
+    ab = algorithmic_bytes(w, es=2 if dt == torch.bfloat16 else 4)
+    kern = {"gdp_recompute_w_u": kernel_entry(us[0], ab["gdp_recompute_w_u"]),
+            "gdp_chunk_h": kernel_entry(us[1], ab["gdp_chunk_h"]),
+            "gdp_chunk_o": kernel_entry(us[2], ab["gdp_chunk_o"])}
+    tot = sum(us)
+    del buf, q, k, v, b, a, beta, g
+    torch.cuda.empty_cache()
+    return {"workload": c["name"], "shape": dict(w, dtype=c["dtype"]), "path": "gdp_chunk_fwd",
+            "us": round(tot, 1), "tokens_per_s": round(B * T / (tot / 1e6), 1), "kernels": kern,
+            "roofline": roofline_of(kern)}
+
+
+def varlen_line(G, torch, dev, stream, reps, segments=16):
+    """The GVA varlen prefill workload: 8 packed requests (lengths drawn in
+    [64, 4096]), prepare with 16 heads from 4 groups (timed on its own), then
+    the segment-parallel chunk forward with GVA (4 key heads for 16 value
+    heads); and the fused form, gdp_prefill_fwd_scan on the expanded heads,
+    end to end."""
+    from gated_delta_product_amd import synth
+    c = synth.CONFIGS[3]
+    p = c["prep"]
+    M = c["M"]
+    d = synth.varlen_prepare_draws(3)
+    cu = d["cu_seqlens"]
+    T = int(cu[-1])
+    x, ba, A_log, dt_bias = d["x"].to(dev), d["ba"].to(dev), d["A_log"].to(dev), d["dt_bias"].to(dev)
+    cu_d = torch.as_tensor(cu, dtype=torch.int32).to(dev)
+    pre = G.prefill_prepare(x, ba, A_log, dt_bias, M, p["H"], p["G"], p["P"], p["N"])
+
+    def run_prep(ev):
+        if ev:
+            ev[0].record(stream)
+        G.prefill_prepare(x, ba, A_log, dt_bias, M, p["H"], p["G"], p["P"], p["N"], out=pre)
+        if ev:
+            ev[1].record(stream)
+
+    prep_us = time_stages(torch, stream, run_prep, 2, reps)[0]
+    q, k, v, beta, g = pre
+    hpg = p["H"] // p["G"]
+    gva = G.ChunkBuffers(q[:, :, ::hpg].contiguous(), k[:, :, ::hpg].contiguous(), v, beta, g, cu_seqlens=cu_d,
+                         cu_seqlens_host=cu)
+
+    def run_scan(ev):
+        if ev:
+            ev[0].record(stream)
+        gva.forward_scan(segments, stage_events=ev[1:] if ev else None)
+
+    us = time_stages(torch, stream, run_scan, 6, reps)
+    seq = G.ChunkBuffers(gva.q, gva.k, v, beta, g, cu_seqlens=cu_d, cu_seqlens_host=cu)
+
+    def run_seq(ev):
+        if ev:
+            ev[0].record(stream)
+        seq.forward()
+        if ev:
+            ev[1].record(stream)
+
+    seq_us = time_stages(torch, stream, run_seq, 2, reps)[0]
+    fz = G.ChunkBuffers(*[torch.empty_like(t) for t in pre], cu_seqlens=cu_d, cu_seqlens_host=cu)
+
+    def run_fused(ev):
+        if ev:
+            ev[0].record(stream)
+        fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], segments, stage_events=ev[1:] if ev else None,
+                        store_v_beta=False)
+
+    fus = time_stages(torch, stream, run_fused, 6, reps)
+
+    def run_fused1(ev):  # every request one segment: no maps
+        if ev:
+            ev[0].record(stream)
+        fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], 1, stage_events=ev[1:] if ev else None,
+                        store_v_beta=False)
+
+    fus1 = time_stages(torch, stream, run_fused1, 6, reps)
+    # algorithmic bytes: the chunk stages at H = 4 key heads, HV = 16
+    w = dict(B=1, T=T, H=c["H"], HV=c["HV"], G=c["H"], K=c["K"], V=c["V"], M=M)
+    ab = algorithmic_bytes(w)
+    wp = dict(B=1, T=T, H=p["H"], HV=p["H"], G=p["G"], K=p["N"], V=p["P"], M=M)
+    prep_b = algorithmic_bytes(wp)["gdp_prefill_prepare"]
+    seg_tok, nsegs = varlen_segments(cu, segments)
+    mapped = sum((n - 1) * seg_tok for n in nsegs if n > 1)
+    sb = scan_bytes(w, segments, None, mapped_tokens=mapped, nstates=sum(nsegs))
+    kern = {"gdp_recompute_w_u": kernel_entry(us[0], ab["gdp_recompute_w_u"]),
+            "gdp_seg_map": kernel_entry(us[1], sb["map"]), "gdp_seg_scan": kernel_entry(us[2], sb["scan"]),
+            "gdp_chunk_h": kernel_entry(us[3], sb["chunk_h"]), "gdp_chunk_o": kernel_entry(us[4], ab["gdp_chunk_o"])}
+    tot = sum(us)
+    sbf = scan_bytes(wp, segments, None, mapped_tokens=mapped, nstates=sum(nsegs))
+    kf = {"gdp_recompute_w_u (prepare fused)": kernel_entry(fus[0], sbf["wy_fused"]),
+          "gdp_seg_map": kernel_entry(fus[1], sbf["map"]), "gdp_seg_scan": kernel_entry(fus[2], sbf["scan"]),
+          "gdp_chunk_h": kernel_entry(fus[3], sbf["chunk_h"]),
+          "gdp_chunk_o": kernel_entry(fus[4], algorithmic_bytes(wp)["gdp_chunk_o"])}
+    out = {"workload": c["name"], "T": T, "cu_seqlens": [int(t) for t in cu], "segments_per_request": nsegs,
+           "seg_tok": seg_tok,
+           "prepare": dict(kernel_entry(prep_us, prep_b), tokens_per_s=round(T / (prep_us / 1e6), 1),
+                           shape=dict(H=p["H"], G=p["G"], P=p["P"], N=p["N"], M=M)),
+           "chunk_fwd_scan_gva": {"path": "gdp_chunk_fwd_scan, H=4 key heads, HV=16", "us": round(tot, 1),
+                                  "tokens_per_s": round(T / (tot / 1e6), 1), "kernels": kern,
+                                  "roofline": roofline_of(kern)},
+           "chunk_fwd_sequential_gva": {"path": "gdp_chunk_fwd (unsegmented chunk_h)", "us": round(seq_us, 1),
+                                        "tokens_per_s": round(T / (seq_us / 1e6), 1)},
+           "prefill_fwd_scan": {"path": "gdp_prefill_fwd_scan (prepare inside WY, H=HV=16 expanded, v and beta "
+                                        "not stored)", "us": round(sum(fus), 1),
+                                "tokens_per_s": round(T / (sum(fus) / 1e6), 1), "kernels": kf,
+                                "roofline": roofline_of(kf)},
+           "prefill_fwd_scan_1seg": {"path": "gdp_prefill_fwd_scan with num_segments=1 (no request split, no "
+                                             "maps)", "us": round(sum(fus1), 1),
+                                     "tokens_per_s": round(T / (sum(fus1) / 1e6), 1),
+                                     "stage_us": [round(u, 1) for u in fus1]}}
+    del gva, seq, fz, pre, x, ba
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +471,8 @@ def main():
     ap.add_argument("--store-v-beta", action="store_true",
                     help="prefill-scan: also store the value copies and beta (no later stage reads them)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (tiny, Householder-copy, GVA varlen prefill, wide-head stress)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB (untimed), "
                          "the known-size kernel that calibrates rocprofv3 byte counters")
@@ -414,6 +615,13 @@ def main():
     if not args.no_decode:
         dec = decode_step(G, torch, dev, stream, max(args.steps, 20))
 
+    cfgs = None
+    if not args.no_configs:
+        cfgs = {"tiny_f32": chunk_fwd_line(G, torch, dev, stream, 1, 10),
+                "householder_m2": chunk_fwd_line(G, torch, dev, stream, 2, 10),
+                "gva_varlen_prepare": varlen_line(G, torch, dev, stream, 10),
+                "wide_head_stress": chunk_fwd_line(G, torch, dev, stream, 5, 5)}
+
     if args.copy_mib > 0:
         n = args.copy_mib * 1024 * 1024 // 2
         src = torch.ones(n, dtype=torch.int16, device=dev)
@@ -438,6 +646,8 @@ def main():
         out["stages_sequential"] = stages
     if dec:
         out["decode"] = dec
+    if cfgs:
+        out["configs"] = cfgs
     print(json.dumps(out), flush=True)
 
 

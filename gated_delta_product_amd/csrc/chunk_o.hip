@@ -61,16 +61,22 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
     T *Vs = (T *)v_dyn;
     __shared__ float sG[4][C], sRk[4][C];                    // per-wave scratch
 
-    // block -> (token chunk, value head, value slab), slabs then heads
-    // fastest: the blocks in flight together cover whole rows of q, k and
-    // o (all heads of a few chunks), so HBM sees long contiguous runs
+    // block -> (token chunk, value head, value slab), heads fastest: the
+    // blocks in flight together cover whole rows of q, k and o (all heads of
+    // a few chunks), so HBM sees long contiguous runs.  With two slabs (V =
+    // 256) the slabs of one (chunk, head) are 8 launch positions apart, so
+    // they run on one XCD and the second reads the query and key rows the
+    // first brought into that XCD's L2: items (chunk, head) go in groups of
+    // 8, each group's slab s blocks at 8 s + x.
     const int nslab = VD / VB;
     const int64_t lin = blockIdx.x;
-    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, lin / ((int64_t)HV * nslab));
+    const int64_t grp = lin / (8 * nslab), rem = lin % (8 * nslab);
+    const int64_t item = grp * 8 + rem % 8;  // (token chunk, value head), heads fastest
+    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, 1, C, item / HV);
     if (loc.seq < 0) return;
-    const int hv = (int)((lin / nslab) % HV);
+    const int hv = (int)(item % HV);
     const int hk = hv / (HV / H);
-    const int vb0 = VB * (int)(lin % nslab);
+    const int vb0 = VB * (int)(rem / 8);
     const int64_t t0 = loc.bos + C * loc.c;  // first token (flattened)
     const int nt = (int)((loc.eos - t0) < C ? (loc.eos - t0) : C);
     const int64_t hidx = items_before(cu, Ttok, M, C, loc.seq) + loc.c * M;
@@ -289,7 +295,8 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
 template <typename T, int KD, int VB>
 static hipError_t launch_chunk_o_t(const ChunkParams &p, hipStream_t stream) {
     const gdp_chunk_args &a = p.a;
-    const int64_t nblk = p.max_tok_chunks * a.HV * (a.V / VB);
+    // (token chunk, head) items padded to a multiple of 8, times the slabs
+    const int64_t nblk = (p.max_tok_chunks * a.HV + 7) / 8 * 8 * (a.V / VB);
     if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)nblk);
     const size_t vdyn = (size_t)a.M * 64 * VB * sizeof(T);  // the V slab of all copies (<= 64 KiB)
