@@ -141,6 +141,8 @@ def scan_bytes(w, segments, nseg, mapped_tokens=None, nstates=None):
                 once; one fp32 K x (K + V) map per segment and head written
       scan      the maps read, one fp32 state per segment and head written
       chunk_h   as algorithmic_bytes, with one state per 64-token chunk
+      chunk_ho  chunk_h and chunk_o as one pass: k, kdecay, gcum, w, u,
+                k_rnorm, q and g read once, o written
     Packed requests give mapped_tokens (the tokens of every segment but the
     last of each request) and nstates (the segments) instead of nseg."""
     T, M, H, HV, G, K, V = w["T"] * w["B"], w["M"], w["H"], w["HV"], w["G"], w["K"], w["V"]
@@ -156,7 +158,10 @@ def scan_bytes(w, segments, nseg, mapped_tokens=None, nstates=None):
     mapb = TMm * H * K * 2 + TMm * HV * 8 + TMm * HV * (K + V) * 2 + maps
     scanb = maps + nstates * HV * V * K * 4
     ch = ab["gdp_chunk_h"] - (math.ceil(T * M / 64) - math.ceil(T / 64)) * HV * V * K * 2
-    return {"wy_fused": wy_fused, "map": mapb, "scan": scanb, "chunk_h": ch}
+    # one pass: k, kdecay, gcum, w, u, k_rnorm, q, g in; o out
+    ho = TM * H * K * 2 + TM * HV * 8 + TM * HV * (K + V) * 2 + TM * H * 4 + T * H * K * 2 + T * HV * 4 \
+        + T * HV * V * 2
+    return {"wy_fused": wy_fused, "map": mapb, "scan": scanb, "chunk_h": ch, "chunk_ho": ho}
 
 
 def decode_bytes(c):
@@ -470,6 +475,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--store-v-beta", action="store_true",
                     help="prefill-scan: also store the value copies and beta (no later stage reads them)")
+    ap.add_argument("--store-vnew-h", action="store_true",
+                    help="scan paths: store v_new and h, i.e. run chunk_h and chunk_o as two launches (by default "
+                         "they run as one pass that stores neither)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (tiny, Householder-copy, GVA varlen prefill, wide-head stress)")
@@ -493,11 +501,12 @@ def main():
     scan = args.path == "scan" or fused
     if args.segments is None:
         args.segments = SCAN_SEGMENTS if scan else SEGMENTS
+    ho = "chunk_h,chunk_o" if args.store_vnew_h else "chunk_h+o in one pass"
     if fused:
-        w["path"] = "prefill_scan(recompute_w_u with prepare,seg_map,seg_scan,chunk_h,chunk_o)" + (
-            "" if args.store_v_beta else "; v, beta not stored")
+        w["path"] = "prefill_scan(recompute_w_u with prepare,seg_map,seg_scan,%s)" % ho + (
+            "" if args.store_v_beta else "; v, beta not stored") + ("" if args.store_vnew_h else "; v_new, h not stored")
     elif scan:
-        w["path"] = "prepare+scan(recompute_w_u,seg_map,seg_scan,chunk_h,chunk_o)"
+        w["path"] = "prepare+scan(recompute_w_u,seg_map,seg_scan,%s)" % ho
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = synth.prepare_draws(1, w["T"], w["M"], w["H"], w["G"], w["V"], w["K"], "bf16", synth.seed_of(4) + 100)
@@ -526,13 +535,13 @@ def main():
             if ev:
                 ev[1].record(stream)
             buf.prefill_scan(x, ba, A_log, dt_bias, Gq, args.segments, stage_events=ev[2:] if ev else None,
-                             store_v_beta=args.store_v_beta)
+                             store_v_beta=args.store_v_beta, store_vnew_h=args.store_vnew_h)
             return
         G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
         if ev:
             ev[1].record(stream)
         if scan:
-            buf.forward_scan(args.segments, stage_events=ev[2:] if ev else None)
+            buf.forward_scan(args.segments, stage_events=ev[2:] if ev else None, store_vnew_h=args.store_vnew_h)
         else:
             buf.forward_pipelined(nseg, chunk_h_events=ev[2:] if ev else None)
 
@@ -572,8 +581,12 @@ def main():
             add("gdp_recompute_w_u", span_us(1, 2), ab["gdp_recompute_w_u"])
         add("gdp_seg_map", span_us(2, 3), sb["map"])
         add("gdp_seg_scan", span_us(3, 4), sb["scan"])
-        add("gdp_chunk_h", span_us(4, 5), sb["chunk_h"], note="all %d segments in one launch" % nseg)
-        add("gdp_chunk_o", span_us(5, 6), ab["gdp_chunk_o"])
+        if args.store_vnew_h:
+            add("gdp_chunk_h", span_us(4, 5), sb["chunk_h"], note="all %d segments in one launch" % nseg)
+            add("gdp_chunk_o", span_us(5, 6), ab["gdp_chunk_o"])
+        else:
+            add("gdp_chunk_ho", span_us(4, 6), sb["chunk_ho"],
+                note="chunk_h and chunk_o as one pass over all %d segments (v_new and h not stored)" % nseg)
     else:
         add("gdp_prefill_prepare", span_us(0, 1), ab["gdp_prefill_prepare"])
         # chunk_h: every segment launch, bracketed on its own stream

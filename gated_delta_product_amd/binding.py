@@ -326,8 +326,15 @@ class ChunkBuffers:
     def chunk_o(self, stream=None):
         self._call(lib().gdp_chunk_o, stream)
 
-    def forward(self, stream=None):
-        self._call(lib().gdp_chunk_fwd, stream)
+    def forward(self, stream=None, store_vnew_h=True):
+        """gdp_chunk_fwd.  store_vnew_h=False passes v_new and h as NULL:
+        chunk_h and chunk_o then run as one pass that stores neither (bf16,
+        M >= 2)."""
+        if store_vnew_h:
+            self._call(lib().gdp_chunk_fwd, stream)
+        else:
+            s = stream if stream is not None else _stream(self.device)
+            _check(lib().gdp_chunk_fwd(ctypes.byref(self._args_without("v_new", "h")), s))
         return self.o
 
     def prefill_pipelined(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, chunk_h_events=None):
@@ -357,13 +364,21 @@ class ChunkBuffers:
         return self._pipelined(lambda ws, ev, s: lib().gdp_chunk_fwd_pipelined(
             ctypes.byref(self.args), int(num_segments), ws, ev, s), num_segments, stream, chunk_h_events)
 
+    def _args_without(self, *names):
+        """A copy of the argument struct with the named tensors set to NULL."""
+        args = type(self.args).from_buffer_copy(self.args)
+        for nm in names:
+            setattr(args, nm, None)
+        return args
+
     def prefill_scan(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, stage_events=None,
-                     store_v_beta=True):
+                     store_v_beta=True, store_vnew_h=True):
         """gdp_prefill_fwd_scan: prepare x / ba into this buffer's q, k, v,
         beta, g (allocated with the prepare shapes) inside the WY stage of the
         segment-parallel forward.  Arguments as prefill_prepare and
         forward_scan.  store_v_beta=False passes v and beta as NULL: nothing
-        after the WY stage reads them, and they are left untouched."""
+        after the WY stage reads them, and they are left untouched.
+        store_vnew_h=False as for forward_scan."""
         _need_cuda(x, ba, A_log, dt_bias)
         d = self.dims
         if x.dim() != 3 or x.stride(2) != 1 or ba.dim() != 3 or ba.stride(2) != 1:
@@ -373,15 +388,13 @@ class ChunkBuffers:
         pa = PrepareArgs(x=x.data_ptr(), x_n_stride=x.stride(0), x_t_stride=x.stride(1), ba=ba.data_ptr(),
                          ba_n_stride=ba.stride(0), ba_t_stride=ba.stride(1), A_log=A_log.data_ptr(),
                          dt_bias=dt_bias.data_ptr(), G=int(num_groups))
-        args = self.args
-        if not store_v_beta:
-            args = type(self.args).from_buffer_copy(self.args)
-            args.v, args.beta = None, None
+        args = self._args_without(*((() if store_v_beta else ("v", "beta")) +
+                                    (() if store_vnew_h else ("v_new", "h"))))
         return self._scan(lambda ws, nb, ev, s: lib().gdp_prefill_fwd_scan(
             ctypes.byref(pa), ctypes.byref(args), int(num_segments), ws, nb, ev, s), num_segments, stream,
             stage_events)
 
-    def forward_scan(self, num_segments, stream=None, stage_events=None):
+    def forward_scan(self, num_segments, stream=None, stage_events=None, store_vnew_h=True):
         """gdp_chunk_fwd_scan: the results of forward() for B == 1, one
         sequence or packed requests (cu_seqlens), to rounding past the first
         segment of each sequence, with every long serial chunk_h chain cut
@@ -391,18 +404,23 @@ class ChunkBuffers:
         they held.
         stage_events: optional 5 events with a cuda_event handle (timing
         enabled, recorded at least once), recorded after the WY stage, the
-        segment maps, the scan, chunk_h and chunk_o."""
+        segment maps, the scan, chunk_h and chunk_o.
+        store_vnew_h=False passes v_new and h as NULL: chunk_h and chunk_o
+        then run as one pass that stores neither (M >= 2), and they keep
+        what they held."""
+        args = self.args if store_vnew_h else self._args_without("v_new", "h")
         return self._scan(lambda ws, nb, ev, s: lib().gdp_chunk_fwd_scan(
-            ctypes.byref(self.args), int(num_segments), ws, nb, ev, s), num_segments, stream, stage_events)
+            ctypes.byref(args), int(num_segments), ws, nb, ev, s), num_segments, stream, stage_events)
 
-    def forward_scan_noalloc(self, num_segments, stream=None, stage_events=None):
+    def forward_scan_noalloc(self, num_segments, stream=None, stage_events=None, store_vnew_h=True):
         """gdp_chunk_fwd_scan_noalloc: forward_scan with the workspace taken
         from the library's own device scratch array (GDP_NOALLOC_SCRATCH_BYTES)
         instead of a tensor; nothing is allocated by the call.  Calls that
         overlap on one GPU share that array."""
         ev = _stage_events(stage_events)
         s = stream if stream is not None else _stream(self.device)
-        _check(lib().gdp_chunk_fwd_scan_noalloc(ctypes.byref(self.args), int(num_segments), ev, s))
+        args = self.args if store_vnew_h else self._args_without("v_new", "h")
+        _check(lib().gdp_chunk_fwd_scan_noalloc(ctypes.byref(args), int(num_segments), ev, s))
         return self.o
 
     def scan_workspace_bytes(self, num_segments):

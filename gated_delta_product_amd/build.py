@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libgdp.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["api.cpp", "prepare.hip", "wy.hip", "chunk_h.hip", "chunk_o.hip", "decode.hip", "scan.hip"]
+SOURCES = ["api.cpp", "prepare.hip", "wy.hip", "chunk_h.hip", "chunk_o.hip", "chunk_ho.hip", "decode.hip",
+           "scan.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

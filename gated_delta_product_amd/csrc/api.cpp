@@ -46,7 +46,8 @@ gdp_status hip_status(hipError_t e, const char *what) {
 // Stage masks for validation.
 // stages of a call; ST_WYP is WY with the prepare fused in, which takes its
 // values and beta from the activations, so it needs neither tensor
-enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u, ST_WYP = 8u };
+// ST_HO is chunk_h and chunk_o as one pass, which stores neither v_new nor h
+enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u, ST_WYP = 8u, ST_HO = 16u };
 
 gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParams *out) {
     if (!a) return fail(GDP_ERR_INVALID, "args is NULL");
@@ -90,12 +91,12 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
         const void *p;
         const char *name;
     } needs[] = {
-        {ST_O, a->q, "q"},           {ST_WY | ST_WYP | ST_H | ST_O, a->k, "k"}, {ST_WY, a->v, "v"},
-        {ST_WY, a->beta, "beta"},    {ST_WY | ST_WYP | ST_O, a->k_rnorm, "k_rnorm"},
-        {ST_WY | ST_WYP | ST_H, a->gcum, "gcum"},    {ST_WY | ST_WYP | ST_H, a->kdecay, "kdecay"},
-        {ST_WY | ST_WYP | ST_H, a->w, "w"},   {ST_WY | ST_WYP | ST_H, a->u, "u"},
+        {ST_O | ST_HO, a->q, "q"},   {ST_WY | ST_WYP | ST_H | ST_O | ST_HO, a->k, "k"}, {ST_WY, a->v, "v"},
+        {ST_WY, a->beta, "beta"},    {ST_WY | ST_WYP | ST_O | ST_HO, a->k_rnorm, "k_rnorm"},
+        {ST_WY | ST_WYP | ST_H | ST_HO, a->gcum, "gcum"},    {ST_WY | ST_WYP | ST_H | ST_HO, a->kdecay, "kdecay"},
+        {ST_WY | ST_WYP | ST_H | ST_HO, a->w, "w"},   {ST_WY | ST_WYP | ST_H | ST_HO, a->u, "u"},
         {ST_H | ST_O, a->v_new, "v_new"},
-        {ST_H | ST_O, a->h, "h"},    {ST_O, a->o, "o"},
+        {ST_H | ST_O, a->h, "h"},    {ST_O | ST_HO, a->o, "o"},
     };
     if (!empty) {
         for (const Need &n : needs) {
@@ -269,9 +270,17 @@ gdp_status gdp_chunk_o(const gdp_chunk_args *a, void *stream) {
 
 gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream) {
     gdp::ChunkParams p;
+    hipStream_t s = (hipStream_t)stream;
+    if (a && a->v_new == nullptr && a->h == nullptr) {  // chunk_h and chunk_o as one pass
+        gdp_status st = check_chunk(a, ST_WY | ST_HO, &p);
+        if (st != GDP_OK || p.nseq == 0) return st;  // (nothing to launch for an empty problem)
+        if (a->M < 2 || a->dtype != GDP_BF16)
+            return fail(GDP_ERR_UNSUPPORTED, "gdp_chunk_fwd: v_new and h may be NULL only for bf16 with M >= 2");
+        if ((st = hip_status(gdp::launch_wy(p, s), "gdp_chunk_fwd: recompute_w_u launch")) != GDP_OK) return st;
+        return hip_status(gdp::launch_chunk_ho(p, s), "gdp_chunk_fwd: chunk_h+o launch");
+    }
     gdp_status st = check_chunk(a, ST_WY | ST_H | ST_O, &p);
     if (st != GDP_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
     if ((st = hip_status(gdp::launch_wy(p, s), "gdp_chunk_fwd: recompute_w_u launch")) != GDP_OK) return st;
     if ((st = hip_status(gdp::launch_chunk_h(p, s), "gdp_chunk_fwd: chunk_h launch")) != GDP_OK) return st;
     return hip_status(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd: chunk_o launch");
@@ -495,9 +504,16 @@ int64_t gdp_scan_workspace_bytes_varlen(int64_t T, int64_t num_seqs, int32_t HV,
 static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp::PrepareParams *prep,
                             int32_t num_segments, void *workspace, int64_t workspace_bytes,
                             void *const *stage_events, void *stream, gdp_status (*scratch_base)(void **) = nullptr) {
+    if (!a) return fail(GDP_ERR_INVALID, "%s: args is NULL", name);
+    // v_new and h both NULL: chunk_h and chunk_o run as one pass that stores
+    // neither (launch_chunk_ho)
+    const bool fused = a->v_new == nullptr && a->h == nullptr;
     gdp::ChunkParams p;
-    gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | ST_H | ST_O, &p);
+    gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | (fused ? ST_HO : ST_H | ST_O), &p);
     if (st != GDP_OK) return st;
+    if (fused && a->M < 2 && p.nseq > 0)
+        return fail(GDP_ERR_UNSUPPORTED, "%s: v_new and h may be NULL (one chunk_h and chunk_o pass) only for M >= 2",
+                    name);
     const bool packed = a->cu_seqlens != nullptr;
     if (a->B != 1)
         return fail(GDP_ERR_INVALID, "%s: B must be 1 (got %lld; packed requests go through cu_seqlens)", name,
@@ -548,7 +564,7 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
     ha.h0 = sp.hstart;
     ha.ht = sp.hstart;
     gdp::ChunkParams hp;
-    if ((st = check_chunk(&ha, ST_H, &hp)) != GDP_OK) return st;
+    if ((st = check_chunk(&ha, fused ? ST_HO : ST_H, &hp)) != GDP_OK) return st;
     // only the states chunk_o reads: the one entering each 64-token chunk.
     // Every segment starts on a 64-token boundary of its sequence, so
     // counting chunks per segment keeps the sequence's own c % M.
@@ -568,10 +584,16 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
     if ((st = mark(1)) != GDP_OK) return st;
     if ((st = run(gdp::launch_seg_scan(sp, s), "gdp_chunk_fwd_scan: segment scan launch")) != GDP_OK) return st;
     if ((st = mark(2)) != GDP_OK) return st;
-    if ((st = run(gdp::launch_chunk_h(hp, s), "gdp_chunk_fwd_scan: chunk_h launch")) != GDP_OK) return st;
-    if ((st = mark(3)) != GDP_OK) return st;
-    if ((st = run(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd_scan: chunk_o launch")) != GDP_OK) return st;
-    if ((st = mark(4)) != GDP_OK) return st;
+    if (fused) {  // chunk_h and chunk_o in one pass: events 3 and 4 bracket nothing
+        if ((st = run(gdp::launch_chunk_ho(hp, s), "gdp_chunk_fwd_scan: chunk_h+o launch")) != GDP_OK) return st;
+        if ((st = mark(3)) != GDP_OK) return st;
+        if ((st = mark(4)) != GDP_OK) return st;
+    } else {
+        if ((st = run(gdp::launch_chunk_h(hp, s), "gdp_chunk_fwd_scan: chunk_h launch")) != GDP_OK) return st;
+        if ((st = mark(3)) != GDP_OK) return st;
+        if ((st = run(gdp::launch_chunk_o(p, s), "gdp_chunk_fwd_scan: chunk_o launch")) != GDP_OK) return st;
+        if ((st = mark(4)) != GDP_OK) return st;
+    }
     if (a->ht) {
         if (packed) {
             if ((st = run(gdp::launch_seg_final(sp, s), "gdp_chunk_fwd_scan: final state launch")) != GDP_OK)

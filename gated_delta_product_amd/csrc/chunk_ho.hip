@@ -1,0 +1,594 @@
+// chunk_ho.hip -- the inter-chunk state recurrence and the output of the
+// Gated Delta Product in one pass: the chunk_h stage (state at each chunk
+// boundary, corrected values) and core.ssm.ops.gdp.chunk_o
+// (chunk_gated_delta_product_fwd_o: the boundary state plus causal in-chunk
+// attention summed over the Householder copies), for callers that need only
+// the output.  Neither the corrected values nor the boundary states leave
+// the chip: each is consumed where it is made.
+//
+// Per sequence and value head, serially over the 64-row chunks c of the
+// expanded stream (token chunk i = c / M holds chunks iM .. iM + M - 1), with
+// h the K x V state entering c:
+//   v_new = u - w h                          (the chunk's corrected values)
+//   h    <- exp2(gl) h + K^T diag(kdecay) v_new
+//   o_t   = scale [ exp(G_t) qhat_t h_{iM}
+//                   + sum over rows e = sM + j of chunks iM.., s <= t:
+//                       exp(G_t - G_s) (qhat_t . khat_e) v_new_e ]
+// with G the within-token-chunk cumulative decay (the chunk_o page's
+// g_cumsum over tokens), the same quantities the two separate stages
+// compute.
+//
+// One block of seven waves per (sequence, value head, 64 value columns):
+// * Compute waves 0-3.  Wave p runs the state chain of the 16-column slice
+//   p exactly as the whole-K form of the chunk_h stage does (fp32 state in
+//   registers, the same operands and order, so the states agree bit for bit),
+//   and it also owns output token tile p (tokens 16p .. 16p + 15 of each
+//   token chunk) over all 64 columns of the block:
+//     - scores of its tokens against the chunk's keys (the K tile is in the
+//       LDS ring already), scaled by the norms and decays, masked to s <= t,
+//       as a high and a low bf16 part;
+//     - the slices' v_new of the chunk come through an LDS exchange (bf16,
+//       one buffer per step parity), and O^T += V^T P^T;
+//     - the state entering each token chunk comes through a second exchange
+//       (bf16), and starts O^T = S Q^T exp(G) for the next token chunk.
+//   The query rows of a token tile are loaded into registers during the
+//   last step of the token chunk before, from L2.
+// * Memory waves 4-5 stream w, K, u, kdecay, gcum and the key norms of each
+//   chunk into a three-stage LDS ring, two chunks ahead (buffer loads with
+//   the LDS destination; the range check zero-fills rows past the end).
+// * Prefetch wave 6 pulls the lines of the chunk two ahead, and the query
+//   rows of the next token chunk, into L2.
+// One barrier per chunk orders it all: the ring stage of chunk c is read
+// before it, the exchanges are written before it and read after it.
+// Requires M >= 2, so that the state exchange of one token chunk is read
+// before the next is written.
+#include "gdp_common.h"
+#include "gdp_internal.h"
+
+namespace gdp {
+
+namespace {
+constexpr int C = 64;
+constexpr int NP = 4;  // 16-column slices per block
+}  // namespace
+
+template <int KD>
+struct HoStage {
+    bf16 w[2][C * (KD / 2)];  // w half tiles [K half], swizzled rows
+    bf16 k[2][C * (KD / 2)];  // K half tiles [K half], swizzled rows
+    bf16 u[NP][C * 16];       // u slices, plain rows of 16 elements
+    float kd[C];              // key decay factor per row (0 past the end)
+    float gc[C];              // cumulative log2 decay per row
+    float rk[C];              // 1 / ||k|| per row (0 past the end)
+};
+
+template <int KD, int VD>
+__global__ void __launch_bounds__((NP + 3) * 64)
+gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
+               const bf16 *__restrict__ u, const float *__restrict__ gcum, const float *__restrict__ k_rnorm,
+               const bf16 *__restrict__ q, const float *__restrict__ g, const int32_t *__restrict__ cu,
+               int64_t nseq, int64_t Ttok, int H, int HV, int M, const float *h0, float *ht,
+               bf16 *__restrict__ o, int64_t uv_ss, float scale) {
+    typedef bf16x8 FragT;
+    typedef bf16x4 HalfT;
+    constexpr int ES = 2;
+    constexpr int KH = KD / 2;           // K rows per half tile
+    constexpr int RB = KH * ES;          // bytes per half-tile row
+    constexpr int UPR = RB / 16;         // 16-byte units per half-tile row
+    constexpr int RPI = 64 / UPR;        // half-tile rows per DMA instruction
+    constexpr int NU = C * 16 * ES / 16 / 64;  // DMA instructions per u slice
+    constexpr int NS = 3;                // ring stages (loads two chunks ahead)
+    constexpr int NKT = KH / 16;         // 16-row state tiles per K half
+    constexpr int NKS = KH / 32;         // contraction steps per K half
+    constexpr int S = VD / 16;           // column slices per head
+    constexpr int SG = S / NP;           // blocks per head
+    constexpr int SB = (int)sizeof(HoStage<KD>);
+    // memory wave 0: w halves, kdecay, key norms; wave 1: K halves, u, gcum
+    constexpr int NDMA0 = 2 * UPR + 2, NDMA1 = 2 * UPR + NU * NP + 1;
+    static_assert(NKS >= 1 && (UPR & (UPR - 1)) == 0 && S % NP == 0 && SB % 16 == 0, "tile shape");
+    static_assert(NDMA1 < 64, "in-flight count must fit the vector memory counter");
+
+    __shared__ __attribute__((aligned(16))) HoStage<KD> ring[NS];
+    // v_new of the chunk, bf16, as O^T = V^T P^T operands: [parity][slice][key half s][lane]
+    __shared__ __attribute__((aligned(16))) FragT Vx[2][NP][2][64];
+    // state entering a token chunk, bf16, as O^T = S Q^T operands: [slice][K half][step][lane]
+    __shared__ __attribute__((aligned(16))) FragT Sx[NP][2][NKS][64];
+    __shared__ __attribute__((aligned(16))) char Pf[1024];  // landing area of L2 prefetches
+
+    // ---- block -> (sequence, value head, slice group); the groups of one
+    // head share an XCD
+    const int64_t P = nseq * HV;
+    const int64_t id = blockIdx.x;
+    const int64_t slot = id / 8, xcd = id % 8;
+    const int64_t pair = (slot / SG) * 8 + xcd;
+    const int slg = (int)(slot % SG);
+    if (pair >= P) return;
+    const int64_t seq = pair / HV;
+    const int hv = (int)(pair % HV);
+    const int hk = hv / (HV / H);
+    int64_t bos, eos;
+    seq_bounds(cu, Ttok, seq, bos, eos);
+    const int64_t rows = (eos - bos) * M;
+    const int nch = (int)ceil_div64(rows, C);
+
+    const int lane = lane_id(), wave = wave_id();
+    const int lg = lane >> 4, lc = lane & 15;
+    // the fp32 state of a compute wave in the permuted K order of the chunk_h
+    // stage: element (kw, kt, q) is S[16 sl + lc][kw KH + 32(kt/2) + 8 lg +
+    // 4(kt%2) + q], one 16-byte unit of h0 / ht
+    auto state_off = [&](int sl_, int kw_, int kt) {
+        return ((seq * HV + hv) * (int64_t)VD + 16 * sl_ + lc) * KD + kw_ * KH + 32 * (kt >> 1) + 8 * lg +
+               4 * (kt & 1);
+    };
+    if (nch == 0) {  // empty sequence: the final state is the initial one
+        if (ht != nullptr && wave < NP) {
+            const int sl = NP * slg + wave;
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+                    *(f32x4 *)(ht + state_off(sl, kw, kt)) = h0 ? *(const f32x4 *)(h0 + state_off(sl, kw, kt)) : zero4();
+        }
+        return;
+    }
+    const int ldk = H * KD, ldw = HV * KD;  // global row strides (elements)
+    const int64_t r0 = bos * M;              // first expanded row of the sequence
+    const int64_t bseq = cu ? 0 : seq;       // batch row of the sequence
+    const int64_t TM = Ttok * M;
+    const int64_t h0r = hm_index(bseq, HV, hv, TM, r0);  // kdecay / gcum of row r0
+    const int64_t k0r = hm_index(bseq, H, hk, TM, r0);   // k_rnorm of row r0
+
+    auto clamp_rows = [](int r) { return r < 0 ? 0 : (r < C ? r : C); };
+    auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
+    // byte offset of element column `col` of half-tile row r (swizzled)
+    auto swz = [&](int r, int col) {
+        const int b = col * ES;
+        return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
+    };
+
+    if (wave == NP + 2) {
+        // ======================= prefetch wave =======================
+        // Pulls the w and K lines of chunk c + 2 into L2 (each block of the
+        // head a share of the rows), the per-row factors (block 0 of the
+        // head), and the query rows of the next token chunk, which the
+        // compute waves load when it starts.
+        constexpr int PF = 2;
+        constexpr int RPB = C / SG;  // rows per block per chunk
+        constexpr int RPC = 64 / (KD * ES / 128);  // rows one pull (a 4-byte load per line) covers
+        static_assert(KD * ES >= 128, "row pulls");
+        const uint32_t pf = lds_addr(&Pf[0]);
+        const int rbw = KD * ES;
+        const char *pw = (const char *)(w + ((r0 + RPB * slg) * HV + hv) * KD);
+        const char *pk = (const char *)(k + ((r0 + RPB * slg) * H + hk) * KD);
+        const char *pd = (const char *)(kdecay + h0r);
+        const char *pg = (const char *)(gcum + h0r);
+        const char *pr = (const char *)(k_rnorm + k0r);
+        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, st4 = (int64_t)C * 4;
+        auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb) {
+            const int lpr = rb / 128;  // lines per row
+            const rsrc_t r = make_rsrc(base, span(nr, ld, rb));
+            dma4(r, (uint32_t)((lane / lpr) * ld + (lane % lpr) * 128), pf);  // rows >= nr: out of range
+        };
+        // rows [0, nr) of a tile, nr <= NR, in pulls of RPC rows
+        auto tile_to_l2 = [&](const char *base, int nr, int ld, auto nrc) {
+            constexpr int NR = decltype(nrc)::value;
+            static_for<0, (NR + RPC - 1) / RPC>([&](auto rc) {
+                constexpr int i = decltype(rc)::value;
+                const int nri = clamp_rows(nr - RPC * i);
+                rows_to_l2(base + (int64_t)RPC * i * ld, nri < RPC ? nri : RPC, ld, rbw);
+            });
+        };
+        const int ntok = (int)(eos - bos);
+        auto prefetch = [&](int c) {
+            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c - RPB * slg));
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c));
+            const int64_t oc = c;
+            tile_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, std::integral_constant<int, RPB>{});
+            tile_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, std::integral_constant<int, RPB>{});
+            if (slg == 0) {
+                dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
+                dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
+                dma4(make_rsrc(pr + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
+                const uint32_t mdv = small_div_magic(M);
+                const int cm = (int)small_div((uint32_t)c, mdv);
+                if (c == cm * M) {  // query rows of token chunk c / M + 1
+                    const int ti = cm + 1;
+                    const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
+                    tile_to_l2((const char *)(q + ((bos + (int64_t)C * ti) * H + hk) * KD), nt, ldk * ES,
+                               std::integral_constant<int, C>{});
+                }
+            }
+        };
+        lds_barrier();  // (chunks 0 and 1 are the memory waves' first loads)
+        for (int c = 0; c < nch; ++c) {
+            prefetch(c + PF);
+            wait_vmcnt<24>();  // bound the number of prefetches in flight
+            lds_barrier();
+        }
+        wait_vmcnt<0>();
+        return;
+    }
+
+    if (wave >= NP) {
+        // ======================= memory waves =======================
+        const int mw = wave - NP;
+        const uint32_t ring_base = lds_addr(&ring[0]);
+        typedef HoStage<KD> Stage;
+        constexpr int OFW = (int)__builtin_offsetof(Stage, w);
+        constexpr int OFK = (int)__builtin_offsetof(Stage, k);
+        constexpr int OFU = (int)__builtin_offsetof(Stage, u);
+        constexpr int OFD = (int)__builtin_offsetof(Stage, kd);
+        constexpr int OFG = (int)__builtin_offsetof(Stage, gc);
+        constexpr int OFR = (int)__builtin_offsetof(Stage, rk);
+        constexpr int HALF = C * KH * ES;  // bytes of one half tile
+        // per-lane source offsets inside a chunk, less the DMA's offset in
+        // its 4 KiB M0 window; half hh of tile rows
+        uint32_t ot[2][UPR];
+#pragma unroll
+        for (int i = 0; i < UPR; ++i) {
+            const int r = i * RPI + lane / UPR;
+            const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
+            const int ld = mw == 0 ? ldw : ldk;
+            ot[0][i] = (uint32_t)((r * ld) * ES + unit * 16 - 1024 * (i % 4));
+            ot[1][i] = ot[0][i] + KH * ES;
+        }
+        uint32_t ou[NU];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) ou[i] = (uint32_t)((i * 64 + lane) * 16 - 1024 * (i % 4));
+        const uint32_t o4 = (uint32_t)(lane * 4);
+        const int sl0 = NP * slg;
+        const char *pt = mw == 0 ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
+        const int ldt = mw == 0 ? ldw : ldk;
+        const int64_t stt = (int64_t)C * ldt * ES;
+        const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl0, HV, VD, uv_ss));
+        const int64_t ssb = uv_ss * ES;  // bytes between consecutive slices of u
+        const char *p4 = mw == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
+        const char *pr = (const char *)(k_rnorm + k0r);
+        const int64_t stu = (int64_t)C * 16 * ES, st4 = (int64_t)C * 4;
+        const int tile_off = mw == 0 ? OFW : OFK;
+        const int off4 = mw == 0 ? OFD : OFG;
+        int rem_issue = (int)rows;
+        auto issue = [&](int st) {
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
+            const uint32_t sb = ring_base + st * SB + tile_off;
+            const rsrc_t rt = make_rsrc(pt, span(n, ldt * ES, KD * ES));
+            static_for<0, 2>([&](auto hc) {
+                constexpr int hh = decltype(hc)::value;
+                static_for<0, UPR>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (i % 4 == 0) set_m0(sb + (hh * HALF + 1024 * i));
+                    dma16_m0<1024 * (i % 4)>(rt, ot[hh][i]);
+                });
+            });
+            if (mw == 1) {
+                static_for<0, NP>([&](auto pc) {
+                    constexpr int pp = decltype(pc)::value;
+                    const rsrc_t ru = make_rsrc(pu + pp * ssb, (uint32_t)(n * 16 * ES));
+                    const uint32_t sbu = ring_base + st * SB + OFU + pp * (C * 16 * ES);
+                    static_for<0, NU>([&](auto ic) {
+                        constexpr int i = decltype(ic)::value;
+                        if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
+                        dma16_m0<1024 * (i % 4)>(ru, ou[i]);
+                    });
+                });
+            } else {
+                dma4(make_rsrc(pr, (uint32_t)(n * 4)), o4, ring_base + st * SB + OFR);
+            }
+            dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
+            pt += stt;
+            pu += stu;
+            p4 += st4;
+            pr += st4;
+            rem_issue -= C;
+        };
+        auto loop = [&](auto ndc) {
+            constexpr int ND = decltype(ndc)::value;
+            issue(0);
+            issue(1);
+            wait_vmcnt<ND>();  // chunk 0 landed
+            lds_barrier();     // publishes stage 0
+            for (int c = 0; c < nch; ++c) {
+                // chunk c + 2 into the stage chunk c - 1 left (freed by the last barrier)
+                issue((c + 2) % NS);
+                wait_vmcnt<ND>();  // chunk c + 1 landed
+                lds_barrier();     // end of step c; publishes stage c + 1
+            }
+            wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
+        };
+        if (mw == 0)
+            loop(std::integral_constant<int, NDMA0>{});
+        else
+            loop(std::integral_constant<int, NDMA1>{});
+        return;
+    }
+
+    // ======================= compute waves =======================
+    // One code path for all four waves and all three ring stages (the wave
+    // and the stage are runtime values): the compute code then fits the
+    // instruction cache, which four wave-specialised copies of it did not.
+    const int pp = wave;  // slice of the block and output token tile
+    const int sl = NP * slg + pp;
+    const uint32_t mdiv = small_div_magic(M);  // x / M for the row -> token maps
+    f32x4 hs[2][NKT];
+#pragma unroll
+    for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = h0 ? *(const f32x4 *)(h0 + state_off(sl, kw, kt)) : zero4();
+    FragT hb[2][NKS];
+    auto pack = [&]() {
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    hb[kw][ks][qq] = (bf16)hs[kw][2 * ks][qq];
+                    hb[kw][ks][4 + qq] = (bf16)hs[kw][2 * ks + 1][qq];
+                }
+    };
+    pack();
+    auto publish_state = [&]() {
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) Sx[pp][kw][ks][lane] = hb[kw][ks];
+    };
+
+    // ---- the output token tile: queries (B operands of both output
+    // products), their norms and decays, for the current token chunk (loaded
+    // at its start; the prefetch wave has pulled the rows into L2)
+    const int ntok = (int)(eos - bos);
+    FragT qf[2][NKS];
+    float gn = 0.f;
+    auto load_q = [&](int ti, FragT (&dst)[2][NKS], float &gdst) {
+        const int nt = clamp_rows(ntok - C * ti);
+        const rsrc_t rq = make_rsrc(q + ((bos + (int64_t)C * ti) * H + hk) * KD, span(nt, ldk * ES, KD * ES));
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                dst[kw][ks] = __builtin_bit_cast(
+                    FragT, buf_load16(rq, (uint32_t)(((16 * pp + lc) * ldk + kw * KH + 32 * ks + 8 * lg) * ES)));
+        gdst = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
+    };
+    float fq = 0.f, Gq = 0.f, Gall = 0.f;  // scale/||q_t||, G_t of this lane's token, G of token `lane`
+    auto token_setup = [&](float gl_) {
+        Gall = wave_inclusive_sum(gl_);
+        Gq = __shfl(Gall, 16 * pp + lc, 64);
+        float ss = 0.f;
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float x = (float)qf[kw][ks][i];
+                    ss += x * x;
+                }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        fq = scale / sqrtf(ss + 1e-6f);
+    };
+    // O^T tiles: oa[ct] holds o[token 16 pp + lc][64 slg + 16 ct + 4 lg + r]
+    f32x4 oa[NP];
+    // the token chunk's start: O^T = S Q^T scaled by exp(G_t) (S from the
+    // state exchange)
+    auto inter = [&]() {
+        const float f = fq * __expf(Gq);
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct) {
+            f32x4 a4 = zero4();
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) a4 = mma(Sx[ct][kw][ks][lane], qf[kw][ks], a4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oa[ct][r] = a4[r] * f;
+        }
+    };
+    auto store_o = [&](int ti) {
+        const int nt = clamp_rows(ntok - C * ti);
+        const rsrc_t ro = make_rsrc(o + ((bos + (int64_t)C * ti) * HV + hv) * VD + 64 * slg,
+                                    span(nt, HV * VD * ES, 64 * ES));
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct) {
+            HalfT o4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o4[r] = (bf16)oa[ct][r];
+            buf_store8(ro, (uint32_t)(((16 * pp + lc) * HV * VD + 16 * ct + 4 * lg) * ES), __builtin_bit_cast(uint2, o4));
+        }
+    };
+
+    load_q(0, qf, gn);
+    token_setup(gn);
+    publish_state();
+    lds_barrier();  // stage 0 landed; the initial state exchange is visible
+    inter();
+    int rem = (int)rows;
+
+    auto step = [&](int c, int st_) {
+        const HoStage<KD> &Sg = ring[st_];
+        const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
+        const int ti = (int)small_div((uint32_t)c, mdiv);                  // token chunk
+        const int m = c - ti * M;
+
+        // ---- phase 1: the partial products of the two K halves (w h)
+        f32x4 acc[2][4];
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                acc[kw][rt] = zero4();
+                const int r = 16 * rt + lc;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const FragT a = *(const FragT *)((const char *)Sg.w[kw] + swz(r, 32 * ks + 8 * lg));
+                    acc[kw][rt] = mma(a, hb[kw][ks], acc[kw][rt]);
+                }
+            }
+        const float glast = Sg.gc[n > 0 ? n - 1 : 0];
+        const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hs[kw][kt][r] *= gl;
+
+        // ---- v_new (published to the exchange as bf16) and the phase-2
+        // operands, with the arithmetic of the chunk_h stage's whole-K form,
+        // then phase 2, h = exp2(gl) h + K^T (kd * v_new), one key half s
+        // (rows 32 s .. 32 s + 31) at a time; every accumulator sees the same
+        // products in the same order as there, so the states agree bit for
+        // bit.  K^T is read transposed from the ring (ds_read_b64_tr_b16,
+        // rows in the state's permuted K order).
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            FragT vb[2], vbl[2], v8;
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const int rt = 2 * s + r2;
+                const HalfT uu = lds_col4<bf16>(Sg.u[pp], 16, 16 * rt + 4 * lg, 0);
+                const f32x4 kd4 = *(const f32x4 *)(&Sg.kd[16 * rt + 4 * lg]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float uf = (float)uu[r];
+                    const float ua0 = uf - acc[0][rt][r], ua1 = uf - acc[1][rt][r];
+                    const float uk0 = ua0 * kd4[r], uk1 = ua1 * kd4[r];
+                    v8[4 * r2 + r] = (bf16)(s == 0 ? ua0 - acc[1][rt][r] : ua1 - acc[0][rt][r]);
+                    const float x0 = __builtin_fmaf(-acc[1][rt][r], kd4[r], uk0);
+                    const float x1 = __builtin_fmaf(-acc[0][rt][r], kd4[r], uk1);
+                    vb[0][4 * r2 + r] = (bf16)x0;
+                    vb[1][4 * r2 + r] = (bf16)x1;
+                    vbl[0][4 * r2 + r] = split_lo<bf16>(x0, vb[0][4 * r2 + r]);
+                    vbl[1][4 * r2 + r] = split_lo<bf16>(x1, vb[1][4 * r2 + r]);
+                }
+            }
+            Vx[c & 1][pp][s][lane] = v8;
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) {
+                    const char *kb = (const char *)Sg.k[kw];
+                    const int kbase = 32 * (kt >> 1) + 4 * (kt & 1);
+                    const int j = lane & 15;
+                    const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
+                    const int col = kbase + 8 * (j & 3);
+                    const HalfT x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
+                    const HalfT x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
+                    const FragT ka = join<bf16>(x0, x1);
+                    hs[kw][kt] = mma(ka, vb[kw], hs[kw][kt]);
+                    hs[kw][kt] = mma(ka, vbl[kw], hs[kw][kt]);
+                }
+        }
+        pack();
+
+        // ---- scores of this wave's token tile against the chunk's keys:
+        // P^T[key r][token t] = fq_t rk_r exp(G_t - G_s) (k_r . q_t) for the
+        // key's token s <= t and r < n, else 0; key row r of chunk c is
+        // expanded row 64c + r of the sequence, token (64c + r)/M, copy
+        // (64c + r) % M
+        const int t_me = 16 * pp + lc;  // this lane's token (within the token chunk)
+        FragT pb[2], pbl[2];
+        bool kact[2];  // key half s holds any key a token of this tile sees (uniform)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int first_tok = (int)small_div((uint32_t)(C * m + 32 * s), mdiv);  // within the token chunk
+            kact[s] = first_tok <= 16 * pp + 15 && 32 * s < n;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int st = 2 * s + s2;
+                f32x4 p = zero4();
+                const int ft = (int)small_div((uint32_t)(C * m + 16 * st), mdiv);
+                if (ft <= 16 * pp + 15 && 16 * st < n) {
+#pragma unroll
+                    for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                        for (int ks = 0; ks < NKS; ++ks) {
+                            const FragT a = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
+                            p = mma(a, qf[kw][ks], p);
+                        }
+                }
+                const f32x4 rk4 = *(const f32x4 *)(&Sg.rk[16 * st + 4 * lg]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * st + 4 * lg + r;
+                    const int sk = (int)small_div((uint32_t)(C * m + row), mdiv);  // key token, 0..63
+                    const float Gs = __shfl(Gall, sk, 64);
+                    const bool ok = row < n && sk <= t_me;
+                    const float x = ok ? p[r] * rk4[r] * fq * __expf(Gq - Gs) : 0.f;
+                    pb[s][4 * s2 + r] = (bf16)x;
+                    pbl[s][4 * s2 + r] = split_lo<bf16>(x, pb[s][4 * s2 + r]);
+                }
+            }
+        }
+
+        // ---- at the end of a token chunk, publish the state entering the
+        // next one
+        const bool last_of_tok = m == M - 1 || c + 1 == nch;
+        if (m == M - 1 && c + 1 < nch) {
+            publish_state();
+            load_q(ti + 1, qf, gn);  // this step's scores are done with qf; the barrier hides the latency
+        }
+        lds_barrier();  // end of step c: ring stage c free, exchanges visible
+
+        // ---- O^T += V^T P^T over the block's column slices
+#pragma unroll
+        for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                if (kact[s]) {
+                    const FragT a = Vx[c & 1][ct][s][lane];
+                    oa[ct] = mma(a, pb[s], oa[ct]);
+                    oa[ct] = mma(a, pbl[s], oa[ct]);
+                }
+        if (last_of_tok) {
+            store_o(ti);
+            if (c + 1 < nch) {  // the next token chunk starts with the state just exchanged
+                token_setup(gn);
+                inter();
+            }
+        }
+        rem -= C;
+    };
+
+    for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) step(c, st_);
+    if (ht != nullptr) {
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) *(f32x4 *)(ht + state_off(sl, kw, kt)) = hs[kw][kt];
+    }
+}
+
+template <int KD, int VD>
+static hipError_t launch_ho_t(const ChunkParams &p, hipStream_t stream) {
+    const gdp_chunk_args &a = p.a;
+    const int64_t P = p.nseq * a.HV;
+    const int64_t SG = VD / 16 / NP;
+    const int64_t nblk = ((P + 7) / 8) * 8 * SG;
+    if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gdp_chunk_ho_k<KD, VD>), dim3((unsigned)nblk), dim3((NP + 3) * 64), 0, stream,
+                       (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.k_rnorm,
+                       (const bf16 *)a.q, a.g, a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.h0, a.ht, (bf16 *)a.o,
+                       p.uv_ss, a.scale);
+    return hipGetLastError();
+}
+
+// bf16 with K in {64, 128}, V in {64, 128, 256}, M in [2, 4]
+hipError_t launch_chunk_ho(const ChunkParams &p, hipStream_t stream) {
+    if (p.nseq == 0 || p.a.T == 0) return hipSuccess;
+    const int K = p.a.K, V = p.a.V;
+    if (p.a.dtype != GDP_BF16 || p.a.M < 2) return hipErrorInvalidValue;
+    if (K == 64 && V == 64) return launch_ho_t<64, 64>(p, stream);
+    if (K == 64 && V == 128) return launch_ho_t<64, 128>(p, stream);
+    if (K == 64 && V == 256) return launch_ho_t<64, 256>(p, stream);
+    if (K == 128 && V == 64) return launch_ho_t<128, 64>(p, stream);
+    if (K == 128 && V == 128) return launch_ho_t<128, 128>(p, stream);
+    if (K == 128 && V == 256) return launch_ho_t<128, 256>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdp

@@ -82,5 +82,8 @@ hipError_t launch_wy(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_wy_prepare(const ChunkParams &p, const PrepareParams &pp, hipStream_t stream);
 hipError_t launch_chunk_h(const ChunkParams &p, hipStream_t stream);
 hipError_t launch_chunk_o(const ChunkParams &p, hipStream_t stream);
+// chunk_h and chunk_o as one pass that stores neither v_new nor h (bf16, K
+// in {64, 128}, V in {64, 128, 256}, M in [2, 4]); h0 / ht as for chunk_h
+hipError_t launch_chunk_ho(const ChunkParams &p, hipStream_t stream);
 
 }  // namespace gdp

@@ -184,6 +184,23 @@ def test_empty_problem_launches_nothing():
     assert B.lib().gdp_chunk_fwd(ctypes.byref(a), None) == B.GDP_OK
 
 
+def test_fused_pass_requirements():
+    """v_new and h both NULL select chunk_h and chunk_o as one pass: it needs
+    q, k_rnorm and o, bf16 and M >= 2; one of the two NULL is an error.
+    Every case is refused before any launch."""
+    L = B.lib()
+    fz = dict(v_new=None, h=None, M=2, T=128, h_chunks=4)
+    assert L.gdp_chunk_fwd(ctypes.byref(_args(**dict(fz, M=1))), None) == B.GDP_ERR_UNSUPPORTED
+    assert L.gdp_chunk_fwd(ctypes.byref(_args(**dict(fz, dtype=B.GDP_F32))), None) == B.GDP_ERR_UNSUPPORTED
+    for nm in ("q", "k_rnorm", "o", "w", "u", "kdecay", "gcum"):
+        assert L.gdp_chunk_fwd(ctypes.byref(_args(**dict(fz, **{nm: None}))), None) == B.GDP_ERR_INVALID, nm
+    assert L.gdp_chunk_fwd(ctypes.byref(_args(M=2, T=128, h_chunks=4, v_new=None)), None) == B.GDP_ERR_INVALID
+    assert L.gdp_chunk_fwd(ctypes.byref(_args(M=2, T=128, h_chunks=4, h=None)), None) == B.GDP_ERR_INVALID
+    ws = ctypes.c_void_p(0x100000)
+    a = _args(**dict(fz, M=1, K=128, V=128))
+    assert L.gdp_chunk_fwd_scan(ctypes.byref(a), 2, ws, 1 << 40, None, None) == B.GDP_ERR_UNSUPPORTED
+
+
 def _prep_call(fn, **kw):
     base = dict(x=0x10000, xn=0, xt=5632, ba=0x20000, bn=0, bt=48, A_log=0x30000, dt_bias=0x40000,
                 n=1, T=16, M=2, H=16, G=4, P=128, N=128, dtype=B.GDP_BF16,

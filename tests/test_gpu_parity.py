@@ -940,6 +940,151 @@ def test_prefill_scan_varlen_workload():
                 tag="varlen prefill scan", buf=fz, hstep=M, want_wu=False)
 
 
+def check_o(buf, q, k, v, beta, g, seqs, hv_list, M, tag, h0=None, scale=None):
+    """o (and the final state when h0 is given) of every listed (sequence,
+    value head) against the oracle, to the bf16 tolerance."""
+    H, HV, K = q.shape[2], v.shape[2], q.shape[3]
+    sc = scale if scale is not None else 1.0 / math.sqrt(K)
+    items = [(si, s_, hv) for si, s_ in enumerate(seqs) for hv in hv_list if s_[2] > s_[1]]
+    log("%s: %d (seq, head) pairs" % (tag, len(items)))
+
+    def one(item):
+        si, (b, t0, t1, _), hv = item
+        hk = hv // (HV // H)
+        return oracle_pair(f32(q[b, t0:t1, hk]), f32(k[b, t0 * M:t1 * M, hk]), f32(v[b, t0 * M:t1 * M, hv]),
+                           f32(beta[b, t0 * M:t1 * M, hv]), None if g is None else f32(g[b, t0:t1, hv]), M, sc,
+                           False, h0=None if h0 is None else h0[si, hv].double().numpy())
+
+    refs = run_pairs(one, items)
+    ao, ah = Acc("o", raw_max_abs=True), Acc("ht", raw_max_abs=True)
+    for (si, (b, t0, t1, _), hv), r in zip(items, refs):
+        ao.add(f32(buf.o[b, t0:t1, hv]), r["o"], True)
+        if h0 is not None:
+            ah.add(f32(buf.ht[si, hv]), r["h_final"], False)
+    ao.check(TOL[torch.bfloat16])
+    if h0 is not None:
+        ah.check(TOL[torch.bfloat16])
+    return ao.rel()
+
+
+FUSED_CASES = [
+    # lengths (None: one sequence of T), T, H, HV, K, V, M, segments, seed, gated, long memory, h0
+    (None, 1000, 2, 4, 128, 128, 2, 5, 71, True, False, True),
+    (None, 700, 1, 2, 64, 128, 3, 4, 72, True, True, False),
+    (None, 513, 2, 2, 128, 64, 4, 3, 73, True, False, True),
+    (None, 65, 2, 2, 128, 128, 2, 4, 74, True, True, True),
+    (None, 300, 1, 2, 64, 64, 2, 64, 75, False, False, False),
+    (None, 1, 1, 1, 64, 64, 3, 4, 79, True, False, True),
+    ([1000, 0, 1, 64, 65, 2500, 130, 700], None, 2, 4, 128, 128, 2, 8, 76, True, False, True),
+    ([3000, 17, 1500], None, 1, 2, 64, 128, 3, 6, 77, True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "%s-K%dV%d-M%d-s%d%s%s" % (
+    "n%d" % len(c[0]) if c[0] else "T%d" % c[1], c[4], c[5], c[6], c[7], "-long" if c[10] else "",
+    "" if c[9] else "-ungated"))
+def test_scan_fused_output_matches_oracle(case):
+    """gdp_chunk_fwd_scan with v_new and h passed as NULL: chunk_h and chunk_o
+    as one pass.  o and the final states against the oracle on every
+    (sequence, head); the final states bit-identical to the two-stage scan
+    form (the fused pass runs the same state arithmetic), w, u and the per-row
+    intermediates too, and v_new and h left untouched."""
+    lens, T, H, HV, K, V, M, nseg, seed, gated, longmem, with_h0 = case
+    cu = None
+    if lens is not None:
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        T = int(cu[-1])
+    d = synth.chunk_draws(1, T, H, HV, K, V, M, "bf16", seed)
+    if longmem:
+        d["dt_bias"] = torch.empty(HV).uniform_(-9, -7, generator=torch.Generator().manual_seed(seed))
+    beta, g = gates(d)
+    beta = beta.reshape(1, T * M, HV)
+    g = g if gated else None
+    nseq = 1 if cu is None else len(lens)
+    h0 = synth.initial_state_draws(nseq, HV, V, K, seed + 100) if with_h0 else None
+    seqs = _seqs_equal(1, T, M) if cu is None else _seqs_varlen(cu, M)
+    cu_d = None if cu is None else torch.as_tensor(cu, dtype=torch.int32).to(DEV)
+    mk = lambda: G.ChunkBuffers(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), beta.to(DEV),
+                                None if g is None else g.to(DEV), cu_seqlens=cu_d, cu_seqlens_host=cu,
+                                initial_state=None if h0 is None else h0.to(DEV), output_final_state=h0 is not None)
+    fz, ref = mk(), mk()
+    fz.h.fill_(H_MARK)
+    fz.v_new.fill_(H_MARK)
+    fz.forward_scan(nseg, stage_events=_stage_events(), store_vnew_h=False)
+    ref.forward_scan(nseg)
+    torch.cuda.synchronize()
+    assert bool((fz.h == H_MARK).all()) and bool((fz.v_new == H_MARK).all()), "v_new or h was written"
+    for nm in ("w", "u", "k_rnorm", "gcum", "kdecay") + (("ht",) if h0 is not None else ()):
+        assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
+    rel = check_o(fz, d["q"], d["k"], d["v"], beta, g, seqs, range(HV), M, "fused scan", h0=h0)
+    if longmem:
+        assert rel <= 4.2e-3, rel
+    # the two-stage form's o, for scale: the two differ by rounding only
+    diff = (fz.o.float() - ref.o.float()).norm() / ref.o.float().norm()
+    log("  fused vs two-stage o: rel-L2 %.3e" % float(diff))
+    assert float(diff) <= 5e-3
+
+
+@pytest.mark.parametrize("B_,T,H,HV,K,V,M,seed", [(2, 600, 2, 4, 128, 256, 3, 81), (3, 200, 1, 1, 64, 256, 2, 82),
+                                                  (2, 300, 2, 2, 128, 64, 4, 83)])
+def test_chunk_fwd_fused_output_matches_oracle(B_, T, H, HV, K, V, M, seed):
+    """gdp_chunk_fwd with v_new and h passed as NULL (B > 1 rows, V = 256):
+    o and the final states against the oracle, the final states and w, u
+    bit-identical to the two-stage call."""
+    d = synth.chunk_draws(B_, T, H, HV, K, V, M, "bf16", seed, a_sigma=3.0 if seed == 81 else 1.0,
+                          plant_edges=seed == 81)
+    beta, g = gates(d)
+    beta = beta.reshape(B_, T * M, HV)
+    h0 = synth.initial_state_draws(B_, HV, V, K, seed + 100)
+    mk = lambda: G.ChunkBuffers(d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV), beta.to(DEV), g.to(DEV),
+                                initial_state=h0.to(DEV), output_final_state=True)
+    fz, ref = mk(), mk()
+    fz.forward(store_vnew_h=False)
+    ref.forward()
+    torch.cuda.synchronize()
+    for nm in ("w", "u", "ht"):
+        assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
+    check_o(fz, d["q"], d["k"], d["v"], beta, g, _seqs_equal(B_, T, M), range(HV), M, "fused chunk_fwd", h0=h0)
+
+
+def test_prefill_scan_fused_long_prefill_sampled():
+    """The timed configuration: gdp_prefill_fwd_scan at B=1, T=32768,
+    H=HV=16, K=V=128, M=2, 16 segments, with v, beta, v_new and h all NULL
+    (prepare in WY, chunk_h and chunk_o in one pass): prepare's stored outputs
+    equal gdp_prefill_prepare's, the final state equals the two-stage scan's
+    bit for bit, and o of sampled heads against the oracle run on the
+    oracle's prepare output."""
+    c = synth.CONFIGS[4]
+    M, H, T = c["M"], c["HV"], c["T"]
+    d = synth.prepare_draws(1, T, M, H, H, c["V"], c["K"], "bf16", synth.seed_of(4) + 100)
+    x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
+    pre = G.prefill_prepare(x, ba, A_log, dt_bias, M, H, H, c["V"], c["K"])
+    h0 = synth.initial_state_draws(1, H, c["V"], c["K"], 91).to(DEV)
+    ref = G.ChunkBuffers(*pre, initial_state=h0, output_final_state=True)
+    ref.forward_scan(16)
+    fz = G.ChunkBuffers(*[torch.full_like(t, 7) for t in pre], initial_state=h0, output_final_state=True)
+    fz.prefill_scan(x, ba, A_log, dt_bias, H, 16, store_v_beta=False, store_vnew_h=False)
+    torch.cuda.synchronize()
+    for nm in ("q", "k", "g"):
+        assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
+    for nm in ("w", "u", "ht", "k_rnorm", "gcum", "kdecay"):
+        assert torch.equal(getattr(fz, nm), getattr(ref, nm)), nm
+    xs, bas = f32(d["x"][0]), f32(d["ba"][0])
+    P_, N_ = c["V"], c["K"]
+    for hv in (0, 11):
+        vh = np.ascontiguousarray(xs[:, : M * H * P_].reshape(T, M, H, P_)[:, :, hv].reshape(T * M, P_))
+        kh = np.ascontiguousarray(xs[:, M * H * P_: M * H * P_ + M * H * N_].reshape(T, M, H, N_)[:, :, hv]
+                                  .reshape(T * M, N_))
+        qh = np.ascontiguousarray(xs[:, M * H * P_ + M * H * N_:].reshape(T, H, N_)[:, hv])
+        bh = OP.sigmoid_rn32(bas[:, : M * H].reshape(T, M, H)[:, :, hv].reshape(T * M))
+        gh = OP.decay_rn32(bas[:, M * H + hv], d["A_log"].numpy()[hv], d["dt_bias"].numpy()[hv])
+        r = oracle.recurrence(qh, kh, vh, bh, np.ascontiguousarray(gh), M, scale=1.0 / math.sqrt(N_),
+                              h0=h0[0, hv].double().cpu().numpy())
+        a = Acc("o[%d]" % hv, raw_max_abs=True)
+        a.add(f32(fz.o[0, :, hv]), r["o"])
+        a.check(TOL[torch.bfloat16])
+
+
 @pytest.mark.parametrize("K,V,M,n", [(128, 128, 2, 64), (64, 256, 3, 64), (128, 64, 1, 64), (128, 128, 2, 12)])
 def test_chunk_h_two_pairs_per_block(K, V, M, n):
     """With many chains (packed requests x 16 value heads) chunk_h runs
