@@ -18,26 +18,27 @@
 // g_cumsum over tokens), the same quantities the two separate stages
 // compute.
 //
-// One block of seven waves per (sequence, value head, 64 value columns):
-// * Compute waves 0-3.  Wave p runs the state chain of the 16-column slice
-//   p exactly as the whole-K form of the chunk_h stage does (fp32 state in
-//   registers, the same operands and order, so the states agree bit for bit),
-//   and it also owns output token tile p (tokens 16p .. 16p + 15 of each
-//   token chunk) over all 64 columns of the block:
-//     - scores of its tokens against the chunk's keys (the K tile is in the
-//       LDS ring already), scaled by the norms and decays, masked to s <= t,
-//       as a high and a low bf16 part;
-//     - the slices' v_new of the chunk come through an LDS exchange (bf16,
-//       one buffer per step parity), and O^T += V^T P^T;
-//     - the state entering each token chunk comes through a second exchange
-//       (bf16), and starts O^T = S Q^T exp(G) for the next token chunk.
-//   The query rows of a token tile are loaded into registers during the
-//   last step of the token chunk before, from L2.
-// * Memory waves 4-5 stream w, K, u, kdecay, gcum and the key norms of each
-//   chunk into a three-stage LDS ring, two chunks ahead (buffer loads with
-//   the LDS destination; the range check zero-fills rows past the end).
-// * Prefetch wave 6 pulls the lines of the chunk two ahead, and the query
-//   rows of the next token chunk, into L2.
+// One block of eight waves per (sequence, value head, 64 value columns):
+// * Chain waves 0-3.  Wave p runs the state chain of the 16-column slice p
+//   exactly as the whole-K form of the chunk_h stage does (fp32 state in
+//   registers, the same operands and order, so the states agree bit for
+//   bit), and publishes to LDS the chunk's v_new (bf16, one buffer per step
+//   parity) and, at the end of each token chunk, the state entering the next
+//   one (bf16).  They issue no global memory instruction in the loop.
+// * Output waves 4-7.  Wave 4 + t owns output token tile t (tokens 16t ..
+//   16t + 15 of each token chunk) over all 64 columns of the block:
+//     - before the step's barrier, the scores of its tokens against the
+//       chunk's keys (the K tile is in the LDS ring), scaled by the norms and
+//       decays, masked to s <= t, as a high and a low bf16 part;
+//     - after it, O^T += V^T P^T with every slice's v_new from the exchange,
+//       and at a token chunk's end the store of o and the start of the next
+//       token chunk, O^T = S Q^T exp(G), with the exchanged state.
+//   Their query rows are loaded into registers a token chunk ahead.  Waves 4
+//   and 5 also stream w, K, u, kdecay, gcum and the key norms of each chunk
+//   into a three-stage LDS ring, two chunks ahead (buffer loads with the LDS
+//   destination; the range check zero-fills rows past the end), and wave 6
+//   pulls the lines of the chunk two ahead, and the next token chunk's query
+//   rows, into L2.
 // One barrier per chunk orders it all: the ring stage of chunk c is read
 // before it, the exchanges are written before it and read after it.
 // Requires M >= 2, so that the state exchange of one token chunk is read
@@ -63,7 +64,7 @@ struct HoStage {
 };
 
 template <int KD, int VD>
-__global__ void __launch_bounds__((NP + 3) * 64)
+__global__ void __launch_bounds__(2 * NP * 64)
 gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
                const bf16 *__restrict__ u, const float *__restrict__ gcum, const float *__restrict__ k_rnorm,
                const bf16 *__restrict__ q, const float *__restrict__ g, const int32_t *__restrict__ cu,
@@ -146,72 +147,17 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
     };
 
-    if (wave == NP + 2) {
-        // ======================= prefetch wave =======================
-        // Pulls the w and K lines of chunk c + 2 into L2 (each block of the
-        // head a share of the rows), the per-row factors (block 0 of the
-        // head), and the query rows of the next token chunk, which the
-        // compute waves load when it starts.
-        constexpr int PF = 2;
-        constexpr int RPB = C / SG;  // rows per block per chunk
-        constexpr int RPC = 64 / (KD * ES / 128);  // rows one pull (a 4-byte load per line) covers
-        static_assert(KD * ES >= 128, "row pulls");
-        const uint32_t pf = lds_addr(&Pf[0]);
-        const int rbw = KD * ES;
-        const char *pw = (const char *)(w + ((r0 + RPB * slg) * HV + hv) * KD);
-        const char *pk = (const char *)(k + ((r0 + RPB * slg) * H + hk) * KD);
-        const char *pd = (const char *)(kdecay + h0r);
-        const char *pg = (const char *)(gcum + h0r);
-        const char *pr = (const char *)(k_rnorm + k0r);
-        const int64_t stw = (int64_t)C * ldw * ES, stk = (int64_t)C * ldk * ES, st4 = (int64_t)C * 4;
-        auto rows_to_l2 = [&](const char *base, int nr, int ld, int rb) {
-            const int lpr = rb / 128;  // lines per row
-            const rsrc_t r = make_rsrc(base, span(nr, ld, rb));
-            dma4(r, (uint32_t)((lane / lpr) * ld + (lane % lpr) * 128), pf);  // rows >= nr: out of range
-        };
-        // rows [0, nr) of a tile, nr <= NR, in pulls of RPC rows
-        auto tile_to_l2 = [&](const char *base, int nr, int ld, auto nrc) {
-            constexpr int NR = decltype(nrc)::value;
-            static_for<0, (NR + RPC - 1) / RPC>([&](auto rc) {
-                constexpr int i = decltype(rc)::value;
-                const int nri = clamp_rows(nr - RPC * i);
-                rows_to_l2(base + (int64_t)RPC * i * ld, nri < RPC ? nri : RPC, ld, rbw);
-            });
-        };
-        const int ntok = (int)(eos - bos);
-        auto prefetch = [&](int c) {
-            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c - RPB * slg));
-            const int n = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c));
-            const int64_t oc = c;
-            tile_to_l2(pw + oc * stw, nr < RPB ? nr : RPB, ldw * ES, std::integral_constant<int, RPB>{});
-            tile_to_l2(pk + oc * stk, nr < RPB ? nr : RPB, ldk * ES, std::integral_constant<int, RPB>{});
-            if (slg == 0) {
-                dma4(make_rsrc(pd + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
-                dma4(make_rsrc(pg + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
-                dma4(make_rsrc(pr + oc * st4, (uint32_t)(n * 4)), (uint32_t)(lane * 4), pf);
-                const uint32_t mdv = small_div_magic(M);
-                const int cm = (int)small_div((uint32_t)c, mdv);
-                if (c == cm * M) {  // query rows of token chunk c / M + 1
-                    const int ti = cm + 1;
-                    const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
-                    tile_to_l2((const char *)(q + ((bos + (int64_t)C * ti) * H + hk) * KD), nt, ldk * ES,
-                               std::integral_constant<int, C>{});
-                }
-            }
-        };
-        lds_barrier();  // (chunks 0 and 1 are the memory waves' first loads)
-        for (int c = 0; c < nch; ++c) {
-            prefetch(c + PF);
-            wait_vmcnt<24>();  // bound the number of prefetches in flight
-            lds_barrier();
-        }
-        wait_vmcnt<0>();
-        return;
-    }
+    const int ntok = (int)(eos - bos);
+    // x / M as __umulhi(x, mdiv): exact for every x < 2^31 when M is 2, 3 or 4
+    const uint32_t mdiv = small_div_magic(M);
 
     if (wave >= NP) {
-        // ======================= memory waves =======================
-        const int mw = wave - NP;
+        // ======================= output waves =======================
+        // Output wave tt owns tokens 16 tt .. 16 tt + 15 of each token chunk
+        // over the block's 64 columns.  Waves 4 and 5 also stream the ring
+        // (tt = 0: w halves, kdecay, key norms; tt = 1: K halves, u, gcum),
+        // and wave 6 issues the L2 pulls.
+        const int tt = wave - NP;
         const uint32_t ring_base = lds_addr(&ring[0]);
         typedef HoStage<KD> Stage;
         constexpr int OFW = (int)__builtin_offsetof(Stage, w);
@@ -221,8 +167,10 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         constexpr int OFG = (int)__builtin_offsetof(Stage, gc);
         constexpr int OFR = (int)__builtin_offsetof(Stage, rk);
         constexpr int HALF = C * KH * ES;  // bytes of one half tile
-        // per-lane source offsets inside a chunk, less the DMA's offset in
-        // its 4 KiB M0 window; half hh of tile rows
+
+        // ---- ring duty (tt < 2): per-lane source offsets inside a chunk,
+        // less the DMA's offset in its 4 KiB M0 window; half hh of tile rows
+        const int mw = tt;
         uint32_t ot[2][UPR];
 #pragma unroll
         for (int i = 0; i < UPR; ++i) {
@@ -243,12 +191,12 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl0, HV, VD, uv_ss));
         const int64_t ssb = uv_ss * ES;  // bytes between consecutive slices of u
         const char *p4 = mw == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
-        const char *pr = (const char *)(k_rnorm + k0r);
+        const char *prk = (const char *)(k_rnorm + k0r);
         const int64_t stu = (int64_t)C * 16 * ES, st4 = (int64_t)C * 4;
         const int tile_off = mw == 0 ? OFW : OFK;
         const int off4 = mw == 0 ? OFD : OFG;
         int rem_issue = (int)rows;
-        auto issue = [&](int st) {
+        auto issue = [&](int st) {  // chunk into ring stage st (waves tt = 0, 1)
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
             const uint32_t sb = ring_base + st * SB + tile_off;
             const rsrc_t rt = make_rsrc(pt, span(n, ldt * ES, KD * ES));
@@ -262,9 +210,9 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
             });
             if (mw == 1) {
                 static_for<0, NP>([&](auto pc) {
-                    constexpr int pp = decltype(pc)::value;
-                    const rsrc_t ru = make_rsrc(pu + pp * ssb, (uint32_t)(n * 16 * ES));
-                    const uint32_t sbu = ring_base + st * SB + OFU + pp * (C * 16 * ES);
+                    constexpr int pq = decltype(pc)::value;
+                    const rsrc_t ru = make_rsrc(pu + pq * ssb, (uint32_t)(n * 16 * ES));
+                    const uint32_t sbu = ring_base + st * SB + OFU + pq * (C * 16 * ES);
                     static_for<0, NU>([&](auto ic) {
                         constexpr int i = decltype(ic)::value;
                         if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
@@ -272,43 +220,265 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     });
                 });
             } else {
-                dma4(make_rsrc(pr, (uint32_t)(n * 4)), o4, ring_base + st * SB + OFR);
+                dma4(make_rsrc(prk, (uint32_t)(n * 4)), o4, ring_base + st * SB + OFR);
             }
             dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
             pt += stt;
             pu += stu;
             p4 += st4;
-            pr += st4;
+            prk += st4;
             rem_issue -= C;
         };
-        auto loop = [&](auto ndc) {
-            constexpr int ND = decltype(ndc)::value;
+        // chunk c + 1 landed: everything but the last issue's DMAs (other
+        // vector memory operations in between only make the wait stricter)
+        auto wait_ring = [&]() {
+            if (tt == 0)
+                wait_vmcnt<NDMA0>();
+            else
+                wait_vmcnt<NDMA1>();
+        };
+
+        // ---- L2 pull duty (tt = 2): the w and K lines of chunk c + 2 (each
+        // block of the head a share of the rows), the per-row factors (block
+        // 0 of the head) and the query rows of the next token chunk
+        constexpr int PF = 2;
+        constexpr int RPB = C / SG;                 // rows per block per chunk
+        constexpr int RPC = 64 / (KD * ES / 128);  // rows one pull (a 4-byte load per line) covers
+        static_assert(KD * ES >= 128, "row pulls");
+        const uint32_t pf = lds_addr(&Pf[0]);
+        const int rbw = KD * ES;
+        auto rows_to_l2 = [&](const char *base, int nr, int ld) {
+            const int lpr = rbw / 128;  // lines per row
+            const rsrc_t r = make_rsrc(base, span(nr, ld, rbw));
+            dma4(r, (uint32_t)((lane / lpr) * ld + (lane % lpr) * 128), pf);  // rows >= nr: out of range
+        };
+        auto tile_to_l2 = [&](const char *base, int nr, int ld, auto nrc) {  // rows [0, nr), nr <= NR
+            constexpr int NR = decltype(nrc)::value;
+            static_for<0, (NR + RPC - 1) / RPC>([&](auto rc) {
+                constexpr int i = decltype(rc)::value;
+                const int nri = clamp_rows(nr - RPC * i);
+                rows_to_l2(base + (int64_t)RPC * i * ld, nri < RPC ? nri : RPC, ld);
+            });
+        };
+        auto prefetch = [&](int c) {
+            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c - RPB * slg));
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c));
+            const int64_t oc = c;
+            tile_to_l2((const char *)(w + ((r0 + RPB * slg) * HV + hv) * KD) + oc * C * ldw * ES,
+                       nr < RPB ? nr : RPB, ldw * ES, std::integral_constant<int, RPB>{});
+            tile_to_l2((const char *)(k + ((r0 + RPB * slg) * H + hk) * KD) + oc * C * ldk * ES,
+                       nr < RPB ? nr : RPB, ldk * ES, std::integral_constant<int, RPB>{});
+            if (slg == 0) {
+                dma4(make_rsrc((const char *)(kdecay + h0r) + oc * st4, (uint32_t)(n * 4)), o4, pf);
+                dma4(make_rsrc((const char *)(gcum + h0r) + oc * st4, (uint32_t)(n * 4)), o4, pf);
+                dma4(make_rsrc((const char *)(k_rnorm + k0r) + oc * st4, (uint32_t)(n * 4)), o4, pf);
+                const int cm = (int)__umulhi((uint32_t)c, mdiv);
+                if (c == cm * M) {  // query rows of token chunk c / M + 1
+                    const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * (cm + 1)));
+                    tile_to_l2((const char *)(q + ((bos + (int64_t)C * (cm + 1)) * H + hk) * KD), nt, ldk * ES,
+                               std::integral_constant<int, C>{});
+                }
+            }
+        };
+
+        // ---- the output tile: queries (B operands of both output
+        // products), their norms and decays for the current token chunk
+        FragT qf[2][NKS], qn[2][NKS];  // this token chunk's queries, and the next one's in flight
+        float gn = 0.f, gnn = 0.f;
+        auto load_q = [&](int ti, FragT (&qf)[2][NKS], float &gn) {
+            const int nt = clamp_rows(ntok - C * ti);
+            const rsrc_t rq = make_rsrc(q + ((bos + (int64_t)C * ti) * H + hk) * KD, span(nt, ldk * ES, KD * ES));
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    qf[kw][ks] = __builtin_bit_cast(
+                        FragT, buf_load16(rq, (uint32_t)(((16 * tt + lc) * ldk + kw * KH + 32 * ks + 8 * lg) * ES)));
+            gn = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
+        };
+        float fq = 0.f, Gq = 0.f, Gall = 0.f;  // scale/||q_t||, G_t of this lane's token, G of token `lane`
+        auto token_setup = [&]() {
+            Gall = wave_inclusive_sum(gn);
+            Gq = __shfl(Gall, 16 * tt + lc, 64);
+            float ss = 0.f;
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float x = (float)qf[kw][ks][i];
+                        ss += x * x;
+                    }
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            fq = scale / sqrtf(ss + 1e-6f);
+        };
+        // O^T tiles: oa[ct] holds o[token 16 tt + lc][64 slg + 16 ct + 4 lg + r]
+        f32x4 oa[NP];
+        auto inter = [&]() {  // O^T = S Q^T exp(G_t), S from the state exchange
+            const float f = fq * __expf(Gq);
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct) {
+                f32x4 a4 = zero4();
+#pragma unroll
+                for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) a4 = mma(Sx[ct][kw][ks][lane], qf[kw][ks], a4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oa[ct][r] = a4[r] * f;
+            }
+        };
+        auto store_o = [&](int ti) {
+            const int nt = clamp_rows(ntok - C * ti);
+            const rsrc_t ro = make_rsrc(o + ((bos + (int64_t)C * ti) * HV + hv) * VD + 64 * slg,
+                                        span(nt, HV * VD * ES, 64 * ES));
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct) {
+                HalfT o4v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o4v[r] = (bf16)oa[ct][r];
+                buf_store8(ro, (uint32_t)(((16 * tt + lc) * HV * VD + 16 * ct + 4 * lg) * ES),
+                           __builtin_bit_cast(uint2, o4v));
+            }
+        };
+
+        load_q(0, qf, gn);
+        token_setup();
+        if (tt < 2) {
             issue(0);
             issue(1);
-            wait_vmcnt<ND>();  // chunk 0 landed
-            lds_barrier();     // publishes stage 0
-            for (int c = 0; c < nch; ++c) {
-                // chunk c + 2 into the stage chunk c - 1 left (freed by the last barrier)
-                issue((c + 2) % NS);
-                wait_vmcnt<ND>();  // chunk c + 1 landed
-                lds_barrier();     // end of step c; publishes stage c + 1
-            }
-            wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
+            if (tt == 0)
+                wait_vmcnt<NDMA0>();  // chunk 0 landed
+            else
+                wait_vmcnt<NDMA1>();
+        }
+        lds_barrier();  // stage 0 landed; the initial state exchange is visible
+        inter();
+        int rem = (int)rows;
+        const int t_me = 16 * tt + lc;  // this lane's token (within the token chunk)
+        // the previous chunk's scores (P V for a chunk runs in the next step,
+        // once its v_new is in the exchange)
+        FragT pb[2], pbl[2];
+        bool kact[2] = {false, false};
+        auto pv = [&](int cprev) {  // O^T += V^T P^T over the block's column slices
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (kact[s]) {
+                        const FragT a = Vx[cprev & 1][ct][s][lane];
+                        oa[ct] = mma(a, pb[s], oa[ct]);
+                        oa[ct] = mma(a, pbl[s], oa[ct]);
+                    }
         };
-        if (mw == 0)
-            loop(std::integral_constant<int, NDMA0>{});
-        else
-            loop(std::integral_constant<int, NDMA1>{});
+        for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) {
+            const int ti = (int)__umulhi((uint32_t)c, mdiv);  // token chunk
+            const int m = c - ti * M;
+            if (m == 0 && c > 0) {  // token chunk ti starts: its queries arrived a token chunk ago
+#pragma unroll
+                for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) qf[kw][ks] = qn[kw][ks];
+                gn = gnn;
+                token_setup();
+            }
+            // the next token chunk's queries, a token chunk ahead and before
+            // this step's ring loads (so the ring waits never wait on them)
+            if (m == 0 && C * (ti + 1) < ntok) load_q(ti + 1, qn, gnn);
+            // chunk c + 2 into the stage chunk c - 1 left (freed by the last barrier)
+            if (tt < 2) issue(st_ == 0 ? 2 : st_ - 1);
+            if (tt == 2) prefetch(c + PF);
+            const HoStage<KD> &Sg = ring[st_];
+            const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
+            // ---- the chunk's key rows (A operands of the scores) and norms,
+            // read before the barrier that frees the ring stage
+            FragT kr[4][2][NKS];
+            f32x4 rk4[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+#pragma unroll
+                for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        kr[st][kw][ks] = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
+                rk4[st] = *(const f32x4 *)(&Sg.rk[16 * st + 4 * lg]);
+            }
+            // ---- the score factors of this step, which need no data of the
+            // chunk: dec = fq_t exp(G_t - G_s) for key row r of the chunk
+            // (expanded row 64 m + r of the token chunk: token s = (64 m +
+            // r) / M, copy (64 m + r) % M) when s <= t and r < n, else 0.
+            // Branch-free (masked entries take exp(0), so they stay finite),
+            // and before the barrier, where the ring waves wait for their
+            // loads anyway.
+            float dec[4][4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * st + 4 * lg + r;
+                    const int sk = (int)__umulhi((uint32_t)(C * m + row), mdiv);  // key token, 0..63 (M >= 2)
+                    const float Gs = __shfl(Gall, sk, 64);
+                    const bool ok = row < n && sk <= t_me;
+                    const float e = __expf(ok ? Gq - Gs : 0.f);
+                    dec[st][r] = ok ? fq * e : 0.f;
+                }
+            if (tt < 2) wait_ring();          // chunk c + 1 landed
+            if (tt == 2) wait_vmcnt<24>();    // bound the number of pulls in flight
+            lds_barrier();  // ring stage c read; chunk c - 1's v_new is in the exchange
+
+            if (c > 0) {
+                pv(c - 1);
+                if (m == 0) {  // chunk c - 1 ended token chunk ti - 1; token chunk ti starts
+                    store_o(ti - 1);
+                    inter();  // the state entering token chunk ti, exchanged in step c - 1
+                }
+            }
+
+            // ---- scores of the tile's tokens against the chunk's keys:
+            // P^T[key r][token t] = rk_r dec[r][t] (k_r . q_t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int first_tok = (int)__umulhi((uint32_t)(C * m + 32 * s), mdiv);
+                kact[s] = first_tok <= 16 * tt + 15 && 32 * s < n;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int st = 2 * s + s2;
+                    f32x4 p = zero4();
+                    const int ft = (int)__umulhi((uint32_t)(C * m + 16 * st), mdiv);
+                    if (ft <= 16 * tt + 15 && 16 * st < n) {
+#pragma unroll
+                        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                            for (int ks = 0; ks < NKS; ++ks) p = mma(kr[st][kw][ks], qf[kw][ks], p);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = p[r] * rk4[st][r] * dec[st][r];
+                        pb[s][4 * s2 + r] = (bf16)x;
+                        pbl[s][4 * s2 + r] = split_lo<bf16>(x, pb[s][4 * s2 + r]);
+                    }
+                }
+            }
+            rem -= C;
+        }
+        lds_barrier();  // the last chunk's v_new is in the exchange
+        pv(nch - 1);
+        store_o((int)__umulhi((uint32_t)(nch - 1), mdiv));
+        wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
         return;
     }
 
-    // ======================= compute waves =======================
+    // ======================= chain waves =======================
+    // Wave pp runs the state chain of the block's 16-column slice pp, with
+    // the operands and order of the chunk_h stage's whole-K form, and
+    // publishes the chunk's v_new (and at token-chunk ends the state) to
+    // the exchanges; it issues no global memory instruction in the loop.
     // One code path for all four waves and all three ring stages (the wave
-    // and the stage are runtime values): the compute code then fits the
-    // instruction cache, which four wave-specialised copies of it did not.
-    const int pp = wave;  // slice of the block and output token tile
+    // and the stage are runtime values), so the code fits the instruction
+    // cache.
+    const int pp = wave;
     const int sl = NP * slg + pp;
-    const uint32_t mdiv = small_div_magic(M);  // x / M for the row -> token maps
     f32x4 hs[2][NKT];
 #pragma unroll
     for (int kw = 0; kw < 2; ++kw)
@@ -326,90 +496,20 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     hb[kw][ks][4 + qq] = (bf16)hs[kw][2 * ks + 1][qq];
                 }
     };
-    pack();
     auto publish_state = [&]() {
 #pragma unroll
         for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) Sx[pp][kw][ks][lane] = hb[kw][ks];
     };
-
-    // ---- the output token tile: queries (B operands of both output
-    // products), their norms and decays, for the current token chunk (loaded
-    // at its start; the prefetch wave has pulled the rows into L2)
-    const int ntok = (int)(eos - bos);
-    FragT qf[2][NKS];
-    float gn = 0.f;
-    auto load_q = [&](int ti, FragT (&dst)[2][NKS], float &gdst) {
-        const int nt = clamp_rows(ntok - C * ti);
-        const rsrc_t rq = make_rsrc(q + ((bos + (int64_t)C * ti) * H + hk) * KD, span(nt, ldk * ES, KD * ES));
-#pragma unroll
-        for (int kw = 0; kw < 2; ++kw)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                dst[kw][ks] = __builtin_bit_cast(
-                    FragT, buf_load16(rq, (uint32_t)(((16 * pp + lc) * ldk + kw * KH + 32 * ks + 8 * lg) * ES)));
-        gdst = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
-    };
-    float fq = 0.f, Gq = 0.f, Gall = 0.f;  // scale/||q_t||, G_t of this lane's token, G of token `lane`
-    auto token_setup = [&](float gl_) {
-        Gall = wave_inclusive_sum(gl_);
-        Gq = __shfl(Gall, 16 * pp + lc, 64);
-        float ss = 0.f;
-#pragma unroll
-        for (int kw = 0; kw < 2; ++kw)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float x = (float)qf[kw][ks][i];
-                    ss += x * x;
-                }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        fq = scale / sqrtf(ss + 1e-6f);
-    };
-    // O^T tiles: oa[ct] holds o[token 16 pp + lc][64 slg + 16 ct + 4 lg + r]
-    f32x4 oa[NP];
-    // the token chunk's start: O^T = S Q^T scaled by exp(G_t) (S from the
-    // state exchange)
-    auto inter = [&]() {
-        const float f = fq * __expf(Gq);
-#pragma unroll
-        for (int ct = 0; ct < NP; ++ct) {
-            f32x4 a4 = zero4();
-#pragma unroll
-            for (int kw = 0; kw < 2; ++kw)
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) a4 = mma(Sx[ct][kw][ks][lane], qf[kw][ks], a4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) oa[ct][r] = a4[r] * f;
-        }
-    };
-    auto store_o = [&](int ti) {
-        const int nt = clamp_rows(ntok - C * ti);
-        const rsrc_t ro = make_rsrc(o + ((bos + (int64_t)C * ti) * HV + hv) * VD + 64 * slg,
-                                    span(nt, HV * VD * ES, 64 * ES));
-#pragma unroll
-        for (int ct = 0; ct < NP; ++ct) {
-            HalfT o4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o4[r] = (bf16)oa[ct][r];
-            buf_store8(ro, (uint32_t)(((16 * pp + lc) * HV * VD + 16 * ct + 4 * lg) * ES), __builtin_bit_cast(uint2, o4));
-        }
-    };
-
-    load_q(0, qf, gn);
-    token_setup(gn);
+    pack();
     publish_state();
     lds_barrier();  // stage 0 landed; the initial state exchange is visible
-    inter();
     int rem = (int)rows;
-
-    auto step = [&](int c, int st_) {
+    for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) {
         const HoStage<KD> &Sg = ring[st_];
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
-        const int ti = (int)small_div((uint32_t)c, mdiv);                  // token chunk
+        const int ti = (int)__umulhi((uint32_t)c, mdiv);
         const int m = c - ti * M;
 
         // ---- phase 1: the partial products of the two K halves (w h)
@@ -426,7 +526,35 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     acc[kw][rt] = mma(a, hb[kw][ks], acc[kw][rt]);
                 }
             }
+        // every other read of the ring stage, before the barrier that frees
+        // it: u, the key decays, the chunk's decay and K^T (read transposed,
+        // ds_read_b64_tr_b16, rows in the state's permuted K order)
+        HalfT uu[4];
+        f32x4 kd4[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            uu[rt] = lds_col4<bf16>(Sg.u[pp], 16, 16 * rt + 4 * lg, 0);
+            kd4[rt] = *(const f32x4 *)(&Sg.kd[16 * rt + 4 * lg]);
+        }
         const float glast = Sg.gc[n > 0 ? n - 1 : 0];
+        FragT ka[2][NKT][2];
+#pragma unroll
+        for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const char *kb = (const char *)Sg.k[kw];
+                    const int kbase = 32 * (kt >> 1) + 4 * (kt & 1);
+                    const int j = lane & 15;
+                    const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
+                    const int col = kbase + 8 * (j & 3);
+                    const HalfT x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
+                    const HalfT x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
+                    ka[kw][kt][s] = join<bf16>(x0, x1);
+                }
         const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
 #pragma unroll
         for (int kw = 0; kw < 2; ++kw)
@@ -434,30 +562,28 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) hs[kw][kt][r] *= gl;
+        lds_barrier();  // ring stage c read; the exchanges of chunk c - 1 were read
 
         // ---- v_new (published to the exchange as bf16) and the phase-2
         // operands, with the arithmetic of the chunk_h stage's whole-K form,
         // then phase 2, h = exp2(gl) h + K^T (kd * v_new), one key half s
         // (rows 32 s .. 32 s + 31) at a time; every accumulator sees the same
         // products in the same order as there, so the states agree bit for
-        // bit.  K^T is read transposed from the ring (ds_read_b64_tr_b16,
-        // rows in the state's permuted K order).
+        // bit
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             FragT vb[2], vbl[2], v8;
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
                 const int rt = 2 * s + r2;
-                const HalfT uu = lds_col4<bf16>(Sg.u[pp], 16, 16 * rt + 4 * lg, 0);
-                const f32x4 kd4 = *(const f32x4 *)(&Sg.kd[16 * rt + 4 * lg]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float uf = (float)uu[r];
+                    const float uf = (float)uu[rt][r];
                     const float ua0 = uf - acc[0][rt][r], ua1 = uf - acc[1][rt][r];
-                    const float uk0 = ua0 * kd4[r], uk1 = ua1 * kd4[r];
+                    const float uk0 = ua0 * kd4[rt][r], uk1 = ua1 * kd4[rt][r];
                     v8[4 * r2 + r] = (bf16)(s == 0 ? ua0 - acc[1][rt][r] : ua1 - acc[0][rt][r]);
-                    const float x0 = __builtin_fmaf(-acc[1][rt][r], kd4[r], uk0);
-                    const float x1 = __builtin_fmaf(-acc[0][rt][r], kd4[r], uk1);
+                    const float x0 = __builtin_fmaf(-acc[1][rt][r], kd4[rt][r], uk0);
+                    const float x1 = __builtin_fmaf(-acc[0][rt][r], kd4[rt][r], uk1);
                     vb[0][4 * r2 + r] = (bf16)x0;
                     vb[1][4 * r2 + r] = (bf16)x1;
                     vbl[0][4 * r2 + r] = split_lo<bf16>(x0, vb[0][4 * r2 + r]);
@@ -469,92 +595,15 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
             for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt) {
-                    const char *kb = (const char *)Sg.k[kw];
-                    const int kbase = 32 * (kt >> 1) + 4 * (kt & 1);
-                    const int j = lane & 15;
-                    const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
-                    const int col = kbase + 8 * (j & 3);
-                    const HalfT x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
-                    const HalfT x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
-                    const FragT ka = join<bf16>(x0, x1);
-                    hs[kw][kt] = mma(ka, vb[kw], hs[kw][kt]);
-                    hs[kw][kt] = mma(ka, vbl[kw], hs[kw][kt]);
+                    hs[kw][kt] = mma(ka[kw][kt][s], vb[kw], hs[kw][kt]);
+                    hs[kw][kt] = mma(ka[kw][kt][s], vbl[kw], hs[kw][kt]);
                 }
         }
         pack();
-
-        // ---- scores of this wave's token tile against the chunk's keys:
-        // P^T[key r][token t] = fq_t rk_r exp(G_t - G_s) (k_r . q_t) for the
-        // key's token s <= t and r < n, else 0; key row r of chunk c is
-        // expanded row 64c + r of the sequence, token (64c + r)/M, copy
-        // (64c + r) % M
-        const int t_me = 16 * pp + lc;  // this lane's token (within the token chunk)
-        FragT pb[2], pbl[2];
-        bool kact[2];  // key half s holds any key a token of this tile sees (uniform)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int first_tok = (int)small_div((uint32_t)(C * m + 32 * s), mdiv);  // within the token chunk
-            kact[s] = first_tok <= 16 * pp + 15 && 32 * s < n;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int st = 2 * s + s2;
-                f32x4 p = zero4();
-                const int ft = (int)small_div((uint32_t)(C * m + 16 * st), mdiv);
-                if (ft <= 16 * pp + 15 && 16 * st < n) {
-#pragma unroll
-                    for (int kw = 0; kw < 2; ++kw)
-#pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) {
-                            const FragT a = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
-                            p = mma(a, qf[kw][ks], p);
-                        }
-                }
-                const f32x4 rk4 = *(const f32x4 *)(&Sg.rk[16 * st + 4 * lg]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * st + 4 * lg + r;
-                    const int sk = (int)small_div((uint32_t)(C * m + row), mdiv);  // key token, 0..63
-                    const float Gs = __shfl(Gall, sk, 64);
-                    const bool ok = row < n && sk <= t_me;
-                    const float x = ok ? p[r] * rk4[r] * fq * __expf(Gq - Gs) : 0.f;
-                    pb[s][4 * s2 + r] = (bf16)x;
-                    pbl[s][4 * s2 + r] = split_lo<bf16>(x, pb[s][4 * s2 + r]);
-                }
-            }
-        }
-
-        // ---- at the end of a token chunk, publish the state entering the
-        // next one
-        const bool last_of_tok = m == M - 1 || c + 1 == nch;
-        if (m == M - 1 && c + 1 < nch) {
-            publish_state();
-            load_q(ti + 1, qf, gn);  // this step's scores are done with qf; the barrier hides the latency
-        }
-        lds_barrier();  // end of step c: ring stage c free, exchanges visible
-
-        // ---- O^T += V^T P^T over the block's column slices
-#pragma unroll
-        for (int ct = 0; ct < NP; ++ct)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                if (kact[s]) {
-                    const FragT a = Vx[c & 1][ct][s][lane];
-                    oa[ct] = mma(a, pb[s], oa[ct]);
-                    oa[ct] = mma(a, pbl[s], oa[ct]);
-                }
-        if (last_of_tok) {
-            store_o(ti);
-            if (c + 1 < nch) {  // the next token chunk starts with the state just exchanged
-                token_setup(gn);
-                inter();
-            }
-        }
+        if (m == M - 1 && c + 1 < nch) publish_state();  // the state entering the next token chunk
         rem -= C;
-    };
-
-    for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) step(c, st_);
+    }
+    lds_barrier();  // the last chunk's v_new is in the exchange (matches the output waves)
     if (ht != nullptr) {
 #pragma unroll
         for (int kw = 0; kw < 2; ++kw)
@@ -570,7 +619,7 @@ static hipError_t launch_ho_t(const ChunkParams &p, hipStream_t stream) {
     const int64_t SG = VD / 16 / NP;
     const int64_t nblk = ((P + 7) / 8) * 8 * SG;
     if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gdp_chunk_ho_k<KD, VD>), dim3((unsigned)nblk), dim3((NP + 3) * 64), 0, stream,
+    hipLaunchKernelGGL((gdp_chunk_ho_k<KD, VD>), dim3((unsigned)nblk), dim3(2 * NP * 64), 0, stream,
                        (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.k_rnorm,
                        (const bf16 *)a.q, a.g, a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.h0, a.ht, (bf16 *)a.o,
                        p.uv_ss, a.scale);
