@@ -84,10 +84,11 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     constexpr int S = VD / 16;           // column slices per head
     constexpr int SG = S / NP;           // blocks per head
     constexpr int SB = (int)sizeof(HoStage<KD>);
-    // memory wave 0: w halves, kdecay, key norms; wave 1: K halves, u, gcum
-    constexpr int NDMA0 = 2 * UPR + 2, NDMA1 = 2 * UPR + NU * NP + 1;
+    // ring loads per chunk of chain wave p: a half tile of w or K, its u
+    // slice and (p < 3) one per-row vector
+    constexpr int NDMA = UPR + NU + 1;
     static_assert(NKS >= 1 && (UPR & (UPR - 1)) == 0 && S % NP == 0 && SB % 16 == 0, "tile shape");
-    static_assert(NDMA1 < 64, "in-flight count must fit the vector memory counter");
+    static_assert(NDMA < 64, "in-flight count must fit the vector memory counter");
 
     __shared__ __attribute__((aligned(16))) HoStage<KD> ring[NS];
     // v_new of the chunk, bf16, as O^T = V^T P^T operands: [parity][slice][key half s][lane]
@@ -150,93 +151,17 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     const int ntok = (int)(eos - bos);
     // x / M as __umulhi(x, mdiv): exact for every x < 2^31 when M is 2, 3 or 4
     const uint32_t mdiv = small_div_magic(M);
+    const uint32_t ring_base = lds_addr(&ring[0]);
+    const int64_t st4 = (int64_t)C * 4;  // bytes of one chunk of a per-row vector
 
     if (wave >= NP) {
         // ======================= output waves =======================
         // Output wave tt owns tokens 16 tt .. 16 tt + 15 of each token chunk
-        // over the block's 64 columns.  Waves 4 and 5 also stream the ring
-        // (tt = 0: w halves, kdecay, key norms; tt = 1: K halves, u, gcum),
-        // and wave 6 issues the L2 pulls.
+        // over the block's 64 columns; wave 6 also issues the L2 pulls.
+        // Their only other memory instructions are their own query loads and
+        // output stores, so the compiler's waits for those are exact.
         const int tt = wave - NP;
-        const uint32_t ring_base = lds_addr(&ring[0]);
-        typedef HoStage<KD> Stage;
-        constexpr int OFW = (int)__builtin_offsetof(Stage, w);
-        constexpr int OFK = (int)__builtin_offsetof(Stage, k);
-        constexpr int OFU = (int)__builtin_offsetof(Stage, u);
-        constexpr int OFD = (int)__builtin_offsetof(Stage, kd);
-        constexpr int OFG = (int)__builtin_offsetof(Stage, gc);
-        constexpr int OFR = (int)__builtin_offsetof(Stage, rk);
-        constexpr int HALF = C * KH * ES;  // bytes of one half tile
-
-        // ---- ring duty (tt < 2): per-lane source offsets inside a chunk,
-        // less the DMA's offset in its 4 KiB M0 window; half hh of tile rows
-        const int mw = tt;
-        uint32_t ot[2][UPR];
-#pragma unroll
-        for (int i = 0; i < UPR; ++i) {
-            const int r = i * RPI + lane / UPR;
-            const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
-            const int ld = mw == 0 ? ldw : ldk;
-            ot[0][i] = (uint32_t)((r * ld) * ES + unit * 16 - 1024 * (i % 4));
-            ot[1][i] = ot[0][i] + KH * ES;
-        }
-        uint32_t ou[NU];
-#pragma unroll
-        for (int i = 0; i < NU; ++i) ou[i] = (uint32_t)((i * 64 + lane) * 16 - 1024 * (i % 4));
         const uint32_t o4 = (uint32_t)(lane * 4);
-        const int sl0 = NP * slg;
-        const char *pt = mw == 0 ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
-        const int ldt = mw == 0 ? ldw : ldk;
-        const int64_t stt = (int64_t)C * ldt * ES;
-        const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl0, HV, VD, uv_ss));
-        const int64_t ssb = uv_ss * ES;  // bytes between consecutive slices of u
-        const char *p4 = mw == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
-        const char *prk = (const char *)(k_rnorm + k0r);
-        const int64_t stu = (int64_t)C * 16 * ES, st4 = (int64_t)C * 4;
-        const int tile_off = mw == 0 ? OFW : OFK;
-        const int off4 = mw == 0 ? OFD : OFG;
-        int rem_issue = (int)rows;
-        auto issue = [&](int st) {  // chunk into ring stage st (waves tt = 0, 1)
-            const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
-            const uint32_t sb = ring_base + st * SB + tile_off;
-            const rsrc_t rt = make_rsrc(pt, span(n, ldt * ES, KD * ES));
-            static_for<0, 2>([&](auto hc) {
-                constexpr int hh = decltype(hc)::value;
-                static_for<0, UPR>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    if constexpr (i % 4 == 0) set_m0(sb + (hh * HALF + 1024 * i));
-                    dma16_m0<1024 * (i % 4)>(rt, ot[hh][i]);
-                });
-            });
-            if (mw == 1) {
-                static_for<0, NP>([&](auto pc) {
-                    constexpr int pq = decltype(pc)::value;
-                    const rsrc_t ru = make_rsrc(pu + pq * ssb, (uint32_t)(n * 16 * ES));
-                    const uint32_t sbu = ring_base + st * SB + OFU + pq * (C * 16 * ES);
-                    static_for<0, NU>([&](auto ic) {
-                        constexpr int i = decltype(ic)::value;
-                        if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
-                        dma16_m0<1024 * (i % 4)>(ru, ou[i]);
-                    });
-                });
-            } else {
-                dma4(make_rsrc(prk, (uint32_t)(n * 4)), o4, ring_base + st * SB + OFR);
-            }
-            dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
-            pt += stt;
-            pu += stu;
-            p4 += st4;
-            prk += st4;
-            rem_issue -= C;
-        };
-        // chunk c + 1 landed: everything but the last issue's DMAs (other
-        // vector memory operations in between only make the wait stricter)
-        auto wait_ring = [&]() {
-            if (tt == 0)
-                wait_vmcnt<NDMA0>();
-            else
-                wait_vmcnt<NDMA1>();
-        };
 
         // ---- L2 pull duty (tt = 2): the w and K lines of chunk c + 2 (each
         // block of the head a share of the rows), the per-row factors (block
@@ -286,7 +211,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         FragT qf[2][NKS], qn[2][NKS];  // this token chunk's queries, and the next one's in flight
         float gn = 0.f, gnn = 0.f;
         auto load_q = [&](int ti, FragT (&qf)[2][NKS], float &gn) {
-            const int nt = clamp_rows(ntok - C * ti);
+            const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
             const rsrc_t rq = make_rsrc(q + ((bos + (int64_t)C * ti) * H + hk) * KD, span(nt, ldk * ES, KD * ES));
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
@@ -318,19 +243,27 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         f32x4 oa[NP];
         auto inter = [&]() {  // O^T = S Q^T exp(G_t), S from the state exchange
             const float f = fq * __expf(Gq);
+            FragT sx[NP][2][NKS];  // every state fragment first, then the products
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+                for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) sx[ct][kw][ks] = Sx[ct][kw][ks][lane];
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of the products
 #pragma unroll
             for (int ct = 0; ct < NP; ++ct) {
                 f32x4 a4 = zero4();
 #pragma unroll
                 for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) a4 = mma(Sx[ct][kw][ks][lane], qf[kw][ks], a4);
+                    for (int ks = 0; ks < NKS; ++ks) a4 = mma(sx[ct][kw][ks], qf[kw][ks], a4);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) oa[ct][r] = a4[r] * f;
             }
         };
         auto store_o = [&](int ti) {
-            const int nt = clamp_rows(ntok - C * ti);
+            const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
             const rsrc_t ro = make_rsrc(o + ((bos + (int64_t)C * ti) * HV + hv) * VD + 64 * slg,
                                         span(nt, HV * VD * ES, 64 * ES));
 #pragma unroll
@@ -345,32 +278,32 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
 
         load_q(0, qf, gn);
         token_setup();
-        if (tt < 2) {
-            issue(0);
-            issue(1);
-            if (tt == 0)
-                wait_vmcnt<NDMA0>();  // chunk 0 landed
-            else
-                wait_vmcnt<NDMA1>();
-        }
         lds_barrier();  // stage 0 landed; the initial state exchange is visible
         inter();
         int rem = (int)rows;
         const int t_me = 16 * tt + lc;  // this lane's token (within the token chunk)
-        // the previous chunk's scores (P V for a chunk runs in the next step,
-        // once its v_new is in the exchange)
+        // scores of one chunk as the B operands of O^T += V^T P^T, high and
+        // low bf16 parts per key half: made for chunk c before step c's
+        // barrier, consumed once chunk c's v_new is in the exchange (after
+        // step c + 1's barrier)
         FragT pb[2], pbl[2];
-        bool kact[2] = {false, false};
         auto pv = [&](int cprev) {  // O^T += V^T P^T over the block's column slices
+            // every v_new fragment first, then the products (masked scores
+            // are exact zeros, so the products of inactive key halves add
+            // nothing)
+            FragT vx[NP][2];
 #pragma unroll
             for (int ct = 0; ct < NP; ++ct)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    if (kact[s]) {
-                        const FragT a = Vx[cprev & 1][ct][s][lane];
-                        oa[ct] = mma(a, pb[s], oa[ct]);
-                        oa[ct] = mma(a, pbl[s], oa[ct]);
-                    }
+                for (int s = 0; s < 2; ++s) vx[ct][s] = Vx[cprev & 1][ct][s][lane];
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of the products
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    oa[ct] = mma(vx[ct][s], pb[s], oa[ct]);
+                    oa[ct] = mma(vx[ct][s], pbl[s], oa[ct]);
+                }
         };
         for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) {
             const int ti = (int)__umulhi((uint32_t)c, mdiv);  // token chunk
@@ -383,16 +316,12 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                 gn = gnn;
                 token_setup();
             }
-            // the next token chunk's queries, a token chunk ahead and before
-            // this step's ring loads (so the ring waits never wait on them)
+            // the next token chunk's queries, a token chunk ahead
             if (m == 0 && C * (ti + 1) < ntok) load_q(ti + 1, qn, gnn);
-            // chunk c + 2 into the stage chunk c - 1 left (freed by the last barrier)
-            if (tt < 2) issue(st_ == 0 ? 2 : st_ - 1);
             if (tt == 2) prefetch(c + PF);
             const HoStage<KD> &Sg = ring[st_];
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
-            // ---- the chunk's key rows (A operands of the scores) and norms,
-            // read before the barrier that frees the ring stage
+            // ---- the chunk's key rows (A operands of the scores) and norms
             FragT kr[4][2][NKS];
             f32x4 rk4[4];
 #pragma unroll
@@ -404,13 +333,11 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                         kr[st][kw][ks] = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
                 rk4[st] = *(const f32x4 *)(&Sg.rk[16 * st + 4 * lg]);
             }
-            // ---- the score factors of this step, which need no data of the
-            // chunk: dec = fq_t exp(G_t - G_s) for key row r of the chunk
-            // (expanded row 64 m + r of the token chunk: token s = (64 m +
-            // r) / M, copy (64 m + r) % M) when s <= t and r < n, else 0.
-            // Branch-free (masked entries take exp(0), so they stay finite),
-            // and before the barrier, where the ring waves wait for their
-            // loads anyway.
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of their uses
+            // ---- the score factors: dec = fq_t exp(G_t - G_s) for key row r
+            // of the chunk (expanded row 64 m + r of the token chunk: token
+            // s = (64 m + r) / M, copy (64 m + r) % M) when s <= t and r < n,
+            // else 0; branch-free, masked entries take exp(0)
             float dec[4][4];
 #pragma unroll
             for (int st = 0; st < 4; ++st)
@@ -423,8 +350,32 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     const float e = __expf(ok ? Gq - Gs : 0.f);
                     dec[st][r] = ok ? fq * e : 0.f;
                 }
-            if (tt < 2) wait_ring();          // chunk c + 1 landed
-            if (tt == 2) wait_vmcnt<24>();    // bound the number of pulls in flight
+            // ---- scores of the tile's tokens against the chunk's keys,
+            // P^T[key r][token t] = rk_r dec[r][t] (k_r . q_t), the four
+            // sub-tiles' products interleaved (masked entries are zeroed by
+            // dec)
+            f32x4 p[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) p[st] = zero4();
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int st = 0; st < 4; ++st) p[st] = mma(kr[st][kw][ks], qf[kw][ks], p[st]);
+            FragT pn[2], pnl[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int st = 2 * s + s2;
+                        const float x = p[st][r] * rk4[st][r] * dec[st][r];
+                        pn[s][4 * s2 + r] = (bf16)x;
+                        pnl[s][4 * s2 + r] = split_lo<bf16>(x, pn[s][4 * s2 + r]);
+                    }
+            if (tt == 2) wait_vmcnt<24>();  // bound the number of pulls in flight
             lds_barrier();  // ring stage c read; chunk c - 1's v_new is in the exchange
 
             if (c > 0) {
@@ -434,38 +385,17 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     inter();  // the state entering token chunk ti, exchanged in step c - 1
                 }
             }
-
-            // ---- scores of the tile's tokens against the chunk's keys:
-            // P^T[key r][token t] = rk_r dec[r][t] (k_r . q_t)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const int first_tok = (int)__umulhi((uint32_t)(C * m + 32 * s), mdiv);
-                kact[s] = first_tok <= 16 * tt + 15 && 32 * s < n;
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int st = 2 * s + s2;
-                    f32x4 p = zero4();
-                    const int ft = (int)__umulhi((uint32_t)(C * m + 16 * st), mdiv);
-                    if (ft <= 16 * tt + 15 && 16 * st < n) {
-#pragma unroll
-                        for (int kw = 0; kw < 2; ++kw)
-#pragma unroll
-                            for (int ks = 0; ks < NKS; ++ks) p = mma(kr[st][kw][ks], qf[kw][ks], p);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float x = p[r] * rk4[st][r] * dec[st][r];
-                        pb[s][4 * s2 + r] = (bf16)x;
-                        pbl[s][4 * s2 + r] = split_lo<bf16>(x, pb[s][4 * s2 + r]);
-                    }
-                }
+                pb[s] = pn[s];
+                pbl[s] = pnl[s];
             }
             rem -= C;
         }
         lds_barrier();  // the last chunk's v_new is in the exchange
         pv(nch - 1);
         store_o((int)__umulhi((uint32_t)(nch - 1), mdiv));
-        wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
+        wait_vmcnt<0>();  // no pull may still target LDS when the block retires
         return;
     }
 
@@ -473,12 +403,79 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     // Wave pp runs the state chain of the block's 16-column slice pp, with
     // the operands and order of the chunk_h stage's whole-K form, and
     // publishes the chunk's v_new (and at token-chunk ends the state) to
-    // the exchanges; it issues no global memory instruction in the loop.
-    // One code path for all four waves and all three ring stages (the wave
-    // and the stage are runtime values), so the code fits the instruction
-    // cache.
+    // the exchanges.  It also streams part of each chunk into the ring, two
+    // chunks ahead: half pp % 2 of the w (pp < 2) or K (pp >= 2) tile, its
+    // own u slice and one per-row vector (pp = 0: kdecay, 1: gcum, 2: key
+    // norms), with no other global memory instruction in the loop, so its
+    // counted waits are exact.  One code path for all four waves and all
+    // three ring stages (the wave and the stage are runtime values), so the
+    // code fits the instruction cache.
     const int pp = wave;
     const int sl = NP * slg + pp;
+    typedef HoStage<KD> Stage;
+    constexpr int OFW = (int)__builtin_offsetof(Stage, w);
+    constexpr int OFK = (int)__builtin_offsetof(Stage, k);
+    constexpr int OFU = (int)__builtin_offsetof(Stage, u);
+    constexpr int OFD = (int)__builtin_offsetof(Stage, kd);
+    constexpr int OFG = (int)__builtin_offsetof(Stage, gc);
+    constexpr int OFR = (int)__builtin_offsetof(Stage, rk);
+    constexpr int HALF = C * KH * ES;  // bytes of one half tile
+    const bool rw = pp < 2;             // w (else K)
+    const int hh = pp & 1;              // half of the tile's columns
+    const int ldt = rw ? ldw : ldk;
+    // per-lane source offsets inside a chunk, less the DMA's offset in its
+    // 4 KiB M0 window
+    uint32_t ot[UPR];
+#pragma unroll
+    for (int i = 0; i < UPR; ++i) {
+        const int r = i * RPI + lane / UPR;
+        const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
+        ot[i] = (uint32_t)((r * ldt) * ES + hh * KH * ES + unit * 16 - 1024 * (i % 4));
+    }
+    uint32_t ou[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) ou[i] = (uint32_t)((i * 64 + lane) * 16 - 1024 * (i % 4));
+    const uint32_t o4 = (uint32_t)(lane * 4);
+    const char *pt = rw ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
+    const int64_t stt = (int64_t)C * ldt * ES;
+    const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl, HV, VD, uv_ss));
+    const int64_t stu = (int64_t)C * 16 * ES;
+    const char *p4 = pp == 0 ? (const char *)(kdecay + h0r)
+                             : (pp == 1 ? (const char *)(gcum + h0r) : (const char *)(k_rnorm + k0r));
+    const int off4 = pp == 0 ? OFD : (pp == 1 ? OFG : OFR);
+    const int tile_off = (rw ? OFW : OFK) + hh * HALF;
+    int rem_issue = (int)rows;
+    auto issue = [&](int st) {  // the next chunk into ring stage st (rows past the end read as zero)
+        const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
+        const uint32_t sb = ring_base + st * SB + tile_off;
+        const rsrc_t rt = make_rsrc(pt, span(n, ldt * ES, KD * ES));  // whole rows: the half is in the offsets
+        static_for<0, UPR>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i % 4 == 0) set_m0(sb + 1024 * i);
+            dma16_m0<1024 * (i % 4)>(rt, ot[i]);
+        });
+        const rsrc_t ru = make_rsrc(pu, (uint32_t)(n * 16 * ES));
+        const uint32_t sbu = ring_base + st * SB + OFU + pp * (C * 16 * ES);
+        static_for<0, NU>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
+            dma16_m0<1024 * (i % 4)>(ru, ou[i]);
+        });
+        if (pp < 3) dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
+        pt += stt;
+        pu += stu;
+        p4 += st4;
+        rem_issue -= C;
+    };
+    // the chunk before the last issue landed: everything but that issue's loads
+    auto wait_ring = [&]() {
+        if (pp < 3)
+            wait_vmcnt<NDMA>();
+        else
+            wait_vmcnt<NDMA - 1>();
+    };
+    issue(0);
+    issue(1);
     f32x4 hs[2][NKT];
 #pragma unroll
     for (int kw = 0; kw < 2; ++kw)
@@ -504,9 +501,12 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     };
     pack();
     publish_state();
+    wait_ring();    // chunk 0 landed
     lds_barrier();  // stage 0 landed; the initial state exchange is visible
     int rem = (int)rows;
     for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) {
+        // chunk c + 2 into the stage chunk c - 1 left (freed by the last barrier)
+        issue(st_ == 0 ? 2 : st_ - 1);
         const HoStage<KD> &Sg = ring[st_];
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
         const int ti = (int)__umulhi((uint32_t)c, mdiv);
@@ -562,6 +562,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) hs[kw][kt][r] *= gl;
+        wait_ring();    // chunk c + 1 landed
         lds_barrier();  // ring stage c read; the exchanges of chunk c - 1 were read
 
         // ---- v_new (published to the exchange as bf16) and the phase-2
@@ -604,6 +605,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         rem -= C;
     }
     lds_barrier();  // the last chunk's v_new is in the exchange (matches the output waves)
+    wait_vmcnt<0>();  // no DMA may still target LDS when the block retires
     if (ht != nullptr) {
 #pragma unroll
         for (int kw = 0; kw < 2; ++kw)
