@@ -24,23 +24,23 @@
 //   registers, the same operands and order, so the states agree bit for
 //   bit), and publishes to LDS the chunk's v_new (bf16, one buffer per step
 //   parity) and, at the end of each token chunk, the state entering the next
-//   one (bf16).  They issue no global memory instruction in the loop.
+//   one (bf16).  They also stream each chunk into a three-stage LDS ring,
+//   two chunks ahead (buffer loads with the LDS destination; the range
+//   check zero-fills rows past the end): wave p a half tile of w (p < 2) or
+//   K (p >= 2), its u slice and one of kdecay, gcum and the key norms.
 // * Output waves 4-7.  Wave 4 + t owns output token tile t (tokens 16t ..
 //   16t + 15 of each token chunk) over all 64 columns of the block:
 //     - before the step's barrier, the scores of its tokens against the
 //       chunk's keys (the K tile is in the LDS ring), scaled by the norms and
-//       decays, masked to s <= t, as a high and a low bf16 part;
-//     - after it, O^T += V^T P^T with every slice's v_new from the exchange,
-//       and at a token chunk's end the store of o and the start of the next
-//       token chunk, O^T = S Q^T exp(G), with the exchanged state.
-//   Their query rows are loaded into registers a token chunk ahead.  Waves 4
-//   and 5 also stream w, K, u, kdecay, gcum and the key norms of each chunk
-//   into a three-stage LDS ring, two chunks ahead (buffer loads with the LDS
-//   destination; the range check zero-fills rows past the end), and wave 6
-//   pulls the lines of the chunk two ahead, and the next token chunk's query
-//   rows, into L2.
+//       decays, masked to s <= t, as a high and a low bf16 part, and in a
+//       token chunk's second step its inter-chunk term O^T = S Q^T exp(G)
+//       from the exchanged state;
+//     - after it, O^T += V^T P^T for the previous chunk with every slice's
+//       v_new from the exchange, and at a token chunk's end the store of o.
+//   Their query rows are loaded into registers a token chunk ahead, and
+//   their norms and decays are made a step before the token chunk starts.
 // One barrier per chunk orders it all: the ring stage of chunk c is read
-// before it, the exchanges are written before it and read after it.
+// before it, the exchanges are written after it and read after the next.
 // Requires M >= 2, so that the state exchange of one token chunk is read
 // before the next is written.
 #include "gdp_common.h"
@@ -95,7 +95,6 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     __shared__ __attribute__((aligned(16))) FragT Vx[2][NP][2][64];
     // state entering a token chunk, bf16, as O^T = S Q^T operands: [slice][K half][step][lane]
     __shared__ __attribute__((aligned(16))) FragT Sx[NP][2][NKS][64];
-    __shared__ __attribute__((aligned(16))) char Pf[1024];  // landing area of L2 prefetches
 
     // ---- block -> (sequence, value head, slice group); the groups of one
     // head share an XCD
@@ -157,54 +156,9 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     if (wave >= NP) {
         // ======================= output waves =======================
         // Output wave tt owns tokens 16 tt .. 16 tt + 15 of each token chunk
-        // over the block's 64 columns; wave 6 also issues the L2 pulls.
-        // Their only other memory instructions are their own query loads and
-        // output stores, so the compiler's waits for those are exact.
+        // over the block's 64 columns.  Its only global memory instructions
+        // are its query loads and output stores.
         const int tt = wave - NP;
-        const uint32_t o4 = (uint32_t)(lane * 4);
-
-        // ---- L2 pull duty (tt = 2): the w and K lines of chunk c + 2 (each
-        // block of the head a share of the rows), the per-row factors (block
-        // 0 of the head) and the query rows of the next token chunk
-        constexpr int PF = 2;
-        constexpr int RPB = C / SG;                 // rows per block per chunk
-        constexpr int RPC = 64 / (KD * ES / 128);  // rows one pull (a 4-byte load per line) covers
-        static_assert(KD * ES >= 128, "row pulls");
-        const uint32_t pf = lds_addr(&Pf[0]);
-        const int rbw = KD * ES;
-        auto rows_to_l2 = [&](const char *base, int nr, int ld) {
-            const int lpr = rbw / 128;  // lines per row
-            const rsrc_t r = make_rsrc(base, span(nr, ld, rbw));
-            dma4(r, (uint32_t)((lane / lpr) * ld + (lane % lpr) * 128), pf);  // rows >= nr: out of range
-        };
-        auto tile_to_l2 = [&](const char *base, int nr, int ld, auto nrc) {  // rows [0, nr), nr <= NR
-            constexpr int NR = decltype(nrc)::value;
-            static_for<0, (NR + RPC - 1) / RPC>([&](auto rc) {
-                constexpr int i = decltype(rc)::value;
-                const int nri = clamp_rows(nr - RPC * i);
-                rows_to_l2(base + (int64_t)RPC * i * ld, nri < RPC ? nri : RPC, ld);
-            });
-        };
-        auto prefetch = [&](int c) {
-            const int nr = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c - RPB * slg));
-            const int n = __builtin_amdgcn_readfirstlane(clamp_rows((int)rows - C * c));
-            const int64_t oc = c;
-            tile_to_l2((const char *)(w + ((r0 + RPB * slg) * HV + hv) * KD) + oc * C * ldw * ES,
-                       nr < RPB ? nr : RPB, ldw * ES, std::integral_constant<int, RPB>{});
-            tile_to_l2((const char *)(k + ((r0 + RPB * slg) * H + hk) * KD) + oc * C * ldk * ES,
-                       nr < RPB ? nr : RPB, ldk * ES, std::integral_constant<int, RPB>{});
-            if (slg == 0) {
-                dma4(make_rsrc((const char *)(kdecay + h0r) + oc * st4, (uint32_t)(n * 4)), o4, pf);
-                dma4(make_rsrc((const char *)(gcum + h0r) + oc * st4, (uint32_t)(n * 4)), o4, pf);
-                dma4(make_rsrc((const char *)(k_rnorm + k0r) + oc * st4, (uint32_t)(n * 4)), o4, pf);
-                const int cm = (int)__umulhi((uint32_t)c, mdiv);
-                if (c == cm * M) {  // query rows of token chunk c / M + 1
-                    const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * (cm + 1)));
-                    tile_to_l2((const char *)(q + ((bos + (int64_t)C * (cm + 1)) * H + hk) * KD), nt, ldk * ES,
-                               std::integral_constant<int, C>{});
-                }
-            }
-        };
 
         // ---- the output tile: queries (B operands of both output
         // products), their norms and decays for the current token chunk
@@ -221,9 +175,11 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                         FragT, buf_load16(rq, (uint32_t)(((16 * tt + lc) * ldk + kw * KH + 32 * ks + 8 * lg) * ES)));
             gn = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
         };
-        float fq = 0.f, Gq = 0.f, Gall = 0.f;  // scale/||q_t||, G_t of this lane's token, G of token `lane`
-        auto token_setup = [&]() {
-            Gall = wave_inclusive_sum(gn);
+        // scale/||q_t||, G_t of this lane's token and G of token `lane`, for
+        // the current token chunk and (made a step before it starts) the next
+        float fq = 0.f, Gq = 0.f, Gall = 0.f, fqn = 0.f, Gqn = 0.f, Galln = 0.f;
+        auto token_setup = [&](const FragT (&qs)[2][NKS], float gs, float &fq, float &Gq, float &Gall) {
+            Gall = wave_inclusive_sum(gs);
             Gq = __shfl(Gall, 16 * tt + lc, 64);
             float ss = 0.f;
 #pragma unroll
@@ -232,7 +188,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                 for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const float x = (float)qf[kw][ks][i];
+                        const float x = (float)qs[kw][ks][i];
                         ss += x * x;
                     }
             ss += __shfl_xor(ss, 16, 64);
@@ -277,9 +233,13 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         };
 
         load_q(0, qf, gn);
-        token_setup();
+        token_setup(qf, gn, fq, Gq, Gall);
         lds_barrier();  // stage 0 landed; the initial state exchange is visible
-        inter();
+        // O^T of a token chunk starts as its inter-chunk term, made in the
+        // token chunk's second step before the barrier (the state exchange
+        // holds the entering state from the step before the token chunk's
+        // first barrier until its M-th), then gathers each chunk's P V
+        bool inter_due = true;
         int rem = (int)rows;
         const int t_me = 16 * tt + lc;  // this lane's token (within the token chunk)
         // scores of one chunk as the B operands of O^T += V^T P^T, high and
@@ -313,12 +273,12 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                 for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) qf[kw][ks] = qn[kw][ks];
-                gn = gnn;
-                token_setup();
+                fq = fqn;
+                Gq = Gqn;
+                Gall = Galln;
             }
             // the next token chunk's queries, a token chunk ahead
             if (m == 0 && C * (ti + 1) < ntok) load_q(ti + 1, qn, gnn);
-            if (tt == 2) prefetch(c + PF);
             const HoStage<KD> &Sg = ring[st_];
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
             // ---- the chunk's key rows (A operands of the scores) and norms
@@ -375,16 +335,21 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                         pn[s][4 * s2 + r] = (bf16)x;
                         pnl[s][4 * s2 + r] = split_lo<bf16>(x, pn[s][4 * s2 + r]);
                     }
-            if (tt == 2) wait_vmcnt<24>();  // bound the number of pulls in flight
+            if (inter_due && m == 1) {
+                inter();  // the state entering token chunk ti
+                inter_due = false;
+            }
             lds_barrier();  // ring stage c read; chunk c - 1's v_new is in the exchange
 
             if (c > 0) {
                 pv(c - 1);
-                if (m == 0) {  // chunk c - 1 ended token chunk ti - 1; token chunk ti starts
+                if (m == 0) {  // chunk c - 1 ended token chunk ti - 1
                     store_o(ti - 1);
-                    inter();  // the state entering token chunk ti, exchanged in step c - 1
+                    inter_due = true;
                 }
             }
+            // the next token chunk's norms and decays, a step before it starts
+            if (m == M - 1 && C * (ti + 1) < ntok) token_setup(qn, gnn, fqn, Gqn, Galln);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 pb[s] = pn[s];
@@ -393,9 +358,9 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
             rem -= C;
         }
         lds_barrier();  // the last chunk's v_new is in the exchange
+        if (inter_due) inter();  // the last token chunk has a single chunk
         pv(nch - 1);
         store_o((int)__umulhi((uint32_t)(nch - 1), mdiv));
-        wait_vmcnt<0>();  // no pull may still target LDS when the block retires
         return;
     }
 
@@ -411,6 +376,9 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     // three ring stages (the wave and the stage are runtime values), so the
     // code fits the instruction cache.
     const int pp = wave;
+    // the state chain is the longer dependency path: its instructions go
+    // first when both waves of a SIMD are ready
+    __builtin_amdgcn_s_setprio(2);
     const int sl = NP * slg + pp;
     typedef HoStage<KD> Stage;
     constexpr int OFW = (int)__builtin_offsetof(Stage, w);
