@@ -34,6 +34,7 @@ KERNELS = {
     "gdp_recompute_w_u": ("gdp_wy_k", ["wy.hip"]),
     "gdp_chunk_h": ("gdp_chunk_h_k", ["chunk_h.hip"]),
     "gdp_chunk_o": ("gdp_chunk_o_k", ["chunk_o.hip"]),
+    "gdp_chunk_ho": ("gdp_chunk_ho_k", ["chunk_ho.hip"]),
     "gdp_seg_map": ("gdp_seg_map_k", ["scan.hip"]),
     "gdp_seg_scan": ("gdp_seg_scan_k", ["scan.hip"]),
 }
