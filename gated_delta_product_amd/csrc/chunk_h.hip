@@ -19,7 +19,7 @@
 // range, so the hardware drops it and nothing else in the schedule changes.
 //
 // One block of five waves per (sequence, value head, 16 value columns), with
-// three roles (the two-slice form is described below):
+// three roles (the two-slice and whole-K forms are described below):
 //
 // * Compute waves 0 and 1 run the serial chain and issue no global memory
 //   instruction at all.  Wave k owns rows [k K/2, (k+1) K/2) of the fp32
@@ -51,6 +51,13 @@
 // and both slices' u, and wave 6 prefetches.  The tiles then cross a CU once
 // per 32 columns.  To fit LDS, the compute waves store their own snapshots
 // and the partial sums are exchanged through two buffers by step parity.
+//
+// With more chains still (bf16, V >= 128), the whole-K form runs NP = 4
+// slices with one compute wave per slice: wave p holds all K rows of slice
+// p's state and forms both K halves' partial products itself, in the same
+// order as the split form, so the bits match and no partial-sum exchange is
+// needed.  Waves 4 and 5 stream the tiles and the four u slices, wave 6
+// prefetches; the tiles cross a CU once per 64 columns.
 #include "gdp_common.h"
 #include "gdp_internal.h"
 
@@ -771,11 +778,14 @@ static hipError_t launch_chunk_h_np(const ChunkParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// One column pair (16 value columns) per block gives the most chains; two
-// pairs per block halve the w and K tiles each CU streams per column, which
-// pays once there are chains enough for every CU several times over (many
-// sequences, or the segments of the segment-parallel forward).  Both give
-// the same bits: every slice runs the same arithmetic.
+// One 16-column slice per block gives the most chains; two slices per block
+// halve the w and K tiles each CU streams per column, and the whole-K form's
+// four slices halve them again.  More slices per block pay once there are
+// chains enough to fill every CU twice over: the whole-K form is taken for
+// bf16 with V >= 128 when sequences x value heads x V / 64 >= 512 blocks,
+// else the two-slice form when sequences x value heads x V / 32 >= 512,
+// else one slice.  All three give the same bits: every slice runs the same
+// arithmetic.
 template <typename T, int KD, int VD>
 static hipError_t launch_chunk_h_t(const ChunkParams &p, hipStream_t stream) {
     if constexpr (std::is_same<T, bf16>::value && VD >= 128) {
