@@ -125,11 +125,15 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 // ---------------------------------------------------------------- gates
 // (core.ssm.ops.gdp.prepare: the gates of gdp_prefill_prepare; shared by the
 // prepare kernels and the WY stage that fuses prepare in)
-// beta = 1 / (1 + exp(-b)) with float32 rounding after each operation;
-// exp is evaluated in double and rounded once.
+// The gates in float32, in the order and with the functions of the eager
+// tensor expressions they replace (core.ssm.ops.gdp.prepare, module
+// description: the gates are to match the eager path bit for bit): the
+// device's float32 exp and log1p, float32 rounding after each operation,
+// no contraction.
+// beta = 1 / (1 + exp(-b))
 __device__ __forceinline__ float gate_beta(float b) {
 #pragma clang fp contract(off)
-    const float e = (float)exp(-(double)b);
+    const float e = expf(-b);
     const float d = 1.0f + e;
     return 1.0f / d;
 }
@@ -139,14 +143,8 @@ __device__ __forceinline__ float gate_beta(float b) {
 __device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
 #pragma clang fp contract(off)
     const float s = a + dt_bias;
-    float sp;
-    if (s > 20.0f) {
-        sp = s;
-    } else {
-        const float e = (float)exp((double)s);
-        sp = (float)log1p((double)e);
-    }
-    const float ea = (float)exp((double)A_log);
+    const float sp = s > 20.0f ? s : log1pf(expf(s));
+    const float ea = expf(A_log);
     return -(ea * sp);
 }
 

@@ -2,7 +2,7 @@
 
 Small workloads are compared on every (sequence, value head); the long and
 wide workloads on sampled heads that the oracle runs end to end.  Tolerances:
-prepare copies bit-exact and gates within 1 ulp; chunk outputs within relative
+prepare copies bit-exact and gates within BETA_ULPS / G_ULPS; chunk outputs within relative
 L2 5e-3 and max-abs 2e-2 (bf16 inputs, fp32 accumulation) -- raw for o, and
 beyond each element's half-ulp bf16 storage quantum for the bf16 intermediates
 w, u, v_new and h, whose values reach ~10."""
@@ -20,6 +20,17 @@ from helpers import TOL, Acc, f32, gates, log, metrics, oracle_pair, run_pairs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+
+
+# The gates are the eager tensor expressions of the prepare page (which asks
+# for bitwise equality with the eager path), so they use the device's float32
+# exp and log1p, each within 1 ulp of the exact value, where the oracle
+# rounds exactly rounded functions per operation.  beta has one such function
+# in its chain (exp, then 1 + e and 1 / d): within 2 ulp of the oracle.  g has
+# three (exp(A_log), exp(s), log1p) and a product: within 4 ulp.  Equality
+# with torch's eager expressions on the device is checked separately
+# (test_gpu_eager_gates).
+BETA_ULPS, G_ULPS = 2, 4
 
 
 def _ulps(a, b):
@@ -262,7 +273,7 @@ def _prepare_check(x, ba, A_log, dt_bias, M, H, G_, P, N, tag):
     ug = _ulps(g.cpu().numpy(), rg)
     log("%s: beta max ulp %d (%d differ), g max ulp %d (%d differ)" % (
         tag, ub.max(), (ub > 0).sum(), ug.max(), (ug > 0).sum()))
-    assert ub.max() <= 1 and ug.max() <= 1
+    assert ub.max() <= BETA_ULPS and ug.max() <= G_ULPS
     return q, k, v, beta, g
 
 
@@ -512,7 +523,7 @@ def test_prefill_pipelined_is_bit_identical():
 def test_decode_prepare_matches_oracle():
     """gdp_decode_prepare: key, value and the query copies bit-exact, the
     query only on each token's last copy and the decay only on its first
-    (exact zeros elsewhere), gates within 1 ulp; bf16 and f32, M = 2 and 3."""
+    (exact zeros elsewhere), gates within BETA_ULPS / G_ULPS; bf16 and f32, M = 2 and 3."""
     cases = (("bf16", 5, 3, 2, 16, 4, 128, 128), ("f32", 3, 2, 3, 4, 2, 64, 64), ("bf16", 64, 1, 4, 16, 16, 128, 128))
     for i, (dt, n, S, M, H, G_, P, N) in enumerate(cases):
         d = synth.prepare_draws(n, S, M, H, G_, P, N, dt, synth.seed_of(3) + 50 + i)
@@ -528,7 +539,7 @@ def test_decode_prepare_matches_oracle():
         assert torch.equal(v.cpu(), torch.from_numpy(rv).to(t)), "v"
         gc = g.cpu().numpy()
         assert np.all(gc[:, [e for e in range(S * M) if e % M]] == 0.0)
-        assert _ulps(beta.cpu().numpy(), rb).max() <= 1 and _ulps(gc, rg).max() <= 1
+        assert _ulps(beta.cpu().numpy(), rb).max() <= BETA_ULPS and _ulps(gc, rg).max() <= G_ULPS
 
 
 def _decode_oracle(q, k, v, beta, g, state, slots, scale=None):
