@@ -352,11 +352,33 @@ def chunk_fwd_line(G, torch, dev, stream, cfg_id, reps):
             "gdp_chunk_h": kernel_entry(us[1], ab["gdp_chunk_h"]),
             "gdp_chunk_o": kernel_entry(us[2], ab["gdp_chunk_o"])}
     tot = sum(us)
+    out = {"workload": c["name"], "shape": dict(w, dtype=c["dtype"]), "path": "gdp_chunk_fwd",
+           "us": round(tot, 1), "tokens_per_s": round(B * T / (tot / 1e6), 1), "kernels": kern,
+           "roofline": roofline_of(kern)}
+    if dt == torch.bfloat16 and M >= 2 and K in (64, 128) and V in (64, 128, 256):
+        # the output-only form: v_new and h NULL, chunk_h and chunk_o as one
+        # pass; its pass time is the whole call less WY alone, both timed here
+        def run_wy(ev):
+            ev[0].record(stream) if ev else None
+            buf.recompute_w_u()
+            ev[1].record(stream) if ev else None
+
+        def run_fused(ev):
+            ev[0].record(stream) if ev else None
+            buf.forward(store_vnew_h=False)
+            ev[1].record(stream) if ev else None
+
+        wy_us = time_stages(torch, stream, run_wy, 2, reps)[0]
+        fz_us = time_stages(torch, stream, run_fused, 2, reps)[0]
+        kf = {"gdp_recompute_w_u": kernel_entry(wy_us, ab["gdp_recompute_w_u"]),
+              "gdp_chunk_ho": dict(kernel_entry(fz_us - wy_us, scan_bytes(w, 1, 1)["chunk_ho"]),
+                                   note="the call less WY alone")}
+        out["fused"] = {"path": "gdp_chunk_fwd with v_new and h NULL (WY, then chunk_h and chunk_o as one pass)",
+                        "us": round(fz_us, 1), "tokens_per_s": round(B * T / (fz_us / 1e6), 1), "kernels": kf,
+                        "roofline": roofline_of(kf)}
     del buf, q, k, v, b, a, beta, g
     torch.cuda.empty_cache()
-    return {"workload": c["name"], "shape": dict(w, dtype=c["dtype"]), "path": "gdp_chunk_fwd",
-            "us": round(tot, 1), "tokens_per_s": round(B * T / (tot / 1e6), 1), "kernels": kern,
-            "roofline": roofline_of(kern)}
+    return out
 
 
 def varlen_line(G, torch, dev, stream, reps, segments=16):
@@ -392,7 +414,7 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
     def run_scan(ev):
         if ev:
             ev[0].record(stream)
-        gva.forward_scan(segments, stage_events=ev[1:] if ev else None)
+        gva.forward_scan(segments, stage_events=ev[1:] if ev else None, store_vnew_h=False)
 
     us = time_stages(torch, stream, run_scan, 6, reps)
     seq = G.ChunkBuffers(gva.q, gva.k, v, beta, g, cu_seqlens=cu_d, cu_seqlens_host=cu)
@@ -400,7 +422,7 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
     def run_seq(ev):
         if ev:
             ev[0].record(stream)
-        seq.forward()
+        seq.forward(store_vnew_h=False)
         if ev:
             ev[1].record(stream)
 
@@ -411,7 +433,7 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
         if ev:
             ev[0].record(stream)
         fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], segments, stage_events=ev[1:] if ev else None,
-                        store_v_beta=False)
+                        store_v_beta=False, store_vnew_h=False)
 
     fus = time_stages(torch, stream, run_fused, 6, reps)
 
@@ -419,7 +441,7 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
         if ev:
             ev[0].record(stream)
         fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], 1, stage_events=ev[1:] if ev else None,
-                        store_v_beta=False)
+                        store_v_beta=False, store_vnew_h=False)
 
     fus1 = time_stages(torch, stream, run_fused1, 6, reps)
     # algorithmic bytes: the chunk stages at H = 4 key heads, HV = 16
@@ -432,28 +454,29 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
     sb = scan_bytes(w, segments, None, mapped_tokens=mapped, nstates=sum(nsegs))
     kern = {"gdp_recompute_w_u": kernel_entry(us[0], ab["gdp_recompute_w_u"]),
             "gdp_seg_map": kernel_entry(us[1], sb["map"]), "gdp_seg_scan": kernel_entry(us[2], sb["scan"]),
-            "gdp_chunk_h": kernel_entry(us[3], sb["chunk_h"]), "gdp_chunk_o": kernel_entry(us[4], ab["gdp_chunk_o"])}
+            "gdp_chunk_ho": kernel_entry(us[3] + us[4], sb["chunk_ho"])}
     tot = sum(us)
     sbf = scan_bytes(wp, segments, None, mapped_tokens=mapped, nstates=sum(nsegs))
     kf = {"gdp_recompute_w_u (prepare fused)": kernel_entry(fus[0], sbf["wy_fused"]),
           "gdp_seg_map": kernel_entry(fus[1], sbf["map"]), "gdp_seg_scan": kernel_entry(fus[2], sbf["scan"]),
-          "gdp_chunk_h": kernel_entry(fus[3], sbf["chunk_h"]),
-          "gdp_chunk_o": kernel_entry(fus[4], algorithmic_bytes(wp)["gdp_chunk_o"])}
+          "gdp_chunk_ho": kernel_entry(fus[3] + fus[4], sbf["chunk_ho"])}
     out = {"workload": c["name"], "T": T, "cu_seqlens": [int(t) for t in cu], "segments_per_request": nsegs,
            "seg_tok": seg_tok,
            "prepare": dict(kernel_entry(prep_us, prep_b), tokens_per_s=round(T / (prep_us / 1e6), 1),
                            shape=dict(H=p["H"], G=p["G"], P=p["P"], N=p["N"], M=M)),
-           "chunk_fwd_scan_gva": {"path": "gdp_chunk_fwd_scan, H=4 key heads, HV=16", "us": round(tot, 1),
+           "chunk_fwd_scan_gva": {"path": "gdp_chunk_fwd_scan, H=4 key heads, HV=16, v_new and h not stored "
+                                          "(chunk_h and chunk_o as one pass)", "us": round(tot, 1),
                                   "tokens_per_s": round(T / (tot / 1e6), 1), "kernels": kern,
                                   "roofline": roofline_of(kern)},
-           "chunk_fwd_sequential_gva": {"path": "gdp_chunk_fwd (unsegmented chunk_h)", "us": round(seq_us, 1),
+           "chunk_fwd_sequential_gva": {"path": "gdp_chunk_fwd, unsegmented, v_new and h not stored",
+                                        "us": round(seq_us, 1),
                                         "tokens_per_s": round(T / (seq_us / 1e6), 1)},
-           "prefill_fwd_scan": {"path": "gdp_prefill_fwd_scan (prepare inside WY, H=HV=16 expanded, v and beta "
-                                        "not stored)", "us": round(sum(fus), 1),
+           "prefill_fwd_scan": {"path": "gdp_prefill_fwd_scan (prepare inside WY, H=HV=16 expanded, v, beta, "
+                                        "v_new and h not stored)", "us": round(sum(fus), 1),
                                 "tokens_per_s": round(T / (sum(fus) / 1e6), 1), "kernels": kf,
                                 "roofline": roofline_of(kf)},
            "prefill_fwd_scan_1seg": {"path": "gdp_prefill_fwd_scan with num_segments=1 (no request split, no "
-                                             "maps)", "us": round(sum(fus1), 1),
+                                             "maps; v, beta, v_new and h not stored)", "us": round(sum(fus1), 1),
                                      "tokens_per_s": round(T / (sum(fus1) / 1e6), 1),
                                      "stage_us": [round(u, 1) for u in fus1]}}
     del gva, seq, fz, pre, x, ba

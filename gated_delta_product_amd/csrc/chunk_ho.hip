@@ -22,7 +22,7 @@
 // * Chain waves 0-3.  Wave p runs the state chain of the 16-column slice p
 //   exactly as the whole-K form of the chunk_h stage does (fp32 state in
 //   registers, the same operands and order, so the states agree bit for
-//   bit), and publishes to LDS the chunk's v_new (bf16, one buffer per step
+//   bit), and publishes to LDS the chunk's v_new (fp16, one buffer per step
 //   parity) and, at the end of each token chunk, the state entering the next
 //   one (bf16).  They also stream each chunk into a three-stage LDS ring,
 //   two chunks ahead (buffer loads with the LDS destination; the range
@@ -32,9 +32,9 @@
 //   16t + 15 of each token chunk) over all 64 columns of the block:
 //     - before the step's barrier, the scores of its tokens against the
 //       chunk's keys (the K tile is in the LDS ring), scaled by the norms and
-//       decays, masked to s <= t, as a high and a low bf16 part, and in a
-//       token chunk's second step its inter-chunk term O^T = S Q^T exp(G)
-//       from the exchanged state;
+//       decays, masked to s <= t, in fp16, and in a token chunk's second
+//       step its inter-chunk term O^T = S Q^T exp(G) from the exchanged
+//       state;
 //     - after it, O^T += V^T P^T for the previous chunk with every slice's
 //       v_new from the exchange, and at a token chunk's end the store of o.
 //   Their query rows are loaded into registers a token chunk ahead, and
@@ -43,6 +43,14 @@
 // before it, the exchanges are written after it and read after the next.
 // Requires M >= 2, so that the state exchange of one token chunk is read
 // before the next is written.
+//
+// Precision.  The state chain keeps the chunk_h stage's operands exactly.
+// The output product O^T += V^T P^T runs on fp16 operands: both are made on
+// chip (v_new by the chain waves, P by the output waves), |P| <= scale, and
+// fp16's 11-bit significand keeps them closer to their fp32 values than
+// bf16 does, with one product per pair where bf16 needed a high and a low
+// part.  v_new must stay within fp16's range (|v_new| < 65504); beyond it
+// the output is not finite.
 #include "gdp_common.h"
 #include "gdp_internal.h"
 
@@ -91,8 +99,8 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     static_assert(NDMA < 64, "in-flight count must fit the vector memory counter");
 
     __shared__ __attribute__((aligned(16))) HoStage<KD> ring[NS];
-    // v_new of the chunk, bf16, as O^T = V^T P^T operands: [parity][slice][key half s][lane]
-    __shared__ __attribute__((aligned(16))) FragT Vx[2][NP][2][64];
+    // v_new of the chunk, fp16, as O^T = V^T P^T operands: [parity][slice][key half s][lane]
+    __shared__ __attribute__((aligned(16))) f16x8 Vx[2][NP][2][64];
     // state entering a token chunk, bf16, as O^T = S Q^T operands: [slice][K half][step][lane]
     __shared__ __attribute__((aligned(16))) FragT Sx[NP][2][NKS][64];
 
@@ -242,16 +250,15 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         bool inter_due = true;
         int rem = (int)rows;
         const int t_me = 16 * tt + lc;  // this lane's token (within the token chunk)
-        // scores of one chunk as the B operands of O^T += V^T P^T, high and
-        // low bf16 parts per key half: made for chunk c before step c's
-        // barrier, consumed once chunk c's v_new is in the exchange (after
-        // step c + 1's barrier)
-        FragT pb[2], pbl[2];
+        // scores of one chunk as the fp16 B operands of O^T += V^T P^T, per
+        // key half: made for chunk c before step c's barrier, consumed once
+        // chunk c's v_new is in the exchange (after step c + 1's barrier)
+        f16x8 pb[2];
         auto pv = [&](int cprev) {  // O^T += V^T P^T over the block's column slices
             // every v_new fragment first, then the products (masked scores
             // are exact zeros, so the products of inactive key halves add
             // nothing)
-            FragT vx[NP][2];
+            f16x8 vx[NP][2];
 #pragma unroll
             for (int ct = 0; ct < NP; ++ct)
 #pragma unroll
@@ -262,7 +269,6 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     oa[ct] = mma(vx[ct][s], pb[s], oa[ct]);
-                    oa[ct] = mma(vx[ct][s], pbl[s], oa[ct]);
                 }
         };
         for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) {
@@ -323,7 +329,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                 for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                     for (int st = 0; st < 4; ++st) p[st] = mma(kr[st][kw][ks], qf[kw][ks], p[st]);
-            FragT pn[2], pnl[2];
+            f16x8 pn[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -332,8 +338,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     for (int r = 0; r < 4; ++r) {
                         const int st = 2 * s + s2;
                         const float x = p[st][r] * rk4[st][r] * dec[st][r];
-                        pn[s][4 * s2 + r] = (bf16)x;
-                        pnl[s][4 * s2 + r] = split_lo<bf16>(x, pn[s][4 * s2 + r]);
+                        pn[s][4 * s2 + r] = (f16)x;
                     }
             if (inter_due && m == 1) {
                 inter();  // the state entering token chunk ti
@@ -353,7 +358,6 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 pb[s] = pn[s];
-                pbl[s] = pnl[s];
             }
             rem -= C;
         }
@@ -541,7 +545,8 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         // bit
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            FragT vb[2], vbl[2], v8;
+            FragT vb[2], vbl[2];
+            f16x8 v8;
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
                 const int rt = 2 * s + r2;
@@ -550,7 +555,7 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
                     const float uf = (float)uu[rt][r];
                     const float ua0 = uf - acc[0][rt][r], ua1 = uf - acc[1][rt][r];
                     const float uk0 = ua0 * kd4[rt][r], uk1 = ua1 * kd4[rt][r];
-                    v8[4 * r2 + r] = (bf16)(s == 0 ? ua0 - acc[1][rt][r] : ua1 - acc[0][rt][r]);
+                    v8[4 * r2 + r] = (f16)(s == 0 ? ua0 - acc[1][rt][r] : ua1 - acc[0][rt][r]);
                     const float x0 = __builtin_fmaf(-acc[1][rt][r], kd4[rt][r], uk0);
                     const float x1 = __builtin_fmaf(-acc[0][rt][r], kd4[rt][r], uk1);
                     vb[0][4 * r2 + r] = (bf16)x0;

@@ -39,6 +39,13 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// fp16 operands (values made on chip, where fp16's 11-bit significand is
+// the better fit than bf16's 8 bits): v_mfma_f32_16x16x32_f16
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
