@@ -433,7 +433,7 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
         if ev:
             ev[0].record(stream)
         fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], segments, stage_events=ev[1:] if ev else None,
-                        store_v_beta=False, store_vnew_h=False)
+                        store_v_beta=False, store_vnew_h=False, store_qk=False)
 
     fus = time_stages(torch, stream, run_fused, 6, reps)
 
@@ -441,7 +441,7 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
         if ev:
             ev[0].record(stream)
         fz.prefill_scan(x, ba, A_log, dt_bias, p["G"], 1, stage_events=ev[1:] if ev else None,
-                        store_v_beta=False, store_vnew_h=False)
+                        store_v_beta=False, store_vnew_h=False, store_qk=False)
 
     fus1 = time_stages(torch, stream, run_fused1, 6, reps)
     # algorithmic bytes: the chunk stages at H = 4 key heads, HV = 16
@@ -457,7 +457,8 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
             "gdp_chunk_ho": kernel_entry(us[3] + us[4], sb["chunk_ho"])}
     tot = sum(us)
     sbf = scan_bytes(wp, segments, None, mapped_tokens=mapped, nstates=sum(nsegs))
-    kf = {"gdp_recompute_w_u (prepare fused)": kernel_entry(fus[0], sbf["wy_fused"]),
+    wyb = sbf["wy_fused"] - (T * (p["G"] + p["H"]) * p["N"] * 2 + T * M * p["H"] * p["N"] * 2)  # no q, k stores
+    kf = {"gdp_recompute_w_u (prepare fused)": kernel_entry(fus[0], wyb),
           "gdp_seg_map": kernel_entry(fus[1], sbf["map"]), "gdp_seg_scan": kernel_entry(fus[2], sbf["scan"]),
           "gdp_chunk_ho": kernel_entry(fus[3] + fus[4], sbf["chunk_ho"])}
     out = {"workload": c["name"], "T": T, "cu_seqlens": [int(t) for t in cu], "segments_per_request": nsegs,
@@ -472,11 +473,11 @@ def varlen_line(G, torch, dev, stream, reps, segments=16):
                                         "us": round(seq_us, 1),
                                         "tokens_per_s": round(T / (seq_us / 1e6), 1)},
            "prefill_fwd_scan": {"path": "gdp_prefill_fwd_scan (prepare inside WY, H=HV=16 expanded, v, beta, "
-                                        "v_new and h not stored)", "us": round(sum(fus), 1),
+                                        "q, k, v_new and h not stored)", "us": round(sum(fus), 1),
                                 "tokens_per_s": round(T / (sum(fus) / 1e6), 1), "kernels": kf,
                                 "roofline": roofline_of(kf)},
            "prefill_fwd_scan_1seg": {"path": "gdp_prefill_fwd_scan with num_segments=1 (no request split, no "
-                                             "maps; v, beta, v_new and h not stored)", "us": round(sum(fus1), 1),
+                                             "maps; v, beta, q, k, v_new and h not stored)", "us": round(sum(fus1), 1),
                                      "tokens_per_s": round(T / (sum(fus1) / 1e6), 1),
                                      "stage_us": [round(u, 1) for u in fus1]}}
     del gva, seq, fz, pre, x, ba
@@ -498,6 +499,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--store-v-beta", action="store_true",
                     help="prefill-scan: also store the value copies and beta (no later stage reads them)")
+    ap.add_argument("--store-qk", action="store_true",
+                    help="prefill-scan: also store q and k (otherwise the later stages read their rows from x)")
     ap.add_argument("--store-vnew-h", action="store_true",
                     help="scan paths: store v_new and h, i.e. run chunk_h and chunk_o as two launches (by default "
                          "they run as one pass that stores neither)")
@@ -525,9 +528,12 @@ def main():
     if args.segments is None:
         args.segments = SCAN_SEGMENTS if scan else SEGMENTS
     ho = "chunk_h,chunk_o" if args.store_vnew_h else "chunk_h+o in one pass"
+    if args.store_vnew_h:
+        args.store_qk = True  # q and k from x only with the one-pass form
     if fused:
         w["path"] = "prefill_scan(recompute_w_u with prepare,seg_map,seg_scan,%s)" % ho + (
-            "" if args.store_v_beta else "; v, beta not stored") + ("" if args.store_vnew_h else "; v_new, h not stored")
+            "" if args.store_v_beta else "; v, beta not stored") + ("" if args.store_vnew_h else "; v_new, h not stored") \
+            + ("" if args.store_qk else "; q, k not stored (read from x)")
     elif scan:
         w["path"] = "prepare+scan(recompute_w_u,seg_map,seg_scan,%s)" % ho
     dev = torch.device("cuda:0")
@@ -558,7 +564,8 @@ def main():
             if ev:
                 ev[1].record(stream)
             buf.prefill_scan(x, ba, A_log, dt_bias, Gq, args.segments, stage_events=ev[2:] if ev else None,
-                             store_v_beta=args.store_v_beta, store_vnew_h=args.store_vnew_h)
+                             store_v_beta=args.store_v_beta, store_vnew_h=args.store_vnew_h,
+                             store_qk=args.store_qk)
             return
         G.prefill_prepare(x, ba, A_log, dt_bias, M, H, Gq, P, N, out=prep_out)
         if ev:
@@ -597,8 +604,10 @@ def main():
     if scan:
         sb = scan_bytes(w, args.segments, nseg)
         if fused:
-            add("gdp_recompute_w_u (prepare fused)", span_us(1, 2), sb["wy_fused"] if not args.store_v_beta
-                else sb["wy_fused"] + w["T"] * w["M"] * w["HV"] * (w["V"] * 2 + 4))
+            wyb = sb["wy_fused"] if not args.store_v_beta else sb["wy_fused"] + w["T"] * w["M"] * w["HV"] * (w["V"] * 2 + 4)
+            if not args.store_qk:  # no q read, no q or k stored
+                wyb -= w["T"] * (w["G"] + w["H"]) * w["K"] * 2 + w["T"] * w["M"] * w["H"] * w["K"] * 2
+            add("gdp_recompute_w_u (prepare fused)", span_us(1, 2), wyb)
         else:
             add("gdp_prefill_prepare", span_us(0, 1), ab["gdp_prefill_prepare"])
             add("gdp_recompute_w_u", span_us(1, 2), ab["gdp_recompute_w_u"])

@@ -372,13 +372,15 @@ class ChunkBuffers:
         return args
 
     def prefill_scan(self, x, ba, A_log, dt_bias, num_groups, num_segments, stream=None, stage_events=None,
-                     store_v_beta=True, store_vnew_h=True):
+                     store_v_beta=True, store_vnew_h=True, store_qk=True):
         """gdp_prefill_fwd_scan: prepare x / ba into this buffer's q, k, v,
         beta, g (allocated with the prepare shapes) inside the WY stage of the
         segment-parallel forward.  Arguments as prefill_prepare and
         forward_scan.  store_v_beta=False passes v and beta as NULL: nothing
         after the WY stage reads them, and they are left untouched.
-        store_vnew_h=False as for forward_scan."""
+        store_vnew_h=False as for forward_scan.  store_qk=False (with
+        store_vnew_h=False) passes q and k as NULL: the later stages read their
+        rows from x, and q and k are left untouched."""
         _need_cuda(x, ba, A_log, dt_bias)
         d = self.dims
         if x.dim() != 3 or x.stride(2) != 1 or ba.dim() != 3 or ba.stride(2) != 1:
@@ -389,7 +391,8 @@ class ChunkBuffers:
                          ba_n_stride=ba.stride(0), ba_t_stride=ba.stride(1), A_log=A_log.data_ptr(),
                          dt_bias=dt_bias.data_ptr(), G=int(num_groups))
         args = self._args_without(*((() if store_v_beta else ("v", "beta")) +
-                                    (() if store_vnew_h else ("v_new", "h"))))
+                                    (() if store_vnew_h else ("v_new", "h")) +
+                                    (() if store_qk else ("q", "k"))))
         return self._scan(lambda ws, nb, ev, s: lib().gdp_prefill_fwd_scan(
             ctypes.byref(pa), ctypes.byref(args), int(num_segments), ws, nb, ev, s), num_segments, stream,
             stage_events)

@@ -47,7 +47,9 @@ gdp_status hip_status(hipError_t e, const char *what) {
 // stages of a call; ST_WYP is WY with the prepare fused in, which takes its
 // values and beta from the activations, so it needs neither tensor
 // ST_HO is chunk_h and chunk_o as one pass, which stores neither v_new nor h
-enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u, ST_WYP = 8u, ST_HO = 16u };
+// ST_QKX: q and k are read from the activations (the fused prefill that
+// does not store them), so neither tensor is needed
+enum : unsigned { ST_WY = 1u, ST_H = 2u, ST_O = 4u, ST_WYP = 8u, ST_HO = 16u, ST_QKX = 32u };
 
 gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParams *out) {
     if (!a) return fail(GDP_ERR_INVALID, "args is NULL");
@@ -90,17 +92,21 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
         unsigned stages;
         const void *p;
         const char *name;
+        bool qk;  // q or k
     } needs[] = {
-        {ST_O | ST_HO, a->q, "q"},   {ST_WY | ST_WYP | ST_H | ST_O | ST_HO, a->k, "k"}, {ST_WY, a->v, "v"},
-        {ST_WY, a->beta, "beta"},    {ST_WY | ST_WYP | ST_O | ST_HO, a->k_rnorm, "k_rnorm"},
-        {ST_WY | ST_WYP | ST_H | ST_HO, a->gcum, "gcum"},    {ST_WY | ST_WYP | ST_H | ST_HO, a->kdecay, "kdecay"},
-        {ST_WY | ST_WYP | ST_H | ST_HO, a->w, "w"},   {ST_WY | ST_WYP | ST_H | ST_HO, a->u, "u"},
-        {ST_H | ST_O, a->v_new, "v_new"},
-        {ST_H | ST_O, a->h, "h"},    {ST_O | ST_HO, a->o, "o"},
+        {ST_O | ST_HO, a->q, "q", true},   {ST_WY | ST_WYP | ST_H | ST_O | ST_HO, a->k, "k", true},
+        {ST_WY, a->v, "v", false},         {ST_WY, a->beta, "beta", false},
+        {ST_WY | ST_WYP | ST_O | ST_HO, a->k_rnorm, "k_rnorm", false},
+        {ST_WY | ST_WYP | ST_H | ST_HO, a->gcum, "gcum", false},
+        {ST_WY | ST_WYP | ST_H | ST_HO, a->kdecay, "kdecay", false},
+        {ST_WY | ST_WYP | ST_H | ST_HO, a->w, "w", false},   {ST_WY | ST_WYP | ST_H | ST_HO, a->u, "u", false},
+        {ST_H | ST_O, a->v_new, "v_new", false},
+        {ST_H | ST_O, a->h, "h", false},    {ST_O | ST_HO, a->o, "o", false},
     };
     if (!empty) {
         for (const Need &n : needs) {
             if (!(n.stages & stages)) continue;
+            if ((stages & ST_QKX) && n.qk) continue;  // read from the activations
             if (!n.p) return fail(GDP_ERR_INVALID, "%s is NULL", n.name);
             if (!aligned16(n.p)) return fail(GDP_ERR_INVALID, "%s is not 16-byte aligned", n.name);
         }
@@ -118,6 +124,8 @@ gdp_status check_chunk(const gdp_chunk_args *a, unsigned stages, gdp::ChunkParam
     out->max_items = empty ? 0 : max_items;
     out->max_tok_chunks = empty ? 0 : max_tok;
     out->uv_ss = T * a->M * 16;
+    out->qk = gdp::QKRows{a->k, a->q, (int64_t)a->M * a->H * a->K, (int64_t)a->H * a->K, (int64_t)a->H * a->K,
+                          (int64_t)a->K, 1};
     return ok();
 }
 
@@ -164,7 +172,7 @@ static gdp_status prepare_check(const char *name, bool decode, const void *x, in
                                 const float *A_log, const float *dt_bias, int64_t n, int64_t T, int32_t M,
                                 int32_t H, int32_t G, int32_t P, int32_t N, gdp_dtype dtype, void *q, void *k,
                                 void *v, float *beta, float *g, gdp::PrepareParams *out,
-                                bool vb_optional = false) {
+                                bool vb_optional = false, bool qk_optional = false) {
     *out = gdp::PrepareParams{};
     if (dtype != GDP_F32 && dtype != GDP_BF16) return fail(GDP_ERR_INVALID, "%s: unknown dtype %d", name, (int)dtype);
     if (n < 0 || T < 0) return fail(GDP_ERR_INVALID, "%s: n and T must be >= 0", name);
@@ -176,7 +184,8 @@ static gdp_status prepare_check(const char *name, bool decode, const void *x, in
     if (x_t_stride < 0 || x_n_stride < 0 || ba_t_stride < 0 || ba_n_stride < 0)
         return fail(GDP_ERR_INVALID, "%s: strides must be >= 0", name);
     if (n == 0 || T == 0) return ok();  // *out stays empty
-    if (!x || !ba || !A_log || !dt_bias || !q || !k || (!v && !vb_optional) || (!beta && !vb_optional) || !g)
+    if (!x || !ba || !A_log || !dt_bias || (!q && !qk_optional) || (!k && !qk_optional) || (!v && !vb_optional) ||
+        (!beta && !vb_optional) || !g)
         return fail(GDP_ERR_INVALID, "%s: a tensor pointer is NULL", name);
     if (T > 1 && x_t_stride < width) return fail(GDP_ERR_INVALID, "%s: x rows overlap (t stride %lld < width %lld)",
                                                  name, (long long)x_t_stride, (long long)width);
@@ -508,9 +517,19 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
     // v_new and h both NULL: chunk_h and chunk_o run as one pass that stores
     // neither (launch_chunk_ho)
     const bool fused = a->v_new == nullptr && a->h == nullptr;
+    // q and k not stored (the fused prefill only): the later stages read
+    // their rows from the activations
+    const bool qkx = prep != nullptr && a->q == nullptr && a->k == nullptr;
+    const unsigned qks = qkx ? ST_QKX : 0u;
     gdp::ChunkParams p;
-    gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | (fused ? ST_HO : ST_H | ST_O), &p);
+    gdp_status st = check_chunk(a, (prep ? ST_WYP : ST_WY) | (fused ? ST_HO : ST_H | ST_O) | qks, &p);
     if (st != GDP_OK) return st;
+    if (qkx) {  // x row: [values (M, H, P) | keys (M, G, N) | queries (G, N)] (bf16 here)
+        const int64_t ko = (int64_t)prep->M * prep->H * prep->P, qo = ko + (int64_t)prep->M * prep->G * prep->N;
+        const char *x = (const char *)prep->x;
+        p.qk = gdp::QKRows{x + 2 * ko, x + 2 * qo, prep->x_t_stride, (int64_t)prep->G * prep->N, prep->x_t_stride,
+                           (int64_t)prep->N, prep->H / prep->G};
+    }
     if (fused && a->M < 2 && p.nseq > 0)
         return fail(GDP_ERR_UNSUPPORTED, "%s: v_new and h may be NULL (one chunk_h and chunk_o pass) only for M >= 2",
                     name);
@@ -564,7 +583,8 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
     ha.h0 = sp.hstart;
     ha.ht = sp.hstart;
     gdp::ChunkParams hp;
-    if ((st = check_chunk(&ha, fused ? ST_HO : ST_H, &hp)) != GDP_OK) return st;
+    if ((st = check_chunk(&ha, (fused ? ST_HO : ST_H) | qks, &hp)) != GDP_OK) return st;
+    hp.qk = p.qk;
     // only the states chunk_o reads: the one entering each 64-token chunk.
     // Every segment starts on a 64-token boundary of its sequence, so
     // counting chunks per segment keeps the sequence's own c % M.
@@ -621,11 +641,16 @@ gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *pa, const gdp_chunk_args
     if (a->HV != a->H)
         return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_scan: prepare makes H value heads (HV=%d, H=%d)", a->HV, a->H);
     if (!a->g && a->T > 0) return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_scan: g is NULL (prepare writes it)");
+    if ((a->q == nullptr) != (a->k == nullptr))
+        return fail(GDP_ERR_INVALID, "gdp_prefill_fwd_scan: q and k must both be given or both be NULL");
+    if (a->q == nullptr && (a->v_new != nullptr || a->h != nullptr))
+        return fail(GDP_ERR_UNSUPPORTED,
+                    "gdp_prefill_fwd_scan: q and k may be NULL only with v_new and h NULL (one chunk_h + chunk_o pass)");
     gdp::PrepareParams pp;
     const gdp_status st = prepare_check("gdp_prefill_fwd_scan", false, pa->x, pa->x_n_stride, pa->x_t_stride, pa->ba,
                                         pa->ba_n_stride, pa->ba_t_stride, pa->A_log, pa->dt_bias, a->B, a->T, a->M,
                                         a->H, pa->G, a->V, a->K, a->dtype, (void *)a->q, (void *)a->k,
-                                        (void *)a->v, (float *)a->beta, (float *)a->g, &pp, true);
+                                        (void *)a->v, (float *)a->beta, (float *)a->g, &pp, true, true);
     if (st != GDP_OK) return st;
     if (pp.T > 0 && !pp.vec16)
         return fail(GDP_ERR_UNSUPPORTED, "gdp_prefill_fwd_scan: x rows and outputs must be 16-byte aligned");

@@ -73,9 +73,9 @@ struct HoStage {
 
 template <int KD, int VD>
 __global__ void __launch_bounds__(2 * NP * 64)
-gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
+gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
                const bf16 *__restrict__ u, const float *__restrict__ gcum, const float *__restrict__ k_rnorm,
-               const bf16 *__restrict__ q, const float *__restrict__ g, const int32_t *__restrict__ cu,
+               const float *__restrict__ g, const int32_t *__restrict__ cu,
                int64_t nseq, int64_t Ttok, int H, int HV, int M, const float *h0, float *ht,
                bf16 *__restrict__ o, int64_t uv_ss, float scale) {
     typedef bf16x8 FragT;
@@ -140,7 +140,9 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         }
         return;
     }
-    const int ldk = H * KD, ldw = HV * KD;  // global row strides (elements)
+    const int ldw = HV * KD;  // w row stride (elements)
+    // q and k rows by token and copy (the q and k tensors, or the activations)
+    const int64_t qkh = (int64_t)(hk / qk.hpg) * qk.hs;  // the key head's element offset in a row
     const int64_t r0 = bos * M;              // first expanded row of the sequence
     const int64_t bseq = cu ? 0 : seq;       // batch row of the sequence
     const int64_t TM = Ttok * M;
@@ -174,13 +176,14 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
         float gn = 0.f, gnn = 0.f;
         auto load_q = [&](int ti, FragT (&qf)[2][NKS], float &gn) {
             const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
-            const rsrc_t rq = make_rsrc(q + ((bos + (int64_t)C * ti) * H + hk) * KD, span(nt, ldk * ES, KD * ES));
+            const rsrc_t rq = make_rsrc((const bf16 *)qk.q + (bos + (int64_t)C * ti) * qk.q_ts + qkh,
+                                        span(nt, (int)qk.q_ts * ES, KD * ES));
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     qf[kw][ks] = __builtin_bit_cast(
-                        FragT, buf_load16(rq, (uint32_t)(((16 * tt + lc) * ldk + kw * KH + 32 * ks + 8 * lg) * ES)));
+                        FragT, buf_load16(rq, (uint32_t)(((16 * tt + lc) * (int)qk.q_ts + kw * KH + 32 * ks + 8 * lg) * ES)));
             gn = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
         };
         // scale/||q_t||, G_t of this lane's token and G of token `lane`, for
@@ -394,22 +397,35 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     constexpr int HALF = C * KH * ES;  // bytes of one half tile
     const bool rw = pp < 2;             // w (else K)
     const int hh = pp & 1;              // half of the tile's columns
-    const int ldt = rw ? ldw : ldk;
     // per-lane source offsets inside a chunk, less the DMA's offset in its
-    // 4 KiB M0 window
+    // 4 KiB M0 window; key rows are addressed by token and copy, so their
+    // row part is added per chunk (krel)
     uint32_t ot[UPR];
 #pragma unroll
     for (int i = 0; i < UPR; ++i) {
         const int r = i * RPI + lane / UPR;
         const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
-        ot[i] = (uint32_t)((r * ldt) * ES + hh * KH * ES + unit * 16 - 1024 * (i % 4));
+        ot[i] = (uint32_t)((rw ? r * ldw * ES : 0) + hh * KH * ES + unit * 16 - 1024 * (i % 4));
+    }
+    // element offset of expanded row e0 + r from the token holding row e0
+    auto krel = [&](int64_t e0, int r) {
+        const uint32_t e = (uint32_t)(e0 + r), tb = __umulhi((uint32_t)e0, mdiv), t = __umulhi(e, mdiv);
+        return (int64_t)(t - tb) * qk.k_ts + (int64_t)(e - t * (uint32_t)M) * qk.k_js;
+    };
+    // when M divides the chunk, every chunk starts on a token (r0 is one), so
+    // the key rows' offsets are the same for every chunk: made once here
+    const bool kfix = !rw && (C % M) == 0;
+    if (kfix) {
+#pragma unroll
+        for (int i = 0; i < UPR; ++i) ot[i] += (uint32_t)(krel(r0, i * RPI + lane / UPR) * ES);
     }
     uint32_t ou[NU];
 #pragma unroll
     for (int i = 0; i < NU; ++i) ou[i] = (uint32_t)((i * 64 + lane) * 16 - 1024 * (i % 4));
     const uint32_t o4 = (uint32_t)(lane * 4);
-    const char *pt = rw ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)(k + (r0 * H + hk) * KD);
-    const int64_t stt = (int64_t)C * ldt * ES;
+    const char *pt = rw ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)((const bf16 *)qk.k + qkh);
+    const int64_t stt = (int64_t)C * ldw * ES;
+    int64_t e_issue = r0;  // first expanded row of the next chunk to issue
     const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl, HV, VD, uv_ss));
     const int64_t stu = (int64_t)C * 16 * ES;
     const char *p4 = pp == 0 ? (const char *)(kdecay + h0r)
@@ -420,11 +436,16 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
     auto issue = [&](int st) {  // the next chunk into ring stage st (rows past the end read as zero)
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
         const uint32_t sb = ring_base + st * SB + tile_off;
-        const rsrc_t rt = make_rsrc(pt, span(n, ldt * ES, KD * ES));  // whole rows: the half is in the offsets
+        // whole rows: the half is in the offsets
+        const int64_t tb = (int64_t)__umulhi((uint32_t)e_issue, mdiv);
+        const uint32_t kspan = n > 0 ? __builtin_amdgcn_readfirstlane((uint32_t)(krel(e_issue, n - 1) * ES)) + KD * ES : 0u;
+        const rsrc_t rt = rw ? make_rsrc(pt, span(n, ldw * ES, KD * ES))
+                             : make_rsrc(pt + tb * qk.k_ts * ES, kspan);
         static_for<0, UPR>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i % 4 == 0) set_m0(sb + 1024 * i);
-            dma16_m0<1024 * (i % 4)>(rt, ot[i]);
+            const uint32_t kr_ = (rw || kfix) ? 0u : (uint32_t)(krel(e_issue, i * RPI + lane / UPR) * ES);
+            dma16_m0<1024 * (i % 4)>(rt, ot[i] + kr_);
         });
         const rsrc_t ru = make_rsrc(pu, (uint32_t)(n * 16 * ES));
         const uint32_t sbu = ring_base + st * SB + OFU + pp * (C * 16 * ES);
@@ -434,7 +455,8 @@ gdp_chunk_ho_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, con
             dma16_m0<1024 * (i % 4)>(ru, ou[i]);
         });
         if (pp < 3) dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
-        pt += stt;
+        if (rw) pt += stt;
+        e_issue += C;
         pu += stu;
         p4 += st4;
         rem_issue -= C;
@@ -595,8 +617,8 @@ static hipError_t launch_ho_t(const ChunkParams &p, hipStream_t stream) {
     const int64_t nblk = ((P + 7) / 8) * 8 * SG;
     if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gdp_chunk_ho_k<KD, VD>), dim3((unsigned)nblk), dim3(2 * NP * 64), 0, stream,
-                       (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.k_rnorm,
-                       (const bf16 *)a.q, a.g, a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.h0, a.ht, (bf16 *)a.o,
+                       p.qk, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.k_rnorm,
+                       a.g, a.cu_seqlens, p.nseq, a.T, a.H, a.HV, a.M, a.h0, a.ht, (bf16 *)a.o,
                        p.uv_ss, a.scale);
     return hipGetLastError();
 }

@@ -26,6 +26,19 @@ struct PrepareParams {
 hipError_t launch_prepare(const PrepareParams &p, hipStream_t stream);
 hipError_t launch_decode(const gdp_decode_args &a, hipStream_t stream);
 
+// Where the stages that read q and k by row (the segment maps and the fused
+// chunk_h + chunk_o pass) find them.  Key copy j of global token t for key
+// head hk starts at element  k_ts t + k_js j + (hk / hpg) hs  of k, and the
+// query of token t at  q_ts t + (hk / hpg) hs  of q.  By default these
+// describe the q [B, T, H, K] and k [B, T*M, H, K] tensors of the call; the
+// fused prefill with q and k not stored points them into the activations x
+// (query/key groups: hpg heads per group, segments of hs elements).
+struct QKRows {
+    const void *k = nullptr, *q = nullptr;
+    int64_t k_ts = 0, k_js = 0, q_ts = 0, hs = 0;
+    int hpg = 1;
+};
+
 // Validated chunk-stage arguments (scale resolved, nseq resolved).
 struct ChunkParams {
     gdp_chunk_args a;
@@ -39,6 +52,7 @@ struct ChunkParams {
     // chunk_h writes the state snapshot of chunk c (counted per sequence)
     // only when c % hstep == 0; 1 writes them all
     int hstep = 1;
+    QKRows qk;  // q and k rows for the segment maps and the fused pass
 };
 
 // Element offset of (batch row b, expanded row e relative to the batch row,

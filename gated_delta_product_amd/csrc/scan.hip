@@ -61,7 +61,7 @@ struct MapRing {
 // chunk's loads have two steps to land and hold no registers.
 template <int KD, int VD>
 __global__ void __launch_bounds__((KD + VD) * 2)
-gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
+gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
               const bf16 *__restrict__ u, const float *__restrict__ gcum, int64_t Ttok, int64_t seg_tok,
               int nmap, int H, int HV, int M, int64_t uv_ss, float *__restrict__ maps,
               const int32_t *__restrict__ seg_cu, const int32_t *__restrict__ seg_last) {
@@ -131,32 +131,51 @@ gdp_seg_map_k(const bf16 *__restrict__ k, const float *__restrict__ kdecay, cons
     // of the tile: lane L's 16 bytes at 1024 ii + 16 L hold unit (L mod UPR)
     // of row (1024 ii + 16 L) / RB after the swizzle, so the lane fetches the
     // source unit that the swizzle puts there.
-    const int64_t ldw_b = (int64_t)HV * KD * 2, ldk_b = (int64_t)H * KD * 2;  // row strides (bytes)
+    // Key rows are addressed by token and copy (QKRows: the k tensor or the
+    // activations), so their offsets are made per chunk: key copy j of token
+    // t sits t k_ts + j k_js elements from the key head's base; a chunk's
+    // offsets count from the token holding its first row
+    const int64_t ldw_b = (int64_t)HV * KD * 2;  // w row stride (bytes)
+    const uint32_t mdiv = small_div_magic(M);
+    const char *kbase = (const char *)qk.k + (int64_t)(hk / qk.hpg) * qk.hs * 2;
     uint32_t goff[NJ];
+    int krow[NJ];  // key tile: the lane's row
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
         const int i = wv + NW * jj;
+        krow[jj] = 0;
         if (i < 2 * NIT) {
             const int t = i / NIT, ii = i % NIT;
             const int byte = 1024 * ii + 16 * lane;
             const int r = byte / RB, us = (byte % RB) / 16;
-            goff[jj] = (uint32_t)(r * (t ? ldk_b : ldw_b) + 16 * ((us ^ r) & (UPR - 1)));
+            const uint32_t unit = (uint32_t)(16 * ((us ^ r) & (UPR - 1)));
+            goff[jj] = t ? unit : (uint32_t)(r * ldw_b) + unit;  // key rows: + the row's offset, per chunk
+            krow[jj] = r;
         } else {
             goff[jj] = (uint32_t)(1024 * ((i - 2 * NIT) % 2) + 16 * lane);
         }
     }
+    // element offset of expanded row e0 + r from the token holding row e0
+    auto krel = [&](int64_t e0, int r) {
+        const uint32_t e = (uint32_t)(e0 + r), tb = small_div((uint32_t)e0, mdiv);
+        const uint32_t t = small_div(e, mdiv);
+        return (int64_t)(t - tb) * qk.k_ts + (int64_t)(e - t * (uint32_t)M) * qk.k_js;
+    };
     auto issue = [&](int c, auto stc) {
         constexpr int st = decltype(stc)::value;
         const int64_t e0 = r0 + 64LL * c;
         const rsrc_t rw = make_rsrc(w + (e0 * HV + hv) * KD, (uint32_t)(63 * ldw_b + RB));
-        const rsrc_t rk = make_rsrc(k + (e0 * H + hk) * KD, (uint32_t)(63 * ldk_b + RB));
+        const int64_t tb = (int64_t)small_div((uint32_t)e0, mdiv);
+        const rsrc_t rk = make_rsrc(kbase + tb * qk.k_ts * 2,
+                                    (uint32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(krel(e0, 63) * 2)) + RB));
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj) {
             const int i = wv + NW * jj;  // wave-uniform
             if (i >= NI) break;
             if (i < 2 * NIT) {
                 const int t = i / NIT, ii = i % NIT;
-                dma16(t ? rk : rw, goff[jj], ring0 + (uint32_t)((t ? OK : OW) + st * TS + 1024 * ii));
+                const uint32_t off = t ? goff[jj] + (uint32_t)(krel(e0, krow[jj]) * 2) : goff[jj];
+                dma16(t ? rk : rw, off, ring0 + (uint32_t)((t ? OK : OW) + st * TS + 1024 * ii));
             } else {
                 const int iu = i - 2 * NIT, sl = iu / 2;  // slice sl, rows 32 (iu % 2) ..
                 const rsrc_t ru = make_rsrc(u + ((int64_t)hv * (VD / 16) + sl) * uv_ss + e0 * 16, 64 * 32);
@@ -516,7 +535,7 @@ static hipError_t launch_map_t(const ScanParams &sp, hipStream_t stream) {
     const int64_t nmap = packed ? sp.nseg : sp.nseg - 1;
     if (nmap <= 0) return hipSuccess;
     hipLaunchKernelGGL((gdp_seg_map_k<KD, VD>), dim3((unsigned)(nmap * a.HV)), dim3((KD + VD) * 2), 0, stream,
-                       (const bf16 *)a.k, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.T, sp.seg_tok,
+                       sp.p.qk, a.kdecay, (const bf16 *)a.w, (const bf16 *)a.u, a.gcum, a.T, sp.seg_tok,
                        (int)nmap, a.H, a.HV, a.M, sp.p.uv_ss, sp.maps, packed ? sp.cu : nullptr, sp.seg_last);
     return hipGetLastError();
 }

@@ -51,7 +51,8 @@ template <typename T> struct Pad { static constexpr int value = 16 / (int)sizeof
 // for them (q, k, v, beta, g, exactly as the prepare kernel does; q and g of
 // a token by the block holding its copy 0) and uses the same values.  v and
 // beta may be NULL: no later stage reads them (the values enter u here), so
-// they are then not stored.
+// they are then not stored.  q and k may be NULL together: the later stages
+// then read their rows from x, and they are neither stored nor (q) loaded.
 template <typename T>
 struct WyFuse {
     const T *x;
@@ -149,7 +150,8 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 const int64_t e = r0 + row, t = e / M;
                 const int j = (int)(e - t * M);
                 kreg[it] = *(const uint4 *)(fz.x + t * fz.xts + kb + ((int64_t)j * fz.G + grp) * KD + cu16 * E);
-                if (j == 0) qreg[it] = *(const uint4 *)(fz.x + t * fz.xts + qb + (int64_t)grp * KD + cu16 * E);
+                if (j == 0 && fz.q != nullptr)
+                    qreg[it] = *(const uint4 *)(fz.x + t * fz.xts + qb + (int64_t)grp * KD + cu16 * E);
             }
         }
         // the gates of the block's rows: beta per row, g per token (on its copy 0)
@@ -176,7 +178,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             const int uidx = tid + 256 * it, row = uidx / KUPR, cu16 = uidx % KUPR;
             const int64_t e = r0 + row, t = e / M;
             const int j = (int)(e - t * M);
-            if (row < n) {
+            if (row < n && fz.k != nullptr) {  // q and k may be NULL: the later stages then read x
                 *(uint4 *)(fz.k + (e * H + hv) * (int64_t)KD + cu16 * E) = kreg[it];
                 if (j == 0) *(uint4 *)(fz.q + (t * H + hv) * (int64_t)KD + cu16 * E) = qreg[it];  // once per token
             }

@@ -360,6 +360,20 @@ def test_prefill_scan_rejects():
     assert b"v is NULL" in B.lib().gdp_last_error()
     assert L.gdp_chunk_fwd_scan(a(beta=None), 2, ws, big, None, None) == B.GDP_ERR_INVALID
     assert b"beta is NULL" in B.lib().gdp_last_error()
+    # q and k: both NULL only with v_new and h NULL (then read from x; the
+    # call gets as far as the workspace check), never one of them alone
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(q=None, k=None, v_new=None, h=None), 2, ws, 64, None,
+                                  None) == B.GDP_ERR_INVALID
+    assert b"workspace" in B.lib().gdp_last_error()
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(q=None, k=None), 2, ws, big, None, None) == \
+        B.GDP_ERR_UNSUPPORTED
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(q=None, v_new=None, h=None), 2, ws, big, None, None) == \
+        B.GDP_ERR_INVALID
+    assert L.gdp_prefill_fwd_scan(ctypes.byref(pa), a(k=None, v_new=None, h=None), 2, ws, big, None, None) == \
+        B.GDP_ERR_INVALID
+    # the plain scan form has no activations to read them from
+    assert L.gdp_chunk_fwd_scan(a(q=None, k=None, v_new=None, h=None), 2, ws, big, None, None) == \
+        B.GDP_ERR_INVALID
 
 
 def test_scan_noalloc_rejects_before_any_hip_call():

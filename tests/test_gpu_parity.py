@@ -1148,7 +1148,8 @@ def test_prefill_scan_is_bit_identical(case):
     g and every chunk output, with an initial state, ragged tails, M = 1..3,
     GQA groups, and the timed workload (T = 32768, 16 heads, 16 segments).
     With v and beta passed as NULL they stay untouched and nothing else
-    changes."""
+    changes; in the one chunk_h + chunk_o pass the same holds for q and k,
+    whose rows the later stages then read from x."""
     T, M, H, G_, P, N, nseg = case
     d = synth.prepare_draws(1, T, M, H, G_, P, N, "bf16", synth.seed_of(4) + 300 + T % 97)
     x, ba, A_log, dt_bias = d["x"].to(DEV), d["ba"].to(DEV), d["A_log"].to(DEV), d["dt_bias"].to(DEV)
@@ -1180,3 +1181,24 @@ def test_prefill_scan_is_bit_identical(case):
             assert torch.equal(a_, b_), nm
     for nm in ("o", "w", "u", "v_new", "h", "ht", "k_rnorm", "gcum", "kdecay"):
         assert torch.equal(getattr(nv, nm), getattr(ref, nm)), "without v, beta: " + nm
+    if M < 2:
+        return  # the one-pass chunk_h + chunk_o form needs M >= 2
+    # one chunk_h + chunk_o pass: with q and k not stored (their rows read
+    # from x by the later stages) every output equals the run that stores
+    # them, and q and k stay untouched
+    runs = []
+    for store_qk in (True, False):
+        o3 = [torch.full_like(t, 7) for t in pre]
+        b3 = G.ChunkBuffers(*o3, initial_state=h0, output_final_state=True)
+        b3.prefill_scan(x, ba, A_log, dt_bias, G_, nseg, store_v_beta=False, store_vnew_h=False, store_qk=store_qk)
+        torch.cuda.synchronize()
+        runs.append((o3, b3))
+    (oq, bq), (ox, bx) = runs
+    for a_, b_, nm in zip(ox, pre, ("q", "k", "v", "beta", "g")):
+        if nm in ("q", "k", "v", "beta"):
+            assert bool((a_ == 7).all()), nm + " was written"
+        else:
+            assert torch.equal(a_, b_), nm
+    assert torch.equal(oq[0], pre[0]) and torch.equal(oq[1], pre[1]), "q, k stored"
+    for nm in ("o", "w", "u", "ht", "k_rnorm", "gcum", "kdecay"):
+        assert torch.equal(getattr(bx, nm), getattr(bq, nm)), "q, k read from x: " + nm
