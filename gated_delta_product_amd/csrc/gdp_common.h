@@ -46,6 +46,26 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// bf16 values as fp16: exact for magnitudes in fp16's normal range
+// [2^-14, 65504]; smaller ones go to fp16's subnormal grid (truncated), larger
+// ones saturate at 65504 (the conversion rounds toward zero, so it never
+// makes an infinity from a finite value)
+__device__ __forceinline__ f16x8 bf16_to_f16(bf16x8 a) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const u32x4 r = __builtin_bit_cast(u32x4, a);
+    f16x8 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_bit_cast(float, r[i] << 16), hi = __builtin_bit_cast(float, r[i] & 0xffff0000u);
+        const f16x2 h = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        out[2 * i] = h[0];
+        out[2 * i + 1] = h[1];
+    }
+    return out;
+}
+// an fp32 value as fp16, rounded to nearest, saturating at +-65504
+__device__ __forceinline__ f16 f16_sat(float x) { return (f16)__builtin_amdgcn_fmed3f(x, -65504.0f, 65504.0f); }
 __device__ __forceinline__ f32x4 mma(f32x8 a, f32x8 b, f32x4 c) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)

@@ -239,12 +239,14 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
             }
         }
         // phase 2: X = exp2(gl) X + K^T (kd ((u | 0) - P)), one half of the
-        // contraction (rows 32 s2 .. 32 s2 + 31 of the chunk) at a time.  The
-        // operand kd ((u | 0) - P) goes in as a high and a low bf16 part
-        // (split_lo), one product each, as in the chunk_h stage; vb[ct] holds
-        // rows 32s2 + 4lg + q (slots 0-3) and 32s2 + 16 + 4lg + q (4-7).
-        // Forming each half's operand just before its products keeps fewer
-        // registers live than forming both first.
+        // contraction (rows 32 s2 .. 32 s2 + 31 of the chunk) at a time, on
+        // fp16 operands: K^T converted from bf16 (exact in fp16's normal
+        // range) and the fp32 operand kd ((u | 0) - P) rounded to fp16 (11
+        // significant bits, saturating), one product per pair where two bf16
+        // parts would need two; vb[ct] holds rows 32s2 + 4lg + q (slots 0-3)
+        // and 32s2 + 16 + 4lg + q (4-7).  Forming each half's operand just
+        // before its products keeps fewer registers live than forming both
+        // first.
         const float gl = __builtin_amdgcn_exp2f(ring.gc[ST][63]);  // the chunk's decay (<= 1)
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
@@ -254,7 +256,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
                 for (int q = 0; q < 4; ++q) xs[kt][ct][q] *= gl;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 vb[2], vbl[2];
+            f16x8 vb[2];
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
                 const int rt = 2 * s2 + r2;
@@ -269,8 +271,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float x = ((float)uu[q] - acc[rt][ct][q]) * kd4[q];
-                        vb[ct][4 * r2 + q] = (bf16)x;
-                        vbl[ct][4 * r2 + q] = split_lo<bf16>(x, vb[ct][4 * r2 + q]);
+                        vb[ct][4 * r2 + q] = f16_sat(x);
                     }
                 }
             }
@@ -282,11 +283,9 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
                     (lds_i16x4 *)(pk + (ST * TS + 32 * s2 * RB))));
                 const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4 *)(pk + (ST * TS + (32 * s2 + 16) * RB))));
-                const bf16x8 a = join<bf16>(x0, x1);
+                const f16x8 a = bf16_to_f16(join<bf16>(x0, x1));
                 xs[kt][0] = mma(a, vb[0], xs[kt][0]);
-                xs[kt][0] = mma(a, vbl[0], xs[kt][0]);
                 xs[kt][1] = mma(a, vb[1], xs[kt][1]);
-                xs[kt][1] = mma(a, vbl[1], xs[kt][1]);
             }
         }
         pack();
