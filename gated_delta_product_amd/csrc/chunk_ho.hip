@@ -218,16 +218,19 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) sx[ct][kw][ks] = Sx[ct][kw][ks][lane];
             __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of the products
+            f32x4 a4[NP];  // the slices' chains interleaved, each in (kw, ks) order
 #pragma unroll
-            for (int ct = 0; ct < NP; ++ct) {
-                f32x4 a4 = zero4();
+            for (int ct = 0; ct < NP; ++ct) a4[ct] = zero4();
 #pragma unroll
-                for (int kw = 0; kw < 2; ++kw)
+            for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) a4 = mma(sx[ct][kw][ks], qf[kw][ks], a4);
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) oa[ct][r] = a4[r] * f;
-            }
+                    for (int ct = 0; ct < NP; ++ct) a4[ct] = mma(sx[ct][kw][ks], qf[kw][ks], a4[ct]);
+#pragma unroll
+            for (int ct = 0; ct < NP; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oa[ct][r] = a4[ct][r] * f;
         };
         auto store_o = [&](int ti) {
             const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
@@ -506,20 +509,23 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         const int ti = (int)__umulhi((uint32_t)c, mdiv);
         const int m = c - ti * M;
 
-        // ---- phase 1: the partial products of the two K halves (w h)
+        // ---- phase 1: the partial products of the two K halves (w h).
+        // Consecutive products go to different accumulators (each still sums
+        // its own products in ks order), so none waits for the one before.
         f32x4 acc[2][4];
 #pragma unroll
         for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                acc[kw][rt] = zero4();
-                const int r = 16 * rt + lc;
+            for (int rt = 0; rt < 4; ++rt) acc[kw][rt] = zero4();
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const FragT a = *(const FragT *)((const char *)Sg.w[kw] + swz(r, 32 * ks + 8 * lg));
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const FragT a = *(const FragT *)((const char *)Sg.w[kw] + swz(16 * rt + lc, 32 * ks + 8 * lg));
                     acc[kw][rt] = mma(a, hb[kw][ks], acc[kw][rt]);
                 }
-            }
         // every other read of the ring stage, before the barrier that frees
         // it: u, the key decays, the chunk's decay and K^T (read transposed,
         // ds_read_b64_tr_b16, rows in the state's permuted K order)
@@ -587,13 +593,17 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                 }
             }
             Vx[c & 1][pp][s][lane] = v8;
+            // every accumulator's high-part product, then every low-part one:
+            // each accumulator sums the same products in the same order, and
+            // consecutive products are independent
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) {
-                    hs[kw][kt] = mma(ka[kw][kt][s], vb[kw], hs[kw][kt]);
-                    hs[kw][kt] = mma(ka[kw][kt][s], vbl[kw], hs[kw][kt]);
-                }
+                for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = mma(ka[kw][kt][s], vb[kw], hs[kw][kt]);
+#pragma unroll
+            for (int kw = 0; kw < 2; ++kw)
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = mma(ka[kw][kt][s], vbl[kw], hs[kw][kt]);
         }
         pack();
         if (m == M - 1 && c + 1 < nch) publish_state();  // the state entering the next token chunk
