@@ -75,15 +75,12 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     constexpr int US = 64 * VD * 2;        // bytes per u tile
     constexpr int NIT = TS / 1024;         // 1 KiB DMA instructions per w or K tile
     constexpr int NIU = US / 1024;         // per u tile
-    constexpr int NI = 2 * NIT + NIU;      // per chunk, shared out over the waves
-    constexpr int NIW = NI / NW;           // issued by every wave (some issue one more)
-    constexpr int NJ = (NI + NW - 1) / NW; // instruction slots per wave
     constexpr int NS = 3;                  // ring stages: loads run two chunks ahead
     typedef MapRing<KD, VD, NS> Ring;
     constexpr int OW = (int)__builtin_offsetof(Ring, w), OK = (int)__builtin_offsetof(Ring, k);
     constexpr int OU = (int)__builtin_offsetof(Ring, u), OD = (int)__builtin_offsetof(Ring, kd);
     constexpr int OG = (int)__builtin_offsetof(Ring, gc);
-    static_assert(XW % 32 == 0 && NKS >= 1 && NIW >= 1, "shape");
+    static_assert(XW % 32 == 0 && NKS >= 1 && NIT >= NW, "shape");
     static_assert(2 * TS + 16 * RB * 3 < 65536 && 2 * US + US < 65536, "fragment offsets fit 16 bits");
 
     __shared__ __attribute__((aligned(16))) Ring ring;
@@ -126,66 +123,114 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     const uint32_t ou = (uint32_t)(OU + (is_e ? 2 * wv : 0) * 2048 + (4 * lg + (j >> 2)) * 32 + 8 * (j & 3));
     const uint32_t okd = (uint32_t)(OD + 16 * lg);
 
-    // ---- DMA slots of this wave: instruction i = wv + NW jj of a chunk.
-    // Instruction ii of a w or K tile fills LDS bytes [1024 ii, 1024 ii + 1024)
-    // of the tile: lane L's 16 bytes at 1024 ii + 16 L hold unit (L mod UPR)
-    // of row (1024 ii + 16 L) / RB after the swizzle, so the lane fetches the
-    // source unit that the swizzle puts there.
-    // Key rows are addressed by token and copy (QKRows: the k tensor or the
-    // activations), so their offsets are made per chunk: key copy j of token
-    // t sits t k_ts + j k_js elements from the key head's base; a chunk's
-    // offsets count from the token holding its first row
+    // ---- DMA slots of this wave: instructions wv, wv + NW, ... of the w
+    // tile, of the K tile and of the u tile of a chunk.  Instruction ii of a
+    // w or K tile fills LDS bytes [1024 ii, 1024 ii + 1024) of the tile: lane
+    // L's 16 bytes at 1024 ii + 16 L hold unit (L mod UPR) of row (1024 ii +
+    // 16 L) / RB after the swizzle, so the lane fetches the source unit that
+    // the swizzle puts there.  Key rows are addressed by token and copy
+    // (QKRows: the k tensor or the activations): key copy j of token t sits
+    // t k_ts + j k_js elements from the key head's base.
+    constexpr int NJT = (NIT + NW - 1) / NW;  // w (and K) slots per wave
+    constexpr int NJU = (NIU + NW - 1) / NW;  // u slots per wave
+    // loads every wave issues per chunk (some issue more): the ring waits
+    // count from this, which is exact or stricter for each wave
+    constexpr int MINC = 2 * (NIT / NW) + NIU / NW;
     const int64_t ldw_b = (int64_t)HV * KD * 2;  // w row stride (bytes)
     const uint32_t mdiv = small_div_magic(M);
     const char *kbase = (const char *)qk.k + (int64_t)(hk / qk.hpg) * qk.hs * 2;
-    uint32_t goff[NJ];
-    int krow[NJ];  // key tile: the lane's row
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-        const int i = wv + NW * jj;
-        krow[jj] = 0;
-        if (i < 2 * NIT) {
-            const int t = i / NIT, ii = i % NIT;
-            const int byte = 1024 * ii + 16 * lane;
-            const int r = byte / RB, us = (byte % RB) / 16;
-            const uint32_t unit = (uint32_t)(16 * ((us ^ r) & (UPR - 1)));
-            goff[jj] = t ? unit : (uint32_t)(r * ldw_b) + unit;  // key rows: + the row's offset, per chunk
-            krow[jj] = r;
-        } else {
-            goff[jj] = (uint32_t)(1024 * ((i - 2 * NIT) % 2) + 16 * lane);
-        }
-    }
     // element offset of expanded row e0 + r from the token holding row e0
     auto krel = [&](int64_t e0, int r) {
         const uint32_t e = (uint32_t)(e0 + r), tb = small_div((uint32_t)e0, mdiv);
         const uint32_t t = small_div(e, mdiv);
         return (int64_t)(t - tb) * qk.k_ts + (int64_t)(e - t * (uint32_t)M) * qk.k_js;
     };
+    // when M divides the chunk every chunk starts on a token (r0 is one), so
+    // the key rows' offsets are the same for every chunk: made once here
+    const bool kfix = (64 % M) == 0;
+    uint32_t ow[NJT], okk[NJT];
+    int krow[NJT];
+#pragma unroll
+    for (int jj = 0; jj < NJT; ++jj) {
+        const int byte = 1024 * (wv + NW * jj) + 16 * lane;
+        const int r = byte / RB, us = (byte % RB) / 16;
+        const uint32_t unit = (uint32_t)(16 * ((us ^ r) & (UPR - 1)));
+        ow[jj] = (uint32_t)(r * ldw_b) + unit;
+        okk[jj] = unit + (kfix ? (uint32_t)(krel(r0, r) * 2) : 0u);
+        krow[jj] = r;
+    }
+    const char *pw = (const char *)(w + (r0 * HV + hv) * KD);  // chunk 0's rows
+    const int64_t stw = 64 * ldw_b;
+    const char *pkf = kbase + (int64_t)small_div((uint32_t)r0, mdiv) * qk.k_ts * 2;  // kfix: chunk 0's token
+    const int64_t stk = kfix ? (int64_t)(64 / M) * qk.k_ts * 2 : 0;
+    const uint32_t kspan_fix = kfix ? __builtin_amdgcn_readfirstlane((uint32_t)(krel(r0, 63) * 2)) + RB : 0u;
+    // u instruction iu: slice iu / 2, rows 32 (iu % 2) .. + 31
+    const char *pu[NJU];
+#pragma unroll
+    for (int jj = 0; jj < NJU; ++jj)
+        pu[jj] = (const char *)(u + ((int64_t)hv * (VD / 16) + (wv + NW * jj) / 2) * uv_ss + r0 * 16);
+    const uint32_t ouu = (uint32_t)(16 * lane);
     auto issue = [&](int c, auto stc) {
         constexpr int st = decltype(stc)::value;
-        const int64_t e0 = r0 + 64LL * c;
-        const rsrc_t rw = make_rsrc(w + (e0 * HV + hv) * KD, (uint32_t)(63 * ldw_b + RB));
-        const int64_t tb = (int64_t)small_div((uint32_t)e0, mdiv);
-        const rsrc_t rk = make_rsrc(kbase + tb * qk.k_ts * 2,
-                                    (uint32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(krel(e0, 63) * 2)) + RB));
-#pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-            const int i = wv + NW * jj;  // wave-uniform
-            if (i >= NI) break;
-            if (i < 2 * NIT) {
-                const int t = i / NIT, ii = i % NIT;
-                const uint32_t off = t ? goff[jj] + (uint32_t)(krel(e0, krow[jj]) * 2) : goff[jj];
-                dma16(t ? rk : rw, off, ring0 + (uint32_t)((t ? OK : OW) + st * TS + 1024 * ii));
-            } else {
-                const int iu = i - 2 * NIT, sl = iu / 2;  // slice sl, rows 32 (iu % 2) ..
-                const rsrc_t ru = make_rsrc(u + ((int64_t)hv * (VD / 16) + sl) * uv_ss + e0 * 16, 64 * 32);
-                dma16(ru, goff[jj], ring0 + (uint32_t)(OU + st * US + 2048 * sl + 1024 * (iu % 2)));
-            }
+        const rsrc_t rw = make_rsrc(pw + c * stw, (uint32_t)(63 * ldw_b + RB));
+        static_for<0, NJT>([&](auto jc) {
+            constexpr int jj = decltype(jc)::value;
+            const int ii = wv + NW * jj;  // wave-uniform
+            if (NIT % NW == 0 || ii < NIT) dma16(rw, ow[jj], ring0 + (uint32_t)(OW + st * TS + 1024 * ii));
+        });
+        if (kfix) {
+            const rsrc_t rk = make_rsrc(pkf + c * stk, kspan_fix);
+            static_for<0, NJT>([&](auto jc) {
+                constexpr int jj = decltype(jc)::value;
+                const int ii = wv + NW * jj;
+                if (NIT % NW == 0 || ii < NIT) dma16(rk, okk[jj], ring0 + (uint32_t)(OK + st * TS + 1024 * ii));
+            });
+        } else {
+            const int64_t e0 = r0 + 64LL * c;
+            const int64_t tb = (int64_t)small_div((uint32_t)e0, mdiv);
+            const rsrc_t rk = make_rsrc(kbase + tb * qk.k_ts * 2,
+                                        (uint32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(krel(e0, 63) * 2)) + RB));
+            static_for<0, NJT>([&](auto jc) {
+                constexpr int jj = decltype(jc)::value;
+                const int ii = wv + NW * jj;
+                if (NIT % NW == 0 || ii < NIT)
+                    dma16(rk, okk[jj] + (uint32_t)(krel(e0, krow[jj]) * 2),
+                          ring0 + (uint32_t)(OK + st * TS + 1024 * ii));
+            });
         }
+        static_for<0, NJU>([&](auto jc) {
+            constexpr int jj = decltype(jc)::value;
+            const int iu = wv + NW * jj;
+            if (NIU % NW == 0 || iu < NIU)
+                dma16(make_rsrc(pu[jj] + c * 2048, 2048), ouu + (uint32_t)(1024 * (iu % 2)),
+                      ring0 + (uint32_t)(OU + st * US + 2048 * (iu / 2) + 1024 * (iu % 2)));
+        });
+        const int64_t e0 = r0 + 64LL * c;
         if (wv == 0)
             dma4(make_rsrc(kdecay + (int64_t)hv * TM + e0, 256), (uint32_t)(4 * lane), ring0 + OD + st * 256);
         if (wv == NW - 1)
             dma4(make_rsrc(gcum + (int64_t)hv * TM + e0, 256), (uint32_t)(4 * lane), ring0 + OG + st * 256);
+    };
+    // this wave's loads of the chunk before the last issue have landed
+    auto wait_ring = [&]() {
+        if (wv == 0 || wv == NW - 1)
+            wait_vmcnt<MINC + 1>();
+        else
+            wait_vmcnt<MINC>();
+    };
+    // the K blocks this wave loaded into ring stage st, bf16 -> fp16 in place
+    // (phase 2 takes K^T as fp16; every wave reads the whole tile, so each
+    // converts only its own share, once)
+    auto convert_k = [&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        static_for<0, NJT>([&](auto jc) {
+            constexpr int jj = decltype(jc)::value;
+            const int ii = wv + NW * jj;
+            if (NIT % NW == 0 || ii < NIT) {
+                bf16x8 *p = (bf16x8 *)((char *)&ring + OK + st * TS + 1024 * ii + 16 * lane);
+                *p = __builtin_bit_cast(bf16x8, bf16_to_f16(*p));
+            }
+        });
     };
 
     // X = [0 | I]
@@ -240,7 +285,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
         }
         // phase 2: X = exp2(gl) X + K^T (kd ((u | 0) - P)), one half of the
         // contraction (rows 32 s2 .. 32 s2 + 31 of the chunk) at a time, on
-        // fp16 operands: K^T converted from bf16 (exact in fp16's normal
+        // fp16 operands: K^T as converted in the ring (exact in fp16's normal
         // range) and the fp32 operand kd ((u | 0) - P) rounded to fp16 (11
         // significant bits, saturating), one product per pair where two bf16
         // parts would need two; vb[ct] holds rows 32s2 + 4lg + q (slots 0-3)
@@ -283,17 +328,21 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
                     (lds_i16x4 *)(pk + (ST * TS + 32 * s2 * RB))));
                 const bf16x4 x1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4 *)(pk + (ST * TS + (32 * s2 + 16) * RB))));
-                const f16x8 a = bf16_to_f16(join<bf16>(x0, x1));
+                const f16x8 a = __builtin_bit_cast(f16x8, join<bf16>(x0, x1));
                 xs[kt][0] = mma(a, vb[0], xs[kt][0]);
                 xs[kt][1] = mma(a, vb[1], xs[kt][1]);
             }
         }
+        // chunk c + 1: this wave's loads have landed (all but this step's
+        // own), and its key blocks go to fp16 for the next step
+        if (c + 1 < nch) {
+            if (more)
+                wait_ring();
+            else
+                wait_vmcnt<0>();
+            convert_k(std::integral_constant<int, (ST + 1) % NS>{});
+        }
         pack();
-        // chunk c + 1 landed: wait for all but this step's own DMAs
-        if (more)
-            wait_vmcnt<NIW>();
-        else
-            wait_vmcnt<0>();
         lds_barrier();  // orders LDS only: the DMAs of chunk c + 2 stay in flight
     };
 
@@ -303,6 +352,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     issue(0, I0{});
     if (nch > 1) issue(1, I1{});
     wait_vmcnt<0>();
+    convert_k(I0{});
     lds_barrier();
     for (int c = 0; c < nch; c += 3) {
         step(c, I0{});

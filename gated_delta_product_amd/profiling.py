@@ -94,13 +94,14 @@ def traffic(fetch_csv, write_csv, copy_mib):
     return res
 
 
-MFMA_PEAK = {"MfmaFlopsBF16": 2.5e15, "MfmaFlopsF32": 157.3e12}  # MI355X dense peaks (flop/s)
+MFMA_PEAK = {"MfmaFlopsBF16": 2.5e15, "MfmaFlopsF16": 2.5e15, "MfmaFlopsF32": 157.3e12}  # MI355X dense peaks (flop/s)
 
 
 def mfma_table(pmc_csv):
-    """Per kernel: matrix-core flops per launch (rocprofv3's MfmaFlopsBF16 /
-    MfmaFlopsF32, i.e. MOPS x 512), the MfmaUtil busy percentage, and the
-    rate over the profiled launch duration against the dense peak."""
+    """Per kernel: matrix-core flops per launch (rocprofv3's MfmaFlopsBF16,
+    MfmaFlopsF16 and MfmaFlopsF32, i.e. MOPS x 512; a counter the run did not
+    take reads as zero), the MfmaUtil busy percentage, and the rate over the
+    profiled launch duration against each dtype's dense peak."""
     acc = defaultdict(lambda: defaultdict(list))
     dur = defaultdict(list)
     with open(pmc_csv) as f:
@@ -111,19 +112,22 @@ def mfma_table(pmc_csv):
             acc[op][r["Counter_Name"]].append(float(r["Counter_Value"]))
             if r["Counter_Name"] == "MfmaUtil":
                 dur[op].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
-    lines = ["| kernel | launches | bf16 MFMA GFLOP | f32 MFMA GFLOP | profiled us | MFMA TFLOP/s | fraction of dense peak | MfmaUtil % |",
-             "|---|---|---|---|---|---|---|---|"]
+    lines = ["| kernel | launches | bf16 MFMA GFLOP | f16 MFMA GFLOP | f32 MFMA GFLOP | profiled us | MFMA TFLOP/s "
+             "| fraction of dense peak | MfmaUtil % |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for op in KERNELS:
         if op not in acc:
             continue
         d = acc[op]
         mean = lambda k: sum(d.get(k, [0.0])) / max(1, len(d.get(k, [0.0])))
-        bf, f32, util = mean("MfmaFlopsBF16"), mean("MfmaFlopsF32"), mean("MfmaUtil")
+        fl = {k: mean(k) for k in MFMA_PEAK}
+        util = mean("MfmaUtil")
         t = sum(dur[op]) / max(1, len(dur[op]))
-        rate = (bf + f32) / t if t > 0 else 0.0
-        frac = (bf / t / MFMA_PEAK["MfmaFlopsBF16"] + f32 / t / MFMA_PEAK["MfmaFlopsF32"]) if t > 0 else 0.0
-        lines.append("| %s | %d | %.2f | %.2f | %.1f | %.1f | %.3f | %.1f |" % (
-            op, len(d.get("MfmaUtil", [])), bf / 1e9, f32 / 1e9, t * 1e6, rate / 1e12, frac, util))
+        rate = sum(fl.values()) / t if t > 0 else 0.0
+        frac = sum(fl[k] / t / MFMA_PEAK[k] for k in MFMA_PEAK) if t > 0 else 0.0
+        lines.append("| %s | %d | %.2f | %.2f | %.2f | %.1f | %.1f | %.3f | %.1f |" % (
+            op, len(d.get("MfmaUtil", [])), fl["MfmaFlopsBF16"] / 1e9, fl["MfmaFlopsF16"] / 1e9,
+            fl["MfmaFlopsF32"] / 1e9, t * 1e6, rate / 1e12, frac, util))
     return "\n".join(lines)
 
 
@@ -167,9 +171,10 @@ def main(argv=None):
     if a.cmd == "mfma":
         digests = ", ".join("%s %s" % (op, src_digest(op)) for op in KERNELS)
         text = ("# %s\n\nCommand (run from the repository root on one MI355X):\n\n    %s\n\n%s\n\n"
-                "MFMA flops are rocprofv3's MfmaFlopsBF16 / MfmaFlopsF32 (matrix-core operations x 512, "
-                "dense tiles as issued); the fraction sums each dtype's rate over its dense peak "
-                "(bf16 2.5 PFLOP/s, f32 157.3 TFLOP/s); durations are the profiled launches.\n\n"
+                "MFMA flops are rocprofv3's MfmaFlopsBF16 / MfmaFlopsF16 / MfmaFlopsF32 (matrix-core "
+                "operations x 512, dense tiles as issued); the fraction sums each dtype's rate over its "
+                "dense peak (bf16 and f16 2.5 PFLOP/s, f32 157.3 TFLOP/s); durations are the profiled "
+                "launches.\n\n"
                 "Kernel source digests: %s\n" % (a.title, a.command, mfma_table(a.pmc_csv), digests))
         with open(a.out, "w") as f:
             f.write(text)
