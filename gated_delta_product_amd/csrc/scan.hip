@@ -80,7 +80,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     constexpr int OW = (int)__builtin_offsetof(Ring, w), OK = (int)__builtin_offsetof(Ring, k);
     constexpr int OU = (int)__builtin_offsetof(Ring, u), OD = (int)__builtin_offsetof(Ring, kd);
     constexpr int OG = (int)__builtin_offsetof(Ring, gc);
-    static_assert(XW % 32 == 0 && NKS >= 1 && NIT >= NW, "shape");
+    static_assert(XW % 64 == 0 && NKS >= 1 && NIT >= NW, "shape: an even number of waves");
     static_assert(2 * TS + 16 * RB * 3 < 65536 && 2 * US + US < 65536, "fragment offsets fit 16 bits");
 
     __shared__ __attribute__((aligned(16))) Ring ring;
@@ -101,6 +101,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     const int lane = lane_id(), wv = wave_id();
     const int lg = lane >> 4, lc = lane & 15, j = lane & 15;
     const bool is_e = 32 * wv < VD;               // wave-uniform
+    const float ue = is_e ? 1.f : 0.f;            // weight of u in the wave's columns
     const uint32_t ring0 = lds_addr(&ring);
     const char *lds = (const char *)&ring;
 
@@ -159,61 +160,65 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
         okk[jj] = unit + (kfix ? (uint32_t)(krel(r0, r) * 2) : 0u);
         krow[jj] = r;
     }
-    const char *pw = (const char *)(w + (r0 * HV + hv) * KD);  // chunk 0's rows
+    // LDS destinations of this wave's slots in stage 0 (slot jj adds
+    // 1024 NW jj, stage st adds st TS or st US); u instruction iu fills bytes
+    // [1024 iu, 1024 iu + 1024) of the u tile: slice iu / 2, rows 32 (iu % 2) ..
+    const uint32_t mw = ring0 + (uint32_t)(OW + 1024 * wv), mk = ring0 + (uint32_t)(OK + 1024 * wv);
+    const uint32_t mu = ring0 + (uint32_t)(OU + 1024 * wv);
+    // sources of the next chunk to issue, advanced by each issue (NW is even,
+    // so slot jj of the u tile is slice wv / 2 + jj NW / 2, same half)
+    const char *pw = (const char *)(w + (r0 * HV + hv) * KD);
     const int64_t stw = 64 * ldw_b;
-    const char *pkf = kbase + (int64_t)small_div((uint32_t)r0, mdiv) * qk.k_ts * 2;  // kfix: chunk 0's token
+    const char *pkf = kbase + (int64_t)small_div((uint32_t)r0, mdiv) * qk.k_ts * 2;  // kfix: the chunk's first token
     const int64_t stk = kfix ? (int64_t)(64 / M) * qk.k_ts * 2 : 0;
     const uint32_t kspan_fix = kfix ? __builtin_amdgcn_readfirstlane((uint32_t)(krel(r0, 63) * 2)) + RB : 0u;
-    // u instruction iu: slice iu / 2, rows 32 (iu % 2) .. + 31
-    const char *pu[NJU];
-#pragma unroll
-    for (int jj = 0; jj < NJU; ++jj)
-        pu[jj] = (const char *)(u + ((int64_t)hv * (VD / 16) + (wv + NW * jj) / 2) * uv_ss + r0 * 16);
-    const uint32_t ouu = (uint32_t)(16 * lane);
-    auto issue = [&](int c, auto stc) {
+    int64_t e_issue = r0;  // first expanded row of the next chunk (per-chunk key offsets)
+    const char *pu = (const char *)(u + ((int64_t)hv * (VD / 16) + wv / 2) * uv_ss + r0 * 16);
+    const int64_t du = (int64_t)(NW / 2) * uv_ss * 2;
+    const uint32_t ouu = (uint32_t)(1024 * (wv & 1) + 16 * lane);
+    // waves 0 and 1 also load the per-row key decays and cumulative decays
+    const char *p4 = (const char *)((wv == 0 ? kdecay : gcum) + (int64_t)hv * TM + r0);
+    const uint32_t m4 = ring0 + (uint32_t)(wv == 0 ? OD : OG);
+    auto issue = [&](auto stc) {
         constexpr int st = decltype(stc)::value;
-        const rsrc_t rw = make_rsrc(pw + c * stw, (uint32_t)(63 * ldw_b + RB));
+        const rsrc_t rw = make_rsrc(pw, (uint32_t)(63 * ldw_b + RB));
         static_for<0, NJT>([&](auto jc) {
             constexpr int jj = decltype(jc)::value;
-            const int ii = wv + NW * jj;  // wave-uniform
-            if (NIT % NW == 0 || ii < NIT) dma16(rw, ow[jj], ring0 + (uint32_t)(OW + st * TS + 1024 * ii));
+            if (NIT % NW == 0 || wv + NW * jj < NIT) dma16_at(rw, ow[jj], mw, st * TS + 1024 * NW * jj);
         });
         if (kfix) {
-            const rsrc_t rk = make_rsrc(pkf + c * stk, kspan_fix);
+            const rsrc_t rk = make_rsrc(pkf, kspan_fix);
             static_for<0, NJT>([&](auto jc) {
                 constexpr int jj = decltype(jc)::value;
-                const int ii = wv + NW * jj;
-                if (NIT % NW == 0 || ii < NIT) dma16(rk, okk[jj], ring0 + (uint32_t)(OK + st * TS + 1024 * ii));
+                if (NIT % NW == 0 || wv + NW * jj < NIT) dma16_at(rk, okk[jj], mk, st * TS + 1024 * NW * jj);
             });
-        } else {
-            const int64_t e0 = r0 + 64LL * c;
-            const int64_t tb = (int64_t)small_div((uint32_t)e0, mdiv);
-            const rsrc_t rk = make_rsrc(kbase + tb * qk.k_ts * 2,
-                                        (uint32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(krel(e0, 63) * 2)) + RB));
+        } else {  // M does not divide the chunk, so M >= 3 and the divisor's magic is not 0
+            const uint32_t e0 = (uint32_t)e_issue, tb = __umulhi(e0, mdiv);
+            auto kr = [&](int r) {
+                const uint32_t e = e0 + (uint32_t)r, t = __umulhi(e, mdiv);
+                return (uint32_t)(((int64_t)(t - tb) * qk.k_ts + (int64_t)(e - t * (uint32_t)M) * qk.k_js) * 2);
+            };
+            const rsrc_t rk = make_rsrc(kbase + (int64_t)tb * qk.k_ts * 2, __builtin_amdgcn_readfirstlane(kr(63)) + RB);
             static_for<0, NJT>([&](auto jc) {
                 constexpr int jj = decltype(jc)::value;
-                const int ii = wv + NW * jj;
-                if (NIT % NW == 0 || ii < NIT)
-                    dma16(rk, okk[jj] + (uint32_t)(krel(e0, krow[jj]) * 2),
-                          ring0 + (uint32_t)(OK + st * TS + 1024 * ii));
+                if (NIT % NW == 0 || wv + NW * jj < NIT) dma16_at(rk, okk[jj] + kr(krow[jj]), mk, st * TS + 1024 * NW * jj);
             });
         }
         static_for<0, NJU>([&](auto jc) {
             constexpr int jj = decltype(jc)::value;
-            const int iu = wv + NW * jj;
-            if (NIU % NW == 0 || iu < NIU)
-                dma16(make_rsrc(pu[jj] + c * 2048, 2048), ouu + (uint32_t)(1024 * (iu % 2)),
-                      ring0 + (uint32_t)(OU + st * US + 2048 * (iu / 2) + 1024 * (iu % 2)));
+            if (NIU % NW == 0 || wv + NW * jj < NIU)
+                dma16_at(make_rsrc(pu + jj * du, 2048), ouu, mu, st * US + 1024 * NW * jj);
         });
-        const int64_t e0 = r0 + 64LL * c;
-        if (wv == 0)
-            dma4(make_rsrc(kdecay + (int64_t)hv * TM + e0, 256), (uint32_t)(4 * lane), ring0 + OD + st * 256);
-        if (wv == NW - 1)
-            dma4(make_rsrc(gcum + (int64_t)hv * TM + e0, 256), (uint32_t)(4 * lane), ring0 + OG + st * 256);
+        if (wv < 2) dma4_at(make_rsrc(p4, 256), (uint32_t)(4 * lane), m4, st * 256);
+        pw += stw;
+        pkf += stk;
+        e_issue += 64;
+        pu += 2048;
+        p4 += 256;
     };
     // this wave's loads of the chunk before the last issue have landed
     auto wait_ring = [&]() {
-        if (wv == 0 || wv == NW - 1)
+        if (wv < 2)
             wait_vmcnt<MINC + 1>();
         else
             wait_vmcnt<MINC>();
@@ -265,7 +270,7 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     auto step = [&](int c, auto stc) {
         constexpr int ST = decltype(stc)::value;
         const bool more = c + 2 < nch;  // uniform
-        if (more) issue(c + 2, std::integral_constant<int, (ST + 2) % NS>{});
+        if (more) issue(std::integral_constant<int, (ST + 2) % NS>{});
 
         // phase 1: P = w X (64 x 32), contraction order of xb
         f32x4 acc[4][2];
@@ -308,14 +313,14 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
                 const f32x4 kd4 = *(const f32x4 *)(lds + okd + (ST * 256 + rt * 64));
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    bf16x4 uu = bf16x4{};
-                    if (is_e)
-                        uu = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(lds + ou) +
-                                          (ST * US + ct * 2048 + rt * 512))));
+                    // every wave reads a u slice (the D waves' reads are
+                    // weighted by 0), so no branch splits the step
+                    const bf16x4 uu = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(lds + ou) +
+                                      (ST * US + ct * 2048 + rt * 512))));
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float x = ((float)uu[q] - acc[rt][ct][q]) * kd4[q];
+                        const float x = __builtin_fmaf((float)uu[q], ue, -acc[rt][ct][q]) * kd4[q];
                         vb[ct][4 * r2 + q] = f16_sat(x);
                     }
                 }
@@ -349,8 +354,8 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    issue(0, I0{});
-    if (nch > 1) issue(1, I1{});
+    issue(I0{});
+    if (nch > 1) issue(I1{});
     wait_vmcnt<0>();
     convert_k(I0{});
     lds_barrier();
