@@ -515,16 +515,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             }
         // gl <= 0; rows past the end carry key decay 0
         const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;
-        // everything that does not need the partner's partial, before the
-        // barrier: u - own partial, its key-decayed copy, the decayed state
-        f32x4 ua[4], uk[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                ua[rt][q] = to_f32(uu[rt][q]) - acc[rt][q];
-                uk[rt][q] = ua[rt][q] * kd4[rt][q];
-            }
+        // the decayed state, before the barrier
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
@@ -538,9 +529,11 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
         for (int rt = 0; rt < 4; ++rt) Xs[xb][pp][kw][rt][lane] = acc[rt];
         lds_barrier();
 
-        // v_new = (u - own) - other; the phase-2 operand kd * v_new as one
-        // fused multiply-add on the precomputed kd * (u - own), in bf16 as
-        // a high and a low part (split_lo), one product each
+        // v_new = u - (P0 + P1), the two halves' partials summed (the sum
+        // is the same in both waves, addition being commutative), and the
+        // phase-2 operand kd * v_new, in bf16 as a high and a low part
+        // (split_lo), one product each; no contraction, so every form of
+        // the stage rounds the same operations
         FragT vb[2], vbl[2];
         T *vt = Vt[c & 1][pp];
         static_for<0, 4>([&](auto rtc) {
@@ -549,8 +542,10 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             HalfT v4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                v4[q] = from_f32<T>(ua[rt][q] - other[q]);
-                const float x = __builtin_fmaf(-other[q], kd4[rt][q], uk[rt][q]);
+#pragma clang fp contract(off)
+                const float v = to_f32(uu[rt][q]) - (acc[rt][q] + other[q]);
+                v4[q] = from_f32<T>(v);
+                const float x = v * kd4[rt][q];
                 vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x);
                 if constexpr (Split<T>::on) vbl[rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x, vb[rt >> 1][4 * (rt & 1) + q]);
             }
@@ -596,10 +591,9 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     if constexpr (FK) {
     // ============ compute waves, whole-K form (one wave per slice) ============
     // The same arithmetic as the split form above, in the same order, so the
-    // bits match: the two K halves' phase-1 partials P0, P1 stay apart; v_new
-    // rows [32kw, 32kw + 32) are (u - P_kw) - P_other, and half kw's phase-2
-    // operand is fma(-P_other, kd, (u - P_kw) kd).  No exchange buffer and no
-    // partner: the one barrier per chunk stays where the split form has it.
+    // bits match: the two K halves' phase-1 partials P0, P1 are formed apart
+    // and v_new = u - (P0 + P1).  No exchange buffer and no partner: the one
+    // barrier per chunk stays where the split form has it.
     auto compute_fk = [&](auto wc) {
     constexpr int pp = decltype(wc)::value;  // slice of the block
     f32x4 hs[2][NKT];
@@ -691,26 +685,19 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                 for (int q = 0; q < 4; ++q) hs[kw][kt][q] *= gl;
         lds_barrier();  // publishes the next stage; Vt[c & 1] is free again
 
-        FragT vb[2][2], vbl[2][2];  // phase-2 operands: high and low bf16 parts
+        FragT vb[2], vbl[2];  // phase-2 operands: high and low bf16 parts
         T *vt = Vt[c & 1][pp];
         static_for<0, 4>([&](auto rtc) {
             constexpr int rt = decltype(rtc)::value;
-            constexpr int ho = rt >> 1;  // the half whose rows these are
             HalfT v4;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float u = to_f32(uu[rt][q]);
-                const float ua0 = u - acc[0][rt][q], ua1 = u - acc[1][rt][q];
-                const float uk0 = ua0 * kd4[rt][q], uk1 = ua1 * kd4[rt][q];
-                v4[q] = from_f32<T>(ho == 0 ? ua0 - acc[1][rt][q] : ua1 - acc[0][rt][q]);
-                const float x0 = __builtin_fmaf(-acc[1][rt][q], kd4[rt][q], uk0);
-                const float x1 = __builtin_fmaf(-acc[0][rt][q], kd4[rt][q], uk1);
-                vb[0][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x0);
-                vb[1][rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x1);
-                if constexpr (Split<T>::on) {
-                    vbl[0][rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x0, vb[0][rt >> 1][4 * (rt & 1) + q]);
-                    vbl[1][rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x1, vb[1][rt >> 1][4 * (rt & 1) + q]);
-                }
+#pragma clang fp contract(off)
+                const float v = to_f32(uu[rt][q]) - (acc[0][rt][q] + acc[1][rt][q]);
+                v4[q] = from_f32<T>(v);
+                const float x = v * kd4[rt][q];
+                vb[rt >> 1][4 * (rt & 1) + q] = from_f32<T>(x);
+                if constexpr (Split<T>::on) vbl[rt >> 1][4 * (rt & 1) + q] = split_lo<T>(x, vb[rt >> 1][4 * (rt & 1) + q]);
             }
             *(HalfT *)(&vt[lc * LDT + 16 * rt + 4 * lg]) = v4;
         });
@@ -722,8 +709,8 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    hs[kw][kt] = mma(ka[kw][kt][s], vb[kw][s], hs[kw][kt]);
-                    if constexpr (Split<T>::on) hs[kw][kt] = mma(ka[kw][kt][s], vbl[kw][s], hs[kw][kt]);
+                    hs[kw][kt] = mma(ka[kw][kt][s], vb[s], hs[kw][kt]);
+                    if constexpr (Split<T>::on) hs[kw][kt] = mma(ka[kw][kt][s], vbl[s], hs[kw][kt]);
                 }
         pack();
         if (c + 1 < nch) put_snapshot(c + 1);  // the state entering chunk c + 1

@@ -565,31 +565,27 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         wait_ring();    // chunk c + 1 landed
         lds_barrier();  // ring stage c read; the exchanges of chunk c - 1 were read
 
-        // ---- v_new (published to the exchange as bf16) and the phase-2
-        // operands, with the arithmetic of the chunk_h stage's whole-K form,
-        // then phase 2, h = exp2(gl) h + K^T (kd * v_new), one key half s
-        // (rows 32 s .. 32 s + 31) at a time; every accumulator sees the same
-        // products in the same order as there, so the states agree bit for
-        // bit
+        // ---- v_new (published to the exchange as fp16) and the phase-2
+        // operands, with the arithmetic of the chunk_h stage's whole-K form
+        // (v_new = u - (P0 + P1), no contraction), then phase 2, h = exp2(gl)
+        // h + K^T (kd * v_new), one key half s (rows 32 s .. 32 s + 31) at a
+        // time; every accumulator sees the same products in the same order as
+        // there, so the states agree bit for bit
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            FragT vb[2], vbl[2];
+            FragT vb, vbl;
             f16x8 v8;
 #pragma unroll
             for (int r2 = 0; r2 < 2; ++r2) {
                 const int rt = 2 * s + r2;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float uf = (float)uu[rt][r];
-                    const float ua0 = uf - acc[0][rt][r], ua1 = uf - acc[1][rt][r];
-                    const float uk0 = ua0 * kd4[rt][r], uk1 = ua1 * kd4[rt][r];
-                    v8[4 * r2 + r] = (f16)(s == 0 ? ua0 - acc[1][rt][r] : ua1 - acc[0][rt][r]);
-                    const float x0 = __builtin_fmaf(-acc[1][rt][r], kd4[rt][r], uk0);
-                    const float x1 = __builtin_fmaf(-acc[0][rt][r], kd4[rt][r], uk1);
-                    vb[0][4 * r2 + r] = (bf16)x0;
-                    vb[1][4 * r2 + r] = (bf16)x1;
-                    vbl[0][4 * r2 + r] = split_lo<bf16>(x0, vb[0][4 * r2 + r]);
-                    vbl[1][4 * r2 + r] = split_lo<bf16>(x1, vb[1][4 * r2 + r]);
+#pragma clang fp contract(off)
+                    const float v = (float)uu[rt][r] - (acc[0][rt][r] + acc[1][rt][r]);
+                    v8[4 * r2 + r] = (f16)v;
+                    const float x = v * kd4[rt][r];
+                    vb[4 * r2 + r] = (bf16)x;
+                    vbl[4 * r2 + r] = split_lo<bf16>(x, vb[4 * r2 + r]);
                 }
             }
             Vx[c & 1][pp][s][lane] = v8;
@@ -599,11 +595,11 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = mma(ka[kw][kt][s], vb[kw], hs[kw][kt]);
+                for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = mma(ka[kw][kt][s], vb, hs[kw][kt]);
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = mma(ka[kw][kt][s], vbl[kw], hs[kw][kt]);
+                for (int kt = 0; kt < NKT; ++kt) hs[kw][kt] = mma(ka[kw][kt][s], vbl, hs[kw][kt]);
         }
         pack();
         if (m == M - 1 && c + 1 < nch) publish_state();  // the state entering the next token chunk
