@@ -103,6 +103,9 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     __shared__ __attribute__((aligned(16))) f16x8 Vx[2][NP][2][64];
     // state entering a token chunk, bf16, as O^T = S Q^T operands: [slice][K half][step][lane]
     __shared__ __attribute__((aligned(16))) FragT Sx[NP][2][NKS][64];
+    // per output wave, the cumulative decay (log2 units) of the token of
+    // each expanded row of its current token chunk (64 M rows, M <= 4)
+    __shared__ __attribute__((aligned(16))) float Grow[NP][4 * C];
 
     // ---- block -> (sequence, value head, slice group); the groups of one
     // head share an XCD
@@ -186,12 +189,15 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                         FragT, buf_load16(rq, (uint32_t)(((16 * tt + lc) * (int)qk.q_ts + kw * KH + 32 * ks + 8 * lg) * ES)));
             gn = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
         };
-        // scale/||q_t||, G_t of this lane's token and G of token `lane`, for
-        // the current token chunk and (made a step before it starts) the next
-        float fq = 0.f, Gq = 0.f, Gall = 0.f, fqn = 0.f, Gqn = 0.f, Galln = 0.f;
-        auto token_setup = [&](const FragT (&qs)[2][NKS], float gs, float &fq, float &Gq, float &Gall) {
-            Gall = wave_inclusive_sum(gs);
-            Gq = __shfl(Gall, 16 * tt + lc, 64);
+        // scale/||q_t|| and G_t (log2 units) of this lane's token, for the
+        // current token chunk and (made a step before it starts) the next;
+        // the row table is written for the token chunk being set up, after
+        // the last read of the current one's (same wave, in order)
+        float fq = 0.f, Gq = 0.f, fqn = 0.f, Gqn = 0.f;
+        auto token_setup = [&](const FragT (&qs)[2][NKS], float gs, float &fq, float &Gq) {
+            const float Gl = wave_inclusive_sum(gs) * 1.44269504088896341f;  // G of token `lane`
+            Gq = __shfl(Gl, 16 * tt + lc, 64);
+            for (int j = 0; j < M; ++j) Grow[tt][lane * M + j] = Gl;
             float ss = 0.f;
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
@@ -209,7 +215,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         // O^T tiles: oa[ct] holds o[token 16 tt + lc][64 slg + 16 ct + 4 lg + r]
         f32x4 oa[NP];
         auto inter = [&]() {  // O^T = S Q^T exp(G_t), S from the state exchange
-            const float f = fq * __expf(Gq);
+            const float f = fq * __builtin_amdgcn_exp2f(Gq);
             FragT sx[NP][2][NKS];  // every state fragment first, then the products
 #pragma unroll
             for (int ct = 0; ct < NP; ++ct)
@@ -247,7 +253,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         };
 
         load_q(0, qf, gn);
-        token_setup(qf, gn, fq, Gq, Gall);
+        token_setup(qf, gn, fq, Gq);
         lds_barrier();  // stage 0 landed; the initial state exchange is visible
         // O^T of a token chunk starts as its inter-chunk term, made in the
         // token chunk's second step before the barrier (the state exchange
@@ -287,7 +293,6 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                     for (int ks = 0; ks < NKS; ++ks) qf[kw][ks] = qn[kw][ks];
                 fq = fqn;
                 Gq = Gqn;
-                Gall = Galln;
             }
             // the next token chunk's queries, a token chunk ahead
             if (m == 0 && C * (ti + 1) < ntok) load_q(ti + 1, qn, gnn);
@@ -295,7 +300,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
             // ---- the chunk's key rows (A operands of the scores) and norms
             FragT kr[4][2][NKS];
-            f32x4 rk4[4];
+            f32x4 rk4[4], gr4[4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -304,22 +309,22 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                     for (int ks = 0; ks < NKS; ++ks)
                         kr[st][kw][ks] = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
                 rk4[st] = *(const f32x4 *)(&Sg.rk[16 * st + 4 * lg]);
+                gr4[st] = *(const f32x4 *)(&Grow[tt][C * m + 16 * st + 4 * lg]);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of their uses
-            // ---- the score factors: dec = fq_t exp(G_t - G_s) for key row r
+            // ---- the score factors: dec = fq_t 2^(G_t - G_s) for key row r
             // of the chunk (expanded row 64 m + r of the token chunk: token
-            // s = (64 m + r) / M, copy (64 m + r) % M) when s <= t and r < n,
-            // else 0; branch-free, masked entries take exp(0)
+            // s = (64 m + r) / M) when s <= t and r < n, else 0.  s <= t
+            // exactly when 64 m + r < (t + 1) M, so one bound per lane covers
+            // both tests; branch-free, masked entries take 2^0
+            const int lim = min((t_me + 1) * M - C * m, n) - 4 * lg;  // row 16 st + 4 lg + r is live when 16 st + r < lim
             float dec[4][4];
 #pragma unroll
             for (int st = 0; st < 4; ++st)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * st + 4 * lg + r;
-                    const int sk = (int)__umulhi((uint32_t)(C * m + row), mdiv);  // key token, 0..63 (M >= 2)
-                    const float Gs = __shfl(Gall, sk, 64);
-                    const bool ok = row < n && sk <= t_me;
-                    const float e = __expf(ok ? Gq - Gs : 0.f);
+                    const bool ok = 16 * st + r < lim;
+                    const float e = __builtin_amdgcn_exp2f(ok ? Gq - gr4[st][r] : 0.f);
                     dec[st][r] = ok ? fq * e : 0.f;
                 }
             // ---- scores of the tile's tokens against the chunk's keys,
@@ -360,7 +365,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                 }
             }
             // the next token chunk's norms and decays, a step before it starts
-            if (m == M - 1 && C * (ti + 1) < ntok) token_setup(qn, gnn, fqn, Gqn, Galln);
+            if (m == M - 1 && C * (ti + 1) < ntok) token_setup(qn, gnn, fqn, Gqn);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 pb[s] = pn[s];
