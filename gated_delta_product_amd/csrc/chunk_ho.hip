@@ -431,8 +431,19 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
     for (int i = 0; i < NU; ++i) ou[i] = (uint32_t)((i * 64 + lane) * 16 - 1024 * (i % 4));
     const uint32_t o4 = (uint32_t)(lane * 4);
-    const char *pt = rw ? (const char *)(w + (r0 * HV + hv) * KD) : (const char *)((const bf16 *)qk.k + qkh);
-    const int64_t stt = (int64_t)C * ldw * ES;
+    // the tile's source: w rows of the chunk, or (fixed offsets) the key rows
+    // from the chunk's first token, advanced by one chunk per issue; with
+    // per-chunk offsets the key head's base
+    const char *kb0 = (const char *)((const bf16 *)qk.k + qkh);
+    const char *pt = rw ? (const char *)(w + (r0 * HV + hv) * KD)
+                        : (kfix ? kb0 + (int64_t)__umulhi((uint32_t)r0, mdiv) * qk.k_ts * ES : kb0);
+    const int64_t stt = rw ? (int64_t)C * ldw * ES : (kfix ? (int64_t)(C / M) * qk.k_ts * ES : 0);
+    // bytes spanned by a chunk's first n key rows when it starts on a token
+    auto kspan_fix = [&](int n) {
+        const uint32_t rr = (uint32_t)(n - 1), t = __umulhi(rr, mdiv);
+        return (uint32_t)(((int64_t)t * qk.k_ts + (int64_t)(rr - t * (uint32_t)M) * qk.k_js) * ES) + KD * ES;
+    };
+    const uint32_t kspan_full = kfix ? kspan_fix(C) : 0u;
     int64_t e_issue = r0;  // first expanded row of the next chunk to issue
     const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl, HV, VD, uv_ss));
     const int64_t stu = (int64_t)C * 16 * ES;
@@ -445,16 +456,26 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem_issue));
         const uint32_t sb = ring_base + st * SB + tile_off;
         // whole rows: the half is in the offsets
-        const int64_t tb = (int64_t)__umulhi((uint32_t)e_issue, mdiv);
-        const uint32_t kspan = n > 0 ? __builtin_amdgcn_readfirstlane((uint32_t)(krel(e_issue, n - 1) * ES)) + KD * ES : 0u;
-        const rsrc_t rt = rw ? make_rsrc(pt, span(n, ldw * ES, KD * ES))
-                             : make_rsrc(pt + tb * qk.k_ts * ES, kspan);
-        static_for<0, UPR>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (i % 4 == 0) set_m0(sb + 1024 * i);
-            const uint32_t kr_ = (rw || kfix) ? 0u : (uint32_t)(krel(e_issue, i * RPI + lane / UPR) * ES);
-            dma16_m0<1024 * (i % 4)>(rt, ot[i] + kr_);
-        });
+        if (rw || kfix) {  // wave-uniform: fixed offsets, no per-chunk row arithmetic
+            const uint32_t range = rw ? span(n, ldw * ES, KD * ES)
+                                      : (n == C ? kspan_full : (n > 0 ? kspan_fix(n) : 0u));
+            const rsrc_t rt = make_rsrc(pt, range);
+            static_for<0, UPR>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i % 4 == 0) set_m0(sb + 1024 * i);
+                dma16_m0<1024 * (i % 4)>(rt, ot[i]);
+            });
+        } else {
+            const int64_t tb = (int64_t)__umulhi((uint32_t)e_issue, mdiv);
+            const uint32_t kspan =
+                n > 0 ? __builtin_amdgcn_readfirstlane((uint32_t)(krel(e_issue, n - 1) * ES)) + KD * ES : 0u;
+            const rsrc_t rt = make_rsrc(pt + tb * qk.k_ts * ES, kspan);
+            static_for<0, UPR>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i % 4 == 0) set_m0(sb + 1024 * i);
+                dma16_m0<1024 * (i % 4)>(rt, ot[i] + (uint32_t)(krel(e_issue, i * RPI + lane / UPR) * ES));
+            });
+        }
         const rsrc_t ru = make_rsrc(pu, (uint32_t)(n * 16 * ES));
         const uint32_t sbu = ring_base + st * SB + OFU + pp * (C * 16 * ES);
         static_for<0, NU>([&](auto ic) {
@@ -463,7 +484,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
             dma16_m0<1024 * (i % 4)>(ru, ou[i]);
         });
         if (pp < 3) dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
-        if (rw) pt += stt;
+        pt += stt;
         e_issue += C;
         pu += stu;
         p4 += st4;
