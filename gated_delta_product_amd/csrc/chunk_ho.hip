@@ -27,7 +27,7 @@
 //   one (bf16).  They also stream each chunk into a three-stage LDS ring,
 //   two chunks ahead (buffer loads with the LDS destination; the range
 //   check zero-fills rows past the end): wave p a half tile of w (p < 2) or
-//   K (p >= 2), its u slice and one of kdecay, gcum and the key norms.
+//   K (p >= 2), its u slice and (p < 2) one of kdecay and gcum.
 // * Output waves 4-7.  Wave 4 + t owns output token tile t (tokens 16t ..
 //   16t + 15 of each token chunk) over all 64 columns of the block:
 //     - before the step's barrier, the scores of its tokens against the
@@ -37,8 +37,10 @@
 //       state;
 //     - after it, O^T += V^T P^T for the previous chunk with every slice's
 //       v_new from the exchange, and at a token chunk's end the store of o.
-//   Their query rows are loaded into registers a token chunk ahead, and
-//   their norms and decays are made a step before the token chunk starts.
+//   Their query rows and the key norms of the token chunk's rows are loaded
+//   a token chunk ahead, and a step before the token chunk starts each
+//   output wave writes a row table (every expanded row's decay less its
+//   log2 key norm) so that a score's whole factor is one 2^x.
 // One barrier per chunk orders it all: the ring stage of chunk c is read
 // before it, the exchanges are written after it and read after the next.
 // Requires M >= 2, so that the state exchange of one token chunk is read
@@ -68,7 +70,6 @@ struct HoStage {
     bf16 u[NP][C * 16];       // u slices, plain rows of 16 elements
     float kd[C];              // key decay factor per row (0 past the end)
     float gc[C];              // cumulative log2 decay per row
-    float rk[C];              // 1 / ||k|| per row (0 past the end)
 };
 
 template <int KD, int VD>
@@ -93,7 +94,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     constexpr int SG = S / NP;           // blocks per head
     constexpr int SB = (int)sizeof(HoStage<KD>);
     // ring loads per chunk of chain wave p: a half tile of w or K, its u
-    // slice and (p < 3) one per-row vector
+    // slice and (p < 2) one per-row vector
     constexpr int NDMA = UPR + NU + 1;
     static_assert(NKS >= 1 && (UPR & (UPR - 1)) == 0 && S % NP == 0 && SB % 16 == 0, "tile shape");
     static_assert(NDMA < 64, "in-flight count must fit the vector memory counter");
@@ -177,6 +178,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         // products), their norms and decays for the current token chunk
         FragT qf[2][NKS], qn[2][NKS];  // this token chunk's queries, and the next one's in flight
         float gn = 0.f, gnn = 0.f;
+        float rkn[4];  // key norms of the next token chunk's rows of token `lane` (copies 0 .. M - 1)
         auto load_q = [&](int ti, FragT (&qf)[2][NKS], float &gn) {
             const int nt = __builtin_amdgcn_readfirstlane(clamp_rows(ntok - C * ti));
             const rsrc_t rq = make_rsrc((const bf16 *)qk.q + (bos + (int64_t)C * ti) * qk.q_ts + qkh,
@@ -188,16 +190,23 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                     qf[kw][ks] = __builtin_bit_cast(
                         FragT, buf_load16(rq, (uint32_t)(((16 * tt + lc) * (int)qk.q_ts + kw * KH + 32 * ks + 8 * lg) * ES)));
             gn = (g != nullptr && lane < nt) ? g[(bos + (int64_t)C * ti + lane) * HV + hv] : 0.f;
+            // rows past the end read as 0 (range check)
+            const rsrc_t rr = make_rsrc(k_rnorm + k0r + (int64_t)C * M * ti, (uint32_t)(nt * M * 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rkn[j] = j < M ? buf_load_f32(rr, (uint32_t)((lane * M + j) * 4)) : 0.f;
         };
-        // scale/||q_t|| and G_t (log2 units) of this lane's token, for the
-        // current token chunk and (made a step before it starts) the next;
-        // the row table is written for the token chunk being set up, after
-        // the last read of the current one's (same wave, in order)
-        float fq = 0.f, Gq = 0.f, fqn = 0.f, Gqn = 0.f;
-        auto token_setup = [&](const FragT (&qs)[2][NKS], float gs, float &fq, float &Gq) {
+        // Gq = G_t + log2(scale / ||q_t||) (log2 units) of this lane's token,
+        // for the current token chunk and (made a step before it starts) the
+        // next; the row table of the token chunk being set up holds
+        // G_s - log2(1 / ||k_e||) for each expanded row e (token s), so one
+        // 2^(Gq - table) is the whole score factor.  It is written after the
+        // last read of the current one's (same wave, in order).
+        float Gq = 0.f, Gqn = 0.f;
+        auto token_setup = [&](const FragT (&qs)[2][NKS], float gs, const float (&rks)[4], float &Gq) {
             const float Gl = wave_inclusive_sum(gs) * 1.44269504088896341f;  // G of token `lane`
-            Gq = __shfl(Gl, 16 * tt + lc, 64);
-            for (int j = 0; j < M; ++j) Grow[tt][lane * M + j] = Gl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < M) Grow[tt][lane * M + j] = Gl - __builtin_amdgcn_logf(rks[j]);
             float ss = 0.f;
 #pragma unroll
             for (int kw = 0; kw < 2; ++kw)
@@ -210,12 +219,12 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                     }
             ss += __shfl_xor(ss, 16, 64);
             ss += __shfl_xor(ss, 32, 64);
-            fq = scale / sqrtf(ss + 1e-6f);
+            Gq = __shfl(Gl, 16 * tt + lc, 64) + __builtin_amdgcn_logf(scale / sqrtf(ss + 1e-6f));
         };
         // O^T tiles: oa[ct] holds o[token 16 tt + lc][64 slg + 16 ct + 4 lg + r]
         f32x4 oa[NP];
         auto inter = [&]() {  // O^T = S Q^T exp(G_t), S from the state exchange
-            const float f = fq * __builtin_amdgcn_exp2f(Gq);
+            const float f = __builtin_amdgcn_exp2f(Gq);  // scale / ||q_t|| 2^G_t
             FragT sx[NP][2][NKS];  // every state fragment first, then the products
 #pragma unroll
             for (int ct = 0; ct < NP; ++ct)
@@ -253,7 +262,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
         };
 
         load_q(0, qf, gn);
-        token_setup(qf, gn, fq, Gq);
+        token_setup(qf, gn, rkn, Gq);
         lds_barrier();  // stage 0 landed; the initial state exchange is visible
         // O^T of a token chunk starts as its inter-chunk term, made in the
         // token chunk's second step before the barrier (the state exchange
@@ -291,7 +300,6 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                 for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) qf[kw][ks] = qn[kw][ks];
-                fq = fqn;
                 Gq = Gqn;
             }
             // the next token chunk's queries, a token chunk ahead
@@ -300,7 +308,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
             const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
             // ---- the chunk's key rows (A operands of the scores) and norms
             FragT kr[4][2][NKS];
-            f32x4 rk4[4], gr4[4];
+            f32x4 gr4[4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -308,15 +316,15 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
                         kr[st][kw][ks] = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
-                rk4[st] = *(const f32x4 *)(&Sg.rk[16 * st + 4 * lg]);
                 gr4[st] = *(const f32x4 *)(&Grow[tt][C * m + 16 * st + 4 * lg]);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of their uses
-            // ---- the score factors: dec = fq_t 2^(G_t - G_s) for key row r
-            // of the chunk (expanded row 64 m + r of the token chunk: token
-            // s = (64 m + r) / M) when s <= t and r < n, else 0.  s <= t
-            // exactly when 64 m + r < (t + 1) M, so one bound per lane covers
-            // both tests; branch-free, masked entries take 2^0
+            // ---- the score factors: dec = (scale / ||q_t||) (1 / ||k_r||)
+            // 2^(G_t - G_s) = 2^(Gq - table) for key row r of the chunk
+            // (expanded row 64 m + r of the token chunk: token s = (64 m + r)
+            // / M) when s <= t and r < n, else 2^-inf = 0.  s <= t exactly
+            // when 64 m + r < (t + 1) M, so one bound per lane covers both
+            // tests; branch-free
             const int lim = min((t_me + 1) * M - C * m, n) - 4 * lg;  // row 16 st + 4 lg + r is live when 16 st + r < lim
             float dec[4][4];
 #pragma unroll
@@ -324,11 +332,10 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const bool ok = 16 * st + r < lim;
-                    const float e = __builtin_amdgcn_exp2f(ok ? Gq - gr4[st][r] : 0.f);
-                    dec[st][r] = ok ? fq * e : 0.f;
+                    dec[st][r] = __builtin_amdgcn_exp2f(ok ? Gq - gr4[st][r] : -__builtin_inff());
                 }
             // ---- scores of the tile's tokens against the chunk's keys,
-            // P^T[key r][token t] = rk_r dec[r][t] (k_r . q_t), the four
+            // P^T[key r][token t] = dec[r][t] (k_r . q_t), the four
             // sub-tiles' products interleaved (masked entries are zeroed by
             // dec)
             f32x4 p[4];
@@ -348,7 +355,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int st = 2 * s + s2;
-                        const float x = p[st][r] * rk4[st][r] * dec[st][r];
+                        const float x = p[st][r] * dec[st][r];
                         pn[s][4 * s2 + r] = (f16)x;
                     }
             if (inter_due && m == 1) {
@@ -365,7 +372,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                 }
             }
             // the next token chunk's norms and decays, a step before it starts
-            if (m == M - 1 && C * (ti + 1) < ntok) token_setup(qn, gnn, fqn, Gqn);
+            if (m == M - 1 && C * (ti + 1) < ntok) token_setup(qn, gnn, rkn, Gqn);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 pb[s] = pn[s];
@@ -385,8 +392,8 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     // publishes the chunk's v_new (and at token-chunk ends the state) to
     // the exchanges.  It also streams part of each chunk into the ring, two
     // chunks ahead: half pp % 2 of the w (pp < 2) or K (pp >= 2) tile, its
-    // own u slice and one per-row vector (pp = 0: kdecay, 1: gcum, 2: key
-    // norms), with no other global memory instruction in the loop, so its
+    // own u slice and (pp < 2) one per-row vector (pp = 0: kdecay, 1:
+    // gcum), with no other global memory instruction in the loop, so its
     // counted waits are exact.  One code path for all four waves and all
     // three ring stages (the wave and the stage are runtime values), so the
     // code fits the instruction cache.
@@ -401,7 +408,6 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     constexpr int OFU = (int)__builtin_offsetof(Stage, u);
     constexpr int OFD = (int)__builtin_offsetof(Stage, kd);
     constexpr int OFG = (int)__builtin_offsetof(Stage, gc);
-    constexpr int OFR = (int)__builtin_offsetof(Stage, rk);
     constexpr int HALF = C * KH * ES;  // bytes of one half tile
     const bool rw = pp < 2;             // w (else K)
     const int hh = pp & 1;              // half of the tile's columns
@@ -447,9 +453,8 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     int64_t e_issue = r0;  // first expanded row of the next chunk to issue
     const char *pu = (const char *)(u + uv_index(bseq, r0 - bseq * TM, hv, 16 * sl, HV, VD, uv_ss));
     const int64_t stu = (int64_t)C * 16 * ES;
-    const char *p4 = pp == 0 ? (const char *)(kdecay + h0r)
-                             : (pp == 1 ? (const char *)(gcum + h0r) : (const char *)(k_rnorm + k0r));
-    const int off4 = pp == 0 ? OFD : (pp == 1 ? OFG : OFR);
+    const char *p4 = pp == 0 ? (const char *)(kdecay + h0r) : (const char *)(gcum + h0r);
+    const int off4 = pp == 0 ? OFD : OFG;
     const int tile_off = (rw ? OFW : OFK) + hh * HALF;
     int rem_issue = (int)rows;
     auto issue = [&](int st) {  // the next chunk into ring stage st (rows past the end read as zero)
@@ -483,7 +488,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
             if constexpr (i % 4 == 0) set_m0(sbu + 1024 * i);
             dma16_m0<1024 * (i % 4)>(ru, ou[i]);
         });
-        if (pp < 3) dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
+        if (pp < 2) dma4(make_rsrc(p4, (uint32_t)(n * 4)), o4, ring_base + st * SB + off4);
         pt += stt;
         e_issue += C;
         pu += stu;
@@ -492,7 +497,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     };
     // the chunk before the last issue landed: everything but that issue's loads
     auto wait_ring = [&]() {
-        if (pp < 3)
+        if (pp < 2)
             wait_vmcnt<NDMA>();
         else
             wait_vmcnt<NDMA - 1>();
