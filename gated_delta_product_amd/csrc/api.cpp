@@ -594,6 +594,10 @@ static gdp_status scan_impl(const char *name, const gdp_chunk_args *a, const gdp
         return stage_events ? hip_status(hipEventRecord((hipEvent_t)stage_events[i], s), "hipEventRecord") : ok();
     };
     auto run = [&](hipError_t e, const char *what) { return hip_status(e, what); };
+    if (!packed && p.nseq == 1 && nslot > 1) {  // WY in the order the segment maps read it
+        p.seg_nch = seg_tok * a->M / 64;
+        p.seg_n = nslot;
+    }
     if ((st = run(prep ? gdp::launch_wy_prepare(p, *prep, s) : gdp::launch_wy(p, s),
                   "gdp_chunk_fwd_scan: recompute_w_u launch")) != GDP_OK)
         return st;

@@ -53,6 +53,9 @@ struct ChunkParams {
     // only when c % hstep == 0; 1 writes them all
     int hstep = 1;
     QKRows qk;  // q and k rows for the segment maps and the fused pass
+    // WY launch order for one sequence cut into seg_n segments of seg_nch
+    // chunks (the last may be shorter): 0 keeps the plain order
+    int64_t seg_nch = 0, seg_n = 0;
 };
 
 // Element offset of (batch row b, expanded row e relative to the batch row,

@@ -71,7 +71,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
          const float *__restrict__ g, const int32_t *__restrict__ cu, int64_t nseq, int64_t Ttok,
          int H, int HV, int M, float *__restrict__ k_rnorm, float *__restrict__ gcum,
          float *__restrict__ kdecay, T *__restrict__ w,
-         T *__restrict__ u, int64_t uv_ss, WyFuse<T> fz) {
+         T *__restrict__ u, int64_t uv_ss, WyFuse<T> fz, int64_t seg_nch, int64_t seg_n) {
     typedef typename Frag<T>::type FragT;
     constexpr int LDK = KD + Pad<T>::value;
     constexpr int LDV = VD + Pad<T>::value;
@@ -95,7 +95,25 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // together cover whole rows of k, v and w (all heads of a few chunks),
     // so HBM sees long contiguous runs
     const int64_t lin = blockIdx.x;
-    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, lin / HV);
+    int64_t ci = lin / HV;
+    // With a segment plan (one sequence, seg_n segments of seg_nch chunks,
+    // the last one nlast <= seg_nch), chunk j of every segment goes before
+    // chunk j - 1 of any: the segment maps, which start at each segment's
+    // first chunk, then meet the most recently written lines first.
+    if (seg_n > 1) {
+        const int64_t F = seg_n - 1, nlast = (Ttok * M + C - 1) / C - F * seg_nch;
+        const int64_t hi = (seg_nch - nlast) * F;  // launch slots of the chunks j >= nlast (F each)
+        int64_t j, sg;
+        if (ci < hi) {
+            j = seg_nch - 1 - ci / F;
+            sg = ci % F;
+        } else {
+            j = nlast - 1 - (ci - hi) / (F + 1);
+            sg = (ci - hi) % (F + 1);
+        }
+        ci = sg * seg_nch + j;
+    }
+    const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, ci);
     if (loc.seq < 0) return;
     const int hv = (int)(lin % HV);
     const int hk = hv / (HV / H);
@@ -416,7 +434,8 @@ static hipError_t launch_wy_t(const ChunkParams &p, hipStream_t stream, const Wy
     dim3 grid((unsigned)(p.max_items * a.HV));
     hipLaunchKernelGGL((gdp_wy_k<T, KD, VD, FUSE>), grid, dim3(256), 0, stream,
                        (const T *)a.k, (const T *)a.v, a.beta, a.g, a.cu_seqlens, p.nseq, a.T,
-                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u, p.uv_ss, fz);
+                       a.H, a.HV, a.M, a.k_rnorm, a.gcum, a.kdecay, (T *)a.w, (T *)a.u, p.uv_ss, fz,
+                       p.seg_nch, p.seg_n);
     return hipGetLastError();
 }
 
