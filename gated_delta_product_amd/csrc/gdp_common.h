@@ -196,6 +196,11 @@ __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a 
 // Exact x / d for 0 <= x < 2^31 and d in [1, 4] (the Householder copy count)
 // with one multiply-high: magic = floor((2^32 - 1) / d) + 1, 0 meaning d = 1.
 __device__ __forceinline__ uint32_t small_div_magic(int d) { return d == 1 ? 0u : 0xFFFFFFFFu / (uint32_t)d + 1u; }
+// x / d for x >= 0 and d in {1, 2, 3, 4}, exact over the whole range: a
+// shift, or for 3 the high half of x * ceil(2^65 / 3) shifted once more
+__device__ __forceinline__ int64_t div_m(int64_t x, int d) {
+    return d == 3 ? (int64_t)(__umul64hi((uint64_t)x, 0xAAAAAAAAAAAAAAABull) >> 1) : x >> (d >> 1);
+}
 __device__ __forceinline__ uint32_t small_div(uint32_t x, uint32_t magic) { return magic ? __umulhi(x, magic) : x; }
 
 // A value the caller knows is the same in every lane, made visibly uniform
@@ -258,10 +263,13 @@ __device__ __forceinline__ ChunkLoc find_chunk(const int32_t *cu, int64_t nseq, 
                                                int64_t rows_per_token, int64_t chunk, int64_t id) {
     ChunkLoc r;
     if (cu == nullptr) {
+        // chunk counts and ids stay below 2^31 (the launch limits), so the
+        // division runs in 32 bits
         const int64_t per = ceil_div64(T * rows_per_token, chunk);
-        r.seq = per > 0 ? id / per : -1;
+        const uint32_t q = per > 0 ? (uint32_t)id / (uint32_t)per : 0u;
+        r.seq = per > 0 ? (int64_t)q : -1;
         if (r.seq >= nseq) r.seq = -1;
-        r.c = per > 0 ? id % per : 0;
+        r.c = per > 0 ? (int64_t)((uint32_t)id - q * (uint32_t)per) : 0;
         r.base = r.seq >= 0 ? r.seq * per : 0;
         seq_bounds(nullptr, T, r.seq < 0 ? 0 : r.seq, r.bos, r.eos);
         return r;

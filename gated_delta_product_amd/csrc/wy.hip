@@ -95,27 +95,30 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // together cover whole rows of k, v and w (all heads of a few chunks),
     // so HBM sees long contiguous runs
     const int64_t lin = blockIdx.x;
-    int64_t ci = lin / HV;
+    // launch ids and chunk counts stay below 2^31 (the launch limits): 32-bit
+    // divisions
+    int64_t ci = (uint32_t)lin / (uint32_t)HV;
     // With a segment plan (one sequence, seg_n segments of seg_nch chunks,
     // the last one nlast <= seg_nch), chunk j of every segment goes before
     // chunk j - 1 of any: the segment maps, which start at each segment's
     // first chunk, then meet the most recently written lines first.
     if (seg_n > 1) {
-        const int64_t F = seg_n - 1, nlast = (Ttok * M + C - 1) / C - F * seg_nch;
-        const int64_t hi = (seg_nch - nlast) * F;  // launch slots of the chunks j >= nlast (F each)
-        int64_t j, sg;
-        if (ci < hi) {
-            j = seg_nch - 1 - ci / F;
-            sg = ci % F;
+        const uint32_t F = (uint32_t)(seg_n - 1), nlast = (uint32_t)((Ttok * M + C - 1) / C - F * seg_nch);
+        const uint32_t hi = ((uint32_t)seg_nch - nlast) * F;  // launch slots of the chunks j >= nlast (F each)
+        const uint32_t c32 = (uint32_t)ci;
+        uint32_t j, sg;
+        if (c32 < hi) {
+            j = (uint32_t)seg_nch - 1 - c32 / F;
+            sg = c32 % F;
         } else {
-            j = nlast - 1 - (ci - hi) / (F + 1);
-            sg = (ci - hi) % (F + 1);
+            j = nlast - 1 - (c32 - hi) / (F + 1);
+            sg = (c32 - hi) % (F + 1);
         }
-        ci = sg * seg_nch + j;
+        ci = (int64_t)sg * seg_nch + j;
     }
     const ChunkLoc loc = find_chunk(cu, nseq, Ttok, M, C, ci);
     if (loc.seq < 0) return;
-    const int hv = (int)(lin % HV);
+    const int hv = (int)((uint32_t)lin % (uint32_t)HV);
     const int hk = hv / (HV / H);
     const int64_t r0 = loc.bos * M + C * loc.c;  // first expanded row (global)
     const int64_t rend = loc.eos * M;
@@ -134,7 +137,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         // (the gates are computed below, once the tile loads are out)
     } else if (wv == 0) {
         b_in = e_in ? beta[e_row * HV + hv] : 0.f;
-        gd_in = (g != nullptr && e_in && (e_row % M) == 0) ? g[(e_row / M) * HV + hv] : 0.f;  // NULL: ungated
+        gd_in = (g != nullptr && e_in && e_row - div_m(e_row, M) * M == 0) ? g[div_m(e_row, M) * HV + hv] : 0.f;  // NULL: ungated
     }
     uint4 vreg[VPT];
     if constexpr (FUSE) {
@@ -154,7 +157,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             const int uidx = tid + 256 * it, row = uidx / VUPR, cu16 = uidx % VUPR;
             vreg[it] = make_uint4(0, 0, 0, 0);
             if (row < n) {
-                const int64_t e = r0 + row, t = e / M;
+                const int64_t e = r0 + row, t = div_m(e, M);
                 const int j = (int)(e - t * M);
                 vreg[it] = *(const uint4 *)(fz.x + t * fz.xts + ((int64_t)j * H + hv) * VD + cu16 * E);
             }
@@ -165,7 +168,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             kreg[it] = make_uint4(0, 0, 0, 0);
             qreg[it] = make_uint4(0, 0, 0, 0);
             if (row < n) {
-                const int64_t e = r0 + row, t = e / M;
+                const int64_t e = r0 + row, t = div_m(e, M);
                 const int j = (int)(e - t * M);
                 kreg[it] = *(const uint4 *)(fz.x + t * fz.xts + kb + ((int64_t)j * fz.G + grp) * KD + cu16 * E);
                 if (j == 0 && fz.q != nullptr)
@@ -174,7 +177,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         }
         // the gates of the block's rows: beta per row, g per token (on its copy 0)
         if (wv == 0 && e_in) {
-            const int64_t t = e_row / M;
+            const int64_t t = div_m(e_row, M);
             const int j = (int)(e_row - t * M);
             b_in = gate_beta(to_f32(fz.ba[t * fz.bts + j * H + hv]));
             if (j == 0) gd_in = gate_g(to_f32(fz.ba[t * fz.bts + M * H + hv]), fz.A_log[hv], fz.dt_bias[hv]);
@@ -187,14 +190,14 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             }
         }
         if (wv == 0 && e_in) {
-            const int64_t t = e_row / M;
+            const int64_t t = div_m(e_row, M);
             if (fz.beta != nullptr) fz.beta[e_row * H + hv] = b_in;
             if (e_row - t * M == 0) fz.g[t * H + hv] = gd_in;
         }
 #pragma unroll
         for (int it = 0; it < KPT; ++it) {
             const int uidx = tid + 256 * it, row = uidx / KUPR, cu16 = uidx % KUPR;
-            const int64_t e = r0 + row, t = e / M;
+            const int64_t e = r0 + row, t = div_m(e, M);
             const int j = (int)(e - t * M);
             if (row < n && fz.k != nullptr) {  // q and k may be NULL: the later stages then read x
                 *(uint4 *)(fz.k + (e * H + hv) * (int64_t)KD + cu16 * E) = kreg[it];
