@@ -276,7 +276,18 @@ gdp_status gdp_recompute_w_u(const gdp_chunk_args *a, void *stream);
 gdp_status gdp_chunk_h(const gdp_chunk_args *a, void *stream);
 /* o from q, k, k_rnorm, v_new, h, g. */
 gdp_status gdp_chunk_o(const gdp_chunk_args *a, void *stream);
-/* gdp_recompute_w_u, gdp_chunk_h, gdp_chunk_o in order on one stream. */
+/* gdp_recompute_w_u, gdp_chunk_h, gdp_chunk_o in order on one stream.
+ * With v_new and h both NULL (bf16, M >= 2) chunk_h and chunk_o run as one
+ * pass (core.ssm.ops.gdp.chunk_o, module description: chunk_h's boundary
+ * states combined with the causal in-chunk attention over the copies) that
+ * stores neither, and h_chunks is not checked.  w, u, k_rnorm, gcum, kdecay
+ * and ht are then bit-identical to the two-stage call, and o agrees with it
+ * to rounding: the one pass forms each score's decay and norm factor as one
+ * power of two of log2-scaled decays and norms, and runs the output product
+ * V^T P^T on fp16 operands, so v_new must stay within fp16's range
+ * (|v_new| < 65504), else o is not finite.  v_new and h NULL with another
+ * dtype or M == 1 return GDP_ERR_UNSUPPORTED; only one of them NULL returns
+ * GDP_ERR_INVALID. */
 gdp_status gdp_chunk_fwd(const gdp_chunk_args *a, void *stream);
 
 /*
@@ -386,8 +397,12 @@ gdp_status gdp_prefill_fwd_pipelined(const gdp_prepare_args *p, const gdp_chunk_
  * gdp_chunk_fwd, and so are h, v_new and o over the first segment of each
  * sequence; the states entering later segments come out of the composed
  * maps, so h, v_new, o and ht there agree with gdp_chunk_fwd to rounding
- * (the composition runs on the same bf16 matrix-core operands with fp32
- * accumulation as the chunk recurrence itself).  Supported: dtype bf16 with
+ * (the composition runs on matrix-core operands with fp32 accumulation like
+ * the chunk recurrence itself: bf16 in its first product and fp16 in its
+ * second, so keys must stay within fp16's range, |k| < 65504).  v_new
+ * and h may both be NULL as for gdp_chunk_fwd: chunk_h and chunk_o then run
+ * as one pass over every segment, from its scanned state, and no state
+ * leaves the chip.  Supported: dtype bf16 with
  * K, V in {64, 128} and T*M*V*2 < 2^31; other shapes return
  * GDP_ERR_UNSUPPORTED.  B > 1 without cu_seqlens returns GDP_ERR_INVALID.
  */
@@ -437,7 +452,13 @@ gdp_status gdp_chunk_fwd_scan_noalloc(const gdp_chunk_args *a, int32_t num_segme
  * g (which must therefore be writable, g not NULL, and HV == H: prepare
  * makes H value heads).  v and beta may be NULL: no stage after WY reads
  * them (the values enter u inside it), so they are then not stored, which
- * saves their HBM writes; every other output is unchanged.  Every output is
+ * saves their HBM writes; every other output is unchanged.  With v_new and
+ * h NULL (the one-pass form), q and k may be NULL too, both or neither: WY
+ * then neither stores the key copies and queries nor loads the queries, and
+ * the segment maps and the one pass read the key and query rows from x at
+ * prepare's offsets, so every other output is bit-identical to the run that
+ * stores them.  q and k NULL with v_new or h given return
+ * GDP_ERR_UNSUPPORTED; only one of q, k NULL returns GDP_ERR_INVALID.  Every output is
  * bit-identical to the two calls in sequence, except that with cu_seqlens
  * the prepare outputs of tokens outside every request (none when the
  * offsets run from 0 to T) are not written.  The requirements are those of
