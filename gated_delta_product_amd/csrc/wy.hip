@@ -246,31 +246,32 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
     __syncthreads();
 
-    // ---- L = strictly lower beta_a exp(g_a - g_b) r_a r_b (K K^T)_ab, row block wv
+    // ---- L = strictly lower beta_a exp(g_a - g_b) r_a r_b (K K^T)_ab: the
+    // ten 16x16 tiles (rt, ct <= rt) shared out three, three, two and two
+    // over the waves (row block by row block, the last wave would take four).
+    // Tile (rt, ct) is coded rt * 4 + ct, one byte per tile of a wave.
     {
-        const int ra = 16 * wv;
-        // factors of this lane's four rows: beta * rnorm, and gamma
-        const f32x4 b4 = *(const f32x4 *)&s_beta[ra + 4 * lg], r4 = *(const f32x4 *)&s_rk[ra + 4 * lg];
-        const f32x4 gr = *(const f32x4 *)&s_gam[ra + 4 * lg];
-        f32x4 rowf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rowf[i] = b4[i] * r4[i];
-        for (int ct = 0; ct <= wv; ++ct) {  // upper blocks: A's transposed lower blocks go there
+        const uint32_t tiles = wv == 0 ? 0x000D0C00u : (wv == 1 ? 0x000E0504u : (wv == 2 ? 0x00000908u : 0x00000F0Au));
+        const int ntile = wv < 2 ? 3 : 2;
+        for (int it = 0; it < ntile; ++it) {
+            const int code = (int)((tiles >> (8 * it)) & 0xffu), rt = code >> 2, ct = code & 3;
+            const int ra = 16 * rt;
+            // factors of this lane's four rows: beta * rnorm, and gamma
+            const f32x4 b4 = *(const f32x4 *)&s_beta[ra + 4 * lg], r4 = *(const f32x4 *)&s_rk[ra + 4 * lg];
+            const f32x4 gr = *(const f32x4 *)&s_gam[ra + 4 * lg];
             f32x4 acc = zero4();
-            {
 #pragma unroll
-                for (int ks = 0; ks < KD / 32; ++ks) {
-                    FragT a = lds_row8<T>(Ks + (ra + lc) * LDK + 32 * ks + 8 * lg);
-                    FragT b = lds_row8<T>(Ks + (16 * ct + lc) * LDK + 32 * ks + 8 * lg);
-                    acc = mma(a, b, acc);
-                }
+            for (int ks = 0; ks < KD / 32; ++ks) {
+                FragT a = lds_row8<T>(Ks + (ra + lc) * LDK + 32 * ks + 8 * lg);
+                FragT b = lds_row8<T>(Ks + (16 * ct + lc) * LDK + 32 * ks + 8 * lg);
+                acc = mma(a, b, acc);
             }
             const int col = 16 * ct + lc;
             const float gc = s_gam[col], rc = s_rk[col];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = ra + 4 * lg + i;
-                const float val = col < row ? rowf[i] * rc * __expf(gr[i] - gc) * acc[i] : 0.f;
+                const float val = col < row ? b4[i] * r4[i] * rc * __expf(gr[i] - gc) * acc[i] : 0.f;
                 Lm[row * LDA + col] = val;
             }
         }
@@ -330,46 +331,47 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
 
     // ---- u^T = V^T (A diag(beta))^T and w^T = Khat^T (A diag(beta e^gamma r))^T
-    //      wave wv produces output rows a in [16 wv, 16 wv + 16).  The lane's
-    //      row of A goes to registers first (blocks past the diagonal are 0),
-    //      then the V tile takes the array's space.
+    //      over the four 16-row blocks of output rows.  Blocks 2 and 3
+    //      contract over two 32-row steps of A, blocks 0 and 1 over one, so
+    //      each wave takes one kind of product for one small and one large
+    //      block: wave 0 u of blocks 0 and 2, wave 1 w of blocks 0 and 2,
+    //      wave 2 u of blocks 1 and 3, wave 3 w of blocks 1 and 3.  The
+    //      lanes' rows of A go to registers first (blocks past the diagonal
+    //      are 0), then the V tile takes the array's space.
     {
-        const int a_row = 16 * wv + lc;  // output row this lane's B fragment covers
-        const int nks = (wv >= 2) ? 2 : 1;  // contraction tiles with any b <= a
-        // A diag(beta) and A diag(beta e^gamma r) as bf16 operands split into
-        // high and low parts (split_lo): rounding them to one bf16 each was
-        // the largest single error of the bf16 path in the long-memory regime
+        const bool do_u = (wv & 1) == 0;           // wave-uniform
+        const int rlo = wv >> 1, rhi = rlo + 2;     // the wave's row blocks (one step, two steps)
+        // A diag(beta) (u) or A diag(beta e^gamma r) (w) as bf16 operands
+        // split into high and low parts (split_lo): rounding them to one
+        // bf16 each was the largest single error of the bf16 path in the
+        // long-memory regime
         constexpr bool SPL = Split<T>::on;
-        FragT bu[2], bw[2], bul[2], bwl[2];
+        auto a_frag = [&](int rt, int ks, FragT &hi, FragT &lo) {
+            const int a_row = 16 * rt + lc;
+            const int b0 = 32 * ks + 8 * lg, bb = b0 >> 4;  // A[a_row][b0 .. b0 + 7], block bb
+            const float *fv = do_u ? s_beta : s_ws;
+            const f32x4 f0 = *(const f32x4 *)&fv[b0], f1 = *(const f32x4 *)&fv[b0 + 4];
+            float av[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks < nks) {
-                const int b0 = 32 * ks + 8 * lg, bb = b0 >> 4;  // A[a_row][b0 .. b0 + 7], block bb
-                const f32x4 be0 = *(const f32x4 *)&s_beta[b0], be1 = *(const f32x4 *)&s_beta[b0 + 4];
-                const f32x4 ws0 = *(const f32x4 *)&s_ws[b0], ws1 = *(const f32x4 *)&s_ws[b0 + 4];
-                float av[8];
+            for (int m = 0; m < 8; ++m) {
+                const int addr = bb == rt ? a_row * LDA + b0 + m : (b0 + m) * LDA + a_row;
+                av[m] = bb <= rt ? Lm[addr] : 0.f;
+            }
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int addr = bb == wv ? a_row * LDA + b0 + m : (b0 + m) * LDA + a_row;
-                    av[m] = bb <= wv ? Lm[addr] : 0.f;
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float xu0 = av[m] * be0[m], xw0 = av[m] * ws0[m];
-                    const float xu1 = av[4 + m] * be1[m], xw1 = av[4 + m] * ws1[m];
-                    bu[ks][m] = from_f32<T>(xu0);
-                    bw[ks][m] = from_f32<T>(xw0);
-                    bu[ks][4 + m] = from_f32<T>(xu1);
-                    bw[ks][4 + m] = from_f32<T>(xw1);
-                    if constexpr (SPL) {
-                        bul[ks][m] = split_lo<T>(xu0, bu[ks][m]);
-                        bwl[ks][m] = split_lo<T>(xw0, bw[ks][m]);
-                        bul[ks][4 + m] = split_lo<T>(xu1, bu[ks][4 + m]);
-                        bwl[ks][4 + m] = split_lo<T>(xw1, bw[ks][4 + m]);
-                    }
+            for (int m = 0; m < 4; ++m) {
+                const float x0 = av[m] * f0[m], x1 = av[4 + m] * f1[m];
+                hi[m] = from_f32<T>(x0);
+                hi[4 + m] = from_f32<T>(x1);
+                if constexpr (SPL) {
+                    lo[m] = split_lo<T>(x0, hi[m]);
+                    lo[4 + m] = split_lo<T>(x1, hi[4 + m]);
                 }
             }
-        }
+        };
+        FragT bs[3], bsl[3];  // [0]: block rlo, step 0; [1], [2]: block rhi, steps 0 and 1
+        a_frag(rlo, 0, bs[0], bsl[0]);
+        a_frag(rhi, 0, bs[1], bsl[1]);
+        a_frag(rhi, 1, bs[2], bsl[2]);
         __syncthreads();  // every row of A is in registers
 #pragma unroll
         for (int it = 0; it < VPT; ++it) {
@@ -377,46 +379,58 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             *(uint4 *)(Vs + row * LDV + cu16 * (16 / (int)sizeof(T))) = vreg[it];
         }
         __syncthreads();
-        const bool row_ok = a_row < n;
-        const int64_t grow = r0 + a_row;
-#pragma unroll
-        for (int vt = 0; vt < VD / 16; ++vt) {
+        // tile of the wave's kind for row block j (0: rlo, one step; 1: rhi,
+        // two steps) and column tile ct: V^T or Khat^T times the split A rows
+        auto prod = [&](int j, const T *X, int ldx, int ct) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (ks < nks) {
-                    FragT a = lds_col8<T>(Vs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * vt);
-                    acc = mma(a, bu[ks], acc);
-                    if constexpr (SPL) acc = mma(a, bul[ks], acc);
+                if (ks <= j) {
+                    FragT a = lds_col8<T>(X, ldx, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * ct);
+                    acc = mma(a, bs[j + ks], acc);
+                    if constexpr (SPL) acc = mma(a, bsl[j + ks], acc);
                 }
             }
-            if (row_ok) {  // u is slice-major: 4 consecutive columns of the row
-                typename Frag<T>::half o4;
+            return acc;
+        };
+        typename Frag<T>::half wq[2][KD / 16];  // w[16 rt + lc][16kt + 4lg .. +3] of the wave's two blocks
+        if (do_u) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o4[q] = from_f32<T>(acc[q]);
-                *(typename Frag<T>::half *)(u + uv_index(bi, grow - bi * TM, hv, 16 * vt + 4 * lg, HV, VD, uv_ss)) = o4;
-            }
-        }
-        typename Frag<T>::half wq[KD / 16];  // w[a_row][16kt + 4lg .. +3]
+            for (int j = 0; j < 2; ++j) {
+                const int a_row = 16 * (j ? rhi : rlo) + lc;
+                const bool row_ok = a_row < n;
+                const int64_t grow = r0 + a_row;
 #pragma unroll
-        for (int kt = 0; kt < KD / 16; ++kt) {
-            f32x4 acc = zero4();
+                for (int vt = 0; vt < VD / 16; ++vt) {
+                    const f32x4 acc = prod(j, Vs, LDV, vt);
+                    if (row_ok) {  // u is slice-major: 4 consecutive columns of the row
+                        typename Frag<T>::half o4;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks < nks) {
-                    FragT a = lds_col8<T>(Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * kt);
-                    acc = mma(a, bw[ks], acc);
-                    if constexpr (SPL) acc = mma(a, bwl[ks], acc);
+                        for (int q = 0; q < 4; ++q) o4[q] = from_f32<T>(acc[q]);
+                        *(typename Frag<T>::half *)(u + uv_index(bi, grow - bi * TM, hv, 16 * vt + 4 * lg, HV, VD, uv_ss)) = o4;
+                    }
                 }
             }
+        } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) wq[kt][q] = from_f32<T>(acc[q]);
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int kt = 0; kt < KD / 16; ++kt) {
+                    const f32x4 acc = prod(j, Ks, LDK, kt);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) wq[j][kt][q] = from_f32<T>(acc[q]);
+                }
         }
         // w leaves through the K tile's space so that every store writes
         // whole 128-byte lines (a lane's four columns are only 8 bytes)
         __syncthreads();  // every wave is done reading K
+        if (!do_u) {
 #pragma unroll
-        for (int kt = 0; kt < KD / 16; ++kt) *(typename Frag<T>::half *)(Ks + a_row * LDK + 16 * kt + 4 * lg) = wq[kt];
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int kt = 0; kt < KD / 16; ++kt)
+                    *(typename Frag<T>::half *)(Ks + (16 * (j ? rhi : rlo) + lc) * LDK + 16 * kt + 4 * lg) = wq[j][kt];
+        }
         __syncthreads();
         constexpr int WU = KD * (int)sizeof(T) / 16;  // 16-byte units per w row
         T *wdst = w + (r0 * HV + hv) * (int64_t)KD;
