@@ -306,24 +306,36 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // fp32 MFMA 16x16x4; T stays in registers and feeds the second product:
     // slot s of lane (g,c) holds T[4g+s][c], so step s contracts over rows
     // {4g+s} and reads A_ii[row][4g+s].
+    // Every operand of a level (up to three products L_im A_mj and A_ii) is
+    // read first, then the products run, so the reads overlap.
+#pragma unroll
     for (int lev = 1; lev < 4; ++lev) {
         if (wv < 4 - lev) {
             const int j = wv, i = wv + lev;
-            f32x4 t = zero4();
-            for (int m = j; m < i; ++m) {
+            float la[3][4], am[3][4], ai[4];
 #pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4) {
-                    const float a = Lm[(16 * i + lc) * LDA + 16 * m + k0 + lg];  // L_im, m < i
-                    const float b = a_at(16 * m + k0 + lg, 16 * j + lc);        // A_mj, m >= j
-                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+            for (int mm = 0; mm < 3; ++mm) {
+                if (mm < lev) {  // m = j + mm < i
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        la[mm][k] = Lm[(16 * i + lc) * LDA + 16 * (j + mm) + 4 * k + lg];  // L_im
+                        am[mm][k] = a_at(16 * (j + mm) + 4 * k + lg, 16 * j + lc);       // A_mj, m >= j
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ai[s] = Lm[(16 * i + lc) * LDA + 16 * i + 4 * lg + s];  // A_ii
+            f32x4 t = zero4();
+#pragma unroll
+            for (int mm = 0; mm < 3; ++mm) {
+                if (mm < lev) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) t = __builtin_amdgcn_mfma_f32_16x16x4f32(la[mm][k], am[mm][k], t, 0, 0, 0);
                 }
             }
             f32x4 r = zero4();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float a = Lm[(16 * i + lc) * LDA + 16 * i + 4 * lg + s];  // A_ii
-                r = __builtin_amdgcn_mfma_f32_16x16x4f32(a, t[s], r, 0, 0, 0);
-            }
+            for (int s = 0; s < 4; ++s) r = __builtin_amdgcn_mfma_f32_16x16x4f32(ai[s], t[s], r, 0, 0, 0);
             // A_ij, transposed: rows 16i + 4lg .. +3 of column 16j + lc
             *(f32x4 *)&Lm[(16 * j + lc) * LDA + 16 * i + 4 * lg] = -r;
         }
