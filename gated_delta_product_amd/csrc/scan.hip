@@ -365,43 +365,64 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
         if (c + 2 < nch) step(c + 2, I2{});
     }
 
-    // the segment's map, rows of X: [E (VD) | D (KD)]
+    // the segment's map: E ([KD][VD] fp32), then D as matrix-core A
+    // fragments of the scan's bf16 products, a high and a low part: 1 KiB
+    // block ((rt KD/32 + ks) 2 + part) holds D[16 rt + (L mod 16)][32 ks +
+    // 8 (L / 16) .. +7] in lane L's 16 bytes
     float *dst = maps + ((int64_t)s * HV + hv) * KD * XW;
+    if (is_e) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dst[(int64_t)kperm(kt, 4 * lg + q) * XW + 32 * wv + 16 * ct + lc] = xs[kt][ct][q];
+                for (int q = 0; q < 4; ++q)
+                    dst[(int64_t)kperm(kt, 4 * lg + q) * VD + 32 * wv + 16 * ct + lc] = xs[kt][ct][q];
+    } else {
+        bf16 *df = (bf16 *)(dst + KD * VD);
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = kperm(kt, 4 * lg + q), c = 32 * wv - VD + 16 * ct + lc;
+                    const int o = ((r >> 4) * (KD / 32) + (c >> 5)) * 1024 + (((c & 31) >> 3) * 16 + (r & 15)) * 8 + (c & 7);
+                    const bf16 hi = (bf16)xs[kt][ct][q];
+                    df[o] = hi;
+                    df[o + 512] = split_lo<bf16>(xs[kt][ct][q], hi);
+                }
+    }
 }
 
 // One block of KD / 32 waves per (value head, 16 value columns): the state
-// slice h[k][j0 .. j0+16) in LDS, carried over the segments in fp32:
+// slice h[k][j0 .. j0+16), carried over the segments in fp32 registers:
 // hstart[s] is the state S entering segment s ([nseg, HV, VD, KD], the
-// layout of initial states), hstart[s+1] = D_s hstart[s] + E_s.  The product
-// runs on fp32 matrix-core tiles (16x16x4): wave w owns rows
-// [32 w, 32 w + 32) of the result.  D_s is staged in LDS by coalesced loads;
-// the maps travel through two register sets, each loaded two segments ahead
-// of its use.  Block 0 also writes the segment offsets cu[0..nseg] (tokens).
-// With packed requests (req_first set) the grid holds per_req blocks per
-// request r, each running the same pass over r's segments req_first[r] ..
-// + req_nseg[r] - 1 of the plan, from r's initial state; the plan kernel
-// has written the offsets.
+// layout of initial states), hstart[s+1] = D_s hstart[s] + E_s.  Wave w owns
+// rows [32 w, 32 w + 32) of the result, as two 16x16 tiles.  The product
+// runs on bf16 matrix-core tiles with each operand split into a high and a
+// low bf16 part (D_s as the map kernel stored it, the state split here):
+// D h = Dhi hhi + Dhi hlo + Dlo hhi, the dropped Dlo hlo term and the
+// parts' rounding about 2^-16 of each product, with fp32 accumulation.
+// Each wave loads its rows of D_s straight into its A fragments (one 1 KiB
+// block per instruction), two segments ahead of their use, through two
+// register sets; the state's parts go through LDS (two buffers, one barrier
+// per segment) as the B operand.  Block 0 also writes the segment offsets
+// cu[0..nseg] (tokens).  With packed requests (req_first set) the grid holds
+// per_req blocks per request r, each running the same pass over r's
+// segments req_first[r] .. + req_nseg[r] - 1 of the plan, from r's initial
+// state; the plan kernel has written the offsets.
 template <int KD, int VD>
 __global__ void __launch_bounds__(KD * 2)
 gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int nseg, int HV, int64_t seg_tok,
                int64_t Ttok, float *__restrict__ hstart, int32_t *__restrict__ cu,
                const int32_t *__restrict__ req_first, const int32_t *__restrict__ req_nseg, int per_req) {
     constexpr int XW = KD + VD;
-    constexpr int NT = KD * 2;       // threads
     constexpr int CB = 16;           // value columns per block
-    constexpr int DU = KD * KD / 4;  // float4 units of D
-    constexpr int NDU = DU / NT;     // per thread
-    constexpr int LDD = KD + 4;      // LDS row stride of D (floats)
+    constexpr int NKS = KD / 32;     // contraction steps
+    constexpr int LDB = 2 * KD + 8;  // LDS row stride of the state's parts (bf16)
     constexpr int SL = VD / CB;      // slices per head
-    __shared__ __attribute__((aligned(16))) float Ds[KD * LDD];
-    __shared__ __attribute__((aligned(16))) float Hs[KD * CB];
+    __shared__ __attribute__((aligned(16))) bf16 Hb[2][CB * LDB];  // row j: h[0..KD)[j] high, then low
 
     // block -> (value head, slice): the slices of one head share an XCD
     // (blocks i and i + 8 do), so each D_s comes from HBM once per head and
@@ -426,73 +447,81 @@ gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int
     if (hv >= HV || nseg <= 0) return;
     const int lane = lane_id(), wv = wave_id();
     const int lg = lane >> 4, lc = lane & 15;
+    // this lane's state entries: h[32 wv + 16 t + 4 lg + q][j0 + lc], in the
+    // [VD, KD] layout four consecutive floats
+    const int64_t so = (int64_t)(j0 + lc) * KD + 32 * wv + 4 * lg;
 
-    // the map of segment s in flight in registers: this thread's share of D_s
-    // (coalesced) and its result tiles' entries of E_s
+    // the map of segment s in flight in registers: this wave's A fragments
+    // of D_s (tiles 2 wv + t) and its result tiles' entries of E_s
     struct MapRegs {
-        f32x4 d[NDU];
+        bf16x8 a[2][NKS][2];
         f32x4 e[2];
     };
     auto load_map = [&](MapRegs &R, int s) {
         const float *m = maps + ((int64_t)s * HV + hv) * KD * XW;
-#pragma unroll
-        for (int i = 0; i < NDU; ++i) {
-            const int id = tid + NT * i, r = id / (KD / 4), c4 = id % (KD / 4);
-            R.d[i] = *(const f32x4 *)(m + (int64_t)r * XW + VD + 4 * c4);
-        }
+        const bf16 *df = (const bf16 *)(m + KD * VD) + 8 * lane;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) R.e[t][q] = m[(int64_t)(32 * wv + 16 * t + 4 * lg + q) * XW + j0 + lc];
-    };
-    // state rows are written out by (row, 8 columns) per thread: coalesced over rows
-    auto write_state = [&](int s) {
-        float *out = hstart + ((int64_t)s * HV + hv) * VD * KD;
-        const int k = tid % KD, c0 = (tid / KD) * 8;
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out[(int64_t)(j0 + c0 + i) * KD + k] = Hs[k * CB + c0 + i];
+                for (int p = 0; p < 2; ++p)
+                    R.a[t][ks][p] = *(const bf16x8 *)(df + (((2 * wv + t) * NKS + ks) * 2 + p) * 512);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) R.e[t][q] = m[(int64_t)(32 * wv + 16 * t + 4 * lg + q) * VD + j0 + lc];
+    };
+    auto write_state = [&](int s, const f32x4 (&h)[2]) {
+        float *out = hstart + ((int64_t)s * HV + hv) * VD * KD + so;
+        *(f32x4 *)out = h[0];
+        *(f32x4 *)(out + 16) = h[1];
     };
     // initial state (S = h^T, V x K)
-    {
-        const int k = tid % KD, c0 = (tid / KD) * 8;
+    f32x4 cur[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Hs[k * CB + c0 + i] = h0 ? h0[((int64_t)hv * VD + j0 + c0 + i) * KD + k] : 0.f;
-    }
+    for (int t = 0; t < 2; ++t) cur[t] = h0 ? *(const f32x4 *)(h0 + (int64_t)hv * VD * KD + so + 16 * t) : zero4();
     const int nm = nseg - 1;  // maps to apply
     MapRegs R0, R1;
     if (nm > 0) load_map(R0, 0);
     if (nm > 1) load_map(R1, 1);
-    // state entering segment s -> hstart[s], then apply map s (from R).  The
-    // next loads into R are issued before this step's stores, so the wait
-    // before storing a set into LDS leaves the other set in flight; the
-    // barriers order LDS only.
+    // state entering segment s (cur) -> hstart[s], then apply map s (from
+    // R) and reload R for segment s + 2.  Buffer s % 2 of Hb is rewritten
+    // two segments later, after every wave has passed the next barrier and
+    // so finished its reads of it.
     auto step = [&](int s, MapRegs &R) {
-        lds_barrier();  // Hs holds the state entering segment s; Ds is free
+        bf16 *hb = Hb[s & 1];
 #pragma unroll
-        for (int i = 0; i < NDU; ++i) {
-            const int id = tid + NT * i, r = id / (KD / 4), c4 = id % (KD / 4);
-            *(f32x4 *)(&Ds[r * LDD + 4 * c4]) = R.d[i];
+        for (int t = 0; t < 2; ++t) {
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                hi[q] = (bf16)cur[t][q];
+                lo[q] = split_lo<bf16>(cur[t][q], hi[q]);
+            }
+            const int k0 = 32 * wv + 16 * t + 4 * lg;
+            *(bf16x4 *)(&hb[lc * LDB + k0]) = hi;
+            *(bf16x4 *)(&hb[lc * LDB + KD + k0]) = lo;
         }
+        write_state(s, cur);
         f32x4 acc[2] = {R.e[0], R.e[1]};
-        if (s + 2 < nm) load_map(R, s + 2);  // in flight for two segments
-        write_state(s);
-        lds_barrier();  // Ds holds D_s
-        // acc[t] += D[32wv + 16t + .., 4ks + ..] h[4ks + .., ..]: lane holds
-        // A[lc][lg] = D[row][4ks + lg] and B[lg][lc] = h[4ks + lg][lc]
-#pragma unroll 8
-        for (int ks = 0; ks < KD / 4; ++ks) {
-            const float b = Hs[(4 * ks + lg) * CB + lc];
+        lds_barrier();  // Hb[s % 2] holds the state
+        // acc[t] += D[32wv + 16t + .., 32ks + ..] h[32ks + .., ..]: lane holds
+        // A[lc][8lg .. +7] = D[row][32ks + 8lg ..] and B = h[32ks + 8lg ..][lc]
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 bh = *(const bf16x8 *)(&hb[lc * LDB + 32 * ks + 8 * lg]);
+            const bf16x8 bl = *(const bf16x8 *)(&hb[lc * LDB + KD + 32 * ks + 8 * lg]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const float a = Ds[(32 * wv + 16 * t + lc) * LDD + 4 * ks + lg];
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
+                acc[t] = mma(R.a[t][ks][1], bh, acc[t]);
+                acc[t] = mma(R.a[t][ks][0], bl, acc[t]);
+                acc[t] = mma(R.a[t][ks][0], bh, acc[t]);
             }
         }
-        lds_barrier();  // every wave has read Hs and Ds
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) Hs[(32 * wv + 16 * t + 4 * lg + q) * CB + lc] = acc[t][q];
+        if (s + 2 < nm) load_map(R, s + 2);  // in flight for two segments
+        cur[0] = acc[0];
+        cur[1] = acc[1];
     };
     int s = 0;
     for (; s + 1 < nm; s += 2) {
@@ -500,8 +529,7 @@ gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int
         step(s + 1, R1);
     }
     if (s < nm) step(s, R0);
-    lds_barrier();
-    write_state(nm);  // the state entering the last segment
+    write_state(nm, cur);  // the state entering the last segment
 }
 
 // Segment plan of packed requests (one block): request r of length L_r is
