@@ -155,11 +155,22 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 
     auto clamp_rows = [](int r) { return r < 0 ? 0 : (r < C ? r : C); };
     auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
-    // byte offset of element column `col` of half-tile row r (swizzled)
-    auto swz = [&](int r, int col) {
+    // 16-byte units of half-tile row r are XOR-swizzled by xw(r) in the w
+    // tiles and by xk(r) in the K tiles.  The K tiles are read both as rows
+    // (scores) and transposed (phase 2, ds_read_b64_tr_b16); with 128-byte
+    // rows, r mod 8 keeps the transposed reads free of bank conflicts and
+    // leaves the row reads 2-way, where (r / 2) mod 8 gave the reverse
+    // (rocprofv3 SQ_LDS_BANK_CONFLICT: 2.5e7 -> 0.9e7 cycles per launch at
+    // the benchmark shape, 6 us less)
+    auto xw = [](int r) { return (r >> 1) & (UPR - 1); };
+    auto xk = [](int r) { return UPR == 8 ? r & 7 : (r >> 1) & (UPR - 1); };
+    // byte offset of element column `col` of half-tile row r, w or K tile
+    auto swz_at = [&](int r, int col, int x) {
         const int b = col * ES;
-        return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
+        return r * RB + ((((b >> 4) ^ x)) << 4) + (b & 15);
     };
+    auto swz = [&](int r, int col) { return swz_at(r, col, xw(r)); };
+    auto swzk = [&](int r, int col) { return swz_at(r, col, xk(r)); };
 
     const int ntok = (int)(eos - bos);
     // x / M as __umulhi(x, mdiv): exact for every x < 2^31 when M is 2, 3 or 4
@@ -315,7 +326,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                 for (int kw = 0; kw < 2; ++kw)
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        kr[st][kw][ks] = *(const FragT *)((const char *)Sg.k[kw] + swz(16 * st + lc, 32 * ks + 8 * lg));
+                        kr[st][kw][ks] = *(const FragT *)((const char *)Sg.k[kw] + swzk(16 * st + lc, 32 * ks + 8 * lg));
                 gr4[st] = *(const f32x4 *)(&Grow[tt][C * m + 16 * st + 4 * lg]);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep the reads together, ahead of their uses
@@ -418,7 +429,7 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
 #pragma unroll
     for (int i = 0; i < UPR; ++i) {
         const int r = i * RPI + lane / UPR;
-        const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
+        const int unit = (lane % UPR) ^ (rw ? xw(r) : xk(r));
         ot[i] = (uint32_t)((rw ? r * ldw * ES : 0) + hh * KH * ES + unit * 16 - 1024 * (i % 4));
     }
     // element offset of expanded row e0 + r from the token holding row e0
@@ -581,9 +592,9 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                     const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
                     const int col = kbase + 8 * (j & 3);
                     const HalfT x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swzk(ra, col)))));
                     const HalfT x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swzk(rb, col)))));
                     ka[kw][kt][s] = join<bf16>(x0, x1);
                 }
         const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;

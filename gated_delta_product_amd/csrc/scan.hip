@@ -38,7 +38,7 @@ __device__ __forceinline__ int kperm(int kt, int i) { return 32 * (kt >> 1) + 8 
 // LDS ring of the map kernel, NS stages of one chunk each, grouped by tile
 // so that every fragment read is one per-lane offset register plus a
 // compile-time offset below 64 KiB: the w and K tiles (rows of KD
-// elements, 16-byte units XOR-swizzled by row), the u tile in 16-column
+// elements, 16-byte units XOR-swizzled by a function of the row), the u tile in 16-column
 // slices as in HBM, and the per-row key decays and cumulative decays.
 template <int KD, int VD, int NS>
 struct MapRing {
@@ -115,11 +115,19 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     // unit), so output lane i receives column kperm(kt, i):
     // o2[kt / 2] + 8 (kt % 2) + st TS + (32s + 16h) RB (tiles 2i and 2i + 1
     // read the two halves of the same 16-byte unit)
+    // The K tile's units are XOR-swizzled by xk(row mod 16), the w tile's by
+    // the row.  With 256-byte rows (KD = 128) the 16 lanes of a group read
+    // 4 rows x 4 units; xk's two bit fields put those 16 reads on 16
+    // different units, where the row itself put them on 4 (rocprofv3
+    // SQ_LDS_BANK_CONFLICT 2.4e7 -> 0.8e7 cycles per launch at the
+    // benchmark shape, 6 us less; every lane still reads the same half of
+    // its unit, so two groups of a 32-lane pass share the banks).
+    auto xk = [](int r) { return UPR == 16 ? ((r & 3) << 2) | ((r >> 2) & 3) : r & (UPR - 1); };
     uint32_t o2[NKT / 2];
     const int ra0 = 4 * lg + (j >> 2);
 #pragma unroll
     for (int kp = 0; kp < NKT / 2; ++kp)
-        o2[kp] = (uint32_t)(OK + ra0 * RB + ((((4 * kp + (j & 3)) ^ ra0) & (UPR - 1)) << 4));
+        o2[kp] = (uint32_t)(OK + ra0 * RB + ((((4 * kp + (j & 3)) ^ xk(ra0)) & (UPR - 1)) << 4));
     // u slice 2wv + ct, rows 16rt + 4lg + j/4, columns 4(j%4): ou + st US + ct 2048 + rt 512
     const uint32_t ou = (uint32_t)(OU + (is_e ? 2 * wv : 0) * 2048 + (4 * lg + (j >> 2)) * 32 + 8 * (j & 3));
     const uint32_t okd = (uint32_t)(OD + 16 * lg);
@@ -155,9 +163,8 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     for (int jj = 0; jj < NJT; ++jj) {
         const int byte = 1024 * (wv + NW * jj) + 16 * lane;
         const int r = byte / RB, us = (byte % RB) / 16;
-        const uint32_t unit = (uint32_t)(16 * ((us ^ r) & (UPR - 1)));
-        ow[jj] = (uint32_t)(r * ldw_b) + unit;
-        okk[jj] = unit + (kfix ? (uint32_t)(krel(r0, r) * 2) : 0u);
+        ow[jj] = (uint32_t)(r * ldw_b) + (uint32_t)(16 * ((us ^ r) & (UPR - 1)));
+        okk[jj] = (uint32_t)(16 * ((us ^ xk(r & 15)) & (UPR - 1))) + (kfix ? (uint32_t)(krel(r0, r) * 2) : 0u);
         krow[jj] = r;
     }
     // LDS destinations of this wave's slots in stage 0 (slot jj adds
