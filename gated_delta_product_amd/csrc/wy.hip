@@ -24,7 +24,7 @@
 // L and A share one LDS array: A's diagonal blocks replace L's (dead once
 // solved) and its lower blocks are stored transposed in the upper triangle,
 // which L leaves unused; the lower blocks of L stay intact until the last
-// level.  With that array, the K tile and the gates the block takes about
+// level, after which A's lower blocks move into their place.  With that array, the K tile and the gates the block takes about
 // 35 KB of LDS at K = V = 128 bf16, so four blocks share a CU.
 // u and w are computed transposed (u^T = V^T A1^T) so each lane ends up with
 // four consecutive columns of one output row, stored as one 8-byte write.
@@ -342,6 +342,21 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
         __syncthreads();
     }
 
+    // ---- the lower blocks of A into place (row-major, over L's dead lower
+    // blocks), so that each lane's 8 elements of a row of A below are two
+    // 16-byte reads: read down a column of the transposed copy they put
+    // 4 lanes on one bank, about 10 us of bank-conflict stalls per launch
+    // at the benchmark shape
+    {
+        const int r = tid & 15, c = tid >> 4;  // element [r][c] of each block
+#pragma unroll
+        for (int b = 0; b < 6; ++b) {
+            const int i = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3), j = b < 3 ? 0 : (b < 5 ? 1 : 2);  // (1,0) .. (3,2)
+            Lm[(16 * i + r) * LDA + 16 * j + c] = Lm[(16 * j + c) * LDA + 16 * i + r];
+        }
+    }
+    __syncthreads();
+
     // ---- u^T = V^T (A diag(beta))^T and w^T = Khat^T (A diag(beta e^gamma r))^T
     //      over the four 16-row blocks of output rows.  Blocks 2 and 3
     //      contract over two 32-row steps of A, blocks 0 and 1 over one, so
@@ -363,11 +378,13 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
             const int b0 = 32 * ks + 8 * lg, bb = b0 >> 4;  // A[a_row][b0 .. b0 + 7], block bb
             const float *fv = do_u ? s_beta : s_ws;
             const f32x4 f0 = *(const f32x4 *)&fv[b0], f1 = *(const f32x4 *)&fv[b0 + 4];
+            // blocks on or below the diagonal are row-major; the ones past it are 0
+            const f32x4 v0 = *(const f32x4 *)&Lm[a_row * LDA + b0], v1 = *(const f32x4 *)&Lm[a_row * LDA + b0 + 4];
             float av[8];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int addr = bb == rt ? a_row * LDA + b0 + m : (b0 + m) * LDA + a_row;
-                av[m] = bb <= rt ? Lm[addr] : 0.f;
+            for (int m = 0; m < 4; ++m) {
+                av[m] = bb <= rt ? v0[m] : 0.f;
+                av[4 + m] = bb <= rt ? v1[m] : 0.f;
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
