@@ -181,11 +181,19 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
     auto clamp_rows = [](int r) { return r < 0 ? 0 : (r < C ? r : C); };
     // bytes a buffer resource must cover for n rows of `width_b` bytes
     auto span = [](int n, int stride_b, int width_b) { return (uint32_t)(n > 0 ? (n - 1) * stride_b + width_b : 0); };
-    // byte offset of element column `col` of half-tile row r (swizzled)
-    auto swz = [&](int r, int col) {
+    // 16-byte units of half-tile row r are XOR-swizzled by xw(r) in the w
+    // tiles and by xk(r) in the K tiles, which are only read transposed:
+    // for bf16 128-byte rows r mod 8 keeps those reads at the 2-way bank
+    // floor of same-half 8-byte reads, where (r / 2) mod 8 made them 4-way
+    auto xw = [](int r) { return (r >> 1) & (UPR - 1); };
+    auto xk = [](int r) { return (UPR == 8 && ES == 2) ? r & 7 : (r >> 1) & (UPR - 1); };
+    // byte offset of element column `col` of half-tile row r, w or K tile
+    auto swz_at = [&](int r, int col, int x) {
         const int b = col * ES;
-        return r * RB + ((((b >> 4) ^ ((r >> 1) & (UPR - 1)))) << 4) + (b & 15);
+        return r * RB + ((((b >> 4) ^ x)) << 4) + (b & 15);
     };
+    auto swz = [&](int r, int col) { return swz_at(r, col, xw(r)); };
+    auto swzk = [&](int r, int col) { return swz_at(r, col, xk(r)); };
 
     if (wave == NC + 2) {
         // ======================= prefetch wave =======================
@@ -258,7 +266,7 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
 #pragma unroll
         for (int i = 0; i < UPR; ++i) {
             const int r = i * RPI + lane / UPR;
-            const int unit = (lane % UPR) ^ ((r >> 1) & (UPR - 1));
+            const int unit = (lane % UPR) ^ (mw == 0 ? xw(r) : xk(r));
             const int ld = mw == 0 ? ldw : ldk;
             ot[0][i] = (uint32_t)((r * ld) * ES + unit * 16 - 1024 * (i % 4));
             ot[1][i] = ot[0][i] + KH * ES;  // second K half of the same rows
@@ -500,15 +508,15 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                     const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
                     const int col = kbase + 8 * (j & 3);
                     x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swzk(ra, col)))));
                     x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swzk(rb, col)))));
                 } else {
                     const int col = kbase + 8 * (lc >> 2) + (lc & 3);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        x0[i] = *(const float *)(kb + swz(32 * s + 4 * lg + i, col));
-                        x1[i] = *(const float *)(kb + swz(32 * s + 16 + 4 * lg + i, col));
+                        x0[i] = *(const float *)(kb + swzk(32 * s + 4 * lg + i, col));
+                        x1[i] = *(const float *)(kb + swzk(32 * s + 16 + 4 * lg + i, col));
                     }
                 }
                 ka[kt][s] = join<T>(x0, x1);
@@ -671,9 +679,9 @@ gdp_chunk_h_k(const T *__restrict__ k, const float *__restrict__ kdecay, const T
                     const int ra = 32 * s + 4 * lg + (j >> 2), rb = ra + 16;
                     const int col = kbase + 8 * (j & 3);
                     const HalfT x0 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(ra, col)))));
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swzk(ra, col)))));
                     const HalfT x1 = __builtin_bit_cast(HalfT, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swz(rb, col)))));
+                        (lds_i16x4 *)((__attribute__((address_space(3))) const char *)(kb + swzk(rb, col)))));
                     ka[kw][kt][s] = join<T>(x0, x1);
                 }
         const float gl = n > 0 ? __builtin_amdgcn_exp2f(glast) : 1.0f;

@@ -348,7 +348,9 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     // 4 lanes on one bank, about 10 us of bank-conflict stalls per launch
     // at the benchmark shape
     {
-        const int r = tid & 15, c = tid >> 4;  // element [r][c] of each block
+        // element [r][c] of each block; this lane order keeps both the column
+        // reads and the row writes of every wave on 64 different banks
+        const int r = tid & 15, c = (4 * ((tid >> 4) & 3) + r + (tid >> 6)) & 15;
 #pragma unroll
         for (int b = 0; b < 6; ++b) {
             const int i = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3), j = b < 3 ? 0 : (b < 5 ? 1 : 2);  // (1,0) .. (3,2)
