@@ -369,8 +369,7 @@ __device__ __forceinline__ void stage_tile(T *dst, const T *src, int64_t rs, int
                 const float f = to_f32(e[i]);
                 s += f * f;
             }
-#pragma unroll
-            for (int d = 1; d < UPR; d <<= 1) s += __shfl_xor(s, d, 64);
+            s = group_sum<UPR>(s);
             if (cu == 0) ssq[row] = s;
         }
     }

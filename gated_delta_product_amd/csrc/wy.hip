@@ -211,8 +211,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 const float f = to_f32(el[i]);
                 sq += f * f;
             }
-#pragma unroll
-            for (int d = 1; d < KUPR; d <<= 1) sq += __shfl_xor(sq, d, 64);
+            sq = group_sum<KUPR>(sq);  // DPP within 16 lanes, bit for bit the xor butterfly
             if (cu16 == 0) s_rk[row] = sq;
         }
     } else {
