@@ -140,12 +140,23 @@ __device__ __forceinline__ typename Frag<T>::type lds_col8(const T *X, int strid
 }
 
 // ---------------------------------------------------------------- wave scans
+// x moved across lanes by a DPP pattern; rows outside row_mask, and lanes
+// whose source lies outside their row, receive 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP moves only (no
+// LDS permutes): a Hillis-Steele scan inside each row of 16 lanes (shifts
+// by 1, 2, 4, 8), then row 1 and row 3 add the last lane of the row before
+// (row_bcast:15), then rows 2 and 3 add lane 31 (row_bcast:31).
 __device__ __forceinline__ float wave_inclusive_sum(float x) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        float y = __shfl_up(x, d, 64);
-        if (lane_id() >= d) x += y;
-    }
+    x += dpp_or_zero<0x111>(x);  // row_shr:1
+    x += dpp_or_zero<0x112>(x);  // row_shr:2
+    x += dpp_or_zero<0x114>(x);  // row_shr:4
+    x += dpp_or_zero<0x118>(x);  // row_shr:8
+    x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
 
