@@ -228,9 +228,8 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
                         const float x = (float)qs[kw][ks][i];
                         ss += x * x;
                     }
-            ss += __shfl_xor(ss, 16, 64);
-            ss += __shfl_xor(ss, 32, 64);
-            Gq = __shfl(Gl, 16 * tt + lc, 64) + __builtin_amdgcn_logf(scale / sqrtf(ss + 1e-6f));
+            ss = xor32_sum(xor16_sum(ss));
+            Gq = row_broadcast(Gl, tt) + __builtin_amdgcn_logf(scale / sqrtf(ss + 1e-6f));
         };
         // O^T tiles: oa[ct] holds o[token 16 tt + lc][64 slg + 16 ct + 4 lg + r]
         f32x4 oa[NP];

@@ -176,8 +176,7 @@ gdp_chunk_o_k(const T *__restrict__ q, const T *__restrict__ k, const float *__r
             const float x = to_f32(qf[ks][i]);
             ss += x * x;
         }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
+    ss = xor32_sum(xor16_sum(ss));
     const float fq = scale / sqrtf(ss + 1e-6f);  // scale * rnorm(q_t)
     const float Gt = sG[wv][t_loc];
 

@@ -260,6 +260,27 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Cross-row moves on gfx950's permlane swaps (VALU, no LDS permutes).
+// v_permlane16_swap exchanges the odd 16-lane rows of one operand with the
+// even rows of the other, v_permlane32_swap the upper half of one with the
+// lower half of the other; with both operands x the two results together
+// hold x and its partner row in every lane.
+__device__ __forceinline__ float xor16_sum(float x) {  // x + x[lane ^ 16], bit for bit
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {  // x + x[lane ^ 32], bit for bit
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x[16 row + lane % 16] in every lane (row wave-uniform, 0..3)
+__device__ __forceinline__ float row_broadcast(float x, int row) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t b = row < 2 ? a[0] : a[1];  // rows (row & ~1, row | 1) twice
+    const auto c = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return __uint_as_float((row & 1) ? c[1] : c[0]);
+}
+
 // Block-cooperative lookup of linear item `id` over sequences, where
 // sequence i owns ceil(len_i * rows_per_token / chunk) consecutive items.
 // Every thread of the block must call it (it uses barriers); wave 0 scans
