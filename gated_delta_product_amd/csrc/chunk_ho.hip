@@ -25,7 +25,7 @@
 //   bit), and publishes to LDS the chunk's v_new (fp16, one buffer per step
 //   parity) and, at the end of each token chunk, the state entering the next
 //   one (bf16).  They also stream each chunk into a three-stage LDS ring,
-//   two chunks ahead (buffer loads with the LDS destination; the range
+//   chunk c + 2 late in step c (buffer loads with the LDS destination; the range
 //   check zero-fills rows past the end): wave p a half tile of w (p < 2) or
 //   K (p >= 2), its u slice and (p < 2) one of kdecay and gcum.
 // * Output waves 4-7.  Wave 4 + t owns output token tile t (tokens 16t ..
@@ -543,8 +543,6 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
     lds_barrier();  // stage 0 landed; the initial state exchange is visible
     int rem = (int)rows;
     for (int c = 0, st_ = 0; c < nch; ++c, st_ = st_ == NS - 1 ? 0 : st_ + 1) {
-        // chunk c + 2 into the stage chunk c - 1 left (freed by the last barrier)
-        issue(st_ == 0 ? 2 : st_ - 1);
         const HoStage<KD> &Sg = ring[st_];
         const int n = __builtin_amdgcn_readfirstlane(clamp_rows(rem));  // valid rows of the chunk
         const int ti = (int)__umulhi((uint32_t)c, mdiv);
@@ -603,6 +601,12 @@ gdp_chunk_ho_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restri
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) hs[kw][kt][r] *= gl;
+        // chunk c + 2 into the stage chunk c - 1 left (free since the last
+        // barrier), issued after this step's products and reads: at the top
+        // of the step the DMA issue, waiting on the CU's vector memory path,
+        // held back phase 1 (about 7 us), and one step is time enough for
+        // the loads
+        issue(st_ == 0 ? 2 : st_ - 1);
         wait_ring();    // chunk c + 1 landed
         lds_barrier();  // ring stage c read; the exchanges of chunk c - 1 were read
 

@@ -57,8 +57,9 @@ struct MapRing {
 // indices per lane and the w operand of phase 1 is one 16-byte row read.
 // Columns below VD are E (fed by u), the others D.  Each chunk streams from
 // HBM straight into the three-stage LDS ring (buffer loads with the LDS as
-// destination, issued two chunks ahead and shared out over all waves), so a
-// chunk's loads have two steps to land and hold no registers.
+// destination, chunk c + 2's issued late in step c and shared out over all
+// waves), so a chunk's loads have more than a step to land and hold no
+// registers.
 template <int KD, int VD>
 __global__ void __launch_bounds__((KD + VD) * 2)
 gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restrict__ w,
@@ -277,7 +278,6 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
     auto step = [&](int c, auto stc) {
         constexpr int ST = decltype(stc)::value;
         const bool more = c + 2 < nch;  // uniform
-        if (more) issue(std::integral_constant<int, (ST + 2) % NS>{});
 
         // phase 1: P = w X (64 x 32), contraction order of xb
         f32x4 acc[4][2];
@@ -345,6 +345,10 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
                 xs[kt][1] = mma(a, vb[1], xs[kt][1]);
             }
         }
+        // chunk c + 2's loads, issued after this step's products: at the top
+        // of the step their issue, waiting on the CU's vector memory path,
+        // held back phase 1 (3 us)
+        if (more) issue(std::integral_constant<int, (ST + 2) % NS>{});
         // chunk c + 1: this wave's loads have landed (all but this step's
         // own), and its key blocks go to fp16 for the next step
         if (c + 1 < nch) {
