@@ -238,28 +238,6 @@ __device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
     return x;
 }
 
-// x moved across lanes by a DPP pattern (every source lane is in range for
-// the patterns used here).
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// Sum over each aligned group of N consecutive lanes (N a power of two up to
-// 64); every lane of the group gets the same bits.  Within 16 lanes the
-// partners come from DPP: swap neighbours, swap pairs, mirror the half row,
-// mirror the row -- after each step all lanes of the growing group agree.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
-    if constexpr (N >= 2) x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
-    if constexpr (N >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
-    if constexpr (N >= 8) x += dpp_move<0x141>(x);  // row_half_mirror
-    if constexpr (N >= 16) x += dpp_move<0x140>(x); // row_mirror
-    if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
-    if constexpr (N >= 64) x += __shfl_xor(x, 32, 64);
-    return x;
-}
-
 // Cross-row moves on gfx950's permlane swaps (VALU, no LDS permutes).
 // v_permlane16_swap exchanges the odd 16-lane rows of one operand with the
 // even rows of the other, v_permlane32_swap the upper half of one with the
@@ -279,6 +257,29 @@ __device__ __forceinline__ float row_broadcast(float x, int row) {
     const uint32_t b = row < 2 ? a[0] : a[1];  // rows (row & ~1, row | 1) twice
     const auto c = __builtin_amdgcn_permlane16_swap(b, b, false, false);
     return __uint_as_float((row & 1) ? c[1] : c[0]);
+}
+
+// x moved across lanes by a DPP pattern (every source lane is in range for
+// the patterns used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over each aligned group of N consecutive lanes (N a power of two up to
+// 64); every lane of the group gets the same bits.  Within 16 lanes the
+// partners come from DPP: swap neighbours, swap pairs, mirror the half row,
+// mirror the row -- after each step all lanes of the growing group agree;
+// across rows from the permlane swaps.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+    if constexpr (N >= 2) x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (N >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (N >= 8) x += dpp_move<0x141>(x);  // row_half_mirror
+    if constexpr (N >= 16) x += dpp_move<0x140>(x); // row_mirror
+    if constexpr (N >= 32) x = xor16_sum(x);
+    if constexpr (N >= 64) x = xor32_sum(x);
+    return x;
 }
 
 // Block-cooperative lookup of linear item `id` over sequences, where

@@ -245,12 +245,37 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
     }
     __syncthreads();
 
+    // ---- diagonal 16x16 block d of A by forward substitution (lane =
+    // column), in place of L's: every row of the block is read before any is
+    // written.  It needs only L's diagonal tile d, which the same wave has
+    // just written (one wave's LDS accesses complete in order).
+    auto solve_diag = [&](int d0) {
+        if (lane < 16) {
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s = (i == lane) ? 1.f : 0.f;
+                f32x4 lr[4];  // row i of the diagonal block (same address in every lane)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (4 * q < i) lr[q] = *(const f32x4 *)&Lm[(d0 + i) * LDA + d0 + 4 * q];
+#pragma unroll
+                for (int b = 0; b < i; ++b) s -= lr[b >> 2][b & 3] * x[b];
+                x[i] = s;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Lm[(d0 + i) * LDA + d0 + lane] = x[i];
+        }
+    };
+
     // ---- L = strictly lower beta_a exp(g_a - g_b) r_a r_b (K K^T)_ab: the
     // ten 16x16 tiles (rt, ct <= rt) shared out three, three, two and two
-    // over the waves (row block by row block, the last wave would take four).
-    // Tile (rt, ct) is coded rt * 4 + ct, one byte per tile of a wave.
+    // over the waves, each wave's first tile a diagonal one, whose block of
+    // A it then solves at once, so the solves overlap the other waves' tiles
+    // and need no barrier of their own.  Tile (rt, ct) is coded rt * 4 + ct,
+    // one byte per tile of a wave.
     {
-        const uint32_t tiles = wv == 0 ? 0x000D0C00u : (wv == 1 ? 0x000E0504u : (wv == 2 ? 0x00000908u : 0x00000F0Au));
+        const uint32_t tiles = wv == 0 ? 0x000D0C00u : (wv == 1 ? 0x000E0405u : (wv == 2 ? 0x0000080Au : 0x0000090Fu));
         const int ntile = wv < 2 ? 3 : 2;
         for (int it = 0; it < ntile; ++it) {
             const int code = (int)((tiles >> (8 * it)) & 0xffu), rt = code >> 2, ct = code & 3;
@@ -273,29 +298,7 @@ gdp_wy_k(const T *__restrict__ k, const T *__restrict__ v, const float *__restri
                 const float val = col < row ? b4[i] * r4[i] * rc * __expf(gr[i] - gc) * acc[i] : 0.f;
                 Lm[row * LDA + col] = val;
             }
-        }
-    }
-    __syncthreads();
-
-    // ---- diagonal 16x16 blocks of A by forward substitution (lane = column),
-    // in place of L's: every row of the block is read before any is written
-    {
-        const int d0 = 16 * wv;
-        if (lane < 16) {
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == lane) ? 1.f : 0.f;
-                f32x4 lr[4];  // row i of the diagonal block (same address in every lane)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (4 * q < i) lr[q] = *(const f32x4 *)&Lm[(d0 + i) * LDA + d0 + 4 * q];
-#pragma unroll
-                for (int b = 0; b < i; ++b) s -= lr[b >> 2][b & 3] * x[b];
-                x[i] = s;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) Lm[(d0 + i) * LDA + d0 + lane] = x[i];
+            if (it == 0) solve_diag(ra);  // the wave's diagonal tile (rt == ct == wv)
         }
     }
     __syncthreads();
