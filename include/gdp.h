@@ -475,9 +475,10 @@ gdp_status gdp_prefill_fwd_scan(const gdp_prepare_args *p, const gdp_chunk_args 
 int32_t gdp_scan_segments(int64_t T, int32_t num_segments);
 
 /* Workspace bytes gdp_chunk_fwd_scan needs for one sequence: per value
-   head, a K x (V + K) fp32 map for every segment but the last and a V x K
-   fp32 state for every segment, plus the segment offsets; -1 on bad
-   arguments. */
+   head, a map of K x (V + K) floats' bytes for every segment but the last
+   (E in fp32, then D as a high and a low bf16 part) and a V x K fp32 state
+   for every segment, plus the segment offsets; -1 on bad arguments.  The
+   workspace is opaque to the caller. */
 int64_t gdp_scan_workspace_bytes(int64_t T, int32_t HV, int32_t K, int32_t V, int32_t num_segments);
 
 /* Workspace bytes gdp_chunk_fwd_scan needs for num_seqs packed requests of T
