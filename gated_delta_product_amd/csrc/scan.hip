@@ -376,19 +376,22 @@ gdp_seg_map_k(QKRows qk, const float *__restrict__ kdecay, const bf16 *__restric
         if (c + 2 < nch) step(c + 2, I2{});
     }
 
-    // the segment's map: E ([KD][VD] fp32), then D as matrix-core A
+    // the segment's map: E (KD x VD fp32, below), then D as matrix-core A
     // fragments of the scan's bf16 products, a high and a low part: 1 KiB
     // block ((rt KD/32 + ks) 2 + part) holds D[16 rt + (L mod 16)][32 ks +
     // 8 (L / 16) .. +7] in lane L's 16 bytes
     float *dst = maps + ((int64_t)s * HV + hv) * KD * XW;
     if (is_e) {
+        // E in the scan's accumulator layout: 1 KiB block (sl KD/16 + rt)
+        // holds E[16 rt + 4 (L / 16) + q][16 sl + (L mod 16)], q = 0..3, in
+        // lane L's 16 bytes; a lane's four rows here are consecutive
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    dst[(int64_t)kperm(kt, 4 * lg + q) * VD + 32 * wv + 16 * ct + lc] = xs[kt][ct][q];
+            for (int ct = 0; ct < 2; ++ct) {
+                const int r0 = kperm(kt, 4 * lg), sl = 2 * wv + ct;  // 16-column slice of the wave's columns 32 wv + 16 ct ..
+                *(f32x4 *)(dst + (((sl * (KD / 16) + (r0 >> 4)) * 64 + 16 * ((r0 & 15) >> 2) + lc) << 2)) = xs[kt][ct];
+            }
     } else {
         bf16 *df = (bf16 *)(dst + KD * VD);
 #pragma unroll
@@ -479,9 +482,7 @@ gdp_seg_scan_k(const float *__restrict__ maps, const float *__restrict__ h0, int
                 for (int p = 0; p < 2; ++p)
                     R.a[t][ks][p] = *(const bf16x8 *)(df + (((2 * wv + t) * NKS + ks) * 2 + p) * 512);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) R.e[t][q] = m[(int64_t)(32 * wv + 16 * t + 4 * lg + q) * VD + j0 + lc];
+        for (int t = 0; t < 2; ++t) R.e[t] = *(const f32x4 *)(m + ((((j0 >> 4) * (KD / 16) + 2 * wv + t) * 64 + lane) << 2));
     };
     auto write_state = [&](int s, const f32x4 (&h)[2]) {
         float *out = hstart + ((int64_t)s * HV + hv) * VD * KD + so;
